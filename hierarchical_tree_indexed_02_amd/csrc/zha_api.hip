@@ -1,0 +1,328 @@
+// zha_api.hip -- host side of the C ABI declared in include/zha.h: argument
+// validation, the tree object and its device workspace, and the launches.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "zha_internal.h"
+
+int zha_score_wgs(const zha_tree* t, int level);
+size_t zha_stack_bytes(int L, int d, int R);
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+zha_status hip_fail(const char* where, hipError_t e) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+  return ZHA_ERR_HIP;
+}
+
+bool valid_refs(int R) { return R == 1 || R == 2 || R == 4 || R == 8 || R == 16; }
+
+zha_status check_desc(const zha_tree_desc* d) {
+  if (!d) return ZHA_ERR_INVALID;
+  if (d->batch < 1 || d->n_kv_heads < 1 || d->n_q_heads < 1 || d->chunk < 2 || d->levels < 1 || d->n_refs < 1 ||
+      d->max_tokens < 1 || d->head_dim < 1)
+    return ZHA_ERR_INVALID;
+  if (d->dtype != ZHA_F32 && d->dtype != ZHA_BF16) return ZHA_ERR_INVALID;
+  if (d->n_q_heads % d->n_kv_heads != 0) return ZHA_ERR_INVALID;
+  if (d->batch > ZHA_MAX_BATCH) return ZHA_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return ZHA_ERR_UNSUPPORTED;
+  if (!valid_refs(d->n_refs)) return ZHA_ERR_UNSUPPORTED;
+  if (d->n_q_heads / d->n_kv_heads > 16) return ZHA_ERR_UNSUPPORTED;
+  if (d->levels > ZHA_MAX_LEVELS) return ZHA_ERR_UNSUPPORTED;
+  if (d->max_tokens >= ((int64_t)1 << 31)) return ZHA_ERR_UNSUPPORTED;
+  double span = pow((double)d->chunk, (double)d->levels);
+  if (span > (double)(1 << 30)) return ZHA_ERR_UNSUPPORTED;
+  if (zha_stack_bytes(d->levels, d->head_dim, d->n_refs) > 160 * 1024) return ZHA_ERR_UNSUPPORTED;
+  return ZHA_OK;
+}
+
+void free_tree(zha_tree* t) {
+  if (!t) return;
+  for (int l = 0; l < ZHA_MAX_LEVELS + 2; ++l) {
+    if (t->m[l]) (void)hipFree(t->m[l]);
+    if (t->b[l]) (void)hipFree(t->b[l]);
+    if (t->kept[l]) (void)hipFree(t->kept[l]);
+  }
+  void* ps[] = {t->refs, t->spine, t->counts, t->scores, t->spart, t->keys, t->apart};
+  for (void* p : ps)
+    if (p) (void)hipFree(p);
+  for (int i = 0; i < 2 * ZHA_MAX_TIMING; ++i)
+    if (t->ev[i]) (void)hipEventDestroy(t->ev[i]);
+  delete t;
+}
+
+template <typename P>
+bool dalloc(zha_tree* t, P** p, size_t bytes) {
+  if (bytes == 0) bytes = 16;
+  void* q = nullptr;
+  if (hipMalloc(&q, bytes) != hipSuccess) return false;
+  *p = (P*)q;
+  t->bytes += (int64_t)bytes;
+  return true;
+}
+
+zha_status check_lens(const zha_tree* t, const int32_t* lens) {
+  if (!lens) return ZHA_ERR_INVALID;
+  for (int b = 0; b < t->desc.batch; ++b) {
+    if (lens[b] < 1) return ZHA_ERR_INVALID;
+    if ((int64_t)lens[b] > t->T) return ZHA_ERR_CAPACITY;
+  }
+  return ZHA_OK;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------------------- timing
+
+void zha_time_begin(zha_tree* t, hipStream_t s) {
+  if (!t->timing || t->n_rec >= ZHA_MAX_TIMING) return;
+  (void)hipEventRecord(t->ev[2 * t->n_rec], s);
+}
+
+void zha_time_end(zha_tree* t, hipStream_t s, int kernel, int level) {
+  if (!t->timing || t->n_rec >= ZHA_MAX_TIMING) return;
+  (void)hipEventRecord(t->ev[2 * t->n_rec + 1], s);
+  t->tk[t->n_rec] = kernel;
+  t->tl[t->n_rec] = level;
+  ++t->n_rec;
+}
+
+extern "C" {
+
+const char* zha_last_error(void) { return g_last_error; }
+
+const char* zha_status_str(zha_status s) {
+  switch (s) {
+    case ZHA_OK: return "ok";
+    case ZHA_ERR_INVALID: return "invalid argument";
+    case ZHA_ERR_CAPACITY: return "length exceeds tree capacity";
+    case ZHA_ERR_NOMEM: return "out of memory";
+    case ZHA_ERR_UNSUPPORTED: return "unsupported shape";
+    case ZHA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
+  if (!out) return ZHA_ERR_INVALID;
+  *out = nullptr;
+  zha_status st = check_desc(desc);
+  if (st != ZHA_OK) return st;
+  zha_tree* t = new (std::nothrow) zha_tree;
+  if (!t) return ZHA_ERR_NOMEM;
+  memset((void*)t, 0, sizeof(zha_tree));
+  t->desc = *desc;
+  hipError_t he = hipGetDevice(&t->device);
+  if (he != hipSuccess) { delete t; return hip_fail("hipGetDevice", he); }
+  t->U = desc->batch * desc->n_kv_heads;
+  t->G = desc->n_q_heads / desc->n_kv_heads;
+  t->R = desc->n_refs;
+  t->d = desc->head_dim;
+  t->C = desc->chunk;
+  t->L = desc->levels;
+  t->T = desc->max_tokens;
+  t->esize = desc->dtype == ZHA_BF16 ? 2 : 4;
+  const int64_t Nc = (t->T / t->C) * t->C;
+  int64_t span = 1;
+  for (int l = 1; l <= t->L; ++l) {
+    span *= t->C;
+    t->span[l] = span;
+    t->cap[l] = (Nc + span - 1) / span;
+  }
+  t->span[0] = 1;
+  t->cap[0] = 0;
+  const int U = t->U, R = t->R, d = t->d, G = t->G, L = t->L;
+  int ws = 4096 / U;
+  if (ws > 1024) ws = 1024;
+  if (ws < 1) ws = 1;
+  t->WS = ws;
+  t->WA = zha_dense_wgs(U);
+  bool ok = true;
+  for (int l = 1; l <= L && ok; ++l) {
+    ok = ok && dalloc(t, &t->m[l], (size_t)U * t->cap[l] * R * d * t->esize);
+    ok = ok && dalloc(t, &t->b[l], (size_t)U * t->cap[l] * R * sizeof(float));
+    ok = ok && dalloc(t, &t->kept[l], (size_t)U * t->cap[l] * sizeof(int32_t));
+  }
+  ok = ok && dalloc(t, &t->refs, (size_t)desc->n_kv_heads * R * d * sizeof(float));
+  ok = ok && dalloc(t, &t->spine, (size_t)U * zha_stack_bytes(L, d, R));
+  ok = ok && dalloc(t, &t->counts, (size_t)2 * (L + 2) * U * sizeof(int32_t));
+  ok = ok && dalloc(t, &t->scores, (size_t)U * t->cap[1] * G * sizeof(float));
+  ok = ok && dalloc(t, &t->spart, (size_t)U * t->WS * G * 2 * sizeof(float));
+  ok = ok && dalloc(t, &t->keys, (size_t)U * t->cap[1] * sizeof(uint32_t));
+  ok = ok && dalloc(t, &t->apart, (size_t)U * t->WA * G * (d + 2) * sizeof(float));
+  if (!ok) {
+    free_tree(t);
+    return ZHA_ERR_NOMEM;
+  }
+  *out = t;
+  return ZHA_OK;
+}
+
+void zha_tree_destroy(zha_tree_t t) { free_tree(t); }
+
+zha_status zha_tree_bytes(zha_tree_t t, int64_t* bytes) {
+  if (!t || !bytes) return ZHA_ERR_INVALID;
+  *bytes = t->bytes;
+  return ZHA_OK;
+}
+
+zha_status zha_build(zha_tree_t t, const void* K, const float* refs, const int32_t* seq_lens, hipStream_t s) {
+  if (!t || !K || !refs) return ZHA_ERR_INVALID;
+  zha_status st = check_lens(t, seq_lens);
+  if (st != ZHA_OK) return st;
+  for (int b = 0; b < t->desc.batch; ++b) t->len.n[b] = seq_lens[b];
+  t->len_prev = t->len;
+  hipError_t e = hipMemcpyAsync(t->refs, refs, (size_t)t->desc.n_kv_heads * t->R * t->d * sizeof(float),
+                                hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return hip_fail("zha_build copy of refs", e);
+  e = zha_launch_build(t, K, s);
+  if (e != hipSuccess) return hip_fail("zha_build launch", e);
+  t->built = true;
+  return ZHA_OK;
+}
+
+zha_status zha_append(zha_tree_t t, const void* K, const int32_t* new_seq_lens, hipStream_t s) {
+  if (!t || !K) return ZHA_ERR_INVALID;
+  if (!t->built) return ZHA_ERR_INVALID;
+  zha_status st = check_lens(t, new_seq_lens);
+  if (st != ZHA_OK) return st;
+  for (int b = 0; b < t->desc.batch; ++b)
+    if (new_seq_lens[b] < t->len.n[b]) return ZHA_ERR_INVALID;
+  t->len_prev = t->len;
+  for (int b = 0; b < t->desc.batch; ++b) t->len.n[b] = new_seq_lens[b];
+  hipError_t e = zha_launch_append(t, K, s);
+  if (e != hipSuccess) return hip_fail("zha_append launch", e);
+  return ZHA_OK;
+}
+
+zha_status zha_route(zha_tree_t t, const void* q, float p, float scale, zha_kept* kept, hipStream_t s) {
+  if (!t || !q || !kept) return ZHA_ERR_INVALID;
+  if (!t->built) return ZHA_ERR_INVALID;
+  if (!(p > 0.0f) || !isfinite(p) || !isfinite(scale)) return ZHA_ERR_INVALID;
+  hipError_t e = zha_launch_route(t, q, p, scale, s);
+  if (e != hipSuccess) return hip_fail("zha_route launch", e);
+  kept->counts = t->counts + (int64_t)(t->L + 2) * t->U + t->U;
+  kept->ids = t->kept[1];
+  kept->cap = t->cap[1];
+  return ZHA_OK;
+}
+
+zha_status zha_attend(zha_tree_t t, const void* q, const void* K, const void* V, const zha_kept* kept, float scale,
+                      float* out, float* lse, hipStream_t s) {
+  if (!t || !q || !K || !V || !kept || !out || !lse) return ZHA_ERR_INVALID;
+  if (!t->built) return ZHA_ERR_INVALID;
+  if (kept->ids != t->kept[1]) return ZHA_ERR_INVALID;  // a view of this tree's last route
+  if (!isfinite(scale)) return ZHA_ERR_INVALID;
+  hipError_t e = zha_launch_attend(t, q, K, V, scale, out, lse, s);
+  if (e != hipSuccess) return hip_fail("zha_attend launch", e);
+  return ZHA_OK;
+}
+
+size_t zha_dense_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                 int64_t max_tokens) {
+  (void)max_tokens;
+  if (batch < 1 || n_kv_heads < 1 || n_q_heads < n_kv_heads || head_dim < 1) return 0;
+  const int U = batch * n_kv_heads;
+  return (size_t)U * zha_dense_wgs(U) * (n_q_heads / n_kv_heads) * (head_dim + 2) * sizeof(float);
+}
+
+zha_status zha_dense_decode(const void* q, const void* K, const void* V, const int32_t* seq_lens, int32_t batch,
+                            int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int64_t max_tokens,
+                            zha_dtype dtype, float scale, float* out, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t s) {
+  if (!q || !K || !V || !seq_lens || !out || !lse || !workspace) return ZHA_ERR_INVALID;
+  if (batch < 1 || n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads != 0 || max_tokens < 1)
+    return ZHA_ERR_INVALID;
+  if (dtype != ZHA_F32 && dtype != ZHA_BF16) return ZHA_ERR_INVALID;
+  if (!isfinite(scale)) return ZHA_ERR_INVALID;
+  if (batch > ZHA_MAX_BATCH || (head_dim != 64 && head_dim != 128) || n_q_heads / n_kv_heads > 16 ||
+      max_tokens >= ((int64_t)1 << 31))
+    return ZHA_ERR_UNSUPPORTED;
+  if (workspace_bytes < zha_dense_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, max_tokens))
+    return ZHA_ERR_INVALID;
+  ZLens len;
+  memset(&len, 0, sizeof(len));
+  for (int b = 0; b < batch; ++b) {
+    if (seq_lens[b] < 1) return ZHA_ERR_INVALID;
+    if ((int64_t)seq_lens[b] > max_tokens) return ZHA_ERR_CAPACITY;
+    len.n[b] = seq_lens[b];
+  }
+  const int U = batch * n_kv_heads;
+  hipError_t e = zha_launch_dense(q, K, V, len, batch, n_q_heads, n_kv_heads, head_dim, max_tokens, dtype, scale,
+                                  out, lse, (float*)workspace, zha_dense_wgs(U), s);
+  if (e != hipSuccess) return hip_fail("zha_dense_decode launch", e);
+  return ZHA_OK;
+}
+
+zha_status zha_tree_level_capacity(zha_tree_t t, int32_t level, int64_t* nodes) {
+  if (!t || !nodes || level < 1 || level > t->L) return ZHA_ERR_INVALID;
+  *nodes = t->cap[level];
+  return ZHA_OK;
+}
+
+zha_status zha_tree_copy_level(zha_tree_t t, int32_t level, void* m_out, float* b_out, hipStream_t s) {
+  if (!t || !m_out || !b_out || level < 1 || level > t->L) return ZHA_ERR_INVALID;
+  const size_t nm = (size_t)t->U * t->cap[level] * t->R;
+  if (hipMemcpyAsync(m_out, t->m[level], nm * t->d * t->esize, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return ZHA_ERR_HIP;
+  if (hipMemcpyAsync(b_out, t->b[level], nm * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return ZHA_ERR_HIP;
+  return ZHA_OK;
+}
+
+zha_status zha_route_copy_level(zha_tree_t t, int32_t level, int32_t* frontier_counts, int32_t* kept_counts,
+                                int32_t* kept_ids, hipStream_t s) {
+  if (!t || !frontier_counts || !kept_counts || !kept_ids || level < 1 || level > t->L) return ZHA_ERR_INVALID;
+  const int U = t->U;
+  const int32_t* cF = t->counts + (int64_t)level * U;
+  const int32_t* cK = t->counts + (int64_t)(t->L + 2) * U + (int64_t)level * U;
+  if (hipMemcpyAsync(frontier_counts, cF, U * sizeof(int32_t), hipMemcpyDeviceToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(kept_counts, cK, U * sizeof(int32_t), hipMemcpyDeviceToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(kept_ids, t->kept[level], (size_t)U * t->cap[level] * sizeof(int32_t), hipMemcpyDeviceToDevice,
+                     s) != hipSuccess)
+    return ZHA_ERR_HIP;
+  return ZHA_OK;
+}
+
+zha_status zha_timing_enable(zha_tree_t t, int32_t enable) {
+  if (!t) return ZHA_ERR_INVALID;
+  if (enable && !t->ev[0]) {
+    for (int i = 0; i < 2 * ZHA_MAX_TIMING; ++i)
+      if (hipEventCreate(&t->ev[i]) != hipSuccess) return ZHA_ERR_HIP;
+  }
+  t->timing = enable != 0;
+  t->n_rec = 0;
+  return ZHA_OK;
+}
+
+zha_status zha_timing_read(zha_tree_t t, int32_t* kernels, int32_t* levels, float* ms, int32_t max_entries,
+                           int32_t* n_entries) {
+  if (!t || !n_entries || max_entries < 0 || (max_entries > 0 && (!kernels || !levels || !ms)))
+    return ZHA_ERR_INVALID;
+  const int n = t->n_rec < max_entries ? t->n_rec : max_entries;
+  for (int i = 0; i < n; ++i) {
+    float x = 0.0f;
+    if (hipEventElapsedTime(&x, t->ev[2 * i], t->ev[2 * i + 1]) != hipSuccess) return ZHA_ERR_HIP;
+    kernels[i] = t->tk[i];
+    levels[i] = t->tl[i];
+    ms[i] = x;
+  }
+  *n_entries = n;
+  t->n_rec = 0;
+  return ZHA_OK;
+}
+
+zha_status zha_calibration_copy(void* dst, const void* src, int64_t n16, hipStream_t s) {
+  if (!dst || !src || n16 < 0) return ZHA_ERR_INVALID;
+  if (((uintptr_t)dst & 15) || ((uintptr_t)src & 15)) return ZHA_ERR_INVALID;
+  hipError_t e = zha_launch_copy16(dst, src, n16, s);
+  if (e != hipSuccess) return hip_fail("zha_calibration_copy launch", e);
+  return ZHA_OK;
+}
+
+}  // extern "C"

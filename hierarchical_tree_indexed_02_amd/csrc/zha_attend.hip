@@ -1,0 +1,418 @@
+// zha_attend.hip -- exact attention over the routed token set, and dense decode.
+//
+// S = {token 0} U (tokens of the kept leaf chunks) U [Nc, N): the first token is
+// always kept as an attention sink, the trailing partial chunk is not in the
+// tree and is always read ([wqu] "How does top-p routing pick tokens?"), and
+// attention over S is exact softmax attention on the raw, unmodified K/V
+// ([wqu] "What is Zyphra Hierarchical Attention (ZHA)?").  Dense decode is the
+// same computation with S = [0, N).
+//
+// Split-K flash decode: each workgroup takes a contiguous slice of the unit's
+// position list (sink and tail first, then the kept chunks' tokens in order),
+// its four waves walk 32 positions at a time with an online softmax, and the
+// G query heads of the KV head share every K/V tile.  Q.K^T runs on the matrix
+// cores with K rows loaded straight from HBM into the operand registers; P.V
+// stages the V tile in LDS and reads it transposed.  P is split into two bf16
+// halves (hi + lo) so the softmax weights keep ~16 significant bits.  Partial
+// (max, sum, o) per workgroup are merged by zha_merge_kernel in fixed order.
+#include "zha_internal.h"
+
+namespace {
+
+struct AttArgs {
+  const void* q;           // [B][Hq][d]
+  const void* K;           // [B][Hkv][T][d]
+  const void* V;
+  const int32_t* kept;     // [U][cap1] level-1 kept chunk ids (sparse only)
+  const int32_t* kept_count;
+  int64_t cap1;
+  float* part;             // [U][W][G][d+2]: o (unnormalised), max (log2 units), sum
+  int W;
+  int Hkv, Hq, G, C, Cshift;
+  int64_t T;               // token stride of K/V
+  float scale_log2;        // scale * log2(e)
+  ZLens len;
+};
+
+struct Positions {
+  int P;        // number of positions
+  int nx;       // positions before the chunk tokens (sink, then tail)
+  int sink;     // 1 when token 0 is read as a separate sink position
+  int Nc;
+  const int32_t* kp;
+};
+
+template <bool DENSE>
+__device__ __forceinline__ Positions unit_positions(const AttArgs& a, int u, int bi) {
+  Positions P;
+  const int N = a.len.n[bi];
+  if (DENSE) {
+    P.P = N; P.nx = N; P.sink = 0; P.Nc = 0; P.kp = nullptr;
+    return P;
+  }
+  const int Nc = (N / a.C) * a.C;
+  const int nK = a.kept_count[u];
+  const int32_t* kp = a.kept + (int64_t)u * a.cap1;
+  const int sink = (Nc > 0 && (nK == 0 || kp[0] != 0)) ? 1 : 0;
+  P.sink = sink;
+  P.nx = sink + (N - Nc);
+  P.P = P.nx + nK * a.C;
+  P.Nc = Nc;
+  P.kp = kp;
+  return P;
+}
+
+// Token index of position p (DENSE: p itself).
+template <bool DENSE>
+__device__ __forceinline__ int pos_token(const Positions& P, int p, int C, int Cshift) {
+  if (DENSE) return p;
+  if (p < P.nx) return (P.sink && p == 0) ? 0 : P.Nc + p - P.sink;
+  const int q = p - P.nx;
+  if (Cshift >= 0) return (P.kp[q >> Cshift] << Cshift) + (q & ((1 << Cshift) - 1));
+  const int k = q / C;
+  return P.kp[k] * C + (q - k * C);
+}
+
+constexpr int ATT_STEP = 32;  // positions per wave step
+
+// ---------------------------------------------------------------- P.V, per storage type
+
+template <typename T, int D> struct PV;
+
+// bf16: V tile [32][D] staged in this wave's LDS region, read transposed.
+template <int D> struct PV<__bf16, D> {
+  static constexpr int LDS_STRIDE = D + 8;                    // elements; keeps 16-B rows, spreads banks
+  static constexpr int LDS_ELEMS = ATT_STEP * LDS_STRIDE;     // per wave
+  static constexpr int ND = D / 16;
+  typedef bf16x8_t vfrag[ATT_STEP * D / 8 / 64];              // 16-B pieces per lane
+  static constexpr int CPR = D / 8;                           // 16-B chunks per row
+  static constexpr int RPI = 64 / CPR;                        // rows per load instruction
+  static constexpr int NLD = ATT_STEP / RPI;
+
+  template <bool DENSE>
+  __device__ static __forceinline__ void load(vfrag& vf, const __bf16* Vb, const Positions& P, int p0, int end,
+                                              int C, int Cshift, int lane) {
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      const int ts = RPI * k + lane / CPR;
+      const int p = p0 + ts;
+      const int tok = p < end ? pos_token<DENSE>(P, p, C, Cshift) : 0;
+      vf[k] = *(const bf16x8_t*)(Vb + (int64_t)tok * D + 8 * (lane % CPR));
+    }
+  }
+  __device__ static __forceinline__ void stage(const vfrag& vf, __bf16* lds, int lane) {
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      const int ts = RPI * k + lane / CPR;
+      *(bf16x8_t*)(lds + ts * LDS_STRIDE + 8 * (lane % CPR)) = vf[k];
+    }
+  }
+  // o[dt] += V^T(d-tile dt) * P^T, k-slot e of lane group grp <-> token e<4 ? 4grp+e : 16+4grp+e-4
+  __device__ static __forceinline__ void mma(f32x4_t (&o)[ND], const __bf16* lds, const float (&p)[2][4], int lane) {
+    const int row = lane & 15, grp = lane >> 4;
+    bf16x8_t ph, pl;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = p[e >> 2][e & 3];
+      const __bf16 hi = Mf<__bf16>::from_f32(x);
+      ph[e] = hi;
+      pl[e] = Mf<__bf16>::from_f32(x - (float)hi);
+    }
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+      bf16x8_t va;
+      const __bf16* col = lds + dt * 16 + row;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ts = (e < 4) ? 4 * grp + e : 16 + 4 * grp + (e - 4);
+        va[e] = col[ts * LDS_STRIDE];
+      }
+      o[dt] = Mf<__bf16>::mma(va, ph, o[dt]);
+      o[dt] = Mf<__bf16>::mma(va, pl, o[dt]);
+    }
+  }
+};
+
+// f32: one element per lane per k-step, V read straight from memory.
+template <int D> struct PV<float, D> {
+  static constexpr int LDS_ELEMS = 0;
+  static constexpr int ND = D / 16;
+  typedef float vfrag[2][4][ND];
+  template <bool DENSE>
+  __device__ static __forceinline__ void load(vfrag& vf, const float* Vb, const Positions& P, int p0, int end,
+                                              int C, int Cshift, int lane) {
+    const int row = lane & 15, grp = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int p = p0 + 16 * t + 4 * grp + jj;
+        const int tok = p < end ? pos_token<DENSE>(P, p, C, Cshift) : 0;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) vf[t][jj][dt] = Vb[(int64_t)tok * D + dt * 16 + row];
+      }
+  }
+  __device__ static __forceinline__ void stage(const vfrag&, float*, int) {}
+  __device__ static __forceinline__ void mma(f32x4_t (&o)[ND], const vfrag& vf, const float (&p)[2][4]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) o[dt] = Mf<float>::mma(vf[t][jj][dt], p[t][jj], o[dt]);
+  }
+};
+
+template <typename T, int D, bool DENSE>
+__global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a) {
+  typedef Mf<T> M;
+  typedef PV<T, D> PVT;
+  constexpr int NK = D / M::KPER;
+  constexpr int ND = D / 16;
+  constexpr int LDS_WAVE = PVT::LDS_ELEMS > 0 ? PVT::LDS_ELEMS : 1;
+  constexpr int COMB_BYTES = 4 * 16 * D * 4 + 2 * 4 * 16 * 4;
+  constexpr int STAGE_BYTES = 4 * LDS_WAVE * (int)sizeof(T);
+  constexpr int SMEM = COMB_BYTES > STAGE_BYTES ? COMB_BYTES : STAGE_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, grp = lane >> 4;
+  const int u = blockIdx.y, bi = u / a.Hkv, g = u % a.Hkv;
+  const int G = a.G;
+  const Positions P = unit_positions<DENSE>(a, u, bi);
+  int per = (P.P + a.W - 1) / a.W;
+  per = ((per + ATT_STEP - 1) / ATT_STEP) * ATT_STEP;
+  const int start = blockIdx.x * per;
+  const int end = min(P.P, start + per);
+
+  const int64_t kvoff = ((int64_t)bi * a.Hkv + g) * a.T * D;
+  const T* Kb = (const T*)a.K + kvoff;
+  const T* Vb = (const T*)a.V + kvoff;
+
+  typename M::frag qf[NK];
+  {
+    const T* qp = (const T*)a.q + ((int64_t)bi * a.Hq + (int64_t)g * G + row) * D + grp * M::EPL;
+#pragma unroll
+    for (int s = 0; s < NK; ++s) qf[s] = row < G ? M::load(qp + s * M::KPER) : M::zero();
+  }
+  T* lds = (T*)smem + wave * LDS_WAVE;
+
+  f32x4_t o[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) o[dt] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  float mrun = -INFINITY, lrun = 0.0f;
+
+  for (int p0 = start + wave * ATT_STEP; p0 < end; p0 += 4 * ATT_STEP) {
+    // K rows of the two 16-token tiles: lane row r -> position p0 + 16t + r
+    typename M::frag kf[2][NK];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int p = p0 + 16 * t + row;
+      const int tok = p < end ? pos_token<DENSE>(P, p, a.C, a.Cshift) : 0;
+      const T* kr = Kb + (int64_t)tok * D + grp * M::EPL;
+#pragma unroll
+      for (int s = 0; s < NK; ++s) kf[t][s] = M::load(kr + s * M::KPER);
+    }
+    typename PVT::vfrag vf;
+    PVT::template load<DENSE>(vf, Vb, P, p0, end, a.C, a.Cshift, lane);
+    // S^T = K Q^T: lane holds tokens 16t + 4grp + jj for head `row`
+    float z[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < NK; ++s) acc = M::mma(kf[t][s], qf[s], acc);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int p = p0 + 16 * t + 4 * grp + jj;
+        z[t][jj] = p < end ? acc[jj] * a.scale_log2 : -INFINITY;
+      }
+    }
+    float mloc = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
+                       fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float mnew = fmaxf(mrun, mloc);
+    float pr[2][4];
+    float alpha = 1.0f, psum = 0.0f;
+    if (mnew == -INFINITY) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) pr[t][jj] = 0.0f;
+    } else {
+      alpha = zexp2(mrun - mnew);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          pr[t][jj] = zexp2(z[t][jj] - mnew);
+          psum += pr[t][jj];
+        }
+    }
+    lrun = lrun * alpha + psum;
+    mrun = mnew;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
+    if constexpr (PVT::LDS_ELEMS > 0) {
+      PVT::stage(vf, lds, lane);
+      PVT::mma(o, lds, pr, lane);
+    } else {
+      PVT::mma(o, vf, pr);
+    }
+  }
+  // per-head sum over the four lane groups, then combine the four waves through LDS
+  lrun += __shfl_xor(lrun, 16);
+  lrun += __shfl_xor(lrun, 32);
+  __syncthreads();  // the staging area is reused below
+  float* so = (float*)smem;                    // [4][16][D]
+  float* sm = so + 4 * 16 * D;                 // [4][16]
+  float* sl = sm + 4 * 16;                     // [4][16]
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) so[(wave * 16 + row) * D + dt * 16 + 4 * grp + jj] = o[dt][jj];
+  if (grp == 0) { sm[wave * 16 + row] = mrun; sl[wave * 16 + row] = lrun; }
+  __syncthreads();
+  float* out = a.part + ((int64_t)u * a.W + blockIdx.x) * G * (D + 2);
+  for (int i = threadIdx.x; i < G * D; i += 256) {
+    const int h = i / D, dd = i % D;
+    float Mx = -INFINITY;
+    for (int w = 0; w < 4; ++w) Mx = fmaxf(Mx, sm[w * 16 + h]);
+    float acc = 0.0f, l = 0.0f;
+    if (Mx != -INFINITY) {
+      for (int w = 0; w < 4; ++w) {
+        const float f = zexp2(sm[w * 16 + h] - Mx);
+        acc += f * so[(w * 16 + h) * D + dd];
+        l += f * sl[w * 16 + h];
+      }
+    }
+    out[h * (D + 2) + dd] = acc;
+    if (dd == 0) {
+      out[h * (D + 2) + D] = Mx;
+      out[h * (D + 2) + D + 1] = l;
+    }
+  }
+}
+
+// Merges the W partials of each (unit, head) in workgroup order.
+template <int D>
+__global__ __launch_bounds__(D) void zha_merge_kernel(const float* part, int W, int G, int Hkv, int Hq, float* out,
+                                                      float* lse) {
+  const int h = blockIdx.x, u = blockIdx.y, dd = threadIdx.x;
+  const int bi = u / Hkv, g = u % Hkv;
+  float Mx = -INFINITY, Lx = 0.0f, Ox = 0.0f;
+  for (int w = 0; w < W; ++w) {
+    const float* r = part + (((int64_t)u * W + w) * G + h) * (D + 2);
+    const float l = r[D + 1];
+    if (l == 0.0f) continue;
+    const float Mw = r[D];
+    const float nM = fmaxf(Mx, Mw);
+    const float f1 = zexp2(Mx - nM), f2 = zexp2(Mw - nM);
+    Lx = Lx * f1 + l * f2;
+    Ox = Ox * f1 + r[dd] * f2;
+    Mx = nM;
+  }
+  const int64_t oh = (int64_t)bi * Hq + (int64_t)g * G + h;
+  out[oh * D + dd] = Ox / Lx;
+  if (dd == 0) lse[oh] = (Mx + zlog2(Lx)) * ZHA_LN2;
+}
+
+template <typename T, int D, bool DENSE>
+hipError_t launch_att(const AttArgs& a, int U, float* out, float* lse, hipStream_t s) {
+  hipLaunchKernelGGL((zha_attend_kernel<T, D, DENSE>), dim3(a.W, U), dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return hipSuccess;
+}
+
+template <int D>
+hipError_t launch_merge(const AttArgs& a, int U, float* out, float* lse, hipStream_t s) {
+  hipLaunchKernelGGL((zha_merge_kernel<D>), dim3(a.G, U), dim3(D), 0, s, (const float*)a.part, a.W, a.G, a.Hkv,
+                     a.Hq, out, lse);
+  return hipGetLastError();
+}
+
+template <bool DENSE>
+hipError_t launch_att_dt(const AttArgs& a, zha_dtype dt, int d, int U, float* out, float* lse, hipStream_t s) {
+  if (dt == ZHA_BF16)
+    return d == 64 ? launch_att<__bf16, 64, DENSE>(a, U, out, lse, s) : launch_att<__bf16, 128, DENSE>(a, U, out, lse, s);
+  return d == 64 ? launch_att<float, 64, DENSE>(a, U, out, lse, s) : launch_att<float, 128, DENSE>(a, U, out, lse, s);
+}
+
+int cshift_of(int C) {
+  if (C <= 0 || (C & (C - 1)) != 0) return -1;
+  int s = 0;
+  while ((1 << s) < C) ++s;
+  return s;
+}
+
+}  // namespace
+
+int zha_dense_wgs(int U) {
+  int w = 1024 / (U > 0 ? U : 1);
+  return w < 1 ? 1 : w;
+}
+
+hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const void* V, float scale, float* out,
+                             float* lse, hipStream_t s) {
+  AttArgs a;
+  a.q = q; a.K = K; a.V = V;
+  a.kept = t->kept[1];
+  a.kept_count = t->counts + (int64_t)(t->L + 2) * t->U + t->U;  // kept counts of level 1
+  a.cap1 = t->cap[1];
+  a.part = t->apart;
+  a.W = t->WA;
+  a.Hkv = t->desc.n_kv_heads;
+  a.Hq = t->desc.n_q_heads;
+  a.G = t->G;
+  a.C = t->C;
+  a.Cshift = cshift_of(t->C);
+  a.T = t->T;
+  a.scale_log2 = scale * ZHA_LOG2E;
+  a.len = t->len;
+  zha_time_begin(t, s);
+  hipError_t e = launch_att_dt<false>(a, t->desc.dtype, t->d, t->U, out, lse, s);
+  if (e != hipSuccess) return e;
+  zha_time_end(t, s, ZHA_K_ATTEND, 0);
+  zha_time_begin(t, s);
+  e = t->d == 64 ? launch_merge<64>(a, t->U, out, lse, s) : launch_merge<128>(a, t->U, out, lse, s);
+  if (e != hipSuccess) return e;
+  zha_time_end(t, s, ZHA_K_MERGE, 0);
+  return hipSuccess;
+}
+
+hipError_t zha_launch_dense(const void* q, const void* K, const void* V, const ZLens& len, int B, int Hq, int Hkv,
+                            int d, int64_t T, zha_dtype dt, float scale, float* out, float* lse, float* part, int WA,
+                            hipStream_t s) {
+  AttArgs a;
+  a.q = q; a.K = K; a.V = V;
+  a.kept = nullptr;
+  a.kept_count = nullptr;
+  a.cap1 = 0;
+  a.part = part;
+  a.W = WA;
+  a.Hkv = Hkv;
+  a.Hq = Hq;
+  a.G = Hq / Hkv;
+  a.C = 1;
+  a.Cshift = 0;
+  a.T = T;
+  a.scale_log2 = scale * ZHA_LOG2E;
+  a.len = len;
+  const int U = B * Hkv;
+  hipError_t e = launch_att_dt<true>(a, dt, d, U, out, lse, s);
+  if (e != hipSuccess) return e;
+  return d == 64 ? launch_merge<64>(a, U, out, lse, s) : launch_merge<128>(a, U, out, lse, s);
+}
+
+__global__ void zha_copy16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, int64_t n) {
+  int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) dst[i] = src[i];
+}
+
+hipError_t zha_launch_copy16(void* dst, const void* src, int64_t n16, hipStream_t s) {
+  hipLaunchKernelGGL(zha_copy16_kernel, dim3(2048), dim3(256), 0, s, (const uint4*)src, (uint4*)dst, n16);
+  return hipGetLastError();
+}

@@ -1,0 +1,174 @@
+// zha_internal.h -- device helpers and host-side tree object of the ZHA library.
+// Page references: see include/zha.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <vector>
+
+#include "../../include/zha.h"
+
+// ----------------------------------------------------------------------------- device types
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16;
+
+#define ZHA_LOG2E 1.4426950408889634f
+#define ZHA_LN2 0.6931471805599453f
+
+// exp and log on the hardware transcendental units (v_exp_f32 / v_log_f32 are base 2).
+__device__ __forceinline__ float zexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float zexp(float x) { return __builtin_amdgcn_exp2f(x * ZHA_LOG2E); }
+__device__ __forceinline__ float zlog(float x) { return __builtin_amdgcn_logf(x) * ZHA_LN2; }
+__device__ __forceinline__ float zlog2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float bf16_bits_to_f32(u16 h) { return __uint_as_float((uint32_t)h << 16); }
+// fp32 -> bf16, round to nearest even (finite values).
+__device__ __forceinline__ u16 f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (u16)(u >> 16);
+}
+
+// Storage-type traits: how many elements one lane feeds a 16x16 MFMA per k-step.
+//   bf16: v_mfma_f32_16x16x32_bf16, 8 elements per lane, k = 32 per instruction.
+//   f32:  v_mfma_f32_16x16x4f32,   1 element per lane,  k = 4 per instruction.
+// Lane i of the wave holds operand row/column (i % 16) and k-slot group (i / 16).
+template <typename T> struct Mf;
+template <> struct Mf<__bf16> {
+  typedef bf16x8_t frag;
+  static constexpr int EPL = 8;
+  static constexpr int KPER = 32;
+  __device__ static __forceinline__ frag load(const __bf16* p) { return *(const bf16x8_t*)p; }
+  __device__ static __forceinline__ frag zero() { bf16x8_t z; for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.0f; return z; }
+  __device__ static __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+  __device__ static __forceinline__ __bf16 from_f32(float x) {
+    return __builtin_bit_cast(__bf16, f32_to_bf16_bits(x));
+  }
+};
+template <> struct Mf<float> {
+  typedef float frag;
+  static constexpr int EPL = 1;
+  static constexpr int KPER = 4;
+  __device__ static __forceinline__ frag load(const float* p) { return *p; }
+  __device__ static __forceinline__ frag zero() { return 0.0f; }
+  __device__ static __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ float to_f32(float x) { return x; }
+  __device__ static __forceinline__ float from_f32(float x) { return x; }
+};
+
+// Sum over the 16 lanes of a DPP row (xor butterfly: every lane ends with the same bits).
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 8, 16);
+  x += __shfl_xor(x, 4, 16);
+  x += __shfl_xor(x, 2, 16);
+  x += __shfl_xor(x, 1, 16);
+  return x;
+}
+
+// fp32 accumulator of one (node, reference query) while its children are folded in:
+// running maximum M, S = sum exp(x - M), V = sum exp(x - M) * m (this lane's slice).
+// Folding child (x, m) and finishing give LSE = M + log S, mean = V / S, the exact
+// log-sum-exp combination of the children ([aitop] abstract: recursive compression).
+template <int E> struct Acc {
+  float M, S;
+  float V[E];
+};
+
+template <int E> __device__ __forceinline__ void acc_clear(Acc<E>& a) {
+  a.M = -INFINITY;
+  a.S = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) a.V[e] = 0.0f;
+}
+
+#pragma clang fp contract(off)
+template <int E> __device__ __forceinline__ void acc_fold(Acc<E>& a, float x, const float (&m)[E]) {
+  if (a.S == 0.0f) {
+    a.M = x;
+    a.S = 1.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) a.V[e] = m[e];
+  } else if (x <= a.M) {
+    float c = zexp(x - a.M);
+    a.S = a.S + c;
+#pragma unroll
+    for (int e = 0; e < E; ++e) a.V[e] = __builtin_fmaf(c, m[e], a.V[e]);
+  } else {
+    float c = zexp(a.M - x);
+    a.S = __builtin_fmaf(a.S, c, 1.0f);
+#pragma unroll
+    for (int e = 0; e < E; ++e) a.V[e] = __builtin_fmaf(a.V[e], c, m[e]);
+    a.M = x;
+  }
+}
+
+template <int E> __device__ __forceinline__ void acc_finish(const Acc<E>& a, float& lse, float (&m)[E]) {
+  lse = a.M + zlog(a.S);
+#pragma unroll
+  for (int e = 0; e < E; ++e) m[e] = a.V[e] / a.S;
+}
+#pragma clang fp contract(on)
+
+// ----------------------------------------------------------------------------- host side
+
+#define ZHA_MAX_LEVELS 16
+#define ZHA_MAX_TIMING 256
+#define ZHA_MAX_BATCH 64
+
+// Sequence lengths travel by value in every kernel's arguments (no device copy,
+// so a sequence of calls can be captured into a graph).
+struct ZLens {
+  int32_t n[ZHA_MAX_BATCH];
+};
+
+struct zha_tree {
+  zha_tree_desc desc;
+  int device;
+  int U, G, R, d, C, L, esize;
+  int64_t T;                      // max_tokens (token stride of K/V)
+  int64_t cap[ZHA_MAX_LEVELS + 2];  // nodes per unit at each level (1..L)
+  int64_t span[ZHA_MAX_LEVELS + 2]; // tokens covered by one node at each level: C^l
+  void* m[ZHA_MAX_LEVELS + 2];      // level planes m [U][cap][R][d]
+  float* b[ZHA_MAX_LEVELS + 2];     // level planes b [U][cap][R]
+  int32_t* kept[ZHA_MAX_LEVELS + 2];// per-level kept ids [U][cap]
+  float* refs;                      // [Hkv][R][d]
+  float* spine;                     // [U][L+1][R*16][E+2] open-node accumulators
+  int32_t* counts;                  // [2][L+2][U]: frontier counts, kept counts per level
+  float* scores;                    // [U][cap1][G]
+  float* spart;                     // [U][WS][G][2] score-kernel partial log-sum-exp
+  uint32_t* keys;                   // [U][cap1]
+  float* apart;                     // [U][WA][G][d+2] attention partials
+  int WS, WA;                       // score and attention workgroups per unit (maximum)
+  ZLens len;                        // current lengths
+  ZLens len_prev;                   // lengths before the last zha_append
+  bool built;
+  int64_t bytes;
+  // timing
+  bool timing;
+  hipEvent_t ev[2 * ZHA_MAX_TIMING];
+  int tk[ZHA_MAX_TIMING], tl[ZHA_MAX_TIMING];
+  int n_rec;
+};
+
+// Timing helpers (record events around a launch when enabled).
+void zha_time_begin(zha_tree* t, hipStream_t s);
+void zha_time_end(zha_tree* t, hipStream_t s, int kernel, int level);
+
+// Launchers (defined next to their kernels).  All return hipSuccess or the launch error.
+hipError_t zha_launch_build(zha_tree* t, const void* K, hipStream_t s);
+hipError_t zha_launch_append(zha_tree* t, const void* K, hipStream_t s);
+hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hipStream_t s);
+hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const void* V, float scale,
+                             float* out, float* lse, hipStream_t s);
+hipError_t zha_launch_dense(const void* q, const void* K, const void* V, const ZLens& len, int B, int Hq,
+                            int Hkv, int d, int64_t T, zha_dtype dt, float scale, float* out, float* lse,
+                            float* part, int WA, hipStream_t s);
+hipError_t zha_launch_copy16(void* dst, const void* src, int64_t n16, hipStream_t s);
+int zha_dense_wgs(int U);

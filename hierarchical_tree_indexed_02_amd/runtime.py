@@ -1,0 +1,105 @@
+"""Torch-side helpers around the ctypes binding: allocation of output and
+inspection buffers on the current device, and a Tree object that owns a
+zha_tree handle.  Every computation happens in libzha.so's kernels."""
+from __future__ import annotations
+
+import torch
+
+from . import zha
+
+_DT = {torch.bfloat16: zha.ZHA_BF16, torch.float32: zha.ZHA_F32}
+
+
+def zdtype(t: torch.dtype) -> int:
+    if t not in _DT:
+        raise ValueError(f"unsupported dtype {t}")
+    return _DT[t]
+
+
+class Tree:
+    """One attention layer's summary tree (library-owned device memory)."""
+
+    def __init__(self, batch, n_kv_heads, n_q_heads, head_dim, chunk, levels, n_refs, max_tokens,
+                 dtype=torch.bfloat16):
+        self.desc = zha.zha_tree_desc(batch, n_kv_heads, n_q_heads, head_dim, chunk, levels, n_refs, max_tokens,
+                                      zdtype(dtype))
+        self.dtype = dtype
+        self.B, self.Hkv, self.Hq, self.d = batch, n_kv_heads, n_q_heads, head_dim
+        self.C, self.L, self.R, self.T = chunk, levels, n_refs, max_tokens
+        self.U = batch * n_kv_heads
+        self.G = n_q_heads // n_kv_heads
+        self.h = zha.zha_tree_create(self.desc)
+        self.kept = None
+
+    def close(self):
+        if getattr(self, "h", None):
+            zha.zha_tree_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def bytes(self) -> int:
+        return zha.zha_tree_bytes(self.h)
+
+    def build(self, K, refs, seq_lens, stream=None):
+        zha.zha_build(self.h, K, refs, seq_lens, stream)
+
+    def append(self, K, new_seq_lens, stream=None):
+        zha.zha_append(self.h, K, new_seq_lens, stream)
+
+    def route(self, q, p, scale=1.0, stream=None):
+        self.kept = zha.zha_route(self.h, q, p, scale, stream)
+        return self.kept
+
+    def attend(self, q, K, V, scale=1.0, out=None, lse=None, stream=None):
+        if out is None:
+            out = torch.empty((self.B, self.Hq, self.d), dtype=torch.float32, device=q.device)
+        if lse is None:
+            lse = torch.empty((self.B, self.Hq), dtype=torch.float32, device=q.device)
+        zha.zha_attend(self.h, q, K, V, self.kept, scale, out, lse, stream)
+        return out, lse
+
+    def capacity(self, level: int) -> int:
+        return zha.zha_tree_level_capacity(self.h, level)
+
+    def level(self, level: int, device="cuda"):
+        """(m [U][cap][R][d] in the tree dtype, b [U][cap][R] fp32) of one level."""
+        cap = self.capacity(level)
+        m = torch.empty((self.U, cap, self.R, self.d), dtype=self.dtype, device=device)
+        b = torch.empty((self.U, cap, self.R), dtype=torch.float32, device=device)
+        zha.zha_tree_copy_level(self.h, level, m, b)
+        return m, b
+
+    def route_level(self, level: int, device="cuda"):
+        """(frontier counts [U], kept counts [U], kept ids [U][cap]) of the last route."""
+        cap = self.capacity(level)
+        nf = torch.empty(self.U, dtype=torch.int32, device=device)
+        nk = torch.empty(self.U, dtype=torch.int32, device=device)
+        ids = torch.empty((self.U, cap), dtype=torch.int32, device=device)
+        zha.zha_route_copy_level(self.h, level, nf, nk, ids)
+        return nf, nk, ids
+
+    def timing(self, enable: bool):
+        zha.zha_timing_enable(self.h, enable)
+
+    def timing_read(self):
+        return zha.zha_timing_read(self.h)
+
+
+def dense_decode(q, K, V, seq_lens, n_kv_heads, scale=1.0, workspace=None, out=None, lse=None, stream=None):
+    B, Hq, d = q.shape
+    T = K.shape[2]
+    if workspace is None:
+        nb = zha.zha_dense_workspace_bytes(B, Hq, n_kv_heads, d, T)
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    zha.zha_dense_decode(q, K, V, seq_lens, B, Hq, n_kv_heads, d, T, zdtype(q.dtype), scale, out, lse, workspace,
+                         workspace.numel(), stream)
+    return out, lse

@@ -1,0 +1,211 @@
+/*
+ * zha.h -- C ABI of the Zyphra Hierarchical Attention (ZHA) decode path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method (page references are by site and section heading):
+ *   [wqu]   wqu.guru, "Zyphra发布层级注意力ZHA：稀疏搜索实现亚二次复杂度"
+ *   [flux]  fluxbbs.com, "Zyphra ZHA 稀疏注意力：8.2 万参数与 373 倍加速推算"
+ *   [aitop] aitop.news, "Zyphra 提出树结构索引器 ZHA，实现亚二次复杂度长上下文注意力"
+ *           (the paper's abstract)
+ *   [icwork] ic.work article on ZHA
+ * Keys of one attention layer's KV cache are cut into chunks of C tokens;
+ * every chunk, and recursively every group of C nodes, is summarised by R
+ * tangent planes of its log attention mass, one per reference query
+ * ([wqu] "Building the tree").  A decode query scores the top nodes, keeps the
+ * smallest set holding a fraction p of the estimated mass, expands only those
+ * nodes' children and repeats down to raw chunks ([wqu] "How does top-p routing
+ * pick tokens?"); exact attention then reads only the kept chunks plus the
+ * first token ([wqu] same section; "What is Zyphra Hierarchical Attention").
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers unless a comment says "host".  All
+ *     device work is enqueued on the given stream; no entry point synchronises
+ *     the host with the device, allocates device memory after
+ *     zha_tree_create, or issues memset nodes, so a call sequence can be
+ *     captured into a HIP graph.
+ *   - B sequences, Hkv KV heads, Hq = G * Hkv query heads (query head h reads
+ *     KV head h / G), head dimension d.  A "unit" is one (sequence, KV head).
+ *   - K and V: [B][Hkv][max_tokens][d], contiguous, dtype of the tree.  q:
+ *     [B][Hq][d], same dtype.  refs: [Hkv][R][d] float32.  out: [B][Hq][d]
+ *     float32.  lse: [B][Hq] float32.  All owned by the caller.
+ *   - Logits are scale * q.k; the tree's planes live in scaled-query space, so
+ *     zha_route and zha_attend must receive the same scale.
+ *   - Level 1 nodes are leaf chunks of C consecutive tokens; a level-l node
+ *     covers C^l tokens; only complete leaf chunks enter the tree (the tree
+ *     spans Nc = C*floor(N/C) tokens; the last node of a level may be partial).
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued; a failed validation returns a status and enqueues nothing.
+ *     A failed launch returns ZHA_ERR_HIP.  Faults inside kernels surface at
+ *     the caller's next synchronisation of the stream.  No exception crosses
+ *     the ABI.  A tree is not thread-safe; distinct trees are independent.
+ */
+#ifndef ZHA_H
+#define ZHA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Every entry point below is exported from libzha.so with default visibility. */
+#define ZHA_API __attribute__((visibility("default")))
+
+typedef struct zha_tree* zha_tree_t;
+
+typedef enum {
+    ZHA_OK = 0,
+    ZHA_ERR_INVALID = 1,      /* an argument is out of range or null */
+    ZHA_ERR_CAPACITY = 2,     /* a length exceeds the tree's max_tokens */
+    ZHA_ERR_NOMEM = 3,        /* device or host allocation failed */
+    ZHA_ERR_UNSUPPORTED = 4,  /* a shape this build does not implement */
+    ZHA_ERR_HIP = 5           /* a HIP runtime call failed */
+} zha_status;
+
+typedef enum { ZHA_F32 = 0, ZHA_BF16 = 1 } zha_dtype;
+
+/* Shape of one layer's tree.  Supported: head_dim in {64, 128};
+ * n_refs in {1, 2, 4, 8, 16}; group = n_q_heads / n_kv_heads in [1, 16];
+ * chunk >= 2; 1 <= levels <= 16 with chunk^levels <= 2^30; max_tokens < 2^31. */
+typedef struct {
+    int32_t batch;        /* B */
+    int32_t n_kv_heads;   /* Hkv */
+    int32_t n_q_heads;    /* Hq, a multiple of Hkv */
+    int32_t head_dim;     /* d */
+    int32_t chunk;        /* C: tokens per leaf chunk and children per node */
+    int32_t levels;       /* L: summary levels */
+    int32_t n_refs;       /* R: reference queries per KV head */
+    int64_t max_tokens;   /* capacity per sequence (the K/V token stride) */
+    zha_dtype dtype;      /* storage dtype of q, K, V and of the planes' m */
+} zha_tree_desc;
+
+/* Kept leaf chunks of the last zha_route on a tree: a view into the tree's
+ * workspace, valid until the next zha_route on the same tree.
+ * counts: device [B*Hkv]; ids: device [B*Hkv][cap], each unit's ids ascending. */
+typedef struct {
+    const int32_t* counts;
+    const int32_t* ids;
+    int64_t cap;
+} zha_kept;
+
+/* Allocates a tree and all its device workspace for the descriptor (the
+ * planes of every level, the fp32 accumulators of each unit's rightmost open
+ * nodes, and the routing/attention scratch).  The current HIP device owns it.
+ * Errors: ZHA_ERR_INVALID (null or out-of-range field), ZHA_ERR_UNSUPPORTED,
+ * ZHA_ERR_NOMEM. */
+ZHA_API zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out);
+ZHA_API void zha_tree_destroy(zha_tree_t tree);
+
+/* Device bytes held by the tree (planes + accumulators + workspace). */
+ZHA_API zha_status zha_tree_bytes(zha_tree_t tree, int64_t* bytes);
+
+/* Builds every level's planes from the caller's keys ([wqu] "Building the
+ * tree"; [aitop] abstract: recursively compressed key summaries).  For each
+ * node and reference query r the node stores m_r (the r-softmax-weighted mean
+ * key, in the tree dtype) and b_r = LSE_r - r.m_r (float32, from the stored
+ * m_r), LSE_r being the log-sum-exp of r.k over the node's tokens.  Parents
+ * combine their children's fp32 (LSE, mean) exactly; leaves read K once.
+ * refs are copied into the tree.  seq_lens (host [B]) sets each sequence's
+ * length N_b, 1 <= N_b <= max_tokens.
+ * Errors: ZHA_ERR_INVALID, ZHA_ERR_CAPACITY, ZHA_ERR_HIP. */
+ZHA_API zha_status zha_build(zha_tree_t tree, const void* K, const float* refs,
+                     const int32_t* seq_lens, hipStream_t stream);
+
+/* Grows the tree after the caller has written rows [N_b, new_N_b) of K (and
+ * V).  Every leaf chunk completed by the new rows gets its planes, is folded
+ * into its ancestors' fp32 accumulators in order, and the planes of the
+ * affected ancestors (complete or still open) are rewritten.  The result is
+ * bit-identical to zha_build over the grown cache.  new_seq_lens: host [B],
+ * N_b <= new_N_b <= max_tokens.  The tree reading of growth is not stated on
+ * the pages, which only say that future queries traverse a tree built over
+ * the KV cache ([aitop] abstract).
+ * Errors: ZHA_ERR_INVALID (shrinking length or no prior zha_build),
+ * ZHA_ERR_CAPACITY, ZHA_ERR_HIP. */
+ZHA_API zha_status zha_append(zha_tree_t tree, const void* K, const int32_t* new_seq_lens,
+                      hipStream_t stream);
+
+/* Routes the Hq decode queries top-down ([wqu] "How does top-p routing pick
+ * tokens?").  For each unit and level, every frontier node i is scored for
+ * each of the G query heads of the KV head as s_hi = max_r (b_ir + scale *
+ * q_h.m_ir); each head's scores are normalised over the frontier by softmax;
+ * the node mass w_i is the mean over the G heads; the kept set is the
+ * shortest prefix, in (w descending, node id ascending) order, whose mass
+ * reaches p times the frontier total (everything when p >= 1); the next
+ * frontier is the kept nodes' children.  The G heads of a KV head share one
+ * kept set.  On return *kept views the level-1 kept chunk ids of each unit.
+ * q: [B][Hq][d] in the tree dtype.  0 < p; p >= 1 keeps every node.
+ * Errors: ZHA_ERR_INVALID (p <= 0 or not finite, null pointer, no prior
+ * zha_build), ZHA_ERR_HIP. */
+ZHA_API zha_status zha_route(zha_tree_t tree, const void* q, float p, float scale,
+                     zha_kept* kept, hipStream_t stream);
+
+/* Exact attention of each query head over S = {token 0} U (tokens of the
+ * kept chunks) U [Nc, N), S a set ([wqu] "How does top-p routing pick
+ * tokens?": the first token is always kept; the trailing partial chunk is not
+ * in the tree and is always read).  out_h = sum_{t in S} softmax_S(scale *
+ * q_h.k_t) v_t and lse_h = log sum_{t in S} exp(scale * q_h.k_t), computed
+ * in float32 from the stored K and V.  kept: the view returned by zha_route
+ * on this tree.  Errors: ZHA_ERR_INVALID, ZHA_ERR_HIP. */
+ZHA_API zha_status zha_attend(zha_tree_t tree, const void* q, const void* K, const void* V,
+                      const zha_kept* kept, float scale, float* out, float* lse,
+                      hipStream_t stream);
+
+/* Dense decode attention over [0, N_b), the comparison baseline.  Same
+ * layouts as zha_attend.  workspace: device scratch of at least
+ * zha_dense_workspace_bytes(...) bytes, owned by the caller.
+ * Errors: ZHA_ERR_INVALID, ZHA_ERR_CAPACITY, ZHA_ERR_UNSUPPORTED, ZHA_ERR_HIP. */
+ZHA_API zha_status zha_dense_decode(const void* q, const void* K, const void* V,
+                            const int32_t* seq_lens /* host [B] */,
+                            int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                            int32_t head_dim, int64_t max_tokens, zha_dtype dtype,
+                            float scale, float* out, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+ZHA_API size_t zha_dense_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                 int32_t head_dim, int64_t max_tokens);
+
+/* ---- inspection (tests and benchmarks) -------------------------------- */
+
+/* Node capacity of a level (per unit): ceil(C*floor(max_tokens/C) / C^level). */
+ZHA_API zha_status zha_tree_level_capacity(zha_tree_t tree, int32_t level, int64_t* nodes);
+
+/* Copies level `level` (1..L) of the tree: m_out [B*Hkv][cap][R][d] in the
+ * tree dtype and b_out [B*Hkv][cap][R] float32 (cap from
+ * zha_tree_level_capacity).  Device buffers owned by the caller. */
+ZHA_API zha_status zha_tree_copy_level(zha_tree_t tree, int32_t level, void* m_out, float* b_out,
+                               hipStream_t stream);
+
+/* Copies the last route's result at `level`: frontier_counts [B*Hkv],
+ * kept_counts [B*Hkv], kept_ids [B*Hkv][cap] (ascending).  The frontier of
+ * level L is every level-L node; the frontier of level l < L is the children
+ * of the kept set of level l + 1.  Device buffers owned by the caller. */
+ZHA_API zha_status zha_route_copy_level(zha_tree_t tree, int32_t level, int32_t* frontier_counts,
+                                int32_t* kept_counts, int32_t* kept_ids, hipStream_t stream);
+
+/* Per-kernel timing.  When enabled, the tree records a HIP event pair on the
+ * stream around every kernel it launches.  After the caller has synchronised
+ * the stream, zha_timing_read returns for each recorded launch its kernel
+ * code (see ZHA_K_*), its level (0 when none) and its duration in ms, and
+ * clears the record.  At most 256 launches are kept. */
+enum { ZHA_K_BUILD = 1, ZHA_K_APPEND = 2, ZHA_K_SCORE = 3, ZHA_K_SELECT = 4,
+       ZHA_K_ATTEND = 5, ZHA_K_MERGE = 6 };
+ZHA_API zha_status zha_timing_enable(zha_tree_t tree, int32_t enable);
+ZHA_API zha_status zha_timing_read(zha_tree_t tree, int32_t* kernels, int32_t* levels, float* ms,
+                           int32_t max_entries, int32_t* n_entries);
+
+/* Copy kernel of known size, used to calibrate hardware byte counters:
+ * dst[i] = src[i] for n 16-byte elements (both device, 16-byte aligned). */
+ZHA_API zha_status zha_calibration_copy(void* dst, const void* src, int64_t n16, hipStream_t stream);
+
+ZHA_API const char* zha_status_str(zha_status status);
+
+/* Text of the last HIP failure that made an entry point return ZHA_ERR_HIP on
+ * the calling thread (empty when none); owned by the library. */
+ZHA_API const char* zha_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZHA_H */

@@ -1,0 +1,264 @@
+"""GPU-vs-oracle parity checks, stage by stage and teacher-forced.
+
+Build:   every checked node's stored planes against the oracle's planes by
+         definition over the node's tokens:
+           |m~ - m| <= 2^-8 |m| + 2e-5   (bf16 storage; fp32: 1e-5 |m| + 1e-5)
+           |(b~ + r.m~) - LSE| <= 1e-4 max(1, |LSE|)
+Route:   at every level the oracle selects from the GPU's own frontier (the
+         children of the GPU's kept set one level up) using the GPU's stored
+         planes; the kept sets must be equal except for nodes whose mass is
+         within 1e-4 (in log) of the boundary nodes, or that sit at the boundary
+         when the cumulative mass is within 1e-4 of p.
+Attend:  the oracle attends over the GPU's kept chunks (+ sink + tail):
+         max |out - out_o| <= 2e-3, max |lse - lse_o| <= 1e-3.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+import zha_inputs as zi
+from hierarchical_tree_indexed_02_amd.runtime import Tree, dense_decode
+
+TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+OUT_TOL, LSE_TOL = 2e-3, 1e-3
+PLANE_TOL = 1e-4
+AMBIG = 1e-4
+
+
+def m_tol(dtype):
+    return (2.0 ** -8, 2e-5) if dtype == "bf16" else (1e-5, 1e-5)
+
+
+class Case:
+    """Inputs of a workload on the host (fp32 arrays holding stored-dtype values) and on the GPU."""
+
+    def __init__(self, cfg: zi.Config, lens=None, n_queries=2, max_tokens=None, device="cuda"):
+        self.cfg = cfg
+        B, Hkv, d = cfg.batch, cfg.n_kv_heads, cfg.head_dim
+        self.B, self.Hkv, self.Hq, self.d = B, Hkv, cfg.n_q_heads, d
+        self.G = cfg.group
+        self.lens = list(lens) if lens is not None else [cfg.n_tokens] * B
+        self.T = max_tokens or max(cfg.max_tokens, max(self.lens))
+        self.q = zi.queries(cfg, n=n_queries)  # [T][B][Hq][d]
+        self.refs = zi.refs(cfg)
+        dt = TORCH_DT[cfg.dtype]
+        self.Kd = torch.zeros((B, Hkv, self.T, d), dtype=dt, device=device)
+        self.Vd = torch.zeros((B, Hkv, self.T, d), dtype=dt, device=device)
+        self.K, self.V = {}, {}
+        for b in range(B):
+            for g in range(Hkv):
+                Ku, Vu = zi.unit_kv(cfg, b, g)
+                self.K[(b, g)], self.V[(b, g)] = Ku, Vu
+                self.Kd[b, g, :cfg.n_tokens] = torch.from_numpy(Ku).to(device=device, dtype=dt)
+                self.Vd[b, g, :cfg.n_tokens] = torch.from_numpy(Vu).to(device=device, dtype=dt)
+        self.refs_d = torch.from_numpy(self.refs).to(device)
+        self.qd = torch.from_numpy(self.q).to(device=device, dtype=dt)
+
+    def add_rows(self, b, g, start, Krows, Vrows):
+        """Host and device copies of rows appended to unit (b, g) at `start`."""
+        dt = TORCH_DT[self.cfg.dtype]
+        n = len(Krows)
+        for src, host in ((Krows, self.K), (Vrows, self.V)):
+            cur = host[(b, g)]
+            if cur.shape[0] < start + n:
+                grown = np.zeros((start + n, self.d), np.float32)
+                grown[:cur.shape[0]] = cur
+                host[(b, g)] = grown
+            host[(b, g)][start:start + n] = src
+        self.Kd[b, g, start:start + n] = torch.from_numpy(np.ascontiguousarray(Krows)).to(self.Kd.device, dt)
+        self.Vd[b, g, start:start + n] = torch.from_numpy(np.ascontiguousarray(Vrows)).to(self.Vd.device, dt)
+
+    def tree(self, levels=None, chunk=None, refs=None):
+        cfg = self.cfg
+        t = Tree(self.B, self.Hkv, self.Hq, self.d, chunk or cfg.chunk, levels or cfg.levels, cfg.n_refs, self.T,
+                 TORCH_DT[cfg.dtype])
+        t.build(self.Kd, self.refs_d if refs is None else refs, self.lens)
+        return t
+
+    def unit_q(self, t, b, g, scale=1.0):
+        return self.q[t, b, g * self.G:(g + 1) * self.G].astype(np.float64) * scale
+
+    def unit_kv(self, b, g):
+        n = self.lens[b]
+        return self.K[(b, g)][:n], self.V[(b, g)][:n]
+
+
+# ----------------------------------------------------------------------------- build
+
+def check_build(case: Case, tree: Tree, sample=None, seed=0):
+    """Checks stored planes against the oracle.  sample: nodes per (unit, level) or None for all."""
+    cfg = case.cfg
+    rel, floor = m_tol(cfg.dtype)
+    rng = np.random.default_rng(seed)
+    worst_m, worst_b, n_checked = 0.0, 0.0, 0
+    for l in range(1, tree.L + 1):
+        m_d, b_d = tree.level(l)
+        for b in range(case.B):
+            N = case.lens[b]
+            n_l = oracle.level_nodes(N, tree.C, l)
+            if n_l == 0:
+                continue
+            nodes = np.arange(n_l)
+            if sample is not None and n_l > sample:
+                nodes = np.unique(np.concatenate([[0, n_l - 1], rng.choice(n_l, sample - 2, replace=False)]))
+            for g in range(case.Hkv):
+                u = b * case.Hkv + g
+                Ku, _ = case.unit_kv(b, g)
+                mg = m_d[u, torch.from_numpy(nodes).to(m_d.device)].float().cpu().numpy().astype(np.float64)
+                bg = b_d[u, torch.from_numpy(nodes).to(b_d.device)].cpu().numpy().astype(np.float64)
+                refs = case.refs[g].astype(np.float64)
+                for i, j in enumerate(nodes):
+                    t0 = j * tree.C ** l
+                    t1 = min((j + 1) * tree.C ** l, (N // tree.C) * tree.C)
+                    m_o, _, lse_o = oracle.node_planes(Ku, t0, t1, refs)
+                    err_m = np.abs(mg[i] - m_o) - (rel * np.abs(m_o) + floor)
+                    assert err_m.max() <= 0, f"m level {l} unit {u} node {j}: excess {err_m.max():.3e}"
+                    plane_at_r = bg[i] + np.einsum("rd,rd->r", refs, mg[i])
+                    err_b = np.abs(plane_at_r - lse_o) / np.maximum(1.0, np.abs(lse_o))
+                    assert err_b.max() <= PLANE_TOL, f"b level {l} unit {u} node {j}: rel {err_b.max():.3e}"
+                    worst_m = max(worst_m, float(np.max(np.abs(mg[i] - m_o))))
+                    worst_b = max(worst_b, float(err_b.max()))
+                    n_checked += 1
+    return dict(nodes=n_checked, worst_m_abs=worst_m, worst_plane_rel=worst_b)
+
+
+# ----------------------------------------------------------------------------- route
+
+def ambiguous(F, w, order, csum, kstar, p):
+    """Node ids whose keep/drop decision is within the parity margin of the boundary."""
+    amb = set()
+    n = len(F)
+    if kstar <= 0 or kstar >= n or p >= 1.0:
+        return amb
+    with np.errstate(divide="ignore"):
+        lw = np.log(w)
+    bk, bk1 = order[kstar - 1], order[kstar]
+    for pos in (bk, bk1):
+        near = np.abs(lw - lw[pos]) < AMBIG
+        amb.update(F[near].tolist())
+    W = csum[-1]
+    c_prev = csum[kstar - 2] / W if kstar >= 2 else -np.inf
+    c_at = csum[kstar - 1] / W
+    if min(abs(c_prev - p), abs(c_at - p)) < AMBIG:
+        amb.update([int(F[bk]), int(F[bk1])])
+    return amb
+
+
+def check_route(case: Case, tree: Tree, t: int, p: float, scale=1.0, units=None):
+    """Teacher-forced route parity at every level.  Returns per-level stats."""
+    stats = {}
+    levels = {}
+    for l in range(tree.L, 0, -1):
+        nf, nk, ids = tree.route_level(l)
+        levels[l] = (nf.cpu().numpy(), nk.cpu().numpy(), ids)
+    planes = {}
+    for l in range(tree.L, 0, -1):
+        m_d, b_d = tree.level(l)
+        planes[l] = (m_d, b_d)
+    n_amb = 0
+    for b in range(case.B):
+        N = case.lens[b]
+        for g in range(case.Hkv):
+            u = b * case.Hkv + g
+            if units is not None and u not in units:
+                continue
+            q = case.unit_q(t, b, g, scale)
+            for l in range(tree.L, 0, -1):
+                nf, nk, ids = levels[l]
+                n_l = oracle.level_nodes(N, tree.C, l)
+                if l == tree.L:
+                    F = np.arange(n_l, dtype=np.int32)
+                else:
+                    nfp, nkp, idsp = levels[l + 1]
+                    parent = idsp[u, :nkp[u]].cpu().numpy()
+                    F = oracle.expand(parent, tree.C, n_l)
+                assert nf[u] == len(F), f"unit {u} level {l}: frontier {nf[u]} != {len(F)}"
+                gpu = ids[u, :nk[u]].cpu().numpy()
+                assert np.all(np.diff(gpu) > 0), f"unit {u} level {l}: kept ids not ascending"
+                if len(F) == 0:
+                    assert nk[u] == 0
+                    continue
+                m_d, b_d = planes[l]
+                Fi = torch.from_numpy(F.astype(np.int64)).to(m_d.device)
+                mF = m_d[u, Fi].float().cpu().numpy().astype(np.float64)
+                bF = b_d[u, Fi].cpu().numpy().astype(np.float64)
+                kept_pos, w, order, csum = oracle.select(mF, bF, q, np.arange(len(F), dtype=np.int32), p)
+                want = set(F[kept_pos].tolist())
+                got = set(gpu.tolist())
+                diff = want ^ got
+                if diff:
+                    amb = ambiguous(F, w, order, csum, len(kept_pos), p)
+                    bad = diff - amb
+                    assert not bad, (f"unit {u} level {l}: {len(bad)} non-ambiguous differences, e.g. "
+                                     f"{sorted(bad)[:5]} (|F|={len(F)}, oracle k={len(want)}, gpu k={len(got)})")
+                    n_amb += len(diff)
+                s = stats.setdefault(l, [0, 0])
+                s[0] += len(F)
+                s[1] += len(got)
+    return dict(levels={l: tuple(v) for l, v in stats.items()}, ambiguous=n_amb)
+
+
+# ----------------------------------------------------------------------------- attend
+
+def check_attend(case: Case, tree: Tree, out, lse, t: int, scale=1.0, units=None):
+    _, nk, ids = tree.route_level(1)
+    nk = nk.cpu().numpy()
+    out = out.cpu().numpy()
+    lse = lse.cpu().numpy()
+    worst_o, worst_l, kappa = 0.0, 0.0, []
+    for b in range(case.B):
+        N = case.lens[b]
+        for g in range(case.Hkv):
+            u = b * case.Hkv + g
+            if units is not None and u not in units:
+                continue
+            kept = ids[u, :nk[u]].cpu().numpy()
+            S = oracle.attend_set(N, tree.C, kept)
+            Ku, Vu = case.unit_kv(b, g)
+            o_o, l_o = oracle.attend(case.unit_q(t, b, g, scale), Ku, Vu, S)
+            hs = slice(g * case.G, (g + 1) * case.G)
+            eo = float(np.max(np.abs(out[b, hs] - o_o)))
+            el = float(np.max(np.abs(lse[b, hs] - l_o)))
+            assert eo <= OUT_TOL, f"unit {u}: out err {eo:.3e}"
+            assert el <= LSE_TOL, f"unit {u}: lse err {el:.3e}"
+            worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+            kappa.append(len(S) / N)
+    return dict(worst_out=worst_o, worst_lse=worst_l, kappa=float(np.mean(kappa)) if kappa else 0.0)
+
+
+def check_dense(case: Case, t: int, scale=1.0, units=None):
+    out, lse = dense_decode(case.qd[t], case.Kd, case.Vd, case.lens, case.Hkv, scale)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    worst = 0.0
+    for b in range(case.B):
+        for g in range(case.Hkv):
+            u = b * case.Hkv + g
+            if units is not None and u not in units:
+                continue
+            Ku, Vu = case.unit_kv(b, g)
+            o_o, l_o = oracle.attend(case.unit_q(t, b, g, scale), Ku, Vu, np.arange(case.lens[b]))
+            hs = slice(g * case.G, (g + 1) * case.G)
+            eo = float(np.max(np.abs(out[b, hs] - o_o)))
+            el = float(np.max(np.abs(lse[b, hs] - l_o)))
+            assert eo <= OUT_TOL and el <= LSE_TOL, f"dense unit {u}: out {eo:.3e} lse {el:.3e}"
+            worst = max(worst, eo)
+    return worst
+
+
+def route_attend(case: Case, tree: Tree, t: int, p: float, scale=1.0):
+    tree.route(case.qd[t], p, scale)
+    out, lse = tree.attend(case.qd[t], case.Kd, case.Vd, scale)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def full_check(case: Case, tree: Tree, t: int, p: float, scale=1.0, units=None):
+    out, lse = route_attend(case, tree, t, p, scale)
+    r = check_route(case, tree, t, p, scale, units)
+    a = check_attend(case, tree, out, lse, t, scale, units)
+    return r, a

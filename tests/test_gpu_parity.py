@@ -1,0 +1,251 @@
+"""HIP path against the fp64 oracle through the C ABI (needs a gfx950 GPU).
+
+Each test prints the case it is about to run before touching the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import zha_inputs as zi
+from parity import Case, check_attend, check_build, check_dense, check_route, full_check, route_attend
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def small(name="deep_256k", **kw):
+    return zi.get_config(name, **kw)
+
+
+# --------------------------------------------------------------------------- tiny workload, everything
+
+def test_tiny_deep_f32_every_query():
+    cfg = zi.get_config("tiny_deep_f32")
+    say("case tiny_deep_f32: N=4096 d=64 C=4 L=3 R=4 fp32, 8 queries")
+    case = Case(cfg, n_queries=cfg.n_queries)
+    tree = case.tree()
+    torch.cuda.synchronize()
+    say(" build", check_build(case, tree))
+    for t in range(cfg.n_queries):
+        r, a = full_check(case, tree, t, 0.95)
+        say(f" t={t}", r, a)
+    say(" dense", check_dense(case, 0))
+
+
+# --------------------------------------------------------------------------- shape variants, ragged tails
+
+VARIANTS = [
+    # (label, config overrides, lengths)
+    ("bf16 d128 C4 L3 R16 G8 B2", dict(batch=2, n_tokens=5000, chunk=4, levels=3, n_refs=16), [5000, 3333]),
+    ("bf16 d64 C4 L2 R4 G4", dict(batch=1, n_tokens=2051, head_dim=64, n_q_heads=16, n_kv_heads=4, chunk=4, levels=2,
+                                  n_refs=4), [2051]),
+    ("f32 d128 C3 L3 R8 G2", dict(batch=1, n_tokens=1000, n_q_heads=8, n_kv_heads=4, chunk=3, levels=3, n_refs=8,
+                                  dtype="f32"), [1000]),
+    ("bf16 d128 C5 L2 R2 G16", dict(batch=1, n_tokens=777, n_q_heads=16, n_kv_heads=1, chunk=5, levels=2, n_refs=2),
+     [777]),
+    ("bf16 d64 C16 L2 R1 G1 B3", dict(batch=3, n_tokens=4109, head_dim=64, n_q_heads=2, n_kv_heads=2, chunk=16,
+                                      levels=2, n_refs=1), [4109, 300, 17]),
+    ("bf16 d128 wide C256 L1 R16", dict(batch=1, n_tokens=16484, chunk=256, levels=1, n_refs=16), [16484]),
+    ("f32 d64 C4 L4 R16 G1", dict(batch=1, n_tokens=3000, head_dim=64, n_q_heads=1, n_kv_heads=1, chunk=4, levels=4,
+                                  n_refs=16, dtype="f32", head_scale=False), [3000]),
+]
+
+
+@pytest.mark.parametrize("label,kw,lens", VARIANTS, ids=[v[0] for v in VARIANTS])
+def test_variants(label, kw, lens):
+    cfg = small(**kw, n_queries=4, needles_per_unit=4)
+    say(f"case {label}: lens={lens}")
+    case = Case(cfg, lens=lens, n_queries=2)
+    tree = case.tree()
+    torch.cuda.synchronize()
+    say(" build", check_build(case, tree))
+    for t in range(2):
+        for p in (0.5, 0.9):
+            r, a = full_check(case, tree, t, p)
+            say(f" t={t} p={p}", r, a)
+    say(" dense", check_dense(case, 0))
+
+
+# --------------------------------------------------------------------------- edge cases
+
+def test_short_sequences_no_tree():
+    """N < C: no complete chunk, no tree; S = [0, N): attention equals dense."""
+    cfg = small(batch=4, n_tokens=40, chunk=16, levels=2, n_refs=4, n_queries=2, needles_per_unit=2)
+    lens = [1, 3, 15, 16]
+    say(f"case short sequences lens={lens} C=16")
+    case = Case(cfg, lens=lens)
+    tree = case.tree()
+    out, lse = route_attend(case, tree, 0, 0.9)
+    r = check_route(case, tree, 0, 0.9)
+    a = check_attend(case, tree, out, lse, 0)
+    _, nk, _ = tree.route_level(1)
+    assert nk.cpu().tolist()[:12] == [0] * 12  # batch entries 0..2 have no complete chunk
+    say(" ", r, a)
+
+
+def test_p_extremes():
+    cfg = small(batch=1, n_tokens=4096 + 7, chunk=4, levels=3, n_refs=16, n_queries=2, needles_per_unit=4)
+    say("case p extremes: N=4103 C=4 L=3 R=16")
+    case = Case(cfg)
+    tree = case.tree()
+    # p = 1 keeps every node; the sparse output equals dense attention
+    out, lse = route_attend(case, tree, 0, 1.0)
+    for l in range(1, tree.L + 1):
+        nf, nk, ids = tree.route_level(l)
+        n_l = oracle.level_nodes(case.lens[0], tree.C, l)
+        assert nk.cpu().tolist() == [n_l] * case.Hkv
+        assert torch.equal(ids[:, :n_l].cpu(), torch.arange(n_l, dtype=torch.int32).repeat(case.Hkv, 1))
+    a = check_attend(case, tree, out, lse, 0)
+    assert abs(a["kappa"] - 1.0) < 1e-12
+    check_dense(case, 0)
+    # tiny p keeps one node per level: the heaviest
+    r, a = full_check(case, tree, 1, 1e-6)
+    for l, (nF, nK) in r["levels"].items():
+        assert nK == case.Hkv, (l, nK)
+    say(" ", r, a)
+
+
+def test_determinism():
+    """Two trees built and routed from the same inputs agree bit for bit."""
+    cfg = small(batch=2, n_tokens=9000, chunk=4, levels=4, n_refs=16, n_queries=2, needles_per_unit=8)
+    say("case determinism: B=2 N=9000 C=4 L=4 R=16")
+    case = Case(cfg)
+    tree = case.tree()
+    o1, l1 = route_attend(case, tree, 0, 0.9)
+    o1, l1 = o1.clone(), l1.clone()
+    tree2 = case.tree()
+    o2, l2 = route_attend(case, tree2, 0, 0.9)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for l in range(1, 5):
+        m1, b1 = tree.level(l)
+        m2, b2 = tree2.level(l)
+        n_l = oracle.level_nodes(case.lens[0], tree.C, l)
+        assert torch.equal(m1[:, :n_l].view(torch.int16), m2[:, :n_l].view(torch.int16))
+        assert torch.equal(b1[:, :n_l], b2[:, :n_l])
+        nf1, nk1, i1 = tree.route_level(l)
+        nf2, nk2, i2 = tree2.route_level(l)
+        assert torch.equal(nf1, nf2) and torch.equal(nk1, nk2)
+        for u in range(case.B * case.Hkv):
+            assert torch.equal(i1[u, :nk1[u]], i2[u, :nk2[u]])
+
+
+# --------------------------------------------------------------------------- growth
+
+def _valid_equal(case, t_inc, t_full):
+    for l in range(1, t_inc.L + 1):
+        m1, b1 = t_inc.level(l)
+        m2, b2 = t_full.level(l)
+        for b in range(case.B):
+            n_l = oracle.level_nodes(case.lens[b], t_inc.C, l)
+            for g in range(case.Hkv):
+                u = b * case.Hkv + g
+                x1, x2 = m1[u, :n_l], m2[u, :n_l]
+                if x1.dtype == torch.bfloat16:
+                    x1, x2 = x1.view(torch.int16), x2.view(torch.int16)
+                assert torch.equal(x1, x2), f"m level {l} unit {u}"
+                assert torch.equal(b1[u, :n_l], b2[u, :n_l]), f"b level {l} unit {u}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_append_equals_rebuild(dtype):
+    cfg = small(batch=2, n_tokens=1200, chunk=4, levels=4, n_refs=8, n_q_heads=8, n_kv_heads=2, n_queries=2,
+                needles_per_unit=4, append_steps=400, dtype=dtype)
+    say(f"case append == rebuild ({dtype}): B=2 N=1200 +400 C=4 L=4 R=8")
+    case = Case(cfg, lens=[1200, 1001], max_tokens=1700)
+    rows = {(b, g): zi.append_rows(cfg, b, g) for b in range(2) for g in range(2)}
+    tree = case.tree()
+    lens = list(case.lens)
+    schedule = [1] * 37 + [5, 64, 3, 200] + [1] * 20
+    done = 0
+    for k in schedule:
+        for b in range(2):
+            for g in range(2):
+                Kr, Vr = rows[(b, g)]
+                case.add_rows(b, g, lens[b], Kr[done:done + k], Vr[done:done + k])
+        lens = [n + k for n in lens]
+        tree.append(case.Kd, lens)
+        done += k
+    case.lens = lens
+    full = case.tree()
+    torch.cuda.synchronize()
+    _valid_equal(case, tree, full)
+    say(" bitwise equal after", len(schedule), "appends; lens", lens)
+    say(" build", check_build(case, tree, sample=64))
+    r, a = full_check(case, tree, 0, 0.9)
+    say(" ", r, a)
+
+
+def test_batched_append_p_sweep():
+    """Batched decode with growth, routing at several p per step (reduced sizes)."""
+    cfg = small("batch8_append_512k", n_tokens=8192, append_steps=64, n_queries=64)
+    say("case batched append: B=8 N=8192 +64 C=4 L=6 R=4, p in {0.7, 0.9, 0.99}")
+    case = Case(cfg, n_queries=64, max_tokens=8192 + 64)
+    rows = {(b, g): zi.append_rows(cfg, b, g) for b in range(cfg.batch) for g in range(cfg.n_kv_heads)}
+    tree = case.tree()
+    lens = list(case.lens)
+    for step in range(64):
+        for b in range(cfg.batch):
+            for g in range(cfg.n_kv_heads):
+                Kr, Vr = rows[(b, g)]
+                case.add_rows(b, g, lens[b], Kr[step:step + 1], Vr[step:step + 1])
+        lens = [n + 1 for n in lens]
+        tree.append(case.Kd, lens)
+        case.lens = lens
+        for p in cfg.p:
+            if step in (0, 1, 2, 3, 31, 63):
+                r, a = full_check(case, tree, step, p, units={0, 5, 17, 31})
+                say(f" step {step} p={p}", r["levels"].get(1), r["ambiguous"], a)
+            else:
+                route_attend(case, tree, step, p)
+    full = case.tree()
+    torch.cuda.synchronize()
+    _valid_equal(case, tree, full)
+    say(" bitwise equal to rebuild after 64 steps")
+
+
+# --------------------------------------------------------------------------- full-size workloads
+
+@pytest.mark.slow
+def test_deep_256k_full():
+    cfg = zi.get_config("deep_256k")
+    say("case deep_256k full: N=262144, 32q/4kv, d=128, C=4 L=6 R=16 p=0.95")
+    case = Case(cfg, n_queries=2)
+    tree = case.tree()
+    torch.cuda.synchronize()
+    say(" build", check_build(case, tree, sample=24))
+    for t in range(2):
+        r, a = full_check(case, tree, t, 0.95)
+        say(f" t={t}", r, a)
+    say(" dense", check_dense(case, 0))
+
+
+@pytest.mark.slow
+def test_wide_256k_full():
+    cfg = zi.get_config("wide_256k")
+    say("case wide_256k full: N=262144, 32q/4kv, d=128, C=256 L=1 R=16 p=0.95")
+    case = Case(cfg, n_queries=2)
+    tree = case.tree()
+    torch.cuda.synchronize()
+    say(" build", check_build(case, tree, sample=48))
+    for t in range(2):
+        r, a = full_check(case, tree, t, 0.95)
+        say(f" t={t}", r, a)
+
+
+@pytest.mark.slow
+def test_deep_1m_full():
+    cfg = zi.get_config("deep_1m")
+    say("case deep_1m full: N=1048576, 32q/4kv, d=128, C=4 L=7 R=16 p=0.95")
+    case = Case(cfg, n_queries=1)
+    tree = case.tree()
+    torch.cuda.synchronize()
+    say(" build", check_build(case, tree, sample=12))
+    r, a = full_check(case, tree, 0, 0.95, units={0, 3})
+    say(" t=0", r, a)
