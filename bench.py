@@ -1,0 +1,292 @@
+"""Decode-step benchmark of the ZHA path on one MI355X.
+
+One step = one decode step of one attention layer: route the B x Hq queries
+through that layer's tree (every level) and attend over the kept chunks plus
+sink and tail.  Inputs are resident in HBM before timing; steps cycle through
+`--layers` replicas of (K, V, tree) so every step reads its layer cold, and
+through `--queries` different decode queries.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps 40] [--warmup 5] [--config deep_256k]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "ZHA decode µs/step/layer at 256K & 1M ctx; achieved HBM GB/s vs peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="deep_256k")
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--queries", type=int, default=8)
+    ap.add_argument("--p", type=float, default=None)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cpu-queries", type=int, default=12)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha(name: str) -> str:
+    path = os.path.join(ROOT, "hierarchical_tree_indexed_02_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(workload: str):
+    """HBM traffic per launch of the dominant kernel from the committed counter summary,
+    or None when there is none or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"score_level1_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path, encoding="utf-8").read()
+    m_sha = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", txt)
+    m_tr = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m_sha or not m_tr or m_sha.group(1) != kernel_sha("zha_route.hip"):
+        return None
+    return float(m_tr.group(1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path would shard by (sequence, KV head) with no exchange, see DESIGN.md", flush=True)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import zha_inputs as zi
+    from hierarchical_tree_indexed_02_amd import zha
+    from hierarchical_tree_indexed_02_amd.runtime import Tree, dense_decode
+
+    cfg = zi.get_config(args.config)
+    p = args.p if args.p is not None else cfg.p[0]
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    es = 2 if cfg.dtype == "bf16" else 4
+    B, Hkv, Hq, d, N = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim, cfg.n_tokens
+    U, G, C, L, R = B * Hkv, cfg.group, cfg.chunk, cfg.levels, cfg.n_refs
+    T = N
+    nq = min(args.queries, cfg.n_queries)
+
+    t0 = time.time()
+    q_host = zi.queries(cfg, n=nq)
+    K0 = torch.empty((B, Hkv, T, d), dtype=dt, device=dev)
+    V0 = torch.empty((B, Hkv, T, d), dtype=dt, device=dev)
+    for b in range(B):
+        for g in range(Hkv):
+            Ku, Vu = zi.unit_kv(cfg, b, g)
+            K0[b, g] = torch.from_numpy(Ku).to(dev, dt)
+            V0[b, g] = torch.from_numpy(Vu).to(dev, dt)
+    qd = torch.from_numpy(q_host).to(dev, dt)
+    refs = torch.from_numpy(zi.refs(cfg)).to(dev)
+    log(f"inputs ready in {time.time() - t0:.1f}s")
+
+    lens = [N] * B
+    Ks, Vs, trees = [K0], [V0], []
+    for _ in range(1, args.layers):
+        Ks.append(K0.clone())
+        Vs.append(V0.clone())
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    build_ms = []
+    for li in range(args.layers):
+        tr = Tree(B, Hkv, Hq, d, C, L, R, T, dt)
+        torch.cuda.synchronize()
+        ev0.record()
+        tr.build(Ks[li], refs, lens)
+        ev1.record()
+        torch.cuda.synchronize()
+        build_ms.append(ev0.elapsed_time(ev1))
+        trees.append(tr)
+    tree_bytes = trees[0].bytes()
+    log(f"trees built: {build_ms} ms; tree+workspace {tree_bytes / 1e9:.2f} GB per layer")
+
+    # a copy kernel of known size, for calibrating hardware byte counters in profiles
+    cal_n16 = (256 << 20) // 16
+    cal_src = torch.empty(cal_n16 * 16, dtype=torch.uint8, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    zha.zha_calibration_copy(cal_dst, cal_src, cal_n16)
+    torch.cuda.synchronize()
+    del cal_src, cal_dst
+
+    outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(args.layers)]
+    lses = [torch.empty((B, Hq), dtype=torch.float32, device=dev) for _ in range(args.layers)]
+
+    def step(i):
+        li, t = i % args.layers, i % nq
+        tr = trees[li]
+        tr.route(qd[t], p, 1.0)
+        tr.attend(qd[t], Ks[li], Vs[li], 1.0, out=outs[li], lse=lses[li])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    for tr in trees:
+        tr.timing(True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    recs = []
+    for tr in trees:
+        recs += tr.timing_read()
+        tr.timing(False)
+
+    # per-kernel durations over the timed region
+    per = {}
+    for k, l, ms in recs:
+        per.setdefault((k, l), []).append(ms)
+    kernels = {f"{zha.KERNEL_NAMES[k]}{'_l' + str(l) if l else ''}": dict(launches=len(v), avg_us=1e3 * sum(v) / len(v),
+                                                                          total_ms=sum(v))
+               for (k, l), v in sorted(per.items())}
+
+    # algorithmic bytes of each step (routes are deterministic: replay each query once, untimed)
+    S_node = R * (d * es + 4)
+    fr_tot = {l: 0 for l in range(1, L + 1)}
+    kept_tot = {l: 0 for l in range(1, L + 1)}
+    attend_tok = 0
+    steps_q = [i % nq for i in range(args.steps)]
+    for t in sorted(set(steps_q)):
+        w = steps_q.count(t)
+        trees[0].route(qd[t], p, 1.0)
+        torch.cuda.synchronize()
+        for l in range(1, L + 1):
+            nf, nk, ids = trees[0].route_level(l)
+            fr_tot[l] += w * int(nf.sum())
+            kept_tot[l] += w * int(nk.sum())
+            if l == 1:
+                nk1 = nk.cpu().numpy()
+                first = ids[:, 0].cpu().numpy()
+                Nc = (N // C) * C
+                for u in range(U):
+                    sink = 1 if (Nc > 0 and (nk1[u] == 0 or first[u] != 0)) else 0
+                    attend_tok += w * (sink + (N - Nc) + int(nk1[u]) * C)
+    nsteps = args.steps
+    route_bytes = sum(fr_tot[l] for l in fr_tot) * S_node / nsteps
+    attend_bytes = attend_tok * 2 * d * es / nsteps
+    io_bytes = B * Hq * d * es + B * Hq * (d + 1) * 4 + 8 * sum(kept_tot.values()) / nsteps
+    step_bytes = route_bytes + attend_bytes + io_bytes
+    kappa = attend_tok / nsteps / (U * N)
+    dense_bytes = U * N * 2 * d * es
+
+    # the dominant kernel: largest share of time in the timed region
+    dom = max(kernels.items(), key=lambda kv: kv[1]["total_ms"])
+    dom_name = dom[0]
+    if dom_name.startswith("score_l"):
+        l = int(dom_name.split("_l")[1])
+        dom_bytes = fr_tot[l] / nsteps * (S_node + G * 4) + B * Hq * d * es + (fr_tot[l] / nsteps / C * 4 if l < L else 0)
+        traffic = committed_traffic(args.config) if l == 1 else None
+    elif dom_name == "attend":
+        dom_bytes = attend_bytes + B * Hq * d * es
+        traffic = None
+    else:
+        dom_bytes = None
+        traffic = None
+    dom_avg_s = dom[1]["avg_us"] * 1e-6
+    achieved = dom_bytes / dom_avg_s / 1e9 if dom_bytes else None
+    roofline = dict(kernel=f"zha_score_kernel (level {dom_name.split('_l')[1]})" if dom_name.startswith("score_l")
+                    else dom_name,
+                    bound="hbm", achieved=round(achieved, 1) if achieved else None, peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBS, 4) if achieved else None,
+                    traffic=traffic, bytes_per_launch=round(dom_bytes) if dom_bytes else None,
+                    avg_launch_us=round(dom[1]["avg_us"], 2))
+    log(f"step {ms_step * 1e3:.1f} us, {step_bytes / 1e6:.1f} MB/step ({step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s), "
+        f"kappa {kappa:.3f}")
+    for k, v in kernels.items():
+        log(f"  {k:12s} {v['launches']:4d} launches  avg {v['avg_us']:8.2f} us")
+
+    # dense decode on the same GPU and inputs, same protocol
+    dense_us = None
+    if not args.no_dense:
+        nb = zha.zha_dense_workspace_bytes(B, Hq, Hkv, d, T)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        for i in range(args.warmup):
+            li = i % args.layers
+            dense_decode(qd[i % nq], Ks[li], Vs[li], lens, Hkv, 1.0, ws, outs[li], lses[li])
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(args.steps):
+            li = i % args.layers
+            dense_decode(qd[i % nq], Ks[li], Vs[li], lens, Hkv, 1.0, ws, outs[li], lses[li])
+        ev1.record()
+        torch.cuda.synchronize()
+        dense_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
+        log(f"dense {dense_us:.1f} us/step ({dense_bytes / (dense_us * 1e-6) / 1e9:.0f} GB/s)")
+
+    # the oracle on the host cores, on a bounded sample: one (sequence, KV head) unit
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        Ku, Vu = zi.unit_kv(cfg, 0, 0)
+        tree_o = oracle.tree_merge(Ku, zi.refs(cfg)[0], C, L)
+        ncpu = min(args.cpu_queries, cfg.n_queries)
+        qc = zi.queries(cfg, n=ncpu)
+        tc0 = time.time()
+        for t in range(ncpu):
+            qu = qc[t, 0, 0:G].astype(np.float64)
+            _, kept = oracle.route(tree_o, N, C, L, qu, p)
+            S = oracle.attend_set(N, C, kept[1])
+            oracle.attend(qu, Ku, Vu, S)
+        sec = time.time() - tc0
+        per_unit_step = sec / ncpu
+        cpu = dict(value=round(per_unit_step * U * 1e6, 1), unit="us/step/layer", cores=oracle.num_threads(),
+                   kind="oracle",
+                   sample=f"route+attend of unit (b=0, kv head 0) for {ncpu} queries ({sec:.1f} s), "
+                          f"scaled by {U} units to one full step; oracle tree built untimed")
+        log(f"cpu oracle {cpu['value']:.0f} us/step on {cpu['cores']} threads")
+
+    result = {
+        "metric": METRIC,
+        "value": round(ms_step * 1e3, 2),
+        "unit": "us/step/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded planted-needle keys/values, random reference queries)",
+        "config": {"workload": cfg.name, "batch": B, "context": N, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "chunk": C, "levels": L, "refs": R, "p": p, "layers_cycled": args.layers},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "dense_us_per_step": round(dense_us, 2) if dense_us else None,
+        "speedup_vs_dense": round(dense_us / (ms_step * 1e3), 3) if dense_us else None,
+        "step_bytes": round(step_bytes),
+        "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_frac_of_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "dense_bytes": dense_bytes,
+        "kappa": round(kappa, 4),
+        "frontier_per_unit": {l: round(fr_tot[l] / nsteps / U, 1) for l in range(L, 0, -1)},
+        "build_us": round(1e3 * float(np.median(build_ms)), 1),
+        "kernels": {k: dict(launches=v["launches"], avg_us=round(v["avg_us"], 2)) for k, v in kernels.items()},
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
