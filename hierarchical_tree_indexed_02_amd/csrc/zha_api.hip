@@ -9,6 +9,8 @@
 #include "zha_internal.h"
 
 int zha_score_wgs(const zha_tree* t, int level);
+int zha_compact_chunks(int64_t nodes);
+int zha_hist_bins();
 size_t zha_stack_bytes(int L, int d, int R);
 
 namespace {
@@ -35,6 +37,7 @@ zha_status check_desc(const zha_tree_desc* d) {
   if (d->n_q_heads / d->n_kv_heads > 16) return ZHA_ERR_UNSUPPORTED;
   if (d->levels > ZHA_MAX_LEVELS) return ZHA_ERR_UNSUPPORTED;
   if (d->max_tokens >= ((int64_t)1 << 31)) return ZHA_ERR_UNSUPPORTED;
+  if (d->max_tokens / d->chunk >= ((int64_t)1 << 30)) return ZHA_ERR_UNSUPPORTED;
   double span = pow((double)d->chunk, (double)d->levels);
   if (span > (double)(1 << 30)) return ZHA_ERR_UNSUPPORTED;
   if (zha_stack_bytes(d->levels, d->head_dim, d->n_refs) > 160 * 1024) return ZHA_ERR_UNSUPPORTED;
@@ -48,7 +51,9 @@ void free_tree(zha_tree* t) {
     if (t->b[l]) (void)hipFree(t->b[l]);
     if (t->kept[l]) (void)hipFree(t->kept[l]);
   }
-  void* ps[] = {t->refs, t->spine, t->counts, t->scores, t->spart, t->keys, t->apart};
+  void* ps[] = {t->refs,   t->spine,  t->counts,    t->scores,   t->spart,    t->keys,     t->apart,
+                t->fh_cnt, t->fh_mass,  t->fh_edge,  t->cut,      t->lb_status,
+                t->lb_epoch, t->last_pos, t->lb_error};
   for (void* p : ps)
     if (p) (void)hipFree(p);
   for (int i = 0; i < 2 * ZHA_MAX_TIMING; ++i)
@@ -138,7 +143,7 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   t->cap[0] = 0;
   const int U = t->U, R = t->R, d = t->d, G = t->G, L = t->L;
   int ws = 4096 / U;
-  if (ws > 1024) ws = 1024;
+  if (ws > 512) ws = 512;
   if (ws < 1) ws = 1;
   t->WS = ws;
   t->WA = zha_dense_wgs(U);
@@ -153,8 +158,30 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   ok = ok && dalloc(t, &t->counts, (size_t)2 * (L + 2) * U * sizeof(int32_t));
   ok = ok && dalloc(t, &t->scores, (size_t)U * t->cap[1] * G * sizeof(float));
   ok = ok && dalloc(t, &t->spart, (size_t)U * t->WS * G * 2 * sizeof(float));
-  ok = ok && dalloc(t, &t->keys, (size_t)U * t->cap[1] * sizeof(uint32_t));
+  t->kstride = (t->cap[1] + 3) / 4 * 4;
+  ok = ok && dalloc(t, &t->keys, (size_t)U * t->kstride * sizeof(uint32_t));
   ok = ok && dalloc(t, &t->apart, (size_t)U * t->WA * G * (d + 2) * sizeof(float));
+  const int nchunk = zha_compact_chunks(t->cap[1]);
+  const int nb = zha_hist_bins();
+  ok = ok && dalloc(t, &t->fh_cnt, (size_t)U * nb * sizeof(uint32_t));
+  ok = ok && dalloc(t, &t->fh_mass, (size_t)U * nb * sizeof(unsigned long long));
+  ok = ok && dalloc(t, &t->fh_edge, (size_t)U * 2 * sizeof(unsigned long long));
+  ok = ok && dalloc(t, &t->cut, (size_t)U * 4 * sizeof(int32_t));
+  ok = ok && dalloc(t, &t->lb_status, (size_t)U * nchunk * sizeof(unsigned long long));
+  ok = ok && dalloc(t, &t->lb_epoch, 2 * sizeof(uint32_t));
+  ok = ok && dalloc(t, &t->last_pos, (size_t)U * sizeof(int32_t));
+  ok = ok && dalloc(t, &t->lb_error, sizeof(int32_t));
+  if (ok) {  // counters and histograms start at zero and are left at zero by the kernels
+    ok = hipMemset(t->fh_cnt, 0, (size_t)U * nb * sizeof(uint32_t)) == hipSuccess &&
+         hipMemset(t->fh_mass, 0, (size_t)U * nb * sizeof(unsigned long long)) == hipSuccess &&
+         hipMemset(t->fh_edge, 0, (size_t)U * 2 * sizeof(unsigned long long)) == hipSuccess &&
+         hipMemset(t->lb_status, 0, (size_t)U * nchunk * sizeof(unsigned long long)) == hipSuccess &&
+         hipMemset(t->last_pos, 0xFF, (size_t)U * sizeof(int32_t)) == hipSuccess &&
+         hipMemset(t->lb_error, 0, sizeof(int32_t)) == hipSuccess;
+    const uint32_t ep[2] = {1u, 0u};  // status words of epoch 0 (all-zero memory) never match
+    ok = ok && hipMemcpy(t->lb_epoch, ep, sizeof(ep), hipMemcpyHostToDevice) == hipSuccess;
+    ok = ok && hipDeviceSynchronize() == hipSuccess;
+  }
   if (!ok) {
     free_tree(t);
     return ZHA_ERR_NOMEM;

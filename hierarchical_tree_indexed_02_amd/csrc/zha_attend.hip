@@ -26,8 +26,8 @@ struct AttArgs {
   const int32_t* kept;     // [U][cap1] level-1 kept chunk ids (sparse only)
   const int32_t* kept_count;
   int64_t cap1;
-  float* part;             // [U][W][G][d+2]: o (unnormalised), max (log2 units), sum
-  int W;
+  float* part;             // o [U][W][G][d] (unnormalised), then (max in log2 units, sum) [U][W][G][2]
+  int W, U;
   int Hkv, Hq, G, C, Cshift;
   int64_t T;               // token stride of K/V
   float scale_log2;        // scale * log2(e)
@@ -274,7 +274,9 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a) {
     for (int jj = 0; jj < 4; ++jj) so[(wave * 16 + row) * D + dt * 16 + 4 * grp + jj] = o[dt][jj];
   if (grp == 0) { sm[wave * 16 + row] = mrun; sl[wave * 16 + row] = lrun; }
   __syncthreads();
-  float* out = a.part + ((int64_t)u * a.W + blockIdx.x) * G * (D + 2);
+  const int64_t rec = ((int64_t)u * a.W + blockIdx.x) * G;  // first (unit, workgroup, head) record
+  float* po = a.part + rec * D;
+  float* pml = a.part + (int64_t)a.U * a.W * G * D + rec * 2;
   for (int i = threadIdx.x; i < G * D; i += 256) {
     const int h = i / D, dd = i % D;
     float Mx = -INFINITY;
@@ -287,35 +289,80 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a) {
         l += f * sl[w * 16 + h];
       }
     }
-    out[h * (D + 2) + dd] = acc;
+    po[h * D + dd] = acc;
     if (dd == 0) {
-      out[h * (D + 2) + D] = Mx;
-      out[h * (D + 2) + D + 1] = l;
+      pml[h * 2] = Mx;
+      pml[h * 2 + 1] = l;
     }
   }
 }
 
-// Merges the W partials of each (unit, head) in workgroup order.
+// Merges the W partials of each (unit, head): the maximum first, then the scaled sums,
+// each thread summing a fixed subset of workgroups and the subsets combined in order.
+constexpr int MERGE_THREADS = 1024;
+constexpr int MERGE_BATCH = 4;
+
 template <int D>
-__global__ __launch_bounds__(D) void zha_merge_kernel(const float* part, int W, int G, int Hkv, int Hq, float* out,
-                                                      float* lse) {
-  const int h = blockIdx.x, u = blockIdx.y, dd = threadIdx.x;
+__global__ __launch_bounds__(MERGE_THREADS) void zha_merge_kernel(const float* part, int U, int W, int G, int Hkv,
+                                                                  int Hq, float* out, float* lse) {
+  constexpr int TPR = D / 4;                  // threads per record (4 floats each)
+  constexpr int NGRP = MERGE_THREADS / TPR;   // workgroup subsets
+  const int h = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int bi = u / Hkv, g = u % Hkv;
-  float Mx = -INFINITY, Lx = 0.0f, Ox = 0.0f;
-  for (int w = 0; w < W; ++w) {
-    const float* r = part + (((int64_t)u * W + w) * G + h) * (D + 2);
-    const float l = r[D + 1];
-    if (l == 0.0f) continue;
-    const float Mw = r[D];
-    const float nM = fmaxf(Mx, Mw);
-    const float f1 = zexp2(Mx - nM), f2 = zexp2(Mw - nM);
-    Lx = Lx * f1 + l * f2;
-    Ox = Ox * f1 + r[dd] * f2;
-    Mx = nM;
+  const float* po = part + ((int64_t)u * W * G + h) * D;                            // record w at po + w*G*D
+  const float* pml = part + (int64_t)U * W * G * D + ((int64_t)u * W * G + h) * 2;  // at pml + w*G*2
+  __shared__ float s_red[MERGE_THREADS / 64];
+  __shared__ float4 s_o[NGRP][TPR];
+  __shared__ float s_l[NGRP];
+  float mx = -INFINITY;
+  for (int w = tid; w < W; w += MERGE_THREADS) {
+    const float2 r = *(const float2*)(pml + (int64_t)w * G * 2);
+    if (r.y > 0.0f) mx = fmaxf(mx, r.x);
   }
-  const int64_t oh = (int64_t)bi * Hq + (int64_t)g * G + h;
-  out[oh * D + dd] = Ox / Lx;
-  if (dd == 0) lse[oh] = (Mx + zlog2(Lx)) * ZHA_LN2;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) s_red[wave] = mx;
+  __syncthreads();
+  float M = s_red[0];
+  for (int k = 1; k < MERGE_THREADS / 64; ++k) M = fmaxf(M, s_red[k]);
+  const int j = tid / TPR, c = tid % TPR;
+  float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float lsum = 0.0f;
+  for (int w0 = j; w0 < W; w0 += NGRP * MERGE_BATCH) {
+    float2 ml[MERGE_BATCH];
+    float4 v[MERGE_BATCH];
+#pragma unroll
+    for (int k = 0; k < MERGE_BATCH; ++k) {
+      const int w = w0 + k * NGRP;
+      ml[k] = w < W ? *(const float2*)(pml + (int64_t)w * G * 2) : make_float2(0.0f, 0.0f);
+      v[k] = w < W ? *(const float4*)(po + (int64_t)w * G * D + 4 * c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int k = 0; k < MERGE_BATCH; ++k) {
+      if (ml[k].y > 0.0f) {
+        const float f = zexp2(ml[k].x - M);
+        acc.x += f * v[k].x; acc.y += f * v[k].y; acc.z += f * v[k].z; acc.w += f * v[k].w;
+        lsum += f * ml[k].y;
+      }
+    }
+  }
+  s_o[j][c] = acc;
+  if (c == 0) s_l[j] = lsum;
+  __syncthreads();
+  if (tid < TPR) {
+    float4 o = s_o[0][tid];
+    float L = s_l[0];
+    for (int k = 1; k < NGRP; ++k) {
+      const float4 v = s_o[k][tid];
+      o.x += v.x; o.y += v.y; o.z += v.z; o.w += v.w;
+      L += s_l[k];
+    }
+    const int64_t oh = (int64_t)bi * Hq + (int64_t)g * G + h;
+    const float inv = 1.0f / L;
+    *(float4*)(out + oh * D + 4 * tid) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+    if (tid == 0) lse[oh] = (M + zlog2(L)) * ZHA_LN2;
+  }
 }
 
 template <typename T, int D, bool DENSE>
@@ -328,8 +375,8 @@ hipError_t launch_att(const AttArgs& a, int U, float* out, float* lse, hipStream
 
 template <int D>
 hipError_t launch_merge(const AttArgs& a, int U, float* out, float* lse, hipStream_t s) {
-  hipLaunchKernelGGL((zha_merge_kernel<D>), dim3(a.G, U), dim3(D), 0, s, (const float*)a.part, a.W, a.G, a.Hkv,
-                     a.Hq, out, lse);
+  hipLaunchKernelGGL((zha_merge_kernel<D>), dim3(a.G, U), dim3(MERGE_THREADS), 0, s, (const float*)a.part, U, a.W,
+                     a.G, a.Hkv, a.Hq, out, lse);
   return hipGetLastError();
 }
 
@@ -363,6 +410,7 @@ hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const vo
   a.cap1 = t->cap[1];
   a.part = t->apart;
   a.W = t->WA;
+  a.U = t->U;
   a.Hkv = t->desc.n_kv_heads;
   a.Hq = t->desc.n_q_heads;
   a.G = t->G;
@@ -392,6 +440,7 @@ hipError_t zha_launch_dense(const void* q, const void* K, const void* V, const Z
   a.cap1 = 0;
   a.part = part;
   a.W = WA;
+  a.U = B * Hkv;
   a.Hkv = Hkv;
   a.Hq = Hq;
   a.G = Hq / Hkv;

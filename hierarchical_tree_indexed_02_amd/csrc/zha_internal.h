@@ -6,7 +6,7 @@
 #include <stdint.h>
 #include <vector>
 
-#include "../../include/zha.h"
+#include "zha.h"
 
 // ----------------------------------------------------------------------------- device types
 
@@ -143,8 +143,17 @@ struct zha_tree {
   int32_t* counts;                  // [2][L+2][U]: frontier counts, kept counts per level
   float* scores;                    // [U][cap1][G]
   float* spart;                     // [U][WS][G][2] score-kernel partial log-sum-exp
-  uint32_t* keys;                   // [U][cap1]
-  float* apart;                     // [U][WA][G][d+2] attention partials
+  uint32_t* keys;                   // [U][kstride] node-mass keys of the level being selected
+  int64_t kstride;                  // cap1 rounded up to a multiple of 4
+  uint32_t* fh_cnt;                 // [U][1024] fine mass histogram (zero between levels)
+  unsigned long long* fh_mass;      // [U][1024]
+  unsigned long long* fh_edge;      // [U][2]
+  int32_t* cut;                     // [U][4] cut of the level being selected
+  unsigned long long* lb_status;    // [U][compaction chunks of level 1] look-back words
+  uint32_t* lb_epoch;               // [2] look-back epoch (starts at 1) and finished-workgroup count
+  int32_t* last_pos;                // [U] largest kept position (-1 between launches)
+  int32_t* lb_error;                // [1] set if a look-back wait ever gives up
+  float* apart;                     // attention partials: o [U][WA][G][d], then (max, sum) [U][WA][G][2]
   int WS, WA;                       // score and attention workgroups per unit (maximum)
   ZLens len;                        // current lengths
   ZLens len_prev;                   // lengths before the last zha_append

@@ -189,7 +189,7 @@ ZHA_API zha_status zha_route_copy_level(zha_tree_t tree, int32_t level, int32_t*
  * code (see ZHA_K_*), its level (0 when none) and its duration in ms, and
  * clears the record.  At most 256 launches are kept. */
 enum { ZHA_K_BUILD = 1, ZHA_K_APPEND = 2, ZHA_K_SCORE = 3, ZHA_K_SELECT = 4,
-       ZHA_K_ATTEND = 5, ZHA_K_MERGE = 6 };
+       ZHA_K_ATTEND = 5, ZHA_K_MERGE = 6, ZHA_K_MASS = 7, ZHA_K_COMPACT = 8 };
 ZHA_API zha_status zha_timing_enable(zha_tree_t tree, int32_t enable);
 ZHA_API zha_status zha_timing_read(zha_tree_t tree, int32_t* kernels, int32_t* levels, float* ms,
                            int32_t max_entries, int32_t* n_entries);

@@ -107,14 +107,14 @@ def check_build(case: Case, tree: Tree, sample=None, seed=0):
                 nodes = np.unique(np.concatenate([[0, n_l - 1], rng.choice(n_l, sample - 2, replace=False)]))
             for g in range(case.Hkv):
                 u = b * case.Hkv + g
-                Ku, _ = case.unit_kv(b, g)
+                Ku = np.ascontiguousarray(case.unit_kv(b, g)[0], dtype=np.float64)  # widened once per unit
                 mg = m_d[u, torch.from_numpy(nodes).to(m_d.device)].float().cpu().numpy().astype(np.float64)
                 bg = b_d[u, torch.from_numpy(nodes).to(b_d.device)].cpu().numpy().astype(np.float64)
                 refs = case.refs[g].astype(np.float64)
                 for i, j in enumerate(nodes):
                     t0 = j * tree.C ** l
                     t1 = min((j + 1) * tree.C ** l, (N // tree.C) * tree.C)
-                    m_o, _, lse_o = oracle.node_planes(Ku, t0, t1, refs)
+                    m_o, _, lse_o = oracle.node_planes(Ku[t0:t1], 0, t1 - t0, refs)
                     err_m = np.abs(mg[i] - m_o) - (rel * np.abs(m_o) + floor)
                     assert err_m.max() <= 0, f"m level {l} unit {u} node {j}: excess {err_m.max():.3e}"
                     plane_at_r = bg[i] + np.einsum("rd,rd->r", refs, mg[i])

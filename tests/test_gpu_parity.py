@@ -55,6 +55,11 @@ VARIANTS = [
     ("bf16 d128 wide C256 L1 R16", dict(batch=1, n_tokens=16484, chunk=256, levels=1, n_refs=16), [16484]),
     ("f32 d64 C4 L4 R16 G1", dict(batch=1, n_tokens=3000, head_dim=64, n_q_heads=1, n_kv_heads=1, chunk=4, levels=4,
                                   n_refs=16, dtype="f32", head_scale=False), [3000]),
+    # frontiers above 8192 nodes take the sampled-window selection and the multi-workgroup masses
+    ("bf16 d128 C4 L2 R16 G8 large frontier", dict(batch=1, n_tokens=65539, n_q_heads=16, n_kv_heads=2, chunk=4,
+                                                   levels=2, n_refs=16), [65539]),
+    ("bf16 d64 C16 L1 R4 G4 large flat", dict(batch=2, n_tokens=200000, head_dim=64, n_q_heads=8, n_kv_heads=2,
+                                              chunk=16, levels=1, n_refs=4), [200000, 150001]),
 ]
 
 
@@ -65,7 +70,7 @@ def test_variants(label, kw, lens):
     case = Case(cfg, lens=lens, n_queries=2)
     tree = case.tree()
     torch.cuda.synchronize()
-    say(" build", check_build(case, tree))
+    say(" build", check_build(case, tree, sample=None if sum(lens) < 20000 else 256))
     for t in range(2):
         for p in (0.5, 0.9):
             r, a = full_check(case, tree, t, p)
