@@ -84,14 +84,18 @@ zha_status check_lens(const zha_tree* t, const int32_t* lens) {
 
 // ----------------------------------------------------------------------------- timing
 
-void zha_time_begin(zha_tree* t, hipStream_t s) {
-  if (!t->timing || t->n_rec >= ZHA_MAX_TIMING) return;
-  (void)hipEventRecord(t->ev[2 * t->n_rec], s);
+static bool zha_timed(const zha_tree* t, int kernel, int level) {
+  return (t->timing_kernels >> kernel & 1) && (t->timing_levels >> level & 1) && t->n_rec < ZHA_MAX_TIMING;
+}
+
+void zha_time_begin(zha_tree* t, hipStream_t s, int kernel, int level) {
+  t->timing_open = zha_timed(t, kernel, level) && hipEventRecord(t->ev[2 * t->n_rec], s) == hipSuccess;
 }
 
 void zha_time_end(zha_tree* t, hipStream_t s, int kernel, int level) {
-  if (!t->timing || t->n_rec >= ZHA_MAX_TIMING) return;
-  (void)hipEventRecord(t->ev[2 * t->n_rec + 1], s);
+  if (!t->timing_open) return;
+  t->timing_open = false;
+  if (hipEventRecord(t->ev[2 * t->n_rec + 1], s) != hipSuccess) return;
   t->tk[t->n_rec] = kernel;
   t->tl[t->n_rec] = level;
   ++t->n_rec;
@@ -316,13 +320,15 @@ zha_status zha_route_copy_level(zha_tree_t t, int32_t level, int32_t* frontier_c
   return ZHA_OK;
 }
 
-zha_status zha_timing_enable(zha_tree_t t, int32_t enable) {
+zha_status zha_timing_enable(zha_tree_t t, int32_t kernel_mask, int32_t level_mask) {
   if (!t) return ZHA_ERR_INVALID;
-  if (enable && !t->ev[0]) {
+  if (kernel_mask && !t->ev[0]) {
     for (int i = 0; i < 2 * ZHA_MAX_TIMING; ++i)
       if (hipEventCreate(&t->ev[i]) != hipSuccess) return ZHA_ERR_HIP;
   }
-  t->timing = enable != 0;
+  t->timing_kernels = kernel_mask;
+  t->timing_levels = level_mask;
+  t->timing_open = false;
   t->n_rec = 0;
   return ZHA_OK;
 }

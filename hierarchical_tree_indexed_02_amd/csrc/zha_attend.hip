@@ -39,6 +39,7 @@ struct Positions {
   int nx;       // positions before the chunk tokens (sink, then tail)
   int sink;     // 1 when token 0 is read as a separate sink position
   int Nc;
+  int nK;       // kept chunks
   const int32_t* kp;
 };
 
@@ -47,7 +48,7 @@ __device__ __forceinline__ Positions unit_positions(const AttArgs& a, int u, int
   Positions P;
   const int N = a.len.n[bi];
   if (DENSE) {
-    P.P = N; P.nx = N; P.sink = 0; P.Nc = 0; P.kp = nullptr;
+    P.P = N; P.nx = N; P.sink = 0; P.Nc = 0; P.nK = 0; P.kp = nullptr;
     return P;
   }
   const int Nc = (N / a.C) * a.C;
@@ -58,22 +59,47 @@ __device__ __forceinline__ Positions unit_positions(const AttArgs& a, int u, int
   P.nx = sink + (N - Nc);
   P.P = P.nx + nK * a.C;
   P.Nc = Nc;
+  P.nK = nK;
   P.kp = kp;
   return P;
 }
 
-// Token index of position p (DENSE: p itself).
-template <bool DENSE>
-__device__ __forceinline__ int pos_token(const Positions& P, int p, int C, int Cshift) {
-  if (DENSE) return p;
-  if (p < P.nx) return (P.sink && p == 0) ? 0 : P.Nc + p - P.sink;
-  const int q = p - P.nx;
-  if (Cshift >= 0) return (P.kp[q >> Cshift] << Cshift) + (q & ((1 << Cshift) - 1));
-  const int k = q / C;
-  return P.kp[k] * C + (q - k * C);
-}
-
 constexpr int ATT_STEP = 32;  // positions per wave step
+
+// Token lookup for one wave's window of ATT_STEP positions starting at p0.  The chunk
+// ids the window touches (at most ATT_STEP / C + 2) are fetched with one load, lane j
+// holding the j-th, and handed to the lanes that need them with a shuffle, so a window's
+// K/V addresses cost one dependent load that can be issued windows ahead.
+template <bool DENSE>
+struct Window {
+  int ids;  // this lane's chunk id (lane j: chunk cb + j of the window)
+
+  __device__ static __forceinline__ int first_chunk(const Positions& P, int p0, int C, int Cshift) {
+    const int q = p0 - P.nx;
+    if (q <= 0) return 0;
+    return Cshift >= 0 ? (q >> Cshift) : q / C;
+  }
+  // Issues the id load of window p0 (nothing to load in dense mode).
+  __device__ __forceinline__ void fetch(const Positions& P, int p0, int end, int C, int Cshift, int lane) {
+    if (DENSE) { ids = 0; return; }
+    const int nwin = ATT_STEP / C + 2;
+    const int k = first_chunk(P, p0, C, Cshift) + lane;
+    ids = (lane < nwin && p0 < end && k < P.nK) ? P.kp[k] : 0;
+  }
+  // Token of position p of window p0; positions at or past `end` map to token 0 (read, masked).
+  // Every lane of the wave must call this together (it shuffles).
+  __device__ __forceinline__ int token(const Positions& P, int p0, int p, int end, int C, int Cshift) const {
+    if (DENSE) return p < end ? p : 0;
+    const int q = p - P.nx;
+    int k = 0;
+    if (q > 0) k = Cshift >= 0 ? (q >> Cshift) : q / C;
+    const int src = min(max(k - first_chunk(P, p0, C, Cshift), 0), 63);
+    const int id = __shfl(ids, src);
+    if (p >= end) return 0;
+    if (q < 0) return (P.sink && p == 0) ? 0 : P.Nc + p - P.sink;
+    return Cshift >= 0 ? (id << Cshift) + (q & ((1 << Cshift) - 1)) : id * C + (q - k * C);
+  }
+};
 
 // ---------------------------------------------------------------- P.V, per storage type
 
@@ -90,13 +116,12 @@ template <int D> struct PV<__bf16, D> {
   static constexpr int NLD = ATT_STEP / RPI;
 
   template <bool DENSE>
-  __device__ static __forceinline__ void load(vfrag& vf, const __bf16* Vb, const Positions& P, int p0, int end,
-                                              int C, int Cshift, int lane) {
+  __device__ static __forceinline__ void load(vfrag& vf, const __bf16* Vb, const Positions& P, const Window<DENSE>& win,
+                                              int p0, int end, int C, int Cshift, int lane) {
 #pragma unroll
     for (int k = 0; k < NLD; ++k) {
       const int ts = RPI * k + lane / CPR;
-      const int p = p0 + ts;
-      const int tok = p < end ? pos_token<DENSE>(P, p, C, Cshift) : 0;
+      const int tok = win.token(P, p0, p0 + ts, end, C, Cshift);
       vf[k] = *(const bf16x8_t*)(Vb + (int64_t)tok * D + 8 * (lane % CPR));
     }
   }
@@ -139,15 +164,15 @@ template <int D> struct PV<float, D> {
   static constexpr int ND = D / 16;
   typedef float vfrag[2][4][ND];
   template <bool DENSE>
-  __device__ static __forceinline__ void load(vfrag& vf, const float* Vb, const Positions& P, int p0, int end,
-                                              int C, int Cshift, int lane) {
+  __device__ static __forceinline__ void load(vfrag& vf, const float* Vb, const Positions& P, const Window<DENSE>& win,
+                                              int p0, int end, int C, int Cshift, int lane) {
     const int row = lane & 15, grp = lane >> 4;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int p = p0 + 16 * t + 4 * grp + jj;
-        const int tok = p < end ? pos_token<DENSE>(P, p, C, Cshift) : 0;
+        const int tok = win.token(P, p0, p, end, C, Cshift);
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) vf[t][jj][dt] = Vb[(int64_t)tok * D + dt * 16 + row];
       }
@@ -202,19 +227,20 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a) {
   for (int dt = 0; dt < ND; ++dt) o[dt] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
   float mrun = -INFINITY, lrun = 0.0f;
 
-  for (int p0 = start + wave * ATT_STEP; p0 < end; p0 += 4 * ATT_STEP) {
-    // K rows of the two 16-token tiles: lane row r -> position p0 + 16t + r
-    typename M::frag kf[2][NK];
+  // One window: K rows of the two 16-token tiles (lane row r -> position p0 + 16t + r) and
+  // the V tile, loaded into registers.
+  auto load_kv = [&](typename M::frag (&kf)[2][NK], typename PVT::vfrag& vf, const Window<DENSE>& win, int p0) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const int p = p0 + 16 * t + row;
-      const int tok = p < end ? pos_token<DENSE>(P, p, a.C, a.Cshift) : 0;
+      const int tok = win.token(P, p0, p0 + 16 * t + row, end, a.C, a.Cshift);
       const T* kr = Kb + (int64_t)tok * D + grp * M::EPL;
 #pragma unroll
       for (int s = 0; s < NK; ++s) kf[t][s] = M::load(kr + s * M::KPER);
     }
-    typename PVT::vfrag vf;
-    PVT::template load<DENSE>(vf, Vb, P, p0, end, a.C, a.Cshift, lane);
+    PVT::template load<DENSE>(vf, Vb, P, win, p0, end, a.C, a.Cshift, lane);
+  };
+  // Online-softmax update with one loaded window.
+  auto compute = [&](const typename M::frag (&kf)[2][NK], const typename PVT::vfrag& vf, int p0) {
     // S^T = K Q^T: lane holds tokens 16t + 4grp + jj for head `row`
     float z[2][4];
 #pragma unroll
@@ -260,6 +286,29 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a) {
     } else {
       PVT::mma(o, vf, pr);
     }
+  };
+
+  // Software pipeline over the wave's windows p0, p0 + 4 ATT_STEP, ...: while window i is
+  // computed, the K/V loads of window i+1 and the chunk ids of window i+2 are in flight.
+  // The two register buffers alternate by unrolling the loop twice.
+  constexpr int WSTEP = 4 * ATT_STEP;
+  int p0 = start + wave * ATT_STEP;
+  Window<DENSE> w0, w1;
+  w0.fetch(P, p0, end, a.C, a.Cshift, lane);
+  w1.fetch(P, p0 + WSTEP, end, a.C, a.Cshift, lane);
+  typename M::frag kA[2][NK], kB[2][NK];
+  typename PVT::vfrag vA, vB;
+  if (p0 < end) load_kv(kA, vA, w0, p0);
+  while (p0 < end) {
+    w0.fetch(P, p0 + 2 * WSTEP, end, a.C, a.Cshift, lane);
+    load_kv(kB, vB, w1, p0 + WSTEP);
+    compute(kA, vA, p0);
+    p0 += WSTEP;
+    if (p0 >= end) break;
+    w1.fetch(P, p0 + 2 * WSTEP, end, a.C, a.Cshift, lane);
+    load_kv(kA, vA, w0, p0 + WSTEP);
+    compute(kB, vB, p0);
+    p0 += WSTEP;
   }
   // per-head sum over the four lane groups, then combine the four waves through LDS
   lrun += __shfl_xor(lrun, 16);
@@ -419,11 +468,11 @@ hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const vo
   a.T = t->T;
   a.scale_log2 = scale * ZHA_LOG2E;
   a.len = t->len;
-  zha_time_begin(t, s);
+  zha_time_begin(t, s, ZHA_K_ATTEND, 0);
   hipError_t e = launch_att_dt<false>(a, t->desc.dtype, t->d, t->U, out, lse, s);
   if (e != hipSuccess) return e;
   zha_time_end(t, s, ZHA_K_ATTEND, 0);
-  zha_time_begin(t, s);
+  zha_time_begin(t, s, ZHA_K_MERGE, 0);
   e = t->d == 64 ? launch_merge<64>(a, t->U, out, lse, s) : launch_merge<128>(a, t->U, out, lse, s);
   if (e != hipSuccess) return e;
   zha_time_end(t, s, ZHA_K_MERGE, 0);

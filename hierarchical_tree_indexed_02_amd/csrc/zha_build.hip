@@ -264,7 +264,7 @@ hipError_t zha_launch_build(zha_tree* t, const void* K, hipStream_t s) {
                       : (t->d == 64 ? allow_lds(zha_build_kernel<float, 64>, sh) : allow_lds(zha_build_kernel<float, 128>, sh));
   if (e0 != hipSuccess) return e0;
   dim3 grid((unsigned)(t->cap[t->L] > 0 ? t->cap[t->L] : 1), (unsigned)t->U), block(16 * t->R);
-  zha_time_begin(t, s);
+  zha_time_begin(t, s, ZHA_K_BUILD, 0);
   if (t->desc.dtype == ZHA_BF16) {
     if (t->d == 64) hipLaunchKernelGGL((zha_build_kernel<__bf16, 64>), grid, block, sh, s, a);
     else hipLaunchKernelGGL((zha_build_kernel<__bf16, 128>), grid, block, sh, s, a);
@@ -286,7 +286,7 @@ hipError_t zha_launch_append(zha_tree* t, const void* K, hipStream_t s) {
                       : (t->d == 64 ? allow_lds(zha_append_kernel<float, 64>, sh) : allow_lds(zha_append_kernel<float, 128>, sh));
   if (e0 != hipSuccess) return e0;
   dim3 grid((unsigned)t->U), block(16 * t->R);
-  zha_time_begin(t, s);
+  zha_time_begin(t, s, ZHA_K_APPEND, 0);
   if (t->desc.dtype == ZHA_BF16) {
     if (t->d == 64) hipLaunchKernelGGL((zha_append_kernel<__bf16, 64>), grid, block, sh, s, a);
     else hipLaunchKernelGGL((zha_append_kernel<__bf16, 128>), grid, block, sh, s, a);

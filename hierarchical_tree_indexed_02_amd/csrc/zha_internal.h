@@ -160,14 +160,16 @@ struct zha_tree {
   bool built;
   int64_t bytes;
   // timing
-  bool timing;
+  int32_t timing_kernels;           // bit k: time launches of kernel code k (0: timing off)
+  int32_t timing_levels;            // bit l: time launches at level l (bit 0: launches with no level)
+  bool timing_open;                 // a begin event is recorded and waits for its end
   hipEvent_t ev[2 * ZHA_MAX_TIMING];
   int tk[ZHA_MAX_TIMING], tl[ZHA_MAX_TIMING];
   int n_rec;
 };
 
 // Timing helpers (record events around a launch when enabled).
-void zha_time_begin(zha_tree* t, hipStream_t s);
+void zha_time_begin(zha_tree* t, hipStream_t s, int kernel, int level);
 void zha_time_end(zha_tree* t, hipStream_t s, int kernel, int level);
 
 // Launchers (defined next to their kernels).  All return hipSuccess or the launch error.

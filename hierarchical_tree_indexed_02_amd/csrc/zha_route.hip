@@ -1058,7 +1058,7 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     sa.Hq = t->desc.n_q_heads;
     sa.G = t->G;
     sa.scale = scale;
-    zha_time_begin(t, s);
+    zha_time_begin(t, s, ZHA_K_SCORE, l);
     if (t->desc.dtype == ZHA_BF16)
       e = t->d == 64 ? launch_score_r<__bf16, 64>(sa, t->R, sa.W, U, s) : launch_score_r<__bf16, 128>(sa, t->R, sa.W, U, s);
     else
@@ -1082,7 +1082,7 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
       sm.G = t->G;
       sm.p = p;
       sm.keep_all = keep_all ? 1 : 0;
-      zha_time_begin(t, s);
+      zha_time_begin(t, s, ZHA_K_SELECT, l);
       hipLaunchKernelGGL(zha_select_small_kernel, dim3(U), dim3(SMT), 0, s, sm);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -1104,7 +1104,7 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
       ma.G = t->G;
       int64_t wm = (t->cap[l] + 1023) / 1024;
       ma.WM = (int)(wm > 256 ? 256 : (wm < 1 ? 1 : wm));
-      zha_time_begin(t, s);
+      zha_time_begin(t, s, ZHA_K_MASS, l);
       hipLaunchKernelGGL(zha_mass_kernel, dim3(ma.WM, U), dim3(256), 0, s, ma);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -1119,7 +1119,7 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
       la.fh_edge = (u64*)t->fh_edge;
       la.cut = t->cut;
       la.p = p;
-      zha_time_begin(t, s);
+      zha_time_begin(t, s, ZHA_K_SELECT, l);
       hipLaunchKernelGGL(zha_select_large_kernel, dim3(U), dim3(LGT), 0, s, la);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -1143,7 +1143,7 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     ca.span_child = span_child;
     ca.lb_error = t->lb_error;
     const int nch = zha_compact_chunks(t->cap[l]);
-    zha_time_begin(t, s);
+    zha_time_begin(t, s, ZHA_K_COMPACT, l);
     hipLaunchKernelGGL(zha_compact_kernel, dim3(nch, U), dim3(CPT), 0, s, ca);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -83,8 +83,12 @@ class Tree:
         zha.zha_route_copy_level(self.h, level, nf, nk, ids)
         return nf, nk, ids
 
-    def timing(self, enable: bool):
-        zha.zha_timing_enable(self.h, enable)
+    def timing(self, enable=True, kernels=None, levels=None):
+        """Record per-launch durations: every launch, or only those of the given kernel
+        codes (zha.ZHA_K_*) at the given levels (0 for launches without a level)."""
+        km = 0 if not enable else (zha.ZHA_TIMING_ALL if kernels is None else sum(1 << k for k in kernels))
+        lm = zha.ZHA_TIMING_ALL if levels is None else sum(1 << l for l in levels)
+        zha.zha_timing_enable(self.h, km, lm)
 
     def timing_read(self):
         return zha.zha_timing_read(self.h)

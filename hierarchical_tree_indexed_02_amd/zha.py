@@ -72,7 +72,7 @@ def load():
             "zha_tree_level_capacity": (st, [vp, c_int32, POINTER(c_int64)]),
             "zha_tree_copy_level": (st, [vp, c_int32, vp, vp, vp]),
             "zha_route_copy_level": (st, [vp, c_int32, vp, vp, vp, vp]),
-            "zha_timing_enable": (st, [vp, c_int32]),
+            "zha_timing_enable": (st, [vp, c_int32, c_int32]),
             "zha_timing_read": (st, [vp, _i32p, _i32p, POINTER(c_float), c_int32, _i32p]),
             "zha_calibration_copy": (st, [vp, vp, c_int64, vp]),
         }
@@ -180,8 +180,11 @@ def zha_route_copy_level(tree: int, level: int, frontier_counts, kept_counts, ke
                                        _stream(stream)), "zha_route_copy_level")
 
 
-def zha_timing_enable(tree: int, enable: bool) -> None:
-    _check(load().zha_timing_enable(tree, 1 if enable else 0), "zha_timing_enable")
+ZHA_TIMING_ALL = -1
+
+
+def zha_timing_enable(tree: int, kernel_mask: int, level_mask: int = ZHA_TIMING_ALL) -> None:
+    _check(load().zha_timing_enable(tree, int(kernel_mask), int(level_mask)), "zha_timing_enable")
 
 
 def zha_timing_read(tree: int, max_entries: int = 256):

@@ -75,7 +75,7 @@ def test_null_arguments_rejected():
     assert lib.zha_route(None, None, ctypes.c_float(0.9), ctypes.c_float(1.0), None, None) == zha.ZHA_ERR_INVALID
     assert lib.zha_attend(None, None, None, None, None, ctypes.c_float(1.0), None, None, None) == zha.ZHA_ERR_INVALID
     assert lib.zha_tree_bytes(None, None) == zha.ZHA_ERR_INVALID
-    assert lib.zha_timing_enable(None, 1) == zha.ZHA_ERR_INVALID
+    assert lib.zha_timing_enable(None, 1, -1) == zha.ZHA_ERR_INVALID
     n = ctypes.c_int32()
     assert lib.zha_timing_read(None, None, None, None, 0, ctypes.byref(n)) == zha.ZHA_ERR_INVALID
     assert lib.zha_calibration_copy(None, None, 1, None) == zha.ZHA_ERR_INVALID
