@@ -53,7 +53,7 @@ void free_tree(zha_tree* t) {
   }
   void* ps[] = {t->refs,   t->spine,  t->counts,    t->scores,   t->spart,    t->keys,     t->apart,
                 t->fh_cnt, t->fh_mass,  t->fh_edge,  t->cut,      t->lb_status,
-                t->lb_epoch, t->last_pos, t->lb_error};
+                t->lb_epoch, t->lb_error};
   for (void* p : ps)
     if (p) (void)hipFree(p);
   for (int i = 0; i < 2 * ZHA_MAX_TIMING; ++i)
@@ -160,7 +160,7 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   ok = ok && dalloc(t, &t->refs, (size_t)desc->n_kv_heads * R * d * sizeof(float));
   ok = ok && dalloc(t, &t->spine, (size_t)U * zha_stack_bytes(L, d, R));
   ok = ok && dalloc(t, &t->counts, (size_t)2 * (L + 2) * U * sizeof(int32_t));
-  ok = ok && dalloc(t, &t->scores, (size_t)U * t->cap[1] * G * sizeof(float));
+  ok = ok && dalloc(t, &t->scores, (size_t)U * t->cap[1] * ((G + 3) & ~3) * sizeof(float));
   ok = ok && dalloc(t, &t->spart, (size_t)U * t->WS * G * 2 * sizeof(float));
   t->kstride = (t->cap[1] + 3) / 4 * 4;
   ok = ok && dalloc(t, &t->keys, (size_t)U * t->kstride * sizeof(uint32_t));
@@ -173,14 +173,12 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   ok = ok && dalloc(t, &t->cut, (size_t)U * 4 * sizeof(int32_t));
   ok = ok && dalloc(t, &t->lb_status, (size_t)U * nchunk * sizeof(unsigned long long));
   ok = ok && dalloc(t, &t->lb_epoch, 2 * sizeof(uint32_t));
-  ok = ok && dalloc(t, &t->last_pos, (size_t)U * sizeof(int32_t));
   ok = ok && dalloc(t, &t->lb_error, sizeof(int32_t));
   if (ok) {  // counters and histograms start at zero and are left at zero by the kernels
     ok = hipMemset(t->fh_cnt, 0, (size_t)U * nb * sizeof(uint32_t)) == hipSuccess &&
          hipMemset(t->fh_mass, 0, (size_t)U * nb * sizeof(unsigned long long)) == hipSuccess &&
          hipMemset(t->fh_edge, 0, (size_t)U * 2 * sizeof(unsigned long long)) == hipSuccess &&
          hipMemset(t->lb_status, 0, (size_t)U * nchunk * sizeof(unsigned long long)) == hipSuccess &&
-         hipMemset(t->last_pos, 0xFF, (size_t)U * sizeof(int32_t)) == hipSuccess &&
          hipMemset(t->lb_error, 0, sizeof(int32_t)) == hipSuccess;
     const uint32_t ep[2] = {1u, 0u};  // status words of epoch 0 (all-zero memory) never match
     ok = ok && hipMemcpy(t->lb_epoch, ep, sizeof(ep), hipMemcpyHostToDevice) == hipSuccess;

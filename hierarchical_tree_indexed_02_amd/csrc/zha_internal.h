@@ -141,7 +141,7 @@ struct zha_tree {
   float* refs;                      // [Hkv][R][d]
   float* spine;                     // [U][L+1][R*16][E+2] open-node accumulators
   int32_t* counts;                  // [2][L+2][U]: frontier counts, kept counts per level
-  float* scores;                    // [U][cap1][G]
+  float* scores;                    // [U][cap1][G rounded up to 4]
   float* spart;                     // [U][WS][G][2] score-kernel partial log-sum-exp
   uint32_t* keys;                   // [U][kstride] node-mass keys of the level being selected
   int64_t kstride;                  // cap1 rounded up to a multiple of 4
@@ -151,7 +151,6 @@ struct zha_tree {
   int32_t* cut;                     // [U][4] cut of the level being selected
   unsigned long long* lb_status;    // [U][compaction chunks of level 1] look-back words
   uint32_t* lb_epoch;               // [2] look-back epoch (starts at 1) and finished-workgroup count
-  int32_t* last_pos;                // [U] largest kept position (-1 between launches)
   int32_t* lb_error;                // [1] set if a look-back wait ever gives up
   float* apart;                     // attention partials: o [U][WA][G][d], then (max, sum) [U][WA][G][2]
   int WS, WA;                       // score and attention workgroups per unit (maximum)

@@ -13,7 +13,7 @@
 //                       HBM once and score them on the matrix cores (G query heads x
 //                       R planes per node is a small dense product), and write the
 //                       per-workgroup (max, sum exp) partials of each head's scores.
-//   small frontiers (<= 4096 nodes): zha_select_small_kernel, one workgroup per unit,
+//   levels of <= 16384 nodes: zha_select_small_kernel, one workgroup per unit,
 //                       forms the node masses, finds the exact cut and compacts, in LDS.
 //   large frontiers:    zha_mass_kernel (many workgroups) forms the masses and an exact
 //                       histogram of them on fixed slices around the uniform mass 1/|F|;
@@ -32,25 +32,24 @@ namespace {
 typedef unsigned long long u64;
 
 constexpr int NB = 1024;                 // histogram slices
-constexpr int SMALL_NODES = 4096;        // frontiers up to this size are selected in LDS
+constexpr int SMALL_NODES = 16384;       // frontiers up to this size are selected in one workgroup
 constexpr int CAND = 8192;               // keys of a crossing slice held in LDS
-constexpr int CH = 1024;                 // compaction chunk (positions per workgroup)
+constexpr int CH = 4096;                 // compaction chunk (positions per workgroup)
 
-// Per-level inputs shared by the kernels of one level.
+// Per-level inputs shared by the kernels of one level.  Node counts per sequence are
+// computed on the host (no integer division on the device).
 struct Level {
   const int32_t* parent;      // kept ids of level l+1 [U][cap_parent]; null at the top level
   const int32_t* parent_nF;   // frontier counts of this level, written by level l+1 [U]
   int64_t cap_parent;
-  int64_t span_l;             // tokens per node at this level, C^l
   int C, Cshift, Hkv;
-  ZLens len;
+  int32_t nodes[ZHA_MAX_BATCH];   // nodes of this level per sequence
+  int32_t child[ZHA_MAX_BATCH];   // nodes of level l-1 per sequence (0 at level 1)
 };
 
 __device__ __forceinline__ int frontier_size(const Level& v, int u) {
   if (v.parent) return v.parent_nF[u];
-  const int64_t N = v.len.n[u / v.Hkv];
-  const int64_t Nc = (N / v.C) * v.C;
-  return (int)((Nc + v.span_l - 1) / v.span_l);
+  return v.nodes[u / v.Hkv];
 }
 
 // Node id of frontier position pos: the top level lists every node; a lower level
@@ -68,11 +67,7 @@ __device__ __forceinline__ int next_frontier(int kept, int last_id, int C, int n
   return C * (kept - 1) + min(C, n_child - last_id * C);
 }
 
-__device__ __forceinline__ int child_nodes(const Level& v, int u, int64_t span_child) {
-  const int64_t N = v.len.n[u / v.Hkv];
-  const int64_t Nc = (N / v.C) * v.C;
-  return (int)((Nc + span_child - 1) / span_child);
-}
+__device__ __forceinline__ int child_nodes(const Level& v, int u) { return v.child[u / v.Hkv]; }
 
 __device__ __forceinline__ void lse_push(float& M, float& S, float x) {
   if (x == -INFINITY) return;
@@ -91,29 +86,45 @@ __device__ __forceinline__ void lse_merge(float& M, float& S, float M2, float S2
   M = mx;
 }
 
-// Fixed-point mass of a key: w * 2^40 truncated (w <= 1 up to rounding).
-__device__ __forceinline__ u64 fx_mass(uint32_t key) { return (u64)(__uint_as_float(key) * 1099511627776.0f); }
+// Fixed-point mass of a key: w * 2^40 truncated (w <= 1 up to rounding), from the bits:
+// w = m * 2^(e - 150) with m the 24-bit significand, so w * 2^40 = m * 2^(e - 110).
+// Branch-free; zero and subnormal keys (far below the 2^-40 resolution) give 0.
+__device__ __forceinline__ u64 fx_mass(uint32_t key) {
+  const int e = (int)(key >> 23) & 0xFF;
+  const u64 m = (u64)((key & 0x7FFFFFu) | 0x800000u);
+  const int sft = e - 110;
+  const u64 up = m << min(max(sft, 0), 63);
+  const u64 dn = m >> min(max(-sft, 0), 63);
+  const u64 r = sft >= 0 ? up : dn;
+  return e == 0 ? 0 : r;
+}
+
+// Score rows hold the G heads' scores of one node padded to a multiple of 4 floats
+// (16-byte aligned rows; the padding is never read as a score).
+__device__ __forceinline__ int score_stride(int G) { return (G + 3) & ~3; }
 
 // Node mass key from its G scores: mean over heads of exp(s_h - LSE_h), as fp32 bits.
-__device__ __forceinline__ uint32_t mass_key(const float (&sv)[16], const float* lse, int G, float invG) {
+__device__ __forceinline__ uint32_t mass_key(const float4 (&sv)[4], const float* lse, int G, float invG) {
   float w = 0.0f;
 #pragma unroll
-  for (int h = 0; h < 16; ++h)
-    if (h < G) w += zexp(sv[h] - lse[h]);
+  for (int h4 = 0; h4 < 4; ++h4) {
+    if (4 * h4 < G) {
+      const float4 v = sv[h4];
+      w += zexp(v.x - lse[4 * h4]);
+      w += 4 * h4 + 1 < G ? zexp(v.y - lse[4 * h4 + 1]) : 0.0f;
+      w += 4 * h4 + 2 < G ? zexp(v.z - lse[4 * h4 + 2]) : 0.0f;
+      w += 4 * h4 + 3 < G ? zexp(v.w - lse[4 * h4 + 3]) : 0.0f;
+    }
+  }
   return __float_as_uint(w * invG);
 }
 
-__device__ __forceinline__ void load_scores(const float* sp, int G, bool valid, float (&sv)[16]) {
-  if ((G & 3) == 0) {  // a node's G scores are 16-byte aligned
+// The scores of one node (sp must point at a readable row: callers clamp the position;
+// the head bound is uniform, so only whole float4 groups are skipped).
+__device__ __forceinline__ void load_scores(const float* sp, int G, float4 (&sv)[4]) {
 #pragma unroll
-    for (int h4 = 0; h4 < 4; ++h4) {
-      const float4 v = (valid && 4 * h4 < G) ? *(const float4*)(sp + 4 * h4) : make_float4(0.f, 0.f, 0.f, 0.f);
-      sv[4 * h4] = v.x; sv[4 * h4 + 1] = v.y; sv[4 * h4 + 2] = v.z; sv[4 * h4 + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int h = 0; h < 16; ++h) sv[h] = (valid && h < G) ? sp[h] : 0.0f;
-  }
+  for (int h4 = 0; h4 < 4; ++h4)
+    sv[h4] = 4 * h4 < G ? *(const float4*)(sp + 4 * h4) : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 // ----------------------------------------------------------------------------------- score
@@ -161,7 +172,8 @@ __global__ __launch_bounds__(256) void zha_score_kernel(ScoreArgs a) {
   const int32_t* par = a.v.parent ? a.v.parent + (int64_t)u * a.v.cap_parent : nullptr;
   const T* mb = (const T*)a.m + (int64_t)u * a.capl * R * D;
   const float* bb = a.b + (int64_t)u * a.capl * R;
-  float* sc = a.scores + (int64_t)u * a.cap1 * G;
+  const int GS = score_stride(G);
+  float* sc = a.scores + (int64_t)u * a.cap1 * GS;
   float runM = -INFINITY, runS = 0.0f;
 
   for (int base = start; base < end; base += SUPER) {
@@ -201,7 +213,7 @@ __global__ __launch_bounds__(256) void zha_score_kernel(ScoreArgs a) {
         const bool writer = (R == 4) || (R == 8 && (grp & 1) == 0) || (R == 16 && grp == 0);
         const int pos = tb[k] + (4 * grp) / R;
         if (writer && row < G && pos < end) {
-          sc[(int64_t)pos * G + row] = mx;
+          sc[(int64_t)pos * GS + row] = mx;
           lse_push(runM, runS, mx);
         }
       } else if (R == 2) {
@@ -210,7 +222,7 @@ __global__ __launch_bounds__(256) void zha_score_kernel(ScoreArgs a) {
           const float mx = fmaxf(v[2 * h2], v[2 * h2 + 1]);
           const int pos = tb[k] + 2 * grp + h2;
           if (row < G && pos < end) {
-            sc[(int64_t)pos * G + row] = mx;
+            sc[(int64_t)pos * GS + row] = mx;
             lse_push(runM, runS, mx);
           }
         }
@@ -219,7 +231,7 @@ __global__ __launch_bounds__(256) void zha_score_kernel(ScoreArgs a) {
         for (int jj = 0; jj < 4; ++jj) {
           const int pos = tb[k] + 4 * grp + jj;
           if (row < G && pos < end) {
-            sc[(int64_t)pos * G + row] = v[jj];
+            sc[(int64_t)pos * GS + row] = v[jj];
             lse_push(runM, runS, v[jj]);
           }
         }
@@ -246,35 +258,38 @@ __global__ __launch_bounds__(256) void zha_score_kernel(ScoreArgs a) {
   }
 }
 
-// Per-head log-sum-exp over the frontier from the W scoring partials of unit u, into
-// lse[0..G).  Heads go to groups of 16 threads; each group combines the partials in a
-// fixed order, so every workgroup that calls this gets the same bits.
-template <int NT>
-__device__ __forceinline__ void frontier_lse(const float* part, int W, int G, int u, float* lse) {
-  static_assert(NT >= 256, "16 threads per head for up to 16 heads");
-  const int h = threadIdx.x >> 4, j = threadIdx.x & 15;
-  float Mx = -INFINITY, Sx = 0.0f;
-  if (h < G) {
-    for (int i0 = j; i0 < W; i0 += 16 * 8) {
-      float2 pv[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int i = i0 + 16 * k;
-        pv[k] = i < W ? *(const float2*)(part + (((int64_t)u * W + i) * G + h) * 2) : make_float2(-INFINITY, 0.0f);
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) lse_merge(Mx, Sx, pv[k].x, pv[k].y);
-    }
-  }
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) {
-    const float M2 = __shfl_xor(Mx, o, 16), S2 = __shfl_xor(Sx, o, 16);
-    lse_merge(Mx, Sx, M2, S2);
-  }
-  if (h < G && j == 0) lse[h] = Mx + zlog(Sx);
-}
-
 // ------------------------------------------------------------------------ shared selection
+//
+// The selection kernels run a handful of workgroups each, so their time is the length of
+// their dependent instruction and memory chains: loads are issued in batches, reductions
+// run across all threads at once, and no step walks a list serially.
+
+// Per-head log-sum-exp over the frontier from the W <= 512 scoring partials of unit u,
+// into lse[0..G), with 256 threads: 16 per head, every partial loaded at once.  Fixed
+// combination order: every workgroup calling this gets the same bits.
+__device__ __forceinline__ void frontier_lse256(const float* part, int W, int G, int u, float* lse) {
+  const int h = threadIdx.x >> 4, j = threadIdx.x & 15;
+  float2 pv[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const int i = j + 16 * k;
+    pv[k] = (h < G && i < W) ? *(const float2*)(part + (((int64_t)u * W + i) * G + h) * 2)
+                             : make_float2(-INFINITY, 0.0f);
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) M = fmaxf(M, pv[k].x);
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 16));
+  float S = 0.0f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) S += pv[k].x == -INFINITY ? 0.0f : pv[k].y * zexp(pv[k].x - M);
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) S += __shfl_xor(S, o, 16);
+  if (h < G && j == 0) lse[h] = M == -INFINITY ? -INFINITY : M + zlog(S);
+}
 
 // Exclusive scan of one u32 per thread over a workgroup of NT threads; total in *tot.
 template <int NT>
@@ -301,132 +316,48 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* tot, u
   return before + inc - x;
 }
 
-// Given an NB-bin histogram of fixed-point masses and the mass already above the bins,
-// find the bin in which the cumulative mass, from the heaviest bin down, reaches T.
-// One wave; lane l owns NB/64 consecutive bins from the top.  Writes only when found.
-__device__ __forceinline__ void find_bin(const u64* hm, u64 above0, u64 T, uint32_t* out_bin, u64* out_above) {
-  constexpr int PER = NB / 64;
-  const int lane = threadIdx.x & 63;
-  u64 ls = 0;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) ls += hm[NB - 1 - PER * lane - e];
-  u64 inc = ls;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const u64 y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  u64 run = above0 + inc - ls;
-  if (run < T && run + ls >= T) {
-    for (int e = 0; e < PER; ++e) {
-      const int bin = NB - 1 - PER * lane - e;
-      const u64 m = hm[bin];
-      if (run < T && run + m >= T) {
-        *out_bin = (uint32_t)bin;
-        *out_above = run;
-        break;
-      }
-      run += m;
-    }
-  }
+// A key range [lo, hi] is cut into slices of 2^s consecutive key values, s the smallest
+// shift that leaves at most NB slices; the slice of a key is a shift (monotone in key).
+constexpr int NB_LOG2 = 10;
+static_assert(NB == 1 << NB_LOG2, "NB is a power of two");
+
+__device__ __forceinline__ int range_shift(uint32_t lo, uint32_t hi) {
+  const uint32_t d = hi - lo;
+  const int bits = d == 0u ? 0 : 32 - __clz((int)d);
+  return bits > NB_LOG2 ? bits - NB_LOG2 : 0;
 }
 
-// Bin of `key` among NB equal slices of the integer key range [lo, lo + span); monotone in key.
-__device__ __forceinline__ uint32_t range_bin(uint32_t key, uint32_t lo, u64 span) {
-  return (uint32_t)(((u64)(key - lo) * (u64)NB) / span);
+__device__ __forceinline__ uint32_t range_bin(uint32_t key, uint32_t lo, int shift) { return (key - lo) >> shift; }
+
+// Key range of slice b of [lo, hi].
+__device__ __forceinline__ void slice_range(uint32_t lo, uint32_t hi, uint32_t b, uint32_t* nlo, uint32_t* nhi) {
+  const int shift = range_shift(lo, hi);
+  const u64 a = (u64)lo + ((u64)b << shift);
+  const u64 e = a + ((u64)1 << shift) - 1;
+  *nlo = (uint32_t)a;
+  *nhi = e < (u64)hi ? (uint32_t)e : hi;
 }
 
-// Key range of slice b of [lo, lo + span).
-__device__ __forceinline__ void slice_range(uint32_t lo, u64 span, uint32_t b, uint32_t* nlo, uint32_t* nhi) {
-  *nlo = lo + (uint32_t)(((u64)b * span + NB - 1) / NB);
-  *nhi = lo + (uint32_t)((((u64)b + 1) * span + NB - 1) / NB) - 1;
-}
-
-// Key window of the fine histogram: 20 binades of fp32 around the uniform mass 1/n
-// (from 2^-16/n to 16/n), cut in NB slices of 1/51 binade.
-__device__ __forceinline__ void fine_window(int n, uint32_t* lo, u64* span) {
+// Key window of the fine histogram: 16 binades of fp32 masses, from 2^-12/n to 16/n
+// around the uniform mass 1/n, in NB slices of 1/64 binade.  Keys below it hold less
+// than 2^-12 of the total mass together.
+constexpr int FINE_SHIFT = 27 - NB_LOG2;
+__device__ __forceinline__ void fine_window(int n, uint32_t* lo, uint32_t* hi) {
   const uint32_t ref = __float_as_uint(1.0f / (float)n);
-  *lo = ref - (16u << 23);
-  *span = (u64)20 << 23;
+  *lo = ref - (12u << 23);
+  *hi = *lo + (1u << 27) - 1u;
 }
 
-// Selection state of one workgroup (LDS).
-template <int NT>
-struct SelSh {
-  uint32_t ckey[CAND];
-  uint32_t cpos[CAND];
-  uint32_t hcnt[NB];
-  u64 hmass[NB];
-  u64 red64[2 * (NT / 64)];
-  uint32_t scan[NT / 64];
-  uint32_t bin, ncand, neq;
-  int lastpos;
-  u64 above, T;
-};
-
-template <int NT>
-__device__ __forceinline__ void hist_clear(SelSh<NT>& sh) {
-  for (int i = threadIdx.x; i < NB; i += NT) { sh.hcnt[i] = 0; sh.hmass[i] = 0; }
-}
-
-template <int NT>
-__device__ __forceinline__ u64 block_sum_u64(u64 x, u64* red) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  __syncthreads();
-  if (lane == 0) red[wave] = x;
-  __syncthreads();
-  u64 t = 0;
-  for (int w = 0; w < NW; ++w) t += red[w];
-  return t;
-}
-
-// Histogram of keys[0, n) over the slices of [lo, lo + span) (keys outside are skipped).
-template <int NT>
-__device__ __forceinline__ void hist_keys(SelSh<NT>& sh, const uint32_t* keys, int n, uint32_t lo, u64 span) {
-  const uint32_t hi = (uint32_t)((u64)lo + span - 1);
-  for (int i = threadIdx.x; i < n; i += NT) {
-    const uint32_t k = keys[i];
-    if (k >= lo && k <= hi) {
-      const uint32_t bn = range_bin(k, lo, span);
-      atomicAdd(&sh.hcnt[bn], 1u);
-      atomicAdd(&sh.hmass[bn], fx_mass(k));
-    }
-  }
-}
-
-// With sh.hmass a histogram of [lo, lo + span) holding the cut and sh.above the mass of
-// every key above the range, refine NB-fold per step over keys[0, n) until one key value
-// remains.  Returns tau; sh.above ends as the mass of the keys above tau.
-template <int NT>
-__device__ __forceinline__ uint32_t refine_cut(SelSh<NT>& sh, const uint32_t* keys, int n, uint32_t lo, u64 span,
-                                               u64 T) {
-  const int wave = threadIdx.x >> 6;
-  if (wave == 0) find_bin(sh.hmass, sh.above, T, &sh.bin, &sh.above);
-  __syncthreads();
-  uint32_t nlo, nhi;
-  slice_range(lo, span, sh.bin, &nlo, &nhi);
-  while (nhi > nlo) {
-    const uint32_t l2 = nlo;
-    const u64 s2 = (u64)nhi - nlo + 1;
-    __syncthreads();
-    hist_clear(sh);
-    __syncthreads();
-    hist_keys<NT>(sh, keys, n, l2, s2);
-    __syncthreads();
-    if (wave == 0) find_bin(sh.hmass, sh.above, T, &sh.bin, &sh.above);
-    __syncthreads();
-    slice_range(l2, s2, sh.bin, &nlo, &nhi);
-  }
-  return nlo;
-}
-
-// Ties at the cut all carry the same mass: the fewest that reach T.
+// Ties at the cut all carry the same mass: the fewest that reach T, ceil((T - above) / mt).
+// Both operands are below 2^42, so the double quotient is within one of the answer and
+// one exact integer correction each way settles it.
 __device__ __forceinline__ uint32_t ties_to_take(uint32_t tau, u64 T, u64 above) {
   const u64 mt = fx_mass(tau) > 0 ? fx_mass(tau) : 1;  // the cut element always carries mass
-  return (uint32_t)((T - above + mt - 1) / mt);
+  const u64 need = T - above;
+  u64 q = (u64)((double)need / (double)mt);
+  if (q * mt < need) ++q;
+  if (q > 0 && (q - 1) * mt >= need) --q;
+  return (uint32_t)q;
 }
 
 __device__ __forceinline__ u64 target_of(float p, u64 total) {
@@ -436,130 +367,468 @@ __device__ __forceinline__ u64 target_of(float p, u64 total) {
   return T;
 }
 
+// Four keys at pos (a multiple of 4) from a buffer of ncap readable keys (a multiple of 4,
+// at least 4): the address is clamped, so the load never branches; callers mask by count.
+__device__ __forceinline__ uint4 load4c(const uint32_t* k, int pos, int ncap) {
+  return *(const uint4*)(k + min(pos, ncap - 4));
+}
+
+
+// Selection state of one workgroup (LDS).  ST = 512 threads: two waves per SIMD keep the
+// throughput phases at full issue rate while a serial step waits only on its own
+// instruction latency.  Each thread owns two histogram bins.
+constexpr int ST = 512;
+constexpr int BPT = NB / ST;             // histogram bins per thread
+static_assert(BPT == 2, "two bins per thread");
+constexpr int RMAX = 64;                 // crossing-slice keys resolved by ranking
+
+struct CutSh {
+  uint32_t hcnt[NB];
+  u64 hmass[NB];
+  uint32_t rkey[RMAX];
+  uint32_t rpos[RMAX];
+  u64 rmass[RMAX];
+  u64 red64[ST / 64];
+  uint32_t scan[ST / 64];
+  uint32_t bin, ncand, tau;
+  int lastpos, tie_last;
+  u64 above;
+};
+
+__device__ __forceinline__ void hist_clear(CutSh& sh) {
+#pragma unroll
+  for (int e = 0; e < BPT; ++e) {
+    sh.hcnt[threadIdx.x + ST * e] = 0;
+    sh.hmass[threadIdx.x + ST * e] = 0;
+  }
+}
+
+// Histogram over the slices of [lo, hi] of the keys src[0, n) (keys outside are skipped);
+// keys (16-byte aligned) are read 16 per thread per round trip.
+__device__ __forceinline__ void hist_keys(CutSh& sh, const uint32_t* src, int n, int ncap, uint32_t lo, uint32_t hi) {
+  const int shift = range_shift(lo, hi);
+  for (int base = 16 * threadIdx.x; base < n; base += 16 * ST) {
+    uint4 kv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kv[j] = load4c(src, base + 4 * j, ncap);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t k4[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t k = k4[e];
+        if (base + 4 * j + e < n && k >= lo && k <= hi) {
+          const uint32_t bn = range_bin(k, lo, shift);
+          atomicAdd(&sh.hcnt[bn], 1u);
+          atomicAdd(&sh.hmass[bn], fx_mass(k));
+        }
+      }
+    }
+  }
+}
+
+// The slice in which the mass, accumulated from the heaviest slice down on top of
+// sh.above, reaches T: thread t owns slices NB-1-2t and NB-2-2t, and a workgroup scan
+// gives every slice the mass above it.  Sets sh.bin and sh.above.
+__device__ __forceinline__ void find_bin(CutSh& sh, u64 T) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const u64 above0 = sh.above;
+  const u64 m0 = sh.hmass[NB - 1 - 2 * tid], m1 = sh.hmass[NB - 2 - 2 * tid];
+  const u64 m = m0 + m1;
+  u64 inc = m;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const u64 y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) sh.red64[wave] = inc;
+  __syncthreads();
+  u64 run = above0 + inc - m;
+#pragma unroll
+  for (int w = 0; w < ST / 64; ++w) run += w < wave ? sh.red64[w] : 0;
+  __syncthreads();
+  if (run < T && run + m0 >= T) {
+    sh.bin = (uint32_t)(NB - 1 - 2 * tid);
+    sh.above = run;
+  } else if (run + m0 < T && run + m >= T) {
+    sh.bin = (uint32_t)(NB - 2 - 2 * tid);
+    sh.above = run + m0;
+  }
+  __syncthreads();
+}
+
+// LDS versions (keys in LDS, position = index): four keys per thread in flight, one
+// short predicated body per key.
+__device__ __forceinline__ void hist_keys_lds(CutSh& sh, const uint32_t* keys, int n, uint32_t lo, uint32_t hi) {
+  const int shift = range_shift(lo, hi);
+  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * ST) {
+    uint32_t k4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) k4[e] = keys[min(i0 + ST * e, n - 1)];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t k = k4[e];
+      if (i0 + ST * e < n && k >= lo && k <= hi) {
+        const uint32_t bn = range_bin(k, lo, shift);
+        atomicAdd(&sh.hcnt[bn], 1u);
+        atomicAdd(&sh.hmass[bn], fx_mass(k));
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void gather_slice_lds(CutSh& sh, const uint32_t* keys, int n, uint32_t lo, uint32_t hi) {
+  if (threadIdx.x == 0) sh.ncand = 0;
+  __syncthreads();
+  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * ST) {
+    uint32_t k4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) k4[e] = keys[min(i0 + ST * e, n - 1)];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = i0 + ST * e;
+      if (i < n && k4[e] >= lo && k4[e] <= hi) {
+        const uint32_t slot = atomicAdd(&sh.ncand, 1u);
+        sh.rkey[slot] = k4[e];
+        sh.rpos[slot] = (uint32_t)i;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Copies the (key, position) pairs of src[0, n) inside [lo, hi] to dk/dp (the caller
+// knows how many there are and sized dk/dp for them).  Positions are src_pos[i], or i
+// itself when src_pos is null.  Keys are read 16 per thread per round trip.
+__device__ __forceinline__ void gather_slice(CutSh& sh, const uint32_t* src, const uint32_t* src_pos, int n,
+                                             int ncap, uint32_t lo, uint32_t hi, uint32_t* dk, uint32_t* dp) {
+  if (threadIdx.x == 0) sh.ncand = 0;
+  __syncthreads();
+  for (int base = 16 * threadIdx.x; base < n; base += 16 * ST) {
+    uint4 kv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kv[j] = load4c(src, base + 4 * j, ncap);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t k4[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = base + 4 * j + e;
+        if (i < n && k4[e] >= lo && k4[e] <= hi) {
+          const uint32_t slot = atomicAdd(&sh.ncand, 1u);
+          dk[slot] = k4[e];
+          dp[slot] = src_pos ? src_pos[i] : (uint32_t)i;
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// The exact cut among the c <= RMAX keys in sh.rkey/rpos, sh.above being the mass of
+// every key above them: each candidate adds up the masses of the candidates ordered
+// before it (mass descending, position ascending); the one whose own mass makes the
+// running total reach T is the last node kept.  Sets sh.tau and sh.tie_last.
+__device__ __forceinline__ void rank_cut(CutSh& sh, int c, u64 T) {
+  const int tid = threadIdx.x;
+  if (tid < c) sh.rmass[tid] = fx_mass(sh.rkey[tid]);
+  __syncthreads();
+  if (tid < c) {
+    const uint32_t mk = sh.rkey[tid], mp = sh.rpos[tid];
+    u64 before = sh.above;
+#pragma unroll 8
+    for (int j = 0; j < c; ++j) {
+      const uint32_t k = sh.rkey[j], q = sh.rpos[j];
+      before += (k > mk || (k == mk && q < mp)) ? sh.rmass[j] : 0;
+    }
+    if (before < T && before + sh.rmass[tid] >= T) {
+      sh.tau = mk;
+      sh.tie_last = (int)mp;
+    }
+  }
+  __syncthreads();
+}
+
+// Position of the n-th (0-based) key equal to tau in position order, by counting scans.
+__device__ __forceinline__ int nth_tie_scan(CutSh& sh, const uint32_t* keys, int nF, int ncap, uint32_t tau,
+                                            uint32_t n) {
+  uint32_t seen = 0;
+  int found = -1;
+  for (int base = 0; base < nF && found < 0; base += 4 * ST) {
+    const int p0 = base + 4 * threadIdx.x;
+    const uint4 kv = load4c(keys, p0, ncap);
+    const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w};
+    uint32_t ne = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ne += (p0 + e < nF && k4[e] == tau) ? 1u : 0u;
+    uint32_t tot;
+    uint32_t ex = block_excl_scan<ST>(ne, &tot, sh.scan) + seen;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (p0 + e < nF && k4[e] == tau) {
+        if (ex == n) sh.lastpos = p0 + e;
+        ++ex;
+      }
+    __syncthreads();
+    seen += tot;
+    found = seen > n ? sh.lastpos : -1;
+    __syncthreads();
+  }
+  return found;
+}
+
+// The cut of LDS keys[0, n) (position = index) given a histogram of [lo, hi] in sh:
+// narrow the range until the crossing slice holds at most RMAX keys, then rank them.
+__device__ __forceinline__ void resolve_cut_lds(CutSh& sh, const uint32_t* keys, int n, uint32_t lo, uint32_t hi,
+                                                u64 T, uint32_t* tau, int* tie_last) {
+  for (;;) {
+    find_bin(sh, T);
+    uint32_t nlo, nhi;
+    slice_range(lo, hi, sh.bin, &nlo, &nhi);
+    const uint32_t cnt = sh.hcnt[sh.bin];
+    if (cnt <= (uint32_t)RMAX) {
+      gather_slice_lds(sh, keys, n, nlo, nhi);
+      rank_cut(sh, (int)cnt, T);
+      *tau = sh.tau;
+      *tie_last = sh.tie_last;
+      return;
+    }
+    if (nhi <= nlo) {  // more than RMAX keys of one value
+      const uint32_t n_take = ties_to_take(nlo, T, sh.above);
+      *tau = nlo;
+      *tie_last = n_take < cnt ? nth_tie_scan(sh, keys, n, SMALL_NODES, nlo, n_take - 1) : 0x7FFFFFFF;
+      return;
+    }
+    lo = nlo;
+    hi = nhi;
+    hist_clear(sh);
+    __syncthreads();
+    hist_keys_lds(sh, keys, n, lo, hi);
+    __syncthreads();
+  }
+}
+
+// The cut of keys[0, n) (position = index) given a histogram of [lo, hi] in sh (sh.above:
+// mass above the range, T within the range).  The range narrows NB-fold per pass until
+// the crossing slice holds at most RMAX keys, which are ranked.  With a candidate buffer
+// (ck/cp, ncap entries), the crossing slice's keys move there once they fit, and later
+// passes scan only them.  A slice of more than RMAX equal keys is split by position.
+// Returns tau and the position of the last kept key equal to tau.
+__device__ __forceinline__ void resolve_cut(CutSh& sh, const uint32_t* keys, int n, int kcap, uint32_t lo, uint32_t hi,
+                                            u64 T, uint32_t* ck, uint32_t* cp, int ncap, uint32_t* tau, int* tie_last) {
+  const uint32_t* sk = keys;
+  const uint32_t* sp = nullptr;
+  int ns = n, scap = kcap;
+  for (;;) {
+    find_bin(sh, T);
+    uint32_t nlo, nhi;
+    slice_range(lo, hi, sh.bin, &nlo, &nhi);
+    const uint32_t cnt = sh.hcnt[sh.bin];
+    if (cnt <= (uint32_t)RMAX) {
+      gather_slice(sh, sk, sp, ns, scap, nlo, nhi, sh.rkey, sh.rpos);
+      rank_cut(sh, (int)cnt, T);
+      *tau = sh.tau;
+      *tie_last = sh.tie_last;
+      return;
+    }
+    if (nhi <= nlo) {  // more than RMAX keys of one value
+      const uint32_t n_take = ties_to_take(nlo, T, sh.above);
+      *tau = nlo;
+      *tie_last = n_take < cnt ? nth_tie_scan(sh, keys, n, kcap, nlo, n_take - 1) : 0x7FFFFFFF;
+      return;
+    }
+    if (ck && !sp && cnt <= (uint32_t)ncap) {
+      gather_slice(sh, sk, sp, ns, scap, nlo, nhi, ck, cp);
+      sk = ck;
+      sp = cp;
+      ns = (int)cnt;
+      scap = ncap;
+    }
+    lo = nlo;
+    hi = nhi;
+    hist_clear(sh);
+    __syncthreads();
+    hist_keys(sh, sk, ns, scap, lo, hi);
+    __syncthreads();
+  }
+}
+
 // --------------------------------------------------------------------------- small levels
 
 struct SmallArgs {
   Level v;
-  const float* scores;    // [U][cap1][G]
+  const float* scores;    // [U][cap1][score row]
   int64_t cap1;
   const float* part;      // [U][W][G][2] scoring partials
-  int W;
+  int W;                  // <= 512
   int32_t* kept;          // [U][capl]
-  int64_t capl;
+  int64_t capl;           // <= SMALL_NODES
+  int npar;               // parent ids read: ceil(capl / C) <= SMALL_NODES / 2
   int32_t* nF_out;        // this level's frontier counts [U]
   int32_t* kept_count;    // [U]
   int32_t* next_nF;       // next level's frontier counts [U]; null at level 1
-  int64_t span_child;     // C^(l-1)
   int G;
   float p;
   int keep_all;
 };
 
-constexpr int SMT = 256;  // threads of the small-level selection
+constexpr int SBATCH = 8;     // frontier positions per thread per load batch
 
-// Whole selection of a frontier of at most SMALL_NODES nodes in one workgroup, in LDS.
-__global__ __launch_bounds__(SMT) void zha_select_small_kernel(SmallArgs a) {
-  __shared__ uint32_t s_keys[SMALL_NODES];
-  __shared__ SelSh<SMT> sh;
-  __shared__ float s_lse[16];
-  __shared__ uint32_t s_mn[SMT / 64], s_mx[SMT / 64];
+struct SmallSh {
+  CutSh cut;
+  alignas(16) uint32_t keys[SMALL_NODES];
+  int32_t par[SMALL_NODES / 2];   // kept parents (C >= 2)
+  uint32_t mn[ST / 64], mx[ST / 64];
+  float lse[16];
+  int last_kept_id;
+};
+
+// Whole selection of a frontier of at most SMALL_NODES nodes in one workgroup: every
+// global read (scoring partials, parent ids, scores) is issued before any result is
+// needed; the masses live in LDS; one histogram over the key range finds the crossing
+// slice, whose keys are ranked; the kept ids are written in order.
+__global__ __launch_bounds__(ST) void zha_select_small_kernel(SmallArgs a) {
+  __shared__ SmallSh sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int u = blockIdx.x;
   const int G = a.G;
+  const int nmax = (int)a.capl;  // >= 1
   const int nF = frontier_size(a.v, u);
-  frontier_lse<SMT>(a.part, a.W, G, u, s_lse);
-  if (tid == 0) sh.lastpos = -1;
+  const int GS = score_stride(G);
+  const float* sc = a.scores + (int64_t)u * a.cap1 * GS;
+  const int32_t* gpar = a.v.parent ? a.v.parent + (int64_t)u * a.v.cap_parent : nullptr;
+
+  // scoring partials (32 lanes per head, W <= 512), parent ids, first batch of scores:
+  // all issued before the first wait, from clamped (always readable) addresses
+  const int ph = tid >> 5, pl = tid & 31;
+  const int phc = min(ph, G - 1);
+  float2 pv[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int i = min(pl + 32 * k, a.W - 1);
+    pv[k] = *(const float2*)(a.part + (((int64_t)u * a.W + i) * G + phc) * 2);
+  }
+  if (gpar) {
+    constexpr int NPL = SMALL_NODES / 2 / ST;
+    int32_t pp[NPL];
+#pragma unroll
+    for (int k = 0; k < NPL; ++k)
+      if (ST * k < a.npar) pp[k] = gpar[min(tid + ST * k, a.npar - 1)];
+#pragma unroll
+    for (int k = 0; k < NPL; ++k)
+      if (ST * k < a.npar) sh.par[tid + ST * k] = pp[k];
+  }
+  float4 sv[SBATCH][4];
+#pragma unroll
+  for (int k = 0; k < SBATCH; ++k)
+    if (ST * k < nmax) load_scores(sc + (int64_t)min(tid + ST * k, nmax - 1) * GS, G, sv[k]);
+  {
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) M = fmaxf(M, pl + 32 * k < a.W ? pv[k].x : -INFINITY);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 32));
+    float S = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const bool ok = pl + 32 * k < a.W && pv[k].x != -INFINITY;
+      S += ok ? pv[k].y * zexp(pv[k].x - M) : 0.0f;
+    }
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) S += __shfl_xor(S, o, 32);
+    if (pl == 0 && ph < G) sh.lse[ph] = M == -INFINITY ? -INFINITY : M + zlog(S);
+    if (tid == 0) { sh.last_kept_id = 0; sh.cut.above = 0; }
+    hist_clear(sh.cut);
+  }
   __syncthreads();
+  float lse[16];
+#pragma unroll
+  for (int h = 0; h < 16; ++h) lse[h] = h < G ? sh.lse[h] : 0.0f;
   const float invG = 1.0f / (float)G;
-  const float* sc = a.scores + (int64_t)u * a.cap1 * G;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int pos = tid; pos < nF; pos += SMT) {
-    float sv[16];
-    load_scores(sc + (int64_t)pos * G, G, true, sv);
-    const uint32_t key = mass_key(sv, s_lse, G, invG);
-    s_keys[pos] = key;
-    mn = min(mn, key);
-    mx = max(mx, key);
+  u64 tot = 0;
+  for (int b0 = 0; b0 < nmax; b0 += ST * SBATCH) {
+#pragma unroll
+    for (int k = 0; k < SBATCH; ++k) {
+      if (b0 + ST * k < nmax) {
+        const int pos = b0 + tid + ST * k;
+        const uint32_t key = mass_key(sv[k], lse, G, invG);
+        const bool ok = pos < nF;
+        if (ok) sh.keys[pos] = key;
+        mn = min(mn, ok ? key : 0xFFFFFFFFu);
+        mx = max(mx, ok ? key : 0u);
+        tot += ok ? fx_mass(key) : 0;
+      }
+    }
+    const int b1 = b0 + ST * SBATCH;
+#pragma unroll
+    for (int k = 0; k < SBATCH; ++k)
+      if (b1 + ST * k < nmax) load_scores(sc + (int64_t)min(b1 + tid + ST * k, nmax - 1) * GS, G, sv[k]);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    tot += __shfl_xor(tot, o);
   }
-  if (lane == 0) { s_mn[wave] = mn; s_mx[wave] = mx; }
-  hist_clear(sh);
+  if (lane == 0) { sh.mn[wave] = mn; sh.mx[wave] = mx; sh.cut.red64[wave] = tot; }
   __syncthreads();
-  uint32_t kmin = s_mn[0], kmax = s_mx[0];
-  for (int w = 1; w < SMT / 64; ++w) { kmin = min(kmin, s_mn[w]); kmax = max(kmax, s_mx[w]); }
-  uint32_t tau = 0, n_take = 0;
-  bool keep_all = a.keep_all || nF == 0;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  u64 total = 0;
+#pragma unroll
+  for (int w = 0; w < ST / 64; ++w) {
+    kmin = min(kmin, sh.mn[w]);
+    kmax = max(kmax, sh.mx[w]);
+    total += sh.cut.red64[w];
+  }
+  uint32_t tau = 0;
+  int tie_last = 0x7FFFFFFF;
+  const bool keep_all = a.keep_all || nF == 0 || total == 0;  // total 0: every mass rounds to zero
   if (!keep_all) {
-    const u64 span = (u64)kmax - kmin + 1;
-    hist_keys<SMT>(sh, s_keys, nF, kmin, span);  // the range covers every key
+    const u64 T = target_of(a.p, total);
     __syncthreads();
-    if (wave == 0) {
-      u64 tot = 0;
-      for (int i = lane; i < NB; i += 64) tot += sh.hmass[i];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
-      if (lane == 0) { sh.T = tot == 0 ? 0 : target_of(a.p, tot); sh.above = 0; }
-    }
+    hist_keys_lds(sh.cut, sh.keys, nF, kmin, kmax);
     __syncthreads();
-    const u64 T = sh.T;
-    if (T == 0) {
-      keep_all = true;  // every mass rounds to zero
-    } else {
-      tau = refine_cut<SMT>(sh, s_keys, nF, kmin, span, T);
-      n_take = ties_to_take(tau, T, sh.above);
-    }
+    resolve_cut_lds(sh.cut, sh.keys, nF, kmin, kmax, T, &tau, &tie_last);
   }
-  // compaction in position order (chunks of SMT * 4 positions)
+  // compaction in position order (chunks of 4 positions per thread)
   int32_t* kept = a.kept + (int64_t)u * a.capl;
-  const int32_t* par = a.v.parent ? a.v.parent + (int64_t)u * a.v.cap_parent : nullptr;
-  uint32_t kept_base = 0, tie_base = 0;
-  for (int base = 0; base < nF; base += SMT * 4) {
+  const int32_t* par = gpar ? sh.par : nullptr;
+  uint32_t kept_base = 0;
+  for (int base = 0; base < nF; base += ST * 4) {
     const int p0 = base + tid * 4;
-    uint32_t ngt = 0, neq = 0;
-    uint32_t k4[4];
+    uint32_t flags = 0, nk = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      k4[e] = p0 + e < nF ? s_keys[p0 + e] : 0u;
-      if (p0 + e < nF) {
-        if (keep_all || k4[e] > tau) ++ngt;
-        else if (k4[e] == tau) ++neq;
-      }
+      const int pos = p0 + e;
+      const uint32_t k = sh.keys[min(pos, nF - 1)];
+      const bool kp = pos < nF && (keep_all || k > tau || (k == tau && pos <= tie_last));
+      flags |= kp ? (1u << e) : 0u;
+      nk += kp ? 1u : 0u;
     }
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan<SMT>((neq << 16) | ngt, &tot, sh.scan);
-    const uint32_t avail = n_take > tie_base ? n_take - tie_base : 0;
-    const uint32_t taken_before = min(ex >> 16, avail);
-    uint32_t take_here = min(neq, avail - taken_before);
-    uint32_t out = kept_base + (ex & 0xFFFFu) + taken_before;
-    int lastp = -1;
+    uint32_t ctot;
+    uint32_t out = kept_base + block_excl_scan<ST>(nk, &ctot, sh.cut.scan);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (p0 + e < nF) {
-        bool keep;
-        if (keep_all || k4[e] > tau) keep = true;
-        else if (k4[e] == tau && take_here > 0) { keep = true; --take_here; }
-        else keep = false;
-        if (keep) {
-          kept[out++] = frontier_id(par, p0 + e, a.v.C, a.v.Cshift);
-          lastp = p0 + e;
-        }
+      if ((flags >> e) & 1u) {
+        const int id = frontier_id(par, p0 + e, a.v.C, a.v.Cshift);
+        kept[out++] = id;
+        if (p0 + e == nF - 1) sh.last_kept_id = id + 1;  // the frontier's last node is kept
       }
     }
-    if (lastp >= 0) atomicMax(&sh.lastpos, lastp);
-    kept_base += (tot & 0xFFFFu) + min(tot >> 16, avail);
-    tie_base += tot >> 16;
-    __syncthreads();
+    kept_base += ctot;
   }
+  __syncthreads();
   if (tid == 0) {
     a.nF_out[u] = nF;
     a.kept_count[u] = (int)kept_base;
     if (a.next_nF) {
-      const int last_id = sh.lastpos >= 0 ? frontier_id(par, sh.lastpos, a.v.C, a.v.Cshift) : 0;
-      a.next_nF[u] = next_frontier((int)kept_base, last_id, a.v.C, child_nodes(a.v, u, a.span_child));
+      // every kept node has C children except possibly the level's last node, which can
+      // only be the frontier's last position
+      const int C = a.v.C;
+      int nx = C * (int)kept_base;
+      if (sh.last_kept_id > 0) nx = next_frontier((int)kept_base, sh.last_kept_id - 1, C, child_nodes(a.v, u));
+      a.next_nF[u] = nx;
     }
   }
 }
@@ -568,7 +837,7 @@ __global__ __launch_bounds__(SMT) void zha_select_small_kernel(SmallArgs a) {
 
 struct MassArgs {
   Level v;
-  const float* scores;    // [U][cap1][G]
+  const float* scores;    // [U][cap1][score row]
   int64_t cap1;
   const float* part;      // [U][W][G][2] scoring partials
   int W;
@@ -593,23 +862,24 @@ __global__ __launch_bounds__(256) void zha_mass_kernel(MassArgs a) {
   const int start = blockIdx.x * per, end = min(nF, start + per);
   if (start >= end) return;
   const int G = a.G;
-  frontier_lse<256>(a.part, a.W, G, u, s_lse);
+  const int GS = score_stride(G);
+  const float* sc = a.scores + (int64_t)u * a.cap1 * GS;
+  // the first batch of scores is in flight while the frontier's LSE is formed
+  float4 sv[MASS_BATCH][4];
+#pragma unroll
+  for (int k = 0; k < MASS_BATCH; ++k) load_scores(sc + (int64_t)min(start + tid + 256 * k, end - 1) * GS, G, sv[k]);
+  frontier_lse256(a.part, a.W, G, u, s_lse);
   for (int i = tid; i < NB; i += 256) { h_cnt[i] = 0; h_mass[i] = 0; }
   __syncthreads();
-  uint32_t wlo;
-  u64 wspan;
-  fine_window(nF, &wlo, &wspan);
-  const uint32_t whi = (uint32_t)((u64)wlo + wspan - 1);
+  uint32_t wlo, whi;
+  fine_window(nF, &wlo, &whi);
   const float invG = 1.0f / (float)G;
-  const float* sc = a.scores + (int64_t)u * a.cap1 * G;
   uint32_t* keys = a.keys + (int64_t)u * a.kstride;
   u64 am = 0, bm = 0;
   for (int p0 = start + tid; p0 < end; p0 += 256 * MASS_BATCH) {
-    float sv[MASS_BATCH][16];
+    if (p0 > start + tid) {
 #pragma unroll
-    for (int k = 0; k < MASS_BATCH; ++k) {
-      const int pos = p0 + 256 * k;
-      load_scores(sc + (int64_t)pos * G, G, pos < end, sv[k]);
+      for (int k = 0; k < MASS_BATCH; ++k) load_scores(sc + (int64_t)min(p0 + 256 * k, end - 1) * GS, G, sv[k]);
     }
 #pragma unroll
     for (int k = 0; k < MASS_BATCH; ++k) {
@@ -619,7 +889,7 @@ __global__ __launch_bounds__(256) void zha_mass_kernel(MassArgs a) {
         keys[pos] = key;
         if (key > whi) am += fx_mass(key);
         else if (key >= wlo) {
-          const uint32_t bn = range_bin(key, wlo, wspan);
+          const uint32_t bn = range_bin(key, wlo, FINE_SHIFT);
           atomicAdd(&h_cnt[bn], 1u);
           atomicAdd(&h_mass[bn], fx_mass(key));
         } else bm += fx_mass(key);
@@ -658,52 +928,18 @@ struct LargeArgs {
   float p;
 };
 
-constexpr int LGT = 1024;  // threads of the large-level selection
+// Resolves the cut of a large frontier.  The first histogram is the fine one built by
+// the mass kernel when the cut lies in its window, else one of every key over their
+// whole range.  Output per unit: tau, and the position of the last kept key equal to
+// tau (equal keys are taken in position order), so that the compaction is a
+// per-position test.
+constexpr int LCAND = 8192;  // crossing-slice keys of a large level held in LDS
 
-__device__ __forceinline__ uint4 load4(const uint32_t* k, int pos, int n) {
-  if (pos + 3 < n) return *(const uint4*)(k + pos);
-  uint4 r = {0u, 0u, 0u, 0u};
-  if (pos < n) r.x = k[pos];
-  if (pos + 1 < n) r.y = k[pos + 1];
-  if (pos + 2 < n) r.z = k[pos + 2];
-  return r;
-}
-
-// Position of the n-th (0-based) key equal to tau in position order, by counting scans.
-__device__ __forceinline__ int nth_tie_scan(SelSh<LGT>& sh, const uint32_t* keys, int nF, uint32_t tau, uint32_t n) {
-  uint32_t seen = 0;
-  int found = -1;
-  for (int base = 0; base < nF && found < 0; base += 4 * LGT) {
-    const int p0 = base + 4 * threadIdx.x;
-    const uint4 kv = load4(keys, p0, nF);
-    const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w};
-    uint32_t ne = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ne += (p0 + e < nF && k4[e] == tau) ? 1u : 0u;
-    uint32_t tot;
-    uint32_t ex = block_excl_scan<LGT>(ne, &tot, sh.scan) + seen;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (p0 + e < nF && k4[e] == tau) {
-        if (ex == n) sh.lastpos = p0 + e;
-        ++ex;
-      }
-    __syncthreads();
-    seen += tot;
-    found = seen > n ? sh.lastpos : -1;
-    __syncthreads();
-  }
-  return found;
-}
-
-// Resolves the cut of a large frontier from the fine histogram: the crossing slice's
-// keys (with their positions) are gathered into LDS and refined.  A cut outside the
-// window, or a slice too full for LDS, falls back to refining over every key.
-// Output per unit: tau, and the position of the last tie at tau that is kept (ties are
-// taken in position order), so that the compaction is a per-position test.
-__global__ __launch_bounds__(LGT) void zha_select_large_kernel(LargeArgs a) {
-  __shared__ SelSh<LGT> sh;
+__global__ __launch_bounds__(ST) void zha_select_large_kernel(LargeArgs a) {
+  __shared__ CutSh sh;
+  __shared__ uint32_t s_ck[LCAND], s_cp[LCAND];
   __shared__ u64 s_tot[2];
+  __shared__ uint32_t s_mn[ST / 64], s_mx[ST / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int u = blockIdx.x;
   const int nF = frontier_size(a.v, u);
@@ -711,143 +947,71 @@ __global__ __launch_bounds__(LGT) void zha_select_large_kernel(LargeArgs a) {
   uint32_t* gc = a.fh_cnt + (int64_t)u * NB;
   u64* gm = a.fh_mass + (int64_t)u * NB;
   // take the unit's histogram and leave it zeroed for the next level
-  for (int i = tid; i < NB; i += LGT) {
-    sh.hcnt[i] = gc[i];
-    sh.hmass[i] = gm[i];
+#pragma unroll
+  for (int e = 0; e < BPT; ++e) {
+    sh.hcnt[tid + ST * e] = gc[tid + ST * e];
+    sh.hmass[tid + ST * e] = gm[tid + ST * e];
   }
   if (tid < 2) s_tot[tid] = a.fh_edge[u * 2 + tid];
   __syncthreads();
-  for (int i = tid; i < NB; i += LGT) { gc[i] = 0; gm[i] = 0; }
+#pragma unroll
+  for (int e = 0; e < BPT; ++e) {
+    gc[tid + ST * e] = 0;
+    gm[tid + ST * e] = 0;
+  }
   if (tid < 2) a.fh_edge[u * 2 + tid] = 0;
+  // window mass: workgroup sum of the bins
+  u64 wm = sh.hmass[tid] + sh.hmass[tid + ST];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) wm += __shfl_xor(wm, o);
+  if (lane == 0) sh.red64[wave] = wm;
+  __syncthreads();
+  wm = 0;
+#pragma unroll
+  for (int w = 0; w < ST / 64; ++w) wm += sh.red64[w];
+  const u64 above = s_tot[0], total = above + wm + s_tot[1];
   uint32_t tau = 0;
   int tie_last = 0x7FFFFFFF;
-  int keep_all = nF == 0;
+  const bool keep_all = nF == 0 || total == 0;  // total 0: every mass rounds to zero
   if (!keep_all) {
-    if (wave == 0) {
-      u64 wm = 0;
-      for (int i = lane; i < NB; i += 64) wm += sh.hmass[i];
+    const u64 T = target_of(a.p, total);
+    uint32_t lo, hi;
+    __syncthreads();
+    if (T > above && T <= above + wm) {  // the cut lies in the window
+      fine_window(nF, &lo, &hi);
+      if (tid == 0) sh.above = above;
+    } else {
+      // every key over its whole range
+      uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+      for (int base = 4 * tid; base < nF; base += 4 * ST) {
+        const uint4 kv = load4c(keys, base, (int)a.kstride);
+        const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) wm += __shfl_xor(wm, o);
-      if (lane == 0) {
-        const u64 above = s_tot[0], below = s_tot[1], total = above + wm + below;
-        const u64 T = total == 0 ? 0 : target_of(a.p, total);
-        sh.T = T;
-        sh.above = above;
-        sh.ncand = (T > above && T <= above + wm) ? 1u : 0u;  // the cut lies in the window
+        for (int e = 0; e < 4; ++e)
+          if (base + e < nF) { mn = min(mn, k4[e]); mx = max(mx, k4[e]); }
       }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+      }
+      if (lane == 0) { s_mn[wave] = mn; s_mx[wave] = mx; }
+      hist_clear(sh);
+      if (tid == 0) sh.above = 0;
+      __syncthreads();
+      lo = 0xFFFFFFFFu;
+      hi = 0u;
+#pragma unroll
+      for (int w = 0; w < ST / 64; ++w) { lo = min(lo, s_mn[w]); hi = max(hi, s_mx[w]); }
+      hist_keys(sh, keys, nF, (int)a.kstride, lo, hi);
     }
     __syncthreads();
-    const u64 T = sh.T;
-    if (T == 0) {
-      keep_all = 1;  // every mass rounds to zero
-    } else {
-      uint32_t wlo;
-      u64 wspan;
-      fine_window(nF, &wlo, &wspan);
-      bool gathered = false;
-      int nc = 0;
-      uint32_t nlo = 0, nhi = 0;
-      if (sh.ncand == 1u) {
-        if (wave == 0) find_bin(sh.hmass, sh.above, T, &sh.bin, &sh.above);
-        __syncthreads();
-        slice_range(wlo, wspan, sh.bin, &nlo, &nhi);
-        const uint32_t cnt = sh.hcnt[sh.bin];
-        __syncthreads();
-        if (cnt <= (uint32_t)CAND) {
-          if (tid == 0) sh.ncand = 0;
-          __syncthreads();
-          for (int base = 4 * tid; base < nF; base += 4 * LGT * 2) {
-            uint4 kv[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) kv[j] = load4(keys, base + 4 * LGT * j, nF);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const uint32_t ks[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int pos = base + 4 * LGT * j + e;
-                if (pos < nF && ks[e] >= nlo && ks[e] <= nhi) {
-                  const uint32_t slot = atomicAdd(&sh.ncand, 1u);
-                  sh.ckey[slot] = ks[e];
-                  sh.cpos[slot] = (uint32_t)pos;
-                }
-              }
-            }
-          }
-          __syncthreads();
-          nc = (int)sh.ncand;
-          gathered = true;
-        }
-      }
-      if (gathered) {
-        // refine within the crossing slice over the gathered keys (sh.above: mass above it)
-        if (nhi > nlo) {
-          const u64 span = (u64)nhi - nlo + 1;
-          hist_clear(sh);
-          __syncthreads();
-          hist_keys<LGT>(sh, sh.ckey, nc, nlo, span);
-          __syncthreads();
-          tau = refine_cut<LGT>(sh, sh.ckey, nc, nlo, span, T);
-        } else {
-          tau = nlo;
-        }
-      } else {
-        // general path: every key, over the whole key range
-        uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-        for (int i = tid; i < nF; i += LGT) { mn = min(mn, keys[i]); mx = max(mx, keys[i]); }
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-          mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-          mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-        }
-        if (lane == 0) { sh.scan[wave] = mn; sh.red64[wave] = mx; }
-        __syncthreads();
-        uint32_t kmin = sh.scan[0], kmax = (uint32_t)sh.red64[0];
-        for (int w = 1; w < LGT / 64; ++w) { kmin = min(kmin, sh.scan[w]); kmax = max(kmax, (uint32_t)sh.red64[w]); }
-        __syncthreads();
-        const u64 span = (u64)kmax - kmin + 1;
-        hist_clear(sh);
-        if (tid == 0) sh.above = 0;
-        __syncthreads();
-        hist_keys<LGT>(sh, keys, nF, kmin, span);
-        __syncthreads();
-        tau = refine_cut<LGT>(sh, keys, nF, kmin, span, T);
-      }
-      const uint32_t n_take = ties_to_take(tau, T, sh.above);
-      // ties: the n_take lowest positions among keys equal to tau are kept
-      __syncthreads();
-      if (tid == 0) sh.neq = 0;
-      __syncthreads();
-      if (gathered) {
-        for (int i = tid; i < nc; i += LGT)
-          if (sh.ckey[i] == tau) atomicAdd(&sh.neq, 1u);
-        __syncthreads();
-        const uint32_t neq = sh.neq;
-        if (n_take < neq) {
-          // rank each tie by position (ties are rare; only counted when the cut splits them)
-          if (tid == 0) sh.lastpos = -1;
-          __syncthreads();
-          for (int i = tid; i < nc; i += LGT) {
-            if (sh.ckey[i] != tau) continue;
-            uint32_t rank = 0;
-            for (int j = 0; j < nc; ++j) rank += (sh.ckey[j] == tau && sh.cpos[j] < sh.cpos[i]) ? 1u : 0u;
-            if (rank == n_take - 1) sh.lastpos = (int)sh.cpos[i];
-          }
-          __syncthreads();
-          tie_last = sh.lastpos;
-        }
-      } else {
-        for (int i = tid; i < nF; i += LGT)
-          if (keys[i] == tau) atomicAdd(&sh.neq, 1u);
-        __syncthreads();
-        if (n_take < sh.neq) tie_last = nth_tie_scan(sh, keys, nF, tau, n_take - 1);
-      }
-    }
+    resolve_cut(sh, keys, nF, (int)a.kstride, lo, hi, T, s_ck, s_cp, LCAND, &tau, &tie_last);
   }
   if (tid == 0) {
     a.cut[u * 4 + 0] = (int32_t)tau;
     a.cut[u * 4 + 1] = tie_last;
-    a.cut[u * 4 + 2] = keep_all;
+    a.cut[u * 4 + 2] = keep_all ? 1 : 0;
   }
 }
 
@@ -860,26 +1024,22 @@ struct CompactArgs {
   u64* status;            // [U][nchunk] look-back words
   int nchunk;
   uint32_t* epoch;        // [2]: epoch of this launch's status words (starts at 1), finished workgroups
-  int32_t* last_pos;      // [U] largest kept position (max-reduced; reset by the last chunk)
   int32_t* kept;          // [U][capl]
   int64_t capl;
   int32_t* nF_out;
   int32_t* kept_count;
   int32_t* next_nF;       // null at level 1
-  int64_t span_child;
   int32_t* lb_error;      // set when a look-back wait gives up (never expected)
 };
 
-constexpr int CPT = 256;  // compaction threads; 4 positions each (CH = 1024 per workgroup)
+constexpr int CPT = 256;  // compaction threads
+constexpr int CPP = 16;   // positions per thread (contiguous)
+static_assert(CH == CPT * CPP, "compaction chunk");
 
 __device__ __forceinline__ u64 lb_word(uint32_t epoch, int inclusive, uint32_t count) {
   return ((u64)epoch << 32) | ((u64)inclusive << 31) | (u64)count;
 }
 
-// Writes the kept ids of one chunk of positions, in order.  Position i is kept when its
-// key is above the cut, or equals it and i is not after the last kept tie.  The kept
-// counts of earlier chunks arrive by a decoupled look-back over per-chunk status words
-// (chunk c waits only on chunks < c, which are dispatched before it).
 __device__ __forceinline__ void compact_epilogue(const CompactArgs& a) {
   // the last workgroup of the launch advances the epoch: every workgroup read it before finishing
   __syncthreads();
@@ -893,9 +1053,50 @@ __device__ __forceinline__ void compact_epilogue(const CompactArgs& a) {
   }
 }
 
+// Kept count of the chunks before chunk c (c >= 1), by a decoupled look-back run by one
+// wave: lane l reads the status word of chunk c-1-l, all 64 at once, waiting (bounded) on
+// words not yet published in this epoch; the nearest inclusive word ends the walk, else
+// the window moves 64 chunks back.
+__device__ __forceinline__ uint32_t look_back(const u64* st, int c, uint32_t epoch, int32_t* lb_error) {
+  const int lane = threadIdx.x & 63;
+  uint32_t before = 0;
+  for (int top = c - 1; top >= 0; top -= 64) {
+    const int j = top - lane;
+    u64 w = lb_word(epoch, 1, 0);  // past chunk 0: nothing more to add
+    if (j >= 0) {
+      int spins = 0;
+      for (;;) {
+        w = __hip_atomic_load(&st[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(w >> 32) == epoch) break;
+        if (++spins > (1 << 22)) {  // bounded wait: flag and continue rather than hang
+          atomicExch(lb_error, 1);
+          w = lb_word(epoch, 1, 0);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    const bool incl = ((w >> 31) & 1u) != 0;
+    const u64 mask = __ballot(incl);
+    const int first = mask ? __ffsll((unsigned long long)mask) - 1 : 64;
+    uint32_t v = lane <= first ? (uint32_t)(w & 0x7FFFFFFFu) : 0u;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    before += v;
+    if (mask) break;
+  }
+  return before;
+}
+
+// Writes the kept ids of one chunk of CH positions, in order.  Position i is kept when its
+// key is above the cut, or equals it and i is not after the last kept tie.  The kept
+// counts of earlier chunks arrive by the look-back (chunk c waits only on chunks < c,
+// which are dispatched before it).  The chunk holding the frontier's last position writes
+// the level's counts.
 __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
   __shared__ uint32_t s_scan[CPT / 64];
   __shared__ uint32_t s_before, s_epoch;
+  __shared__ int s_last_kept;
   const int tid = threadIdx.x;
   const int u = blockIdx.y, c = blockIdx.x;
   const int nF = frontier_size(a.v, u);
@@ -909,80 +1110,65 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
   const uint32_t tau = (uint32_t)a.cut[u * 4 + 0];
   const int tie_last = a.cut[u * 4 + 1];
   const uint32_t* keys = a.keys + (int64_t)u * a.kstride;
-  const int p0 = base + 4 * tid;
-  uint32_t k4[4] = {0u, 0u, 0u, 0u};
-  if (!keep_all) {
-    const uint4 kv = load4(keys, p0, nF);
-    k4[0] = kv.x; k4[1] = kv.y; k4[2] = kv.z; k4[3] = kv.w;
-  }
-  bool kp[4];
-  uint32_t nk = 0;
-  int last_local = -1;
+  const int32_t* par = a.v.parent ? a.v.parent + (int64_t)u * a.v.cap_parent : nullptr;
+  const int p0 = base + CPP * tid;
+  uint4 kv[CPP / 4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int pos = p0 + e;
-    kp[e] = pos < nF && (keep_all || k4[e] > tau || (k4[e] == tau && pos <= tie_last));
-    if (kp[e]) { ++nk; last_local = pos; }
+  for (int j = 0; j < CPP / 4; ++j) kv[j] = load4c(keys, p0 + 4 * j, (int)a.kstride);
+  // node ids of the positions (independent of the prefix: loaded before the look-back)
+  int id[CPP];
+#pragma unroll
+  for (int e = 0; e < CPP; ++e) id[e] = frontier_id(par, min(p0 + e, nF - 1), a.v.C, a.v.Cshift);
+  uint32_t flags = 0;
+#pragma unroll
+  for (int j = 0; j < CPP / 4; ++j) {
+    const uint32_t k4[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int pos = p0 + 4 * j + e;
+      const bool kp = pos < nF && (keep_all || k4[e] > tau || (k4[e] == tau && pos <= tie_last));
+      flags |= kp ? (1u << (4 * j + e)) : 0u;
+    }
   }
   uint32_t tot;
-  const uint32_t ex = block_excl_scan<CPT>(nk, &tot, s_scan);
-  // largest kept position of the unit, raised (device-scope atomic, completed: its
-  // returned value is used below) before this chunk's status word is published
-  __shared__ int s_lp[CPT / 64];
-  int lp_old = -1;
-  if (last_local >= 0) lp_old = atomicMax(&a.last_pos[u], last_local);
-  lp_old = max(lp_old, __shfl_xor(lp_old, 32));
-  if ((tid & 63) == 0) s_lp[tid >> 6] = lp_old;
-  __syncthreads();
-  const int lp_seen = max(max(s_lp[0], s_lp[1]), max(s_lp[2], s_lp[3]));
+  const uint32_t ex = block_excl_scan<CPT>((uint32_t)__popc(flags), &tot, s_scan);
   u64* st = a.status + (int64_t)u * a.nchunk;
   const uint32_t epoch = s_epoch;
-  if (tid == 0) {
-    uint32_t before = 0;
-    const uint32_t dep = lp_seen < -1 ? 1u : 0u;  // always 0: orders the publish after the atomics
-    if (c == 0) {
-      __hip_atomic_store(&st[0], lb_word(epoch, 1, tot + dep), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      __hip_atomic_store(&st[c], lb_word(epoch, 0, tot + dep), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      for (int i = c - 1; i >= 0; --i) {
-        u64 w = 0;
-        int spins = 0;
-        for (;;) {
-          w = __hip_atomic_load(&st[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          if ((uint32_t)(w >> 32) == epoch) break;
-          if (++spins > (1 << 22)) {  // bounded wait: flag and continue rather than hang
-            atomicExch(a.lb_error, 1);
-            w = lb_word(epoch, 1, 0);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-        before += (uint32_t)(w & 0x7FFFFFFFu);
-        if ((w >> 31) & 1) break;
-      }
+  if (tid == 0)
+    __hip_atomic_store(&st[c], lb_word(epoch, c == 0 ? 1 : 0, tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (c > 0 && tid < 64) {
+    const uint32_t before = look_back(st, c, epoch, a.lb_error);
+    if (tid == 0) {
       __hip_atomic_store(&st[c], lb_word(epoch, 1, before + tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_before = before;
     }
-    s_before = before;
+  } else if (tid == 0) {
+    s_before = 0;
   }
+  if (tid == 0) s_last_kept = 0;
   __syncthreads();
   uint32_t out = s_before + ex;
   int32_t* kept = a.kept + (int64_t)u * a.capl;
-  const int32_t* par = a.v.parent ? a.v.parent + (int64_t)u * a.v.cap_parent : nullptr;
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    if (kp[e]) kept[out++] = frontier_id(par, p0 + e, a.v.C, a.v.Cshift);
-  // the chunk holding the last position finishes the level's counts: by now every earlier
-  // chunk has raised last_pos (before publishing the status words this chunk has read)
+  for (int e = 0; e < CPP; ++e) {
+    if ((flags >> e) & 1u) {
+      kept[out++] = id[e];
+      if (p0 + e == nF - 1) s_last_kept = id[e] + 1;  // the frontier's last node is kept
+    }
+  }
+  __syncthreads();
   if (base + CH >= nF && tid == 0) {
     const uint32_t total = s_before + tot;
     a.nF_out[u] = nF;
     a.kept_count[u] = (int)total;
-    const int lp = __hip_atomic_load(&a.last_pos[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (a.next_nF) {
-      const int last_id = lp >= 0 ? frontier_id(par, lp, a.v.C, a.v.Cshift) : 0;
-      a.next_nF[u] = next_frontier((int)total, last_id, a.v.C, child_nodes(a.v, u, a.span_child));
+      // every kept node has C children except possibly the level's last node, which can
+      // only be the frontier's last position
+      const int C = a.v.C;
+      int nx = C * (int)total;
+      if (s_last_kept > 0) nx = next_frontier((int)total, s_last_kept - 1, C, child_nodes(a.v, u));
+      a.next_nF[u] = nx;
     }
-    __hip_atomic_store(&a.last_pos[u], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   compact_epilogue(a);
 }
@@ -1037,13 +1223,15 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     v.parent = l < L ? t->kept[l + 1] : nullptr;
     v.parent_nF = l < L ? cntF + (int64_t)l * U : nullptr;  // written by level l+1
     v.cap_parent = l < L ? t->cap[l + 1] : 0;
-    v.span_l = t->span[l];
     v.C = t->C;
     v.Cshift = Cshift;
     v.Hkv = t->desc.n_kv_heads;
-    v.len = t->len;
+    for (int b = 0; b < t->desc.batch; ++b) {
+      const int64_t Nc = ((int64_t)t->len.n[b] / t->C) * t->C;
+      v.nodes[b] = (int32_t)((Nc + t->span[l] - 1) / t->span[l]);
+      v.child[b] = l > 1 ? (int32_t)((Nc + t->span[l - 1] - 1) / t->span[l - 1]) : 0;
+    }
     int32_t* next_nF = l > 1 ? cntF + (int64_t)(l - 1) * U : nullptr;
-    const int64_t span_child = l > 1 ? t->span[l - 1] : 1;
 
     ScoreArgs sa;
     sa.v = v;
@@ -1075,15 +1263,15 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
       sm.W = sa.W;
       sm.kept = t->kept[l];
       sm.capl = t->cap[l];
+      sm.npar = (int)((t->cap[l] + t->C - 1) / t->C);
       sm.nF_out = cntF + (int64_t)l * U;
       sm.kept_count = cntK + (int64_t)l * U;
       sm.next_nF = next_nF;
-      sm.span_child = span_child;
       sm.G = t->G;
       sm.p = p;
       sm.keep_all = keep_all ? 1 : 0;
       zha_time_begin(t, s, ZHA_K_SELECT, l);
-      hipLaunchKernelGGL(zha_select_small_kernel, dim3(U), dim3(SMT), 0, s, sm);
+      hipLaunchKernelGGL(zha_select_small_kernel, dim3(U), dim3(ST), 0, s, sm);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       zha_time_end(t, s, ZHA_K_SELECT, l);
@@ -1120,7 +1308,7 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
       la.cut = t->cut;
       la.p = p;
       zha_time_begin(t, s, ZHA_K_SELECT, l);
-      hipLaunchKernelGGL(zha_select_large_kernel, dim3(U), dim3(LGT), 0, s, la);
+      hipLaunchKernelGGL(zha_select_large_kernel, dim3(U), dim3(ST), 0, s, la);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       zha_time_end(t, s, ZHA_K_SELECT, l);
@@ -1134,13 +1322,11 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     ca.status = (u64*)t->lb_status;
     ca.nchunk = zha_compact_chunks(t->cap[1]);
     ca.epoch = t->lb_epoch;  // device-side: graph replays keep advancing it
-    ca.last_pos = t->last_pos;
     ca.kept = t->kept[l];
     ca.capl = t->cap[l];
     ca.nF_out = cntF + (int64_t)l * U;
     ca.kept_count = cntK + (int64_t)l * U;
     ca.next_nF = next_nF;
-    ca.span_child = span_child;
     ca.lb_error = t->lb_error;
     const int nch = zha_compact_chunks(t->cap[l]);
     zha_time_begin(t, s, ZHA_K_COMPACT, l);
