@@ -146,11 +146,11 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   t->span[0] = 1;
   t->cap[0] = 0;
   const int U = t->U, R = t->R, d = t->d, G = t->G, L = t->L;
-  int ws = 4096 / U;
+  int ws = 1024 / U;  // score workgroups per unit: about four per compute unit in all
   if (ws > 512) ws = 512;
   if (ws < 1) ws = 1;
   t->WS = ws;
-  t->WA = zha_dense_wgs(U);
+  t->WA = zha_sparse_wgs(U);
   bool ok = true;
   for (int l = 1; l <= L && ok; ++l) {
     ok = ok && dalloc(t, &t->m[l], (size_t)U * t->cap[l] * R * d * t->esize);

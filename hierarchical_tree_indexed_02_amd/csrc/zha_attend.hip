@@ -445,6 +445,11 @@ int cshift_of(int C) {
 
 }  // namespace
 
+int zha_sparse_wgs(int U) {
+  int w = 512 / (U > 0 ? U : 1);
+  return w < 1 ? 1 : w;
+}
+
 int zha_dense_wgs(int U) {
   int w = 1024 / (U > 0 ? U : 1);
   return w < 1 ? 1 : w;

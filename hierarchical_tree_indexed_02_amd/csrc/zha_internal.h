@@ -181,4 +181,5 @@ hipError_t zha_launch_dense(const void* q, const void* K, const void* V, const Z
                             int Hkv, int d, int64_t T, zha_dtype dt, float scale, float* out, float* lse,
                             float* part, int WA, hipStream_t s);
 hipError_t zha_launch_copy16(void* dst, const void* src, int64_t n16, hipStream_t s);
+int zha_sparse_wgs(int U);
 int zha_dense_wgs(int U);

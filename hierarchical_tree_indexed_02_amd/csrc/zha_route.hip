@@ -148,7 +148,7 @@ struct ScoreArgs {
 // Lane i loads its row's plane slice (k-slot group i/16) straight from HBM; the
 // query fragments stay in registers for the whole workgroup.
 template <typename T, int R, int D, int UN>
-__global__ __launch_bounds__(256) void zha_score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
   typedef Mf<T> M;
   constexpr int NK = D / M::KPER;
   constexpr int NPT = 16 / R;
@@ -176,29 +176,53 @@ __global__ __launch_bounds__(256) void zha_score_kernel(ScoreArgs a) {
   float* sc = a.scores + (int64_t)u * a.cap1 * GS;
   float runM = -INFINITY, runS = 0.0f;
 
-  for (int base = start; base < end; base += SUPER) {
-    typename M::frag af[UN][NK];
-    float bv[UN][4];
-    int tb[UN];
+  typedef typename M::frag Frag;
+  // Parent entries of this lane's tiles in the super-tile at `base` (the one load a node
+  // id depends on).
+  auto fetch_par = [&](int base, int (&pp)[UN]) {
 #pragma unroll
     for (int k = 0; k < UN; ++k) {
-      tb[k] = base + (k * 4 + wave) * NPT;
-      const int pos = tb[k] + row / R;
+      const int pos = base + (k * 4 + wave) * NPT + row / R;
+      pp[k] = (par && pos < end) ? par[a.v.Cshift >= 0 ? (pos >> a.v.Cshift) : pos / a.v.C] : 0;
+    }
+  };
+  // Plane fragments and offsets of this lane's tiles in the super-tile at `base`.
+  auto load_stage = [&](int base, const int (&pp)[UN], Frag (&af)[UN][NK], float (&bv)[UN][4]) {
+#pragma unroll
+    for (int k = 0; k < UN; ++k) {
+      const int tbk = base + (k * 4 + wave) * NPT;
+      const int pos = tbk + row / R;
       const bool v = pos < end;
-      const int id = v ? frontier_id(par, pos, a.v.C, a.v.Cshift) : 0;
+      int id = pos;
+      if (par) id = a.v.Cshift >= 0 ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
+                                    : pp[k] * a.v.C + pos % a.v.C;
+      id = v ? id : 0;
       const T* mp = mb + ((int64_t)id * R + (row % R)) * D + grp * M::EPL;
 #pragma unroll
       for (int s = 0; s < NK; ++s) af[k][s] = v ? M::load(mp + s * M::KPER) : M::zero();
+      if constexpr (R >= 4) {
+        // rows 4grp..4grp+3 of this lane belong to one node: its four offsets in one load
+        const int id2 = __shfl(id, 4 * grp);
+        const bool v2 = tbk + (4 * grp) / R < end;
+        const float4 b4 = v2 ? *(const float4*)(bb + (int64_t)id2 * R + (4 * grp) % R)
+                             : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        bv[k][0] = b4.x; bv[k][1] = b4.y; bv[k][2] = b4.z; bv[k][3] = b4.w;
+      } else {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r2 = 4 * grp + jj;
-        const int id2 = __shfl(id, r2);
-        const bool v2 = tb[k] + r2 / R < end;
-        bv[k][jj] = v2 ? bb[(int64_t)id2 * R + (r2 % R)] : -INFINITY;
+        for (int jj = 0; jj < 4; ++jj) {
+          const int r2 = 4 * grp + jj;
+          const int id2 = __shfl(id, r2);
+          const bool v2 = tbk + r2 / R < end;
+          bv[k][jj] = v2 ? bb[(int64_t)id2 * R + (r2 % R)] : -INFINITY;
+        }
       }
     }
+  };
+  // Scores of the super-tile at `base` from its loaded planes.
+  auto compute = [&](const Frag (&af)[UN][NK], const float (&bv)[UN][4], int base) {
 #pragma unroll
     for (int k = 0; k < UN; ++k) {
+      const int tbk = base + (k * 4 + wave) * NPT;
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int s = 0; s < NK; ++s) acc = M::mma(af[k][s], qf[s], acc);
@@ -211,7 +235,7 @@ __global__ __launch_bounds__(256) void zha_score_kernel(ScoreArgs a) {
         if (R >= 8) mx = fmaxf(mx, __shfl_xor(mx, 16));
         if (R >= 16) mx = fmaxf(mx, __shfl_xor(mx, 32));
         const bool writer = (R == 4) || (R == 8 && (grp & 1) == 0) || (R == 16 && grp == 0);
-        const int pos = tb[k] + (4 * grp) / R;
+        const int pos = tbk + (4 * grp) / R;
         if (writer && row < G && pos < end) {
           sc[(int64_t)pos * GS + row] = mx;
           lse_push(runM, runS, mx);
@@ -220,7 +244,7 @@ __global__ __launch_bounds__(256) void zha_score_kernel(ScoreArgs a) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const float mx = fmaxf(v[2 * h2], v[2 * h2 + 1]);
-          const int pos = tb[k] + 2 * grp + h2;
+          const int pos = tbk + 2 * grp + h2;
           if (row < G && pos < end) {
             sc[(int64_t)pos * GS + row] = mx;
             lse_push(runM, runS, mx);
@@ -229,7 +253,7 @@ __global__ __launch_bounds__(256) void zha_score_kernel(ScoreArgs a) {
       } else {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const int pos = tb[k] + 4 * grp + jj;
+          const int pos = tbk + 4 * grp + jj;
           if (row < G && pos < end) {
             sc[(int64_t)pos * GS + row] = v[jj];
             lse_push(runM, runS, v[jj]);
@@ -237,6 +261,27 @@ __global__ __launch_bounds__(256) void zha_score_kernel(ScoreArgs a) {
         }
       }
     }
+  };
+
+  // Software pipeline over the workgroup's super-tiles: while one is scored, the planes of
+  // the next and the parent entries of the one after are in flight.  The two register
+  // buffers alternate by unrolling the loop twice.
+  int ppA[UN], ppB[UN];
+  Frag afA[UN][NK], afB[UN][NK];
+  float bvA[UN][4], bvB[UN][4];
+  fetch_par(start, ppA);
+  fetch_par(start + SUPER, ppB);
+  if (start < end) load_stage(start, ppA, afA, bvA);
+  for (int base = start; base < end;) {
+    fetch_par(base + 2 * SUPER, ppA);
+    load_stage(base + SUPER, ppB, afB, bvB);
+    compute(afA, bvA, base);
+    base += SUPER;
+    if (base >= end) break;
+    fetch_par(base + 2 * SUPER, ppB);
+    load_stage(base + SUPER, ppA, afA, bvA);
+    compute(afB, bvB, base);
+    base += SUPER;
   }
   // per-head (max, sum exp) of this workgroup: lanes of one head, then the 4 waves
   {
