@@ -11,7 +11,8 @@
 int zha_score_wgs(const zha_tree* t, int level);
 int zha_compact_chunks(int64_t nodes);
 int zha_hist_bins();
-size_t zha_stack_bytes(int L, int d, int R);
+size_t zha_spine_bytes(int L, int d, int R);
+size_t zha_build_lds_bytes(int S, int L, int d, int R, int esize);
 
 namespace {
 
@@ -23,6 +24,18 @@ zha_status hip_fail(const char* where, hipError_t e) {
 }
 
 bool valid_refs(int R) { return R == 1 || R == 2 || R == 4 || R == 8 || R == 16; }
+
+// Subtree level of the build: the highest level whose nodes cover at most 256 tokens (>= 1).
+int subtree_level(int C, int L) {
+  int S = 1;
+  int64_t span = C;
+  for (int l = 2; l <= L; ++l) {
+    span *= C;
+    if (span > 256) break;
+    S = l;
+  }
+  return S;
+}
 
 zha_status check_desc(const zha_tree_desc* d) {
   if (!d) return ZHA_ERR_INVALID;
@@ -40,7 +53,9 @@ zha_status check_desc(const zha_tree_desc* d) {
   if (d->max_tokens / d->chunk >= ((int64_t)1 << 30)) return ZHA_ERR_UNSUPPORTED;
   double span = pow((double)d->chunk, (double)d->levels);
   if (span > (double)(1 << 30)) return ZHA_ERR_UNSUPPORTED;
-  if (zha_stack_bytes(d->levels, d->head_dim, d->n_refs) > 160 * 1024) return ZHA_ERR_UNSUPPORTED;
+  const int esize = d->dtype == ZHA_BF16 ? 2 : 4;
+  if (zha_build_lds_bytes(subtree_level(d->chunk, d->levels), d->levels, d->head_dim, d->n_refs, esize) > 160 * 1024)
+    return ZHA_ERR_UNSUPPORTED;
   return ZHA_OK;
 }
 
@@ -51,7 +66,7 @@ void free_tree(zha_tree* t) {
     if (t->b[l]) (void)hipFree(t->b[l]);
     if (t->kept[l]) (void)hipFree(t->kept[l]);
   }
-  void* ps[] = {t->refs,   t->spine,  t->counts,    t->scores,   t->spart,    t->keys,     t->apart,
+  void* ps[] = {t->refs,   t->spine,  t->sub_lse, t->sub_m,  t->counts,    t->scores,   t->spart,    t->keys,     t->apart,
                 t->fh_cnt, t->fh_mass,  t->fh_edge,  t->cut,      t->lb_status,
                 t->lb_epoch, t->lb_error};
   for (void* p : ps)
@@ -158,7 +173,12 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
     ok = ok && dalloc(t, &t->kept[l], (size_t)U * t->cap[l] * sizeof(int32_t));
   }
   ok = ok && dalloc(t, &t->refs, (size_t)desc->n_kv_heads * R * d * sizeof(float));
-  ok = ok && dalloc(t, &t->spine, (size_t)U * zha_stack_bytes(L, d, R));
+  ok = ok && dalloc(t, &t->spine, (size_t)U * zha_spine_bytes(L, d, R));
+  t->S = subtree_level(t->C, L);
+  if (t->S < L) {
+    ok = ok && dalloc(t, &t->sub_lse, (size_t)U * t->cap[t->S] * R * sizeof(float));
+    ok = ok && dalloc(t, &t->sub_m, (size_t)U * t->cap[t->S] * R * d * sizeof(float));
+  }
   ok = ok && dalloc(t, &t->counts, (size_t)2 * (L + 2) * U * sizeof(int32_t));
   ok = ok && dalloc(t, &t->scores, (size_t)U * t->cap[1] * ((G + 3) & ~3) * sizeof(float));
   ok = ok && dalloc(t, &t->spart, (size_t)U * t->WS * G * 2 * sizeof(float));

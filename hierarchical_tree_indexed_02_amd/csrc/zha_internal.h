@@ -64,11 +64,20 @@ template <> struct Mf<float> {
 };
 
 // Sum over the 16 lanes of a DPP row (xor butterfly: every lane ends with the same bits).
+// Sum over each row of 16 lanes, the total left in every lane of the row, with four
+// DPP adds (data-parallel-primitive lane moves within a row, no LDS round trip): swap
+// neighbours, swap pairs (each lane then holds its quad's sum), add the half-row mirror
+// (lanes i and 7-i: each lane holds its 8-lane half's sum), add the row mirror (lanes i
+// and 15-i).  Fixed order: every caller gets the same bits for the same inputs.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float sum16(float x) {
-  x += __shfl_xor(x, 8, 16);
-  x += __shfl_xor(x, 4, 16);
-  x += __shfl_xor(x, 2, 16);
-  x += __shfl_xor(x, 1, 16);
+  x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);  // row_half_mirror
+  x += dpp_mov<0x140>(x);  // row_mirror
   return x;
 }
 
@@ -111,8 +120,9 @@ template <int E> __device__ __forceinline__ void acc_fold(Acc<E>& a, float x, co
 
 template <int E> __device__ __forceinline__ void acc_finish(const Acc<E>& a, float& lse, float (&m)[E]) {
   lse = a.M + zlog(a.S);
+  const float inv = 1.0f / a.S;
 #pragma unroll
-  for (int e = 0; e < E; ++e) m[e] = a.V[e] / a.S;
+  for (int e = 0; e < E; ++e) m[e] = a.V[e] * inv;
 }
 #pragma clang fp contract(on)
 
@@ -140,6 +150,9 @@ struct zha_tree {
   int32_t* kept[ZHA_MAX_LEVELS + 2];// per-level kept ids [U][cap]
   float* refs;                      // [Hkv][R][d]
   float* spine;                     // [U][L+1][R*16][E+2] open-node accumulators
+  int S;                            // subtree level of the build (highest level of <= 256 tokens)
+  float* sub_lse;                   // [U][cap_S][R] fp32 LSE of finished level-S nodes (S < L only)
+  float* sub_m;                     // [U][cap_S][R][d] fp32 means of finished level-S nodes
   int32_t* counts;                  // [2][L+2][U]: frontier counts, kept counts per level
   float* scores;                    // [U][cap1][G rounded up to 4]
   float* spart;                     // [U][WS][G][2] score-kernel partial log-sum-exp
