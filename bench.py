@@ -2,9 +2,13 @@
 
 One step = one decode step of one attention layer: route the B x Hq queries
 through that layer's tree (every level) and attend over the kept chunks plus
-sink and tail.  Inputs are resident in HBM before timing; steps cycle through
-`--layers` replicas of (K, V, tree) so every step reads its layer cold, and
-through `--queries` different decode queries.  Prints one JSON line.
+sink and tail.  For a workload with decode-time growth (batch8_append_512k) a
+step first appends one K/V row per sequence (zha_append), then routes and
+attends once for each p of the workload's sweep; `value` is append + route +
+attend at the first p (or --p), and `p_sweep` gives every p.  Inputs are
+resident in HBM before timing; steps cycle through `--layers` replicas of
+(K, V, tree) so every step reads its layer cold, and through `--queries`
+different decode queries.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 40] [--warmup 5] [--config deep_256k]
 """
@@ -79,28 +83,36 @@ def main():
 
     cfg = zi.get_config(args.config)
     p = args.p if args.p is not None else cfg.p[0]
+    growing = cfg.append_steps > 0
+    p_sweep = [p] + [x for x in cfg.p if x != p] if growing else [p]
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     es = 2 if cfg.dtype == "bf16" else 4
     B, Hkv, Hq, d, N = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim, cfg.n_tokens
     U, G, C, L, R = B * Hkv, cfg.group, cfg.chunk, cfg.levels, cfg.n_refs
-    T = N
+    T = cfg.max_tokens  # token stride: room for the rows appended during decode
     nq = min(args.queries, cfg.n_queries)
 
     t0 = time.time()
-    q_host = zi.queries(cfg, n=nq)
+    q_all = zi.queries(cfg)
+    q_host = q_all[:nq]
     K0 = torch.empty((B, Hkv, T, d), dtype=dt, device=dev)
     V0 = torch.empty((B, Hkv, T, d), dtype=dt, device=dev)
     for b in range(B):
         for g in range(Hkv):
-            Ku, Vu = zi.unit_kv(cfg, b, g)
-            K0[b, g] = torch.from_numpy(Ku).to(dev, dt)
-            V0[b, g] = torch.from_numpy(Vu).to(dev, dt)
+            Ku, Vu = zi.unit_kv(cfg, b, g, q_all)
+            K0[b, g, :N] = torch.from_numpy(Ku).to(dev, dt)
+            V0[b, g, :N] = torch.from_numpy(Vu).to(dev, dt)
+            if growing:  # the rows each decode step appends (written by the caller before zha_append)
+                Ka, Va = zi.append_rows(cfg, b, g)
+                K0[b, g, N:] = torch.from_numpy(Ka).to(dev, dt)
+                V0[b, g, N:] = torch.from_numpy(Va).to(dev, dt)
     qd = torch.from_numpy(q_host).to(dev, dt)
     refs = torch.from_numpy(zi.refs(cfg)).to(dev)
     log(f"inputs ready in {time.time() - t0:.1f}s")
 
     lens = [N] * B
+    layer_lens = [[N] * B for _ in range(args.layers)]
     Ks, Vs, trees = [K0], [V0], []
     for _ in range(1, args.layers):
         Ks.append(K0.clone())
@@ -130,9 +142,31 @@ def main():
     outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(args.layers)]
     lses = [torch.empty((B, Hq), dtype=torch.float32, device=dev) for _ in range(args.layers)]
 
-    def step(i):
+    segs = []  # growing workloads: per-step event pairs of append and of each p's route + attend
+
+    def seg(name, fn, record):
+        if record:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            segs[-1][name] = (a, b)
+        else:
+            fn()
+
+    def step(i, record=False):
         li, t = i % args.layers, i % nq
         tr = trees[li]
+        if growing:
+            if record:
+                segs.append({})
+            if layer_lens[li][0] < T:
+                layer_lens[li] = [n + 1 for n in layer_lens[li]]
+                seg("append", lambda: tr.append(Ks[li], layer_lens[li]), record)
+            for x in p_sweep:
+                seg(x, lambda x=x: (tr.route(qd[t], x, 1.0),
+                                    tr.attend(qd[t], Ks[li], Vs[li], 1.0, out=outs[li], lse=lses[li])), record)
+            return
         tr.route(qd[t], p, 1.0)
         tr.attend(qd[t], Ks[li], Vs[li], 1.0, out=outs[li], lse=lses[li])
 
@@ -165,11 +199,18 @@ def main():
     torch.cuda.synchronize()
     ev0.record()
     for i in range(args.steps):
-        step(i)
+        step(i, record=growing)
     ev1.record()
     torch.cuda.synchronize()
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
+    seg_us = {}
+    if growing:
+        for sg in segs:
+            for k, (a, b) in sg.items():
+                seg_us.setdefault(k, []).append(1e3 * a.elapsed_time(b))
+        seg_us = {k: sum(v) / len(v) for k, v in seg_us.items()}
+        ms_step = (seg_us.get("append", 0.0) + seg_us[p]) * 1e-3  # append + route + attend at p
     live = []
     for tr in trees:
         live += [ms for _, _, ms in tr.timing_read()]
@@ -193,17 +234,19 @@ def main():
             if l == 1:
                 nk1 = nk.cpu().numpy()
                 first = ids[:, 0].cpu().numpy()
-                Nc = (N // C) * C
                 for u in range(U):
+                    Nu = layer_lens[0][u // Hkv]
+                    Nc = (Nu // C) * C
                     sink = 1 if (Nc > 0 and (nk1[u] == 0 or first[u] != 0)) else 0
-                    attend_tok += w * (sink + (N - Nc) + int(nk1[u]) * C)
+                    attend_tok += w * (sink + (Nu - Nc) + int(nk1[u]) * C)
     nsteps = args.steps
     route_bytes = sum(fr_tot[l] for l in fr_tot) * S_node / nsteps
     attend_bytes = attend_tok * 2 * d * es / nsteps
     io_bytes = B * Hq * d * es + B * Hq * (d + 1) * 4 + 8 * sum(kept_tot.values()) / nsteps
     step_bytes = route_bytes + attend_bytes + io_bytes
-    kappa = attend_tok / nsteps / (U * N)
-    dense_bytes = U * N * 2 * d * es
+    Ncur = layer_lens[0][0]
+    kappa = attend_tok / nsteps / (U * Ncur)
+    dense_bytes = U * Ncur * 2 * d * es
 
     # the dominant kernel: largest share of the step's time
     if dom_name.startswith("score_l"):
@@ -226,6 +269,8 @@ def main():
                     avg_launch_us=round(dom_live_us, 2))
     log(f"step {ms_step * 1e3:.1f} us, {step_bytes / 1e6:.1f} MB/step ({step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s), "
         f"kappa {kappa:.3f}")
+    if growing:
+        log("  segments (us): " + ", ".join(f"{k}: {v:.1f}" for k, v in seg_us.items()))
     for k, v in kernels.items():
         log(f"  {k:12s} {v['launches']:4d} launches  avg {v['avg_us']:8.2f} us")
 
@@ -236,12 +281,12 @@ def main():
         ws = torch.empty(nb, dtype=torch.uint8, device=dev)
         for i in range(args.warmup):
             li = i % args.layers
-            dense_decode(qd[i % nq], Ks[li], Vs[li], lens, Hkv, 1.0, ws, outs[li], lses[li])
+            dense_decode(qd[i % nq], Ks[li], Vs[li], layer_lens[li], Hkv, 1.0, ws, outs[li], lses[li])
         torch.cuda.synchronize()
         ev0.record()
         for i in range(args.steps):
             li = i % args.layers
-            dense_decode(qd[i % nq], Ks[li], Vs[li], lens, Hkv, 1.0, ws, outs[li], lses[li])
+            dense_decode(qd[i % nq], Ks[li], Vs[li], layer_lens[li], Hkv, 1.0, ws, outs[li], lses[li])
         ev1.record()
         torch.cuda.synchronize()
         dense_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
@@ -251,7 +296,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         import oracle
-        Ku, Vu = zi.unit_kv(cfg, 0, 0)
+        Ku, Vu = zi.unit_kv(cfg, 0, 0, q_all)
         tree_o = oracle.tree_merge(Ku, zi.refs(cfg)[0], C, L)
         ncpu = min(args.cpu_queries, cfg.n_queries)
         qc = zi.queries(cfg, n=ncpu)
@@ -297,6 +342,10 @@ def main():
         "build_us": round(1e3 * float(np.median(build_ms)), 1),
         "kernels": {k: dict(launches=v["launches"], avg_us=round(v["avg_us"], 2)) for k, v in kernels.items()},
     }
+    if growing:
+        result["append_us"] = round(seg_us.get("append", 0.0), 2)
+        result["p_sweep"] = {str(x): round(seg_us.get("append", 0.0) + seg_us[x], 2) for x in p_sweep}
+        result["config"]["appended_per_step"] = 1
     print(json.dumps(result), flush=True)
 
 

@@ -12,7 +12,8 @@
 // its four waves walk 32 positions at a time with an online softmax, and the
 // G query heads of the KV head share every K/V tile.  Q.K^T runs on the matrix
 // cores with K rows loaded straight from HBM into the operand registers; P.V
-// stages the V tile in LDS and reads it transposed.  P is split into two bf16
+// stages the V tile in LDS and reads it transposed.  K and V are read once per step:
+// their loads carry the nontemporal hint so they do not displace reused data in the caches.  P is split into two bf16
 // halves (hi + lo) so the softmax weights keep ~16 significant bits.  Partial
 // (max, sum, o) per workgroup are merged by zha_merge_kernel in fixed order.
 #include "zha_internal.h"
@@ -122,7 +123,7 @@ template <int D> struct PV<__bf16, D> {
     for (int k = 0; k < NLD; ++k) {
       const int ts = RPI * k + lane / CPR;
       const int tok = win.token(P, p0, p0 + ts, end, C, Cshift);
-      vf[k] = *(const bf16x8_t*)(Vb + (int64_t)tok * D + 8 * (lane % CPR));
+      vf[k] = __builtin_nontemporal_load((const bf16x8_t*)(Vb + (int64_t)tok * D + 8 * (lane % CPR)));
     }
   }
   __device__ static __forceinline__ void stage(const vfrag& vf, __bf16* lds, int lane) {
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a) {
       const int tok = win.token(P, p0, p0 + 16 * t + row, end, a.C, a.Cshift);
       const T* kr = Kb + (int64_t)tok * D + grp * M::EPL;
 #pragma unroll
-      for (int s = 0; s < NK; ++s) kf[t][s] = M::load(kr + s * M::KPER);
+      for (int s = 0; s < NK; ++s) kf[t][s] = M::load_stream(kr + s * M::KPER);
     }
     PVT::template load<DENSE>(vf, Vb, P, win, p0, end, a.C, a.Cshift, lane);
   };

@@ -41,6 +41,7 @@ template <> struct Mf<__bf16> {
   static constexpr int EPL = 8;
   static constexpr int KPER = 32;
   __device__ static __forceinline__ frag load(const __bf16* p) { return *(const bf16x8_t*)p; }
+  __device__ static __forceinline__ frag load_stream(const __bf16* p) { return __builtin_nontemporal_load((const bf16x8_t*)p); }
   __device__ static __forceinline__ frag zero() { bf16x8_t z; for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.0f; return z; }
   __device__ static __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -55,6 +56,7 @@ template <> struct Mf<float> {
   static constexpr int EPL = 1;
   static constexpr int KPER = 4;
   __device__ static __forceinline__ frag load(const float* p) { return *p; }
+  __device__ static __forceinline__ frag load_stream(const float* p) { return __builtin_nontemporal_load(p); }
   __device__ static __forceinline__ frag zero() { return 0.0f; }
   __device__ static __forceinline__ f32x4_t mma(frag a, frag b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
