@@ -13,7 +13,7 @@
 //                       HBM once and score them on the matrix cores (G query heads x
 //                       R planes per node is a small dense product), and write the
 //                       per-workgroup (max, sum exp) partials of each head's scores.
-//   levels of <= 16384 nodes: zha_select_small_kernel, one workgroup per unit,
+//   levels of <= 8192 nodes: zha_select_small_kernel, one workgroup per unit,
 //                       forms the node masses, finds the exact cut and compacts, in LDS.
 //   large frontiers:    zha_mass_kernel (many workgroups) forms the masses and an exact
 //                       histogram of them on fixed slices around the uniform mass 1/|F|;
@@ -32,7 +32,7 @@ namespace {
 typedef unsigned long long u64;
 
 constexpr int NB = 1024;                 // histogram slices
-constexpr int SMALL_NODES = 16384;       // frontiers up to this size are selected in one workgroup
+constexpr int SMALL_NODES = 8192;        // frontiers up to this size are selected in one workgroup
 constexpr int CAND = 8192;               // keys of a crossing slice held in LDS
 constexpr int CH = 4096;                 // compaction chunk (positions per workgroup)
 

@@ -55,10 +55,10 @@ VARIANTS = [
     ("bf16 d128 wide C256 L1 R16", dict(batch=1, n_tokens=16484, chunk=256, levels=1, n_refs=16), [16484]),
     ("f32 d64 C4 L4 R16 G1", dict(batch=1, n_tokens=3000, head_dim=64, n_q_heads=1, n_kv_heads=1, chunk=4, levels=4,
                                   n_refs=16, dtype="f32", head_scale=False), [3000]),
-    # levels of up to 16384 nodes are selected by one workgroup (several load batches here);
+    # levels of up to 8192 nodes are selected by one workgroup (two load batches here);
     # larger levels take the multi-workgroup masses, the histogram cut and the look-back compaction
-    ("bf16 d64 C16 L1 R4 G4 mid flat", dict(batch=2, n_tokens=200000, head_dim=64, n_q_heads=8, n_kv_heads=2,
-                                            chunk=16, levels=1, n_refs=4), [200000, 150001]),
+    ("bf16 d64 C16 L1 R4 G4 mid flat", dict(batch=2, n_tokens=100000, head_dim=64, n_q_heads=8, n_kv_heads=2,
+                                            chunk=16, levels=1, n_refs=4), [100000, 75001]),
     ("bf16 d128 C4 L2 R16 G8 large frontier", dict(batch=1, n_tokens=65539, n_q_heads=16, n_kv_heads=2, chunk=4,
                                                    levels=2, n_refs=16), [65539]),
     ("bf16 d64 C8 L1 R4 G4 large flat", dict(batch=2, n_tokens=200000, head_dim=64, n_q_heads=8, n_kv_heads=2,
