@@ -161,7 +161,7 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   t->span[0] = 1;
   t->cap[0] = 0;
   const int U = t->U, R = t->R, d = t->d, G = t->G, L = t->L;
-  int ws = 1024 / U;  // score workgroups per unit: about four per compute unit in all
+  int ws = 2048 / U;  // score workgroups per unit: two rounds of four per compute unit in all
   if (ws > 512) ws = 512;
   if (ws < 1) ws = 1;
   t->WS = ws;

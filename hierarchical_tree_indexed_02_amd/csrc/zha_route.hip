@@ -158,10 +158,11 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
   const int u = blockIdx.y, bi = u / a.v.Hkv, g = u % a.v.Hkv;
   const int G = a.G;
   const int nF = frontier_size(a.v, u);
-  int per = (nF + a.W - 1) / a.W;
-  per = ((per + SUPER - 1) / SUPER) * SUPER;
-  const int start = blockIdx.x * per;
-  const int end = min(nF, start + per);
+  // Super-tiles are dealt to the workgroups in turn: at any moment the unit's workgroups
+  // read neighbouring addresses, sweeping the planes in order.
+  const int start = blockIdx.x * SUPER;
+  const int step = a.W * SUPER;
+  const int end = nF;
 
   typename M::frag qf[NK];
   {
@@ -270,18 +271,18 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
   Frag afA[UN][NK], afB[UN][NK];
   float bvA[UN][4], bvB[UN][4];
   fetch_par(start, ppA);
-  fetch_par(start + SUPER, ppB);
+  fetch_par(start + step, ppB);
   if (start < end) load_stage(start, ppA, afA, bvA);
   for (int base = start; base < end;) {
-    fetch_par(base + 2 * SUPER, ppA);
-    load_stage(base + SUPER, ppB, afB, bvB);
+    fetch_par(base + 2 * step, ppA);
+    load_stage(base + step, ppB, afB, bvB);
     compute(afA, bvA, base);
-    base += SUPER;
+    base += step;
     if (base >= end) break;
-    fetch_par(base + 2 * SUPER, ppB);
-    load_stage(base + SUPER, ppA, afA, bvA);
+    fetch_par(base + 2 * step, ppB);
+    load_stage(base + step, ppA, afA, bvA);
     compute(afB, bvB, base);
-    base += SUPER;
+    base += step;
   }
   // per-head (max, sum exp) of this workgroup: lanes of one head, then the 4 waves
   {
@@ -653,6 +654,42 @@ __device__ __forceinline__ void resolve_cut_lds(CutSh& sh, const uint32_t* keys,
   }
 }
 
+// gather_slice over keys in global memory (position = index): 64 keys per thread per
+// round trip, so a unit's tens of thousands of keys take one or two.
+__device__ __forceinline__ void gather_slice_global(CutSh& sh, const uint32_t* src, int n, int ncap, uint32_t lo,
+                                                    uint32_t hi, uint32_t* dk, uint32_t* dp) {
+  if (threadIdx.x == 0) sh.ncand = 0;
+  __syncthreads();
+  for (int base = 64 * threadIdx.x; base < n; base += 64 * ST) {
+    uint4 kv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) kv[j] = load4c(src, base + 4 * j, ncap);
+    // matches as a bit mask (no per-key branch), one reservation per thread, then only
+    // the matching keys are written
+    u64 mask = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t k4[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool hit = base + 4 * j + e < n && k4[e] >= lo && k4[e] <= hi;
+        mask |= hit ? (u64)1 << (4 * j + e) : 0;
+      }
+    }
+    if (mask) {
+      uint32_t slot = atomicAdd(&sh.ncand, (uint32_t)__popcll(mask));
+      while (mask) {
+        const int b = __ffsll((unsigned long long)mask) - 1;
+        mask &= mask - 1;
+        dk[slot] = src[base + b];  // re-read (cached): a register array cannot be indexed by b
+        dp[slot] = (uint32_t)(base + b);
+        ++slot;
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // The cut of keys[0, n) (position = index) given a histogram of [lo, hi] in sh (sh.above:
 // mass above the range, T within the range).  The range narrows NB-fold per pass until
 // the crossing slice holds at most RMAX keys, which are ranked.  With a candidate buffer
@@ -670,7 +707,8 @@ __device__ __forceinline__ void resolve_cut(CutSh& sh, const uint32_t* keys, int
     slice_range(lo, hi, sh.bin, &nlo, &nhi);
     const uint32_t cnt = sh.hcnt[sh.bin];
     if (cnt <= (uint32_t)RMAX) {
-      gather_slice(sh, sk, sp, ns, scap, nlo, nhi, sh.rkey, sh.rpos);
+      if (sp) gather_slice(sh, sk, sp, ns, scap, nlo, nhi, sh.rkey, sh.rpos);
+      else gather_slice_global(sh, sk, ns, scap, nlo, nhi, sh.rkey, sh.rpos);
       rank_cut(sh, (int)cnt, T);
       *tau = sh.tau;
       *tie_last = sh.tie_last;
@@ -683,7 +721,7 @@ __device__ __forceinline__ void resolve_cut(CutSh& sh, const uint32_t* keys, int
       return;
     }
     if (ck && !sp && cnt <= (uint32_t)ncap) {
-      gather_slice(sh, sk, sp, ns, scap, nlo, nhi, ck, cp);
+      gather_slice_global(sh, sk, ns, scap, nlo, nhi, ck, cp);
       sk = ck;
       sp = cp;
       ns = (int)cnt;
