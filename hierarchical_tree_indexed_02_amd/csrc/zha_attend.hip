@@ -7,9 +7,9 @@
 // ([wqu] "What is Zyphra Hierarchical Attention (ZHA)?").  Dense decode is the
 // same computation with S = [0, N).
 //
-// Split-K flash decode: each workgroup takes a contiguous slice of the unit's
-// position list (sink and tail first, then the kept chunks' tokens in order),
-// its four waves walk 32 positions at a time with an online softmax, and the
+// Split-K flash decode: the unit's position list (sink and tail first, then the kept
+// chunks' tokens in order) is cut into blocks of 128 positions dealt to the workgroups
+// in turn; a workgroup's four waves take 32 positions each with an online softmax, and the
 // G query heads of the KV head share every K/V tile.  Q.K^T runs on the matrix
 // cores with K rows loaded straight from HBM into the operand registers; P.V
 // stages the V tile in LDS and reads it transposed.  K and V are read once per step:
@@ -206,10 +206,12 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a) {
   const int u = blockIdx.y, bi = u / a.Hkv, g = u % a.Hkv;
   const int G = a.G;
   const Positions P = unit_positions<DENSE>(a, u, bi);
-  int per = (P.P + a.W - 1) / a.W;
-  per = ((per + ATT_STEP - 1) / ATT_STEP) * ATT_STEP;
-  const int start = blockIdx.x * per;
-  const int end = min(P.P, start + per);
+  // Blocks of 4 * ATT_STEP positions are dealt to the workgroups in turn, so the unit's
+  // workgroups read neighbouring K/V rows at any moment.
+  constexpr int WSTEP = 4 * ATT_STEP;
+  const int start = blockIdx.x * WSTEP;
+  const int gstep = a.W * WSTEP;
+  const int end = P.P;
 
   const int64_t kvoff = ((int64_t)bi * a.Hkv + g) * a.T * D;
   const T* Kb = (const T*)a.K + kvoff;
@@ -289,27 +291,26 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a) {
     }
   };
 
-  // Software pipeline over the wave's windows p0, p0 + 4 ATT_STEP, ...: while window i is
+  // Software pipeline over the wave's windows p0, p0 + gstep, ...: while window i is
   // computed, the K/V loads of window i+1 and the chunk ids of window i+2 are in flight.
   // The two register buffers alternate by unrolling the loop twice.
-  constexpr int WSTEP = 4 * ATT_STEP;
   int p0 = start + wave * ATT_STEP;
   Window<DENSE> w0, w1;
   w0.fetch(P, p0, end, a.C, a.Cshift, lane);
-  w1.fetch(P, p0 + WSTEP, end, a.C, a.Cshift, lane);
+  w1.fetch(P, p0 + gstep, end, a.C, a.Cshift, lane);
   typename M::frag kA[2][NK], kB[2][NK];
   typename PVT::vfrag vA, vB;
   if (p0 < end) load_kv(kA, vA, w0, p0);
   while (p0 < end) {
-    w0.fetch(P, p0 + 2 * WSTEP, end, a.C, a.Cshift, lane);
-    load_kv(kB, vB, w1, p0 + WSTEP);
+    w0.fetch(P, p0 + 2 * gstep, end, a.C, a.Cshift, lane);
+    load_kv(kB, vB, w1, p0 + gstep);
     compute(kA, vA, p0);
-    p0 += WSTEP;
+    p0 += gstep;
     if (p0 >= end) break;
-    w1.fetch(P, p0 + 2 * WSTEP, end, a.C, a.Cshift, lane);
-    load_kv(kA, vA, w0, p0 + WSTEP);
+    w1.fetch(P, p0 + 2 * gstep, end, a.C, a.Cshift, lane);
+    load_kv(kA, vA, w0, p0 + gstep);
     compute(kB, vB, p0);
-    p0 += WSTEP;
+    p0 += gstep;
   }
   // per-head sum over the four lane groups, then combine the four waves through LDS
   lrun += __shfl_xor(lrun, 16);
@@ -452,8 +453,10 @@ int zha_sparse_wgs(int U) {
 }
 
 int zha_dense_wgs(int U) {
-  int w = 1024 / (U > 0 ? U : 1);
-  return w < 1 ? 1 : w;
+  // one long-running workgroup per compute unit at small batch (measured best for the
+  // in-order sweep of a unit's rows); at least 16 per unit at large batch
+  int w = 256 / (U > 0 ? U : 1);
+  return w < 16 ? 16 : w;
 }
 
 hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const void* V, float scale, float* out,
