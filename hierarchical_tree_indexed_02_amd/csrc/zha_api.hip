@@ -11,6 +11,8 @@
 int zha_score_wgs(const zha_tree* t, int level);
 int zha_compact_chunks(int64_t nodes);
 int zha_hist_bins();
+int64_t zha_sel_cand_entries(int U);
+int zha_sel_ctr_words(int U);
 size_t zha_spine_bytes(int L, int d, int R);
 size_t zha_build_lds_bytes(int S, int L, int d, int R, int esize);
 
@@ -67,7 +69,7 @@ void free_tree(zha_tree* t) {
     if (t->kept[l]) (void)hipFree(t->kept[l]);
   }
   void* ps[] = {t->refs,   t->spine,  t->sub_lse, t->sub_m,  t->counts,    t->scores,   t->spart,    t->keys,     t->apart,
-                t->fh_cnt, t->fh_mass,  t->fh_edge,  t->cut,      t->lb_status,
+                t->fh_cnt, t->fh_mass,  t->fh_edge,  t->cut,      t->sel_cand, t->sel_ctr, t->lb_status,
                 t->lb_epoch, t->lb_error};
   for (void* p : ps)
     if (p) (void)hipFree(p);
@@ -191,6 +193,8 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   ok = ok && dalloc(t, &t->fh_mass, (size_t)U * nb * sizeof(unsigned long long));
   ok = ok && dalloc(t, &t->fh_edge, (size_t)U * 2 * sizeof(unsigned long long));
   ok = ok && dalloc(t, &t->cut, (size_t)U * 4 * sizeof(int32_t));
+  ok = ok && dalloc(t, &t->sel_cand, (size_t)zha_sel_cand_entries(U) * 2 * sizeof(uint32_t));
+  ok = ok && dalloc(t, &t->sel_ctr, (size_t)zha_sel_ctr_words(U) * sizeof(uint32_t));
   ok = ok && dalloc(t, &t->lb_status, (size_t)U * nchunk * sizeof(unsigned long long));
   ok = ok && dalloc(t, &t->lb_epoch, 2 * sizeof(uint32_t));
   ok = ok && dalloc(t, &t->lb_error, sizeof(int32_t));
@@ -198,6 +202,7 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
     ok = hipMemset(t->fh_cnt, 0, (size_t)U * nb * sizeof(uint32_t)) == hipSuccess &&
          hipMemset(t->fh_mass, 0, (size_t)U * nb * sizeof(unsigned long long)) == hipSuccess &&
          hipMemset(t->fh_edge, 0, (size_t)U * 2 * sizeof(unsigned long long)) == hipSuccess &&
+         hipMemset(t->sel_ctr, 0, (size_t)zha_sel_ctr_words(U) * sizeof(uint32_t)) == hipSuccess &&
          hipMemset(t->lb_status, 0, (size_t)U * nchunk * sizeof(unsigned long long)) == hipSuccess &&
          hipMemset(t->lb_error, 0, sizeof(int32_t)) == hipSuccess;
     const uint32_t ep[2] = {1u, 0u};  // status words of epoch 0 (all-zero memory) never match

@@ -164,6 +164,8 @@ struct zha_tree {
   unsigned long long* fh_mass;      // [U][1024]
   unsigned long long* fh_edge;      // [U][2]
   int32_t* cut;                     // [U][4] cut of the level being selected
+  uint32_t* sel_cand;               // [U][min(32, 256/U)][8192][2] crossing-slice (key, position) pairs per selection workgroup
+  uint32_t* sel_ctr;                // [U][1 + 32] selection workgroups arrived (zero between levels), candidates per workgroup
   unsigned long long* lb_status;    // [U][compaction chunks of level 1] look-back words
   uint32_t* lb_epoch;               // [2] look-back epoch (starts at 1) and finished-workgroup count
   int32_t* lb_error;                // [1] set if a look-back wait ever gives up

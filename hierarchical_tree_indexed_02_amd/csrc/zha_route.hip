@@ -33,7 +33,6 @@ typedef unsigned long long u64;
 
 constexpr int NB = 1024;                 // histogram slices
 constexpr int SMALL_NODES = 8192;        // frontiers up to this size are selected in one workgroup
-constexpr int CAND = 8192;               // keys of a crossing slice held in LDS
 constexpr int CH = 4096;                 // compaction chunk (positions per workgroup)
 
 // Per-level inputs shared by the kernels of one level.  Node counts per sequence are
@@ -523,47 +522,29 @@ __device__ __forceinline__ void hist_keys_lds(CutSh& sh, const uint32_t* keys, i
   }
 }
 
-__device__ __forceinline__ void gather_slice_lds(CutSh& sh, const uint32_t* keys, int n, uint32_t lo, uint32_t hi) {
+// Positions are pos[i] (candidates carrying their frontier positions) or i itself (pos null).
+__device__ __forceinline__ void gather_slice_lds(CutSh& sh, const uint32_t* keys, const uint32_t* pos, int n,
+                                                 uint32_t lo, uint32_t hi) {
   if (threadIdx.x == 0) sh.ncand = 0;
   __syncthreads();
-  for (int i0 = threadIdx.x; i0 < n; i0 += 4 * ST) {
+  const int lane = threadIdx.x & 63;
+  for (int i0 = threadIdx.x - lane; i0 < n; i0 += 4 * ST) {  // uniform per wave
     uint32_t k4[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) k4[e] = keys[min(i0 + ST * e, n - 1)];
+    for (int e = 0; e < 4; ++e) k4[e] = keys[min(i0 + lane + ST * e, n - 1)];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = i0 + ST * e;
-      if (i < n && k4[e] >= lo && k4[e] <= hi) {
-        const uint32_t slot = atomicAdd(&sh.ncand, 1u);
-        sh.rkey[slot] = k4[e];
-        sh.rpos[slot] = (uint32_t)i;
-      }
-    }
-  }
-  __syncthreads();
-}
-
-// Copies the (key, position) pairs of src[0, n) inside [lo, hi] to dk/dp (the caller
-// knows how many there are and sized dk/dp for them).  Positions are src_pos[i], or i
-// itself when src_pos is null.  Keys are read 16 per thread per round trip.
-__device__ __forceinline__ void gather_slice(CutSh& sh, const uint32_t* src, const uint32_t* src_pos, int n,
-                                             int ncap, uint32_t lo, uint32_t hi, uint32_t* dk, uint32_t* dp) {
-  if (threadIdx.x == 0) sh.ncand = 0;
-  __syncthreads();
-  for (int base = 16 * threadIdx.x; base < n; base += 16 * ST) {
-    uint4 kv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) kv[j] = load4c(src, base + 4 * j, ncap);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t k4[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = base + 4 * j + e;
-        if (i < n && k4[e] >= lo && k4[e] <= hi) {
-          const uint32_t slot = atomicAdd(&sh.ncand, 1u);
-          dk[slot] = k4[e];
-          dp[slot] = src_pos ? src_pos[i] : (uint32_t)i;
+      const int i = i0 + lane + ST * e;
+      const bool hit = i < n && k4[e] >= lo && k4[e] <= hi;
+      const u64 m = __ballot(hit);  // one reservation per wave
+      if (m) {
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&sh.ncand, (uint32_t)__popcll(m));
+        base = __shfl(base, 0);
+        if (hit) {
+          const uint32_t slot = base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+          sh.rkey[slot] = k4[e];
+          sh.rpos[slot] = pos ? pos[i] : (uint32_t)i;
         }
       }
     }
@@ -623,17 +604,20 @@ __device__ __forceinline__ int nth_tie_scan(CutSh& sh, const uint32_t* keys, int
   return found;
 }
 
-// The cut of LDS keys[0, n) (position = index) given a histogram of [lo, hi] in sh:
-// narrow the range until the crossing slice holds at most RMAX keys, then rank them.
-__device__ __forceinline__ void resolve_cut_lds(CutSh& sh, const uint32_t* keys, int n, uint32_t lo, uint32_t hi,
-                                                u64 T, uint32_t* tau, int* tie_last) {
+// The cut of LDS keys[0, n) given a histogram of [lo, hi] in sh: narrow the range until
+// the crossing slice holds at most RMAX keys, then rank them.  Positions are pos[i] (LDS
+// candidates; ties of one value are then split by a scan of the global keys gkeys[0, gn)
+// in position order) or i itself (pos null: keys is the whole frontier in position order).
+__device__ __forceinline__ void resolve_cut_lds(CutSh& sh, const uint32_t* keys, const uint32_t* pos, int n,
+                                                uint32_t lo, uint32_t hi, u64 T, const uint32_t* gkeys, int gn,
+                                                int gcap, uint32_t* tau, int* tie_last) {
   for (;;) {
     find_bin(sh, T);
     uint32_t nlo, nhi;
     slice_range(lo, hi, sh.bin, &nlo, &nhi);
     const uint32_t cnt = sh.hcnt[sh.bin];
     if (cnt <= (uint32_t)RMAX) {
-      gather_slice_lds(sh, keys, n, nlo, nhi);
+      gather_slice_lds(sh, keys, pos, n, nlo, nhi);
       rank_cut(sh, (int)cnt, T);
       *tau = sh.tau;
       *tie_last = sh.tie_last;
@@ -642,7 +626,9 @@ __device__ __forceinline__ void resolve_cut_lds(CutSh& sh, const uint32_t* keys,
     if (nhi <= nlo) {  // more than RMAX keys of one value
       const uint32_t n_take = ties_to_take(nlo, T, sh.above);
       *tau = nlo;
-      *tie_last = n_take < cnt ? nth_tie_scan(sh, keys, n, SMALL_NODES, nlo, n_take - 1) : 0x7FFFFFFF;
+      if (n_take >= cnt) *tie_last = 0x7FFFFFFF;
+      else if (pos) *tie_last = nth_tie_scan(sh, gkeys, gn, gcap, nlo, n_take - 1);
+      else *tie_last = nth_tie_scan(sh, keys, n, SMALL_NODES, nlo, n_take - 1);
       return;
     }
     lo = nlo;
@@ -690,25 +676,21 @@ __device__ __forceinline__ void gather_slice_global(CutSh& sh, const uint32_t* s
   __syncthreads();
 }
 
-// The cut of keys[0, n) (position = index) given a histogram of [lo, hi] in sh (sh.above:
-// mass above the range, T within the range).  The range narrows NB-fold per pass until
-// the crossing slice holds at most RMAX keys, which are ranked.  With a candidate buffer
-// (ck/cp, ncap entries), the crossing slice's keys move there once they fit, and later
-// passes scan only them.  A slice of more than RMAX equal keys is split by position.
-// Returns tau and the position of the last kept key equal to tau.
+// The cut of keys[0, n) (position = index, global memory) given a histogram of [lo, hi]
+// in sh (sh.above: mass above the range, T within the range).  The range narrows NB-fold
+// per pass until the crossing slice holds at most RMAX keys, which are ranked.  Once the
+// crossing slice fits the LDS candidate buffer (ck/cp, ncap entries) its keys and
+// positions move there and the LDS resolver finishes.  A slice of more than RMAX equal
+// keys is split by position.  Returns tau and the position of the last kept key equal to tau.
 __device__ __forceinline__ void resolve_cut(CutSh& sh, const uint32_t* keys, int n, int kcap, uint32_t lo, uint32_t hi,
                                             u64 T, uint32_t* ck, uint32_t* cp, int ncap, uint32_t* tau, int* tie_last) {
-  const uint32_t* sk = keys;
-  const uint32_t* sp = nullptr;
-  int ns = n, scap = kcap;
   for (;;) {
     find_bin(sh, T);
     uint32_t nlo, nhi;
     slice_range(lo, hi, sh.bin, &nlo, &nhi);
     const uint32_t cnt = sh.hcnt[sh.bin];
     if (cnt <= (uint32_t)RMAX) {
-      if (sp) gather_slice(sh, sk, sp, ns, scap, nlo, nhi, sh.rkey, sh.rpos);
-      else gather_slice_global(sh, sk, ns, scap, nlo, nhi, sh.rkey, sh.rpos);
+      gather_slice_global(sh, keys, n, kcap, nlo, nhi, sh.rkey, sh.rpos);
       rank_cut(sh, (int)cnt, T);
       *tau = sh.tau;
       *tie_last = sh.tie_last;
@@ -720,18 +702,20 @@ __device__ __forceinline__ void resolve_cut(CutSh& sh, const uint32_t* keys, int
       *tie_last = n_take < cnt ? nth_tie_scan(sh, keys, n, kcap, nlo, n_take - 1) : 0x7FFFFFFF;
       return;
     }
-    if (ck && !sp && cnt <= (uint32_t)ncap) {
-      gather_slice_global(sh, sk, ns, scap, nlo, nhi, ck, cp);
-      sk = ck;
-      sp = cp;
-      ns = (int)cnt;
-      scap = ncap;
+    if (cnt <= (uint32_t)ncap) {
+      gather_slice_global(sh, keys, n, kcap, nlo, nhi, ck, cp);
+      hist_clear(sh);
+      __syncthreads();
+      hist_keys_lds(sh, ck, (int)cnt, nlo, nhi);
+      __syncthreads();
+      resolve_cut_lds(sh, ck, cp, (int)cnt, nlo, nhi, T, keys, n, kcap, tau, tie_last);
+      return;
     }
     lo = nlo;
     hi = nhi;
     hist_clear(sh);
     __syncthreads();
-    hist_keys(sh, sk, ns, scap, lo, hi);
+    hist_keys(sh, keys, n, kcap, lo, hi);
     __syncthreads();
   }
 }
@@ -872,7 +856,7 @@ __global__ __launch_bounds__(ST) void zha_select_small_kernel(SmallArgs a) {
     __syncthreads();
     hist_keys_lds(sh.cut, sh.keys, nF, kmin, kmax);
     __syncthreads();
-    resolve_cut_lds(sh.cut, sh.keys, nF, kmin, kmax, T, &tau, &tie_last);
+    resolve_cut_lds(sh.cut, sh.keys, nullptr, nF, kmin, kmax, T, nullptr, 0, 0, &tau, &tie_last);
   }
   // compaction in position order (chunks of 4 positions per thread)
   int32_t* kept = a.kept + (int64_t)u * a.capl;
@@ -1008,41 +992,65 @@ struct LargeArgs {
   u64* fh_mass;
   u64* fh_edge;           // [U][2]
   int32_t* cut;           // [U][4]: tau, last tie position kept, keep_all
+  uint32_t* cand;         // [U][KSS][LCAND][2]: (key, position) of the crossing slice found by
+                          // each workgroup, in any order (written and read with agent-scope atomics)
+  uint32_t* ctr;          // [U][1 + KSMAX]: workgroups arrived (zero between launches), then the
+                          // number of candidates each workgroup wrote
+  int KS;                 // workgroups per unit (<= KSS)
+  int KSS;                // candidate regions per unit
   float p;
 };
 
-// Resolves the cut of a large frontier.  The first histogram is the fine one built by
-// the mass kernel when the cut lies in its window, else one of every key over their
-// whole range.  Output per unit: tau, and the position of the last kept key equal to
-// tau (equal keys are taken in position order), so that the compaction is a
-// per-position test.
+// Resolves the cut of a large frontier with KS workgroups per unit.  The first histogram
+// is the fine one built by the mass kernel.  When the cut lies in its window and the
+// crossing slice holds at most LCAND keys, every workgroup finds that slice and copies the
+// (key, position) pairs of its share of the frontier that fall in it to the unit's
+// candidate buffer; the last workgroup to arrive (an acquire-release counter, so it sees
+// every other workgroup's candidates) resolves the cut among them in LDS.  Otherwise the
+// last workgroup resolves the cut alone over every key.  Output per unit: tau, and the
+// position of the last kept key equal to tau (equal keys are taken in position order), so
+// that the compaction is a per-position test.
 constexpr int LCAND = 8192;  // crossing-slice keys of a large level held in LDS
+constexpr int KSMAX = 32;    // selection workgroups per unit at most
+
+// Candidate regions per unit: at most KSMAX, and few enough that every workgroup of a
+// launch is resident at once (one per compute unit).
+int sel_regions(int U) {
+  const int k = 256 / (U > 0 ? U : 1);
+  return k < 1 ? 1 : (k > KSMAX ? KSMAX : k);
+}
+// Workgroups per unit: one per 4096 nodes, at most one per region.
+int sel_large_wgs(int64_t cap, int U) {
+  const int64_t k = cap / 4096;
+  return k < 1 ? 1 : (int)(k < sel_regions(U) ? k : sel_regions(U));
+}
 
 __global__ __launch_bounds__(ST) void zha_select_large_kernel(LargeArgs a) {
   __shared__ CutSh sh;
-  __shared__ uint32_t s_ck[LCAND], s_cp[LCAND];
+  __shared__ __attribute__((aligned(16))) uint32_t s_ck[LCAND];
+  __shared__ __attribute__((aligned(16))) uint32_t s_cp[LCAND];
   __shared__ u64 s_tot[2];
   __shared__ uint32_t s_mn[ST / 64], s_mx[ST / 64];
+  __shared__ int s_last;
+  __shared__ uint32_t s_wcnt;
+  __shared__ uint32_t s_off[KSMAX + 1], s_xoff[KSMAX + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int u = blockIdx.x;
+  const int u = blockIdx.y, j = blockIdx.x;
+  uint32_t* ctr = a.ctr + (int64_t)u * (1 + KSMAX);
   const int nF = frontier_size(a.v, u);
+  const int kcap = (int)a.kstride;
   const uint32_t* keys = a.keys + (int64_t)u * a.kstride;
   uint32_t* gc = a.fh_cnt + (int64_t)u * NB;
   u64* gm = a.fh_mass + (int64_t)u * NB;
-  // take the unit's histogram and leave it zeroed for the next level
+  // every workgroup reads the unit's histogram
 #pragma unroll
   for (int e = 0; e < BPT; ++e) {
     sh.hcnt[tid + ST * e] = gc[tid + ST * e];
     sh.hmass[tid + ST * e] = gm[tid + ST * e];
   }
   if (tid < 2) s_tot[tid] = a.fh_edge[u * 2 + tid];
+  if (tid == 0) s_wcnt = 0;
   __syncthreads();
-#pragma unroll
-  for (int e = 0; e < BPT; ++e) {
-    gc[tid + ST * e] = 0;
-    gm[tid + ST * e] = 0;
-  }
-  if (tid < 2) a.fh_edge[u * 2 + tid] = 0;
   // window mass: workgroup sum of the bins
   u64 wm = sh.hmass[tid] + sh.hmass[tid + ST];
 #pragma unroll
@@ -1053,49 +1061,187 @@ __global__ __launch_bounds__(ST) void zha_select_large_kernel(LargeArgs a) {
 #pragma unroll
   for (int w = 0; w < ST / 64; ++w) wm += sh.red64[w];
   const u64 above = s_tot[0], total = above + wm + s_tot[1];
+  const bool keep_all = nF == 0 || total == 0;  // total 0: every mass rounds to zero
+  const u64 T = keep_all ? 0 : target_of(a.p, total);
+  const bool inwin = !keep_all && T > above && T <= above + wm;  // the cut lies in the window
+  uint32_t wlo = 0, whi = 0, nlo = 0, nhi = 0, cnt = 0;
+  bool gathered = false;
+  if (inwin) {
+    fine_window(nF, &wlo, &whi);
+    if (tid == 0) sh.above = above;
+    __syncthreads();
+    find_bin(sh, T);
+    slice_range(wlo, whi, sh.bin, &nlo, &nhi);
+    cnt = sh.hcnt[sh.bin];
+    gathered = cnt <= (uint32_t)LCAND;  // the same decision in every workgroup
+    if (gathered) {
+      // this workgroup's share: blocks of 4 * ST positions dealt in turn, four blocks in
+      // flight per thread; hits are written from registers to this workgroup's own region,
+      // one LDS reservation per wave
+      u64* cand = (u64*)a.cand + ((int64_t)u * a.KSS + j) * LCAND;  // key low, position high
+      for (int b0 = j; b0 * 4 * ST < nF; b0 += 4 * a.KS) {
+        uint4 kv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kv[r] = load4c(keys, ((b0 + r * a.KS) * ST + tid) * 4, kcap);
+        uint32_t mask = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int p0 = ((b0 + r * a.KS) * ST + tid) * 4;
+          const uint32_t k4[4] = {kv[r].x, kv[r].y, kv[r].z, kv[r].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool hit = p0 + e < nF && k4[e] >= nlo && k4[e] <= nhi;
+            mask |= hit ? 1u << (4 * r + e) : 0u;
+          }
+        }
+        const uint32_t c = (uint32_t)__popc(mask);
+        uint32_t inc = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_up(inc, o);
+          if (lane >= o) inc += y;
+        }
+        uint32_t wbase = 0;
+        if (lane == 63 && inc) wbase = atomicAdd(&s_wcnt, inc);
+        wbase = __shfl(wbase, 63);
+        uint32_t slot = wbase + inc - c;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int p0 = ((b0 + r * a.KS) * ST + tid) * 4;
+          const uint32_t k4[4] = {kv[r].x, kv[r].y, kv[r].z, kv[r].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if ((mask >> (4 * r + e)) & 1u) {
+              if (slot < (uint32_t)LCAND)
+                __hip_atomic_store(&cand[slot], ((u64)(uint32_t)(p0 + e) << 32) | k4[e], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+              ++slot;
+            }
+          }
+        }
+      }
+    }
+  }
+  // arrive; the last workgroup of the unit goes on
+  __syncthreads();
+  if (tid == 0) {
+    __hip_atomic_store(&ctr[1 + j], s_wcnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t before = __hip_atomic_fetch_add(&ctr[0], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = before == (uint32_t)(a.KS - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // every workgroup has read the histogram and written its candidates
   uint32_t tau = 0;
   int tie_last = 0x7FFFFFFF;
-  const bool keep_all = nF == 0 || total == 0;  // total 0: every mass rounds to zero
   if (!keep_all) {
-    const u64 T = target_of(a.p, total);
-    uint32_t lo, hi;
-    __syncthreads();
-    if (T > above && T <= above + wm) {  // the cut lies in the window
-      fine_window(nF, &lo, &hi);
-      if (tid == 0) sh.above = above;
-    } else {
-      // every key over its whole range
-      uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-      for (int base = 4 * tid; base < nF; base += 4 * ST) {
-        const uint4 kv = load4c(keys, base, (int)a.kstride);
-        const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w};
+    if (gathered) {
+      // The workgroups' regions, concatenated.  The counts and the first E0 entries of every
+      // region are loaded together (entries past a region's count are ignored), then the
+      // rare remainder of longer regions.
+      const u64* cand = (const u64*)a.cand + (int64_t)u * a.KSS * LCAND;
+      const int E0 = ST / a.KS;
+      const int w0 = tid / E0, k0 = tid - w0 * E0;
+      const bool own = w0 < a.KS;
+      const u64 c0 = own ? __hip_atomic_load(&cand[(int64_t)w0 * LCAND + k0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : 0;
+      if (wave == 0) {  // exclusive scans of the KS <= 32 counts and of their excess over E0
+        const uint32_t cw = lane < a.KS ? __hip_atomic_load(&ctr[1 + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                        : 0u;
+        const uint32_t xw = cw > (uint32_t)E0 ? cw - (uint32_t)E0 : 0u;
+        uint32_t inc = cw, xinc = xw;
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (base + e < nF) { mn = min(mn, k4[e]); mx = max(mx, k4[e]); }
+        for (int o = 1; o < 32; o <<= 1) {
+          const uint32_t y = __shfl_up(inc, o), xy = __shfl_up(xinc, o);
+          if (lane >= o) { inc += y; xinc += xy; }
+        }
+        if (lane < a.KS) { s_off[lane] = inc - cw; s_xoff[lane] = xinc - xw; }
+        if (lane == a.KS - 1) { s_off[a.KS] = inc; s_xoff[a.KS] = xinc; }
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
-      }
-      if (lane == 0) { s_mn[wave] = mn; s_mx[wave] = mx; }
-      hist_clear(sh);
-      if (tid == 0) sh.above = 0;
       __syncthreads();
-      lo = 0xFFFFFFFFu;
-      hi = 0u;
+      if (own && (uint32_t)k0 < s_off[w0 + 1] - s_off[w0]) {
+        s_ck[s_off[w0] + k0] = (uint32_t)c0;
+        s_cp[s_off[w0] + k0] = (uint32_t)(c0 >> 32);
+      }
+      // entries past the first E0 of their region, all loads of a pass issued together
+      const int X = (int)s_xoff[a.KS];
+      for (int x = tid; x < X; x += ST) {
+        int lo = 0, hi = a.KS - 1;  // the region w with s_xoff[w] <= x < s_xoff[w + 1]
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_xoff[mid] <= (uint32_t)x) lo = mid; else hi = mid - 1;
+        }
+        const int k = E0 + (x - (int)s_xoff[lo]);
+        const u64 c = __hip_atomic_load(&cand[(int64_t)lo * LCAND + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_ck[s_off[lo] + k] = (uint32_t)c;
+        s_cp[s_off[lo] + k] = (uint32_t)(c >> 32);
+      }
+      __syncthreads();
+      if (cnt <= (uint32_t)RMAX) {
+        if (tid < (int)cnt) {
+          sh.rkey[tid] = s_ck[tid];
+          sh.rpos[tid] = s_cp[tid];
+        }
+        __syncthreads();
+        rank_cut(sh, (int)cnt, T);
+        tau = sh.tau;
+        tie_last = sh.tie_last;
+      } else {
+        hist_clear(sh);
+        __syncthreads();
+        hist_keys_lds(sh, s_ck, (int)cnt, nlo, nhi);
+        __syncthreads();
+        resolve_cut_lds(sh, s_ck, s_cp, (int)cnt, nlo, nhi, T, keys, nF, kcap, &tau, &tie_last);
+      }
+    } else {
+      uint32_t lo, hi;
+      if (inwin) {  // crossing slice of more than LCAND keys: start again from the fine histogram
+        lo = wlo;
+        hi = whi;
+        if (tid == 0) sh.above = above;
+      } else {
+        // every key over its whole range
+        uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+        for (int base = 4 * tid; base < nF; base += 4 * ST) {
+          const uint4 kv = load4c(keys, base, kcap);
+          const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
-      for (int w = 0; w < ST / 64; ++w) { lo = min(lo, s_mn[w]); hi = max(hi, s_mx[w]); }
-      hist_keys(sh, keys, nF, (int)a.kstride, lo, hi);
+          for (int e = 0; e < 4; ++e)
+            if (base + e < nF) { mn = min(mn, k4[e]); mx = max(mx, k4[e]); }
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+          mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+          mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+        }
+        if (lane == 0) { s_mn[wave] = mn; s_mx[wave] = mx; }
+        hist_clear(sh);
+        if (tid == 0) sh.above = 0;
+        __syncthreads();
+        lo = 0xFFFFFFFFu;
+        hi = 0u;
+#pragma unroll
+        for (int w = 0; w < ST / 64; ++w) { lo = min(lo, s_mn[w]); hi = max(hi, s_mx[w]); }
+        hist_keys(sh, keys, nF, kcap, lo, hi);
+      }
+      __syncthreads();
+      resolve_cut(sh, keys, nF, kcap, lo, hi, T, s_ck, s_cp, LCAND, &tau, &tie_last);
     }
-    __syncthreads();
-    resolve_cut(sh, keys, nF, (int)a.kstride, lo, hi, T, s_ck, s_cp, LCAND, &tau, &tie_last);
   }
   if (tid == 0) {
     a.cut[u * 4 + 0] = (int32_t)tau;
     a.cut[u * 4 + 1] = tie_last;
     a.cut[u * 4 + 2] = keep_all ? 1 : 0;
   }
+  // leave the unit's histogram and counters at zero for the next level (last, so that no
+  // workgroup barrier waits for these stores)
+#pragma unroll
+  for (int e = 0; e < BPT; ++e) {
+    gc[tid + ST * e] = 0;
+    gm[tid + ST * e] = 0;
+  }
+  if (tid < 2) a.fh_edge[u * 2 + tid] = 0;
+  if (tid == 0) ctr[0] = 0;
 }
 
 struct CompactArgs {
@@ -1293,6 +1439,8 @@ int zha_score_wgs(const zha_tree* t, int level) {
 
 int zha_compact_chunks(int64_t nodes) { return (int)((nodes + CH - 1) / CH); }
 int zha_hist_bins() { return NB; }
+int64_t zha_sel_cand_entries(int U) { return (int64_t)U * sel_regions(U) * LCAND; }
+int zha_sel_ctr_words(int U) { return U * (1 + KSMAX); }
 
 hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hipStream_t s) {
   const int U = t->U, L = t->L;
@@ -1389,9 +1537,13 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
       la.fh_mass = (u64*)t->fh_mass;
       la.fh_edge = (u64*)t->fh_edge;
       la.cut = t->cut;
+      la.cand = t->sel_cand;
+      la.ctr = t->sel_ctr;
+      la.KS = sel_large_wgs(t->cap[l], U);
+      la.KSS = sel_regions(U);
       la.p = p;
       zha_time_begin(t, s, ZHA_K_SELECT, l);
-      hipLaunchKernelGGL(zha_select_large_kernel, dim3(U), dim3(ST), 0, s, la);
+      hipLaunchKernelGGL(zha_select_large_kernel, dim3(la.KS, U), dim3(ST), 0, s, la);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       zha_time_end(t, s, ZHA_K_SELECT, l);

@@ -81,6 +81,45 @@ def test_variants(label, kw, lens):
     say(" dense", check_dense(case, 0))
 
 
+# --------------------------------------------------------------------------- large-level selection paths
+
+def test_large_level_cut_paths():
+    """A 16384-node level takes the multi-workgroup selection; p from tiny to nearly 1 puts
+    the cut at the heaviest node (a crossing slice of a few keys), inside the fine window
+    (hundreds of keys, narrowed again in LDS) and below the window (every key's range)."""
+    cfg = small(batch=1, n_tokens=65539, n_q_heads=16, n_kv_heads=2, chunk=4, levels=2, n_refs=16, n_queries=2,
+                needles_per_unit=4)
+    say("case large-level cut paths: N=65539 C=4 L=2 R=16 G=8, p in 1e-6 .. 0.999999")
+    case = Case(cfg, n_queries=2)
+    tree = case.tree()
+    for p in (1e-6, 0.3, 0.9, 0.999999):
+        r, a = full_check(case, tree, int(p < 0.5), p)
+        say(f" p={p}", r, a)
+
+
+def test_equal_masses_large_level():
+    """All keys zero: every node of a 10000-node level carries the same mass, so the crossing
+    slice is one value held by every node (more than the candidate buffer) and the cut is
+    split by position: exactly the first ceil(p n) ids are kept."""
+    cfg = small(batch=1, n_tokens=40000, n_q_heads=8, n_kv_heads=2, chunk=4, levels=1, n_refs=4, head_dim=64,
+                n_queries=2, needles_per_unit=2)
+    say("case equal masses: N=40000 C=4 L=1 R=4, K = 0, p=0.33333")
+    case = Case(cfg, n_queries=2)
+    case.Kd.zero_()
+    for key in case.K:
+        case.K[key] = np.zeros_like(case.K[key])
+    tree = case.tree()
+    p = 0.33333
+    r, a = full_check(case, tree, 0, p)
+    nf, nk, ids = tree.route_level(1)
+    n = 10000
+    k = int(np.ceil(p * n))
+    assert nf.cpu().tolist() == [n] * case.Hkv
+    assert nk.cpu().tolist() == [k] * case.Hkv, nk.cpu().tolist()
+    assert torch.equal(ids[:, :k].cpu(), torch.arange(k, dtype=torch.int32).repeat(case.Hkv, 1))
+    say(" ", r, a)
+
+
 # --------------------------------------------------------------------------- edge cases
 
 def test_short_sequences_no_tree():
