@@ -48,10 +48,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_sha(name: str) -> str:
-    path = os.path.join(ROOT, "hierarchical_tree_indexed_02_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+SCORE_END = b"// ------------------------------------------------------------------------ shared selection"
+
+
+def score_kernel_sha() -> str:
+    """First 16 hex digits of the SHA-256 of the scoring kernel's source: zha_route.hip up to
+    the shared-selection section (the kernel and every helper it uses), then zha_internal.h."""
+    csrc = os.path.join(ROOT, "hierarchical_tree_indexed_02_amd", "csrc")
+    with open(os.path.join(csrc, "zha_route.hip"), "rb") as f:
+        route = f.read()
+    with open(os.path.join(csrc, "zha_internal.h"), "rb") as f:
+        internal = f.read()
+    end = route.find(SCORE_END)
+    return hashlib.sha256(route[:end if end >= 0 else len(route)] + internal).hexdigest()[:16]
 
 
 def committed_traffic(workload: str):
@@ -63,7 +72,7 @@ def committed_traffic(workload: str):
     txt = open(path, encoding="utf-8").read()
     m_sha = re.search(r"kernel_source_sha:\s*([0-9a-f]+)", txt)
     m_tr = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m_sha or not m_tr or m_sha.group(1) != kernel_sha("zha_route.hip"):
+    if not m_sha or not m_tr or m_sha.group(1) != score_kernel_sha():
         return None
     return float(m_tr.group(1))
 
