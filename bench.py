@@ -41,6 +41,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-queries", type=int, default=12)
+    ap.add_argument("--summary", choices=["native", "fp8"], default="native",
+                    help="storage of the planes' m for the headline measurement")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the extra pass with fp8 summaries (reported beside the headline)")
     return ap.parse_args()
 
 
@@ -120,168 +124,196 @@ def main():
     refs = torch.from_numpy(zi.refs(cfg)).to(dev)
     log(f"inputs ready in {time.time() - t0:.1f}s")
 
-    lens = [N] * B
-    layer_lens = [[N] * B for _ in range(args.layers)]
-    Ks, Vs, trees = [K0], [V0], []
+    Ks, Vs = [K0], [V0]
     for _ in range(1, args.layers):
         Ks.append(K0.clone())
         Vs.append(V0.clone())
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    build_ms = []
-    for li in range(args.layers):
-        tr = Tree(B, Hkv, Hq, d, C, L, R, T, dt)
-        torch.cuda.synchronize()
-        ev0.record()
-        tr.build(Ks[li], refs, lens)
-        ev1.record()
-        torch.cuda.synchronize()
-        build_ms.append(ev0.elapsed_time(ev1))
-        trees.append(tr)
-    tree_bytes = trees[0].bytes()
-    log(f"trees built: {build_ms} ms; tree+workspace {tree_bytes / 1e9:.2f} GB per layer")
-
-    # a copy kernel of known size, for calibrating hardware byte counters in profiles
-    cal_n16 = (256 << 20) // 16
-    cal_src = torch.empty(cal_n16 * 16, dtype=torch.uint8, device=dev)
-    cal_dst = torch.empty_like(cal_src)
-    zha.zha_calibration_copy(cal_dst, cal_src, cal_n16)
-    torch.cuda.synchronize()
-    del cal_src, cal_dst
-
     outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(args.layers)]
     lses = [torch.empty((B, Hq), dtype=torch.float32, device=dev) for _ in range(args.layers)]
 
-    segs = []  # growing workloads: per-step event pairs of append and of each p's route + attend
+    def measure(summary):
+        """Builds one tree per layer replica with the given m storage, times the stage
+        breakdown and the K-step region, and replays the routes for the byte counts."""
+        lens = [N] * B
+        layer_lens = [[N] * B for _ in range(args.layers)]
+        trees = []
+        build_ms = []
+        for li in range(args.layers):
+            tr = Tree(B, Hkv, Hq, d, C, L, R, T, dt, summary=summary)
+            torch.cuda.synchronize()
+            ev0.record()
+            tr.build(Ks[li], refs, lens)
+            ev1.record()
+            torch.cuda.synchronize()
+            build_ms.append(ev0.elapsed_time(ev1))
+            trees.append(tr)
+        tree_bytes = trees[0].bytes()
+        log(f"trees built: {build_ms} ms; tree+workspace {tree_bytes / 1e9:.2f} GB per layer")
 
-    def seg(name, fn, record):
-        if record:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            segs[-1][name] = (a, b)
-        else:
-            fn()
+        if summary == args.summary:
+            # a copy kernel of known size, for calibrating hardware byte counters in profiles
+            cal_n16 = (256 << 20) // 16
+            cal_src = torch.empty(cal_n16 * 16, dtype=torch.uint8, device=dev)
+            cal_dst = torch.empty_like(cal_src)
+            zha.zha_calibration_copy(cal_dst, cal_src, cal_n16)
+            torch.cuda.synchronize()
+            del cal_src, cal_dst
 
-    def step(i, record=False):
-        li, t = i % args.layers, i % nq
-        tr = trees[li]
-        if growing:
+        segs = []  # growing workloads: per-step event pairs of append and of each p's route + attend
+
+        def seg(name, fn, record):
             if record:
-                segs.append({})
-            if layer_lens[li][0] < T:
-                layer_lens[li] = [n + 1 for n in layer_lens[li]]
-                seg("append", lambda: tr.append(Ks[li], layer_lens[li]), record)
-            for x in p_sweep:
-                seg(x, lambda x=x: (tr.route(qd[t], x, 1.0),
-                                    tr.attend(qd[t], Ks[li], Vs[li], 1.0, out=outs[li], lse=lses[li])), record)
-            return
-        tr.route(qd[t], p, 1.0)
-        tr.attend(qd[t], Ks[li], Vs[li], 1.0, out=outs[li], lse=lses[li])
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn()
+                b.record()
+                segs[-1][name] = (a, b)
+            else:
+                fn()
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+        def step(i, record=False):
+            li, t = i % args.layers, i % nq
+            tr = trees[li]
+            if growing:
+                if record:
+                    segs.append({})
+                if layer_lens[li][0] < T:
+                    layer_lens[li] = [n + 1 for n in layer_lens[li]]
+                    seg("append", lambda: tr.append(Ks[li], layer_lens[li]), record)
+                for x in p_sweep:
+                    seg(x, lambda x=x: (tr.route(qd[t], x, 1.0),
+                                        tr.attend(qd[t], Ks[li], Vs[li], 1.0, out=outs[li], lse=lses[li])), record)
+                return
+            tr.route(qd[t], p, 1.0)
+            tr.attend(qd[t], Ks[li], Vs[li], 1.0, out=outs[li], lse=lses[li])
 
-    # stage breakdown: every launch timed with HIP events (events between launches add
-    # a little time, so this pass is not the one whose step time is reported)
-    for tr in trees:
-        tr.timing(True)
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    recs = []
-    for tr in trees:
-        recs += tr.timing_read()
-        tr.timing(False)
-    per = {}
-    for k, l, ms in recs:
-        per.setdefault((k, l), []).append(ms)
-    kernels = {f"{zha.KERNEL_NAMES[k]}{'_l' + str(l) if l else ''}": dict(launches=len(v), avg_us=1e3 * sum(v) / len(v),
-                                                                          total_ms=sum(v), code=k, level=l)
-               for (k, l), v in sorted(per.items())}
-    dom_name, dom = max(kernels.items(), key=lambda kv: kv[1]["total_ms"])
-
-    # timed region: K steps, with an event pair around the dominant kernel only
-    for tr in trees:
-        tr.timing(True, kernels=[dom["code"]], levels=[dom["level"]])
-    torch.cuda.synchronize()
-    ev0.record()
-    for i in range(args.steps):
-        step(i, record=growing)
-    ev1.record()
-    torch.cuda.synchronize()
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
-    seg_us = {}
-    if growing:
-        for sg in segs:
-            for k, (a, b) in sg.items():
-                seg_us.setdefault(k, []).append(1e3 * a.elapsed_time(b))
-        seg_us = {k: sum(v) / len(v) for k, v in seg_us.items()}
-        ms_step = (seg_us.get("append", 0.0) + seg_us[p]) * 1e-3  # append + route + attend at p
-    live = []
-    for tr in trees:
-        live += [ms for _, _, ms in tr.timing_read()]
-        tr.timing(False)
-    dom_live_us = 1e3 * sum(live) / len(live)
-
-    # algorithmic bytes of each step (routes are deterministic: replay each query once, untimed)
-    S_node = R * (d * es + 4)
-    fr_tot = {l: 0 for l in range(1, L + 1)}
-    kept_tot = {l: 0 for l in range(1, L + 1)}
-    attend_tok = 0
-    steps_q = [i % nq for i in range(args.steps)]
-    for t in sorted(set(steps_q)):
-        w = steps_q.count(t)
-        trees[0].route(qd[t], p, 1.0)
+        for i in range(args.warmup):
+            step(i)
         torch.cuda.synchronize()
-        for l in range(1, L + 1):
-            nf, nk, ids = trees[0].route_level(l)
-            fr_tot[l] += w * int(nf.sum())
-            kept_tot[l] += w * int(nk.sum())
-            if l == 1:
-                nk1 = nk.cpu().numpy()
-                first = ids[:, 0].cpu().numpy()
-                for u in range(U):
-                    Nu = layer_lens[0][u // Hkv]
-                    Nc = (Nu // C) * C
-                    sink = 1 if (Nc > 0 and (nk1[u] == 0 or first[u] != 0)) else 0
-                    attend_tok += w * (sink + (Nu - Nc) + int(nk1[u]) * C)
-    nsteps = args.steps
-    route_bytes = sum(fr_tot[l] for l in fr_tot) * S_node / nsteps
-    attend_bytes = attend_tok * 2 * d * es / nsteps
-    io_bytes = B * Hq * d * es + B * Hq * (d + 1) * 4 + 8 * sum(kept_tot.values()) / nsteps
-    step_bytes = route_bytes + attend_bytes + io_bytes
-    Ncur = layer_lens[0][0]
-    kappa = attend_tok / nsteps / (U * Ncur)
-    dense_bytes = U * Ncur * 2 * d * es
 
-    # the dominant kernel: largest share of the step's time
-    if dom_name.startswith("score_l"):
-        l = dom["level"]
-        dom_bytes = fr_tot[l] / nsteps * (S_node + G * 4) + B * Hq * d * es + (fr_tot[l] / nsteps / C * 4 if l < L else 0)
-        traffic = committed_traffic(args.config) if l == 1 else None
-    elif dom_name == "attend":
-        dom_bytes = attend_bytes + B * Hq * d * es
-        traffic = None
-    else:
-        dom_bytes = None
-        traffic = None
-    dom_avg_s = dom_live_us * 1e-6
-    achieved = dom_bytes / dom_avg_s / 1e9 if dom_bytes else None
-    roofline = dict(kernel=f"zha_score_kernel (level {dom_name.split('_l')[1]})" if dom_name.startswith("score_l")
-                    else dom_name,
-                    bound="hbm", achieved=round(achieved, 1) if achieved else None, peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=round(achieved / PEAK_HBM_GBS, 4) if achieved else None,
-                    traffic=traffic, bytes_per_launch=round(dom_bytes) if dom_bytes else None,
-                    avg_launch_us=round(dom_live_us, 2))
-    log(f"step {ms_step * 1e3:.1f} us, {step_bytes / 1e6:.1f} MB/step ({step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s), "
-        f"kappa {kappa:.3f}")
-    if growing:
-        log("  segments (us): " + ", ".join(f"{k}: {v:.1f}" for k, v in seg_us.items()))
-    for k, v in kernels.items():
-        log(f"  {k:12s} {v['launches']:4d} launches  avg {v['avg_us']:8.2f} us")
+        # stage breakdown: every launch timed with HIP events (events between launches add
+        # a little time, so this pass is not the one whose step time is reported)
+        for tr in trees:
+            tr.timing(True)
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        recs = []
+        for tr in trees:
+            recs += tr.timing_read()
+            tr.timing(False)
+        per = {}
+        for k, l, ms in recs:
+            per.setdefault((k, l), []).append(ms)
+        kernels = {f"{zha.KERNEL_NAMES[k]}{'_l' + str(l) if l else ''}": dict(launches=len(v), avg_us=1e3 * sum(v) / len(v),
+                                                                              total_ms=sum(v), code=k, level=l)
+                   for (k, l), v in sorted(per.items())}
+        dom_name, dom = max(kernels.items(), key=lambda kv: kv[1]["total_ms"])
+
+        # timed region: K steps, with an event pair around the dominant kernel only
+        for tr in trees:
+            tr.timing(True, kernels=[dom["code"]], levels=[dom["level"]])
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(args.steps):
+            step(i, record=growing)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms_total = ev0.elapsed_time(ev1)
+        ms_step = ms_total / args.steps
+        seg_us = {}
+        if growing:
+            for sg in segs:
+                for k, (a, b) in sg.items():
+                    seg_us.setdefault(k, []).append(1e3 * a.elapsed_time(b))
+            seg_us = {k: sum(v) / len(v) for k, v in seg_us.items()}
+            ms_step = (seg_us.get("append", 0.0) + seg_us[p]) * 1e-3  # append + route + attend at p
+        live = []
+        for tr in trees:
+            live += [ms for _, _, ms in tr.timing_read()]
+            tr.timing(False)
+        dom_live_us = 1e3 * sum(live) / len(live)
+
+        # algorithmic bytes of each step (routes are deterministic: replay each query once, untimed)
+        S_node = R * (d + 8) if summary == "fp8" else R * (d * es + 4)
+        fr_tot = {l: 0 for l in range(1, L + 1)}
+        kept_tot = {l: 0 for l in range(1, L + 1)}
+        attend_tok = 0
+        steps_q = [i % nq for i in range(args.steps)]
+        for t in sorted(set(steps_q)):
+            w = steps_q.count(t)
+            trees[0].route(qd[t], p, 1.0)
+            torch.cuda.synchronize()
+            for l in range(1, L + 1):
+                nf, nk, ids = trees[0].route_level(l)
+                fr_tot[l] += w * int(nf.sum())
+                kept_tot[l] += w * int(nk.sum())
+                if l == 1:
+                    nk1 = nk.cpu().numpy()
+                    first = ids[:, 0].cpu().numpy()
+                    for u in range(U):
+                        Nu = layer_lens[0][u // Hkv]
+                        Nc = (Nu // C) * C
+                        sink = 1 if (Nc > 0 and (nk1[u] == 0 or first[u] != 0)) else 0
+                        attend_tok += w * (sink + (Nu - Nc) + int(nk1[u]) * C)
+        nsteps = args.steps
+        route_bytes = sum(fr_tot[l] for l in fr_tot) * S_node / nsteps
+        attend_bytes = attend_tok * 2 * d * es / nsteps
+        io_bytes = B * Hq * d * es + B * Hq * (d + 1) * 4 + 8 * sum(kept_tot.values()) / nsteps
+        step_bytes = route_bytes + attend_bytes + io_bytes
+        Ncur = layer_lens[0][0]
+        kappa = attend_tok / nsteps / (U * Ncur)
+        dense_bytes = U * Ncur * 2 * d * es
+
+        # the dominant kernel: largest share of the step's time
+        if dom_name.startswith("score_l"):
+            l = dom["level"]
+            dom_bytes = fr_tot[l] / nsteps * (S_node + G * 4) + B * Hq * d * es + (fr_tot[l] / nsteps / C * 4 if l < L else 0)
+            traffic = committed_traffic(args.config) if l == 1 and summary == "native" else None
+        elif dom_name == "attend":
+            dom_bytes = attend_bytes + B * Hq * d * es
+            traffic = None
+        else:
+            dom_bytes = None
+            traffic = None
+        dom_avg_s = dom_live_us * 1e-6
+        achieved = dom_bytes / dom_avg_s / 1e9 if dom_bytes else None
+        roofline = dict(kernel=f"zha_score_kernel (level {dom_name.split('_l')[1]})" if dom_name.startswith("score_l")
+                        else dom_name,
+                        bound="hbm", achieved=round(achieved, 1) if achieved else None, peak=PEAK_HBM_GBS, unit="GB/s",
+                        frac=round(achieved / PEAK_HBM_GBS, 4) if achieved else None,
+                        traffic=traffic, bytes_per_launch=round(dom_bytes) if dom_bytes else None,
+                        avg_launch_us=round(dom_live_us, 2))
+        log(f"step {ms_step * 1e3:.1f} us, {step_bytes / 1e6:.1f} MB/step ({step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s), "
+            f"kappa {kappa:.3f}")
+        if growing:
+            log("  segments (us): " + ", ".join(f"{k}: {v:.1f}" for k, v in seg_us.items()))
+        for k, v in kernels.items():
+            log(f"  {k:12s} {v['launches']:4d} launches  avg {v['avg_us']:8.2f} us")
+
+        for tr in trees:
+            tr.close()
+        torch.cuda.empty_cache()
+        return dict(ms_step=ms_step, step_bytes=step_bytes, kappa=kappa, kernels=kernels, roofline=roofline,
+                    seg_us=seg_us, fr_tot=fr_tot, build_ms=build_ms, tree_bytes=tree_bytes, layer_lens=layer_lens,
+                    dense_bytes=dense_bytes, nsteps=nsteps)
+
+    res = measure(args.summary)
+    ms_step, step_bytes, kappa, kernels = res["ms_step"], res["step_bytes"], res["kappa"], res["kernels"]
+    roofline, seg_us, fr_tot, build_ms = res["roofline"], res["seg_us"], res["fr_tot"], res["build_ms"]
+    layer_lens, dense_bytes, nsteps = res["layer_lens"], res["dense_bytes"], res["nsteps"]
+    fp8 = None
+    if not args.no_fp8 and args.summary == "native" and cfg.dtype == "bf16":
+        log("-- the same workload with fp8 summaries")
+        r8 = measure("fp8")
+        fp8 = dict(us_per_step=round(r8["ms_step"] * 1e3, 2), step_bytes=round(r8["step_bytes"]),
+                   step_gbs=round(r8["step_bytes"] / (r8["ms_step"] * 1e-3) / 1e9, 1), kappa=round(r8["kappa"], 4),
+                   roofline=r8["roofline"], build_us=round(1e3 * float(np.median(r8["build_ms"])), 1),
+                   tree_bytes=r8["tree_bytes"],
+                   kernels={k: round(v["avg_us"], 2) for k, v in r8["kernels"].items()})
+        if growing:
+            fp8["p_sweep"] = {str(x): round(r8["seg_us"].get("append", 0.0) + r8["seg_us"][x], 2) for x in p_sweep}
 
     # dense decode on the same GPU and inputs, same protocol
     dense_us = None
@@ -351,6 +383,9 @@ def main():
         "build_us": round(1e3 * float(np.median(build_ms)), 1),
         "kernels": {k: dict(launches=v["launches"], avg_us=round(v["avg_us"], 2)) for k, v in kernels.items()},
     }
+    result["config"]["summary"] = args.summary
+    if fp8 is not None:
+        result["fp8_summaries"] = fp8
     if growing:
         result["append_us"] = round(seg_us.get("append", 0.0), 2)
         result["p_sweep"] = {str(x): round(seg_us.get("append", 0.0) + seg_us[x], 2) for x in p_sweep}

@@ -45,6 +45,8 @@ zha_status check_desc(const zha_tree_desc* d) {
       d->max_tokens < 1 || d->head_dim < 1)
     return ZHA_ERR_INVALID;
   if (d->dtype != ZHA_F32 && d->dtype != ZHA_BF16) return ZHA_ERR_INVALID;
+  if (d->summary != ZHA_SUMMARY_NATIVE && d->summary != ZHA_SUMMARY_FP8) return ZHA_ERR_INVALID;
+  if (d->summary == ZHA_SUMMARY_FP8 && d->dtype != ZHA_BF16) return ZHA_ERR_UNSUPPORTED;
   if (d->n_q_heads % d->n_kv_heads != 0) return ZHA_ERR_INVALID;
   if (d->batch > ZHA_MAX_BATCH) return ZHA_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return ZHA_ERR_UNSUPPORTED;
@@ -66,6 +68,7 @@ void free_tree(zha_tree* t) {
   for (int l = 0; l < ZHA_MAX_LEVELS + 2; ++l) {
     if (t->m[l]) (void)hipFree(t->m[l]);
     if (t->b[l]) (void)hipFree(t->b[l]);
+    if (t->ms[l]) (void)hipFree(t->ms[l]);
     if (t->kept[l]) (void)hipFree(t->kept[l]);
   }
   void* ps[] = {t->refs,   t->spine,  t->sub_lse, t->sub_m,  t->counts,    t->scores,   t->spart,    t->keys,     t->apart,
@@ -153,6 +156,7 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   t->L = desc->levels;
   t->T = desc->max_tokens;
   t->esize = desc->dtype == ZHA_BF16 ? 2 : 4;
+  t->f8 = desc->summary == ZHA_SUMMARY_FP8;
   const int64_t Nc = (t->T / t->C) * t->C;
   int64_t span = 1;
   for (int l = 1; l <= t->L; ++l) {
@@ -170,8 +174,9 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   t->WA = zha_sparse_wgs(U);
   bool ok = true;
   for (int l = 1; l <= L && ok; ++l) {
-    ok = ok && dalloc(t, &t->m[l], (size_t)U * t->cap[l] * R * d * t->esize);
+    ok = ok && dalloc(t, &t->m[l], (size_t)U * t->cap[l] * R * d * (t->f8 ? 1 : t->esize));
     ok = ok && dalloc(t, &t->b[l], (size_t)U * t->cap[l] * R * sizeof(float));
+    if (t->f8) ok = ok && dalloc(t, &t->ms[l], (size_t)U * t->cap[l] * R * sizeof(float));
     ok = ok && dalloc(t, &t->kept[l], (size_t)U * t->cap[l] * sizeof(int32_t));
   }
   ok = ok && dalloc(t, &t->refs, (size_t)desc->n_kv_heads * R * d * sizeof(float));
@@ -322,9 +327,22 @@ zha_status zha_tree_level_capacity(zha_tree_t t, int32_t level, int64_t* nodes) 
 zha_status zha_tree_copy_level(zha_tree_t t, int32_t level, void* m_out, float* b_out, hipStream_t s) {
   if (!t || !m_out || !b_out || level < 1 || level > t->L) return ZHA_ERR_INVALID;
   const size_t nm = (size_t)t->U * t->cap[level] * t->R;
-  if (hipMemcpyAsync(m_out, t->m[level], nm * t->d * t->esize, hipMemcpyDeviceToDevice, s) != hipSuccess)
+  if (t->f8) {
+    const hipError_t e = zha_launch_decode_fp8((const uint8_t*)t->m[level], t->ms[level], (int64_t)nm, t->d,
+                                               (__bf16*)m_out, s);
+    if (e != hipSuccess) return hip_fail("zha_tree_copy_level", e);
+  } else if (hipMemcpyAsync(m_out, t->m[level], nm * t->d * t->esize, hipMemcpyDeviceToDevice, s) != hipSuccess) {
     return ZHA_ERR_HIP;
+  }
   if (hipMemcpyAsync(b_out, t->b[level], nm * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return ZHA_ERR_HIP;
+  return ZHA_OK;
+}
+
+zha_status zha_tree_copy_scales(zha_tree_t t, int32_t level, float* scale_out, hipStream_t s) {
+  if (!t || !scale_out || level < 1 || level > t->L || !t->f8) return ZHA_ERR_INVALID;
+  const size_t nm = (size_t)t->U * t->cap[level] * t->R;
+  if (hipMemcpyAsync(scale_out, t->ms[level], nm * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
     return ZHA_ERR_HIP;
   return ZHA_OK;
 }

@@ -33,6 +33,7 @@ struct BuildArgs {
   const float* refs;        // [Hkv][R][d]
   void* m[ZHA_MAX_LEVELS + 2];
   float* b[ZHA_MAX_LEVELS + 2];
+  float* ms[ZHA_MAX_LEVELS + 2];    // fp8 summaries: row scales (m holds e4m3 codes); null entries otherwise
   int64_t cap[ZHA_MAX_LEVELS + 2];
   int64_t lpn[ZHA_MAX_LEVELS + 2];  // leaves per node at level l: C^(l-1)
   float* spine;             // [U][L+1][E+2][NT]
@@ -137,20 +138,47 @@ __device__ __forceinline__ void leaf_planes(const T* Kb, int64_t c, int C, int l
   acc_finish(acc, lse, m);
 }
 
-// Store node j of level l: m~ = m rounded to the storage type, b = LSE - r.m~.
+// Store node j of level l: m~ = m rounded to the storage type, b = LSE - r.m~.  With fp8
+// summaries the row (16 lanes) shares one power-of-two scale from its largest magnitude.
 template <typename T, int E, int D>
 __device__ __forceinline__ void emit(const BuildArgs& a, int u, int l, int64_t j, int r, int ln, const float (&rv)[E],
                                      float lse, const float (&m)[E]) {
-  T* mp = (T*)a.m[l] + (((int64_t)u * a.cap[l] + j) * a.R + r) * D + ln * E;
+  const int64_t row = ((int64_t)u * a.cap[l] + j) * a.R + r;
   float mt[E];
+  if (a.ms[l]) {
+    float amax = 0.0f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const T x = Mf<T>::from_f32(m[e]);
-    mp[e] = x;
-    mt[e] = Mf<T>::to_f32(x);
+    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(m[e]));
+    const int ex = fp8_row_exp(max16(amax));
+    uint8_t* cp = (uint8_t*)a.m[l] + row * D + ln * E;
+    uint32_t w[(E + 3) / 4];
+#pragma unroll
+    for (int i = 0; i < (E + 3) / 4; ++i) w[i] = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t c = fp8_encode(__builtin_ldexpf(m[e], -ex));
+      w[e / 4] |= c << (8 * (e % 4));
+      mt[e] = __builtin_ldexpf(fp8_value(c), ex);
+    }
+    if constexpr (E % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < E / 4; ++i) ((uint32_t*)cp)[i] = w[i];
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) cp[e] = (uint8_t)(w[e / 4] >> (8 * (e % 4)));
+    }
+    if (ln == 0) a.ms[l][row] = __builtin_ldexpf(1.0f, ex);
+  } else {
+    T* mp = (T*)a.m[l] + row * D + ln * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const T x = Mf<T>::from_f32(m[e]);
+      mp[e] = x;
+      mt[e] = Mf<T>::to_f32(x);
+    }
   }
   const float rm = dot_slice<E>(rv, mt);
-  if (ln == 0) a.b[l][((int64_t)u * a.cap[l] + j) * a.R + r] = lse - rm;
+  if (ln == 0) a.b[l][row] = lse - rm;
 }
 
 // Accumulator stack of levels lbase.. in LDS, struct-of-arrays [l - lbase][E+2][NT].
@@ -410,6 +438,7 @@ BuildArgs make_args(const zha_tree* t, const void* K) {
   for (int l = 0; l < ZHA_MAX_LEVELS + 2; ++l) {
     a.m[l] = t->m[l];
     a.b[l] = t->b[l];
+    a.ms[l] = t->ms[l];
     a.cap[l] = t->cap[l];
     a.lpn[l] = l >= 1 ? t->span[l] / t->C : 1;
   }
@@ -428,6 +457,16 @@ BuildArgs make_args(const zha_tree* t, const void* K) {
   a.len = t->len;
   a.len_prev = t->len_prev;
   return a;
+}
+
+// Decoded fp8 summaries: out[row][k] = value(code[row][k]) * scale[row], exact in bf16.
+__global__ __launch_bounds__(256) void zha_decode_fp8_kernel(const uint8_t* codes, const float* scale, int64_t rows,
+                                                              int d, __bf16* out) {
+  const int64_t n = rows * d;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const float v = fp8_value(codes[i]) * scale[i / d];
+    out[i] = Mf<__bf16>::from_f32(v);
+  }
 }
 
 }  // namespace
@@ -507,4 +546,13 @@ hipError_t zha_launch_append(zha_tree* t, const void* K, hipStream_t s) {
   if (e != hipSuccess) return e;
   zha_time_end(t, s, ZHA_K_APPEND, 0);
   return hipSuccess;
+}
+
+hipError_t zha_launch_decode_fp8(const uint8_t* codes, const float* scale, int64_t rows, int d, __bf16* out,
+                                 hipStream_t s) {
+  int64_t blocks = (rows * d + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(zha_decode_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes, scale, rows, d, out);
+  return hipGetLastError();
 }

@@ -65,6 +65,45 @@ template <> struct Mf<float> {
   __device__ static __forceinline__ float from_f32(float x) { return x; }
 };
 
+// ---------------------------------------------------------------- fp8 (OCP e4m3) summaries
+//
+// A row of m is stored as e4m3 codes times a power-of-two scale 2^e, e the smallest
+// integer with max|m| * 2^-e <= 448 (the largest e4m3 value).  Encoding rounds m * 2^-e to
+// the nearest e4m3 value, ties to even mantissa, subnormals (multiples of 2^-9 below 2^-6)
+// kept.  Decoding uses the hardware conversion (exact: every e4m3 value is a float).
+
+// Scale exponent of a row whose largest magnitude is amax (0 for an all-zero row).
+__device__ __forceinline__ int fp8_row_exp(float amax) {
+  if (!(amax >= 1e-30f)) return 0;  // an all-zero (or negligible) row: every code is 0
+  const uint32_t u = __float_as_uint(amax);
+  const int ea = (int)((u >> 23) & 0xFF) - 127;   // amax = M * 2^ea, M in [1, 2) (normal amax)
+  const uint32_t mant = u & 0x7FFFFFu;            // M > 1.75 <=> mantissa field > 0.75 * 2^23
+  return ea - 8 + (mant > 0x600000u ? 1 : 0);
+}
+
+// e4m3 code of f (|f| <= 448): sign, 4-bit biased exponent (bias 7), 3-bit mantissa.
+__device__ __forceinline__ uint32_t fp8_encode(float f) {
+  const uint32_t sgn = __float_as_uint(f) >> 31;
+  const float a = fabsf(f);
+  uint32_t code;
+  if (a < 0.015625f) {                           // below 2^-6: subnormal steps of 2^-9
+    const uint32_t q = (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8 (8 is the smallest normal)
+    code = q;                                    // q == 8 encodes exponent field 1, mantissa 0
+  } else {
+    const int E = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;        // -6..8
+    const uint32_t t = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 3 - E));  // 8..16
+    code = t == 16u ? (uint32_t)(E + 8) << 3 : ((uint32_t)(E + 7) << 3) | (t - 8u);
+  }
+  return (sgn << 7) | code;
+}
+
+// Value of e4m3 code c (normal or subnormal; codes here never hold NaN).
+__device__ __forceinline__ float fp8_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float v = e == 0u ? (float)m * 0.001953125f : __builtin_ldexpf(1.0f + (float)m * 0.125f, (int)e - 7);
+  return (c & 0x80u) ? -v : v;
+}
+
 // Sum over the 16 lanes of a DPP row (xor butterfly: every lane ends with the same bits).
 // Sum over each row of 16 lanes, the total left in every lane of the row, with four
 // DPP adds (data-parallel-primitive lane moves within a row, no LDS round trip): swap
@@ -80,6 +119,14 @@ __device__ __forceinline__ float sum16(float x) {
   x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
   x += dpp_mov<0x141>(x);  // row_half_mirror
   x += dpp_mov<0x140>(x);  // row_mirror
+  return x;
+}
+// Maximum over the 16 lanes of a DPP row, in every lane of the row (same moves as sum16).
+__device__ __forceinline__ float max16(float x) {
+  x = fmaxf(x, dpp_mov<0xB1>(x));
+  x = fmaxf(x, dpp_mov<0x4E>(x));
+  x = fmaxf(x, dpp_mov<0x141>(x));
+  x = fmaxf(x, dpp_mov<0x140>(x));
   return x;
 }
 
@@ -147,8 +194,10 @@ struct zha_tree {
   int64_t T;                      // max_tokens (token stride of K/V)
   int64_t cap[ZHA_MAX_LEVELS + 2];  // nodes per unit at each level (1..L)
   int64_t span[ZHA_MAX_LEVELS + 2]; // tokens covered by one node at each level: C^l
-  void* m[ZHA_MAX_LEVELS + 2];      // level planes m [U][cap][R][d]
+  void* m[ZHA_MAX_LEVELS + 2];      // level planes m [U][cap][R][d] (tree dtype, or fp8 e4m3 codes)
   float* b[ZHA_MAX_LEVELS + 2];     // level planes b [U][cap][R]
+  float* ms[ZHA_MAX_LEVELS + 2];    // fp8 summaries: power-of-two scale of each m row [U][cap][R] (else null)
+  bool f8;                          // m stored as fp8 e4m3 codes
   int32_t* kept[ZHA_MAX_LEVELS + 2];// per-level kept ids [U][cap]
   float* refs;                      // [Hkv][R][d]
   float* spine;                     // [U][L+1][R*16][E+2] open-node accumulators
@@ -198,5 +247,7 @@ hipError_t zha_launch_dense(const void* q, const void* K, const void* V, const Z
                             int Hkv, int d, int64_t T, zha_dtype dt, float scale, float* out, float* lse,
                             float* part, int WA, hipStream_t s);
 hipError_t zha_launch_copy16(void* dst, const void* src, int64_t n16, hipStream_t s);
+hipError_t zha_launch_decode_fp8(const uint8_t* codes, const float* scale, int64_t rows, int d, __bf16* out,
+                                 hipStream_t s);
 int zha_sparse_wgs(int U);
 int zha_dense_wgs(int U);

@@ -130,8 +130,9 @@ __device__ __forceinline__ void load_scores(const float* sp, int G, float4 (&sv)
 
 struct ScoreArgs {
   Level v;
-  const void* m;          // level planes m [U][capl][R][d]
+  const void* m;          // level planes m [U][capl][R][d] (tree dtype, or fp8 e4m3 codes)
   const float* b;         // level planes b [U][capl][R]
+  const float* ms;        // fp8 summaries: row scales [U][capl][R]
   const void* q;          // [B][Hq][d]
   int64_t capl;
   float* scores;          // [U][cap1][G]
@@ -142,16 +143,38 @@ struct ScoreArgs {
   float scale;
 };
 
+// Eight fp8 e4m3 codes (two dwords) as eight bf16 values (exact), by the hardware
+// conversion; element e is byte e.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 r;
+  const uint32_t w[2] = {lo, hi};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+    const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+    // upper halves of the floats: bf16 values, exact (an e4m3 value has 4 significant bits)
+    r[2 * i] = __builtin_amdgcn_perm(__float_as_uint(f01[1]), __float_as_uint(f01[0]), 0x07060302u);
+    r[2 * i + 1] = __builtin_amdgcn_perm(__float_as_uint(f23[1]), __float_as_uint(f23[0]), 0x07060302u);
+  }
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
 // Scores one level's frontier.  Rows of an MFMA tile are (node, reference query)
 // pairs: 16/R nodes per tile; columns are the KV head's query heads (G <= 16).
 // Lane i loads its row's plane slice (k-slot group i/16) straight from HBM; the
-// query fragments stay in registers for the whole workgroup.
-template <typename T, int R, int D, int UN>
+// query fragments stay in registers for the whole workgroup.  F8: the planes are fp8
+// codes; lane (row, group) loads its row's d/4 contiguous codes, decodes them to bf16 in
+// registers, and the query fragments take the same k order (the dot product does not
+// depend on it); the row's scale multiplies the product.
+template <typename T, int R, int D, int UN, bool F8>
 __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
   typedef Mf<T> M;
   constexpr int NK = D / M::KPER;
+  constexpr int NR = F8 ? D / 64 : 1;   // 16-byte code loads per lane per tile (F8)
   constexpr int NPT = 16 / R;
   constexpr int SUPER = 4 * UN * NPT;
+  static_assert(!F8 || M::EPL == 8, "fp8 planes feed the bf16 matrix instruction");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, grp = lane >> 4;
   const int u = blockIdx.y, bi = u / a.v.Hkv, g = u % a.v.Hkv;
@@ -165,13 +188,18 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
 
   typename M::frag qf[NK];
   {
-    const T* qp = (const T*)a.q + ((int64_t)bi * a.Hq + (int64_t)g * G + row) * D + grp * M::EPL;
+    const T* qp = (const T*)a.q + ((int64_t)bi * a.Hq + (int64_t)g * G + row) * D;
 #pragma unroll
-    for (int s = 0; s < NK; ++s) qf[s] = row < G ? M::load(qp + s * M::KPER) : M::zero();
+    for (int s = 0; s < NK; ++s) {
+      const int k0 = F8 ? grp * (D / 4) + s * 8 : s * M::KPER + grp * M::EPL;
+      qf[s] = row < G ? M::load(qp + k0) : M::zero();
+    }
   }
   const int32_t* par = a.v.parent ? a.v.parent + (int64_t)u * a.v.cap_parent : nullptr;
   const T* mb = (const T*)a.m + (int64_t)u * a.capl * R * D;
+  const uint8_t* m8 = (const uint8_t*)a.m + (int64_t)u * a.capl * R * D;
   const float* bb = a.b + (int64_t)u * a.capl * R;
+  const float* sb = F8 ? a.ms + (int64_t)u * a.capl * R : nullptr;
   const int GS = score_stride(G);
   float* sc = a.scores + (int64_t)u * a.cap1 * GS;
   float runM = -INFINITY, runS = 0.0f;
@@ -218,47 +246,107 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
       }
     }
   };
-  // Scores of the super-tile at `base` from its loaded planes.
-  auto compute = [&](const Frag (&af)[UN][NK], const float (&bv)[UN][4], int base) {
+  // Scores of the super-tile at `base` from its loaded planes (F8: rs holds the rows'
+  // scales, which multiply the product; unused otherwise).
+  // Scores of tile k of the super-tile at `base` from its plane fragments (F8: rs holds the
+  // rows' scales, which multiply the product; unused otherwise).
+  auto score_tile = [&](int k, const Frag (&afk)[NK], const float (&bvk)[4], const float (&rs)[4], int base) {
+    const int tbk = base + (k * 4 + wave) * NPT;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int k = 0; k < UN; ++k) {
-      const int tbk = base + (k * 4 + wave) * NPT;
-      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s = 0; s < NK; ++s) acc = M::mma(afk[s], qf[s], acc);
+    float v[4];
 #pragma unroll
-      for (int s = 0; s < NK; ++s) acc = M::mma(af[k][s], qf[s], acc);
-      float v[4];
+    for (int jj = 0; jj < 4; ++jj) {
+      const float mul = F8 ? a.scale * rs[jj] : a.scale;
+      v[jj] = bvk[jj] == -INFINITY ? -INFINITY : fmaf(acc[jj], mul, bvk[jj]);
+    }
+    // maximum over each node's planes; rows 4*grp+jj of this lane belong to node (4*grp+jj)/R
+    if (R >= 4) {
+      float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+      if (R >= 8) mx = fmaxf(mx, __shfl_xor(mx, 16));
+      if (R >= 16) mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool writer = (R == 4) || (R == 8 && (grp & 1) == 0) || (R == 16 && grp == 0);
+      const int pos = tbk + (4 * grp) / R;
+      if (writer && row < G && pos < end) {
+        sc[(int64_t)pos * GS + row] = mx;
+        lse_push(runM, runS, mx);
+      }
+    } else if (R == 2) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) v[jj] = bv[k][jj] == -INFINITY ? -INFINITY : fmaf(acc[jj], a.scale, bv[k][jj]);
-      // maximum over each node's planes; rows 4*grp+jj of this lane belong to node (4*grp+jj)/R
-      if (R >= 4) {
-        float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-        if (R >= 8) mx = fmaxf(mx, __shfl_xor(mx, 16));
-        if (R >= 16) mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const bool writer = (R == 4) || (R == 8 && (grp & 1) == 0) || (R == 16 && grp == 0);
-        const int pos = tbk + (4 * grp) / R;
-        if (writer && row < G && pos < end) {
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const float mx = fmaxf(v[2 * h2], v[2 * h2 + 1]);
+        const int pos = tbk + 2 * grp + h2;
+        if (row < G && pos < end) {
           sc[(int64_t)pos * GS + row] = mx;
           lse_push(runM, runS, mx);
         }
-      } else if (R == 2) {
+      }
+    } else {
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const float mx = fmaxf(v[2 * h2], v[2 * h2 + 1]);
-          const int pos = tbk + 2 * grp + h2;
-          if (row < G && pos < end) {
-            sc[(int64_t)pos * GS + row] = mx;
-            lse_push(runM, runS, mx);
-          }
+      for (int jj = 0; jj < 4; ++jj) {
+        const int pos = tbk + 4 * grp + jj;
+        if (row < G && pos < end) {
+          sc[(int64_t)pos * GS + row] = v[jj];
+          lse_push(runM, runS, v[jj]);
         }
+      }
+    }
+  };
+
+  auto compute = [&](const Frag (&af)[UN][NK], const float (&bv)[UN][4], int base) {
+#pragma unroll
+    for (int k = 0; k < UN; ++k) score_tile(k, af[k], bv[k], bv[k], base);
+  };
+  // F8: codes, offsets and scales of this lane's tiles in the super-tile at `base`.
+  auto load_stage8 = [&](int base, const int (&pp)[UN], uint4 (&rw)[UN][NR], float (&bv)[UN][4],
+                         float (&sv)[UN][4]) {
+#pragma unroll
+    for (int k = 0; k < UN; ++k) {
+      const int tbk = base + (k * 4 + wave) * NPT;
+      const int pos = tbk + row / R;
+      const bool v = pos < end;
+      int id = pos;
+      if (par) id = a.v.Cshift >= 0 ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
+                                    : pp[k] * a.v.C + pos % a.v.C;
+      id = v ? id : 0;
+      const uint8_t* cp = m8 + ((int64_t)id * R + (row % R)) * D + grp * (D / 4);
+#pragma unroll
+      for (int i = 0; i < NR; ++i) rw[k][i] = v ? *(const uint4*)(cp + 16 * i) : make_uint4(0u, 0u, 0u, 0u);
+      if constexpr (R >= 4) {
+        const int id2 = __shfl(id, 4 * grp);
+        const bool v2 = tbk + (4 * grp) / R < end;
+        const int64_t o = (int64_t)id2 * R + (4 * grp) % R;
+        const float4 b4 = v2 ? *(const float4*)(bb + o) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        const float4 s4 = v2 ? *(const float4*)(sb + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+        bv[k][0] = b4.x; bv[k][1] = b4.y; bv[k][2] = b4.z; bv[k][3] = b4.w;
+        sv[k][0] = s4.x; sv[k][1] = s4.y; sv[k][2] = s4.z; sv[k][3] = s4.w;
       } else {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const int pos = tbk + 4 * grp + jj;
-          if (row < G && pos < end) {
-            sc[(int64_t)pos * GS + row] = v[jj];
-            lse_push(runM, runS, v[jj]);
-          }
+          const int r2 = 4 * grp + jj;
+          const int id2 = __shfl(id, r2);
+          const bool v2 = tbk + r2 / R < end;
+          const int64_t o = (int64_t)id2 * R + (r2 % R);
+          bv[k][jj] = v2 ? bb[o] : -INFINITY;
+          sv[k][jj] = v2 ? sb[o] : 0.0f;
         }
+      }
+    }
+  };
+  // F8: decode the codes (lane k-slots s*8 .. s*8+7 of its d/4 codes per matrix step),
+  // then score as the bf16 path does with the row scale in the multiplier.
+  auto compute8 = [&](const uint4 (&rw)[UN][NR], const float (&bv)[UN][4], const float (&sv)[UN][4], int base) {
+    if constexpr (F8) {
+#pragma unroll
+      for (int k = 0; k < UN; ++k) {
+        Frag afk[NK];
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+          const uint4 q4 = rw[k][s / 2];
+          afk[s] = (s & 1) ? fp8x8_to_bf16(q4.z, q4.w) : fp8x8_to_bf16(q4.x, q4.y);
+        }
+        score_tile(k, afk, bv[k], sv[k], base);
       }
     }
   };
@@ -267,21 +355,38 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
   // the next and the parent entries of the one after are in flight.  The two register
   // buffers alternate by unrolling the loop twice.
   int ppA[UN], ppB[UN];
-  Frag afA[UN][NK], afB[UN][NK];
   float bvA[UN][4], bvB[UN][4];
   fetch_par(start, ppA);
   fetch_par(start + step, ppB);
-  if (start < end) load_stage(start, ppA, afA, bvA);
-  for (int base = start; base < end;) {
-    fetch_par(base + 2 * step, ppA);
-    load_stage(base + step, ppB, afB, bvB);
-    compute(afA, bvA, base);
-    base += step;
-    if (base >= end) break;
-    fetch_par(base + 2 * step, ppB);
-    load_stage(base + step, ppA, afA, bvA);
-    compute(afB, bvB, base);
-    base += step;
+  if constexpr (F8) {
+    uint4 rwA[UN][NR], rwB[UN][NR];
+    float svA[UN][4], svB[UN][4];
+    if (start < end) load_stage8(start, ppA, rwA, bvA, svA);
+    for (int base = start; base < end;) {
+      fetch_par(base + 2 * step, ppA);
+      load_stage8(base + step, ppB, rwB, bvB, svB);
+      compute8(rwA, bvA, svA, base);
+      base += step;
+      if (base >= end) break;
+      fetch_par(base + 2 * step, ppB);
+      load_stage8(base + step, ppA, rwA, bvA, svA);
+      compute8(rwB, bvB, svB, base);
+      base += step;
+    }
+  } else {
+    Frag afA[UN][NK], afB[UN][NK];
+    if (start < end) load_stage(start, ppA, afA, bvA);
+    for (int base = start; base < end;) {
+      fetch_par(base + 2 * step, ppA);
+      load_stage(base + step, ppB, afB, bvB);
+      compute(afA, bvA, base);
+      base += step;
+      if (base >= end) break;
+      fetch_par(base + 2 * step, ppB);
+      load_stage(base + step, ppA, afA, bvA);
+      compute(afB, bvB, base);
+      base += step;
+    }
   }
   // per-head (max, sum exp) of this workgroup: lanes of one head, then the 4 waves
   {
@@ -1402,20 +1507,22 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
   compact_epilogue(a);
 }
 
-template <typename T, int R, int D>
+// Two tiles per wave per pipeline stage (for fp8 codes too: four would not fit in the
+// registers of four workgroups per compute unit, and fewer workgroups measured slower).
+template <typename T, int R, int D, bool F8>
 hipError_t launch_score(const ScoreArgs& a, int W, int U, hipStream_t s) {
-  hipLaunchKernelGGL((zha_score_kernel<T, R, D, 2>), dim3(W, U), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((zha_score_kernel<T, R, D, 2, F8>), dim3(W, U), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, bool F8 = false>
 hipError_t launch_score_r(const ScoreArgs& a, int R, int W, int U, hipStream_t s) {
   switch (R) {
-    case 1: return launch_score<T, 1, D>(a, W, U, s);
-    case 2: return launch_score<T, 2, D>(a, W, U, s);
-    case 4: return launch_score<T, 4, D>(a, W, U, s);
-    case 8: return launch_score<T, 8, D>(a, W, U, s);
-    default: return launch_score<T, 16, D>(a, W, U, s);
+    case 1: return launch_score<T, 1, D, F8>(a, W, U, s);
+    case 2: return launch_score<T, 2, D, F8>(a, W, U, s);
+    case 4: return launch_score<T, 4, D, F8>(a, W, U, s);
+    case 8: return launch_score<T, 8, D, F8>(a, W, U, s);
+    default: return launch_score<T, 16, D, F8>(a, W, U, s);
   }
 }
 
@@ -1431,7 +1538,8 @@ int cshift_of(int C) {
 // Score workgroups per unit at a level: about one 8-node super-tile each at small
 // levels, at most t->WS.
 int zha_score_wgs(const zha_tree* t, int level) {
-  int64_t w = (t->cap[level] + 7) / 8;
+  const int per = 8;  // nodes of one super-tile at R = 16
+  int64_t w = (t->cap[level] + per - 1) / per;
   if (w < 1) w = 1;
   if (w > t->WS) w = t->WS;
   return (int)w;
@@ -1468,6 +1576,7 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     sa.v = v;
     sa.m = t->m[l];
     sa.b = t->b[l];
+    sa.ms = t->ms[l];
     sa.q = q;
     sa.capl = t->cap[l];
     sa.scores = t->scores;
@@ -1478,7 +1587,10 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     sa.G = t->G;
     sa.scale = scale;
     zha_time_begin(t, s, ZHA_K_SCORE, l);
-    if (t->desc.dtype == ZHA_BF16)
+    if (t->f8)
+      e = t->d == 64 ? launch_score_r<__bf16, 64, true>(sa, t->R, sa.W, U, s)
+                     : launch_score_r<__bf16, 128, true>(sa, t->R, sa.W, U, s);
+    else if (t->desc.dtype == ZHA_BF16)
       e = t->d == 64 ? launch_score_r<__bf16, 64>(sa, t->R, sa.W, U, s) : launch_score_r<__bf16, 128>(sa, t->R, sa.W, U, s);
     else
       e = t->d == 64 ? launch_score_r<float, 64>(sa, t->R, sa.W, U, s) : launch_score_r<float, 128>(sa, t->R, sa.W, U, s);

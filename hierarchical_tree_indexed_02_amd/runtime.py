@@ -20,10 +20,16 @@ class Tree:
     """One attention layer's summary tree (library-owned device memory)."""
 
     def __init__(self, batch, n_kv_heads, n_q_heads, head_dim, chunk, levels, n_refs, max_tokens,
-                 dtype=torch.bfloat16):
+                 dtype=torch.bfloat16, summary="native"):
+        """summary: "native" (m stored in dtype) or "fp8" (e4m3 codes with a power-of-two
+        scale per node and reference; dtype bf16 only)."""
+        if summary not in ("native", "fp8"):
+            raise ValueError(f"unsupported summary storage {summary!r}")
         self.desc = zha.zha_tree_desc(batch, n_kv_heads, n_q_heads, head_dim, chunk, levels, n_refs, max_tokens,
-                                      zdtype(dtype))
+                                      zdtype(dtype),
+                                      zha.ZHA_SUMMARY_FP8 if summary == "fp8" else zha.ZHA_SUMMARY_NATIVE)
         self.dtype = dtype
+        self.summary = summary
         self.B, self.Hkv, self.Hq, self.d = batch, n_kv_heads, n_q_heads, head_dim
         self.C, self.L, self.R, self.T = chunk, levels, n_refs, max_tokens
         self.U = batch * n_kv_heads
@@ -67,12 +73,19 @@ class Tree:
         return zha.zha_tree_level_capacity(self.h, level)
 
     def level(self, level: int, device="cuda"):
-        """(m [U][cap][R][d] in the tree dtype, b [U][cap][R] fp32) of one level."""
+        """(m [U][cap][R][d] in the tree dtype, b [U][cap][R] fp32) of one level; with fp8
+        summaries m holds the decoded values (code times the row's power-of-two scale)."""
         cap = self.capacity(level)
         m = torch.empty((self.U, cap, self.R, self.d), dtype=self.dtype, device=device)
         b = torch.empty((self.U, cap, self.R), dtype=torch.float32, device=device)
         zha.zha_tree_copy_level(self.h, level, m, b)
         return m, b
+
+    def scales(self, level: int, device="cuda"):
+        """Row scales [U][cap][R] fp32 of one level of a tree with fp8 summaries."""
+        sc = torch.empty((self.U, self.capacity(level), self.R), dtype=torch.float32, device=device)
+        zha.zha_tree_copy_scales(self.h, level, sc)
+        return sc
 
     def route_level(self, level: int, device="cuda"):
         """(frontier counts [U], kept counts [U], kept ids [U][cap]) of the last route."""

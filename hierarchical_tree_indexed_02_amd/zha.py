@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libzha.so")
 
 ZHA_OK, ZHA_ERR_INVALID, ZHA_ERR_CAPACITY, ZHA_ERR_NOMEM, ZHA_ERR_UNSUPPORTED, ZHA_ERR_HIP = range(6)
 ZHA_F32, ZHA_BF16 = 0, 1
+ZHA_SUMMARY_NATIVE, ZHA_SUMMARY_FP8 = 0, 1
 ZHA_K_BUILD, ZHA_K_APPEND, ZHA_K_SCORE, ZHA_K_SELECT, ZHA_K_ATTEND, ZHA_K_MERGE, ZHA_K_MASS, ZHA_K_COMPACT = range(1, 9)
 KERNEL_NAMES = {1: "build", 2: "append", 3: "score", 4: "select", 5: "attend", 6: "merge", 7: "mass", 8: "compact"}
 
@@ -24,7 +25,7 @@ KERNEL_NAMES = {1: "build", 2: "append", 3: "score", 4: "select", 5: "attend", 6
 class zha_tree_desc(Structure):
     _fields_ = [("batch", c_int32), ("n_kv_heads", c_int32), ("n_q_heads", c_int32), ("head_dim", c_int32),
                 ("chunk", c_int32), ("levels", c_int32), ("n_refs", c_int32), ("max_tokens", c_int64),
-                ("dtype", c_int)]
+                ("dtype", c_int), ("summary", c_int)]
 
 
 class zha_kept(Structure):
@@ -71,6 +72,7 @@ def load():
             "zha_dense_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int64]),
             "zha_tree_level_capacity": (st, [vp, c_int32, POINTER(c_int64)]),
             "zha_tree_copy_level": (st, [vp, c_int32, vp, vp, vp]),
+            "zha_tree_copy_scales": (st, [vp, c_int32, vp, vp]),
             "zha_route_copy_level": (st, [vp, c_int32, vp, vp, vp, vp]),
             "zha_timing_enable": (st, [vp, c_int32, c_int32]),
             "zha_timing_read": (st, [vp, _i32p, _i32p, POINTER(c_float), c_int32, _i32p]),
@@ -173,6 +175,10 @@ def zha_tree_level_capacity(tree: int, level: int) -> int:
 
 def zha_tree_copy_level(tree: int, level: int, m_out, b_out, stream=None) -> None:
     _check(load().zha_tree_copy_level(tree, level, _ptr(m_out), _ptr(b_out), _stream(stream)), "zha_tree_copy_level")
+
+
+def zha_tree_copy_scales(tree: int, level: int, scale_out, stream=None) -> None:
+    _check(load().zha_tree_copy_scales(tree, level, _ptr(scale_out), _stream(stream)), "zha_tree_copy_scales")
 
 
 def zha_route_copy_level(tree: int, level: int, frontier_counts, kept_counts, kept_ids, stream=None) -> None:

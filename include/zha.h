@@ -66,6 +66,18 @@ typedef enum {
 
 typedef enum { ZHA_F32 = 0, ZHA_BF16 = 1 } zha_dtype;
 
+/* Storage of the planes' m.  ZHA_SUMMARY_NATIVE: m in the tree dtype.
+ * ZHA_SUMMARY_FP8 (tree dtype bf16 only): a low-precision router summary
+ * ([wqu] opening bullets: a router variant in a 4-bit format was also tested;
+ * the pages give no format, this build offers 8 bits).  Each (node, reference)
+ * row of d values is stored as OCP fp8 e4m3 codes times a power-of-two scale
+ * 2^e, e the smallest integer with max|m| * 2^-e <= 448; each value m * 2^-e is
+ * rounded to the nearest e4m3 value (ties to even mantissa, subnormals kept).
+ * b = LSE - r.m~ is formed from the decoded m~ = code * 2^e, as for native
+ * storage, so every plane stays exact at q = r.  A level-1 node then takes
+ * R * (d + 8) bytes instead of R * (2d + 4). */
+typedef enum { ZHA_SUMMARY_NATIVE = 0, ZHA_SUMMARY_FP8 = 1 } zha_summary;
+
 /* Shape of one layer's tree.  Supported: head_dim in {64, 128};
  * n_refs in {1, 2, 4, 8, 16}; group = n_q_heads / n_kv_heads in [1, 16];
  * chunk >= 2; 1 <= levels <= 16 with chunk^levels <= 2^30; max_tokens < 2^31. */
@@ -78,7 +90,8 @@ typedef struct {
     int32_t levels;       /* L: summary levels */
     int32_t n_refs;       /* R: reference queries per KV head */
     int64_t max_tokens;   /* capacity per sequence (the K/V token stride) */
-    zha_dtype dtype;      /* storage dtype of q, K, V and of the planes' m */
+    zha_dtype dtype;      /* storage dtype of q, K and V, and of the planes' m when native */
+    zha_summary summary;  /* storage of the planes' m (ZHA_SUMMARY_FP8 needs dtype bf16) */
 } zha_tree_desc;
 
 /* Kept leaf chunks of the last zha_route on a tree: a view into the tree's
@@ -172,9 +185,15 @@ ZHA_API zha_status zha_tree_level_capacity(zha_tree_t tree, int32_t level, int64
 
 /* Copies level `level` (1..L) of the tree: m_out [B*Hkv][cap][R][d] in the
  * tree dtype and b_out [B*Hkv][cap][R] float32 (cap from
- * zha_tree_level_capacity).  Device buffers owned by the caller. */
+ * zha_tree_level_capacity).  With fp8 summaries m_out receives the decoded
+ * m~ = code * 2^e, exact in bf16.  Device buffers owned by the caller. */
 ZHA_API zha_status zha_tree_copy_level(zha_tree_t tree, int32_t level, void* m_out, float* b_out,
                                hipStream_t stream);
+
+/* Copies the row scales 2^e of level `level` of a tree with fp8 summaries:
+ * scale_out [B*Hkv][cap][R] float32, a device buffer owned by the caller.
+ * Errors: ZHA_ERR_INVALID (null pointer, level out of range, native tree). */
+ZHA_API zha_status zha_tree_copy_scales(zha_tree_t tree, int32_t level, float* scale_out, hipStream_t stream);
 
 /* Copies the last route's result at `level`: frontier_counts [B*Hkv],
  * kept_counts [B*Hkv], kept_ids [B*Hkv][cap] (ascending).  The frontier of

@@ -61,6 +61,12 @@ def _bind(path: str):
     L.zo_attend.argtypes = [_f64p, _int, _int, _f64p, _f64p, _i64p, _i64, _f64p, _f64p]
     L.zo_attend_blockwise.restype = None
     L.zo_attend_blockwise.argtypes = [_f64p, _int, _int, _f64p, _f64p, _i64p, _i64, _i64, _f64p, _f64p]
+    L.zo_e4m3_round.restype = ctypes.c_double
+    L.zo_e4m3_round.argtypes = [ctypes.c_double]
+    L.zo_e4m3_row_exp.restype = _int
+    L.zo_e4m3_row_exp.argtypes = [ctypes.c_double]
+    L.zo_fp8_rows.restype = None
+    L.zo_fp8_rows.argtypes = [_f64p, _i64, _int, _f64p, _f64p]
     L.zo_num_threads.restype = _int
     L.zo_num_threads.argtypes = []
     L.zo_set_num_threads.restype = None
@@ -123,6 +129,34 @@ def node_planes(K, t0: int, t1: int, refs):
     m = np.empty((R, d)); b = np.empty(R); lse = np.empty(R)
     lib().zo_node_planes(_p(K, _f64p), d, t0, t1, _p(refs, _f64p), R, _p(m, _f64p), _p(b, _f64p), _p(lse, _f64p))
     return m, b, lse
+
+
+def e4m3_round(x: float) -> float:
+    """Nearest OCP fp8 e4m3 value to x (|x| <= 448), ties to even mantissa."""
+    return lib().zo_e4m3_round(float(x))
+
+
+def e4m3_row_exp(amax: float) -> int:
+    """Smallest s with amax * 2^-s <= 448 (0 for amax = 0)."""
+    return lib().zo_e4m3_row_exp(float(amax))
+
+
+def fp8_rows(m):
+    """fp8 summary storage of rows m [..., d]: (m~ = grid value * 2^s per row, scale 2^s [...])."""
+    m = _f64(m)
+    shp = m.shape
+    d = shp[-1]
+    flat = m.reshape(-1, d)
+    out = np.empty_like(flat); sc = np.empty(flat.shape[0])
+    lib().zo_fp8_rows(_p(flat, _f64p), flat.shape[0], d, _p(out, _f64p), _p(sc, _f64p))
+    return out.reshape(shp), sc.reshape(shp[:-1])
+
+
+def fp8_planes(m, lse, refs):
+    """Planes with fp8-stored means: (m~ [n][R][d], b~ = LSE - r.m~ [n][R], scale [n][R])."""
+    mq, sc = fp8_rows(m)
+    b = _f64(lse) - np.einsum("nrd,rd->nr", mq, _f64(refs))
+    return mq, b, sc
 
 
 class Tree:

@@ -213,6 +213,64 @@ ZO_EXPORT void zo_tree_merge(const double* K, int64_t N, int d, const double* re
 
 /* ------------------------------------------------------------------ routing */
 
+/* ------------------------------------------------------- fp8 router summaries
+ *
+ * Optional low-precision storage of the planes' m ([wqu] opening bullets: a
+ * router variant in a 4-bit format was also tested; the pages name no format;
+ * this is the 8-bit reading).  The grid is OCP fp8 e4m3: sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits; normal values (1 + f/8) 2^(e-7) for biased e in
+ * 1..15 up to 448 = 1.75 * 2^8 (code 0x7F is not a number), subnormals f * 2^-9.
+ * A row of m (one node, one reference query) is stored as grid values times a
+ * power of two 2^s, s the smallest integer with max|m| 2^-s <= 448, each value
+ * rounded to the nearest grid value, ties to the value whose last mantissa bit
+ * is 0.  b = LSE - r.m~ is formed from the stored m~, as for any storage.
+ */
+
+/* Nearest e4m3 grid value to x (|x| <= 448), ties to even mantissa. */
+ZO_EXPORT double zo_e4m3_round(double x)
+{
+    const double a = fabs(x);
+    double step;
+    if (a < ldexp(1.0, -6)) {
+        step = ldexp(1.0, -9);                 /* subnormal spacing */
+    } else {
+        int e;
+        frexp(a, &e);                          /* a = f 2^e, f in [0.5, 1): binade 2^(e-1) */
+        step = ldexp(1.0, (e - 1) - 3);        /* three mantissa bits */
+    }
+    const double n = a / step;                 /* exact: step is a power of two */
+    double r = floor(n);
+    const double frac = n - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    const double v = r * step;
+    return x < 0 ? -v : v;
+}
+
+/* Scale exponent s of a row with largest magnitude amax: the smallest integer
+ * with amax 2^-s <= 448 (0 for an all-zero row). */
+ZO_EXPORT int zo_e4m3_row_exp(double amax)
+{
+    if (!(amax > 0.0)) return 0;
+    int e;
+    frexp(amax, &e);
+    int s = e - 12;                            /* amax 2^-s >= 2^11 > 448 */
+    while (ldexp(amax, -s) > 448.0) ++s;
+    return s;
+}
+
+/* Stores n rows of d values as fp8 summaries: out = grid value * 2^s per row,
+ * scale[i] = 2^s_i. */
+ZO_EXPORT void zo_fp8_rows(const double* m, int64_t n, int d, double* out, double* scale)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        double amax = 0.0;
+        for (int k = 0; k < d; ++k) amax = fmax(amax, fabs(m[i * d + k]));
+        const int sx = zo_e4m3_row_exp(amax);
+        for (int k = 0; k < d; ++k) out[i * d + k] = ldexp(zo_e4m3_round(ldexp(m[i * d + k], -sx)), sx);
+        scale[i] = ldexp(1.0, sx);
+    }
+}
+
 /* Node score for head h: the maximum over the R tangent planes (query pre-scaled). */
 static double zo_score(const double* m_node, const double* b_node, int R, int d, const double* qh)
 {

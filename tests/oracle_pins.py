@@ -358,9 +358,86 @@ def pin_attend_set():
         assert S.tolist() == sorted(want), (N, C, kept)
 
 
+# ------------------------------------------------------- fp8 summaries
+
+def _e4m3_grid():
+    """Every finite OCP e4m3 value by its code (sign, 4-bit exponent with bias 7,
+    3-bit mantissa; exponent field 0 is subnormal; code 0x7F / 0xFF is not a number)."""
+    vals = {}
+    for c in range(256):
+        sgn, e, f = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and f == 7:
+            continue
+        v = f * 2.0 ** -9 if e == 0 else (1 + f / 8) * 2.0 ** (e - 7)
+        vals[c] = -v if sgn else v
+    return vals
+
+
+def _bruteforce_e4m3(x, grid):
+    """Nearest grid value by enumeration; on a tie the code with the even mantissa bit."""
+    best = None
+    for c, v in grid.items():
+        d = abs(v - x)
+        if best is None or d < best[0] or (d == best[0] and (c & 1) == 0 and (best[1] & 1) == 1):
+            best = (d, c, v)
+    return best[2]
+
+
+def pin_fp8_quantizer():
+    """The oracle's e4m3 rounding equals enumeration of the format's 254 finite values
+    (nearest, ties to even mantissa) on grid points, midpoints, just off midpoints and
+    random values over the whole range, subnormals included; 448 is the largest value."""
+    grid = _e4m3_grid()
+    assert max(grid.values()) == 448.0 and min(v for v in grid.values() if v > 0) == 2.0 ** -9
+    pos = sorted(v for v in grid.values() if v >= 0)
+    xs = []
+    for a, b in zip(pos, pos[1:]):
+        mid = 0.5 * (a + b)
+        xs += [a, mid, mid * (1 + 1e-9), mid * (1 - 1e-9), -mid, -a]
+    rng = np.random.default_rng(5)
+    xs += list(rng.uniform(-448, 448, 300)) + list(rng.uniform(-1, 1, 300) * 2.0 ** rng.integers(-12, 9, 300))
+    for x in xs:
+        got = oracle.e4m3_round(x)
+        want = _bruteforce_e4m3(x, grid)
+        assert got == want or (got == 0 and want == 0), f"e4m3({x!r}) = {got!r}, nearest is {want!r}"
+
+
+def pin_fp8_rows():
+    """Row storage: the scale is the smallest power of two that brings the row's largest
+    magnitude within 448 (checked against the neighbouring exponent), every stored value is
+    a grid value times the scale, and the error is within half a grid step."""
+    grid = set(abs(v) for v in _e4m3_grid().values())
+    rng = np.random.default_rng(6)
+    m = rng.standard_normal((40, 32)) * 10.0 ** rng.uniform(-4, 3, (40, 1))
+    m[3] = 0.0
+    m[5, :] = 448.0 * 2.0 ** -3          # an exact power-of-two boundary
+    mq, sc = oracle.fp8_rows(m)
+    for i in range(m.shape[0]):
+        amax = np.max(np.abs(m[i]))
+        s = math.log2(sc[i])
+        assert s == int(s), "scale is a power of two"
+        if amax == 0:
+            assert np.all(mq[i] == 0) and sc[i] == 1.0
+            continue
+        assert amax / sc[i] <= 448.0 and amax / (sc[i] / 2) > 448.0, f"row {i}: scale not minimal"
+        for v, x in zip(mq[i], m[i]):
+            c = abs(v) / sc[i]
+            assert c in grid, f"row {i}: {v} is not a grid value times the scale"
+            a = abs(x) / sc[i]
+            half = 2.0 ** -10 if a < 2.0 ** -6 else 2.0 ** (math.floor(math.log2(a)) - 4)
+            assert abs(v - x) / sc[i] <= half * (1 + 1e-12), f"row {i}: error beyond half a step"
+    # planes from fp8 means stay exact at q = r (b is formed from the stored mean)
+    K, _, refs, _ = _rand(7, 40, 16, 4, 1)
+    t = oracle.tree_definition(K, refs, 4, 2)
+    for l in (1, 2):
+        mq, b, _ = oracle.fp8_planes(t.m[l], t.lse[l], refs)
+        at_r = b + np.einsum("nrd,rd->nr", mq, refs)
+        _close(at_r, t.lse[l], 1e-12, f"fp8 plane at q = r, level {l}")
+
+
 ALL_PINS = [
     pin_geometry, pin_tangent_planes, pin_merge_equals_definition, pin_top_p_minimal,
     pin_bruteforce_tiny, pin_nucleus_single_tokens, pin_exact_reference, pin_translation_permutation,
     pin_value_closed_forms, pin_equal_masses, pin_single_level_nesting, pin_growth,
-    pin_dense_two_ways, pin_p_one_is_dense, pin_attend_set,
+    pin_dense_two_ways, pin_p_one_is_dense, pin_attend_set, pin_fp8_quantizer, pin_fp8_rows,
 ]

@@ -4,6 +4,10 @@ Build:   every checked node's stored planes against the oracle's planes by
          definition over the node's tokens:
            |m~ - m| <= 2^-8 |m| + 2e-5   (bf16 storage; fp32: 1e-5 |m| + 1e-5)
            |(b~ + r.m~) - LSE| <= 1e-4 max(1, |LSE|)
+         fp8 summaries (row scale s from the tree): m~ / s is an e4m3 value, the
+         row's largest |m~| / s lies in [224, 448] (s is the smallest power of two
+         that fits), and |m~ - m| <= 2^-4 |m| + 2^-10 s + 1e-5 |m| + 2e-5 (half a
+         grid step, plus the fp32 floor of the mean before rounding).
 Route:   at every level the oracle selects from the GPU's own frontier (the
          children of the GPU's kept set one level up) using the GPU's stored
          planes; the kept sets must be equal except for nodes whose mass is
@@ -72,10 +76,10 @@ class Case:
         self.Kd[b, g, start:start + n] = torch.from_numpy(np.ascontiguousarray(Krows)).to(self.Kd.device, dt)
         self.Vd[b, g, start:start + n] = torch.from_numpy(np.ascontiguousarray(Vrows)).to(self.Vd.device, dt)
 
-    def tree(self, levels=None, chunk=None, refs=None):
+    def tree(self, levels=None, chunk=None, refs=None, summary="native"):
         cfg = self.cfg
         t = Tree(self.B, self.Hkv, self.Hq, self.d, chunk or cfg.chunk, levels or cfg.levels, cfg.n_refs, self.T,
-                 TORCH_DT[cfg.dtype])
+                 TORCH_DT[cfg.dtype], summary=summary)
         t.build(self.Kd, self.refs_d if refs is None else refs, self.lens)
         return t
 
@@ -89,14 +93,42 @@ class Case:
 
 # ----------------------------------------------------------------------------- build
 
+E4M3 = None
+
+
+def _e4m3_values():
+    """Every finite e4m3 magnitude (OCP: bias 7, 3 mantissa bits, subnormals below 2^-6)."""
+    global E4M3
+    if E4M3 is None:
+        v = [f * 2.0 ** -9 for f in range(8)] + [(1 + f / 8) * 2.0 ** (e - 7) for e in range(1, 16) for f in range(8)]
+        E4M3 = np.array(sorted(set(x for x in v if x <= 448.0)))
+    return E4M3
+
+
+def _check_fp8_rows(mg, sg, m_o, where):
+    """fp8 storage of one node's rows: grid membership, minimal scale, error bound."""
+    grid = _e4m3_values()
+    codes = np.abs(mg) / sg[:, None]
+    idx = np.clip(np.searchsorted(grid, codes), 0, len(grid) - 1)
+    on_grid = (grid[idx] == codes) | (grid[np.maximum(idx - 1, 0)] == codes)
+    assert on_grid.all(), f"{where}: stored m / scale is not an e4m3 value"
+    rmax = codes.max(axis=1)
+    nz = rmax > 0
+    assert np.all((rmax[nz] >= 224.0) & (rmax[nz] <= 448.0)), f"{where}: row scale not minimal ({rmax[nz].min()}, {rmax.max()})"
+    err = np.abs(mg - m_o) - (2.0 ** -4 * np.abs(m_o) + 2.0 ** -10 * sg[:, None] + 1e-5 * np.abs(m_o) + 2e-5)
+    assert err.max() <= 0, f"{where}: m excess {err.max():.3e}"
+
+
 def check_build(case: Case, tree: Tree, sample=None, seed=0):
     """Checks stored planes against the oracle.  sample: nodes per (unit, level) or None for all."""
     cfg = case.cfg
     rel, floor = m_tol(cfg.dtype)
+    fp8 = getattr(tree, "summary", "native") == "fp8"
     rng = np.random.default_rng(seed)
     worst_m, worst_b, n_checked = 0.0, 0.0, 0
     for l in range(1, tree.L + 1):
         m_d, b_d = tree.level(l)
+        s_d = tree.scales(l) if fp8 else None
         for b in range(case.B):
             N = case.lens[b]
             n_l = oracle.level_nodes(N, tree.C, l)
@@ -110,13 +142,18 @@ def check_build(case: Case, tree: Tree, sample=None, seed=0):
                 Ku = np.ascontiguousarray(case.unit_kv(b, g)[0], dtype=np.float64)  # widened once per unit
                 mg = m_d[u, torch.from_numpy(nodes).to(m_d.device)].float().cpu().numpy().astype(np.float64)
                 bg = b_d[u, torch.from_numpy(nodes).to(b_d.device)].cpu().numpy().astype(np.float64)
+                sg = (s_d[u, torch.from_numpy(nodes).to(s_d.device)].cpu().numpy().astype(np.float64)
+                      if fp8 else None)
                 refs = case.refs[g].astype(np.float64)
                 for i, j in enumerate(nodes):
                     t0 = j * tree.C ** l
                     t1 = min((j + 1) * tree.C ** l, (N // tree.C) * tree.C)
                     m_o, _, lse_o = oracle.node_planes(Ku[t0:t1], 0, t1 - t0, refs)
-                    err_m = np.abs(mg[i] - m_o) - (rel * np.abs(m_o) + floor)
-                    assert err_m.max() <= 0, f"m level {l} unit {u} node {j}: excess {err_m.max():.3e}"
+                    if fp8:
+                        _check_fp8_rows(mg[i], sg[i], m_o, f"fp8 level {l} unit {u} node {j}")
+                    else:
+                        err_m = np.abs(mg[i] - m_o) - (rel * np.abs(m_o) + floor)
+                        assert err_m.max() <= 0, f"m level {l} unit {u} node {j}: excess {err_m.max():.3e}"
                     plane_at_r = bg[i] + np.einsum("rd,rd->r", refs, mg[i])
                     err_b = np.abs(plane_at_r - lse_o) / np.maximum(1.0, np.abs(lse_o))
                     assert err_b.max() <= PLANE_TOL, f"b level {l} unit {u} node {j}: rel {err_b.max():.3e}"

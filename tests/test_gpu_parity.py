@@ -81,6 +81,28 @@ def test_variants(label, kw, lens):
     say(" dense", check_dense(case, 0))
 
 
+# --------------------------------------------------------------------------- fp8 router summaries
+
+FP8_VARIANTS = [v for v in VARIANTS if v[1].get("dtype", "bf16") == "bf16" and "mid flat" not in v[0]
+                and "large flat" not in v[0]]
+
+
+@pytest.mark.parametrize("label,kw,lens", FP8_VARIANTS, ids=[v[0] for v in FP8_VARIANTS])
+def test_fp8_summaries(label, kw, lens):
+    """Planes stored as e4m3 codes with a power-of-two row scale: storage checked against the
+    oracle's means, routing teacher-forced on the decoded planes, attention on the kept set."""
+    cfg = small(**kw, n_queries=4, needles_per_unit=4)
+    say(f"case fp8 summaries {label}: lens={lens}")
+    case = Case(cfg, lens=lens, n_queries=2)
+    tree = case.tree(summary="fp8")
+    torch.cuda.synchronize()
+    say(" build", check_build(case, tree, sample=None if sum(lens) < 20000 else 256))
+    for t in range(2):
+        for p in (0.5, 0.95):
+            r, a = full_check(case, tree, t, p)
+            say(f" t={t} p={p}", r, a)
+
+
 # --------------------------------------------------------------------------- large-level selection paths
 
 def test_large_level_cut_paths():
@@ -186,9 +208,11 @@ def test_determinism():
 # --------------------------------------------------------------------------- growth
 
 def _valid_equal(case, t_inc, t_full):
+    fp8 = t_inc.summary == "fp8"
     for l in range(1, t_inc.L + 1):
         m1, b1 = t_inc.level(l)
         m2, b2 = t_full.level(l)
+        s1, s2 = (t_inc.scales(l), t_full.scales(l)) if fp8 else (None, None)
         for b in range(case.B):
             n_l = oracle.level_nodes(case.lens[b], t_inc.C, l)
             for g in range(case.Hkv):
@@ -198,16 +222,18 @@ def _valid_equal(case, t_inc, t_full):
                     x1, x2 = x1.view(torch.int16), x2.view(torch.int16)
                 assert torch.equal(x1, x2), f"m level {l} unit {u}"
                 assert torch.equal(b1[u, :n_l], b2[u, :n_l]), f"b level {l} unit {u}"
+                if fp8:
+                    assert torch.equal(s1[u, :n_l], s2[u, :n_l]), f"scale level {l} unit {u}"
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_append_equals_rebuild(dtype):
+@pytest.mark.parametrize("dtype,summary", [("bf16", "native"), ("f32", "native"), ("bf16", "fp8")])
+def test_append_equals_rebuild(dtype, summary):
     cfg = small(batch=2, n_tokens=1200, chunk=4, levels=4, n_refs=8, n_q_heads=8, n_kv_heads=2, n_queries=2,
                 needles_per_unit=4, append_steps=400, dtype=dtype)
-    say(f"case append == rebuild ({dtype}): B=2 N=1200 +400 C=4 L=4 R=8")
+    say(f"case append == rebuild ({dtype}, {summary} summaries): B=2 N=1200 +400 C=4 L=4 R=8")
     case = Case(cfg, lens=[1200, 1001], max_tokens=1700)
     rows = {(b, g): zi.append_rows(cfg, b, g) for b in range(2) for g in range(2)}
-    tree = case.tree()
+    tree = case.tree(summary=summary)
     lens = list(case.lens)
     schedule = [1] * 37 + [5, 64, 3, 200] + [1] * 20
     done = 0
@@ -220,7 +246,7 @@ def test_append_equals_rebuild(dtype):
         tree.append(case.Kd, lens)
         done += k
     case.lens = lens
-    full = case.tree()
+    full = case.tree(summary=summary)
     torch.cuda.synchronize()
     _valid_equal(case, tree, full)
     say(" bitwise equal after", len(schedule), "appends; lens", lens)
@@ -271,6 +297,19 @@ def test_deep_256k_full():
         r, a = full_check(case, tree, t, 0.95)
         say(f" t={t}", r, a)
     say(" dense", check_dense(case, 0))
+
+
+@pytest.mark.slow
+def test_deep_256k_fp8_full():
+    cfg = zi.get_config("deep_256k")
+    say("case deep_256k full, fp8 summaries: N=262144, 32q/4kv, d=128, C=4 L=6 R=16 p=0.95")
+    case = Case(cfg, n_queries=2)
+    tree = case.tree(summary="fp8")
+    torch.cuda.synchronize()
+    say(" build", check_build(case, tree, sample=24))
+    for t in range(2):
+        r, a = full_check(case, tree, t, 0.95)
+        say(f" t={t}", r, a)
 
 
 @pytest.mark.slow

@@ -46,6 +46,12 @@ MUTANTS = [
      "double w = exp(zo_dot(qh, K + S[i] * d, d) - mx);"),
     ("attention_value_index", "for (int j = 0; j < d; ++j) o[j] += w * V[S[i] * d + j];",
      "for (int j = 0; j < d; ++j) o[j] += w * V[S[i] * d + (d - 1 - j)];"),
+    ("e4m3_ties_away", "if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;",
+     "if (frac >= 0.5) r += 1.0;"),
+    ("e4m3_two_mantissa_bits", "step = ldexp(1.0, (e - 1) - 3);", "step = ldexp(1.0, (e - 1) - 2);"),
+    ("e4m3_no_subnormals", "step = ldexp(1.0, -9);                 /* subnormal spacing */",
+     "step = ldexp(1.0, -6);                 /* subnormal spacing */"),
+    ("fp8_scale_not_minimal", "while (ldexp(amax, -s) > 448.0) ++s;", "while (ldexp(amax, -s) > 224.0) ++s;"),
     ("attention_one_head", "const double* qh = q + (int64_t)h * d;\n        double mx = -INFINITY;\n        for (int64_t i = 0; i < nS; ++i) {",
      "const double* qh = q;\n        double mx = -INFINITY;\n        for (int64_t i = 0; i < nS; ++i) {"),
 ]
