@@ -71,7 +71,7 @@ void free_tree(zha_tree* t) {
     if (t->ms[l]) (void)hipFree(t->ms[l]);
     if (t->kept[l]) (void)hipFree(t->kept[l]);
   }
-  void* ps[] = {t->refs,   t->spine,  t->sub_lse, t->sub_m,  t->counts,    t->scores,   t->spart,    t->keys,     t->apart,
+  void* ps[] = {t->refs,   t->spine,  t->sub_lse, t->sub_m,  t->counts,    t->geo,      t->scores,   t->spart,    t->keys,     t->apart,
                 t->fh_cnt, t->fh_mass,  t->fh_edge,  t->cut,      t->sel_cand, t->sel_ctr, t->lb_status,
                 t->lb_epoch, t->lb_error};
   for (void* p : ps)
@@ -187,6 +187,7 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
     ok = ok && dalloc(t, &t->sub_m, (size_t)U * t->cap[t->S] * R * d * sizeof(float));
   }
   ok = ok && dalloc(t, &t->counts, (size_t)2 * (L + 2) * U * sizeof(int32_t));
+  ok = ok && dalloc(t, &t->geo, (size_t)(L + 2) * desc->batch * sizeof(int32_t));
   ok = ok && dalloc(t, &t->scores, (size_t)U * t->cap[1] * ((G + 3) & ~3) * sizeof(float));
   ok = ok && dalloc(t, &t->spart, (size_t)U * t->WS * G * 2 * sizeof(float));
   t->kstride = (t->cap[1] + 3) / 4 * 4;
@@ -208,6 +209,7 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
          hipMemset(t->fh_mass, 0, (size_t)U * nb * sizeof(unsigned long long)) == hipSuccess &&
          hipMemset(t->fh_edge, 0, (size_t)U * 2 * sizeof(unsigned long long)) == hipSuccess &&
          hipMemset(t->sel_ctr, 0, (size_t)zha_sel_ctr_words(U) * sizeof(uint32_t)) == hipSuccess &&
+         hipMemset(t->geo, 0, (size_t)(L + 2) * desc->batch * sizeof(int32_t)) == hipSuccess &&
          hipMemset(t->lb_status, 0, (size_t)U * nchunk * sizeof(unsigned long long)) == hipSuccess &&
          hipMemset(t->lb_error, 0, sizeof(int32_t)) == hipSuccess;
     const uint32_t ep[2] = {1u, 0u};  // status words of epoch 0 (all-zero memory) never match

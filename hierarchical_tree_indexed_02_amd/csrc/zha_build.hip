@@ -45,7 +45,28 @@ struct BuildArgs {
   int64_t T;
   ZLens len;                // lengths after the operation
   ZLens len_prev;           // append: lengths before it
+  int32_t* geo;             // [L+2][B]: row 0 the lengths, row l the nodes of level l per sequence
+  int B;
 };
+
+// Row 0 of the geometry table holds each sequence's length, row l (1..L) its number of
+// level-l nodes, ceil(Nc / C^l) with Nc = C*floor(N / C); row L+1 is zero.  The routing
+// kernels read their frontier sizes here instead of taking them by value.  Written by
+// workgroup (0, 0) of the first kernel of a build or an append.
+__device__ __forceinline__ void write_geo(const BuildArgs& a) {
+  if (blockIdx.x != 0 || blockIdx.y != 0) return;
+  for (int b = threadIdx.x; b < a.B; b += blockDim.x) {
+    const int64_t N = a.len.n[b];
+    const int64_t Nc = (N / a.C) * a.C;
+    a.geo[b] = (int32_t)N;
+    int64_t span = 1;
+    for (int l = 1; l <= a.L; ++l) {
+      span *= a.C;
+      a.geo[(int64_t)l * a.B + b] = (int32_t)((Nc + span - 1) / span);
+    }
+    a.geo[(int64_t)(a.L + 1) * a.B + b] = 0;
+  }
+}
 
 // Node indices fit in 32 bits (C^L <= 2^30 and max_tokens < 2^31): divisions by C are
 // shifts when C is a power of two.
@@ -283,6 +304,7 @@ __device__ __forceinline__ void spine_io(const BuildArgs& a, Stack<E>& st, int u
 // One workgroup per (level-S node, unit); blockDim = 16 R.
 template <typename T, int D>
 __global__ __launch_bounds__(256, 4) void zha_build_subtree_kernel(BuildArgs a) {
+  write_geo(a);
   constexpr int E = D / 16;
   extern __shared__ float lds[];
   const int NT = blockDim.x;
@@ -403,6 +425,7 @@ __global__ __launch_bounds__(256) void zha_build_upper_kernel(BuildArgs a) {
 // One workgroup per unit: fold the leaves completed by the new rows through every level.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void zha_append_kernel(BuildArgs a) {
+  write_geo(a);
   constexpr int E = D / 16;
   extern __shared__ float lds_stack[];
   const int tid = threadIdx.x, r = tid >> 4, ln = tid & 15;
@@ -456,6 +479,8 @@ BuildArgs make_args(const zha_tree* t, const void* K) {
   a.T = t->T;
   a.len = t->len;
   a.len_prev = t->len_prev;
+  a.geo = t->geo;
+  a.B = t->desc.batch;
   return a;
 }
 

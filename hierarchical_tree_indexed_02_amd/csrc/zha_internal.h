@@ -220,6 +220,7 @@ struct zha_tree {
   int32_t* lb_error;                // [1] set if a look-back wait ever gives up
   float* apart;                     // attention partials: o [U][WA][G][d], then (max, sum) [U][WA][G][2]
   int WS, WA;                       // score and attention workgroups per unit (maximum)
+  int32_t* geo;                     // [L+2][B] device: lengths (row 0), nodes of level l per sequence (row l)
   ZLens len;                        // current lengths
   ZLens len_prev;                   // lengths before the last zha_append
   bool built;

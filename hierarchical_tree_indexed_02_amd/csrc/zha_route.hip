@@ -35,15 +35,16 @@ constexpr int NB = 1024;                 // histogram slices
 constexpr int SMALL_NODES = 8192;        // frontiers up to this size are selected in one workgroup
 constexpr int CH = 4096;                 // compaction chunk (positions per workgroup)
 
-// Per-level inputs shared by the kernels of one level.  Node counts per sequence are
-// computed on the host (no integer division on the device).
+// Per-level inputs shared by the kernels of one level.  Node counts per sequence come from
+// the tree's geometry table (written by the build and append kernels), so the launch
+// arguments stay small (a launch's cost grows with the size of its arguments).
 struct Level {
   const int32_t* parent;      // kept ids of level l+1 [U][cap_parent]; null at the top level
   const int32_t* parent_nF;   // frontier counts of this level, written by level l+1 [U]
   int64_t cap_parent;
   int C, Cshift, Hkv;
-  int32_t nodes[ZHA_MAX_BATCH];   // nodes of this level per sequence
-  int32_t child[ZHA_MAX_BATCH];   // nodes of level l-1 per sequence (0 at level 1)
+  const int32_t* nodes;       // nodes of this level per sequence [B]
+  const int32_t* child;       // nodes of level l-1 per sequence [B] (unused at level 1)
 };
 
 __device__ __forceinline__ int frontier_size(const Level& v, int u) {
@@ -866,6 +867,7 @@ __global__ __launch_bounds__(ST) void zha_select_small_kernel(SmallArgs a) {
   const int G = a.G;
   const int nmax = (int)a.capl;  // >= 1
   const int nF = frontier_size(a.v, u);
+  const int nchild = a.next_nF ? child_nodes(a.v, u) : 0;  // loaded now, used at the end
   const int GS = score_stride(G);
   const float* sc = a.scores + (int64_t)u * a.cap1 * GS;
   const int32_t* gpar = a.v.parent ? a.v.parent + (int64_t)u * a.v.cap_parent : nullptr;
@@ -999,7 +1001,7 @@ __global__ __launch_bounds__(ST) void zha_select_small_kernel(SmallArgs a) {
       // only be the frontier's last position
       const int C = a.v.C;
       int nx = C * (int)kept_base;
-      if (sh.last_kept_id > 0) nx = next_frontier((int)kept_base, sh.last_kept_id - 1, C, child_nodes(a.v, u));
+      if (sh.last_kept_id > 0) nx = next_frontier((int)kept_base, sh.last_kept_id - 1, C, nchild);
       a.next_nF[u] = nx;
     }
   }
@@ -1435,6 +1437,7 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
   const int u = blockIdx.y, c = blockIdx.x;
   const int nF = frontier_size(a.v, u);
   const int base = c * CH;
+  const int nchild = a.next_nF && base + CH >= nF ? child_nodes(a.v, u) : 0;  // loaded now, used at the end
   if (tid == 0) s_epoch = __hip_atomic_load(&a.epoch[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (base >= nF) {
     compact_epilogue(a);
@@ -1500,7 +1503,7 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
       // only be the frontier's last position
       const int C = a.v.C;
       int nx = C * (int)total;
-      if (s_last_kept > 0) nx = next_frontier((int)total, s_last_kept - 1, C, child_nodes(a.v, u));
+      if (s_last_kept > 0) nx = next_frontier((int)total, s_last_kept - 1, C, nchild);
       a.next_nF[u] = nx;
     }
   }
@@ -1565,11 +1568,8 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     v.C = t->C;
     v.Cshift = Cshift;
     v.Hkv = t->desc.n_kv_heads;
-    for (int b = 0; b < t->desc.batch; ++b) {
-      const int64_t Nc = ((int64_t)t->len.n[b] / t->C) * t->C;
-      v.nodes[b] = (int32_t)((Nc + t->span[l] - 1) / t->span[l]);
-      v.child[b] = l > 1 ? (int32_t)((Nc + t->span[l - 1] - 1) / t->span[l - 1]) : 0;
-    }
+    v.nodes = t->geo + (int64_t)l * t->desc.batch;
+    v.child = t->geo + (int64_t)(l - 1) * t->desc.batch;
     int32_t* next_nF = l > 1 ? cntF + (int64_t)(l - 1) * U : nullptr;
 
     ScoreArgs sa;
