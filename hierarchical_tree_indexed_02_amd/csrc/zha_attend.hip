@@ -32,8 +32,13 @@ struct AttArgs {
   int Hkv, Hq, G, C, Cshift;
   int64_t T;               // token stride of K/V
   float scale_log2;        // scale * log2(e)
-  ZLens len;
+  const int32_t* lens;     // sparse: sequence lengths [B] on the device (the tree's geometry row 0)
 };
+
+// Dense launches take the lengths by value (the dense entry point gets them from the host);
+// sparse launches read them from the tree, so their arguments stay small.
+template <bool DENSE> struct LensArg { ZLens len; };
+template <> struct LensArg<false> {};
 
 struct Positions {
   int P;        // number of positions
@@ -45,9 +50,11 @@ struct Positions {
 };
 
 template <bool DENSE>
-__device__ __forceinline__ Positions unit_positions(const AttArgs& a, int u, int bi) {
+__device__ __forceinline__ Positions unit_positions(const AttArgs& a, const LensArg<DENSE>& la, int u, int bi) {
   Positions P;
-  const int N = a.len.n[bi];
+  int N;
+  if constexpr (DENSE) N = la.len.n[bi];
+  else N = a.lens[bi];
   if (DENSE) {
     P.P = N; P.nx = N; P.sink = 0; P.Nc = 0; P.nK = 0; P.kp = nullptr;
     return P;
@@ -190,7 +197,7 @@ template <int D> struct PV<float, D> {
 };
 
 template <typename T, int D, bool DENSE>
-__global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a) {
+__global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENSE> la) {
   typedef Mf<T> M;
   typedef PV<T, D> PVT;
   constexpr int NK = D / M::KPER;
@@ -205,7 +212,7 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a) {
   const int row = lane & 15, grp = lane >> 4;
   const int u = blockIdx.y, bi = u / a.Hkv, g = u % a.Hkv;
   const int G = a.G;
-  const Positions P = unit_positions<DENSE>(a, u, bi);
+  const Positions P = unit_positions<DENSE>(a, la, u, bi);
   // Blocks of 4 * ATT_STEP positions are dealt to the workgroups in turn, so the unit's
   // workgroups read neighbouring K/V rows at any moment.
   constexpr int WSTEP = 4 * ATT_STEP;
@@ -417,8 +424,8 @@ __global__ __launch_bounds__(MERGE_THREADS) void zha_merge_kernel(const float* p
 }
 
 template <typename T, int D, bool DENSE>
-hipError_t launch_att(const AttArgs& a, int U, float* out, float* lse, hipStream_t s) {
-  hipLaunchKernelGGL((zha_attend_kernel<T, D, DENSE>), dim3(a.W, U), dim3(256), 0, s, a);
+hipError_t launch_att(const AttArgs& a, const LensArg<DENSE>& la, int U, float* out, float* lse, hipStream_t s) {
+  hipLaunchKernelGGL((zha_attend_kernel<T, D, DENSE>), dim3(a.W, U), dim3(256), 0, s, a, la);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return hipSuccess;
@@ -432,10 +439,13 @@ hipError_t launch_merge(const AttArgs& a, int U, float* out, float* lse, hipStre
 }
 
 template <bool DENSE>
-hipError_t launch_att_dt(const AttArgs& a, zha_dtype dt, int d, int U, float* out, float* lse, hipStream_t s) {
+hipError_t launch_att_dt(const AttArgs& a, const LensArg<DENSE>& la, zha_dtype dt, int d, int U, float* out,
+                         float* lse, hipStream_t s) {
   if (dt == ZHA_BF16)
-    return d == 64 ? launch_att<__bf16, 64, DENSE>(a, U, out, lse, s) : launch_att<__bf16, 128, DENSE>(a, U, out, lse, s);
-  return d == 64 ? launch_att<float, 64, DENSE>(a, U, out, lse, s) : launch_att<float, 128, DENSE>(a, U, out, lse, s);
+    return d == 64 ? launch_att<__bf16, 64, DENSE>(a, la, U, out, lse, s)
+                   : launch_att<__bf16, 128, DENSE>(a, la, U, out, lse, s);
+  return d == 64 ? launch_att<float, 64, DENSE>(a, la, U, out, lse, s)
+                 : launch_att<float, 128, DENSE>(a, la, U, out, lse, s);
 }
 
 int cshift_of(int C) {
@@ -476,9 +486,9 @@ hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const vo
   a.Cshift = cshift_of(t->C);
   a.T = t->T;
   a.scale_log2 = scale * ZHA_LOG2E;
-  a.len = t->len;
+  a.lens = t->geo;
   zha_time_begin(t, s, ZHA_K_ATTEND, 0);
-  hipError_t e = launch_att_dt<false>(a, t->desc.dtype, t->d, t->U, out, lse, s);
+  hipError_t e = launch_att_dt<false>(a, LensArg<false>{}, t->desc.dtype, t->d, t->U, out, lse, s);
   if (e != hipSuccess) return e;
   zha_time_end(t, s, ZHA_K_ATTEND, 0);
   zha_time_begin(t, s, ZHA_K_MERGE, 0);
@@ -506,9 +516,11 @@ hipError_t zha_launch_dense(const void* q, const void* K, const void* V, const Z
   a.Cshift = 0;
   a.T = T;
   a.scale_log2 = scale * ZHA_LOG2E;
-  a.len = len;
+  a.lens = nullptr;
   const int U = B * Hkv;
-  hipError_t e = launch_att_dt<true>(a, dt, d, U, out, lse, s);
+  LensArg<true> la;
+  la.len = len;
+  hipError_t e = launch_att_dt<true>(a, la, dt, d, U, out, lse, s);
   if (e != hipSuccess) return e;
   return d == 64 ? launch_merge<64>(a, U, out, lse, s) : launch_merge<128>(a, U, out, lse, s);
 }
