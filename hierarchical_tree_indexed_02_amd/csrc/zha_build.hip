@@ -171,22 +171,23 @@ __device__ __forceinline__ void emit(const BuildArgs& a, int u, int l, int64_t j
 #pragma unroll
     for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(m[e]));
     const int ex = fp8_row_exp(max16(amax));
-    uint8_t* cp = (uint8_t*)a.m[l] + row * D + ln * E;
-    uint32_t w[(E + 3) / 4];
+    static_assert(E % 4 == 0, "whole code words per lane");
+    uint32_t* cp = (uint32_t*)((uint8_t*)a.m[l] + row * D + ln * E);
 #pragma unroll
-    for (int i = 0; i < (E + 3) / 4; ++i) w[i] = 0u;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const uint32_t c = fp8_encode(__builtin_ldexpf(m[e], -ex));
-      w[e / 4] |= c << (8 * (e % 4));
-      mt[e] = __builtin_ldexpf(fp8_value(c), ex);
-    }
-    if constexpr (E % 4 == 0) {
-#pragma unroll
-      for (int i = 0; i < E / 4; ++i) ((uint32_t*)cp)[i] = w[i];
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) cp[e] = (uint8_t)(w[e / 4] >> (8 * (e % 4)));
+    for (int i = 0; i < E / 4; ++i) {
+      // hardware conversions: round to nearest even onto the e4m3 grid (|x| <= 448 here),
+      // and back (exact)
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(m[4 * i], -ex), __builtin_ldexpf(m[4 * i + 1], -ex), 0,
+                                              false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_ldexpf(m[4 * i + 2], -ex), __builtin_ldexpf(m[4 * i + 3], -ex), w,
+                                          true);
+      cp[i] = (uint32_t)w;
+      const auto v01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+      const auto v23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+      mt[4 * i] = __builtin_ldexpf(v01[0], ex);
+      mt[4 * i + 1] = __builtin_ldexpf(v01[1], ex);
+      mt[4 * i + 2] = __builtin_ldexpf(v23[0], ex);
+      mt[4 * i + 3] = __builtin_ldexpf(v23[1], ex);
     }
     if (ln == 0) a.ms[l][row] = __builtin_ldexpf(1.0f, ex);
   } else {

@@ -70,7 +70,10 @@ template <> struct Mf<float> {
 // A row of m is stored as e4m3 codes times a power-of-two scale 2^e, e the smallest
 // integer with max|m| * 2^-e <= 448 (the largest e4m3 value).  Encoding rounds m * 2^-e to
 // the nearest e4m3 value, ties to even mantissa, subnormals (multiples of 2^-9 below 2^-6)
-// kept.  Decoding uses the hardware conversion (exact: every e4m3 value is a float).
+// kept; the hardware conversion does exactly this for inputs within +-448 (checked against
+// enumeration of the format on every grid point, midpoint and near-midpoint; it keeps the
+// sign of a negative value that rounds to zero, which decodes to the same zero).  Decoding
+// uses the hardware conversion too (exact: every e4m3 value is a float).
 
 // Scale exponent of a row whose largest magnitude is amax (0 for an all-zero row).
 __device__ __forceinline__ int fp8_row_exp(float amax) {
@@ -79,22 +82,6 @@ __device__ __forceinline__ int fp8_row_exp(float amax) {
   const int ea = (int)((u >> 23) & 0xFF) - 127;   // amax = M * 2^ea, M in [1, 2) (normal amax)
   const uint32_t mant = u & 0x7FFFFFu;            // M > 1.75 <=> mantissa field > 0.75 * 2^23
   return ea - 8 + (mant > 0x600000u ? 1 : 0);
-}
-
-// e4m3 code of f (|f| <= 448): sign, 4-bit biased exponent (bias 7), 3-bit mantissa.
-__device__ __forceinline__ uint32_t fp8_encode(float f) {
-  const uint32_t sgn = __float_as_uint(f) >> 31;
-  const float a = fabsf(f);
-  uint32_t code;
-  if (a < 0.015625f) {                           // below 2^-6: subnormal steps of 2^-9
-    const uint32_t q = (uint32_t)__builtin_rintf(a * 512.0f);  // 0..8 (8 is the smallest normal)
-    code = q;                                    // q == 8 encodes exponent field 1, mantissa 0
-  } else {
-    const int E = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;        // -6..8
-    const uint32_t t = (uint32_t)__builtin_rintf(__builtin_ldexpf(a, 3 - E));  // 8..16
-    code = t == 16u ? (uint32_t)(E + 8) << 3 : ((uint32_t)(E + 7) << 3) | (t - 8u);
-  }
-  return (sgn << 7) | code;
 }
 
 // Value of e4m3 code c (normal or subnormal; codes here never hold NaN).

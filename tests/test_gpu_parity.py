@@ -103,6 +103,58 @@ def test_fp8_summaries(label, kw, lens):
             say(f" t={t} p={p}", r, a)
 
 
+def _e4m3_nonnegative():
+    """Every non-negative finite e4m3 value: zero, the subnormals f 2^-9 and the normals up to 448."""
+    v = [f * 2.0 ** -9 for f in range(0, 8)] + [(1 + f / 8) * 2.0 ** (e - 7) for e in range(1, 16) for f in range(8)]
+    return sorted(x for x in v if x <= 448.0)
+
+
+def test_fp8_rounding_exact():
+    """Leaves whose C keys are equal have m = that key exactly, so the stored codes can be
+    compared with the oracle's rounding bit for bit: every midpoint between neighbouring e4m3
+    values (ties go to the even mantissa, subnormals included), the bf16 neighbours of each
+    midpoint, and rows whose largest value sits on either side of a scale boundary."""
+    grid = _e4m3_nonnegative()
+    mids = [0.5 * (a + b) for a, b in zip(grid, grid[1:])]
+    vals = []
+    for m in mids:
+        lo = float(torch.tensor(m, dtype=torch.float64).to(torch.bfloat16).float())
+        assert lo == m, "every e4m3 midpoint is a bf16 value"
+        up = float(torch.nextafter(torch.tensor(m, dtype=torch.bfloat16), torch.tensor(1e9, dtype=torch.bfloat16)))
+        dn = float(torch.nextafter(torch.tensor(m, dtype=torch.bfloat16), torch.tensor(-1e9, dtype=torch.bfloat16)))
+        vals += [m, -m, up, -dn]
+    d, C = 128, 4
+    per_row = d - 1
+    rows = []
+    for i in range(0, len(vals), per_row):
+        chunk = vals[i:i + per_row]
+        chunk += [0.0] * (per_row - len(chunk))
+        rows.append([448.0] + chunk)                      # largest value exactly 448: scale 2^0
+    rows.append([450.0] + [v / 2 for v in vals[:per_row]])  # 450 needs scale 2^1
+    rows.append([-0.875] + [v / 512 for v in vals[:per_row]])  # largest 0.875 = 448 * 2^-9
+    keys = np.array(rows, dtype=np.float32)
+    n_leaf = len(rows)
+    N = n_leaf * C
+    cfg = small(batch=1, n_tokens=N, n_q_heads=1, n_kv_heads=1, head_dim=d, chunk=C, levels=1, n_refs=4,
+                n_queries=2, needles_per_unit=1)
+    say(f"case fp8 rounding of exact midpoints: {n_leaf} leaves of {C} equal keys, d={d}")
+    case = Case(cfg, lens=[N], n_queries=2)
+    Kfull = np.repeat(keys, C, axis=0)
+    case.Kd[0, 0, :N] = torch.from_numpy(Kfull).to(case.Kd.device, torch.bfloat16)
+    assert torch.equal(case.Kd[0, 0, :N].float().cpu(), torch.from_numpy(Kfull)), "keys are bf16 values"
+    tree = case.tree(summary="fp8")
+    m_d, _ = tree.level(1)
+    s_d = tree.scales(1)
+    got_m = m_d[0, :n_leaf].double().cpu().numpy()            # [n_leaf][R][d]
+    got_s = s_d[0, :n_leaf].double().cpu().numpy()            # [n_leaf][R]
+    want_m, want_s = oracle.fp8_rows(np.repeat(keys[:, None, :].astype(np.float64), cfg.n_refs, axis=1))
+    bad = np.argwhere(got_m != want_m)
+    assert bad.size == 0, f"{len(bad)} stored values differ from the oracle's rounding, e.g. leaf/ref/k {bad[0].tolist()}: " \
+                          f"gpu {got_m[tuple(bad[0])]!r} oracle {want_m[tuple(bad[0])]!r}"
+    assert np.array_equal(got_s, want_s), "row scales differ"
+    say(f" {got_m.size} stored values equal the oracle's rounding; scales {sorted(set(got_s.ravel().tolist()))}")
+
+
 # --------------------------------------------------------------------------- large-level selection paths
 
 def test_large_level_cut_paths():
