@@ -45,6 +45,8 @@ def parse():
                     help="storage of the planes' m for the headline measurement")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the extra pass with fp8 summaries (reported beside the headline)")
+    ap.add_argument("--no-per-head", action="store_true",
+                    help="skip the extra pass that routes every query head alone (reported beside the headline)")
     return ap.parse_args()
 
 
@@ -132,7 +134,7 @@ def main():
     outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(args.layers)]
     lses = [torch.empty((B, Hq), dtype=torch.float32, device=dev) for _ in range(args.layers)]
 
-    def measure(summary):
+    def measure(summary, mode="group"):
         """Builds one tree per layer replica with the given m storage, times the stage
         breakdown and the K-step region, and replays the routes for the byte counts."""
         lens = [N] * B
@@ -140,7 +142,7 @@ def main():
         trees = []
         build_ms = []
         for li in range(args.layers):
-            tr = Tree(B, Hkv, Hq, d, C, L, R, T, dt, summary=summary)
+            tr = Tree(B, Hkv, Hq, d, C, L, R, T, dt, summary=summary, per_head_routes=mode == "per_head")
             torch.cuda.synchronize()
             ev0.record()
             tr.build(Ks[li], refs, lens)
@@ -182,10 +184,10 @@ def main():
                     layer_lens[li] = [n + 1 for n in layer_lens[li]]
                     seg("append", lambda: tr.append(Ks[li], layer_lens[li]), record)
                 for x in p_sweep:
-                    seg(x, lambda x=x: (tr.route(qd[t], x, 1.0),
+                    seg(x, lambda x=x: (tr.route(qd[t], x, 1.0, mode=mode),
                                         tr.attend(qd[t], Ks[li], Vs[li], 1.0, out=outs[li], lse=lses[li])), record)
                 return
-            tr.route(qd[t], p, 1.0)
+            tr.route(qd[t], p, 1.0, mode=mode)
             tr.attend(qd[t], Ks[li], Vs[li], 1.0, out=outs[li], lse=lses[li])
 
         for i in range(args.warmup):
@@ -237,13 +239,15 @@ def main():
 
         # algorithmic bytes of each step (routes are deterministic: replay each query once, untimed)
         S_node = R * (d + 8) if summary == "fp8" else R * (d * es + 4)
+        RU = U * (G if mode == "per_head" else 1)  # routing units
+        Gr = G if mode == "group" else 1           # query heads per routing unit
         fr_tot = {l: 0 for l in range(1, L + 1)}
         kept_tot = {l: 0 for l in range(1, L + 1)}
         attend_tok = 0
         steps_q = [i % nq for i in range(args.steps)]
         for t in sorted(set(steps_q)):
             w = steps_q.count(t)
-            trees[0].route(qd[t], p, 1.0)
+            trees[0].route(qd[t], p, 1.0, mode=mode)
             torch.cuda.synchronize()
             for l in range(1, L + 1):
                 nf, nk, ids = trees[0].route_level(l)
@@ -252,8 +256,8 @@ def main():
                 if l == 1:
                     nk1 = nk.cpu().numpy()
                     first = ids[:, 0].cpu().numpy()
-                    for u in range(U):
-                        Nu = layer_lens[0][u // Hkv]
+                    for u in range(RU):
+                        Nu = layer_lens[0][u // (RU // B)]
                         Nc = (Nu // C) * C
                         sink = 1 if (Nc > 0 and (nk1[u] == 0 or first[u] != 0)) else 0
                         attend_tok += w * (sink + (Nu - Nc) + int(nk1[u]) * C)
@@ -263,13 +267,13 @@ def main():
         io_bytes = B * Hq * d * es + B * Hq * (d + 1) * 4 + 8 * sum(kept_tot.values()) / nsteps
         step_bytes = route_bytes + attend_bytes + io_bytes
         Ncur = layer_lens[0][0]
-        kappa = attend_tok / nsteps / (U * Ncur)
+        kappa = attend_tok / nsteps / (RU * Ncur)
         dense_bytes = U * Ncur * 2 * d * es
 
         # the dominant kernel: largest share of the step's time
         if dom_name.startswith("score_l"):
             l = dom["level"]
-            dom_bytes = fr_tot[l] / nsteps * (S_node + G * 4) + B * Hq * d * es + (fr_tot[l] / nsteps / C * 4 if l < L else 0)
+            dom_bytes = fr_tot[l] / nsteps * (S_node + Gr * 4) + B * Hq * d * es + (fr_tot[l] / nsteps / C * 4 if l < L else 0)
             traffic = committed_traffic(args.config) if l == 1 and summary == "native" else None
         elif dom_name == "attend":
             dom_bytes = attend_bytes + B * Hq * d * es
@@ -314,6 +318,16 @@ def main():
                    kernels={k: round(v["avg_us"], 2) for k, v in r8["kernels"].items()})
         if growing:
             fp8["p_sweep"] = {str(x): round(r8["seg_us"].get("append", 0.0) + r8["seg_us"][x], 2) for x in p_sweep}
+    per_head = None
+    if not args.no_per_head and args.summary == "native":
+        log("-- the same workload, every query head routed alone")
+        rh = measure("native", mode="per_head")
+        per_head = dict(us_per_step=round(rh["ms_step"] * 1e3, 2), step_bytes=round(rh["step_bytes"]),
+                        step_gbs=round(rh["step_bytes"] / (rh["ms_step"] * 1e-3) / 1e9, 1),
+                        kappa=round(rh["kappa"], 4), roofline=rh["roofline"],
+                        kernels={k: round(v["avg_us"], 2) for k, v in rh["kernels"].items()})
+        if growing:
+            per_head["p_sweep"] = {str(x): round(rh["seg_us"].get("append", 0.0) + rh["seg_us"][x], 2) for x in p_sweep}
 
     # dense decode on the same GPU and inputs, same protocol
     dense_us = None
@@ -386,6 +400,8 @@ def main():
     result["config"]["summary"] = args.summary
     if fp8 is not None:
         result["fp8_summaries"] = fp8
+    if per_head is not None:
+        result["per_head_routes"] = per_head
     if growing:
         result["append_us"] = round(seg_us.get("append", 0.0), 2)
         result["p_sweep"] = {str(x): round(seg_us.get("append", 0.0) + seg_us[x], 2) for x in p_sweep}

@@ -6,6 +6,8 @@
 
 #include <new>
 
+#include <algorithm>
+
 #include "zha_internal.h"
 
 int zha_score_wgs(const zha_tree* t, int level);
@@ -167,17 +169,27 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   t->span[0] = 1;
   t->cap[0] = 0;
   const int U = t->U, R = t->R, d = t->d, G = t->G, L = t->L;
-  int ws = 2048 / U;  // score workgroups per unit: two rounds of four per compute unit in all
-  if (ws > 512) ws = 512;
-  if (ws < 1) ws = 1;
-  t->WS = ws;
+  // routing workspace: for U routing units of G heads, and with per-head routes also for
+  // U*G routing units of one head; every per-unit array is sized for the larger count
+  const int RUmax = desc->per_head_routes ? U * G : U;
+  t->RUmax = RUmax;
+  t->hr = 1;
+  t->RU = U;
+  t->WS = zha_score_wgs_units(U);
   t->WA = zha_sparse_wgs(U);
+  size_t spart_n = (size_t)U * t->WS * G * 2, apart_n = (size_t)U * t->WA * G * (d + 2);
+  size_t score_n = (size_t)U * ((G + 3) & ~3);
+  if (desc->per_head_routes) {
+    spart_n = std::max(spart_n, (size_t)RUmax * zha_score_wgs_units(RUmax) * 2);
+    apart_n = std::max(apart_n, (size_t)RUmax * zha_sparse_wgs(RUmax) * (d + 2));
+    score_n = std::max(score_n, (size_t)RUmax * 4);
+  }
   bool ok = true;
   for (int l = 1; l <= L && ok; ++l) {
     ok = ok && dalloc(t, &t->m[l], (size_t)U * t->cap[l] * R * d * (t->f8 ? 1 : t->esize));
     ok = ok && dalloc(t, &t->b[l], (size_t)U * t->cap[l] * R * sizeof(float));
     if (t->f8) ok = ok && dalloc(t, &t->ms[l], (size_t)U * t->cap[l] * R * sizeof(float));
-    ok = ok && dalloc(t, &t->kept[l], (size_t)U * t->cap[l] * sizeof(int32_t));
+    ok = ok && dalloc(t, &t->kept[l], (size_t)RUmax * t->cap[l] * sizeof(int32_t));
   }
   ok = ok && dalloc(t, &t->refs, (size_t)desc->n_kv_heads * R * d * sizeof(float));
   ok = ok && dalloc(t, &t->spine, (size_t)U * zha_spine_bytes(L, d, R));
@@ -186,31 +198,33 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
     ok = ok && dalloc(t, &t->sub_lse, (size_t)U * t->cap[t->S] * R * sizeof(float));
     ok = ok && dalloc(t, &t->sub_m, (size_t)U * t->cap[t->S] * R * d * sizeof(float));
   }
-  ok = ok && dalloc(t, &t->counts, (size_t)2 * (L + 2) * U * sizeof(int32_t));
+  ok = ok && dalloc(t, &t->counts, (size_t)2 * (L + 2) * RUmax * sizeof(int32_t));
   ok = ok && dalloc(t, &t->geo, (size_t)(L + 2) * desc->batch * sizeof(int32_t));
-  ok = ok && dalloc(t, &t->scores, (size_t)U * t->cap[1] * ((G + 3) & ~3) * sizeof(float));
-  ok = ok && dalloc(t, &t->spart, (size_t)U * t->WS * G * 2 * sizeof(float));
+  ok = ok && dalloc(t, &t->scores, (size_t)t->cap[1] * score_n * sizeof(float));
+  ok = ok && dalloc(t, &t->spart, spart_n * sizeof(float));
   t->kstride = (t->cap[1] + 3) / 4 * 4;
-  ok = ok && dalloc(t, &t->keys, (size_t)U * t->kstride * sizeof(uint32_t));
-  ok = ok && dalloc(t, &t->apart, (size_t)U * t->WA * G * (d + 2) * sizeof(float));
+  ok = ok && dalloc(t, &t->keys, (size_t)RUmax * t->kstride * sizeof(uint32_t));
+  ok = ok && dalloc(t, &t->apart, apart_n * sizeof(float));
   const int nchunk = zha_compact_chunks(t->cap[1]);
   const int nb = zha_hist_bins();
-  ok = ok && dalloc(t, &t->fh_cnt, (size_t)U * nb * sizeof(uint32_t));
-  ok = ok && dalloc(t, &t->fh_mass, (size_t)U * nb * sizeof(unsigned long long));
-  ok = ok && dalloc(t, &t->fh_edge, (size_t)U * 2 * sizeof(unsigned long long));
-  ok = ok && dalloc(t, &t->cut, (size_t)U * 4 * sizeof(int32_t));
-  ok = ok && dalloc(t, &t->sel_cand, (size_t)zha_sel_cand_entries(U) * 2 * sizeof(uint32_t));
-  ok = ok && dalloc(t, &t->sel_ctr, (size_t)zha_sel_ctr_words(U) * sizeof(uint32_t));
-  ok = ok && dalloc(t, &t->lb_status, (size_t)U * nchunk * sizeof(unsigned long long));
+  ok = ok && dalloc(t, &t->fh_cnt, (size_t)RUmax * nb * sizeof(uint32_t));
+  ok = ok && dalloc(t, &t->fh_mass, (size_t)RUmax * nb * sizeof(unsigned long long));
+  ok = ok && dalloc(t, &t->fh_edge, (size_t)RUmax * 2 * sizeof(unsigned long long));
+  ok = ok && dalloc(t, &t->cut, (size_t)RUmax * 4 * sizeof(int32_t));
+  const int64_t cand_n = std::max(zha_sel_cand_entries(U), zha_sel_cand_entries(RUmax));
+  const int ctr_n = std::max(zha_sel_ctr_words(U), zha_sel_ctr_words(RUmax));
+  ok = ok && dalloc(t, &t->sel_cand, (size_t)cand_n * 2 * sizeof(uint32_t));
+  ok = ok && dalloc(t, &t->sel_ctr, (size_t)ctr_n * sizeof(uint32_t));
+  ok = ok && dalloc(t, &t->lb_status, (size_t)RUmax * nchunk * sizeof(unsigned long long));
   ok = ok && dalloc(t, &t->lb_epoch, 2 * sizeof(uint32_t));
   ok = ok && dalloc(t, &t->lb_error, sizeof(int32_t));
   if (ok) {  // counters and histograms start at zero and are left at zero by the kernels
-    ok = hipMemset(t->fh_cnt, 0, (size_t)U * nb * sizeof(uint32_t)) == hipSuccess &&
-         hipMemset(t->fh_mass, 0, (size_t)U * nb * sizeof(unsigned long long)) == hipSuccess &&
-         hipMemset(t->fh_edge, 0, (size_t)U * 2 * sizeof(unsigned long long)) == hipSuccess &&
-         hipMemset(t->sel_ctr, 0, (size_t)zha_sel_ctr_words(U) * sizeof(uint32_t)) == hipSuccess &&
+    ok = hipMemset(t->fh_cnt, 0, (size_t)RUmax * nb * sizeof(uint32_t)) == hipSuccess &&
+         hipMemset(t->fh_mass, 0, (size_t)RUmax * nb * sizeof(unsigned long long)) == hipSuccess &&
+         hipMemset(t->fh_edge, 0, (size_t)RUmax * 2 * sizeof(unsigned long long)) == hipSuccess &&
+         hipMemset(t->sel_ctr, 0, (size_t)ctr_n * sizeof(uint32_t)) == hipSuccess &&
          hipMemset(t->geo, 0, (size_t)(L + 2) * desc->batch * sizeof(int32_t)) == hipSuccess &&
-         hipMemset(t->lb_status, 0, (size_t)U * nchunk * sizeof(unsigned long long)) == hipSuccess &&
+         hipMemset(t->lb_status, 0, (size_t)RUmax * nchunk * sizeof(unsigned long long)) == hipSuccess &&
          hipMemset(t->lb_error, 0, sizeof(int32_t)) == hipSuccess;
     const uint32_t ep[2] = {1u, 0u};  // status words of epoch 0 (all-zero memory) never match
     ok = ok && hipMemcpy(t->lb_epoch, ep, sizeof(ep), hipMemcpyHostToDevice) == hipSuccess;
@@ -261,16 +275,27 @@ zha_status zha_append(zha_tree_t t, const void* K, const int32_t* new_seq_lens, 
   return ZHA_OK;
 }
 
-zha_status zha_route(zha_tree_t t, const void* q, float p, float scale, zha_kept* kept, hipStream_t s) {
+zha_status zha_route_ex(zha_tree_t t, const void* q, float p, float scale, zha_route_mode mode, zha_kept* kept,
+                        hipStream_t s) {
   if (!t || !q || !kept) return ZHA_ERR_INVALID;
   if (!t->built) return ZHA_ERR_INVALID;
   if (!(p > 0.0f) || !isfinite(p) || !isfinite(scale)) return ZHA_ERR_INVALID;
+  if (mode != ZHA_ROUTE_GROUP && mode != ZHA_ROUTE_PER_HEAD) return ZHA_ERR_INVALID;
+  if (mode == ZHA_ROUTE_PER_HEAD && t->RUmax != t->U * t->G) return ZHA_ERR_INVALID;
+  t->hr = mode == ZHA_ROUTE_PER_HEAD ? t->G : 1;
+  t->RU = t->U * t->hr;
+  t->WS = zha_score_wgs_units(t->RU);
+  t->WA = zha_sparse_wgs(t->RU);
   hipError_t e = zha_launch_route(t, q, p, scale, s);
   if (e != hipSuccess) return hip_fail("zha_route launch", e);
-  kept->counts = t->counts + (int64_t)(t->L + 2) * t->U + t->U;
+  kept->counts = t->counts + (int64_t)(t->L + 2) * t->RU + t->RU;
   kept->ids = t->kept[1];
   kept->cap = t->cap[1];
   return ZHA_OK;
+}
+
+zha_status zha_route(zha_tree_t t, const void* q, float p, float scale, zha_kept* kept, hipStream_t s) {
+  return zha_route_ex(t, q, p, scale, ZHA_ROUTE_GROUP, kept, s);
 }
 
 zha_status zha_attend(zha_tree_t t, const void* q, const void* K, const void* V, const zha_kept* kept, float scale,
@@ -352,7 +377,7 @@ zha_status zha_tree_copy_scales(zha_tree_t t, int32_t level, float* scale_out, h
 zha_status zha_route_copy_level(zha_tree_t t, int32_t level, int32_t* frontier_counts, int32_t* kept_counts,
                                 int32_t* kept_ids, hipStream_t s) {
   if (!t || !frontier_counts || !kept_counts || !kept_ids || level < 1 || level > t->L) return ZHA_ERR_INVALID;
-  const int U = t->U;
+  const int U = t->RU;  // routing units of the last route
   const int32_t* cF = t->counts + (int64_t)level * U;
   const int32_t* cK = t->counts + (int64_t)(t->L + 2) * U + (int64_t)level * U;
   if (hipMemcpyAsync(frontier_counts, cF, U * sizeof(int32_t), hipMemcpyDeviceToDevice, s) != hipSuccess ||

@@ -28,7 +28,8 @@ struct AttArgs {
   const int32_t* kept_count;
   int64_t cap1;
   float* part;             // o [U][W][G][d] (unnormalised), then (max in log2 units, sum) [U][W][G][2]
-  int W, U;
+  int W, U;                // workgroups per unit; routing units (U = B * Hkv * hr)
+  int hr;                  // routing units per (sequence, KV head): 1, or G when each head is routed alone
   int Hkv, Hq, G, C, Cshift;
   int64_t T;               // token stride of K/V
   float scale_log2;        // scale * log2(e)
@@ -210,7 +211,9 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, grp = lane >> 4;
-  const int u = blockIdx.y, bi = u / a.Hkv, g = u % a.Hkv;
+  // u: routing unit, of G query heads; up: its (sequence, KV head) unit.  Units are numbered
+  // (sequence, KV head, head group), so the unit's first query head is u * G.
+  const int u = blockIdx.y, up = u / a.hr, bi = up / a.Hkv;
   const int G = a.G;
   const Positions P = unit_positions<DENSE>(a, la, u, bi);
   // Blocks of 4 * ATT_STEP positions are dealt to the workgroups in turn, so the unit's
@@ -220,13 +223,13 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
   const int gstep = a.W * WSTEP;
   const int end = P.P;
 
-  const int64_t kvoff = ((int64_t)bi * a.Hkv + g) * a.T * D;
+  const int64_t kvoff = (int64_t)up * a.T * D;
   const T* Kb = (const T*)a.K + kvoff;
   const T* Vb = (const T*)a.V + kvoff;
 
   typename M::frag qf[NK];
   {
-    const T* qp = (const T*)a.q + ((int64_t)bi * a.Hq + (int64_t)g * G + row) * D + grp * M::EPL;
+    const T* qp = (const T*)a.q + ((int64_t)u * G + row) * D + grp * M::EPL;
 #pragma unroll
     for (int s = 0; s < NK; ++s) qf[s] = row < G ? M::load(qp + s * M::KPER) : M::zero();
   }
@@ -361,13 +364,12 @@ constexpr int MERGE_THREADS = 1024;
 constexpr int MERGE_BATCH = 4;
 
 template <int D>
-__global__ __launch_bounds__(MERGE_THREADS) void zha_merge_kernel(const float* part, int U, int W, int G, int Hkv,
-                                                                  int Hq, float* out, float* lse) {
+__global__ __launch_bounds__(MERGE_THREADS) void zha_merge_kernel(const float* part, int U, int W, int G, float* out,
+                                                                  float* lse) {
   constexpr int TPR = D / 4;                  // threads per record (4 floats each)
   constexpr int NGRP = MERGE_THREADS / TPR;   // workgroup subsets
   const int h = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int bi = u / Hkv, g = u % Hkv;
   const float* po = part + ((int64_t)u * W * G + h) * D;                            // record w at po + w*G*D
   const float* pml = part + (int64_t)U * W * G * D + ((int64_t)u * W * G + h) * 2;  // at pml + w*G*2
   __shared__ float s_red[MERGE_THREADS / 64];
@@ -416,7 +418,7 @@ __global__ __launch_bounds__(MERGE_THREADS) void zha_merge_kernel(const float* p
       o.x += v.x; o.y += v.y; o.z += v.z; o.w += v.w;
       L += s_l[k];
     }
-    const int64_t oh = (int64_t)bi * Hq + (int64_t)g * G + h;
+    const int64_t oh = (int64_t)u * G + h;  // units are numbered (sequence, KV head, head group)
     const float inv = 1.0f / L;
     *(float4*)(out + oh * D + 4 * tid) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
     if (tid == 0) lse[oh] = (M + zlog2(L)) * ZHA_LN2;
@@ -434,7 +436,7 @@ hipError_t launch_att(const AttArgs& a, const LensArg<DENSE>& la, int U, float* 
 template <int D>
 hipError_t launch_merge(const AttArgs& a, int U, float* out, float* lse, hipStream_t s) {
   hipLaunchKernelGGL((zha_merge_kernel<D>), dim3(a.G, U), dim3(MERGE_THREADS), 0, s, (const float*)a.part, U, a.W,
-                     a.G, a.Hkv, a.Hq, out, lse);
+                     a.G, out, lse);
   return hipGetLastError();
 }
 
@@ -474,25 +476,26 @@ hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const vo
   AttArgs a;
   a.q = q; a.K = K; a.V = V;
   a.kept = t->kept[1];
-  a.kept_count = t->counts + (int64_t)(t->L + 2) * t->U + t->U;  // kept counts of level 1
+  a.kept_count = t->counts + (int64_t)(t->L + 2) * t->RU + t->RU;  // kept counts of level 1
   a.cap1 = t->cap[1];
   a.part = t->apart;
   a.W = t->WA;
-  a.U = t->U;
+  a.U = t->RU;
+  a.hr = t->hr;
   a.Hkv = t->desc.n_kv_heads;
   a.Hq = t->desc.n_q_heads;
-  a.G = t->G;
+  a.G = t->G / t->hr;
   a.C = t->C;
   a.Cshift = cshift_of(t->C);
   a.T = t->T;
   a.scale_log2 = scale * ZHA_LOG2E;
   a.lens = t->geo;
   zha_time_begin(t, s, ZHA_K_ATTEND, 0);
-  hipError_t e = launch_att_dt<false>(a, LensArg<false>{}, t->desc.dtype, t->d, t->U, out, lse, s);
+  hipError_t e = launch_att_dt<false>(a, LensArg<false>{}, t->desc.dtype, t->d, t->RU, out, lse, s);
   if (e != hipSuccess) return e;
   zha_time_end(t, s, ZHA_K_ATTEND, 0);
   zha_time_begin(t, s, ZHA_K_MERGE, 0);
-  e = t->d == 64 ? launch_merge<64>(a, t->U, out, lse, s) : launch_merge<128>(a, t->U, out, lse, s);
+  e = t->d == 64 ? launch_merge<64>(a, t->RU, out, lse, s) : launch_merge<128>(a, t->RU, out, lse, s);
   if (e != hipSuccess) return e;
   zha_time_end(t, s, ZHA_K_MERGE, 0);
   return hipSuccess;
@@ -509,6 +512,7 @@ hipError_t zha_launch_dense(const void* q, const void* K, const void* V, const Z
   a.part = part;
   a.W = WA;
   a.U = B * Hkv;
+  a.hr = 1;
   a.Hkv = Hkv;
   a.Hq = Hq;
   a.G = Hq / Hkv;

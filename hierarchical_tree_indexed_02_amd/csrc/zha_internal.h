@@ -206,7 +206,10 @@ struct zha_tree {
   uint32_t* lb_epoch;               // [2] look-back epoch (starts at 1) and finished-workgroup count
   int32_t* lb_error;                // [1] set if a look-back wait ever gives up
   float* apart;                     // attention partials: o [U][WA][G][d], then (max, sum) [U][WA][G][2]
-  int WS, WA;                       // score and attention workgroups per unit (maximum)
+  int WS, WA;                       // score and attention workgroups per routing unit, last route's mode
+  int hr;                           // routing units per (sequence, KV head) of the last route: 1 or G
+  int RU;                           // routing units of the last route: U * hr
+  int RUmax;                        // routing units the workspace is sized for: U, or U * G (per-head routes)
   int32_t* geo;                     // [L+2][B] device: lengths (row 0), nodes of level l per sequence (row l)
   ZLens len;                        // current lengths
   ZLens len_prev;                   // lengths before the last zha_append
@@ -238,4 +241,5 @@ hipError_t zha_launch_copy16(void* dst, const void* src, int64_t n16, hipStream_
 hipError_t zha_launch_decode_fp8(const uint8_t* codes, const float* scale, int64_t rows, int d, __bf16* out,
                                  hipStream_t s);
 int zha_sparse_wgs(int U);
+int zha_score_wgs_units(int RU);  // score workgroups per routing unit (before the level's own cap)
 int zha_dense_wgs(int U);

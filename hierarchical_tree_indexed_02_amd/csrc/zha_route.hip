@@ -140,7 +140,9 @@ struct ScoreArgs {
   int64_t cap1;
   float* part;            // [U][W][G][2]: (max, sum exp) of the workgroup's scores per head
   int W;                  // workgroups per unit
-  int Hq, G;
+  int Hq, G;              // query heads; heads per routing unit
+  int Gq;                 // query heads per KV head
+  int hr;                 // routing units per (sequence, KV head): 1, or Gq when each head is routed alone
   float scale;
 };
 
@@ -178,7 +180,9 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
   static_assert(!F8 || M::EPL == 8, "fp8 planes feed the bf16 matrix instruction");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, grp = lane >> 4;
-  const int u = blockIdx.y, bi = u / a.v.Hkv, g = u % a.v.Hkv;
+  // u: routing unit (frontier, scores, partials); up: its (sequence, KV head) unit (planes)
+  const int u = blockIdx.y, up = u / a.hr, h0 = (u - up * a.hr) * a.G;
+  const int Hkv = a.v.Hkv / a.hr, bi = up / Hkv, g = up % Hkv;
   const int G = a.G;
   const int nF = frontier_size(a.v, u);
   // Super-tiles are dealt to the workgroups in turn: at any moment the unit's workgroups
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
 
   typename M::frag qf[NK];
   {
-    const T* qp = (const T*)a.q + ((int64_t)bi * a.Hq + (int64_t)g * G + row) * D;
+    const T* qp = (const T*)a.q + ((int64_t)bi * a.Hq + (int64_t)g * a.Gq + h0 + row) * D;
 #pragma unroll
     for (int s = 0; s < NK; ++s) {
       const int k0 = F8 ? grp * (D / 4) + s * 8 : s * M::KPER + grp * M::EPL;
@@ -197,10 +201,10 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
     }
   }
   const int32_t* par = a.v.parent ? a.v.parent + (int64_t)u * a.v.cap_parent : nullptr;
-  const T* mb = (const T*)a.m + (int64_t)u * a.capl * R * D;
-  const uint8_t* m8 = (const uint8_t*)a.m + (int64_t)u * a.capl * R * D;
-  const float* bb = a.b + (int64_t)u * a.capl * R;
-  const float* sb = F8 ? a.ms + (int64_t)u * a.capl * R : nullptr;
+  const T* mb = (const T*)a.m + (int64_t)up * a.capl * R * D;
+  const uint8_t* m8 = (const uint8_t*)a.m + (int64_t)up * a.capl * R * D;
+  const float* bb = a.b + (int64_t)up * a.capl * R;
+  const float* sb = F8 ? a.ms + (int64_t)up * a.capl * R : nullptr;
   const int GS = score_stride(G);
   float* sc = a.scores + (int64_t)u * a.cap1 * GS;
   float runM = -INFINITY, runS = 0.0f;
@@ -1540,6 +1544,12 @@ int cshift_of(int C) {
 
 // Score workgroups per unit at a level: about one 8-node super-tile each at small
 // levels, at most t->WS.
+int zha_score_wgs_units(int RU) {
+  int ws = 2048 / (RU > 0 ? RU : 1);  // two rounds of four workgroups per compute unit in all
+  if (ws > 512) ws = 512;
+  return ws < 1 ? 1 : ws;
+}
+
 int zha_score_wgs(const zha_tree* t, int level) {
   const int per = 8;  // nodes of one super-tile at R = 16
   int64_t w = (t->cap[level] + per - 1) / per;
@@ -1554,7 +1564,9 @@ int64_t zha_sel_cand_entries(int U) { return (int64_t)U * sel_regions(U) * LCAND
 int zha_sel_ctr_words(int U) { return U * (1 + KSMAX); }
 
 hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hipStream_t s) {
-  const int U = t->U, L = t->L;
+  // U: routing units of this route (t->U (sequence, KV head) pairs, or t->U * G (sequence,
+  // query head) pairs for per-head routes); Gr: query heads per routing unit
+  const int U = t->RU, L = t->L, Gr = t->G / t->hr;
   const int Cshift = cshift_of(t->C);
   int32_t* cntF = t->counts;                         // [L+2][U]
   int32_t* cntK = t->counts + (int64_t)(L + 2) * U;  // [L+2][U]
@@ -1567,7 +1579,7 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     v.cap_parent = l < L ? t->cap[l + 1] : 0;
     v.C = t->C;
     v.Cshift = Cshift;
-    v.Hkv = t->desc.n_kv_heads;
+    v.Hkv = t->desc.n_kv_heads * t->hr;  // routing units per sequence
     v.nodes = t->geo + (int64_t)l * t->desc.batch;
     v.child = t->geo + (int64_t)(l - 1) * t->desc.batch;
     int32_t* next_nF = l > 1 ? cntF + (int64_t)(l - 1) * U : nullptr;
@@ -1584,7 +1596,9 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     sa.part = t->spart;
     sa.W = zha_score_wgs(t, l);
     sa.Hq = t->desc.n_q_heads;
-    sa.G = t->G;
+    sa.G = Gr;
+    sa.Gq = t->G;
+    sa.hr = t->hr;
     sa.scale = scale;
     zha_time_begin(t, s, ZHA_K_SCORE, l);
     if (t->f8)
@@ -1610,7 +1624,7 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
       sm.nF_out = cntF + (int64_t)l * U;
       sm.kept_count = cntK + (int64_t)l * U;
       sm.next_nF = next_nF;
-      sm.G = t->G;
+      sm.G = Gr;
       sm.p = p;
       sm.keep_all = keep_all ? 1 : 0;
       zha_time_begin(t, s, ZHA_K_SELECT, l);
@@ -1632,7 +1646,7 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
       ma.fh_cnt = t->fh_cnt;
       ma.fh_mass = (u64*)t->fh_mass;
       ma.fh_edge = (u64*)t->fh_edge;
-      ma.G = t->G;
+      ma.G = Gr;
       int64_t wm = (t->cap[l] + 1023) / 1024;
       ma.WM = (int)(wm > 256 ? 256 : (wm < 1 ? 1 : wm));
       zha_time_begin(t, s, ZHA_K_MASS, l);

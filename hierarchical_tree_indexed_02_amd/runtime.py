@@ -20,14 +20,17 @@ class Tree:
     """One attention layer's summary tree (library-owned device memory)."""
 
     def __init__(self, batch, n_kv_heads, n_q_heads, head_dim, chunk, levels, n_refs, max_tokens,
-                 dtype=torch.bfloat16, summary="native"):
+                 dtype=torch.bfloat16, summary="native", per_head_routes=False):
         """summary: "native" (m stored in dtype) or "fp8" (e4m3 codes with a power-of-two
-        scale per node and reference; dtype bf16 only)."""
+        scale per node and reference; dtype bf16 only).  per_head_routes: the tree also serves
+        routes that give every query head its own kept set (route(..., mode="per_head"))."""
         if summary not in ("native", "fp8"):
             raise ValueError(f"unsupported summary storage {summary!r}")
         self.desc = zha.zha_tree_desc(batch, n_kv_heads, n_q_heads, head_dim, chunk, levels, n_refs, max_tokens,
                                       zdtype(dtype),
-                                      zha.ZHA_SUMMARY_FP8 if summary == "fp8" else zha.ZHA_SUMMARY_NATIVE)
+                                      zha.ZHA_SUMMARY_FP8 if summary == "fp8" else zha.ZHA_SUMMARY_NATIVE,
+                                      1 if per_head_routes else 0)
+        self.RU = batch * n_kv_heads  # routing units of the last route
         self.dtype = dtype
         self.summary = summary
         self.B, self.Hkv, self.Hq, self.d = batch, n_kv_heads, n_q_heads, head_dim
@@ -57,8 +60,17 @@ class Tree:
     def append(self, K, new_seq_lens, stream=None):
         zha.zha_append(self.h, K, new_seq_lens, stream)
 
-    def route(self, q, p, scale=1.0, stream=None):
-        self.kept = zha.zha_route(self.h, q, p, scale, stream)
+    def route(self, q, p, scale=1.0, stream=None, mode="group"):
+        """mode "group": one kept set per (sequence, KV head); "per_head": one per (sequence,
+        query head), each head routed alone.  Routing units are numbered with the head fastest."""
+        if mode == "group":
+            self.kept = zha.zha_route(self.h, q, p, scale, stream)
+            self.RU = self.U
+        elif mode == "per_head":
+            self.kept = zha.zha_route_ex(self.h, q, p, scale, zha.ZHA_ROUTE_PER_HEAD, stream)
+            self.RU = self.U * self.G
+        else:
+            raise ValueError(f"unknown routing mode {mode!r}")
         return self.kept
 
     def attend(self, q, K, V, scale=1.0, out=None, lse=None, stream=None):
@@ -88,11 +100,12 @@ class Tree:
         return sc
 
     def route_level(self, level: int, device="cuda"):
-        """(frontier counts [U], kept counts [U], kept ids [U][cap]) of the last route."""
+        """(frontier counts [RU], kept counts [RU], kept ids [RU][cap]) of the last route, per
+        routing unit (RU = U after a group route, U * G after a per-head route)."""
         cap = self.capacity(level)
-        nf = torch.empty(self.U, dtype=torch.int32, device=device)
-        nk = torch.empty(self.U, dtype=torch.int32, device=device)
-        ids = torch.empty((self.U, cap), dtype=torch.int32, device=device)
+        nf = torch.empty(self.RU, dtype=torch.int32, device=device)
+        nk = torch.empty(self.RU, dtype=torch.int32, device=device)
+        ids = torch.empty((self.RU, cap), dtype=torch.int32, device=device)
         zha.zha_route_copy_level(self.h, level, nf, nk, ids)
         return nf, nk, ids
 

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libzha.so")
 ZHA_OK, ZHA_ERR_INVALID, ZHA_ERR_CAPACITY, ZHA_ERR_NOMEM, ZHA_ERR_UNSUPPORTED, ZHA_ERR_HIP = range(6)
 ZHA_F32, ZHA_BF16 = 0, 1
 ZHA_SUMMARY_NATIVE, ZHA_SUMMARY_FP8 = 0, 1
+ZHA_ROUTE_GROUP, ZHA_ROUTE_PER_HEAD = 0, 1
 ZHA_K_BUILD, ZHA_K_APPEND, ZHA_K_SCORE, ZHA_K_SELECT, ZHA_K_ATTEND, ZHA_K_MERGE, ZHA_K_MASS, ZHA_K_COMPACT = range(1, 9)
 KERNEL_NAMES = {1: "build", 2: "append", 3: "score", 4: "select", 5: "attend", 6: "merge", 7: "mass", 8: "compact"}
 
@@ -25,7 +26,7 @@ KERNEL_NAMES = {1: "build", 2: "append", 3: "score", 4: "select", 5: "attend", 6
 class zha_tree_desc(Structure):
     _fields_ = [("batch", c_int32), ("n_kv_heads", c_int32), ("n_q_heads", c_int32), ("head_dim", c_int32),
                 ("chunk", c_int32), ("levels", c_int32), ("n_refs", c_int32), ("max_tokens", c_int64),
-                ("dtype", c_int), ("summary", c_int)]
+                ("dtype", c_int), ("summary", c_int), ("per_head_routes", c_int32)]
 
 
 class zha_kept(Structure):
@@ -66,6 +67,7 @@ def load():
             "zha_build": (st, [vp, vp, vp, _i32p, vp]),
             "zha_append": (st, [vp, vp, _i32p, vp]),
             "zha_route": (st, [vp, vp, c_float, c_float, POINTER(zha_kept), vp]),
+            "zha_route_ex": (st, [vp, vp, c_float, c_float, c_int, POINTER(zha_kept), vp]),
             "zha_attend": (st, [vp, vp, vp, vp, POINTER(zha_kept), c_float, vp, vp, vp]),
             "zha_dense_decode": (st, [vp, vp, vp, _i32p, c_int32, c_int32, c_int32, c_int32, c_int64, c_int,
                                       c_float, vp, vp, vp, c_size_t, vp]),
@@ -148,6 +150,13 @@ def zha_append(tree: int, K, new_seq_lens, stream=None) -> None:
 def zha_route(tree: int, q, p: float, scale: float, stream=None) -> zha_kept:
     kept = zha_kept()
     _check(load().zha_route(tree, _ptr(q), float(p), float(scale), ctypes.byref(kept), _stream(stream)), "zha_route")
+    return kept
+
+
+def zha_route_ex(tree: int, q, p: float, scale: float, mode: int, stream=None) -> zha_kept:
+    kept = zha_kept()
+    _check(load().zha_route_ex(tree, _ptr(q), float(p), float(scale), int(mode), ctypes.byref(kept), _stream(stream)),
+           "zha_route_ex")
     return kept
 
 

@@ -92,7 +92,20 @@ typedef struct {
     int64_t max_tokens;   /* capacity per sequence (the K/V token stride) */
     zha_dtype dtype;      /* storage dtype of q, K and V, and of the planes' m when native */
     zha_summary summary;  /* storage of the planes' m (ZHA_SUMMARY_FP8 needs dtype bf16) */
+    int32_t per_head_routes; /* nonzero: the tree also serves ZHA_ROUTE_PER_HEAD routes (its
+                                routing workspace is sized for B*Hq routing units) */
 } zha_tree_desc;
+
+/* How the G query heads of one KV head are routed.  ZHA_ROUTE_GROUP: one kept
+ * set per (sequence, KV head), from the mean over the G heads of each head's
+ * frontier-normalised mass (the reading taken for grouped-query attention).
+ * ZHA_ROUTE_PER_HEAD: every query head is routed alone, as the pages describe
+ * routing for a single query ([wqu] "How does top-p routing pick tokens?"): one
+ * kept set per (sequence, query head), and attention of each head over its own
+ * set.  A "routing unit" is a (sequence, KV head) in group mode and a
+ * (sequence, query head) in per-head mode, numbered (b, KV head, head in group)
+ * with the head fastest. */
+typedef enum { ZHA_ROUTE_GROUP = 0, ZHA_ROUTE_PER_HEAD = 1 } zha_route_mode;
 
 /* Kept leaf chunks of the last zha_route on a tree: a view into the tree's
  * workspace, valid until the next zha_route on the same tree.
@@ -154,6 +167,16 @@ ZHA_API zha_status zha_append(zha_tree_t tree, const void* K, const int32_t* new
 ZHA_API zha_status zha_route(zha_tree_t tree, const void* q, float p, float scale,
                      zha_kept* kept, hipStream_t stream);
 
+/* zha_route with a routing mode.  ZHA_ROUTE_GROUP is zha_route.  With
+ * ZHA_ROUTE_PER_HEAD (tree created with per_head_routes) every routing unit
+ * is one (sequence, query head): its frontier, softmax, top-p cut and kept
+ * set are that head's alone; *kept then views [B*Hq] counts and [B*Hq][cap]
+ * ids, and zha_attend gives every head its own attention set.
+ * Errors: as zha_route, and ZHA_ERR_INVALID for a per-head route on a tree
+ * created without per_head_routes or for an unknown mode. */
+ZHA_API zha_status zha_route_ex(zha_tree_t tree, const void* q, float p, float scale, zha_route_mode mode,
+                        zha_kept* kept, hipStream_t stream);
+
 /* Exact attention of each query head over S = {token 0} U (tokens of the
  * kept chunks) U [Nc, N), S a set ([wqu] "How does top-p routing pick
  * tokens?": the first token is always kept; the trailing partial chunk is not
@@ -195,10 +218,11 @@ ZHA_API zha_status zha_tree_copy_level(zha_tree_t tree, int32_t level, void* m_o
  * Errors: ZHA_ERR_INVALID (null pointer, level out of range, native tree). */
 ZHA_API zha_status zha_tree_copy_scales(zha_tree_t tree, int32_t level, float* scale_out, hipStream_t stream);
 
-/* Copies the last route's result at `level`: frontier_counts [B*Hkv],
- * kept_counts [B*Hkv], kept_ids [B*Hkv][cap] (ascending).  The frontier of
- * level L is every level-L node; the frontier of level l < L is the children
- * of the kept set of level l + 1.  Device buffers owned by the caller. */
+/* Copies the last route's result at `level`, per routing unit (RU = B*Hkv after
+ * a group route, B*Hq after a per-head route): frontier_counts [RU],
+ * kept_counts [RU], kept_ids [RU][cap] (ascending).  The frontier of level L is
+ * every level-L node; the frontier of level l < L is the children of the kept
+ * set of level l + 1.  Device buffers owned by the caller. */
 ZHA_API zha_status zha_route_copy_level(zha_tree_t tree, int32_t level, int32_t* frontier_counts,
                                 int32_t* kept_counts, int32_t* kept_ids, hipStream_t stream);
 

@@ -76,10 +76,10 @@ class Case:
         self.Kd[b, g, start:start + n] = torch.from_numpy(np.ascontiguousarray(Krows)).to(self.Kd.device, dt)
         self.Vd[b, g, start:start + n] = torch.from_numpy(np.ascontiguousarray(Vrows)).to(self.Vd.device, dt)
 
-    def tree(self, levels=None, chunk=None, refs=None, summary="native"):
+    def tree(self, levels=None, chunk=None, refs=None, summary="native", per_head_routes=False):
         cfg = self.cfg
         t = Tree(self.B, self.Hkv, self.Hq, self.d, chunk or cfg.chunk, levels or cfg.levels, cfg.n_refs, self.T,
-                 TORCH_DT[cfg.dtype], summary=summary)
+                 TORCH_DT[cfg.dtype], summary=summary, per_head_routes=per_head_routes)
         t.build(self.Kd, self.refs_d if refs is None else refs, self.lens)
         return t
 
@@ -185,8 +185,20 @@ def ambiguous(F, w, order, csum, kstar, p):
     return amb
 
 
-def check_route(case: Case, tree: Tree, t: int, p: float, scale=1.0, units=None):
-    """Teacher-forced route parity at every level.  Returns per-level stats."""
+def routing_units(case: Case, mode: str):
+    """(routing unit, sequence, KV head, first query head in the group, heads) of a route:
+    one unit of G heads per (sequence, KV head), or one unit per query head, head fastest."""
+    for b in range(case.B):
+        for g in range(case.Hkv):
+            if mode == "group":
+                yield b * case.Hkv + g, b, g, 0, case.G
+            else:
+                for h in range(case.G):
+                    yield (b * case.Hkv + g) * case.G + h, b, g, h, 1
+
+
+def check_route(case: Case, tree: Tree, t: int, p: float, scale=1.0, units=None, mode="group"):
+    """Teacher-forced route parity at every level, per routing unit.  Returns per-level stats."""
     stats = {}
     levels = {}
     for l in range(tree.L, 0, -1):
@@ -197,73 +209,72 @@ def check_route(case: Case, tree: Tree, t: int, p: float, scale=1.0, units=None)
         m_d, b_d = tree.level(l)
         planes[l] = (m_d, b_d)
     n_amb = 0
-    for b in range(case.B):
+    for v, b, g, h0, nh in routing_units(case, mode):
         N = case.lens[b]
-        for g in range(case.Hkv):
-            u = b * case.Hkv + g
-            if units is not None and u not in units:
+        pu = b * case.Hkv + g  # the (sequence, KV head) unit whose tree is routed
+        if units is not None and pu not in units:
+            continue
+        q = case.unit_q(t, b, g, scale)[h0:h0 + nh]
+        u = v  # routing unit: frontier, kept ids
+        for l in range(tree.L, 0, -1):
+            nf, nk, ids = levels[l]
+            n_l = oracle.level_nodes(N, tree.C, l)
+            if l == tree.L:
+                F = np.arange(n_l, dtype=np.int32)
+            else:
+                nfp, nkp, idsp = levels[l + 1]
+                parent = idsp[u, :nkp[u]].cpu().numpy()
+                F = oracle.expand(parent, tree.C, n_l)
+            assert nf[u] == len(F), f"unit {u} level {l}: frontier {nf[u]} != {len(F)}"
+            gpu = ids[u, :nk[u]].cpu().numpy()
+            assert np.all(np.diff(gpu) > 0), f"unit {u} level {l}: kept ids not ascending"
+            if len(F) == 0:
+                assert nk[u] == 0
                 continue
-            q = case.unit_q(t, b, g, scale)
-            for l in range(tree.L, 0, -1):
-                nf, nk, ids = levels[l]
-                n_l = oracle.level_nodes(N, tree.C, l)
-                if l == tree.L:
-                    F = np.arange(n_l, dtype=np.int32)
-                else:
-                    nfp, nkp, idsp = levels[l + 1]
-                    parent = idsp[u, :nkp[u]].cpu().numpy()
-                    F = oracle.expand(parent, tree.C, n_l)
-                assert nf[u] == len(F), f"unit {u} level {l}: frontier {nf[u]} != {len(F)}"
-                gpu = ids[u, :nk[u]].cpu().numpy()
-                assert np.all(np.diff(gpu) > 0), f"unit {u} level {l}: kept ids not ascending"
-                if len(F) == 0:
-                    assert nk[u] == 0
-                    continue
-                m_d, b_d = planes[l]
-                Fi = torch.from_numpy(F.astype(np.int64)).to(m_d.device)
-                mF = m_d[u, Fi].float().cpu().numpy().astype(np.float64)
-                bF = b_d[u, Fi].cpu().numpy().astype(np.float64)
-                kept_pos, w, order, csum = oracle.select(mF, bF, q, np.arange(len(F), dtype=np.int32), p)
-                want = set(F[kept_pos].tolist())
-                got = set(gpu.tolist())
-                diff = want ^ got
-                if diff:
-                    amb = ambiguous(F, w, order, csum, len(kept_pos), p)
-                    bad = diff - amb
-                    assert not bad, (f"unit {u} level {l}: {len(bad)} non-ambiguous differences, e.g. "
-                                     f"{sorted(bad)[:5]} (|F|={len(F)}, oracle k={len(want)}, gpu k={len(got)})")
-                    n_amb += len(diff)
-                s = stats.setdefault(l, [0, 0])
-                s[0] += len(F)
-                s[1] += len(got)
+            m_d, b_d = planes[l]
+            Fi = torch.from_numpy(F.astype(np.int64)).to(m_d.device)
+            mF = m_d[pu, Fi].float().cpu().numpy().astype(np.float64)
+            bF = b_d[pu, Fi].cpu().numpy().astype(np.float64)
+            kept_pos, w, order, csum = oracle.select(mF, bF, q, np.arange(len(F), dtype=np.int32), p)
+            want = set(F[kept_pos].tolist())
+            got = set(gpu.tolist())
+            diff = want ^ got
+            if diff:
+                amb = ambiguous(F, w, order, csum, len(kept_pos), p)
+                bad = diff - amb
+                assert not bad, (f"unit {u} level {l}: {len(bad)} non-ambiguous differences, e.g. "
+                                 f"{sorted(bad)[:5]} (|F|={len(F)}, oracle k={len(want)}, gpu k={len(got)})")
+                n_amb += len(diff)
+            s = stats.setdefault(l, [0, 0])
+            s[0] += len(F)
+            s[1] += len(got)
     return dict(levels={l: tuple(v) for l, v in stats.items()}, ambiguous=n_amb)
 
 
 # ----------------------------------------------------------------------------- attend
 
-def check_attend(case: Case, tree: Tree, out, lse, t: int, scale=1.0, units=None):
+def check_attend(case: Case, tree: Tree, out, lse, t: int, scale=1.0, units=None, mode="group"):
+    """The oracle's attention over each routing unit's GPU kept set, for that unit's heads."""
     _, nk, ids = tree.route_level(1)
     nk = nk.cpu().numpy()
     out = out.cpu().numpy()
     lse = lse.cpu().numpy()
     worst_o, worst_l, kappa = 0.0, 0.0, []
-    for b in range(case.B):
+    for v, b, g, h0, nh in routing_units(case, mode):
         N = case.lens[b]
-        for g in range(case.Hkv):
-            u = b * case.Hkv + g
-            if units is not None and u not in units:
-                continue
-            kept = ids[u, :nk[u]].cpu().numpy()
-            S = oracle.attend_set(N, tree.C, kept)
-            Ku, Vu = case.unit_kv(b, g)
-            o_o, l_o = oracle.attend(case.unit_q(t, b, g, scale), Ku, Vu, S)
-            hs = slice(g * case.G, (g + 1) * case.G)
-            eo = float(np.max(np.abs(out[b, hs] - o_o)))
-            el = float(np.max(np.abs(lse[b, hs] - l_o)))
-            assert eo <= OUT_TOL, f"unit {u}: out err {eo:.3e}"
-            assert el <= LSE_TOL, f"unit {u}: lse err {el:.3e}"
-            worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
-            kappa.append(len(S) / N)
+        if units is not None and b * case.Hkv + g not in units:
+            continue
+        kept = ids[v, :nk[v]].cpu().numpy()
+        S = oracle.attend_set(N, tree.C, kept)
+        Ku, Vu = case.unit_kv(b, g)
+        o_o, l_o = oracle.attend(case.unit_q(t, b, g, scale)[h0:h0 + nh], Ku, Vu, S)
+        hs = slice(g * case.G + h0, g * case.G + h0 + nh)
+        eo = float(np.max(np.abs(out[b, hs] - o_o)))
+        el = float(np.max(np.abs(lse[b, hs] - l_o)))
+        assert eo <= OUT_TOL, f"routing unit {v}: out err {eo:.3e}"
+        assert el <= LSE_TOL, f"routing unit {v}: lse err {el:.3e}"
+        worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+        kappa.append(len(S) / N)
     return dict(worst_out=worst_o, worst_lse=worst_l, kappa=float(np.mean(kappa)) if kappa else 0.0)
 
 
@@ -287,15 +298,15 @@ def check_dense(case: Case, t: int, scale=1.0, units=None):
     return worst
 
 
-def route_attend(case: Case, tree: Tree, t: int, p: float, scale=1.0):
-    tree.route(case.qd[t], p, scale)
+def route_attend(case: Case, tree: Tree, t: int, p: float, scale=1.0, mode="group"):
+    tree.route(case.qd[t], p, scale, mode=mode)
     out, lse = tree.attend(case.qd[t], case.Kd, case.Vd, scale)
     torch.cuda.synchronize()
     return out, lse
 
 
-def full_check(case: Case, tree: Tree, t: int, p: float, scale=1.0, units=None):
-    out, lse = route_attend(case, tree, t, p, scale)
-    r = check_route(case, tree, t, p, scale, units)
-    a = check_attend(case, tree, out, lse, t, scale, units)
+def full_check(case: Case, tree: Tree, t: int, p: float, scale=1.0, units=None, mode="group"):
+    out, lse = route_attend(case, tree, t, p, scale, mode)
+    r = check_route(case, tree, t, p, scale, units, mode)
+    a = check_attend(case, tree, out, lse, t, scale, units, mode)
     return r, a

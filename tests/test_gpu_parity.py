@@ -10,6 +10,7 @@ import torch
 
 import oracle
 import zha_inputs as zi
+from hierarchical_tree_indexed_02_amd import zha
 from parity import Case, check_attend, check_build, check_dense, check_route, full_check, route_attend
 
 pytestmark = pytest.mark.gpu
@@ -153,6 +154,68 @@ def test_fp8_rounding_exact():
                           f"gpu {got_m[tuple(bad[0])]!r} oracle {want_m[tuple(bad[0])]!r}"
     assert np.array_equal(got_s, want_s), "row scales differ"
     say(f" {got_m.size} stored values equal the oracle's rounding; scales {sorted(set(got_s.ravel().tolist()))}")
+
+
+# --------------------------------------------------------------------------- per-query-head routing
+
+PER_HEAD_VARIANTS = [
+    ("per-head bf16 d128 C4 L3 R16 G8 B2", dict(batch=2, n_tokens=5000, chunk=4, levels=3, n_refs=16), [5000, 3333]),
+    ("per-head bf16 d64 C4 L2 R4 G4", dict(batch=1, n_tokens=2051, head_dim=64, n_q_heads=16, n_kv_heads=4, chunk=4,
+                                            levels=2, n_refs=4), [2051]),
+    ("per-head f32 d128 C3 L3 R8 G2", dict(batch=1, n_tokens=1000, n_q_heads=8, n_kv_heads=4, chunk=3, levels=3,
+                                           n_refs=8, dtype="f32"), [1000]),
+    ("per-head bf16 d128 C4 L2 R16 G8 large frontier", dict(batch=1, n_tokens=65539, n_q_heads=16, n_kv_heads=2,
+                                                            chunk=4, levels=2, n_refs=16), [65539]),
+]
+
+
+@pytest.mark.parametrize("label,kw,lens", PER_HEAD_VARIANTS, ids=[v[0] for v in PER_HEAD_VARIANTS])
+def test_per_head_routing(label, kw, lens):
+    """Every query head routed alone (its own frontier, softmax, cut and attention set),
+    teacher-forced per (sequence, query head) against the oracle with that head's query."""
+    cfg = small(**kw, n_queries=4, needles_per_unit=4)
+    say(f"case {label}: lens={lens}")
+    case = Case(cfg, lens=lens, n_queries=2)
+    tree = case.tree(per_head_routes=True)
+    for t in range(2):
+        for p in (0.5, 0.9):
+            r, a = full_check(case, tree, t, p, mode="per_head")
+            say(f" t={t} p={p}", r, a)
+    # group routes on the same tree are unchanged by the per-head ones
+    out0, lse0 = route_attend(case, tree, 0, 0.9)
+    _, nk0, ids0 = tree.route_level(1)
+    route_attend(case, tree, 1, 0.9, mode="per_head")
+    out1, lse1 = route_attend(case, tree, 0, 0.9)
+    _, nk1, ids1 = tree.route_level(1)
+    assert torch.equal(nk0, nk1) and torch.equal(ids0, ids1) and torch.equal(out0, out1) and torch.equal(lse0, lse1)
+
+
+def test_per_head_equals_group_at_one_head():
+    """With one query head per KV head the two modes are the same computation: kept sets and
+    outputs are bit-identical."""
+    cfg = small(batch=2, n_tokens=9000, n_q_heads=4, n_kv_heads=4, chunk=4, levels=4, n_refs=16, n_queries=2,
+                needles_per_unit=4)
+    say("case per-head == group at G = 1: B=2 N=9000 Hq=Hkv=4 C=4 L=4 R=16")
+    case = Case(cfg, lens=[9000, 7001], n_queries=2)
+    tree = case.tree(per_head_routes=True)
+    for p in (0.5, 0.95):
+        og, lg = route_attend(case, tree, 0, p)
+        kg = [tree.route_level(l) for l in range(1, tree.L + 1)]
+        oh, lh = route_attend(case, tree, 0, p, mode="per_head")
+        kh = [tree.route_level(l) for l in range(1, tree.L + 1)]
+        for (a1, b1, c1), (a2, b2, c2) in zip(kg, kh):
+            assert torch.equal(a1, a2) and torch.equal(b1, b2) and torch.equal(c1, c2)
+        assert torch.equal(og, oh) and torch.equal(lg, lh)
+
+
+def test_per_head_needs_the_workspace():
+    cfg = small(batch=1, n_tokens=1000, n_q_heads=8, n_kv_heads=2, chunk=4, levels=2, n_refs=4, n_queries=2,
+                needles_per_unit=2)
+    say("case per-head route on a tree without the per-head workspace")
+    case = Case(cfg, lens=[1000], n_queries=2)
+    tree = case.tree()
+    with pytest.raises(zha.ZhaError):
+        tree.route(case.qd[0], 0.9, mode="per_head")
 
 
 # --------------------------------------------------------------------------- large-level selection paths
