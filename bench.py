@@ -47,6 +47,9 @@ def parse():
                     help="skip the extra pass with fp8 summaries (reported beside the headline)")
     ap.add_argument("--no-per-head", action="store_true",
                     help="skip the extra pass that routes every query head alone (reported beside the headline)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the workload's inputs under other tree geometries (C, L, R) and p, and fit a "
+                         "step-time model (bytes at the measured bandwidths + a fixed cost per routing level)")
     return ap.parse_args()
 
 
@@ -81,6 +84,54 @@ def committed_traffic(workload: str):
     if not m_sha or not m_tr or m_sha.group(1) != score_kernel_sha():
         return None
     return float(m_tr.group(1))
+
+
+# Tree geometries (chunk C, levels L, references R) over the same 256K-token inputs: C^L = 4096
+# tokens per top node except where noted, and the flat C = 256 tree.
+SWEEP = [(4, 6, 16, 0.95), (4, 6, 4, 0.95), (4, 6, 1, 0.95), (4, 6, 16, 0.7), (8, 4, 16, 0.95), (8, 4, 4, 0.95),
+         (16, 3, 16, 0.95), (16, 3, 4, 0.95), (64, 2, 16, 0.95), (4, 5, 16, 0.95), (256, 1, 16, 0.95),
+         (256, 1, 4, 0.95), (256, 1, 16, 0.7)]
+
+
+def geometry_sweep(measure, cfg, zi, torch, np, dev, N, B, Hkv, d, es, log):
+    """Times route + attend under each geometry of SWEEP and fits
+        t_step = route_bytes / BW_route + attend_bytes / BW_attend + n_small * c_small + n_large * c_large + c0
+    by least squares (n_small / n_large: routing levels of at most / more than 8192 nodes
+    per unit); returns one record per geometry with the fitted prediction."""
+    rows = []
+    for C, L, R, p in SWEEP:
+        if C ** L > N:
+            continue
+        g = zi.get_config(cfg.name, chunk=C, levels=L, n_refs=R)
+        refs = torch.from_numpy(zi.refs(g)).to(dev)
+        log(f"-- geometry C={C} L={L} R={R} p={p}")
+        r = measure("native", "group", C=C, L=L, R=R, refs=refs, p=p)
+        caps = [-(-((N // C) * C) // C ** l) for l in range(1, L + 1)]
+        n_small = sum(1 for c in caps if c <= 8192)
+        kern = r["kernels"]
+        route_us = sum(v["avg_us"] for k, v in kern.items() if k.split("_l")[0] in ("score", "select", "mass", "compact"))
+        att_us = kern.get("attend", {}).get("avg_us", 0.0)
+        S_node = R * (d * es + 4)
+        route_bytes = sum(r["fr_tot"].values()) * S_node / r["nsteps"]
+        rows.append(dict(C=C, L=L, R=R, p=p, us_per_step=round(r["ms_step"] * 1e3, 2),
+                         step_bytes=round(r["step_bytes"]), route_bytes=round(route_bytes),
+                         attend_bytes=round(r["step_bytes"] - route_bytes), kappa=round(r["kappa"], 4),
+                         route_us=round(route_us, 1), attend_us=round(att_us, 1), small_levels=n_small,
+                         large_levels=L - n_small, tree_bytes=r["tree_bytes"]))
+    X = np.array([[x["route_bytes"] / 1e9, x["attend_bytes"] / 1e9, x["small_levels"], x["large_levels"], 1.0]
+                  for x in rows])
+    y = np.array([x["us_per_step"] for x in rows])
+    coef, *_ = np.linalg.lstsq(X, y, rcond=None)
+    for x, pred in zip(rows, X @ coef):
+        x["model_us"] = round(float(pred), 1)
+    fit = dict(us_per_GB_route=round(float(coef[0]), 2), us_per_GB_attend=round(float(coef[1]), 2),
+               us_per_small_level=round(float(coef[2]), 2), us_per_large_level=round(float(coef[3]), 2),
+               us_fixed=round(float(coef[4]), 2))
+    log("geometry sweep fit: " + ", ".join(f"{k} {v}" for k, v in fit.items()))
+    for x in rows:
+        log(f"  C={x['C']:3d} L={x['L']} R={x['R']:2d} p={x['p']}: {x['us_per_step']:8.1f} us (model {x['model_us']:8.1f}), "
+            f"kappa {x['kappa']:.3f}, route {x['route_bytes'] / 1e6:7.1f} MB, attend {x['attend_bytes'] / 1e6:6.1f} MB")
+    return dict(fit=fit, rows=rows)
 
 
 def main():
@@ -134,9 +185,10 @@ def main():
     outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(args.layers)]
     lses = [torch.empty((B, Hq), dtype=torch.float32, device=dev) for _ in range(args.layers)]
 
-    def measure(summary, mode="group"):
-        """Builds one tree per layer replica with the given m storage, times the stage
-        breakdown and the K-step region, and replays the routes for the byte counts."""
+    def measure(summary, mode="group", C=C, L=L, R=R, refs=refs, p=p):
+        """Builds one tree per layer replica with the given m storage (and geometry C, L, R),
+        times the stage breakdown and the K-step region, and replays the routes for the
+        byte counts."""
         lens = [N] * B
         layer_lens = [[N] * B for _ in range(args.layers)]
         trees = []
@@ -318,6 +370,9 @@ def main():
                    kernels={k: round(v["avg_us"], 2) for k, v in r8["kernels"].items()})
         if growing:
             fp8["p_sweep"] = {str(x): round(r8["seg_us"].get("append", 0.0) + r8["seg_us"][x], 2) for x in p_sweep}
+    sweep = None
+    if args.sweep and not growing:
+        sweep = geometry_sweep(measure, cfg, zi, torch, np, dev, N, B, Hkv, d, es, log)
     per_head = None
     if not args.no_per_head and args.summary == "native":
         log("-- the same workload, every query head routed alone")
@@ -402,6 +457,8 @@ def main():
         result["fp8_summaries"] = fp8
     if per_head is not None:
         result["per_head_routes"] = per_head
+    if sweep is not None:
+        result["geometry_sweep"] = sweep
     if growing:
         result["append_us"] = round(seg_us.get("append", 0.0), 2)
         result["p_sweep"] = {str(x): round(seg_us.get("append", 0.0) + seg_us[x], 2) for x in p_sweep}
