@@ -397,7 +397,6 @@ zha_status zha_timing_enable(zha_tree_t t, int32_t kernel_mask, int32_t level_ma
   t->timing_kernels = kernel_mask;
   t->timing_levels = level_mask;
   t->timing_open = false;
-  t->n_rec = 0;
   return ZHA_OK;
 }
 

@@ -1036,7 +1036,9 @@ __global__ __launch_bounds__(256) void zha_mass_kernel(MassArgs a) {
   __shared__ u64 s_edge[2][4];
   const int u = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nF = frontier_size(a.v, u);
-  const int per = (nF + a.WM - 1) / a.WM;
+  // at least 1024 positions per workgroup (one batch of loads per thread): a workgroup's
+  // cost is mostly its histogram flush, so a small frontier uses few workgroups
+  const int per = max((nF + a.WM - 1) / a.WM, 256 * MASS_BATCH);
   const int start = blockIdx.x * per, end = min(nF, start + per);
   if (start >= end) return;
   const int G = a.G;
