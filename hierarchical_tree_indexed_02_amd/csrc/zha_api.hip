@@ -7,6 +7,7 @@
 #include <new>
 
 #include <algorithm>
+#include <vector>
 
 #include "zha_internal.h"
 
@@ -216,7 +217,7 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   ok = ok && dalloc(t, &t->sel_cand, (size_t)cand_n * 2 * sizeof(uint32_t));
   ok = ok && dalloc(t, &t->sel_ctr, (size_t)ctr_n * sizeof(uint32_t));
   ok = ok && dalloc(t, &t->lb_status, (size_t)RUmax * nchunk * sizeof(unsigned long long));
-  ok = ok && dalloc(t, &t->lb_epoch, 2 * sizeof(uint32_t));
+  ok = ok && dalloc(t, &t->lb_epoch, (size_t)RUmax * 2 * sizeof(uint32_t));
   ok = ok && dalloc(t, &t->lb_error, sizeof(int32_t));
   if (ok) {  // counters and histograms start at zero and are left at zero by the kernels
     ok = hipMemset(t->fh_cnt, 0, (size_t)RUmax * nb * sizeof(uint32_t)) == hipSuccess &&
@@ -226,8 +227,10 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
          hipMemset(t->geo, 0, (size_t)(L + 2) * desc->batch * sizeof(int32_t)) == hipSuccess &&
          hipMemset(t->lb_status, 0, (size_t)RUmax * nchunk * sizeof(unsigned long long)) == hipSuccess &&
          hipMemset(t->lb_error, 0, sizeof(int32_t)) == hipSuccess;
-    const uint32_t ep[2] = {1u, 0u};  // status words of epoch 0 (all-zero memory) never match
-    ok = ok && hipMemcpy(t->lb_epoch, ep, sizeof(ep), hipMemcpyHostToDevice) == hipSuccess;
+    // every unit's epoch starts at 1: status words of epoch 0 (all-zero memory) never match
+    std::vector<uint32_t> ep((size_t)RUmax * 2, 0u);
+    for (int u = 0; u < RUmax; ++u) ep[(size_t)u * 2] = 1u;
+    ok = ok && hipMemcpy(t->lb_epoch, ep.data(), ep.size() * sizeof(uint32_t), hipMemcpyHostToDevice) == hipSuccess;
     ok = ok && hipDeviceSynchronize() == hipSuccess;
   }
   if (!ok) {

@@ -203,7 +203,7 @@ struct zha_tree {
   uint32_t* sel_cand;               // [U][min(32, 256/U)][8192][2] crossing-slice (key, position) pairs per selection workgroup
   uint32_t* sel_ctr;                // [U][1 + 32] selection workgroups arrived (zero between levels), candidates per workgroup
   unsigned long long* lb_status;    // [U][compaction chunks of level 1] look-back words
-  uint32_t* lb_epoch;               // [2] look-back epoch (starts at 1) and finished-workgroup count
+  uint32_t* lb_epoch;               // [RUmax][2] look-back epoch per unit (starts at 1), finished-workgroup count
   int32_t* lb_error;                // [1] set if a look-back wait ever gives up
   float* apart;                     // attention partials: o [U][WA][G][d], then (max, sum) [U][WA][G][2]
   int WS, WA;                       // score and attention workgroups per routing unit, last route's mode

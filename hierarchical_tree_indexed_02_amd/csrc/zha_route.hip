@@ -1365,7 +1365,7 @@ struct CompactArgs {
   int keep_all;           // p >= 1: every position is kept (cut unused)
   u64* status;            // [U][nchunk] look-back words
   int nchunk;
-  uint32_t* epoch;        // [2]: epoch of this launch's status words (starts at 1), finished workgroups
+  uint32_t* epoch;        // [U][2]: epoch of the unit's status words (starts at 1), its finished workgroups
   int32_t* kept;          // [U][capl]
   int64_t capl;
   int32_t* nF_out;
@@ -1383,14 +1383,15 @@ __device__ __forceinline__ u64 lb_word(uint32_t epoch, int inclusive, uint32_t c
 }
 
 __device__ __forceinline__ void compact_epilogue(const CompactArgs& a) {
-  // the last workgroup of the launch advances the epoch: every workgroup read it before finishing
+  // the last workgroup of the unit advances the unit's epoch: every workgroup of the unit
+  // read it before finishing (one counter per unit keeps the atomics on one address few)
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t n = gridDim.x * gridDim.y;
-    if (atomicAdd(&a.epoch[1], 1u) == n - 1) {
-      __hip_atomic_store(&a.epoch[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t e = __hip_atomic_load(&a.epoch[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&a.epoch[0], e + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t* ep = a.epoch + 2 * blockIdx.y;
+    if (atomicAdd(&ep[1], 1u) == gridDim.x - 1) {
+      __hip_atomic_store(&ep[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t e = __hip_atomic_load(&ep[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&ep[0], e + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -1444,7 +1445,7 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
   const int nF = frontier_size(a.v, u);
   const int base = c * CH;
   const int nchild = a.next_nF && base + CH >= nF ? child_nodes(a.v, u) : 0;  // loaded now, used at the end
-  if (tid == 0) s_epoch = __hip_atomic_load(&a.epoch[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) s_epoch = __hip_atomic_load(&a.epoch[2 * u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (base >= nF) {
     compact_epilogue(a);
     return;
