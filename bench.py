@@ -226,6 +226,8 @@ def main():
             else:
                 fn()
 
+        tmask = {}  # growing workloads: kernel timing mask, applied to the headline p's launches only
+
         def step(i, record=False):
             li, t = i % args.layers, i % nq
             tr = trees[li]
@@ -234,10 +236,16 @@ def main():
                     segs.append({})
                 if layer_lens[li][0] < T:
                     layer_lens[li] = [n + 1 for n in layer_lens[li]]
+                    if tmask:  # the append is timed in the breakdown pass only
+                        tr.timing(tmask["kernels"] is None)
                     seg("append", lambda: tr.append(Ks[li], layer_lens[li]), record)
                 for x in p_sweep:
+                    if tmask:
+                        tr.timing(x == p, **tmask)
                     seg(x, lambda x=x: (tr.route(qd[t], x, 1.0, mode=mode),
                                         tr.attend(qd[t], Ks[li], Vs[li], 1.0, out=outs[li], lse=lses[li])), record)
+                if tmask:
+                    tr.timing(False)
                 return
             tr.route(qd[t], p, 1.0, mode=mode)
             tr.attend(qd[t], Ks[li], Vs[li], 1.0, out=outs[li], lse=lses[li])
@@ -250,6 +258,8 @@ def main():
         # a little time, so this pass is not the one whose step time is reported)
         for tr in trees:
             tr.timing(True)
+        if growing:
+            tmask.update(kernels=None, levels=None)
         for i in range(args.steps):
             step(i)
         torch.cuda.synchronize()
@@ -268,6 +278,8 @@ def main():
         # timed region: K steps, with an event pair around the dominant kernel only
         for tr in trees:
             tr.timing(True, kernels=[dom["code"]], levels=[dom["level"]])
+        if growing:
+            tmask.update(kernels=[dom["code"]], levels=[dom["level"]])
         torch.cuda.synchronize()
         ev0.record()
         for i in range(args.steps):
