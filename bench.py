@@ -45,6 +45,8 @@ def parse():
                     help="storage of the planes' m for the headline measurement")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the extra pass with fp8 summaries (reported beside the headline)")
+    ap.add_argument("--block", type=int, default=8,
+                    help="also route and attend blocks of this many queries per sequence (0: skip)")
     ap.add_argument("--no-per-head", action="store_true",
                     help="skip the extra pass that routes every query head alone (reported beside the headline)")
     ap.add_argument("--sweep", action="store_true",
@@ -185,6 +187,86 @@ def main():
     outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(args.layers)]
     lses = [torch.empty((B, Hq), dtype=torch.float32, device=dev) for _ in range(args.layers)]
 
+    def kernel_table(recs):
+        per = {}
+        for k, l, ms in recs:
+            per.setdefault((k, l), []).append(ms)
+        return {f"{zha.KERNEL_NAMES[k]}{'_l' + str(l) if l else ''}": dict(launches=len(v), avg_us=1e3 * sum(v) / len(v),
+                                                                           total_ms=sum(v), code=k, level=l)
+                for (k, l), v in sorted(per.items())}
+
+    def measure_block(Tq, mode="group"):
+        """A block of Tq queries per sequence (the first Tq decode queries; a speculative
+        verification step or a prefill chunk) routed and attended over the tree of the N_b
+        cached tokens, N_b = N - Tq when the block's rows would not fit after N."""
+        Nb = N if N + Tq <= T else N - Tq
+        trees = []
+        for li in range(args.layers):
+            tr = Tree(B, Hkv, Hq, d, C, L, R, T, dt, per_head_routes=mode == "per_head", max_queries=Tq)
+            tr.build(Ks[li], refs, [Nb] * B)
+            trees.append(tr)
+        qb = torch.from_numpy(np.ascontiguousarray(q_all[:Tq].transpose(1, 0, 2, 3))).to(dev, dt)
+        ob = [torch.empty((B, Tq, Hq, d), dtype=torch.float32, device=dev) for _ in range(args.layers)]
+        lb = [torch.empty((B, Tq, Hq), dtype=torch.float32, device=dev) for _ in range(args.layers)]
+
+        def step(i):
+            li = i % args.layers
+            trees[li].route_multi(qb, p, 1.0, mode=mode)
+            trees[li].attend_multi(qb, Ks[li], Vs[li], 1.0, out=ob[li], lse=lb[li])
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        for tr in trees:
+            tr.timing(True)
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        recs = []
+        for tr in trees:
+            recs += tr.timing_read()
+            tr.timing(False)
+        kernels = kernel_table(recs)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(args.steps):
+            step(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        us = 1e3 * ev0.elapsed_time(ev1) / args.steps
+        # algorithmic bytes: replay the block's route once
+        hr = G if mode == "per_head" else 1
+        RU = U * Tq * hr
+        trees[0].route_multi(qb, p, 1.0, mode=mode)
+        torch.cuda.synchronize()
+        S_node = R * (d * es + 4)
+        route_bytes = 0
+        for l in range(1, L + 1):
+            nf, _, _ = trees[0].route_level(l)
+            route_bytes += int(nf.sum()) * S_node
+        _, nk, ids = trees[0].route_level(1)
+        nk1 = nk.cpu().numpy()
+        first = ids[:, 0].cpu().numpy()
+        Nc = (Nb // C) * C
+        tok = 0
+        for u in range(RU):
+            tq = (u // hr // Hkv) % Tq
+            sink = 1 if (Nc > 0 and (nk1[u] == 0 or first[u] != 0)) else 0
+            tok += sink + (Nb + tq + 1 - Nc) + int(nk1[u]) * C
+        attend_bytes = tok * 2 * d * es
+        nbytes = route_bytes + attend_bytes
+        for tr in trees:
+            tr.close()
+        torch.cuda.empty_cache()
+        log(f"block of {Tq} ({mode}): {us:.1f} us ({us / Tq:.1f} us per query), {nbytes / 1e6:.1f} MB "
+            f"({nbytes / (us * 1e-6) / 1e9:.0f} GB/s), kappa {tok / (RU * Nb):.3f}")
+        for k, v in kernels.items():
+            log(f"  {k:12s} {v['launches']:4d} launches  avg {v['avg_us']:8.2f} us")
+        return dict(queries=Tq, cached_tokens=Nb, mode=mode, us_per_block=round(us, 2),
+                    us_per_query=round(us / Tq, 2), block_bytes=round(nbytes),
+                    block_gbs=round(nbytes / (us * 1e-6) / 1e9, 1), kappa=round(tok / (RU * Nb), 4),
+                    kernels={k: round(v["avg_us"], 2) for k, v in kernels.items()})
+
     def measure(summary, mode="group", C=C, L=L, R=R, refs=refs, p=p):
         """Builds one tree per layer replica with the given m storage (and geometry C, L, R),
         times the stage breakdown and the K-step region, and replays the routes for the
@@ -267,12 +349,7 @@ def main():
         for tr in trees:
             recs += tr.timing_read()
             tr.timing(False)
-        per = {}
-        for k, l, ms in recs:
-            per.setdefault((k, l), []).append(ms)
-        kernels = {f"{zha.KERNEL_NAMES[k]}{'_l' + str(l) if l else ''}": dict(launches=len(v), avg_us=1e3 * sum(v) / len(v),
-                                                                              total_ms=sum(v), code=k, level=l)
-                   for (k, l), v in sorted(per.items())}
+        kernels = kernel_table(recs)
         dom_name, dom = max(kernels.items(), key=lambda kv: kv[1]["total_ms"])
 
         # timed region: K steps, with an event pair around the dominant kernel only
@@ -396,6 +473,11 @@ def main():
         if growing:
             per_head["p_sweep"] = {str(x): round(rh["seg_us"].get("append", 0.0) + rh["seg_us"][x], 2) for x in p_sweep}
 
+    block = None
+    if args.block > 0 and args.summary == "native":
+        log(f"-- blocks of {args.block} queries per sequence, each routed alone")
+        block = measure_block(args.block)
+
     # dense decode on the same GPU and inputs, same protocol
     dense_us = None
     if not args.no_dense:
@@ -471,6 +553,8 @@ def main():
         result["per_head_routes"] = per_head
     if sweep is not None:
         result["geometry_sweep"] = sweep
+    if block is not None:
+        result["query_block"] = block
     if growing:
         result["append_us"] = round(seg_us.get("append", 0.0), 2)
         result["p_sweep"] = {str(x): round(seg_us.get("append", 0.0) + seg_us[x], 2) for x in p_sweep}

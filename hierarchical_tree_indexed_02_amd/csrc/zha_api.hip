@@ -51,6 +51,12 @@ zha_status check_desc(const zha_tree_desc* d) {
   if (d->summary != ZHA_SUMMARY_NATIVE && d->summary != ZHA_SUMMARY_FP8) return ZHA_ERR_INVALID;
   if (d->summary == ZHA_SUMMARY_FP8 && d->dtype != ZHA_BF16) return ZHA_ERR_UNSUPPORTED;
   if (d->n_q_heads % d->n_kv_heads != 0) return ZHA_ERR_INVALID;
+  if (d->max_queries < 0) return ZHA_ERR_INVALID;
+  {  // routing units of the largest route index the second grid dimension
+    const int64_t ru = (int64_t)d->batch * d->n_kv_heads * (d->max_queries > 1 ? d->max_queries : 1) *
+                       (d->per_head_routes ? d->n_q_heads / d->n_kv_heads : 1);
+    if (ru > 65535) return ZHA_ERR_UNSUPPORTED;
+  }
   if (d->batch > ZHA_MAX_BATCH) return ZHA_ERR_UNSUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return ZHA_ERR_UNSUPPORTED;
   if (!valid_refs(d->n_refs)) return ZHA_ERR_UNSUPPORTED;
@@ -170,20 +176,32 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   t->span[0] = 1;
   t->cap[0] = 0;
   const int U = t->U, R = t->R, d = t->d, G = t->G, L = t->L;
-  // routing workspace: for U routing units of G heads, and with per-head routes also for
-  // U*G routing units of one head; every per-unit array is sized for the larger count
-  const int RUmax = desc->per_head_routes ? U * G : U;
+  // routing workspace: a route has U * Tq * hr routing units of G / hr heads (Tq queries per
+  // sequence up to max_queries; hr = 1, or G with per-head routes); every per-unit array is
+  // sized for the largest count, and the per-workgroup partials for the largest product
+  const int maxq = desc->max_queries > 1 ? desc->max_queries : 1;
+  const int RUmax = U * maxq * (desc->per_head_routes ? G : 1);
   t->RUmax = RUmax;
   t->hr = 1;
+  t->Tq = 1;
+  t->multi = false;
   t->RU = U;
   t->WS = zha_score_wgs_units(U);
   t->WA = zha_sparse_wgs(U);
-  size_t spart_n = (size_t)U * t->WS * G * 2, apart_n = (size_t)U * t->WA * G * (d + 2);
-  size_t score_n = (size_t)U * ((G + 3) & ~3);
-  if (desc->per_head_routes) {
-    spart_n = std::max(spart_n, (size_t)RUmax * zha_score_wgs_units(RUmax) * 2);
-    apart_n = std::max(apart_n, (size_t)RUmax * zha_sparse_wgs(RUmax) * (d + 2));
-    score_n = std::max(score_n, (size_t)RUmax * 4);
+  size_t spart_n = 0, apart_n = 0, score_n = 0;
+  int64_t cand_n = 0;
+  int ctr_n = 0;
+  const int hrs[2] = {1, G};
+  for (int i = 0; i < (desc->per_head_routes ? 2 : 1); ++i) {
+    const int hr = hrs[i], Gr = G / hr;
+    for (int tq = 1; tq <= maxq; ++tq) {
+      const int ru = U * tq * hr;
+      spart_n = std::max(spart_n, (size_t)ru * zha_score_wgs_units(ru) * Gr * 2);
+      apart_n = std::max(apart_n, (size_t)ru * zha_sparse_wgs(ru) * Gr * (d + 2));
+      score_n = std::max(score_n, (size_t)ru * ((Gr + 3) & ~3));
+      cand_n = std::max(cand_n, zha_sel_cand_entries(ru));
+      ctr_n = std::max(ctr_n, zha_sel_ctr_words(ru));
+    }
   }
   bool ok = true;
   for (int l = 1; l <= L && ok; ++l) {
@@ -212,8 +230,6 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   ok = ok && dalloc(t, &t->fh_mass, (size_t)RUmax * nb * sizeof(unsigned long long));
   ok = ok && dalloc(t, &t->fh_edge, (size_t)RUmax * 2 * sizeof(unsigned long long));
   ok = ok && dalloc(t, &t->cut, (size_t)RUmax * 4 * sizeof(int32_t));
-  const int64_t cand_n = std::max(zha_sel_cand_entries(U), zha_sel_cand_entries(RUmax));
-  const int ctr_n = std::max(zha_sel_ctr_words(U), zha_sel_ctr_words(RUmax));
   ok = ok && dalloc(t, &t->sel_cand, (size_t)cand_n * 2 * sizeof(uint32_t));
   ok = ok && dalloc(t, &t->sel_ctr, (size_t)ctr_n * sizeof(uint32_t));
   ok = ok && dalloc(t, &t->lb_status, (size_t)RUmax * nchunk * sizeof(unsigned long long));
@@ -278,15 +294,21 @@ zha_status zha_append(zha_tree_t t, const void* K, const int32_t* new_seq_lens, 
   return ZHA_OK;
 }
 
-zha_status zha_route_ex(zha_tree_t t, const void* q, float p, float scale, zha_route_mode mode, zha_kept* kept,
-                        hipStream_t s) {
+// A route of Tq queries per sequence (multi: a block of queries, whose attention also reads
+// the block's own rows).
+static zha_status route_queries(zha_tree* t, const void* q, int Tq, bool multi, float p, float scale,
+                                zha_route_mode mode, zha_kept* kept, hipStream_t s) {
   if (!t || !q || !kept) return ZHA_ERR_INVALID;
   if (!t->built) return ZHA_ERR_INVALID;
   if (!(p > 0.0f) || !isfinite(p) || !isfinite(scale)) return ZHA_ERR_INVALID;
   if (mode != ZHA_ROUTE_GROUP && mode != ZHA_ROUTE_PER_HEAD) return ZHA_ERR_INVALID;
-  if (mode == ZHA_ROUTE_PER_HEAD && t->RUmax != t->U * t->G) return ZHA_ERR_INVALID;
+  if (mode == ZHA_ROUTE_PER_HEAD && !t->desc.per_head_routes) return ZHA_ERR_INVALID;
+  if (Tq < 1) return ZHA_ERR_INVALID;
+  if (Tq > (t->desc.max_queries > 1 ? t->desc.max_queries : 1)) return ZHA_ERR_CAPACITY;
   t->hr = mode == ZHA_ROUTE_PER_HEAD ? t->G : 1;
-  t->RU = t->U * t->hr;
+  t->Tq = Tq;
+  t->multi = multi;
+  t->RU = t->U * Tq * t->hr;
   t->WS = zha_score_wgs_units(t->RU);
   t->WA = zha_sparse_wgs(t->RU);
   hipError_t e = zha_launch_route(t, q, p, scale, s);
@@ -295,6 +317,16 @@ zha_status zha_route_ex(zha_tree_t t, const void* q, float p, float scale, zha_r
   kept->ids = t->kept[1];
   kept->cap = t->cap[1];
   return ZHA_OK;
+}
+
+zha_status zha_route_ex(zha_tree_t t, const void* q, float p, float scale, zha_route_mode mode, zha_kept* kept,
+                        hipStream_t s) {
+  return route_queries(t, q, 1, false, p, scale, mode, kept, s);
+}
+
+zha_status zha_route_multi(zha_tree_t t, const void* q, int32_t n_queries, float p, float scale,
+                           zha_route_mode mode, zha_kept* kept, hipStream_t s) {
+  return route_queries(t, q, n_queries, true, p, scale, mode, kept, s);
 }
 
 zha_status zha_route(zha_tree_t t, const void* q, float p, float scale, zha_kept* kept, hipStream_t s) {
@@ -306,9 +338,24 @@ zha_status zha_attend(zha_tree_t t, const void* q, const void* K, const void* V,
   if (!t || !q || !K || !V || !kept || !out || !lse) return ZHA_ERR_INVALID;
   if (!t->built) return ZHA_ERR_INVALID;
   if (kept->ids != t->kept[1]) return ZHA_ERR_INVALID;  // a view of this tree's last route
+  if (t->multi) return ZHA_ERR_INVALID;                 // a block of queries: zha_attend_multi
   if (!isfinite(scale)) return ZHA_ERR_INVALID;
   hipError_t e = zha_launch_attend(t, q, K, V, scale, out, lse, s);
   if (e != hipSuccess) return hip_fail("zha_attend launch", e);
+  return ZHA_OK;
+}
+
+zha_status zha_attend_multi(zha_tree_t t, const void* q, int32_t n_queries, const void* K, const void* V,
+                            const zha_kept* kept, float scale, float* out, float* lse, hipStream_t s) {
+  if (!t || !q || !K || !V || !kept || !out || !lse) return ZHA_ERR_INVALID;
+  if (!t->built) return ZHA_ERR_INVALID;
+  if (kept->ids != t->kept[1]) return ZHA_ERR_INVALID;
+  if (!t->multi || n_queries != t->Tq) return ZHA_ERR_INVALID;  // the last route carried this block
+  if (!isfinite(scale)) return ZHA_ERR_INVALID;
+  for (int b = 0; b < t->desc.batch; ++b)  // the block's rows N .. N + Tq - 1 lie inside K and V
+    if ((int64_t)t->len.n[b] + n_queries > t->T) return ZHA_ERR_CAPACITY;
+  hipError_t e = zha_launch_attend(t, q, K, V, scale, out, lse, s);
+  if (e != hipSuccess) return hip_fail("zha_attend_multi launch", e);
   return ZHA_OK;
 }
 

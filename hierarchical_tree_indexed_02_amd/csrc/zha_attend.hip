@@ -21,15 +21,17 @@
 namespace {
 
 struct AttArgs {
-  const void* q;           // [B][Hq][d]
+  const void* q;           // [B][Tq][Hq][d]
   const void* K;           // [B][Hkv][T][d]
   const void* V;
   const int32_t* kept;     // [U][cap1] level-1 kept chunk ids (sparse only)
   const int32_t* kept_count;
   int64_t cap1;
   float* part;             // o [U][W][G][d] (unnormalised), then (max in log2 units, sum) [U][W][G][2]
-  int W, U;                // workgroups per unit; routing units (U = B * Hkv * hr)
-  int hr;                  // routing units per (sequence, KV head): 1, or G when each head is routed alone
+  int W, U;                // workgroups per unit; routing units (U = B * Tq * Hkv * hr)
+  int hr;                  // routing units per (query, KV head): 1, or G when each head is routed alone
+  int Tq;                  // queries per sequence
+  int qtail;               // 1: query t of a block also reads the block's rows [N, N + t]
   int Hkv, Hq, G, C, Cshift;
   int64_t T;               // token stride of K/V
   float scale_log2;        // scale * log2(e)
@@ -61,11 +63,14 @@ __device__ __forceinline__ Positions unit_positions(const AttArgs& a, const Lens
     return P;
   }
   const int Nc = (N / a.C) * a.C;
+  // tail [Nc, Ne): the partial chunk, and for a block of queries the block's rows up to
+  // and including the unit's own
+  const int Ne = a.qtail ? N + unit_query(u, a.hr, a.Hkv, a.Tq) + 1 : N;
   const int nK = a.kept_count[u];
   const int32_t* kp = a.kept + (int64_t)u * a.cap1;
   const int sink = (Nc > 0 && (nK == 0 || kp[0] != 0)) ? 1 : 0;
   P.sink = sink;
-  P.nx = sink + (N - Nc);
+  P.nx = sink + (Ne - Nc);
   P.P = P.nx + nK * a.C;
   P.Nc = Nc;
   P.nK = nK;
@@ -212,8 +217,8 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, grp = lane >> 4;
   // u: routing unit, of G query heads; up: its (sequence, KV head) unit.  Units are numbered
-  // (sequence, KV head, head group), so the unit's first query head is u * G.
-  const int u = blockIdx.y, up = u / a.hr, bi = up / a.Hkv;
+  // (sequence, query, KV head, head group), so the unit's first query head is u * G.
+  const int u = blockIdx.y, up = plane_unit(u, a.hr, a.Hkv, a.Tq), bi = up / a.Hkv;
   const int G = a.G;
   const Positions P = unit_positions<DENSE>(a, la, u, bi);
   // Blocks of 4 * ATT_STEP positions are dealt to the workgroups in turn, so the unit's
@@ -482,6 +487,8 @@ hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const vo
   a.W = t->WA;
   a.U = t->RU;
   a.hr = t->hr;
+  a.Tq = t->Tq;
+  a.qtail = t->multi ? 1 : 0;
   a.Hkv = t->desc.n_kv_heads;
   a.Hq = t->desc.n_q_heads;
   a.G = t->G / t->hr;
@@ -513,6 +520,8 @@ hipError_t zha_launch_dense(const void* q, const void* K, const void* V, const Z
   a.W = WA;
   a.U = B * Hkv;
   a.hr = 1;
+  a.Tq = 1;
+  a.qtail = 0;
   a.Hkv = Hkv;
   a.Hq = Hq;
   a.G = Hq / Hkv;

@@ -162,6 +162,17 @@ template <int E> __device__ __forceinline__ void acc_finish(const Acc<E>& a, flo
 }
 #pragma clang fp contract(on)
 
+// Routing units are numbered ((sequence * Tq + query) * Hkv + KV head) * hr + head group:
+// Tq queries per sequence, hr routing units per (query, KV head).  A unit's query heads are
+// rows u * G' .. u * G' + G' - 1 of q [B][Tq][Hq][d] (G' = Gq / hr heads per unit); its
+// planes and K/V are those of its (sequence, KV head) pair, returned here.
+__device__ __forceinline__ int plane_unit(int u, int hr, int Hkv, int Tq) {
+  const int x = u / hr;
+  return (x / (Hkv * Tq)) * Hkv + x % Hkv;
+}
+// The unit's query index within its sequence's block of Tq queries.
+__device__ __forceinline__ int unit_query(int u, int hr, int Hkv, int Tq) { return (u / hr / Hkv) % Tq; }
+
 // ----------------------------------------------------------------------------- host side
 
 #define ZHA_MAX_LEVELS 16
@@ -207,9 +218,12 @@ struct zha_tree {
   int32_t* lb_error;                // [1] set if a look-back wait ever gives up
   float* apart;                     // attention partials: o [U][WA][G][d], then (max, sum) [U][WA][G][2]
   int WS, WA;                       // score and attention workgroups per routing unit, last route's mode
-  int hr;                           // routing units per (sequence, KV head) of the last route: 1 or G
-  int RU;                           // routing units of the last route: U * hr
-  int RUmax;                        // routing units the workspace is sized for: U, or U * G (per-head routes)
+  int hr;                           // routing units per (query, KV head) of the last route: 1 or G
+  int Tq;                           // queries per sequence of the last route (1 unless multi-query)
+  bool multi;                       // the last route was a multi-query route
+  int RU;                           // routing units of the last route: U * Tq * hr
+  int RUmax;                        // routing units the workspace is sized for: U * max_queries, times G
+                                    // with per-head routes
   int32_t* geo;                     // [L+2][B] device: lengths (row 0), nodes of level l per sequence (row l)
   ZLens len;                        // current lengths
   ZLens len_prev;                   // lengths before the last zha_append
@@ -233,7 +247,7 @@ hipError_t zha_launch_build(zha_tree* t, const void* K, hipStream_t s);
 hipError_t zha_launch_append(zha_tree* t, const void* K, hipStream_t s);
 hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hipStream_t s);
 hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const void* V, float scale,
-                             float* out, float* lse, hipStream_t s);
+                             float* out, float* lse, hipStream_t s);  // tail per t->multi
 hipError_t zha_launch_dense(const void* q, const void* K, const void* V, const ZLens& len, int B, int Hq,
                             int Hkv, int d, int64_t T, zha_dtype dt, float scale, float* out, float* lse,
                             float* part, int WA, hipStream_t s);

@@ -134,15 +134,15 @@ struct ScoreArgs {
   const void* m;          // level planes m [U][capl][R][d] (tree dtype, or fp8 e4m3 codes)
   const float* b;         // level planes b [U][capl][R]
   const float* ms;        // fp8 summaries: row scales [U][capl][R]
-  const void* q;          // [B][Hq][d]
+  const void* q;          // [B][Tq][Hq][d]
   int64_t capl;
   float* scores;          // [U][cap1][G]
   int64_t cap1;
   float* part;            // [U][W][G][2]: (max, sum exp) of the workgroup's scores per head
   int W;                  // workgroups per unit
-  int Hq, G;              // query heads; heads per routing unit
-  int Gq;                 // query heads per KV head
-  int hr;                 // routing units per (sequence, KV head): 1, or Gq when each head is routed alone
+  int G;                  // query heads per routing unit
+  int hr;                 // routing units per (query, KV head): 1, or Gq when each head is routed alone
+  int Hkv, Tq;            // KV heads; queries per sequence
   float scale;
 };
 
@@ -181,8 +181,7 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, grp = lane >> 4;
   // u: routing unit (frontier, scores, partials); up: its (sequence, KV head) unit (planes)
-  const int u = blockIdx.y, up = u / a.hr, h0 = (u - up * a.hr) * a.G;
-  const int Hkv = a.v.Hkv / a.hr, bi = up / Hkv, g = up % Hkv;
+  const int u = blockIdx.y, up = plane_unit(u, a.hr, a.Hkv, a.Tq);
   const int G = a.G;
   const int nF = frontier_size(a.v, u);
   // Super-tiles are dealt to the workgroups in turn: at any moment the unit's workgroups
@@ -193,7 +192,7 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
 
   typename M::frag qf[NK];
   {
-    const T* qp = (const T*)a.q + ((int64_t)bi * a.Hq + (int64_t)g * a.Gq + h0 + row) * D;
+    const T* qp = (const T*)a.q + ((int64_t)u * G + row) * D;
 #pragma unroll
     for (int s = 0; s < NK; ++s) {
       const int k0 = F8 ? grp * (D / 4) + s * 8 : s * M::KPER + grp * M::EPL;
@@ -1567,8 +1566,8 @@ int64_t zha_sel_cand_entries(int U) { return (int64_t)U * sel_regions(U) * LCAND
 int zha_sel_ctr_words(int U) { return U * (1 + KSMAX); }
 
 hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hipStream_t s) {
-  // U: routing units of this route (t->U (sequence, KV head) pairs, or t->U * G (sequence,
-  // query head) pairs for per-head routes); Gr: query heads per routing unit
+  // U: routing units of this route (t->U * Tq (sequence, query, KV head) triples, times G
+  // (one per query head) for per-head routes); Gr: query heads per routing unit
   const int U = t->RU, L = t->L, Gr = t->G / t->hr;
   const int Cshift = cshift_of(t->C);
   int32_t* cntF = t->counts;                         // [L+2][U]
@@ -1582,7 +1581,7 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     v.cap_parent = l < L ? t->cap[l + 1] : 0;
     v.C = t->C;
     v.Cshift = Cshift;
-    v.Hkv = t->desc.n_kv_heads * t->hr;  // routing units per sequence
+    v.Hkv = t->desc.n_kv_heads * t->hr * t->Tq;  // routing units per sequence
     v.nodes = t->geo + (int64_t)l * t->desc.batch;
     v.child = t->geo + (int64_t)(l - 1) * t->desc.batch;
     int32_t* next_nF = l > 1 ? cntF + (int64_t)(l - 1) * U : nullptr;
@@ -1598,10 +1597,10 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     sa.cap1 = t->cap[1];
     sa.part = t->spart;
     sa.W = zha_score_wgs(t, l);
-    sa.Hq = t->desc.n_q_heads;
     sa.G = Gr;
-    sa.Gq = t->G;
     sa.hr = t->hr;
+    sa.Hkv = t->desc.n_kv_heads;
+    sa.Tq = t->Tq;
     sa.scale = scale;
     zha_time_begin(t, s, ZHA_K_SCORE, l);
     if (t->f8)

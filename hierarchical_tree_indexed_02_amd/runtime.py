@@ -20,16 +20,17 @@ class Tree:
     """One attention layer's summary tree (library-owned device memory)."""
 
     def __init__(self, batch, n_kv_heads, n_q_heads, head_dim, chunk, levels, n_refs, max_tokens,
-                 dtype=torch.bfloat16, summary="native", per_head_routes=False):
+                 dtype=torch.bfloat16, summary="native", per_head_routes=False, max_queries=1):
         """summary: "native" (m stored in dtype) or "fp8" (e4m3 codes with a power-of-two
         scale per node and reference; dtype bf16 only).  per_head_routes: the tree also serves
-        routes that give every query head its own kept set (route(..., mode="per_head"))."""
+        routes that give every query head its own kept set (route(..., mode="per_head")).
+        max_queries: queries per sequence one route_multi may carry."""
         if summary not in ("native", "fp8"):
             raise ValueError(f"unsupported summary storage {summary!r}")
         self.desc = zha.zha_tree_desc(batch, n_kv_heads, n_q_heads, head_dim, chunk, levels, n_refs, max_tokens,
                                       zdtype(dtype),
                                       zha.ZHA_SUMMARY_FP8 if summary == "fp8" else zha.ZHA_SUMMARY_NATIVE,
-                                      1 if per_head_routes else 0)
+                                      1 if per_head_routes else 0, max_queries)
         self.RU = batch * n_kv_heads  # routing units of the last route
         self.dtype = dtype
         self.summary = summary
@@ -39,6 +40,7 @@ class Tree:
         self.G = n_q_heads // n_kv_heads
         self.h = zha.zha_tree_create(self.desc)
         self.kept = None
+        self.Tq = 1  # queries per sequence of the last route
 
     def close(self):
         if getattr(self, "h", None):
@@ -71,7 +73,32 @@ class Tree:
             self.RU = self.U * self.G
         else:
             raise ValueError(f"unknown routing mode {mode!r}")
+        self.Tq = 1
         return self.kept
+
+    def route_multi(self, q, p, scale=1.0, stream=None, mode="group"):
+        """Routes a block of queries q [B][Tq][Hq][d], each on its own, over the tree as it
+        stands (the block's own tokens are not in it).  Routing units are numbered
+        ((b * Tq + t) * Hkv + KV head) * hr + head (hr = 1, or G per head)."""
+        if mode not in ("group", "per_head"):
+            raise ValueError(f"unknown routing mode {mode!r}")
+        Tq = int(q.shape[1])
+        m = zha.ZHA_ROUTE_GROUP if mode == "group" else zha.ZHA_ROUTE_PER_HEAD
+        self.kept = zha.zha_route_multi(self.h, q, Tq, p, scale, m, stream)
+        self.Tq = Tq
+        self.RU = self.U * Tq * (1 if mode == "group" else self.G)
+        return self.kept
+
+    def attend_multi(self, q, K, V, scale=1.0, out=None, lse=None, stream=None):
+        """Attention of the block routed by route_multi: query t also reads the block's rows
+        N .. N + t of K and V (N: the tree's length).  out [B][Tq][Hq][d], lse [B][Tq][Hq]."""
+        Tq = int(q.shape[1])
+        if out is None:
+            out = torch.empty((self.B, Tq, self.Hq, self.d), dtype=torch.float32, device=q.device)
+        if lse is None:
+            lse = torch.empty((self.B, Tq, self.Hq), dtype=torch.float32, device=q.device)
+        zha.zha_attend_multi(self.h, q, Tq, K, V, self.kept, scale, out, lse, stream)
+        return out, lse
 
     def attend(self, q, K, V, scale=1.0, out=None, lse=None, stream=None):
         if out is None:
@@ -101,7 +128,7 @@ class Tree:
 
     def route_level(self, level: int, device="cuda"):
         """(frontier counts [RU], kept counts [RU], kept ids [RU][cap]) of the last route, per
-        routing unit (RU = U after a group route, U * G after a per-head route)."""
+        routing unit (RU = U * Tq, times G after a per-head route)."""
         cap = self.capacity(level)
         nf = torch.empty(self.RU, dtype=torch.int32, device=device)
         nk = torch.empty(self.RU, dtype=torch.int32, device=device)

@@ -26,7 +26,8 @@ KERNEL_NAMES = {1: "build", 2: "append", 3: "score", 4: "select", 5: "attend", 6
 class zha_tree_desc(Structure):
     _fields_ = [("batch", c_int32), ("n_kv_heads", c_int32), ("n_q_heads", c_int32), ("head_dim", c_int32),
                 ("chunk", c_int32), ("levels", c_int32), ("n_refs", c_int32), ("max_tokens", c_int64),
-                ("dtype", c_int), ("summary", c_int), ("per_head_routes", c_int32)]
+                ("dtype", c_int), ("summary", c_int), ("per_head_routes", c_int32),
+                ("max_queries", c_int32)]
 
 
 class zha_kept(Structure):
@@ -69,6 +70,8 @@ def load():
             "zha_route": (st, [vp, vp, c_float, c_float, POINTER(zha_kept), vp]),
             "zha_route_ex": (st, [vp, vp, c_float, c_float, c_int, POINTER(zha_kept), vp]),
             "zha_attend": (st, [vp, vp, vp, vp, POINTER(zha_kept), c_float, vp, vp, vp]),
+            "zha_route_multi": (st, [vp, vp, c_int32, c_float, c_float, c_int, POINTER(zha_kept), vp]),
+            "zha_attend_multi": (st, [vp, vp, c_int32, vp, vp, POINTER(zha_kept), c_float, vp, vp, vp]),
             "zha_dense_decode": (st, [vp, vp, vp, _i32p, c_int32, c_int32, c_int32, c_int32, c_int64, c_int,
                                       c_float, vp, vp, vp, c_size_t, vp]),
             "zha_dense_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int64]),
@@ -158,6 +161,19 @@ def zha_route_ex(tree: int, q, p: float, scale: float, mode: int, stream=None) -
     _check(load().zha_route_ex(tree, _ptr(q), float(p), float(scale), int(mode), ctypes.byref(kept), _stream(stream)),
            "zha_route_ex")
     return kept
+
+
+def zha_route_multi(tree: int, q, n_queries: int, p: float, scale: float, mode: int, stream=None) -> zha_kept:
+    kept = zha_kept()
+    _check(load().zha_route_multi(tree, _ptr(q), int(n_queries), float(p), float(scale), int(mode),
+                                  ctypes.byref(kept), _stream(stream)), "zha_route_multi")
+    return kept
+
+
+def zha_attend_multi(tree: int, q, n_queries: int, K, V, kept: zha_kept, scale: float, out, lse,
+                     stream=None) -> None:
+    _check(load().zha_attend_multi(tree, _ptr(q), int(n_queries), _ptr(K), _ptr(V), ctypes.byref(kept),
+                                   float(scale), _ptr(out), _ptr(lse), _stream(stream)), "zha_attend_multi")
 
 
 def zha_attend(tree: int, q, K, V, kept: zha_kept, scale: float, out, lse, stream=None) -> None:

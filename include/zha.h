@@ -94,6 +94,9 @@ typedef struct {
     zha_summary summary;  /* storage of the planes' m (ZHA_SUMMARY_FP8 needs dtype bf16) */
     int32_t per_head_routes; /* nonzero: the tree also serves ZHA_ROUTE_PER_HEAD routes (its
                                 routing workspace is sized for B*Hq routing units) */
+    int32_t max_queries;  /* queries per sequence one zha_route_multi may carry (0 is taken
+                             as 1); the routing workspace is sized for that many.  The routing
+                             units of the largest route must number at most 65535 */
 } zha_tree_desc;
 
 /* How the G query heads of one KV head are routed.  ZHA_ROUTE_GROUP: one kept
@@ -177,16 +180,48 @@ ZHA_API zha_status zha_route(zha_tree_t tree, const void* q, float p, float scal
 ZHA_API zha_status zha_route_ex(zha_tree_t tree, const void* q, float p, float scale, zha_route_mode mode,
                         zha_kept* kept, hipStream_t stream);
 
+/* Routes a block of Tq = n_queries consecutive queries of every sequence,
+ * each query on its own, as a decode query is routed: the queries of a
+ * prefill chunk or of a speculative verification step.  Every query descends
+ * the tree from the top ([aitop] abstract: later queries traverse the tree top
+ * down; [flux] "树形索引是怎么搭的": routing plus final attention per query grows
+ * sublinearly with length, so attention over a whole sequence is
+ * subquadratic).  The tree holds the N_b tokens before the block (the block's
+ * own keys are not in it); query t of sequence b stands at position N_b + t.
+ * q: [B][Tq][Hq][d] in the tree dtype.  Routing units are numbered
+ * ((b * Tq + t) * Hkv + KV head) * hr + head, hr = 1 (ZHA_ROUTE_GROUP) or G
+ * (ZHA_ROUTE_PER_HEAD); *kept views B*Tq*Hkv*hr counts and id rows.  A unit's
+ * kept set is the one zha_route_ex would give that query alone.
+ * Errors: as zha_route_ex; ZHA_ERR_INVALID for n_queries < 1;
+ * ZHA_ERR_CAPACITY for n_queries above the tree's max_queries. */
+ZHA_API zha_status zha_route_multi(zha_tree_t tree, const void* q, int32_t n_queries, float p, float scale,
+                           zha_route_mode mode, zha_kept* kept, hipStream_t stream);
+
 /* Exact attention of each query head over S = {token 0} U (tokens of the
  * kept chunks) U [Nc, N), S a set ([wqu] "How does top-p routing pick
  * tokens?": the first token is always kept; the trailing partial chunk is not
  * in the tree and is always read).  out_h = sum_{t in S} softmax_S(scale *
  * q_h.k_t) v_t and lse_h = log sum_{t in S} exp(scale * q_h.k_t), computed
  * in float32 from the stored K and V.  kept: the view returned by zha_route
- * on this tree.  Errors: ZHA_ERR_INVALID, ZHA_ERR_HIP. */
+ * on this tree.  Errors: ZHA_ERR_INVALID (also when the last route was a
+ * zha_route_multi), ZHA_ERR_HIP. */
 ZHA_API zha_status zha_attend(zha_tree_t tree, const void* q, const void* K, const void* V,
                       const zha_kept* kept, float scale, float* out, float* lse,
                       hipStream_t stream);
+
+/* Exact attention of a block of queries routed by zha_route_multi.  Query t
+ * of sequence b attends S = {token 0} U (tokens of its kept chunks) U
+ * [Nc_b, N_b + t + 1): besides the partial chunk, the block's rows up to its
+ * own position, causally.  Rows N_b .. N_b + Tq - 1 of K and V hold the
+ * block's keys and values (written there by the caller; zha_append adds them
+ * to the tree afterwards).  q: [B][Tq][Hq][d]; out: [B][Tq][Hq][d] float32;
+ * lse: [B][Tq][Hq] float32; same formulas as zha_attend.
+ * Errors: ZHA_ERR_INVALID (kept is not the view of this tree's last route, or
+ * that route was not a zha_route_multi of n_queries queries), ZHA_ERR_CAPACITY
+ * (N_b + n_queries > max_tokens for some b), ZHA_ERR_HIP. */
+ZHA_API zha_status zha_attend_multi(zha_tree_t tree, const void* q, int32_t n_queries, const void* K,
+                            const void* V, const zha_kept* kept, float scale, float* out, float* lse,
+                            hipStream_t stream);
 
 /* Dense decode attention over [0, N_b), the comparison baseline.  Same
  * layouts as zha_attend.  workspace: device scratch of at least

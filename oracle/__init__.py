@@ -57,6 +57,8 @@ def _bind(path: str):
                            _i32p, _i64p, _i32p, _i64p]
     L.zo_attend_set.restype = _i64
     L.zo_attend_set.argtypes = [_i64, _int, _i32p, _i64, _i64p]
+    L.zo_block_attend_set.restype = _i64
+    L.zo_block_attend_set.argtypes = [_i64, _int, _i32p, _i64, _i64, _i64p]
     L.zo_attend.restype = None
     L.zo_attend.argtypes = [_f64p, _int, _int, _f64p, _f64p, _i64p, _i64, _f64p, _f64p]
     L.zo_attend_blockwise.restype = None
@@ -236,6 +238,15 @@ def attend_set(N: int, C: int, kept):
     kept = np.ascontiguousarray(kept, dtype=np.int32)
     out = np.empty(max(N, 1), dtype=np.int64)
     n = lib().zo_attend_set(N, C, _p(kept, _i32p), len(kept), _p(out, _i64p))
+    return out[:n].copy()
+
+
+def block_attend_set(N: int, C: int, kept, t: int):
+    """Attention set of query t of a block of queries after N cached tokens: the decode set
+    over the cache plus the block's rows N .. N + t (zo_block_attend_set)."""
+    kept = np.ascontiguousarray(kept, dtype=np.int32)
+    out = np.empty(N + t + 1, dtype=np.int64)
+    n = lib().zo_block_attend_set(N, C, _p(kept, _i32p), len(kept), t, _p(out, _i64p))
     return out[:n].copy()
 
 

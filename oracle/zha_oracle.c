@@ -33,7 +33,9 @@
  *     The G heads of one KV head share one kept set: the mass of a node is the
  *     mean over heads of each head's frontier-normalised mass.
  *   - The attention set is token 0 (the sink), the tokens of the kept leaf
- *     chunks and the trailing partial chunk [Nc, N).
+ *     chunks and the trailing partial chunk [Nc, N); a query of a block of
+ *     queries after the N cached tokens also reads the block's rows up to its
+ *     own position.
  *
  * Every floating-point quantity is double.  OpenMP only splits independent
  * outputs across threads; each output is computed by one thread in a fixed
@@ -432,6 +434,37 @@ ZO_EXPORT int64_t zo_attend_set(int64_t N, int C, const int32_t* kept, int64_t n
     for (int64_t t = Nc; t < N; ++t) in[t] = 1;
     int64_t n = 0;
     for (int64_t t = 0; t < N; ++t) if (in[t]) tokens_out[n++] = t;
+    free(in);
+    return n;
+}
+
+/*
+ * Attention set of query t of a block of queries standing at positions N, N+1, ...
+ * right after a cache of N tokens (a prefill chunk, or the drafts of a speculative
+ * verification step): the decode set over the N cached tokens (token 0, the kept
+ * chunks, the partial chunk [Nc, N)) and the block's own rows N .. N+t, no later one.
+ * Reading: every query of the block descends the tree as it stood before the block
+ * ([aitop] abstract: later queries traverse the tree from the top; [flux]
+ * "树形索引是怎么搭的": routing plus attention per query is sublinear, so a whole
+ * sequence is subquadratic), and attention is causal.  tokens_out holds N + t + 1
+ * entries at most.
+ */
+ZO_EXPORT int64_t zo_block_attend_set(int64_t N, int C, const int32_t* kept, int64_t nK, int64_t t,
+                                      int64_t* tokens_out)
+{
+    int64_t E = N + t + 1;          /* positions 0 .. N+t may be read */
+    if (N < 0 || t < 0) return 0;
+    unsigned char* in = (unsigned char*)calloc((size_t)E, 1);
+    int64_t Nc = zo_tree_tokens(N, C);
+    in[0] = 1;
+    for (int64_t k = 0; k < nK; ++k)
+        for (int c = 0; c < C; ++c) {
+            int64_t x = (int64_t)kept[k] * C + c;
+            if (x < Nc) in[x] = 1;
+        }
+    for (int64_t x = Nc; x < E; ++x) in[x] = 1;
+    int64_t n = 0;
+    for (int64_t x = 0; x < E; ++x) if (in[x]) tokens_out[n++] = x;
     free(in);
     return n;
 }

@@ -358,6 +358,61 @@ def pin_attend_set():
         assert S.tolist() == sorted(want), (N, C, kept)
 
 
+# ------------------------------------------------- blocks of queries
+
+def pin_block_attend_set():
+    """Query t of a block after N cached tokens reads token 0, its kept chunks, the partial
+    chunk and the block's rows N .. N + t: built here position by position."""
+    for N, C, kept, t in [(103, 4, [1, 3, 7], 0), (103, 4, [1, 3, 7], 5), (100, 4, [0, 24], 3), (0, 4, [], 2),
+                          (3, 4, [], 0), (1024, 256, [2], 300), (17, 4, [], 9)]:
+        S = oracle.block_attend_set(N, C, np.array(kept, dtype=np.int32), t)
+        Nc = (N // C) * C
+        want = [x for x in range(N + t + 1)
+                if x == 0 or x >= Nc or (x // C) in kept]
+        assert S.tolist() == want, (N, C, kept, t)
+
+
+def pin_block_p_one_is_causal():
+    """With p = 1 every query of a block reads every earlier position and itself: the
+    block's outputs are causal attention (torch's attention with the causal mask)."""
+    import torch
+    for N, C, L, T in [(4 ** 3 + 6, 4, 3, 7), (4 ** 3, 4, 3, 5)]:
+        d, R, G = 8, 2, 2
+        K, V, refs, _ = _rand(41, N + T, d, R, G)
+        rng = np.random.default_rng(42)
+        Q = rng.standard_normal((T, G, d)) / math.sqrt(d) * 3.0
+        tree = oracle.tree_definition(K[:N], refs, C, L)
+        mask = np.arange(N + T)[None, :] <= (N + np.arange(T))[:, None]          # [T][N+T]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(Q).transpose(0, 1), torch.tensor(K)[None].expand(G, N + T, d),
+            torch.tensor(V)[None].expand(G, N + T, d), attn_mask=torch.tensor(mask)[None], scale=1.0)
+        for t in range(T):
+            _, Kp = oracle.route(tree, N, C, L, Q[t], 1.0)
+            S = oracle.block_attend_set(N, C, Kp[1], t)
+            assert np.array_equal(S, np.arange(N + t + 1)), (N, t)
+            o, _ = oracle.attend(Q[t], K, V, S)
+            _close(o, ref[:, t, :].numpy(), 1e-12, f"block query {t} at p=1")
+
+
+def pin_block_first_query_is_decode():
+    """Query 0 of a block after N tokens is the decode query of a cache of N + 1 tokens
+    when token N does not complete a chunk: the tree is the same (it holds complete chunks
+    only), so are the route and the attention set."""
+    N, C, L, d, R, G, p = 4 ** 3 * 2 + 5, 4, 3, 8, 3, 2, 0.8
+    assert (N + 1) % C != 0
+    K, V, refs, q = _rand(43, N + 1, d, R, G)
+    t_blk = oracle.tree_definition(K[:N], refs, C, L)
+    t_dec = oracle.tree_definition(K[:N + 1], refs, C, L)
+    _, Kb = oracle.route(t_blk, N, C, L, q, p)
+    _, Kd = oracle.route(t_dec, N + 1, C, L, q, p)
+    for l in range(1, L + 1):
+        assert np.array_equal(Kb[l], Kd[l]), l
+    Sb = oracle.block_attend_set(N, C, Kb[1], 0)
+    Sd = oracle.attend_set(N + 1, C, Kd[1])
+    assert np.array_equal(Sb, Sd)
+    assert Sb[-1] == N
+
+
 # ------------------------------------------------------- fp8 summaries
 
 def _e4m3_grid():
@@ -440,4 +495,5 @@ ALL_PINS = [
     pin_bruteforce_tiny, pin_nucleus_single_tokens, pin_exact_reference, pin_translation_permutation,
     pin_value_closed_forms, pin_equal_masses, pin_single_level_nesting, pin_growth,
     pin_dense_two_ways, pin_p_one_is_dense, pin_attend_set, pin_fp8_quantizer, pin_fp8_rows,
+    pin_block_attend_set, pin_block_p_one_is_causal, pin_block_first_query_is_decode,
 ]

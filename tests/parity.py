@@ -76,10 +76,10 @@ class Case:
         self.Kd[b, g, start:start + n] = torch.from_numpy(np.ascontiguousarray(Krows)).to(self.Kd.device, dt)
         self.Vd[b, g, start:start + n] = torch.from_numpy(np.ascontiguousarray(Vrows)).to(self.Vd.device, dt)
 
-    def tree(self, levels=None, chunk=None, refs=None, summary="native", per_head_routes=False):
+    def tree(self, levels=None, chunk=None, refs=None, summary="native", per_head_routes=False, max_queries=1):
         cfg = self.cfg
         t = Tree(self.B, self.Hkv, self.Hq, self.d, chunk or cfg.chunk, levels or cfg.levels, cfg.n_refs, self.T,
-                 TORCH_DT[cfg.dtype], summary=summary, per_head_routes=per_head_routes)
+                 TORCH_DT[cfg.dtype], summary=summary, per_head_routes=per_head_routes, max_queries=max_queries)
         t.build(self.Kd, self.refs_d if refs is None else refs, self.lens)
         return t
 
@@ -197,8 +197,28 @@ def routing_units(case: Case, mode: str):
                     yield (b * case.Hkv + g) * case.G + h, b, g, h, 1
 
 
+def block_units(case: Case, Tq: int, mode: str):
+    """(routing unit, sequence, query in the block, KV head, first head in the group, heads) of
+    a block route: units numbered ((b * Tq + t) * Hkv + KV head) * hr + head."""
+    hr = 1 if mode == "group" else case.G
+    for b in range(case.B):
+        for t in range(Tq):
+            for g in range(case.Hkv):
+                for h in range(hr):
+                    yield ((b * Tq + t) * case.Hkv + g) * hr + h, b, t, g, h, case.G // hr
+
+
 def check_route(case: Case, tree: Tree, t: int, p: float, scale=1.0, units=None, mode="group"):
     """Teacher-forced route parity at every level, per routing unit.  Returns per-level stats."""
+    items = []
+    for v, b, g, h0, nh in routing_units(case, mode):
+        if units is None or b * case.Hkv + g in units:
+            items.append((v, b, g, case.unit_q(t, b, g, scale)[h0:h0 + nh]))
+    return check_route_items(case, tree, p, items)
+
+
+def check_route_items(case: Case, tree: Tree, p: float, items):
+    """Route parity of the listed routing units: (unit, sequence, KV head, its queries [heads][d])."""
     stats = {}
     levels = {}
     for l in range(tree.L, 0, -1):
@@ -209,12 +229,9 @@ def check_route(case: Case, tree: Tree, t: int, p: float, scale=1.0, units=None,
         m_d, b_d = tree.level(l)
         planes[l] = (m_d, b_d)
     n_amb = 0
-    for v, b, g, h0, nh in routing_units(case, mode):
+    for v, b, g, q in items:
         N = case.lens[b]
         pu = b * case.Hkv + g  # the (sequence, KV head) unit whose tree is routed
-        if units is not None and pu not in units:
-            continue
-        q = case.unit_q(t, b, g, scale)[h0:h0 + nh]
         u = v  # routing unit: frontier, kept ids
         for l in range(tree.L, 0, -1):
             nf, nk, ids = levels[l]
@@ -276,6 +293,33 @@ def check_attend(case: Case, tree: Tree, out, lse, t: int, scale=1.0, units=None
         worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
         kappa.append(len(S) / N)
     return dict(worst_out=worst_o, worst_lse=worst_l, kappa=float(np.mean(kappa)) if kappa else 0.0)
+
+
+def check_block(case: Case, tree: Tree, qb, p: float, out, lse, scale=1.0, mode="group", units=None):
+    """A block of queries routed by route_multi and attended by attend_multi: route parity of
+    every routing unit, and the oracle's attention of query t over token 0, its GPU kept
+    chunks, the partial chunk and the block's rows N .. N + t.  qb: host [B][Tq][Hq][d]."""
+    Tq = qb.shape[1]
+    sel = [x for x in block_units(case, Tq, mode) if units is None or x[0] in units]
+    items = [(v, b, g, qb[b, t, g * case.G + h * nh:g * case.G + (h + 1) * nh].astype(np.float64) * scale)
+             for v, b, t, g, h, nh in sel]
+    r = check_route_items(case, tree, p, items)
+    _, nk, ids = tree.route_level(1)
+    nk = nk.cpu().numpy()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    worst_o, worst_l = 0.0, 0.0
+    for (v, b, t, g, h, nh), (_, _, _, q) in zip(sel, items):
+        N = case.lens[b]
+        S = oracle.block_attend_set(N, tree.C, ids[v, :nk[v]].cpu().numpy(), t)
+        Ku, Vu = case.K[(b, g)][:N + Tq], case.V[(b, g)][:N + Tq]
+        o_o, l_o = oracle.attend(q, Ku, Vu, S)
+        hs = slice(g * case.G + h * nh, g * case.G + (h + 1) * nh)
+        eo = float(np.max(np.abs(out[b, t, hs] - o_o)))
+        el = float(np.max(np.abs(lse[b, t, hs] - l_o)))
+        assert eo <= OUT_TOL, f"routing unit {v} (b={b} t={t} g={g}): out err {eo:.3e}"
+        assert el <= LSE_TOL, f"routing unit {v} (b={b} t={t} g={g}): lse err {el:.3e}"
+        worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+    return r, dict(worst_out=worst_o, worst_lse=worst_l, units=len(sel))
 
 
 def check_dense(case: Case, t: int, scale=1.0, units=None):

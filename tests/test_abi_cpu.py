@@ -39,10 +39,11 @@ def test_status_strings():
 
 def _desc(**kw):
     base = dict(batch=1, n_kv_heads=4, n_q_heads=32, head_dim=128, chunk=4, levels=6, n_refs=16, max_tokens=1 << 18,
-                dtype=zha.ZHA_BF16)
+                dtype=zha.ZHA_BF16, summary=zha.ZHA_SUMMARY_NATIVE, per_head_routes=0, max_queries=0)
     base.update(kw)
     return zha.zha_tree_desc(*[base[k] for k in ("batch", "n_kv_heads", "n_q_heads", "head_dim", "chunk", "levels",
-                                                   "n_refs", "max_tokens", "dtype")])
+                                                   "n_refs", "max_tokens", "dtype", "summary", "per_head_routes",
+                                                   "max_queries")])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -60,6 +61,10 @@ def _desc(**kw):
     (dict(batch=65), zha.ZHA_ERR_UNSUPPORTED),
     (dict(chunk=4, levels=16), zha.ZHA_ERR_UNSUPPORTED),
     (dict(max_tokens=1 << 31), zha.ZHA_ERR_UNSUPPORTED),
+    (dict(max_queries=-1), zha.ZHA_ERR_INVALID),
+    # routing units of the largest route: 64 * 4 * 256 = 65536, one more than a grid dimension holds
+    (dict(batch=64, max_queries=256), zha.ZHA_ERR_UNSUPPORTED),
+    (dict(batch=64, max_queries=32, per_head_routes=1), zha.ZHA_ERR_UNSUPPORTED),
 ])
 def test_create_rejects(kw, status):
     with pytest.raises(zha.ZhaError) as ei:
@@ -74,6 +79,10 @@ def test_null_arguments_rejected():
     assert lib.zha_append(None, None, None, None) == zha.ZHA_ERR_INVALID
     assert lib.zha_route(None, None, ctypes.c_float(0.9), ctypes.c_float(1.0), None, None) == zha.ZHA_ERR_INVALID
     assert lib.zha_attend(None, None, None, None, None, ctypes.c_float(1.0), None, None, None) == zha.ZHA_ERR_INVALID
+    assert lib.zha_route_multi(None, None, 2, ctypes.c_float(0.9), ctypes.c_float(1.0), 0, None,
+                               None) == zha.ZHA_ERR_INVALID
+    assert lib.zha_attend_multi(None, None, 2, None, None, None, ctypes.c_float(1.0), None, None,
+                                None) == zha.ZHA_ERR_INVALID
     assert lib.zha_tree_bytes(None, None) == zha.ZHA_ERR_INVALID
     assert lib.zha_timing_enable(None, 1, -1) == zha.ZHA_ERR_INVALID
     n = ctypes.c_int32()

@@ -11,7 +11,7 @@ import torch
 import oracle
 import zha_inputs as zi
 from hierarchical_tree_indexed_02_amd import zha
-from parity import Case, check_attend, check_build, check_dense, check_route, full_check, route_attend
+from parity import Case, check_attend, check_block, check_build, check_dense, check_route, full_check, route_attend
 
 pytestmark = pytest.mark.gpu
 
@@ -216,6 +216,80 @@ def test_per_head_needs_the_workspace():
     tree = case.tree()
     with pytest.raises(zha.ZhaError):
         tree.route(case.qd[0], 0.9, mode="per_head")
+
+
+# --------------------------------------------------------------------------- blocks of queries
+
+def block_of(case: Case, Tq: int):
+    """The first Tq decode queries of every sequence as one block: host [B][Tq][Hq][d] and device."""
+    qb = np.ascontiguousarray(case.q[:Tq].transpose(1, 0, 2, 3))
+    return qb, case.qd[:Tq].transpose(0, 1).contiguous()
+
+
+MULTI_VARIANTS = [
+    # lengths leave the block's rows inside the generated keys; 4990 % 4 = 2, so the tails of
+    # the later queries cross a chunk boundary
+    ("block bf16 d128 C4 L3 R16 G8 B2 T5", dict(batch=2, n_tokens=5000, chunk=4, levels=3, n_refs=16), [4990, 3333],
+     5, "group", 5),
+    ("block bf16 d128 C4 L3 R16 G8 B2 T5 per-head", dict(batch=2, n_tokens=5000, chunk=4, levels=3, n_refs=16),
+     [4990, 3333], 5, "per_head", 5),
+    ("block f32 d64 C3 L3 R4 G2 T7 of 9", dict(batch=1, n_tokens=1100, head_dim=64, n_q_heads=8, n_kv_heads=4,
+                                               chunk=3, levels=3, n_refs=4, dtype="f32"), [1001], 7, "group", 9),
+    ("block bf16 d128 C4 L2 R16 G8 T3 large frontier", dict(batch=1, n_tokens=65560, n_q_heads=16, n_kv_heads=2,
+                                                            chunk=4, levels=2, n_refs=16), [65539], 3, "group", 3),
+    ("block bf16 d128 C4 L3 R4 G4 B3 T4 short sequences", dict(batch=3, n_tokens=600, n_q_heads=16, chunk=4,
+                                                                 levels=3, n_refs=4), [3, 1, 517], 4, "group", 4),
+]
+
+
+@pytest.mark.parametrize("label,kw,lens,Tq,mode,maxq", MULTI_VARIANTS, ids=[v[0] for v in MULTI_VARIANTS])
+def test_block_routing(label, kw, lens, Tq, mode, maxq):
+    """A block of Tq queries per sequence, each routed alone over the tree of the N cached
+    tokens and attending its kept chunks plus the block's rows up to its own position."""
+    cfg = small(**kw, n_queries=max(Tq, 4), needles_per_unit=4)
+    say(f"case {label}: lens={lens} Tq={Tq} mode={mode} max_queries={maxq}")
+    case = Case(cfg, lens=lens, n_queries=Tq, max_tokens=cfg.n_tokens)
+    tree = case.tree(per_head_routes=mode == "per_head", max_queries=maxq)
+    qb, qbd = block_of(case, Tq)
+    for p in (0.5, 0.9, 1.0):
+        tree.route_multi(qbd, p, mode=mode)
+        out, lse = tree.attend_multi(qbd, case.Kd, case.Vd)
+        torch.cuda.synchronize()
+        r, a = check_block(case, tree, qb, p, out, lse, mode=mode)
+        say(f" p={p}", r, a)
+
+
+def test_block_capacity_and_order():
+    """A block needs a tree sized for it and its rows inside K/V; a block route is attended
+    only by attend_multi of the same size, a single-query route only by attend; block routes
+    leave later single-query routes unchanged."""
+    cfg = small(batch=1, n_tokens=1000, n_q_heads=8, n_kv_heads=2, chunk=4, levels=2, n_refs=4, n_queries=4,
+                needles_per_unit=2)
+    say("case block routing errors: N=996 of max 1000, max_queries 4")
+    case = Case(cfg, lens=[996], n_queries=4, max_tokens=1000)
+    tree = case.tree(max_queries=4)
+    out0, lse0 = route_attend(case, tree, 0, 0.9)
+    qb4, qbd4 = block_of(case, 4)
+    with pytest.raises(zha.ZhaError) as ei:
+        tree.route_multi(torch.cat([qbd4, qbd4[:, :1]], 1).contiguous(), 0.9)
+    assert ei.value.status == zha.ZHA_ERR_CAPACITY
+    tree.route_multi(qbd4, 0.9)  # N + 4 = max_tokens: fits
+    with pytest.raises(zha.ZhaError):
+        tree.attend(case.qd[0], case.Kd, case.Vd)
+    with pytest.raises(zha.ZhaError):
+        tree.attend_multi(qbd4[:, :3].contiguous(), case.Kd, case.Vd)
+    out, lse = tree.attend_multi(qbd4, case.Kd, case.Vd)
+    torch.cuda.synchronize()
+    say(" block of 4 at the capacity edge", *check_block(case, tree, qb4, 0.9, out, lse))
+    out1, lse1 = route_attend(case, tree, 0, 0.9)
+    assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
+    with pytest.raises(zha.ZhaError):
+        tree.attend_multi(qbd4, case.Kd, case.Vd)
+    tree.append(case.Kd, [997])  # N + 4 > max_tokens now
+    tree.route_multi(qbd4, 0.9)
+    with pytest.raises(zha.ZhaError) as ei:
+        tree.attend_multi(qbd4, case.Kd, case.Vd)
+    assert ei.value.status == zha.ZHA_ERR_CAPACITY
 
 
 # --------------------------------------------------------------------------- large-level selection paths

@@ -52,6 +52,11 @@ MUTANTS = [
     ("e4m3_no_subnormals", "step = ldexp(1.0, -9);                 /* subnormal spacing */",
      "step = ldexp(1.0, -6);                 /* subnormal spacing */"),
     ("fp8_scale_not_minimal", "while (ldexp(amax, -s) > 448.0) ++s;", "while (ldexp(amax, -s) > 224.0) ++s;"),
+    ("block_tail_short", "for (int64_t x = Nc; x < E; ++x) in[x] = 1;", "for (int64_t x = Nc; x < E - 1; ++x) in[x] = 1;"),
+    ("block_tail_skips_partial_chunk", "for (int64_t x = Nc; x < E; ++x) in[x] = 1;",
+     "for (int64_t x = N; x < E; ++x) in[x] = 1;"),
+    ("block_tail_to_block_end", "int64_t E = N + t + 1;          /* positions 0 .. N+t may be read */",
+     "int64_t E = N + t + 2;          /* positions 0 .. N+t may be read */"),
     ("attention_one_head", "const double* qh = q + (int64_t)h * d;\n        double mx = -INFINITY;\n        for (int64_t i = 0; i < nS; ++i) {",
      "const double* qh = q;\n        double mx = -INFINITY;\n        for (int64_t i = 0; i < nS; ++i) {"),
 ]
