@@ -79,10 +79,11 @@ void free_tree(zha_tree* t) {
     if (t->b[l]) (void)hipFree(t->b[l]);
     if (t->ms[l]) (void)hipFree(t->ms[l]);
     if (t->kept[l]) (void)hipFree(t->kept[l]);
+    if (t->krank[l]) (void)hipFree(t->krank[l]);
   }
   void* ps[] = {t->refs,   t->spine,  t->sub_lse, t->sub_m,  t->counts,    t->geo,      t->scores,   t->spart,    t->keys,     t->apart,
                 t->fh_cnt, t->fh_mass,  t->fh_edge,  t->cut,      t->sel_cand, t->sel_ctr, t->lb_status,
-                t->lb_epoch, t->lb_error};
+                t->lb_epoch, t->lb_error, t->route_ctr};
   for (void* p : ps)
     if (p) (void)hipFree(p);
   for (int i = 0; i < 2 * ZHA_MAX_TIMING; ++i)
@@ -201,15 +202,26 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
       score_n = std::max(score_n, (size_t)ru * ((Gr + 3) & ~3));
       cand_n = std::max(cand_n, zha_sel_cand_entries(ru));
       ctr_n = std::max(ctr_n, zha_sel_ctr_words(ru));
+      const int ts = zha_union_queries(R, G, tq, hr);
+      if (ts > 0) {  // union scoring: partials of every unit for each workgroup of its group
+        const int ng = U * ((tq + ts - 1) / ts);
+        spart_n = std::max(spart_n, (size_t)ru * zha_score_wgs_units(ng) * Gr * 2);
+      }
     }
   }
+  // kept ranks for union routes: some route this tree may serve groups several units
+  bool uni = false;
+  for (int i = 0; i < (desc->per_head_routes ? 2 : 1); ++i)
+    for (int tq = 1; tq <= maxq; ++tq) uni = uni || zha_union_queries(R, G, tq, hrs[i]) > 0;
   bool ok = true;
   for (int l = 1; l <= L && ok; ++l) {
     ok = ok && dalloc(t, &t->m[l], (size_t)U * t->cap[l] * R * d * (t->f8 ? 1 : t->esize));
     ok = ok && dalloc(t, &t->b[l], (size_t)U * t->cap[l] * R * sizeof(float));
     if (t->f8) ok = ok && dalloc(t, &t->ms[l], (size_t)U * t->cap[l] * R * sizeof(float));
     ok = ok && dalloc(t, &t->kept[l], (size_t)RUmax * t->cap[l] * sizeof(int32_t));
+    if (uni) ok = ok && dalloc(t, &t->krank[l], (size_t)RUmax * t->cap[l] * sizeof(unsigned long long));
   }
+  if (uni) ok = ok && dalloc(t, &t->route_ctr, sizeof(uint32_t));
   ok = ok && dalloc(t, &t->refs, (size_t)desc->n_kv_heads * R * d * sizeof(float));
   ok = ok && dalloc(t, &t->spine, (size_t)U * zha_spine_bytes(L, d, R));
   t->S = subtree_level(t->C, L);
@@ -243,6 +255,10 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
          hipMemset(t->geo, 0, (size_t)(L + 2) * desc->batch * sizeof(int32_t)) == hipSuccess &&
          hipMemset(t->lb_status, 0, (size_t)RUmax * nchunk * sizeof(unsigned long long)) == hipSuccess &&
          hipMemset(t->lb_error, 0, sizeof(int32_t)) == hipSuccess;
+    // kept ranks carry the stamp of the route that wrote them; stamps start at 1
+    for (int l = 1; l <= L && ok && uni; ++l)
+      ok = hipMemset(t->krank[l], 0, (size_t)RUmax * t->cap[l] * sizeof(unsigned long long)) == hipSuccess;
+    if (uni) ok = ok && hipMemset(t->route_ctr, 0, sizeof(uint32_t)) == hipSuccess;
     // every unit's epoch starts at 1: status words of epoch 0 (all-zero memory) never match
     std::vector<uint32_t> ep((size_t)RUmax * 2, 0u);
     for (int u = 0; u < RUmax; ++u) ep[(size_t)u * 2] = 1u;

@@ -197,6 +197,9 @@ struct zha_tree {
   float* ms[ZHA_MAX_LEVELS + 2];    // fp8 summaries: power-of-two scale of each m row [U][cap][R] (else null)
   bool f8;                          // m stored as fp8 e4m3 codes
   int32_t* kept[ZHA_MAX_LEVELS + 2];// per-level kept ids [U][cap]
+  unsigned long long* krank[ZHA_MAX_LEVELS + 2];  // union routes: per-level (stamp << 32) | rank in the
+                                    // unit's kept list, by node id [RUmax][cap] (null: no union routes)
+  uint32_t* route_ctr;              // [1] stamp of the current union route (advanced on the device)
   float* refs;                      // [Hkv][R][d]
   float* spine;                     // [U][L+1][R*16][E+2] open-node accumulators
   int S;                            // subtree level of the build (highest level of <= 256 tokens)
@@ -256,4 +259,7 @@ hipError_t zha_launch_decode_fp8(const uint8_t* codes, const float* scale, int64
                                  hipStream_t s);
 int zha_sparse_wgs(int U);
 int zha_score_wgs_units(int RU);  // score workgroups per routing unit (before the level's own cap)
+// Union scoring of a route with Tq queries per sequence and hr units per (query, KV head):
+// queries per group (0: no union scoring) and groups per (sequence, KV head).
+int zha_union_queries(int R, int Gq, int Tq, int hr);
 int zha_dense_wgs(int U);

@@ -139,11 +139,19 @@ struct ScoreArgs {
   float* scores;          // [U][cap1][G]
   int64_t cap1;
   float* part;            // [U][W][G][2]: (max, sum exp) of the workgroup's scores per head
-  int W;                  // workgroups per unit
+  int W;                  // workgroups per unit (per group of units when scoring unions)
   int G;                  // query heads per routing unit
   int hr;                 // routing units per (query, KV head): 1, or Gq when each head is routed alone
   int Hkv, Tq;            // KV heads; queries per sequence
   float scale;
+  // Union scoring: one row of workgroups per group of the routing units that share one
+  // (sequence, KV head): the hr units of each of TS consecutive queries (TS * Gq <= 16
+  // matrix columns).  A node is scored once for every column; a unit keeps the scores of
+  // the nodes of its own frontier.
+  const u64* krank;       // [RU][cap_parent]: the parent level's kept nodes, (stamp << 32) | rank in
+                          // the unit's kept list; null at the top level (every node is a member)
+  uint32_t* route_ctr;    // route stamp; the top level's first workgroup advances it
+  int TS, NTC;            // queries per group; groups per (sequence, KV head)
 };
 
 // Eight fp8 e4m3 codes (two dwords) as eight bf16 values (exact), by the hardware
@@ -170,7 +178,11 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 // codes; lane (row, group) loads its row's d/4 contiguous codes, decodes them to bf16 in
 // registers, and the query fragments take the same k order (the dot product does not
 // depend on it); the row's scale multiplies the product.
-template <typename T, int R, int D, int UN, bool F8>
+// UNI (R >= 4): the workgroup row scores the union of the frontiers of a group of routing
+// units in node-id order; column c is head j of unit cu(c); a node is loaded when some
+// column's unit has its parent kept (a stamped rank entry), and each column keeps the
+// scores of its unit's member nodes at the unit's frontier positions.
+template <typename T, int R, int D, int UN, bool F8, bool UNI>
 __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
   typedef Mf<T> M;
   constexpr int NK = D / M::KPER;
@@ -178,28 +190,54 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
   constexpr int NPT = 16 / R;
   constexpr int SUPER = 4 * UN * NPT;
   static_assert(!F8 || M::EPL == 8, "fp8 planes feed the bf16 matrix instruction");
+  static_assert(!UNI || R >= 4, "union scoring keeps one node per lane group");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, grp = lane >> 4;
-  // u: routing unit (frontier, scores, partials); up: its (sequence, KV head) unit (planes)
-  const int u = blockIdx.y, up = plane_unit(u, a.hr, a.Hkv, a.Tq);
   const int G = a.G;
-  const int nF = frontier_size(a.v, u);
+  // u: routing unit (frontier, scores, partials) of this lane's column; up: its (sequence,
+  // KV head) unit (planes); qrow: the column's query row; colok: the column is a query head
+  int u, up, qrow, jcol, end;
+  bool colok;
+  if constexpr (UNI) {
+    up = blockIdx.y / a.NTC;
+    const int tc = blockIdx.y - up * a.NTC, bi = up / a.Hkv, g = up - bi * a.Hkv;
+    const int per_t = a.hr * G;  // columns per query
+    const int tt = row / per_t, h = (row / G) % a.hr, t = tc * a.TS + tt;
+    colok = tt < a.TS && t < a.Tq;
+    u = ((bi * a.Tq + min(t, a.Tq - 1)) * a.Hkv + g) * a.hr + h;
+    jcol = row % G;
+    qrow = u * G + jcol;
+    end = a.v.nodes[bi];
+    if (a.route_ctr && !a.krank && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+      // top level of a route: a new stamp, so kept ranks written by earlier routes stop matching
+      const uint32_t s0 = __hip_atomic_load(a.route_ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.route_ctr, s0 + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {
+    u = blockIdx.y;
+    up = plane_unit(u, a.hr, a.Hkv, a.Tq);
+    colok = row < G;
+    jcol = row;
+    qrow = u * G + row;
+    end = frontier_size(a.v, u);
+  }
+  const uint32_t stamp = (UNI && a.krank) ? a.route_ctr[0] : 0u;
   // Super-tiles are dealt to the workgroups in turn: at any moment the unit's workgroups
   // read neighbouring addresses, sweeping the planes in order.
   const int start = blockIdx.x * SUPER;
   const int step = a.W * SUPER;
-  const int end = nF;
 
   typename M::frag qf[NK];
   {
-    const T* qp = (const T*)a.q + ((int64_t)u * G + row) * D;
+    const T* qp = (const T*)a.q + (int64_t)qrow * D;
 #pragma unroll
     for (int s = 0; s < NK; ++s) {
       const int k0 = F8 ? grp * (D / 4) + s * 8 : s * M::KPER + grp * M::EPL;
-      qf[s] = row < G ? M::load(qp + k0) : M::zero();
+      qf[s] = colok ? M::load(qp + k0) : M::zero();
     }
   }
-  const int32_t* par = a.v.parent ? a.v.parent + (int64_t)u * a.v.cap_parent : nullptr;
+  const int32_t* par = (!UNI && a.v.parent) ? a.v.parent + (int64_t)u * a.v.cap_parent : nullptr;
+  const u64* kr = (UNI && a.krank) ? a.krank + (int64_t)u * a.v.cap_parent : nullptr;
   const T* mb = (const T*)a.m + (int64_t)up * a.capl * R * D;
   const uint8_t* m8 = (const uint8_t*)a.m + (int64_t)up * a.capl * R * D;
   const float* bb = a.b + (int64_t)up * a.capl * R;
@@ -210,24 +248,63 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
 
   typedef typename M::frag Frag;
   // Parent entries of this lane's tiles in the super-tile at `base` (the one load a node
-  // id depends on).
-  auto fetch_par = [&](int base, int (&pp)[UN]) {
+  // id depends on).  UNI: the kept-rank entry of the parent of the lane's node (4grp/R)
+  // for the lane's column unit.
+  auto fetch_par = [&](int base, int (&pp)[UN], u64 (&rk)[UN]) {
 #pragma unroll
     for (int k = 0; k < UN; ++k) {
-      const int pos = base + (k * 4 + wave) * NPT + row / R;
-      pp[k] = (par && pos < end) ? par[a.v.Cshift >= 0 ? (pos >> a.v.Cshift) : pos / a.v.C] : 0;
+      if constexpr (UNI) {
+        const int id = base + (k * 4 + wave) * NPT + (4 * grp) / R;
+        const int P = a.v.Cshift >= 0 ? (id >> a.v.Cshift) : id / a.v.C;
+        rk[k] = (kr && colok && id < end) ? kr[P] : 0;
+        pp[k] = 0;
+      } else {
+        const int pos = base + (k * 4 + wave) * NPT + row / R;
+        pp[k] = (par && pos < end) ? par[a.v.Cshift >= 0 ? (pos >> a.v.Cshift) : pos / a.v.C] : 0;
+        rk[k] = 0;
+      }
+    }
+  };
+  // UNI: membership of the lane's node for its column (mem), the node's position in the
+  // column unit's frontier (wpos), and which nodes of each tile some column needs (act).
+  auto members = [&](int base, const u64 (&rk)[UN], bool (&mem)[UN], int (&wpos)[UN], uint32_t (&act)[UN]) {
+#pragma unroll
+    for (int k = 0; k < UN; ++k) {
+      const int id = base + (k * 4 + wave) * NPT + (4 * grp) / R;
+      bool m;
+      int pos;
+      if (kr) {
+        m = colok && id < end && (uint32_t)(rk[k] >> 32) == stamp;
+        const int rank = (int)(uint32_t)rk[k];
+        pos = a.v.Cshift >= 0 ? (rank << a.v.Cshift) + (id & ((1 << a.v.Cshift) - 1)) : rank * a.v.C + id % a.v.C;
+      } else {
+        m = colok && id < end;
+        pos = id;
+      }
+      mem[k] = m;
+      wpos[k] = pos;
+      const u64 bal = __ballot(m);
+      // node n of the tile is handled by lanes [n * 64 / NPT, (n + 1) * 64 / NPT)
+      uint32_t am = 0;
+#pragma unroll
+      for (int n = 0; n < NPT; ++n) {
+        const u64 seg = NPT == 1 ? bal : (bal >> (n * (64 / NPT))) & ((1ull << (64 / NPT)) - 1);
+        am |= seg != 0 ? (1u << n) : 0u;
+      }
+      act[k] = am;
     }
   };
   // Plane fragments and offsets of this lane's tiles in the super-tile at `base`.
-  auto load_stage = [&](int base, const int (&pp)[UN], Frag (&af)[UN][NK], float (&bv)[UN][4]) {
+  auto load_stage = [&](int base, const int (&pp)[UN], const uint32_t (&act)[UN], Frag (&af)[UN][NK],
+                        float (&bv)[UN][4]) {
 #pragma unroll
     for (int k = 0; k < UN; ++k) {
       const int tbk = base + (k * 4 + wave) * NPT;
       const int pos = tbk + row / R;
-      const bool v = pos < end;
+      const bool v = UNI ? ((act[k] >> (row / R)) & 1u) != 0 : pos < end;
       int id = pos;
-      if (par) id = a.v.Cshift >= 0 ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
-                                    : pp[k] * a.v.C + pos % a.v.C;
+      if (!UNI && par) id = a.v.Cshift >= 0 ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
+                                           : pp[k] * a.v.C + pos % a.v.C;
       id = v ? id : 0;
       const T* mp = mb + ((int64_t)id * R + (row % R)) * D + grp * M::EPL;
 #pragma unroll
@@ -235,7 +312,7 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
       if constexpr (R >= 4) {
         // rows 4grp..4grp+3 of this lane belong to one node: its four offsets in one load
         const int id2 = __shfl(id, 4 * grp);
-        const bool v2 = tbk + (4 * grp) / R < end;
+        const bool v2 = UNI ? ((act[k] >> ((4 * grp) / R)) & 1u) != 0 : tbk + (4 * grp) / R < end;
         const float4 b4 = v2 ? *(const float4*)(bb + (int64_t)id2 * R + (4 * grp) % R)
                              : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         bv[k][0] = b4.x; bv[k][1] = b4.y; bv[k][2] = b4.z; bv[k][3] = b4.w;
@@ -250,11 +327,11 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
       }
     }
   };
-  // Scores of the super-tile at `base` from its loaded planes (F8: rs holds the rows'
-  // scales, which multiply the product; unused otherwise).
   // Scores of tile k of the super-tile at `base` from its plane fragments (F8: rs holds the
-  // rows' scales, which multiply the product; unused otherwise).
-  auto score_tile = [&](int k, const Frag (&afk)[NK], const float (&bvk)[4], const float (&rs)[4], int base) {
+  // rows' scales, which multiply the product; unused otherwise).  UNI: the lane writes for
+  // its column when its node is a member, at the column unit's frontier position.
+  auto score_tile = [&](int k, const Frag (&afk)[NK], const float (&bvk)[4], const float (&rs)[4], int base,
+                        bool memk, int wposk) {
     const int tbk = base + (k * 4 + wave) * NPT;
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -271,9 +348,10 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
       if (R >= 8) mx = fmaxf(mx, __shfl_xor(mx, 16));
       if (R >= 16) mx = fmaxf(mx, __shfl_xor(mx, 32));
       const bool writer = (R == 4) || (R == 8 && (grp & 1) == 0) || (R == 16 && grp == 0);
-      const int pos = tbk + (4 * grp) / R;
-      if (writer && row < G && pos < end) {
-        sc[(int64_t)pos * GS + row] = mx;
+      const int pos = UNI ? wposk : tbk + (4 * grp) / R;
+      const bool ok = UNI ? memk : (colok && pos < end);
+      if (writer && ok) {
+        sc[(int64_t)pos * GS + jcol] = mx;
         lse_push(runM, runS, mx);
       }
     } else if (R == 2) {
@@ -281,8 +359,8 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
       for (int h2 = 0; h2 < 2; ++h2) {
         const float mx = fmaxf(v[2 * h2], v[2 * h2 + 1]);
         const int pos = tbk + 2 * grp + h2;
-        if (row < G && pos < end) {
-          sc[(int64_t)pos * GS + row] = mx;
+        if (colok && pos < end) {
+          sc[(int64_t)pos * GS + jcol] = mx;
           lse_push(runM, runS, mx);
         }
       }
@@ -290,36 +368,37 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int pos = tbk + 4 * grp + jj;
-        if (row < G && pos < end) {
-          sc[(int64_t)pos * GS + row] = v[jj];
+        if (colok && pos < end) {
+          sc[(int64_t)pos * GS + jcol] = v[jj];
           lse_push(runM, runS, v[jj]);
         }
       }
     }
   };
 
-  auto compute = [&](const Frag (&af)[UN][NK], const float (&bv)[UN][4], int base) {
+  auto compute = [&](const Frag (&af)[UN][NK], const float (&bv)[UN][4], int base, const bool (&mem)[UN],
+                     const int (&wpos)[UN]) {
 #pragma unroll
-    for (int k = 0; k < UN; ++k) score_tile(k, af[k], bv[k], bv[k], base);
+    for (int k = 0; k < UN; ++k) score_tile(k, af[k], bv[k], bv[k], base, mem[k], wpos[k]);
   };
   // F8: codes, offsets and scales of this lane's tiles in the super-tile at `base`.
-  auto load_stage8 = [&](int base, const int (&pp)[UN], uint4 (&rw)[UN][NR], float (&bv)[UN][4],
-                         float (&sv)[UN][4]) {
+  auto load_stage8 = [&](int base, const int (&pp)[UN], const uint32_t (&act)[UN], uint4 (&rw)[UN][NR],
+                         float (&bv)[UN][4], float (&sv)[UN][4]) {
 #pragma unroll
     for (int k = 0; k < UN; ++k) {
       const int tbk = base + (k * 4 + wave) * NPT;
       const int pos = tbk + row / R;
-      const bool v = pos < end;
+      const bool v = UNI ? ((act[k] >> (row / R)) & 1u) != 0 : pos < end;
       int id = pos;
-      if (par) id = a.v.Cshift >= 0 ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
-                                    : pp[k] * a.v.C + pos % a.v.C;
+      if (!UNI && par) id = a.v.Cshift >= 0 ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
+                                           : pp[k] * a.v.C + pos % a.v.C;
       id = v ? id : 0;
       const uint8_t* cp = m8 + ((int64_t)id * R + (row % R)) * D + grp * (D / 4);
 #pragma unroll
       for (int i = 0; i < NR; ++i) rw[k][i] = v ? *(const uint4*)(cp + 16 * i) : make_uint4(0u, 0u, 0u, 0u);
       if constexpr (R >= 4) {
         const int id2 = __shfl(id, 4 * grp);
-        const bool v2 = tbk + (4 * grp) / R < end;
+        const bool v2 = UNI ? ((act[k] >> ((4 * grp) / R)) & 1u) != 0 : tbk + (4 * grp) / R < end;
         const int64_t o = (int64_t)id2 * R + (4 * grp) % R;
         const float4 b4 = v2 ? *(const float4*)(bb + o) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         const float4 s4 = v2 ? *(const float4*)(sb + o) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -340,7 +419,8 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
   };
   // F8: decode the codes (lane k-slots s*8 .. s*8+7 of its d/4 codes per matrix step),
   // then score as the bf16 path does with the row scale in the multiplier.
-  auto compute8 = [&](const uint4 (&rw)[UN][NR], const float (&bv)[UN][4], const float (&sv)[UN][4], int base) {
+  auto compute8 = [&](const uint4 (&rw)[UN][NR], const float (&bv)[UN][4], const float (&sv)[UN][4], int base,
+                      const bool (&mem)[UN], const int (&wpos)[UN]) {
     if constexpr (F8) {
 #pragma unroll
       for (int k = 0; k < UN; ++k) {
@@ -350,7 +430,7 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
           const uint4 q4 = rw[k][s / 2];
           afk[s] = (s & 1) ? fp8x8_to_bf16(q4.z, q4.w) : fp8x8_to_bf16(q4.x, q4.y);
         }
-        score_tile(k, afk, bv[k], sv[k], base);
+        score_tile(k, afk, bv[k], sv[k], base, mem[k], wpos[k]);
       }
     }
   };
@@ -359,40 +439,49 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
   // the next and the parent entries of the one after are in flight.  The two register
   // buffers alternate by unrolling the loop twice.
   int ppA[UN], ppB[UN];
+  u64 rkA[UN], rkB[UN];
+  bool mA[UN], mB[UN];
+  int wA[UN], wB[UN];
+  uint32_t acA[UN], acB[UN];
   float bvA[UN][4], bvB[UN][4];
-  fetch_par(start, ppA);
-  fetch_par(start + step, ppB);
+  fetch_par(start, ppA, rkA);
+  fetch_par(start + step, ppB, rkB);
+  if constexpr (UNI) members(start, rkA, mA, wA, acA);
   if constexpr (F8) {
     uint4 rwA[UN][NR], rwB[UN][NR];
     float svA[UN][4], svB[UN][4];
-    if (start < end) load_stage8(start, ppA, rwA, bvA, svA);
+    if (start < end) load_stage8(start, ppA, acA, rwA, bvA, svA);
     for (int base = start; base < end;) {
-      fetch_par(base + 2 * step, ppA);
-      load_stage8(base + step, ppB, rwB, bvB, svB);
-      compute8(rwA, bvA, svA, base);
+      if constexpr (UNI) members(base + step, rkB, mB, wB, acB);
+      fetch_par(base + 2 * step, ppA, rkA);
+      load_stage8(base + step, ppB, acB, rwB, bvB, svB);
+      compute8(rwA, bvA, svA, base, mA, wA);
       base += step;
       if (base >= end) break;
-      fetch_par(base + 2 * step, ppB);
-      load_stage8(base + step, ppA, rwA, bvA, svA);
-      compute8(rwB, bvB, svB, base);
+      if constexpr (UNI) members(base + step, rkA, mA, wA, acA);
+      fetch_par(base + 2 * step, ppB, rkB);
+      load_stage8(base + step, ppA, acA, rwA, bvA, svA);
+      compute8(rwB, bvB, svB, base, mB, wB);
       base += step;
     }
   } else {
     Frag afA[UN][NK], afB[UN][NK];
-    if (start < end) load_stage(start, ppA, afA, bvA);
+    if (start < end) load_stage(start, ppA, acA, afA, bvA);
     for (int base = start; base < end;) {
-      fetch_par(base + 2 * step, ppA);
-      load_stage(base + step, ppB, afB, bvB);
-      compute(afA, bvA, base);
+      if constexpr (UNI) members(base + step, rkB, mB, wB, acB);
+      fetch_par(base + 2 * step, ppA, rkA);
+      load_stage(base + step, ppB, acB, afB, bvB);
+      compute(afA, bvA, base, mA, wA);
       base += step;
       if (base >= end) break;
-      fetch_par(base + 2 * step, ppB);
-      load_stage(base + step, ppA, afA, bvA);
-      compute(afB, bvB, base);
+      if constexpr (UNI) members(base + step, rkA, mA, wA, acA);
+      fetch_par(base + 2 * step, ppB, rkB);
+      load_stage(base + step, ppA, acA, afA, bvA);
+      compute(afB, bvB, base, mB, wB);
       base += step;
     }
   }
-  // per-head (max, sum exp) of this workgroup: lanes of one head, then the 4 waves
+  // per-column (max, sum exp) of this workgroup: lanes of one column, then the 4 waves
   {
     float M2 = __shfl_xor(runM, 16), S2 = __shfl_xor(runS, 16);
     lse_merge(runM, runS, M2, S2);
@@ -401,12 +490,15 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
     lse_merge(runM, runS, M2, S2);
   }
   __shared__ float sM[4][16], sS[4][16];
+  __shared__ int sU[16], sJ[16];
+  __shared__ bool sOk[16];
   if (grp == 0) { sM[wave][row] = runM; sS[wave][row] = runS; }
+  if (wave == 0 && grp == 0) { sU[row] = u; sJ[row] = jcol; sOk[row] = colok; }
   __syncthreads();
-  if (threadIdx.x < G) {
+  if (threadIdx.x < 16 && sOk[threadIdx.x]) {
     float Mx = sM[0][threadIdx.x], Sx = sS[0][threadIdx.x];
     for (int w = 1; w < 4; ++w) lse_merge(Mx, Sx, sM[w][threadIdx.x], sS[w][threadIdx.x]);
-    float* pp = a.part + (((int64_t)u * a.W + blockIdx.x) * G + threadIdx.x) * 2;
+    float* pp = a.part + (((int64_t)sU[threadIdx.x] * a.W + blockIdx.x) * G + sJ[threadIdx.x]) * 2;
     pp[0] = Mx;
     pp[1] = Sx;
   }
@@ -846,6 +938,8 @@ struct SmallArgs {
   int G;
   float p;
   int keep_all;
+  u64* krank;             // union routes: [U][capl] (stamp << 32) | rank of each kept node; else null
+  const uint32_t* route_ctr;  // the route's stamp
 };
 
 constexpr int SBATCH = 8;     // frontier positions per thread per load batch
@@ -871,6 +965,7 @@ __global__ __launch_bounds__(ST) void zha_select_small_kernel(SmallArgs a) {
   const int nmax = (int)a.capl;  // >= 1
   const int nF = frontier_size(a.v, u);
   const int nchild = a.next_nF ? child_nodes(a.v, u) : 0;  // loaded now, used at the end
+  const uint32_t stamp = a.krank ? a.route_ctr[0] : 0u;
   const int GS = score_stride(G);
   const float* sc = a.scores + (int64_t)u * a.cap1 * GS;
   const int32_t* gpar = a.v.parent ? a.v.parent + (int64_t)u * a.v.cap_parent : nullptr;
@@ -970,6 +1065,7 @@ __global__ __launch_bounds__(ST) void zha_select_small_kernel(SmallArgs a) {
   }
   // compaction in position order (chunks of 4 positions per thread)
   int32_t* kept = a.kept + (int64_t)u * a.capl;
+  u64* kr = a.krank ? a.krank + (int64_t)u * a.capl : nullptr;
   const int32_t* par = gpar ? sh.par : nullptr;
   uint32_t kept_base = 0;
   for (int base = 0; base < nF; base += ST * 4) {
@@ -989,6 +1085,7 @@ __global__ __launch_bounds__(ST) void zha_select_small_kernel(SmallArgs a) {
     for (int e = 0; e < 4; ++e) {
       if ((flags >> e) & 1u) {
         const int id = frontier_id(par, p0 + e, a.v.C, a.v.Cshift);
+        if (kr) kr[id] = ((u64)stamp << 32) | out;
         kept[out++] = id;
         if (p0 + e == nF - 1) sh.last_kept_id = id + 1;  // the frontier's last node is kept
       }
@@ -1371,6 +1468,8 @@ struct CompactArgs {
   int32_t* kept_count;
   int32_t* next_nF;       // null at level 1
   int32_t* lb_error;      // set when a look-back wait gives up (never expected)
+  u64* krank;             // union routes: [U][capl] (stamp << 32) | rank of each kept node; else null
+  const uint32_t* route_ctr;  // the route's stamp
 };
 
 constexpr int CPT = 256;  // compaction threads
@@ -1449,6 +1548,7 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
     compact_epilogue(a);
     return;
   }
+  const uint32_t stamp = a.krank ? a.route_ctr[0] : 0u;
   const bool keep_all = a.keep_all || a.cut[u * 4 + 2] != 0;
   const uint32_t tau = (uint32_t)a.cut[u * 4 + 0];
   const int tie_last = a.cut[u * 4 + 1];
@@ -1492,9 +1592,11 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
   __syncthreads();
   uint32_t out = s_before + ex;
   int32_t* kept = a.kept + (int64_t)u * a.capl;
+  u64* kr = a.krank ? a.krank + (int64_t)u * a.capl : nullptr;
 #pragma unroll
   for (int e = 0; e < CPP; ++e) {
     if ((flags >> e) & 1u) {
+      if (kr) kr[id[e]] = ((u64)stamp << 32) | out;
       kept[out++] = id[e];
       if (p0 + e == nF - 1) s_last_kept = id[e] + 1;  // the frontier's last node is kept
     }
@@ -1518,20 +1620,28 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
 
 // Two tiles per wave per pipeline stage (for fp8 codes too: four would not fit in the
 // registers of four workgroups per compute unit, and fewer workgroups measured slower).
-template <typename T, int R, int D, bool F8>
-hipError_t launch_score(const ScoreArgs& a, int W, int U, hipStream_t s) {
-  hipLaunchKernelGGL((zha_score_kernel<T, R, D, 2, F8>), dim3(W, U), dim3(256), 0, s, a);
+template <typename T, int R, int D, bool F8, bool UNI>
+hipError_t launch_score(const ScoreArgs& a, int W, int rows, hipStream_t s) {
+  hipLaunchKernelGGL((zha_score_kernel<T, R, D, 2, F8, UNI>), dim3(W, rows), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
+// rows: routing units, or groups of them (uni; R >= 4 there)
 template <typename T, int D, bool F8 = false>
-hipError_t launch_score_r(const ScoreArgs& a, int R, int W, int U, hipStream_t s) {
+hipError_t launch_score_r(const ScoreArgs& a, int R, int W, int rows, bool uni, hipStream_t s) {
+  if (uni) {
+    switch (R) {
+      case 4: return launch_score<T, 4, D, F8, true>(a, W, rows, s);
+      case 8: return launch_score<T, 8, D, F8, true>(a, W, rows, s);
+      default: return launch_score<T, 16, D, F8, true>(a, W, rows, s);
+    }
+  }
   switch (R) {
-    case 1: return launch_score<T, 1, D, F8>(a, W, U, s);
-    case 2: return launch_score<T, 2, D, F8>(a, W, U, s);
-    case 4: return launch_score<T, 4, D, F8>(a, W, U, s);
-    case 8: return launch_score<T, 8, D, F8>(a, W, U, s);
-    default: return launch_score<T, 16, D, F8>(a, W, U, s);
+    case 1: return launch_score<T, 1, D, F8, false>(a, W, rows, s);
+    case 2: return launch_score<T, 2, D, F8, false>(a, W, rows, s);
+    case 4: return launch_score<T, 4, D, F8, false>(a, W, rows, s);
+    case 8: return launch_score<T, 8, D, F8, false>(a, W, rows, s);
+    default: return launch_score<T, 16, D, F8, false>(a, W, rows, s);
   }
 }
 
@@ -1560,6 +1670,18 @@ int zha_score_wgs(const zha_tree* t, int level) {
   return (int)w;
 }
 
+// Union scoring groups the routing units that share one (sequence, KV head): the hr units of
+// each of TS consecutive queries, TS * Gq <= 16 columns of the matrix tile.  Only worth it
+// (and only built) when a group holds several units and a tile row holds one node's planes
+// for one lane group (R >= 4).
+int zha_union_queries(int R, int Gq, int Tq, int hr) {
+  if (R < 4 || Gq < 1 || Gq > 16) return 0;
+  int ts = 16 / Gq;
+  if (ts > Tq) ts = Tq;
+  if (ts < 1) ts = 1;
+  return ts * hr > 1 ? ts : 0;
+}
+
 int zha_compact_chunks(int64_t nodes) { return (int)((nodes + CH - 1) / CH); }
 int zha_hist_bins() { return NB; }
 int64_t zha_sel_cand_entries(int U) { return (int64_t)U * sel_regions(U) * LCAND; }
@@ -1573,6 +1695,11 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
   int32_t* cntF = t->counts;                         // [L+2][U]
   int32_t* cntK = t->counts + (int64_t)(L + 2) * U;  // [L+2][U]
   const bool keep_all = p >= 1.0f;
+  // union scoring: groups of the units sharing one (sequence, KV head), TS queries each
+  const int TS = zha_union_queries(t->R, t->G, t->Tq, t->hr);
+  const bool uni = TS > 0 && t->krank[1] != nullptr;
+  const int NTC = uni ? (t->Tq + TS - 1) / TS : 1;
+  const int rows = uni ? t->U * NTC : U;  // rows of the scoring grid
   hipError_t e;
   for (int l = L; l >= 1; --l) {
     Level v;
@@ -1596,7 +1723,17 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     sa.scores = t->scores;
     sa.cap1 = t->cap[1];
     sa.part = t->spart;
-    sa.W = zha_score_wgs(t, l);
+    if (uni) {
+      int64_t w = (t->cap[l] + 7) / 8;
+      const int wr = zha_score_wgs_units(rows);
+      sa.W = (int)(w < 1 ? 1 : (w > wr ? wr : w));
+    } else {
+      sa.W = zha_score_wgs(t, l);
+    }
+    sa.krank = uni && l < L ? t->krank[l + 1] : nullptr;
+    sa.route_ctr = uni ? t->route_ctr : nullptr;
+    sa.TS = TS;
+    sa.NTC = NTC;
     sa.G = Gr;
     sa.hr = t->hr;
     sa.Hkv = t->desc.n_kv_heads;
@@ -1604,12 +1741,14 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     sa.scale = scale;
     zha_time_begin(t, s, ZHA_K_SCORE, l);
     if (t->f8)
-      e = t->d == 64 ? launch_score_r<__bf16, 64, true>(sa, t->R, sa.W, U, s)
-                     : launch_score_r<__bf16, 128, true>(sa, t->R, sa.W, U, s);
+      e = t->d == 64 ? launch_score_r<__bf16, 64, true>(sa, t->R, sa.W, rows, uni, s)
+                     : launch_score_r<__bf16, 128, true>(sa, t->R, sa.W, rows, uni, s);
     else if (t->desc.dtype == ZHA_BF16)
-      e = t->d == 64 ? launch_score_r<__bf16, 64>(sa, t->R, sa.W, U, s) : launch_score_r<__bf16, 128>(sa, t->R, sa.W, U, s);
+      e = t->d == 64 ? launch_score_r<__bf16, 64>(sa, t->R, sa.W, rows, uni, s)
+                     : launch_score_r<__bf16, 128>(sa, t->R, sa.W, rows, uni, s);
     else
-      e = t->d == 64 ? launch_score_r<float, 64>(sa, t->R, sa.W, U, s) : launch_score_r<float, 128>(sa, t->R, sa.W, U, s);
+      e = t->d == 64 ? launch_score_r<float, 64>(sa, t->R, sa.W, rows, uni, s)
+                     : launch_score_r<float, 128>(sa, t->R, sa.W, rows, uni, s);
     if (e != hipSuccess) return e;
     zha_time_end(t, s, ZHA_K_SCORE, l);
 
@@ -1629,6 +1768,8 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
       sm.G = Gr;
       sm.p = p;
       sm.keep_all = keep_all ? 1 : 0;
+      sm.krank = uni ? t->krank[l] : nullptr;
+      sm.route_ctr = t->route_ctr;
       zha_time_begin(t, s, ZHA_K_SELECT, l);
       hipLaunchKernelGGL(zha_select_small_kernel, dim3(U), dim3(ST), 0, s, sm);
       e = hipGetLastError();
@@ -1691,6 +1832,8 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     ca.kept_count = cntK + (int64_t)l * U;
     ca.next_nF = next_nF;
     ca.lb_error = t->lb_error;
+    ca.krank = uni ? t->krank[l] : nullptr;
+    ca.route_ctr = t->route_ctr;
     const int nch = zha_compact_chunks(t->cap[l]);
     zha_time_begin(t, s, ZHA_K_COMPACT, l);
     hipLaunchKernelGGL(zha_compact_kernel, dim3(nch, U), dim3(CPT), 0, s, ca);
