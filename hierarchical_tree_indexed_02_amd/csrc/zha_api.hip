@@ -206,6 +206,7 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
       if (ts > 0) {  // union scoring: partials of every unit for each workgroup of its group
         const int ng = U * ((tq + ts - 1) / ts);
         spart_n = std::max(spart_n, (size_t)ru * zha_score_wgs_units(ng) * Gr * 2);
+        apart_n = std::max(apart_n, (size_t)ru * zha_sparse_wgs(ng) * Gr * (d + 2));
       }
     }
   }

@@ -36,6 +36,13 @@ struct AttArgs {
   int64_t T;               // token stride of K/V
   float scale_log2;        // scale * log2(e)
   const int32_t* lens;     // sparse: sequence lengths [B] on the device (the tree's geometry row 0)
+  // Union attention: one row of workgroups per group of routing units sharing one (sequence,
+  // KV head) (the hr units of TS consecutive queries, at most 16 query heads in all).  The
+  // group's tokens are read once, in order, and each query head's softmax takes the tokens
+  // of its unit's set only.
+  const u64* krank;        // level-1 kept ranks [U][cap1]: (stamp << 32) | rank, by chunk id
+  const uint32_t* route_ctr;  // the last route's stamp
+  int TS, NTC;             // queries per group; groups per (sequence, KV head)
 };
 
 // Dense launches take the lengths by value (the dense entry point gets them from the host);
@@ -202,10 +209,11 @@ template <int D> struct PV<float, D> {
   }
 };
 
-template <typename T, int D, bool DENSE>
+template <typename T, int D, bool DENSE, bool UNI>
 __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENSE> la) {
   typedef Mf<T> M;
   typedef PV<T, D> PVT;
+  constexpr bool TD = DENSE || UNI;  // positions are tokens
   constexpr int NK = D / M::KPER;
   constexpr int ND = D / 16;
   constexpr int LDS_WAVE = PVT::LDS_ELEMS > 0 ? PVT::LDS_ELEMS : 1;
@@ -218,9 +226,37 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
   const int row = lane & 15, grp = lane >> 4;
   // u: routing unit, of G query heads; up: its (sequence, KV head) unit.  Units are numbered
   // (sequence, query, KV head, head group), so the unit's first query head is u * G.
-  const int u = blockIdx.y, up = plane_unit(u, a.hr, a.Hkv, a.Tq), bi = up / a.Hkv;
+  // UNI: lane column `row` is head jcol of unit u; the group reads tokens [0, end) and a
+  // column takes token 0, the tokens of its unit's kept chunks and its tail [Nc, Ne).
   const int G = a.G;
-  const Positions P = unit_positions<DENSE>(a, la, u, bi);
+  int u, up, bi, jcol, Ne = 0, Nc = 0;
+  bool colok;
+  Positions P;
+  if constexpr (UNI) {
+    up = blockIdx.y / a.NTC;
+    const int tc = blockIdx.y - up * a.NTC, g = up % a.Hkv;
+    bi = up / a.Hkv;
+    const int per_t = a.hr * G;
+    const int tt = row / per_t, h = (row / G) % a.hr, tq = tc * a.TS + tt;
+    colok = tt < a.TS && tq < a.Tq;
+    u = ((bi * a.Tq + min(tq, a.Tq - 1)) * a.Hkv + g) * a.hr + h;
+    jcol = row % G;
+    const int N = a.lens[bi];
+    Nc = (N / a.C) * a.C;
+    Ne = a.qtail ? N + min(tq, a.Tq - 1) + 1 : N;
+    const int tlast = min(tc * a.TS + a.TS, a.Tq) - 1;  // the group's last query
+    const int Nend = a.qtail ? N + tlast + 1 : N;
+    P.P = Nend; P.nx = Nend; P.sink = 0; P.Nc = 0; P.nK = 0; P.kp = nullptr;
+  } else {
+    u = blockIdx.y;
+    up = plane_unit(u, a.hr, a.Hkv, a.Tq);
+    bi = up / a.Hkv;
+    colok = row < G;
+    jcol = row;
+    P = unit_positions<DENSE>(a, la, u, bi);
+  }
+  const u64* kr1 = UNI ? a.krank + (int64_t)u * a.cap1 : nullptr;
+  const uint32_t stamp = UNI ? a.route_ctr[0] : 0u;
   // Blocks of 4 * ATT_STEP positions are dealt to the workgroups in turn, so the unit's
   // workgroups read neighbouring K/V rows at any moment.
   constexpr int WSTEP = 4 * ATT_STEP;
@@ -234,9 +270,9 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
 
   typename M::frag qf[NK];
   {
-    const T* qp = (const T*)a.q + ((int64_t)u * G + row) * D + grp * M::EPL;
+    const T* qp = (const T*)a.q + ((int64_t)u * G + jcol) * D + grp * M::EPL;
 #pragma unroll
-    for (int s = 0; s < NK; ++s) qf[s] = row < G ? M::load(qp + s * M::KPER) : M::zero();
+    for (int s = 0; s < NK; ++s) qf[s] = colok ? M::load(qp + s * M::KPER) : M::zero();
   }
   T* lds = (T*)smem + wave * LDS_WAVE;
 
@@ -247,7 +283,7 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
 
   // One window: K rows of the two 16-token tiles (lane row r -> position p0 + 16t + r) and
   // the V tile, loaded into registers.
-  auto load_kv = [&](typename M::frag (&kf)[2][NK], typename PVT::vfrag& vf, const Window<DENSE>& win, int p0) {
+  auto load_kv = [&](typename M::frag (&kf)[2][NK], typename PVT::vfrag& vf, const Window<TD>& win, int p0) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int tok = win.token(P, p0, p0 + 16 * t + row, end, a.C, a.Cshift);
@@ -255,10 +291,37 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
 #pragma unroll
       for (int s = 0; s < NK; ++s) kf[t][s] = M::load_stream(kr + s * M::KPER);
     }
-    PVT::template load<DENSE>(vf, Vb, P, win, p0, end, a.C, a.Cshift, lane);
+    PVT::template load<TD>(vf, Vb, P, win, p0, end, a.C, a.Cshift, lane);
+  };
+  // UNI: kept-rank entries of the chunks of this lane's tokens p0 + 16t + 4grp + jj (one
+  // per 4 tokens when C is a power of two >= 4), for the lane's column unit.
+  auto fetch_rank = [&](int p0, u64 (&rk)[2][4]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int tok = p0 + 16 * t + 4 * grp + jj;
+        const bool need = colok && tok < Nc && (jj == 0 || a.Cshift < 2);
+        const int k = a.Cshift >= 0 ? (tok >> a.Cshift) : tok / a.C;
+        rk[t][jj] = need ? kr1[k] : 0;
+      }
+  };
+  // UNI: bit 4t + jj: token p0 + 16t + 4grp + jj is in the column's set
+  auto member_bits = [&](int p0, const u64 (&rk)[2][4]) {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int tok = p0 + 16 * t + 4 * grp + jj;
+        const u64 r = a.Cshift >= 2 ? rk[t][0] : rk[t][jj];
+        const bool in = colok && (tok < Nc ? (tok == 0 || (uint32_t)(r >> 32) == stamp) : tok < Ne);
+        bits |= in ? (1u << (4 * t + jj)) : 0u;
+      }
+    return bits;
   };
   // Online-softmax update with one loaded window.
-  auto compute = [&](const typename M::frag (&kf)[2][NK], const typename PVT::vfrag& vf, int p0) {
+  auto compute = [&](const typename M::frag (&kf)[2][NK], const typename PVT::vfrag& vf, int p0, uint32_t bits) {
     // S^T = K Q^T: lane holds tokens 16t + 4grp + jj for head `row`
     float z[2][4];
 #pragma unroll
@@ -269,7 +332,8 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int p = p0 + 16 * t + 4 * grp + jj;
-        z[t][jj] = p < end ? acc[jj] * a.scale_log2 : -INFINITY;
+        const bool in = UNI ? ((bits >> (4 * t + jj)) & 1u) != 0 : p < end;
+        z[t][jj] = in ? acc[jj] * a.scale_log2 : -INFINITY;
       }
     }
     float mloc = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
@@ -310,22 +374,48 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
   // computed, the K/V loads of window i+1 and the chunk ids of window i+2 are in flight.
   // The two register buffers alternate by unrolling the loop twice.
   int p0 = start + wave * ATT_STEP;
-  Window<DENSE> w0, w1;
-  w0.fetch(P, p0, end, a.C, a.Cshift, lane);
-  w1.fetch(P, p0 + gstep, end, a.C, a.Cshift, lane);
+  Window<TD> w0, w1;
   typename M::frag kA[2][NK], kB[2][NK];
   typename PVT::vfrag vA, vB;
-  if (p0 < end) load_kv(kA, vA, w0, p0);
-  while (p0 < end) {
-    w0.fetch(P, p0 + 2 * gstep, end, a.C, a.Cshift, lane);
-    load_kv(kB, vB, w1, p0 + gstep);
-    compute(kA, vA, p0);
-    p0 += gstep;
-    if (p0 >= end) break;
-    w1.fetch(P, p0 + 2 * gstep, end, a.C, a.Cshift, lane);
-    load_kv(kA, vA, w0, p0 + gstep);
-    compute(kB, vB, p0);
-    p0 += gstep;
+  if constexpr (UNI) {
+    // windows no column needs are neither loaded nor computed (a wave-uniform decision)
+    u64 rA[2][4], rB[2][4];
+    w0.fetch(P, p0, end, a.C, a.Cshift, lane);
+    fetch_rank(p0, rA);
+    fetch_rank(p0 + gstep, rB);
+    uint32_t bA = member_bits(p0, rA), bB = 0;
+    bool anyA = __ballot(bA != 0) != 0, anyB = false;
+    if (p0 < end && anyA) load_kv(kA, vA, w0, p0);
+    while (p0 < end) {
+      bB = member_bits(p0 + gstep, rB);
+      anyB = __ballot(bB != 0) != 0;
+      fetch_rank(p0 + 2 * gstep, rA);
+      if (p0 + gstep < end && anyB) load_kv(kB, vB, w0, p0 + gstep);
+      if (anyA) compute(kA, vA, p0, bA);
+      p0 += gstep;
+      if (p0 >= end) break;
+      bA = member_bits(p0 + gstep, rA);
+      anyA = __ballot(bA != 0) != 0;
+      fetch_rank(p0 + 2 * gstep, rB);
+      if (p0 + gstep < end && anyA) load_kv(kA, vA, w0, p0 + gstep);
+      if (anyB) compute(kB, vB, p0, bB);
+      p0 += gstep;
+    }
+  } else {
+    w0.fetch(P, p0, end, a.C, a.Cshift, lane);
+    w1.fetch(P, p0 + gstep, end, a.C, a.Cshift, lane);
+    if (p0 < end) load_kv(kA, vA, w0, p0);
+    while (p0 < end) {
+      w0.fetch(P, p0 + 2 * gstep, end, a.C, a.Cshift, lane);
+      load_kv(kB, vB, w1, p0 + gstep);
+      compute(kA, vA, p0, 0u);
+      p0 += gstep;
+      if (p0 >= end) break;
+      w1.fetch(P, p0 + 2 * gstep, end, a.C, a.Cshift, lane);
+      load_kv(kA, vA, w0, p0 + gstep);
+      compute(kB, vB, p0, 0u);
+      p0 += gstep;
+    }
   }
   // per-head sum over the four lane groups, then combine the four waves through LDS
   lrun += __shfl_xor(lrun, 16);
@@ -339,12 +429,17 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) so[(wave * 16 + row) * D + dt * 16 + 4 * grp + jj] = o[dt][jj];
   if (grp == 0) { sm[wave * 16 + row] = mrun; sl[wave * 16 + row] = lrun; }
+  __shared__ int s_rec[16];  // each column's (unit, workgroup, head) record; -1: no query head
+  if (wave == 0 && grp == 0) s_rec[row] = colok ? (u * a.W + (int)blockIdx.x) * G + jcol : -1;
   __syncthreads();
-  const int64_t rec = ((int64_t)u * a.W + blockIdx.x) * G;  // first (unit, workgroup, head) record
-  float* po = a.part + rec * D;
-  float* pml = a.part + (int64_t)a.U * a.W * G * D + rec * 2;
-  for (int i = threadIdx.x; i < G * D; i += 256) {
+  float* pml0 = a.part + (int64_t)a.U * a.W * G * D;
+  const int ncol = UNI ? 16 : G;
+  for (int i = threadIdx.x; i < ncol * D; i += 256) {
     const int h = i / D, dd = i % D;
+    const int rec = s_rec[h];
+    if (rec < 0) continue;
+    float* po = a.part + (int64_t)rec * D;
+    float* pml = pml0 + (int64_t)rec * 2;
     float Mx = -INFINITY;
     for (int w = 0; w < 4; ++w) Mx = fmaxf(Mx, sm[w * 16 + h]);
     float acc = 0.0f, l = 0.0f;
@@ -355,10 +450,10 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
         l += f * sl[w * 16 + h];
       }
     }
-    po[h * D + dd] = acc;
+    po[dd] = acc;
     if (dd == 0) {
-      pml[h * 2] = Mx;
-      pml[h * 2 + 1] = l;
+      pml[0] = Mx;
+      pml[1] = l;
     }
   }
 }
@@ -430,12 +525,11 @@ __global__ __launch_bounds__(MERGE_THREADS) void zha_merge_kernel(const float* p
   }
 }
 
-template <typename T, int D, bool DENSE>
-hipError_t launch_att(const AttArgs& a, const LensArg<DENSE>& la, int U, float* out, float* lse, hipStream_t s) {
-  hipLaunchKernelGGL((zha_attend_kernel<T, D, DENSE>), dim3(a.W, U), dim3(256), 0, s, a, la);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return hipSuccess;
+// rows: routing units, or groups of them (UNI)
+template <typename T, int D, bool DENSE, bool UNI = false>
+hipError_t launch_att(const AttArgs& a, const LensArg<DENSE>& la, int rows, hipStream_t s) {
+  hipLaunchKernelGGL((zha_attend_kernel<T, D, DENSE, UNI>), dim3(a.W, rows), dim3(256), 0, s, a, la);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -445,14 +539,13 @@ hipError_t launch_merge(const AttArgs& a, int U, float* out, float* lse, hipStre
   return hipGetLastError();
 }
 
-template <bool DENSE>
-hipError_t launch_att_dt(const AttArgs& a, const LensArg<DENSE>& la, zha_dtype dt, int d, int U, float* out,
-                         float* lse, hipStream_t s) {
+template <bool DENSE, bool UNI = false>
+hipError_t launch_att_dt(const AttArgs& a, const LensArg<DENSE>& la, zha_dtype dt, int d, int rows, hipStream_t s) {
   if (dt == ZHA_BF16)
-    return d == 64 ? launch_att<__bf16, 64, DENSE>(a, la, U, out, lse, s)
-                   : launch_att<__bf16, 128, DENSE>(a, la, U, out, lse, s);
-  return d == 64 ? launch_att<float, 64, DENSE>(a, la, U, out, lse, s)
-                 : launch_att<float, 128, DENSE>(a, la, U, out, lse, s);
+    return d == 64 ? launch_att<__bf16, 64, DENSE, UNI>(a, la, rows, s)
+                   : launch_att<__bf16, 128, DENSE, UNI>(a, la, rows, s);
+  return d == 64 ? launch_att<float, 64, DENSE, UNI>(a, la, rows, s)
+                 : launch_att<float, 128, DENSE, UNI>(a, la, rows, s);
 }
 
 int cshift_of(int C) {
@@ -497,8 +590,18 @@ hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const vo
   a.T = t->T;
   a.scale_log2 = scale * ZHA_LOG2E;
   a.lens = t->geo;
+  // union attention: the groups of the route's union scoring, when it had one
+  const int TS = zha_union_queries(t->R, t->G, t->Tq, t->hr);
+  const bool uni = TS > 0 && t->krank[1] != nullptr;
+  a.krank = uni ? t->krank[1] : nullptr;
+  a.route_ctr = t->route_ctr;
+  a.TS = TS;
+  a.NTC = uni ? (t->Tq + TS - 1) / TS : 1;
+  const int rows = uni ? t->U * a.NTC : t->RU;
+  if (uni) a.W = zha_sparse_wgs(rows);
   zha_time_begin(t, s, ZHA_K_ATTEND, 0);
-  hipError_t e = launch_att_dt<false>(a, LensArg<false>{}, t->desc.dtype, t->d, t->RU, out, lse, s);
+  hipError_t e = uni ? launch_att_dt<false, true>(a, LensArg<false>{}, t->desc.dtype, t->d, rows, s)
+                     : launch_att_dt<false>(a, LensArg<false>{}, t->desc.dtype, t->d, rows, s);
   if (e != hipSuccess) return e;
   zha_time_end(t, s, ZHA_K_ATTEND, 0);
   zha_time_begin(t, s, ZHA_K_MERGE, 0);
@@ -530,10 +633,14 @@ hipError_t zha_launch_dense(const void* q, const void* K, const void* V, const Z
   a.T = T;
   a.scale_log2 = scale * ZHA_LOG2E;
   a.lens = nullptr;
+  a.krank = nullptr;
+  a.route_ctr = nullptr;
+  a.TS = 0;
+  a.NTC = 1;
   const int U = B * Hkv;
   LensArg<true> la;
   la.len = len;
-  hipError_t e = launch_att_dt<true>(a, la, dt, d, U, out, lse, s);
+  hipError_t e = launch_att_dt<true>(a, la, dt, d, U, s);
   if (e != hipSuccess) return e;
   return d == 64 ? launch_merge<64>(a, U, out, lse, s) : launch_merge<128>(a, U, out, lse, s);
 }

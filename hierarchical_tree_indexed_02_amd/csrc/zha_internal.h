@@ -13,6 +13,7 @@
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
+typedef unsigned long long u64;
 
 #define ZHA_LOG2E 1.4426950408889634f
 #define ZHA_LN2 0.6931471805599453f

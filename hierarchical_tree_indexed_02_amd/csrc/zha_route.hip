@@ -29,7 +29,7 @@
 
 namespace {
 
-typedef unsigned long long u64;
+
 
 constexpr int NB = 1024;                 // histogram slices
 constexpr int SMALL_NODES = 8192;        // frontiers up to this size are selected in one workgroup
