@@ -43,6 +43,7 @@ struct AttArgs {
   const u64* krank;        // level-1 kept ranks [U][cap1]: (stamp << 32) | rank, by chunk id
   const uint32_t* route_ctr;  // the last route's stamp
   int TS, NTC;             // queries per group; groups per (sequence, KV head)
+  int CT;                  // column tiles of a group (16 query heads each): wave w takes tile w % CT
 };
 
 // Dense launches take the lengths by value (the dense entry point gets them from the host);
@@ -209,8 +210,8 @@ template <int D> struct PV<float, D> {
   }
 };
 
-template <typename T, int D, bool DENSE, bool UNI>
-__global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENSE> la) {
+template <typename T, int D, bool DENSE, bool UNI, bool C4 = false>
+__global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_attend_kernel(AttArgs a, LensArg<DENSE> la) {
   typedef Mf<T> M;
   typedef PV<T, D> PVT;
   constexpr bool TD = DENSE || UNI;  // positions are tokens
@@ -229,6 +230,10 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
   // UNI: lane column `row` is head jcol of unit u; the group reads tokens [0, end) and a
   // column takes token 0, the tokens of its unit's kept chunks and its tail [Nc, Ne).
   const int G = a.G;
+  // UNI with several column tiles: the waves of one window slot ws read the same K/V rows
+  // (the cache serves all but the first) for different query heads
+  const int CT = UNI ? a.CT : 1, ct = wave % CT, ws = wave / CT, NWS = 4 / CT;
+  const int col = ct * 16 + row;
   int u, up, bi, jcol, Ne = 0, Nc = 0;
   bool colok;
   Positions P;
@@ -237,10 +242,10 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
     const int tc = blockIdx.y - up * a.NTC, g = up % a.Hkv;
     bi = up / a.Hkv;
     const int per_t = a.hr * G;
-    const int tt = row / per_t, h = (row / G) % a.hr, tq = tc * a.TS + tt;
+    const int tt = col / per_t, h = (col / G) % a.hr, tq = tc * a.TS + tt;
     colok = tt < a.TS && tq < a.Tq;
     u = ((bi * a.Tq + min(tq, a.Tq - 1)) * a.Hkv + g) * a.hr + h;
-    jcol = row % G;
+    jcol = col % G;
     const int N = a.lens[bi];
     Nc = (N / a.C) * a.C;
     Ne = a.qtail ? N + min(tq, a.Tq - 1) + 1 : N;
@@ -259,7 +264,7 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
   const uint32_t stamp = UNI ? a.route_ctr[0] : 0u;
   // Blocks of 4 * ATT_STEP positions are dealt to the workgroups in turn, so the unit's
   // workgroups read neighbouring K/V rows at any moment.
-  constexpr int WSTEP = 4 * ATT_STEP;
+  const int WSTEP = NWS * ATT_STEP;
   const int start = blockIdx.x * WSTEP;
   const int gstep = a.W * WSTEP;
   const int end = P.P;
@@ -293,29 +298,29 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
     }
     PVT::template load<TD>(vf, Vb, P, win, p0, end, a.C, a.Cshift, lane);
   };
-  // UNI: kept-rank entries of the chunks of this lane's tokens p0 + 16t + 4grp + jj (one
-  // per 4 tokens when C is a power of two >= 4), for the lane's column unit.
-  auto fetch_rank = [&](int p0, u64 (&rk)[2][4]) {
+  // UNI: stamps (the high words of the kept-rank entries) of the chunks of this lane's tokens
+  // p0 + 16t + 4grp + jj for the lane's column unit; one per 4 tokens when 4 divides C.
+  auto fetch_rank = [&](int p0, uint32_t (&rk)[2][4]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
+      for (int jj = 0; jj < (C4 ? 1 : 4); ++jj) {
         const int tok = p0 + 16 * t + 4 * grp + jj;
-        const bool need = colok && tok < Nc && (jj == 0 || a.Cshift < 2);
+        const bool need = colok && tok < Nc;
         const int k = a.Cshift >= 0 ? (tok >> a.Cshift) : tok / a.C;
-        rk[t][jj] = need ? kr1[k] : 0;
+        rk[t][jj] = need ? ((const uint32_t*)(kr1 + k))[1] : 0u;
       }
   };
   // UNI: bit 4t + jj: token p0 + 16t + 4grp + jj is in the column's set
-  auto member_bits = [&](int p0, const u64 (&rk)[2][4]) {
+  auto member_bits = [&](int p0, const uint32_t (&rk)[2][4]) {
     uint32_t bits = 0;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int tok = p0 + 16 * t + 4 * grp + jj;
-        const u64 r = a.Cshift >= 2 ? rk[t][0] : rk[t][jj];
-        const bool in = colok && (tok < Nc ? (tok == 0 || (uint32_t)(r >> 32) == stamp) : tok < Ne);
+        const uint32_t r = C4 ? rk[t][0] : rk[t][jj];
+        const bool in = colok && (tok < Nc ? (tok == 0 || r == stamp) : tok < Ne);
         bits |= in ? (1u << (4 * t + jj)) : 0u;
       }
     return bits;
@@ -373,13 +378,13 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
   // Software pipeline over the wave's windows p0, p0 + gstep, ...: while window i is
   // computed, the K/V loads of window i+1 and the chunk ids of window i+2 are in flight.
   // The two register buffers alternate by unrolling the loop twice.
-  int p0 = start + wave * ATT_STEP;
+  int p0 = start + ws * ATT_STEP;
   Window<TD> w0, w1;
   typename M::frag kA[2][NK], kB[2][NK];
   typename PVT::vfrag vA, vB;
   if constexpr (UNI) {
     // windows no column needs are neither loaded nor computed (a wave-uniform decision)
-    u64 rA[2][4], rB[2][4];
+    uint32_t rA[2][4], rB[2][4];
     w0.fetch(P, p0, end, a.C, a.Cshift, lane);
     fetch_rank(p0, rA);
     fetch_rank(p0 + gstep, rB);
@@ -429,22 +434,23 @@ __global__ __launch_bounds__(256) void zha_attend_kernel(AttArgs a, LensArg<DENS
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) so[(wave * 16 + row) * D + dt * 16 + 4 * grp + jj] = o[dt][jj];
   if (grp == 0) { sm[wave * 16 + row] = mrun; sl[wave * 16 + row] = lrun; }
-  __shared__ int s_rec[16];  // each column's (unit, workgroup, head) record; -1: no query head
-  if (wave == 0 && grp == 0) s_rec[row] = colok ? (u * a.W + (int)blockIdx.x) * G + jcol : -1;
+  __shared__ int s_rec[64];  // each column's (unit, workgroup, head) record; -1: no query head
+  if (ws == 0 && grp == 0) s_rec[col] = colok ? (u * a.W + (int)blockIdx.x) * G + jcol : -1;
   __syncthreads();
   float* pml0 = a.part + (int64_t)a.U * a.W * G * D;
-  const int ncol = UNI ? 16 : G;
+  const int ncol = UNI ? 16 * CT : G;
+  // column c: the waves c / 16, c / 16 + CT, ... hold its partial sums, in their row c % 16
   for (int i = threadIdx.x; i < ncol * D; i += 256) {
-    const int h = i / D, dd = i % D;
-    const int rec = s_rec[h];
+    const int c = i / D, dd = i % D, c0 = c >> 4, h = c & 15;
+    const int rec = s_rec[c];
     if (rec < 0) continue;
     float* po = a.part + (int64_t)rec * D;
     float* pml = pml0 + (int64_t)rec * 2;
     float Mx = -INFINITY;
-    for (int w = 0; w < 4; ++w) Mx = fmaxf(Mx, sm[w * 16 + h]);
+    for (int w = c0; w < 4; w += CT) Mx = fmaxf(Mx, sm[w * 16 + h]);
     float acc = 0.0f, l = 0.0f;
     if (Mx != -INFINITY) {
-      for (int w = 0; w < 4; ++w) {
+      for (int w = c0; w < 4; w += CT) {
         const float f = zexp2(sm[w * 16 + h] - Mx);
         acc += f * so[(w * 16 + h) * D + dd];
         l += f * sl[w * 16 + h];
@@ -525,10 +531,17 @@ __global__ __launch_bounds__(MERGE_THREADS) void zha_merge_kernel(const float* p
   }
 }
 
-// rows: routing units, or groups of them (UNI)
+// rows: routing units, or groups of them (UNI; C4: the chunk size is a power of two >= 4)
 template <typename T, int D, bool DENSE, bool UNI = false>
 hipError_t launch_att(const AttArgs& a, const LensArg<DENSE>& la, int rows, hipStream_t s) {
-  hipLaunchKernelGGL((zha_attend_kernel<T, D, DENSE, UNI>), dim3(a.W, rows), dim3(256), 0, s, a, la);
+  if constexpr (UNI) {
+    if (a.Cshift >= 2)
+      hipLaunchKernelGGL((zha_attend_kernel<T, D, DENSE, true, true>), dim3(a.W, rows), dim3(256), 0, s, a, la);
+    else
+      hipLaunchKernelGGL((zha_attend_kernel<T, D, DENSE, true, false>), dim3(a.W, rows), dim3(256), 0, s, a, la);
+  } else {
+    hipLaunchKernelGGL((zha_attend_kernel<T, D, DENSE, false>), dim3(a.W, rows), dim3(256), 0, s, a, la);
+  }
   return hipGetLastError();
 }
 
@@ -597,6 +610,7 @@ hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const vo
   a.route_ctr = t->route_ctr;
   a.TS = TS;
   a.NTC = uni ? (t->Tq + TS - 1) / TS : 1;
+  a.CT = uni ? zha_union_tiles(TS, t->G) : 1;
   const int rows = uni ? t->U * a.NTC : t->RU;
   if (uni) a.W = zha_sparse_wgs(rows);
   zha_time_begin(t, s, ZHA_K_ATTEND, 0);
@@ -637,6 +651,7 @@ hipError_t zha_launch_dense(const void* q, const void* K, const void* V, const Z
   a.route_ctr = nullptr;
   a.TS = 0;
   a.NTC = 1;
+  a.CT = 1;
   const int U = B * Hkv;
   LensArg<true> la;
   la.len = len;

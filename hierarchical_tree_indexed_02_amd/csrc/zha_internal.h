@@ -263,4 +263,5 @@ int zha_score_wgs_units(int RU);  // score workgroups per routing unit (before t
 // Union scoring of a route with Tq queries per sequence and hr units per (query, KV head):
 // queries per group (0: no union scoring) and groups per (sequence, KV head).
 int zha_union_queries(int R, int Gq, int Tq, int hr);
+int zha_union_tiles(int TS, int Gq);  // matrix column tiles (16 columns each) of a union group
 int zha_dense_wgs(int U);

@@ -145,13 +145,14 @@ struct ScoreArgs {
   int Hkv, Tq;            // KV heads; queries per sequence
   float scale;
   // Union scoring: one row of workgroups per group of the routing units that share one
-  // (sequence, KV head): the hr units of each of TS consecutive queries (TS * Gq <= 16
-  // matrix columns).  A node is scored once for every column; a unit keeps the scores of
-  // the nodes of its own frontier.
+  // (sequence, KV head): the hr units of each of TS consecutive queries (TS * Gq <= 64
+  // matrix columns, 16 per column tile).  A node is scored once for every column; a unit
+  // keeps the scores of the nodes of its own frontier.
   const u64* krank;       // [RU][cap_parent]: the parent level's kept nodes, (stamp << 32) | rank in
                           // the unit's kept list; null at the top level (every node is a member)
   uint32_t* route_ctr;    // route stamp; the top level's first workgroup advances it
   int TS, NTC;            // queries per group; groups per (sequence, KV head)
+  int CT;                 // column tiles of a group (16 columns each): wave w scores tile w % CT
 };
 
 // Eight fp8 e4m3 codes (two dwords) as eight bf16 values (exact), by the hardware
@@ -183,17 +184,21 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 // column's unit has its parent kept (a stamped rank entry), and each column keeps the
 // scores of its unit's member nodes at the unit's frontier positions.
 template <typename T, int R, int D, int UN, bool F8, bool UNI>
-__global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a) {
   typedef Mf<T> M;
   constexpr int NK = D / M::KPER;
   constexpr int NR = F8 ? D / 64 : 1;   // 16-byte code loads per lane per tile (F8)
   constexpr int NPT = 16 / R;
-  constexpr int SUPER = 4 * UN * NPT;
   static_assert(!F8 || M::EPL == 8, "fp8 planes feed the bf16 matrix instruction");
   static_assert(!UNI || R >= 4, "union scoring keeps one node per lane group");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, grp = lane >> 4;
   const int G = a.G;
+  // UNI with several column tiles: the waves of one tile slot ws read the same planes (the
+  // cache serves all but the first) and score different columns
+  const int CT = UNI ? a.CT : 1, ct = wave % CT, ws = wave / CT, NWS = 4 / CT;
+  const int col = ct * 16 + row;
+  const int SUPER = NWS * UN * NPT;
   // u: routing unit (frontier, scores, partials) of this lane's column; up: its (sequence,
   // KV head) unit (planes); qrow: the column's query row; colok: the column is a query head
   int u, up, qrow, jcol, end;
@@ -202,10 +207,10 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
     up = blockIdx.y / a.NTC;
     const int tc = blockIdx.y - up * a.NTC, bi = up / a.Hkv, g = up - bi * a.Hkv;
     const int per_t = a.hr * G;  // columns per query
-    const int tt = row / per_t, h = (row / G) % a.hr, t = tc * a.TS + tt;
+    const int tt = col / per_t, h = (col / G) % a.hr, t = tc * a.TS + tt;
     colok = tt < a.TS && t < a.Tq;
     u = ((bi * a.Tq + min(t, a.Tq - 1)) * a.Hkv + g) * a.hr + h;
-    jcol = row % G;
+    jcol = col % G;
     qrow = u * G + jcol;
     end = a.v.nodes[bi];
     if (a.route_ctr && !a.krank && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
@@ -254,12 +259,12 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int k = 0; k < UN; ++k) {
       if constexpr (UNI) {
-        const int id = base + (k * 4 + wave) * NPT + (4 * grp) / R;
+        const int id = base + (k * NWS + ws) * NPT + (4 * grp) / R;
         const int P = a.v.Cshift >= 0 ? (id >> a.v.Cshift) : id / a.v.C;
         rk[k] = (kr && colok && id < end) ? kr[P] : 0;
         pp[k] = 0;
       } else {
-        const int pos = base + (k * 4 + wave) * NPT + row / R;
+        const int pos = base + (k * NWS + ws) * NPT + row / R;
         pp[k] = (par && pos < end) ? par[a.v.Cshift >= 0 ? (pos >> a.v.Cshift) : pos / a.v.C] : 0;
         rk[k] = 0;
       }
@@ -270,7 +275,7 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
   auto members = [&](int base, const u64 (&rk)[UN], bool (&mem)[UN], int (&wpos)[UN], uint32_t (&act)[UN]) {
 #pragma unroll
     for (int k = 0; k < UN; ++k) {
-      const int id = base + (k * 4 + wave) * NPT + (4 * grp) / R;
+      const int id = base + (k * NWS + ws) * NPT + (4 * grp) / R;
       bool m;
       int pos;
       if (kr) {
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
                         float (&bv)[UN][4]) {
 #pragma unroll
     for (int k = 0; k < UN; ++k) {
-      const int tbk = base + (k * 4 + wave) * NPT;
+      const int tbk = base + (k * NWS + ws) * NPT;
       const int pos = tbk + row / R;
       const bool v = UNI ? ((act[k] >> (row / R)) & 1u) != 0 : pos < end;
       int id = pos;
@@ -332,7 +337,7 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
   // its column when its node is a member, at the column unit's frontier position.
   auto score_tile = [&](int k, const Frag (&afk)[NK], const float (&bvk)[4], const float (&rs)[4], int base,
                         bool memk, int wposk) {
-    const int tbk = base + (k * 4 + wave) * NPT;
+    const int tbk = base + (k * NWS + ws) * NPT;
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < NK; ++s) acc = M::mma(afk[s], qf[s], acc);
@@ -386,7 +391,7 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
                          float (&bv)[UN][4], float (&sv)[UN][4]) {
 #pragma unroll
     for (int k = 0; k < UN; ++k) {
-      const int tbk = base + (k * 4 + wave) * NPT;
+      const int tbk = base + (k * NWS + ws) * NPT;
       const int pos = tbk + row / R;
       const bool v = UNI ? ((act[k] >> (row / R)) & 1u) != 0 : pos < end;
       int id = pos;
@@ -481,7 +486,7 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
       base += step;
     }
   }
-  // per-column (max, sum exp) of this workgroup: lanes of one column, then the 4 waves
+  // per-column (max, sum exp) of this workgroup: lanes of one column, then the waves
   {
     float M2 = __shfl_xor(runM, 16), S2 = __shfl_xor(runS, 16);
     lse_merge(runM, runS, M2, S2);
@@ -490,15 +495,18 @@ __global__ __launch_bounds__(256, 4) void zha_score_kernel(ScoreArgs a) {
     lse_merge(runM, runS, M2, S2);
   }
   __shared__ float sM[4][16], sS[4][16];
-  __shared__ int sU[16], sJ[16];
-  __shared__ bool sOk[16];
+  __shared__ int sU[64], sJ[64];
+  __shared__ bool sOk[64];
   if (grp == 0) { sM[wave][row] = runM; sS[wave][row] = runS; }
-  if (wave == 0 && grp == 0) { sU[row] = u; sJ[row] = jcol; sOk[row] = colok; }
+  if (ws == 0 && grp == 0) { sU[col] = u; sJ[col] = jcol; sOk[col] = colok; }
   __syncthreads();
-  if (threadIdx.x < 16 && sOk[threadIdx.x]) {
-    float Mx = sM[0][threadIdx.x], Sx = sS[0][threadIdx.x];
-    for (int w = 1; w < 4; ++w) lse_merge(Mx, Sx, sM[w][threadIdx.x], sS[w][threadIdx.x]);
-    float* pp = a.part + (((int64_t)sU[threadIdx.x] * a.W + blockIdx.x) * G + sJ[threadIdx.x]) * 2;
+  // column c: the waves c / 16, c / 16 + CT, ... scored it
+  const int c = threadIdx.x;
+  if (c < 16 * CT && sOk[c]) {
+    const int c0 = c >> 4, r = c & 15;
+    float Mx = sM[c0][r], Sx = sS[c0][r];
+    for (int w = c0 + CT; w < 4; w += CT) lse_merge(Mx, Sx, sM[w][r], sS[w][r]);
+    float* pp = a.part + (((int64_t)sU[c] * a.W + blockIdx.x) * G + sJ[c]) * 2;
     pp[0] = Mx;
     pp[1] = Sx;
   }
@@ -1671,15 +1679,21 @@ int zha_score_wgs(const zha_tree* t, int level) {
 }
 
 // Union scoring groups the routing units that share one (sequence, KV head): the hr units of
-// each of TS consecutive queries, TS * Gq <= 16 columns of the matrix tile.  Only worth it
-// (and only built) when a group holds several units and a tile row holds one node's planes
-// for one lane group (R >= 4).
+// each of TS consecutive queries, TS * Gq <= 64 columns in up to four matrix column tiles.
+// Only worth it (and only built) when a group holds several units and a tile row holds one
+// node's planes for one lane group (R >= 4).
 int zha_union_queries(int R, int Gq, int Tq, int hr) {
   if (R < 4 || Gq < 1 || Gq > 16) return 0;
-  int ts = 16 / Gq;
+  int ts = 64 / Gq;
   if (ts > Tq) ts = Tq;
   if (ts < 1) ts = 1;
   return ts * hr > 1 ? ts : 0;
+}
+
+// Column tiles of a union group of TS queries (Gq columns each): 1, 2 or 4.
+int zha_union_tiles(int TS, int Gq) {
+  const int cols = TS * Gq;
+  return cols <= 16 ? 1 : (cols <= 32 ? 2 : 4);
 }
 
 int zha_compact_chunks(int64_t nodes) { return (int)((nodes + CH - 1) / CH); }
@@ -1699,6 +1713,7 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
   const int TS = zha_union_queries(t->R, t->G, t->Tq, t->hr);
   const bool uni = TS > 0 && t->krank[1] != nullptr;
   const int NTC = uni ? (t->Tq + TS - 1) / TS : 1;
+  const int CT = uni ? zha_union_tiles(TS, t->G) : 1;
   const int rows = uni ? t->U * NTC : U;  // rows of the scoring grid
   hipError_t e;
   for (int l = L; l >= 1; --l) {
@@ -1734,6 +1749,7 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     sa.route_ctr = uni ? t->route_ctr : nullptr;
     sa.TS = TS;
     sa.NTC = NTC;
+    sa.CT = CT;
     sa.G = Gr;
     sa.hr = t->hr;
     sa.Hkv = t->desc.n_kv_heads;
