@@ -502,6 +502,37 @@ def test_deep_256k_fp8_full():
 
 
 @pytest.mark.slow
+def test_deep_256k_per_head_full():
+    """Per-head routes at full size (the launch shapes the benchmark times): two KV heads'
+    16 query heads checked against the oracle."""
+    cfg = zi.get_config("deep_256k")
+    say("case deep_256k full, per-head routes: N=262144, 32q/4kv, d=128, C=4 L=6 R=16 p=0.95, KV heads 0 and 3")
+    case = Case(cfg, n_queries=1)
+    tree = case.tree(per_head_routes=True)
+    torch.cuda.synchronize()
+    r, a = full_check(case, tree, 0, 0.95, units={0, 3}, mode="per_head")
+    say(" t=0", r, a)
+
+
+@pytest.mark.slow
+def test_deep_256k_block_full():
+    """A block of 8 queries over the first N - 8 tokens at full size (the benchmark's block
+    leg): queries 0 and 7 of KV heads 0 and 3 checked against the oracle."""
+    cfg = zi.get_config("deep_256k")
+    N = cfg.n_tokens
+    say(f"case deep_256k full, block of 8 queries after {N - 8} tokens: 32q/4kv, d=128, C=4 L=6 R=16 p=0.95")
+    case = Case(cfg, lens=[N - 8], n_queries=8, max_tokens=N)
+    tree = case.tree(max_queries=8)
+    qb, qbd = block_of(case, 8)
+    tree.route_multi(qbd, 0.95)
+    out, lse = tree.attend_multi(qbd, case.Kd, case.Vd)
+    torch.cuda.synchronize()
+    units = {((0 * 8 + t) * case.Hkv + g) for t in (0, 7) for g in (0, 3)}
+    r, a = check_block(case, tree, qb, 0.95, out, lse, units=units)
+    say(" queries 0 and 7", r, a)
+
+
+@pytest.mark.slow
 def test_wide_256k_full():
     cfg = zi.get_config("wide_256k")
     say("case wide_256k full: N=262144, 32q/4kv, d=128, C=256 L=1 R=16 p=0.95")
