@@ -83,7 +83,7 @@ void free_tree(zha_tree* t) {
   }
   void* ps[] = {t->refs,   t->spine,  t->sub_lse, t->sub_m,  t->counts,    t->geo,      t->scores,   t->spart,    t->keys,     t->apart,
                 t->fh_cnt, t->fh_mass,  t->fh_edge,  t->cut,      t->sel_cand, t->sel_ctr, t->lb_status,
-                t->lb_epoch, t->lb_error, t->route_ctr};
+                t->lb_epoch, t->lb_error, t->route_ctr, t->uflag, t->ulist, t->ucount};
   for (void* p : ps)
     if (p) (void)hipFree(p);
   for (int i = 0; i < 2 * ZHA_MAX_TIMING; ++i)
@@ -236,6 +236,11 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   ok = ok && dalloc(t, &t->spart, spart_n * sizeof(float));
   t->kstride = (t->cap[1] + 3) / 4 * 4;
   ok = ok && dalloc(t, &t->keys, (size_t)RUmax * t->kstride * sizeof(uint32_t));
+  if (uni) {
+    ok = ok && dalloc(t, &t->uflag, (size_t)U * t->kstride * sizeof(uint32_t));
+    ok = ok && dalloc(t, &t->ulist, (size_t)U * t->cap[1] * sizeof(int32_t));
+    ok = ok && dalloc(t, &t->ucount, (size_t)2 * U * sizeof(int32_t));
+  }
   ok = ok && dalloc(t, &t->apart, apart_n * sizeof(float));
   const int nchunk = zha_compact_chunks(t->cap[1]);
   const int nb = zha_hist_bins();
@@ -260,6 +265,7 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
     for (int l = 1; l <= L && ok && uni; ++l)
       ok = hipMemset(t->krank[l], 0, (size_t)RUmax * t->cap[l] * sizeof(unsigned long long)) == hipSuccess;
     if (uni) ok = ok && hipMemset(t->route_ctr, 0, sizeof(uint32_t)) == hipSuccess;
+    if (uni) ok = ok && hipMemset(t->uflag, 0, (size_t)U * t->kstride * sizeof(uint32_t)) == hipSuccess;
     // every unit's epoch starts at 1: status words of epoch 0 (all-zero memory) never match
     std::vector<uint32_t> ep((size_t)RUmax * 2, 0u);
     for (int u = 0; u < RUmax; ++u) ep[(size_t)u * 2] = 1u;

@@ -42,6 +42,8 @@ struct AttArgs {
   // of its unit's set only.
   const u64* krank;        // level-1 kept ranks [U][cap1]: (stamp << 32) | rank, by chunk id
   const uint32_t* route_ctr;  // the last route's stamp
+  const int32_t* ulist;    // [B*Hkv][cap1] chunks kept by some routing unit of the (sequence, KV head)
+  const int32_t* ucount;   // [B*Hkv]
   int TS, NTC;             // queries per group; groups per (sequence, KV head)
   int CT;                  // column tiles of a group (16 query heads each): wave w takes tile w % CT
 };
@@ -210,11 +212,11 @@ template <int D> struct PV<float, D> {
   }
 };
 
-template <typename T, int D, bool DENSE, bool UNI, bool C4 = false>
+template <typename T, int D, bool DENSE, bool UNI>
 __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_attend_kernel(AttArgs a, LensArg<DENSE> la) {
   typedef Mf<T> M;
   typedef PV<T, D> PVT;
-  constexpr bool TD = DENSE || UNI;  // positions are tokens
+  constexpr bool TD = DENSE;  // positions are tokens
   constexpr int NK = D / M::KPER;
   constexpr int ND = D / 16;
   constexpr int LDS_WAVE = PVT::LDS_ELEMS > 0 ? PVT::LDS_ELEMS : 1;
@@ -227,8 +229,9 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
   const int row = lane & 15, grp = lane >> 4;
   // u: routing unit, of G query heads; up: its (sequence, KV head) unit.  Units are numbered
   // (sequence, query, KV head, head group), so the unit's first query head is u * G.
-  // UNI: lane column `row` is head jcol of unit u; the group reads tokens [0, end) and a
-  // column takes token 0, the tokens of its unit's kept chunks and its tail [Nc, Ne).
+  // UNI: lane column `col` is head jcol of unit u; the group reads token 0, the tail up to
+  // the group's last query and the chunks some unit of the (sequence, KV head) kept, and a
+  // column takes token 0, the tokens of its unit's kept chunks and its own tail [Nc, Ne).
   const int G = a.G;
   // UNI with several column tiles: the waves of one window slot ws read the same K/V rows
   // (the cache serves all but the first) for different query heads
@@ -251,7 +254,14 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
     Ne = a.qtail ? N + min(tq, a.Tq - 1) + 1 : N;
     const int tlast = min(tc * a.TS + a.TS, a.Tq) - 1;  // the group's last query
     const int Nend = a.qtail ? N + tlast + 1 : N;
-    P.P = Nend; P.nx = Nend; P.sink = 0; P.Nc = 0; P.nK = 0; P.kp = nullptr;
+    const int nK = a.ucount[up];
+    const int32_t* kp = a.ulist + (int64_t)up * a.cap1;
+    P.sink = (Nc > 0 && (nK == 0 || kp[0] != 0)) ? 1 : 0;
+    P.nx = P.sink + (Nend - Nc);
+    P.P = P.nx + nK * a.C;
+    P.Nc = Nc;
+    P.nK = nK;
+    P.kp = kp;
   } else {
     u = blockIdx.y;
     up = plane_unit(u, a.hr, a.Hkv, a.Tq);
@@ -298,30 +308,39 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
     }
     PVT::template load<TD>(vf, Vb, P, win, p0, end, a.C, a.Cshift, lane);
   };
-  // UNI: stamps (the high words of the kept-rank entries) of the chunks of this lane's tokens
-  // p0 + 16t + 4grp + jj for the lane's column unit; one per 4 tokens when 4 divides C.
-  auto fetch_rank = [&](int p0, uint32_t (&rk)[2][4]) {
+  // UNI: stamps (the high words of the kept-rank entries) of the chunks of this lane's
+  // positions p0 + 16t + 4grp + jj for the lane's column unit (0 outside the chunk part).
+  // Every lane calls this together (the token lookup shuffles).
+  auto fetch_rank = [&](const Window<TD>& win, int p0, uint32_t (&rk)[2][4]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int jj = 0; jj < (C4 ? 1 : 4); ++jj) {
-        const int tok = p0 + 16 * t + 4 * grp + jj;
-        const bool need = colok && tok < Nc;
+      for (int jj = 0; jj < 4; ++jj) {
+        const int p = p0 + 16 * t + 4 * grp + jj;
+        const int tok = win.token(P, p0, p, end, a.C, a.Cshift);
+        const bool need = colok && p < end && p >= P.nx;
         const int k = a.Cshift >= 0 ? (tok >> a.Cshift) : tok / a.C;
         rk[t][jj] = need ? ((const uint32_t*)(kr1 + k))[1] : 0u;
       }
   };
-  // UNI: bit 4t + jj: token p0 + 16t + 4grp + jj is in the column's set
+  // UNI: bit 4t + jj: position p0 + 16t + 4grp + jj is in the column's set: token 0 always,
+  // the tail up to the column's own end, a chunk token when the column's unit kept it
+  const bool chunk0 = UNI && Nc > 0 && !P.sink;  // token 0 is the union list's first chunk token
   auto member_bits = [&](int p0, const uint32_t (&rk)[2][4]) {
     uint32_t bits = 0;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int tok = p0 + 16 * t + 4 * grp + jj;
-        const uint32_t r = C4 ? rk[t][0] : rk[t][jj];
-        const bool in = colok && (tok < Nc ? (tok == 0 || r == stamp) : tok < Ne);
-        bits |= in ? (1u << (4 * t + jj)) : 0u;
+        const int p = p0 + 16 * t + 4 * grp + jj;
+        bool in;
+        if (p < P.nx) {
+          const int tok = (P.sink && p == 0) ? 0 : P.Nc + p - P.sink;
+          in = tok == 0 || tok < Ne;
+        } else {
+          in = p < end && (rk[t][jj] == stamp || (p == P.nx && chunk0));
+        }
+        bits |= (colok && in) ? (1u << (4 * t + jj)) : 0u;
       }
     return bits;
   };
@@ -383,27 +402,24 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
   typename M::frag kA[2][NK], kB[2][NK];
   typename PVT::vfrag vA, vB;
   if constexpr (UNI) {
-    // windows no column needs are neither loaded nor computed (a wave-uniform decision)
+    // the sparse pipeline over the union's positions, with the column stamps of each window
+    // fetched one window ahead (they depend on the window's chunk ids)
     uint32_t rA[2][4], rB[2][4];
     w0.fetch(P, p0, end, a.C, a.Cshift, lane);
-    fetch_rank(p0, rA);
-    fetch_rank(p0 + gstep, rB);
-    uint32_t bA = member_bits(p0, rA), bB = 0;
-    bool anyA = __ballot(bA != 0) != 0, anyB = false;
-    if (p0 < end && anyA) load_kv(kA, vA, w0, p0);
+    w1.fetch(P, p0 + gstep, end, a.C, a.Cshift, lane);
+    fetch_rank(w0, p0, rA);
+    if (p0 < end) load_kv(kA, vA, w0, p0);
     while (p0 < end) {
-      bB = member_bits(p0 + gstep, rB);
-      anyB = __ballot(bB != 0) != 0;
-      fetch_rank(p0 + 2 * gstep, rA);
-      if (p0 + gstep < end && anyB) load_kv(kB, vB, w0, p0 + gstep);
-      if (anyA) compute(kA, vA, p0, bA);
+      fetch_rank(w1, p0 + gstep, rB);
+      w0.fetch(P, p0 + 2 * gstep, end, a.C, a.Cshift, lane);
+      load_kv(kB, vB, w1, p0 + gstep);
+      compute(kA, vA, p0, member_bits(p0, rA));
       p0 += gstep;
       if (p0 >= end) break;
-      bA = member_bits(p0 + gstep, rA);
-      anyA = __ballot(bA != 0) != 0;
-      fetch_rank(p0 + 2 * gstep, rB);
-      if (p0 + gstep < end && anyA) load_kv(kA, vA, w0, p0 + gstep);
-      if (anyB) compute(kB, vB, p0, bB);
+      fetch_rank(w0, p0 + gstep, rA);
+      w1.fetch(P, p0 + 2 * gstep, end, a.C, a.Cshift, lane);
+      load_kv(kA, vA, w0, p0 + gstep);
+      compute(kB, vB, p0, member_bits(p0, rB));
       p0 += gstep;
     }
   } else {
@@ -531,17 +547,10 @@ __global__ __launch_bounds__(MERGE_THREADS) void zha_merge_kernel(const float* p
   }
 }
 
-// rows: routing units, or groups of them (UNI; C4: the chunk size is a power of two >= 4)
+// rows: routing units, or groups of them (UNI)
 template <typename T, int D, bool DENSE, bool UNI = false>
 hipError_t launch_att(const AttArgs& a, const LensArg<DENSE>& la, int rows, hipStream_t s) {
-  if constexpr (UNI) {
-    if (a.Cshift >= 2)
-      hipLaunchKernelGGL((zha_attend_kernel<T, D, DENSE, true, true>), dim3(a.W, rows), dim3(256), 0, s, a, la);
-    else
-      hipLaunchKernelGGL((zha_attend_kernel<T, D, DENSE, true, false>), dim3(a.W, rows), dim3(256), 0, s, a, la);
-  } else {
-    hipLaunchKernelGGL((zha_attend_kernel<T, D, DENSE, false>), dim3(a.W, rows), dim3(256), 0, s, a, la);
-  }
+  hipLaunchKernelGGL((zha_attend_kernel<T, D, DENSE, UNI>), dim3(a.W, rows), dim3(256), 0, s, a, la);
   return hipGetLastError();
 }
 
@@ -608,6 +617,8 @@ hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const vo
   const bool uni = TS > 0 && t->krank[1] != nullptr;
   a.krank = uni ? t->krank[1] : nullptr;
   a.route_ctr = t->route_ctr;
+  a.ulist = t->ulist;
+  a.ucount = t->ucount;
   a.TS = TS;
   a.NTC = uni ? (t->Tq + TS - 1) / TS : 1;
   a.CT = uni ? zha_union_tiles(TS, t->G) : 1;
@@ -649,6 +660,8 @@ hipError_t zha_launch_dense(const void* q, const void* K, const void* V, const Z
   a.lens = nullptr;
   a.krank = nullptr;
   a.route_ctr = nullptr;
+  a.ulist = nullptr;
+  a.ucount = nullptr;
   a.TS = 0;
   a.NTC = 1;
   a.CT = 1;

@@ -201,6 +201,10 @@ struct zha_tree {
   unsigned long long* krank[ZHA_MAX_LEVELS + 2];  // union routes: per-level (stamp << 32) | rank in the
                                     // unit's kept list, by node id [RUmax][cap] (null: no union routes)
   uint32_t* route_ctr;              // [1] stamp of the current union route (advanced on the device)
+  uint32_t* uflag;                  // union routes: [U][kstride] stamp of each leaf chunk kept by some
+                                    // routing unit of the (sequence, KV head)
+  int32_t* ulist;                   // [U][cap1] those chunks in order (the union's level-1 kept list)
+  int32_t* ucount;                  // [2][U]: chunks in the list; chunks scanned
   float* refs;                      // [Hkv][R][d]
   float* spine;                     // [U][L+1][R*16][E+2] open-node accumulators
   int S;                            // subtree level of the build (highest level of <= 256 tokens)

@@ -948,6 +948,9 @@ struct SmallArgs {
   int keep_all;
   u64* krank;             // union routes: [U][capl] (stamp << 32) | rank of each kept node; else null
   const uint32_t* route_ctr;  // the route's stamp
+  uint32_t* uflag;        // union routes at level 1: [B*Hkv][ufstride] stamp of every kept chunk
+  int64_t ufstride;
+  int hr, Hkv, Tq;        // routing-unit numbering (for the unit's (sequence, KV head))
 };
 
 constexpr int SBATCH = 8;     // frontier positions per thread per load batch
@@ -1074,6 +1077,7 @@ __global__ __launch_bounds__(ST) void zha_select_small_kernel(SmallArgs a) {
   // compaction in position order (chunks of 4 positions per thread)
   int32_t* kept = a.kept + (int64_t)u * a.capl;
   u64* kr = a.krank ? a.krank + (int64_t)u * a.capl : nullptr;
+  uint32_t* uf = a.uflag ? a.uflag + (int64_t)plane_unit(u, a.hr, a.Hkv, a.Tq) * a.ufstride : nullptr;
   const int32_t* par = gpar ? sh.par : nullptr;
   uint32_t kept_base = 0;
   for (int base = 0; base < nF; base += ST * 4) {
@@ -1094,6 +1098,7 @@ __global__ __launch_bounds__(ST) void zha_select_small_kernel(SmallArgs a) {
       if ((flags >> e) & 1u) {
         const int id = frontier_id(par, p0 + e, a.v.C, a.v.Cshift);
         if (kr) kr[id] = ((u64)stamp << 32) | out;
+        if (uf) uf[id] = stamp;
         kept[out++] = id;
         if (p0 + e == nF - 1) sh.last_kept_id = id + 1;  // the frontier's last node is kept
       }
@@ -1478,6 +1483,9 @@ struct CompactArgs {
   int32_t* lb_error;      // set when a look-back wait gives up (never expected)
   u64* krank;             // union routes: [U][capl] (stamp << 32) | rank of each kept node; else null
   const uint32_t* route_ctr;  // the route's stamp
+  uint32_t* uflag;        // union routes at level 1: [B*Hkv][kstride] stamp of every kept chunk
+  int hr, Hkv, Tq;        // routing-unit numbering (for the unit's (sequence, KV head))
+  int stamp_keys;         // 1: keep the positions whose key equals the route's stamp (no cut)
 };
 
 constexpr int CPT = 256;  // compaction threads
@@ -1553,13 +1561,18 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
   const int nchild = a.next_nF && base + CH >= nF ? child_nodes(a.v, u) : 0;  // loaded now, used at the end
   if (tid == 0) s_epoch = __hip_atomic_load(&a.epoch[2 * u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (base >= nF) {
+    if (c == 0 && tid == 0) {  // an empty frontier (a sequence without nodes at this level)
+      a.nF_out[u] = 0;
+      a.kept_count[u] = 0;
+      if (a.next_nF) a.next_nF[u] = 0;
+    }
     compact_epilogue(a);
     return;
   }
-  const uint32_t stamp = a.krank ? a.route_ctr[0] : 0u;
-  const bool keep_all = a.keep_all || a.cut[u * 4 + 2] != 0;
-  const uint32_t tau = (uint32_t)a.cut[u * 4 + 0];
-  const int tie_last = a.cut[u * 4 + 1];
+  const uint32_t stamp = (a.krank || a.uflag || a.stamp_keys) ? a.route_ctr[0] : 0u;
+  const bool keep_all = !a.stamp_keys && (a.keep_all || a.cut[u * 4 + 2] != 0);
+  const uint32_t tau = a.stamp_keys ? 0u : (uint32_t)a.cut[u * 4 + 0];
+  const int tie_last = a.stamp_keys ? 0 : a.cut[u * 4 + 1];
   const uint32_t* keys = a.keys + (int64_t)u * a.kstride;
   const int32_t* par = a.v.parent ? a.v.parent + (int64_t)u * a.v.cap_parent : nullptr;
   const int p0 = base + CPP * tid;
@@ -1577,7 +1590,8 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int pos = p0 + 4 * j + e;
-      const bool kp = pos < nF && (keep_all || k4[e] > tau || (k4[e] == tau && pos <= tie_last));
+      const bool kp = pos < nF && (a.stamp_keys ? k4[e] == stamp
+                                                 : (keep_all || k4[e] > tau || (k4[e] == tau && pos <= tie_last)));
       flags |= kp ? (1u << (4 * j + e)) : 0u;
     }
   }
@@ -1601,10 +1615,12 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
   uint32_t out = s_before + ex;
   int32_t* kept = a.kept + (int64_t)u * a.capl;
   u64* kr = a.krank ? a.krank + (int64_t)u * a.capl : nullptr;
+  uint32_t* uf = a.uflag ? a.uflag + (int64_t)plane_unit(u, a.hr, a.Hkv, a.Tq) * a.kstride : nullptr;
 #pragma unroll
   for (int e = 0; e < CPP; ++e) {
     if ((flags >> e) & 1u) {
       if (kr) kr[id[e]] = ((u64)stamp << 32) | out;
+      if (uf) uf[id[e]] = stamp;
       kept[out++] = id[e];
       if (p0 + e == nF - 1) s_last_kept = id[e] + 1;  // the frontier's last node is kept
     }
@@ -1786,6 +1802,11 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
       sm.keep_all = keep_all ? 1 : 0;
       sm.krank = uni ? t->krank[l] : nullptr;
       sm.route_ctr = t->route_ctr;
+      sm.uflag = uni && l == 1 ? t->uflag : nullptr;
+      sm.ufstride = t->kstride;
+      sm.hr = t->hr;
+      sm.Hkv = t->desc.n_kv_heads;
+      sm.Tq = t->Tq;
       zha_time_begin(t, s, ZHA_K_SELECT, l);
       hipLaunchKernelGGL(zha_select_small_kernel, dim3(U), dim3(ST), 0, s, sm);
       e = hipGetLastError();
@@ -1850,12 +1871,55 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     ca.lb_error = t->lb_error;
     ca.krank = uni ? t->krank[l] : nullptr;
     ca.route_ctr = t->route_ctr;
+    ca.uflag = uni && l == 1 ? t->uflag : nullptr;
+    ca.hr = t->hr;
+    ca.Hkv = t->desc.n_kv_heads;
+    ca.Tq = t->Tq;
+    ca.stamp_keys = 0;
     const int nch = zha_compact_chunks(t->cap[l]);
     zha_time_begin(t, s, ZHA_K_COMPACT, l);
     hipLaunchKernelGGL(zha_compact_kernel, dim3(nch, U), dim3(CPT), 0, s, ca);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     zha_time_end(t, s, ZHA_K_COMPACT, l);
+  }
+  if (uni) {
+    // the union's level-1 kept list of every (sequence, KV head): the chunks whose flag holds
+    // this route's stamp, in order (what union attention reads)
+    CompactArgs ca;
+    ca.v.parent = nullptr;
+    ca.v.parent_nF = nullptr;
+    ca.v.cap_parent = 0;
+    ca.v.C = t->C;
+    ca.v.Cshift = Cshift;
+    ca.v.Hkv = t->desc.n_kv_heads;
+    ca.v.nodes = t->geo + t->desc.batch;  // level-1 nodes per sequence
+    ca.v.child = t->geo;
+    ca.keys = t->uflag;
+    ca.kstride = t->kstride;
+    ca.cut = t->cut;
+    ca.keep_all = 0;
+    ca.status = (u64*)t->lb_status;
+    ca.nchunk = zha_compact_chunks(t->cap[1]);
+    ca.epoch = t->lb_epoch;
+    ca.kept = t->ulist;
+    ca.capl = t->cap[1];
+    ca.nF_out = t->ucount + t->U;
+    ca.kept_count = t->ucount;
+    ca.next_nF = nullptr;
+    ca.lb_error = t->lb_error;
+    ca.krank = nullptr;
+    ca.route_ctr = t->route_ctr;
+    ca.uflag = nullptr;
+    ca.hr = 1;
+    ca.Hkv = t->desc.n_kv_heads;
+    ca.Tq = 1;
+    ca.stamp_keys = 1;
+    zha_time_begin(t, s, ZHA_K_COMPACT, 0);
+    hipLaunchKernelGGL(zha_compact_kernel, dim3(zha_compact_chunks(t->cap[1]), t->U), dim3(CPT), 0, s, ca);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    zha_time_end(t, s, ZHA_K_COMPACT, 0);
   }
   return hipSuccess;
 }

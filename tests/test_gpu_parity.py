@@ -308,6 +308,22 @@ def test_large_level_cut_paths():
         say(f" p={p}", r, a)
 
 
+def test_large_level_with_short_sequence():
+    """A batch where one sequence has no leaf chunk while the other's level 1 takes the
+    large-level path: the empty unit keeps nothing and attends its few tokens densely."""
+    cfg = small(batch=3, n_tokens=65600, n_q_heads=8, n_kv_heads=2, chunk=4, levels=2, n_refs=16, n_queries=2,
+                needles_per_unit=4)
+    lens = [65539, 3, 1]
+    say(f"case large level with short sequences: lens={lens} C=4 L=2 (16384-node level 1)")
+    case = Case(cfg, lens=lens, n_queries=2)
+    tree = case.tree()
+    for p in (0.5, 0.95):
+        r, a = full_check(case, tree, 0, p)
+        _, nk, _ = tree.route_level(1)
+        assert nk.cpu().tolist()[2:] == [0, 0, 0, 0]
+        say(f" p={p}", r, a)
+
+
 def test_equal_masses_large_level():
     """All keys zero: every node of a 10000-node level carries the same mass, so the crossing
     slice is one value held by every node (more than the candidate buffer) and the cut is
