@@ -212,8 +212,16 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   }
   // kept ranks for union routes: some route this tree may serve groups several units
   bool uni = false;
+  int ugmax = 0;  // union groups of the largest union route
   for (int i = 0; i < (desc->per_head_routes ? 2 : 1); ++i)
-    for (int tq = 1; tq <= maxq; ++tq) uni = uni || zha_union_queries(R, G, tq, hrs[i]) > 0;
+    for (int tq = 1; tq <= maxq; ++tq) {
+      const int ts = zha_union_queries(R, G, tq, hrs[i]);
+      if (ts > 0) {
+        uni = true;
+        ugmax = std::max(ugmax, U * ((tq + ts - 1) / ts));
+      }
+    }
+  t->UGmax = ugmax;
   bool ok = true;
   for (int l = 1; l <= L && ok; ++l) {
     ok = ok && dalloc(t, &t->m[l], (size_t)U * t->cap[l] * R * d * (t->f8 ? 1 : t->esize));
@@ -237,9 +245,9 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   t->kstride = (t->cap[1] + 3) / 4 * 4;
   ok = ok && dalloc(t, &t->keys, (size_t)RUmax * t->kstride * sizeof(uint32_t));
   if (uni) {
-    ok = ok && dalloc(t, &t->uflag, (size_t)U * t->kstride * sizeof(uint32_t));
-    ok = ok && dalloc(t, &t->ulist, (size_t)U * t->cap[1] * sizeof(int32_t));
-    ok = ok && dalloc(t, &t->ucount, (size_t)2 * U * sizeof(int32_t));
+    ok = ok && dalloc(t, &t->uflag, (size_t)ugmax * t->kstride * sizeof(uint32_t));
+    ok = ok && dalloc(t, &t->ulist, (size_t)ugmax * t->cap[1] * sizeof(int32_t));
+    ok = ok && dalloc(t, &t->ucount, (size_t)2 * ugmax * sizeof(int32_t));
   }
   ok = ok && dalloc(t, &t->apart, apart_n * sizeof(float));
   const int nchunk = zha_compact_chunks(t->cap[1]);
@@ -265,7 +273,7 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
     for (int l = 1; l <= L && ok && uni; ++l)
       ok = hipMemset(t->krank[l], 0, (size_t)RUmax * t->cap[l] * sizeof(unsigned long long)) == hipSuccess;
     if (uni) ok = ok && hipMemset(t->route_ctr, 0, sizeof(uint32_t)) == hipSuccess;
-    if (uni) ok = ok && hipMemset(t->uflag, 0, (size_t)U * t->kstride * sizeof(uint32_t)) == hipSuccess;
+    if (uni) ok = ok && hipMemset(t->uflag, 0, (size_t)ugmax * t->kstride * sizeof(uint32_t)) == hipSuccess;
     // every unit's epoch starts at 1: status words of epoch 0 (all-zero memory) never match
     std::vector<uint32_t> ep((size_t)RUmax * 2, 0u);
     for (int u = 0; u < RUmax; ++u) ep[(size_t)u * 2] = 1u;

@@ -42,10 +42,9 @@ struct AttArgs {
   // of its unit's set only.
   const u64* krank;        // level-1 kept ranks [U][cap1]: (stamp << 32) | rank, by chunk id
   const uint32_t* route_ctr;  // the last route's stamp
-  const int32_t* ulist;    // [B*Hkv][cap1] chunks kept by some routing unit of the (sequence, KV head)
-  const int32_t* ucount;   // [B*Hkv]
+  const int32_t* ulist;    // [groups][cap1] chunks kept by some routing unit of the group
+  const int32_t* ucount;   // [groups]
   int TS, NTC;             // queries per group; groups per (sequence, KV head)
-  int CT;                  // column tiles of a group (16 query heads each): wave w takes tile w % CT
 };
 
 // Dense launches take the lengths by value (the dense entry point gets them from the host);
@@ -230,13 +229,10 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
   // u: routing unit, of G query heads; up: its (sequence, KV head) unit.  Units are numbered
   // (sequence, query, KV head, head group), so the unit's first query head is u * G.
   // UNI: lane column `col` is head jcol of unit u; the group reads token 0, the tail up to
-  // the group's last query and the chunks some unit of the (sequence, KV head) kept, and a
-  // column takes token 0, the tokens of its unit's kept chunks and its own tail [Nc, Ne).
+  // its last query and the chunks some unit of the group kept, and a column takes token 0,
+  // the tokens of its unit's kept chunks and its own tail [Nc, Ne).
   const int G = a.G;
-  // UNI with several column tiles: the waves of one window slot ws read the same K/V rows
-  // (the cache serves all but the first) for different query heads
-  const int CT = UNI ? a.CT : 1, ct = wave % CT, ws = wave / CT, NWS = 4 / CT;
-  const int col = ct * 16 + row;
+  const int col = row;
   int u, up, bi, jcol, Ne = 0, Nc = 0;
   bool colok;
   Positions P;
@@ -254,8 +250,8 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
     Ne = a.qtail ? N + min(tq, a.Tq - 1) + 1 : N;
     const int tlast = min(tc * a.TS + a.TS, a.Tq) - 1;  // the group's last query
     const int Nend = a.qtail ? N + tlast + 1 : N;
-    const int nK = a.ucount[up];
-    const int32_t* kp = a.ulist + (int64_t)up * a.cap1;
+    const int nK = a.ucount[blockIdx.y];
+    const int32_t* kp = a.ulist + (int64_t)blockIdx.y * a.cap1;
     P.sink = (Nc > 0 && (nK == 0 || kp[0] != 0)) ? 1 : 0;
     P.nx = P.sink + (Nend - Nc);
     P.P = P.nx + nK * a.C;
@@ -274,7 +270,7 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
   const uint32_t stamp = UNI ? a.route_ctr[0] : 0u;
   // Blocks of 4 * ATT_STEP positions are dealt to the workgroups in turn, so the unit's
   // workgroups read neighbouring K/V rows at any moment.
-  const int WSTEP = NWS * ATT_STEP;
+  constexpr int WSTEP = 4 * ATT_STEP;
   const int start = blockIdx.x * WSTEP;
   const int gstep = a.W * WSTEP;
   const int end = P.P;
@@ -397,7 +393,7 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
   // Software pipeline over the wave's windows p0, p0 + gstep, ...: while window i is
   // computed, the K/V loads of window i+1 and the chunk ids of window i+2 are in flight.
   // The two register buffers alternate by unrolling the loop twice.
-  int p0 = start + ws * ATT_STEP;
+  int p0 = start + wave * ATT_STEP;
   Window<TD> w0, w1;
   typename M::frag kA[2][NK], kB[2][NK];
   typename PVT::vfrag vA, vB;
@@ -450,23 +446,22 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) so[(wave * 16 + row) * D + dt * 16 + 4 * grp + jj] = o[dt][jj];
   if (grp == 0) { sm[wave * 16 + row] = mrun; sl[wave * 16 + row] = lrun; }
-  __shared__ int s_rec[64];  // each column's (unit, workgroup, head) record; -1: no query head
-  if (ws == 0 && grp == 0) s_rec[col] = colok ? (u * a.W + (int)blockIdx.x) * G + jcol : -1;
+  __shared__ int s_rec[16];  // each column's (unit, workgroup, head) record; -1: no query head
+  if (wave == 0 && grp == 0) s_rec[col] = colok ? (u * a.W + (int)blockIdx.x) * G + jcol : -1;
   __syncthreads();
   float* pml0 = a.part + (int64_t)a.U * a.W * G * D;
-  const int ncol = UNI ? 16 * CT : G;
-  // column c: the waves c / 16, c / 16 + CT, ... hold its partial sums, in their row c % 16
+  const int ncol = UNI ? 16 : G;
   for (int i = threadIdx.x; i < ncol * D; i += 256) {
-    const int c = i / D, dd = i % D, c0 = c >> 4, h = c & 15;
-    const int rec = s_rec[c];
+    const int h = i / D, dd = i % D;
+    const int rec = s_rec[h];
     if (rec < 0) continue;
     float* po = a.part + (int64_t)rec * D;
     float* pml = pml0 + (int64_t)rec * 2;
     float Mx = -INFINITY;
-    for (int w = c0; w < 4; w += CT) Mx = fmaxf(Mx, sm[w * 16 + h]);
+    for (int w = 0; w < 4; ++w) Mx = fmaxf(Mx, sm[w * 16 + h]);
     float acc = 0.0f, l = 0.0f;
     if (Mx != -INFINITY) {
-      for (int w = c0; w < 4; w += CT) {
+      for (int w = 0; w < 4; ++w) {
         const float f = zexp2(sm[w * 16 + h] - Mx);
         acc += f * so[(w * 16 + h) * D + dd];
         l += f * sl[w * 16 + h];
@@ -621,7 +616,6 @@ hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const vo
   a.ucount = t->ucount;
   a.TS = TS;
   a.NTC = uni ? (t->Tq + TS - 1) / TS : 1;
-  a.CT = uni ? zha_union_tiles(TS, t->G) : 1;
   const int rows = uni ? t->U * a.NTC : t->RU;
   if (uni) a.W = zha_sparse_wgs(rows);
   zha_time_begin(t, s, ZHA_K_ATTEND, 0);
@@ -664,7 +658,6 @@ hipError_t zha_launch_dense(const void* q, const void* K, const void* V, const Z
   a.ucount = nullptr;
   a.TS = 0;
   a.NTC = 1;
-  a.CT = 1;
   const int U = B * Hkv;
   LensArg<true> la;
   la.len = len;

@@ -173,6 +173,10 @@ __device__ __forceinline__ int plane_unit(int u, int hr, int Hkv, int Tq) {
 }
 // The unit's query index within its sequence's block of Tq queries.
 __device__ __forceinline__ int unit_query(int u, int hr, int Hkv, int Tq) { return (u / hr / Hkv) % Tq; }
+// The unit's union group, numbered (sequence, KV head, query chunk of TS queries; NTC chunks).
+__device__ __forceinline__ int union_group(int u, int hr, int Hkv, int Tq, int TS, int NTC) {
+  return plane_unit(u, hr, Hkv, Tq) * NTC + unit_query(u, hr, Hkv, Tq) / TS;
+}
 
 // ----------------------------------------------------------------------------- host side
 
@@ -201,10 +205,11 @@ struct zha_tree {
   unsigned long long* krank[ZHA_MAX_LEVELS + 2];  // union routes: per-level (stamp << 32) | rank in the
                                     // unit's kept list, by node id [RUmax][cap] (null: no union routes)
   uint32_t* route_ctr;              // [1] stamp of the current union route (advanced on the device)
-  uint32_t* uflag;                  // union routes: [U][kstride] stamp of each leaf chunk kept by some
-                                    // routing unit of the (sequence, KV head)
-  int32_t* ulist;                   // [U][cap1] those chunks in order (the union's level-1 kept list)
-  int32_t* ucount;                  // [2][U]: chunks in the list; chunks scanned
+  uint32_t* uflag;                  // union routes: [groups][kstride] stamp of each leaf chunk kept by
+                                    // some routing unit of the union group
+  int32_t* ulist;                   // [groups][cap1] those chunks in order (the group's level-1 kept list)
+  int32_t* ucount;                  // [2][groups]: chunks in the list; chunks scanned
+  int UGmax;                        // union groups the workspace is sized for
   float* refs;                      // [Hkv][R][d]
   float* spine;                     // [U][L+1][R*16][E+2] open-node accumulators
   int S;                            // subtree level of the build (highest level of <= 256 tokens)
@@ -267,5 +272,4 @@ int zha_score_wgs_units(int RU);  // score workgroups per routing unit (before t
 // Union scoring of a route with Tq queries per sequence and hr units per (query, KV head):
 // queries per group (0: no union scoring) and groups per (sequence, KV head).
 int zha_union_queries(int R, int Gq, int Tq, int hr);
-int zha_union_tiles(int TS, int Gq);  // matrix column tiles (16 columns each) of a union group
 int zha_dense_wgs(int U);

@@ -145,14 +145,13 @@ struct ScoreArgs {
   int Hkv, Tq;            // KV heads; queries per sequence
   float scale;
   // Union scoring: one row of workgroups per group of the routing units that share one
-  // (sequence, KV head): the hr units of each of TS consecutive queries (TS * Gq <= 64
-  // matrix columns, 16 per column tile).  A node is scored once for every column; a unit
-  // keeps the scores of the nodes of its own frontier.
+  // (sequence, KV head): the hr units of each of TS consecutive queries (TS * Gq <= 16
+  // matrix columns).  A node is scored once for every column; a unit keeps the scores of
+  // the nodes of its own frontier.
   const u64* krank;       // [RU][cap_parent]: the parent level's kept nodes, (stamp << 32) | rank in
                           // the unit's kept list; null at the top level (every node is a member)
   uint32_t* route_ctr;    // route stamp; the top level's first workgroup advances it
   int TS, NTC;            // queries per group; groups per (sequence, KV head)
-  int CT;                 // column tiles of a group (16 columns each): wave w scores tile w % CT
 };
 
 // Eight fp8 e4m3 codes (two dwords) as eight bf16 values (exact), by the hardware
@@ -194,11 +193,8 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, grp = lane >> 4;
   const int G = a.G;
-  // UNI with several column tiles: the waves of one tile slot ws read the same planes (the
-  // cache serves all but the first) and score different columns
-  const int CT = UNI ? a.CT : 1, ct = wave % CT, ws = wave / CT, NWS = 4 / CT;
-  const int col = ct * 16 + row;
-  const int SUPER = NWS * UN * NPT;
+  constexpr int SUPER = 4 * UN * NPT;
+  const int col = row;
   // u: routing unit (frontier, scores, partials) of this lane's column; up: its (sequence,
   // KV head) unit (planes); qrow: the column's query row; colok: the column is a query head
   int u, up, qrow, jcol, end;
@@ -259,12 +255,12 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
 #pragma unroll
     for (int k = 0; k < UN; ++k) {
       if constexpr (UNI) {
-        const int id = base + (k * NWS + ws) * NPT + (4 * grp) / R;
+        const int id = base + (k * 4 + wave) * NPT + (4 * grp) / R;
         const int P = a.v.Cshift >= 0 ? (id >> a.v.Cshift) : id / a.v.C;
         rk[k] = (kr && colok && id < end) ? kr[P] : 0;
         pp[k] = 0;
       } else {
-        const int pos = base + (k * NWS + ws) * NPT + row / R;
+        const int pos = base + (k * 4 + wave) * NPT + row / R;
         pp[k] = (par && pos < end) ? par[a.v.Cshift >= 0 ? (pos >> a.v.Cshift) : pos / a.v.C] : 0;
         rk[k] = 0;
       }
@@ -275,7 +271,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
   auto members = [&](int base, const u64 (&rk)[UN], bool (&mem)[UN], int (&wpos)[UN], uint32_t (&act)[UN]) {
 #pragma unroll
     for (int k = 0; k < UN; ++k) {
-      const int id = base + (k * NWS + ws) * NPT + (4 * grp) / R;
+      const int id = base + (k * 4 + wave) * NPT + (4 * grp) / R;
       bool m;
       int pos;
       if (kr) {
@@ -304,7 +300,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
                         float (&bv)[UN][4]) {
 #pragma unroll
     for (int k = 0; k < UN; ++k) {
-      const int tbk = base + (k * NWS + ws) * NPT;
+      const int tbk = base + (k * 4 + wave) * NPT;
       const int pos = tbk + row / R;
       const bool v = UNI ? ((act[k] >> (row / R)) & 1u) != 0 : pos < end;
       int id = pos;
@@ -337,7 +333,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
   // its column when its node is a member, at the column unit's frontier position.
   auto score_tile = [&](int k, const Frag (&afk)[NK], const float (&bvk)[4], const float (&rs)[4], int base,
                         bool memk, int wposk) {
-    const int tbk = base + (k * NWS + ws) * NPT;
+    const int tbk = base + (k * 4 + wave) * NPT;
     f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < NK; ++s) acc = M::mma(afk[s], qf[s], acc);
@@ -391,7 +387,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
                          float (&bv)[UN][4], float (&sv)[UN][4]) {
 #pragma unroll
     for (int k = 0; k < UN; ++k) {
-      const int tbk = base + (k * NWS + ws) * NPT;
+      const int tbk = base + (k * 4 + wave) * NPT;
       const int pos = tbk + row / R;
       const bool v = UNI ? ((act[k] >> (row / R)) & 1u) != 0 : pos < end;
       int id = pos;
@@ -486,7 +482,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
       base += step;
     }
   }
-  // per-column (max, sum exp) of this workgroup: lanes of one column, then the waves
+  // per-column (max, sum exp) of this workgroup: lanes of one column, then the 4 waves
   {
     float M2 = __shfl_xor(runM, 16), S2 = __shfl_xor(runS, 16);
     lse_merge(runM, runS, M2, S2);
@@ -495,17 +491,15 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
     lse_merge(runM, runS, M2, S2);
   }
   __shared__ float sM[4][16], sS[4][16];
-  __shared__ int sU[64], sJ[64];
-  __shared__ bool sOk[64];
+  __shared__ int sU[16], sJ[16];
+  __shared__ bool sOk[16];
   if (grp == 0) { sM[wave][row] = runM; sS[wave][row] = runS; }
-  if (ws == 0 && grp == 0) { sU[col] = u; sJ[col] = jcol; sOk[col] = colok; }
+  if (wave == 0 && grp == 0) { sU[row] = u; sJ[row] = jcol; sOk[row] = colok; }
   __syncthreads();
-  // column c: the waves c / 16, c / 16 + CT, ... scored it
   const int c = threadIdx.x;
-  if (c < 16 * CT && sOk[c]) {
-    const int c0 = c >> 4, r = c & 15;
-    float Mx = sM[c0][r], Sx = sS[c0][r];
-    for (int w = c0 + CT; w < 4; w += CT) lse_merge(Mx, Sx, sM[w][r], sS[w][r]);
+  if (c < 16 && sOk[c]) {
+    float Mx = sM[0][c], Sx = sS[0][c];
+    for (int w = 1; w < 4; ++w) lse_merge(Mx, Sx, sM[w][c], sS[w][c]);
     float* pp = a.part + (((int64_t)sU[c] * a.W + blockIdx.x) * G + sJ[c]) * 2;
     pp[0] = Mx;
     pp[1] = Sx;
@@ -948,9 +942,9 @@ struct SmallArgs {
   int keep_all;
   u64* krank;             // union routes: [U][capl] (stamp << 32) | rank of each kept node; else null
   const uint32_t* route_ctr;  // the route's stamp
-  uint32_t* uflag;        // union routes at level 1: [B*Hkv][ufstride] stamp of every kept chunk
+  uint32_t* uflag;        // union routes at level 1: [groups][ufstride] stamp of every kept chunk
   int64_t ufstride;
-  int hr, Hkv, Tq;        // routing-unit numbering (for the unit's (sequence, KV head))
+  int hr, Hkv, Tq, TS, NTC;  // routing-unit numbering and union groups (for the unit's group)
 };
 
 constexpr int SBATCH = 8;     // frontier positions per thread per load batch
@@ -1077,7 +1071,7 @@ __global__ __launch_bounds__(ST) void zha_select_small_kernel(SmallArgs a) {
   // compaction in position order (chunks of 4 positions per thread)
   int32_t* kept = a.kept + (int64_t)u * a.capl;
   u64* kr = a.krank ? a.krank + (int64_t)u * a.capl : nullptr;
-  uint32_t* uf = a.uflag ? a.uflag + (int64_t)plane_unit(u, a.hr, a.Hkv, a.Tq) * a.ufstride : nullptr;
+  uint32_t* uf = a.uflag ? a.uflag + (int64_t)union_group(u, a.hr, a.Hkv, a.Tq, a.TS, a.NTC) * a.ufstride : nullptr;
   const int32_t* par = gpar ? sh.par : nullptr;
   uint32_t kept_base = 0;
   for (int base = 0; base < nF; base += ST * 4) {
@@ -1483,8 +1477,8 @@ struct CompactArgs {
   int32_t* lb_error;      // set when a look-back wait gives up (never expected)
   u64* krank;             // union routes: [U][capl] (stamp << 32) | rank of each kept node; else null
   const uint32_t* route_ctr;  // the route's stamp
-  uint32_t* uflag;        // union routes at level 1: [B*Hkv][kstride] stamp of every kept chunk
-  int hr, Hkv, Tq;        // routing-unit numbering (for the unit's (sequence, KV head))
+  uint32_t* uflag;        // union routes at level 1: [groups][kstride] stamp of every kept chunk
+  int hr, Hkv, Tq, TS, NTC;  // routing-unit numbering and union groups (for the unit's group)
   int stamp_keys;         // 1: keep the positions whose key equals the route's stamp (no cut)
 };
 
@@ -1615,7 +1609,7 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
   uint32_t out = s_before + ex;
   int32_t* kept = a.kept + (int64_t)u * a.capl;
   u64* kr = a.krank ? a.krank + (int64_t)u * a.capl : nullptr;
-  uint32_t* uf = a.uflag ? a.uflag + (int64_t)plane_unit(u, a.hr, a.Hkv, a.Tq) * a.kstride : nullptr;
+  uint32_t* uf = a.uflag ? a.uflag + (int64_t)union_group(u, a.hr, a.Hkv, a.Tq, a.TS, a.NTC) * a.kstride : nullptr;
 #pragma unroll
   for (int e = 0; e < CPP; ++e) {
     if ((flags >> e) & 1u) {
@@ -1695,21 +1689,17 @@ int zha_score_wgs(const zha_tree* t, int level) {
 }
 
 // Union scoring groups the routing units that share one (sequence, KV head): the hr units of
-// each of TS consecutive queries, TS * Gq <= 64 columns in up to four matrix column tiles.
-// Only worth it (and only built) when a group holds several units and a tile row holds one
+// each of TS consecutive queries, TS * Gq <= 16 columns of the matrix tile.  (Wider groups
+// in several column tiles, one per wave, measured no faster: every wave still loads each
+// tile, and a window shared by four waves leaves a quarter of the loads in flight.)  Only
+// worth it (and only built) when a group holds several units and a tile row holds one
 // node's planes for one lane group (R >= 4).
 int zha_union_queries(int R, int Gq, int Tq, int hr) {
   if (R < 4 || Gq < 1 || Gq > 16) return 0;
-  int ts = 64 / Gq;
+  int ts = 16 / Gq;
   if (ts > Tq) ts = Tq;
   if (ts < 1) ts = 1;
   return ts * hr > 1 ? ts : 0;
-}
-
-// Column tiles of a union group of TS queries (Gq columns each): 1, 2 or 4.
-int zha_union_tiles(int TS, int Gq) {
-  const int cols = TS * Gq;
-  return cols <= 16 ? 1 : (cols <= 32 ? 2 : 4);
 }
 
 int zha_compact_chunks(int64_t nodes) { return (int)((nodes + CH - 1) / CH); }
@@ -1729,7 +1719,6 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
   const int TS = zha_union_queries(t->R, t->G, t->Tq, t->hr);
   const bool uni = TS > 0 && t->krank[1] != nullptr;
   const int NTC = uni ? (t->Tq + TS - 1) / TS : 1;
-  const int CT = uni ? zha_union_tiles(TS, t->G) : 1;
   const int rows = uni ? t->U * NTC : U;  // rows of the scoring grid
   hipError_t e;
   for (int l = L; l >= 1; --l) {
@@ -1765,7 +1754,6 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     sa.route_ctr = uni ? t->route_ctr : nullptr;
     sa.TS = TS;
     sa.NTC = NTC;
-    sa.CT = CT;
     sa.G = Gr;
     sa.hr = t->hr;
     sa.Hkv = t->desc.n_kv_heads;
@@ -1807,6 +1795,8 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
       sm.hr = t->hr;
       sm.Hkv = t->desc.n_kv_heads;
       sm.Tq = t->Tq;
+      sm.TS = TS;
+      sm.NTC = NTC;
       zha_time_begin(t, s, ZHA_K_SELECT, l);
       hipLaunchKernelGGL(zha_select_small_kernel, dim3(U), dim3(ST), 0, s, sm);
       e = hipGetLastError();
@@ -1875,6 +1865,8 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     ca.hr = t->hr;
     ca.Hkv = t->desc.n_kv_heads;
     ca.Tq = t->Tq;
+    ca.TS = TS;
+    ca.NTC = NTC;
     ca.stamp_keys = 0;
     const int nch = zha_compact_chunks(t->cap[l]);
     zha_time_begin(t, s, ZHA_K_COMPACT, l);
@@ -1884,15 +1876,16 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     zha_time_end(t, s, ZHA_K_COMPACT, l);
   }
   if (uni) {
-    // the union's level-1 kept list of every (sequence, KV head): the chunks whose flag holds
-    // this route's stamp, in order (what union attention reads)
+    // the level-1 kept list of every union group: the chunks whose flag holds this route's
+    // stamp, in order (what union attention reads); groups are numbered (sequence, KV head,
+    // query chunk)
     CompactArgs ca;
     ca.v.parent = nullptr;
     ca.v.parent_nF = nullptr;
     ca.v.cap_parent = 0;
     ca.v.C = t->C;
     ca.v.Cshift = Cshift;
-    ca.v.Hkv = t->desc.n_kv_heads;
+    ca.v.Hkv = t->desc.n_kv_heads * NTC;  // groups per sequence
     ca.v.nodes = t->geo + t->desc.batch;  // level-1 nodes per sequence
     ca.v.child = t->geo;
     ca.keys = t->uflag;
@@ -1904,7 +1897,7 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     ca.epoch = t->lb_epoch;
     ca.kept = t->ulist;
     ca.capl = t->cap[1];
-    ca.nF_out = t->ucount + t->U;
+    ca.nF_out = t->ucount + t->U * NTC;
     ca.kept_count = t->ucount;
     ca.next_nF = nullptr;
     ca.lb_error = t->lb_error;
@@ -1914,9 +1907,11 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     ca.hr = 1;
     ca.Hkv = t->desc.n_kv_heads;
     ca.Tq = 1;
+    ca.TS = 1;
+    ca.NTC = 1;
     ca.stamp_keys = 1;
     zha_time_begin(t, s, ZHA_K_COMPACT, 0);
-    hipLaunchKernelGGL(zha_compact_kernel, dim3(zha_compact_chunks(t->cap[1]), t->U), dim3(CPT), 0, s, ca);
+    hipLaunchKernelGGL(zha_compact_kernel, dim3(zha_compact_chunks(t->cap[1]), t->U * NTC), dim3(CPT), 0, s, ca);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     zha_time_end(t, s, ZHA_K_COMPACT, 0);
