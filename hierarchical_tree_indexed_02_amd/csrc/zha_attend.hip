@@ -609,7 +609,7 @@ hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const vo
   a.lens = t->geo;
   // union attention: the groups of the route's union scoring, when it had one
   const int TS = zha_union_queries(t->R, t->G, t->Tq, t->hr);
-  const bool uni = TS > 0 && t->krank[1] != nullptr;
+  const bool uni = t->uni_route;
   a.krank = uni ? t->krank[1] : nullptr;
   a.route_ctr = t->route_ctr;
   a.ulist = t->ulist;

@@ -210,6 +210,7 @@ struct zha_tree {
   int32_t* ulist;                   // [groups][cap1] those chunks in order (the group's level-1 kept list)
   int32_t* ucount;                  // [2][groups]: chunks in the list; chunks scanned
   int UGmax;                        // union groups the workspace is sized for
+  bool uni_route;                   // the last route ran the union kernels
   float* refs;                      // [Hkv][R][d]
   float* spine;                     // [U][L+1][R*16][E+2] open-node accumulators
   int S;                            // subtree level of the build (highest level of <= 256 tokens)

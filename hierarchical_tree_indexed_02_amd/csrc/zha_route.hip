@@ -1717,7 +1717,11 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
   const bool keep_all = p >= 1.0f;
   // union scoring: groups of the units sharing one (sequence, KV head), TS queries each
   const int TS = zha_union_queries(t->R, t->G, t->Tq, t->hr);
-  const bool uni = TS > 0 && t->krank[1] != nullptr;
+  // Union kernels pay a walk over each level's node ids and a list per group; they win when
+  // the units' kept sets overlap much (high p) or a group holds many units, and lose for
+  // pairs of units with sparse sets (measured: two queries of a block at p = 0.7, batch 8).
+  const bool uni = TS > 0 && t->krank[1] != nullptr && (TS * t->hr >= 4 || p >= 0.8f);
+  t->uni_route = uni;
   const int NTC = uni ? (t->Tq + TS - 1) / TS : 1;
   const int rows = uni ? t->U * NTC : U;  // rows of the scoring grid
   hipError_t e;
