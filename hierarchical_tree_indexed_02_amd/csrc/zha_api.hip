@@ -202,10 +202,13 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
       score_n = std::max(score_n, (size_t)ru * ((Gr + 3) & ~3));
       cand_n = std::max(cand_n, zha_sel_cand_entries(ru));
       ctr_n = std::max(ctr_n, zha_sel_ctr_words(ru));
-      const int ts = zha_union_queries(R, G, tq, hr);
-      if (ts > 0) {  // union scoring: partials of every unit for each workgroup of its group
-        const int ng = U * ((tq + ts - 1) / ts);
+      const int ts = zha_union_queries(R, G, tq, hr), tss = zha_union_score_queries(R, G, tq, hr);
+      if (tss > 0) {  // union scoring: partials of every unit for each workgroup of its group
+        const int ng = U * ((tq + tss - 1) / tss);
         spart_n = std::max(spart_n, (size_t)ru * zha_score_wgs_units(ng) * Gr * 2);
+      }
+      if (ts > 0) {  // union attention: partials of every unit for each workgroup of its group
+        const int ng = U * ((tq + ts - 1) / ts);
         apart_n = std::max(apart_n, (size_t)ru * zha_sparse_wgs(ng) * Gr * (d + 2));
       }
     }
@@ -220,6 +223,7 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
         uni = true;
         ugmax = std::max(ugmax, U * ((tq + ts - 1) / ts));
       }
+      uni = uni || zha_union_score_queries(R, G, tq, hrs[i]) > 0;
     }
   t->UGmax = ugmax;
   bool ok = true;

@@ -179,35 +179,40 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 // registers, and the query fragments take the same k order (the dot product does not
 // depend on it); the row's scale multiplies the product.
 // UNI (R >= 4): the workgroup row scores the union of the frontiers of a group of routing
-// units in node-id order; column c is head j of unit cu(c); a node is loaded when some
-// column's unit has its parent kept (a stamped rank entry), and each column keeps the
-// scores of its unit's member nodes at the unit's frontier positions.
-template <typename T, int R, int D, int UN, bool F8, bool UNI>
+// units in node-id order, in NT column tiles of 16 (column c = 16 * tile + lane row is head
+// jcol of unit cu(c)): every loaded plane tile feeds NT matrix products.  A node is loaded
+// when some column's unit has its parent kept (a stamped rank entry), and each column keeps
+// the scores of its unit's member nodes at the unit's frontier positions.
+template <typename T, int R, int D, int UN, bool F8, bool UNI, int NT>
 __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a) {
   typedef Mf<T> M;
   constexpr int NK = D / M::KPER;
   constexpr int NR = F8 ? D / 64 : 1;   // 16-byte code loads per lane per tile (F8)
   constexpr int NPT = 16 / R;
+  constexpr int SUPER = 4 * UN * NPT;
   static_assert(!F8 || M::EPL == 8, "fp8 planes feed the bf16 matrix instruction");
   static_assert(!UNI || R >= 4, "union scoring keeps one node per lane group");
+  static_assert(UNI || NT == 1, "one column tile unless scoring unions");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, grp = lane >> 4;
   const int G = a.G;
-  constexpr int SUPER = 4 * UN * NPT;
-  const int col = row;
-  // u: routing unit (frontier, scores, partials) of this lane's column; up: its (sequence,
-  // KV head) unit (planes); qrow: the column's query row; colok: the column is a query head
-  int u, up, qrow, jcol, end;
-  bool colok;
+  // per column tile n: u[n] the routing unit (frontier, scores, partials) of this lane's
+  // column, jc[n] its head in the unit, ok[n] the column is a query head; up: the (sequence,
+  // KV head) unit whose planes are scored
+  int u[NT], jc[NT], up, end;
+  bool ok[NT];
   if constexpr (UNI) {
     up = blockIdx.y / a.NTC;
     const int tc = blockIdx.y - up * a.NTC, bi = up / a.Hkv, g = up - bi * a.Hkv;
     const int per_t = a.hr * G;  // columns per query
-    const int tt = col / per_t, h = (col / G) % a.hr, t = tc * a.TS + tt;
-    colok = tt < a.TS && t < a.Tq;
-    u = ((bi * a.Tq + min(t, a.Tq - 1)) * a.Hkv + g) * a.hr + h;
-    jcol = col % G;
-    qrow = u * G + jcol;
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int col = 16 * n + row;
+      const int tt = col / per_t, h = (col / G) % a.hr, t = tc * a.TS + tt;
+      ok[n] = tt < a.TS && t < a.Tq;
+      u[n] = ((bi * a.Tq + min(t, a.Tq - 1)) * a.Hkv + g) * a.hr + h;
+      jc[n] = col % G;
+    }
     end = a.v.nodes[bi];
     if (a.route_ctr && !a.krank && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
       // top level of a route: a new stamp, so kept ranks written by earlier routes stop matching
@@ -215,12 +220,11 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
       __hip_atomic_store(a.route_ctr, s0 + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else {
-    u = blockIdx.y;
-    up = plane_unit(u, a.hr, a.Hkv, a.Tq);
-    colok = row < G;
-    jcol = row;
-    qrow = u * G + row;
-    end = frontier_size(a.v, u);
+    u[0] = blockIdx.y;
+    up = plane_unit(u[0], a.hr, a.Hkv, a.Tq);
+    ok[0] = row < G;
+    jc[0] = row;
+    end = frontier_size(a.v, u[0]);
   }
   const uint32_t stamp = (UNI && a.krank) ? a.route_ctr[0] : 0u;
   // Super-tiles are dealt to the workgroups in turn: at any moment the unit's workgroups
@@ -228,63 +232,72 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
   const int start = blockIdx.x * SUPER;
   const int step = a.W * SUPER;
 
-  typename M::frag qf[NK];
-  {
-    const T* qp = (const T*)a.q + (int64_t)qrow * D;
+  typename M::frag qf[NT][NK];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const T* qp = (const T*)a.q + ((int64_t)u[n] * G + jc[n]) * D;
 #pragma unroll
     for (int s = 0; s < NK; ++s) {
       const int k0 = F8 ? grp * (D / 4) + s * 8 : s * M::KPER + grp * M::EPL;
-      qf[s] = colok ? M::load(qp + k0) : M::zero();
+      qf[n][s] = ok[n] ? M::load(qp + k0) : M::zero();
     }
   }
-  const int32_t* par = (!UNI && a.v.parent) ? a.v.parent + (int64_t)u * a.v.cap_parent : nullptr;
-  const u64* kr = (UNI && a.krank) ? a.krank + (int64_t)u * a.v.cap_parent : nullptr;
+  const int32_t* par = (!UNI && a.v.parent) ? a.v.parent + (int64_t)u[0] * a.v.cap_parent : nullptr;
   const T* mb = (const T*)a.m + (int64_t)up * a.capl * R * D;
   const uint8_t* m8 = (const uint8_t*)a.m + (int64_t)up * a.capl * R * D;
   const float* bb = a.b + (int64_t)up * a.capl * R;
   const float* sb = F8 ? a.ms + (int64_t)up * a.capl * R : nullptr;
   const int GS = score_stride(G);
-  float* sc = a.scores + (int64_t)u * a.cap1 * GS;
-  float runM = -INFINITY, runS = 0.0f;
+  float runM[NT], runS[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) { runM[n] = -INFINITY; runS[n] = 0.0f; }
 
   typedef typename M::frag Frag;
   // Parent entries of this lane's tiles in the super-tile at `base` (the one load a node
-  // id depends on).  UNI: the kept-rank entry of the parent of the lane's node (4grp/R)
-  // for the lane's column unit.
-  auto fetch_par = [&](int base, int (&pp)[UN], u64 (&rk)[UN]) {
+  // id depends on).  UNI: the kept-rank entries of the parent of the lane's node (4grp/R)
+  // for the lane's column units.
+  auto fetch_par = [&](int base, int (&pp)[UN], u64 (&rk)[UN][NT]) {
 #pragma unroll
     for (int k = 0; k < UN; ++k) {
       if constexpr (UNI) {
         const int id = base + (k * 4 + wave) * NPT + (4 * grp) / R;
         const int P = a.v.Cshift >= 0 ? (id >> a.v.Cshift) : id / a.v.C;
-        rk[k] = (kr && colok && id < end) ? kr[P] : 0;
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+          rk[k][n] = (a.krank && ok[n] && id < end) ? a.krank[(int64_t)u[n] * a.v.cap_parent + P] : 0;
         pp[k] = 0;
       } else {
         const int pos = base + (k * 4 + wave) * NPT + row / R;
         pp[k] = (par && pos < end) ? par[a.v.Cshift >= 0 ? (pos >> a.v.Cshift) : pos / a.v.C] : 0;
-        rk[k] = 0;
+        rk[k][0] = 0;
       }
     }
   };
-  // UNI: membership of the lane's node for its column (mem), the node's position in the
+  // UNI: membership of the lane's node for its columns (mem), the node's position in each
   // column unit's frontier (wpos), and which nodes of each tile some column needs (act).
-  auto members = [&](int base, const u64 (&rk)[UN], bool (&mem)[UN], int (&wpos)[UN], uint32_t (&act)[UN]) {
+  auto members = [&](int base, const u64 (&rk)[UN][NT], bool (&mem)[UN][NT], int (&wpos)[UN][NT],
+                     uint32_t (&act)[UN]) {
 #pragma unroll
     for (int k = 0; k < UN; ++k) {
       const int id = base + (k * 4 + wave) * NPT + (4 * grp) / R;
-      bool m;
-      int pos;
-      if (kr) {
-        m = colok && id < end && (uint32_t)(rk[k] >> 32) == stamp;
-        const int rank = (int)(uint32_t)rk[k];
-        pos = a.v.Cshift >= 0 ? (rank << a.v.Cshift) + (id & ((1 << a.v.Cshift) - 1)) : rank * a.v.C + id % a.v.C;
-      } else {
-        m = colok && id < end;
-        pos = id;
+      bool any = false;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        bool m;
+        int pos;
+        if (a.krank) {
+          m = ok[n] && id < end && (uint32_t)(rk[k][n] >> 32) == stamp;
+          const int rank = (int)(uint32_t)rk[k][n];
+          pos = a.v.Cshift >= 0 ? (rank << a.v.Cshift) + (id & ((1 << a.v.Cshift) - 1)) : rank * a.v.C + id % a.v.C;
+        } else {
+          m = ok[n] && id < end;
+          pos = id;
+        }
+        mem[k][n] = m;
+        wpos[k][n] = pos;
+        any = any || m;
       }
-      mem[k] = m;
-      wpos[k] = pos;
-      const u64 bal = __ballot(m);
+      const u64 bal = __ballot(any);
       // node n of the tile is handled by lanes [n * 64 / NPT, (n + 1) * 64 / NPT)
       uint32_t am = 0;
 #pragma unroll
@@ -328,57 +341,62 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
       }
     }
   };
-  // Scores of tile k of the super-tile at `base` from its plane fragments (F8: rs holds the
-  // rows' scales, which multiply the product; unused otherwise).  UNI: the lane writes for
-  // its column when its node is a member, at the column unit's frontier position.
+  // Scores of tile k of the super-tile at `base` from its plane fragments, for every column
+  // tile (F8: rs holds the rows' scales, which multiply the product; unused otherwise).
+  // UNI: the lane writes for a column when its node is a member of the column's unit, at
+  // that unit's frontier position.
   auto score_tile = [&](int k, const Frag (&afk)[NK], const float (&bvk)[4], const float (&rs)[4], int base,
-                        bool memk, int wposk) {
+                        const bool (&memk)[NT], const int (&wposk)[NT]) {
     const int tbk = base + (k * 4 + wave) * NPT;
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int s = 0; s < NK; ++s) acc = M::mma(afk[s], qf[s], acc);
-    float v[4];
+    for (int n = 0; n < NT; ++n) {
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const float mul = F8 ? a.scale * rs[jj] : a.scale;
-      v[jj] = bvk[jj] == -INFINITY ? -INFINITY : fmaf(acc[jj], mul, bvk[jj]);
-    }
-    // maximum over each node's planes; rows 4*grp+jj of this lane belong to node (4*grp+jj)/R
-    if (R >= 4) {
-      float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-      if (R >= 8) mx = fmaxf(mx, __shfl_xor(mx, 16));
-      if (R >= 16) mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool writer = (R == 4) || (R == 8 && (grp & 1) == 0) || (R == 16 && grp == 0);
-      const int pos = UNI ? wposk : tbk + (4 * grp) / R;
-      const bool ok = UNI ? memk : (colok && pos < end);
-      if (writer && ok) {
-        sc[(int64_t)pos * GS + jcol] = mx;
-        lse_push(runM, runS, mx);
-      }
-    } else if (R == 2) {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const float mx = fmaxf(v[2 * h2], v[2 * h2 + 1]);
-        const int pos = tbk + 2 * grp + h2;
-        if (colok && pos < end) {
-          sc[(int64_t)pos * GS + jcol] = mx;
-          lse_push(runM, runS, mx);
-        }
-      }
-    } else {
+      for (int s = 0; s < NK; ++s) acc = M::mma(afk[s], qf[n][s], acc);
+      float v[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int pos = tbk + 4 * grp + jj;
-        if (colok && pos < end) {
-          sc[(int64_t)pos * GS + jcol] = v[jj];
-          lse_push(runM, runS, v[jj]);
+        const float mul = F8 ? a.scale * rs[jj] : a.scale;
+        v[jj] = bvk[jj] == -INFINITY ? -INFINITY : fmaf(acc[jj], mul, bvk[jj]);
+      }
+      float* sc = a.scores + (int64_t)u[n] * a.cap1 * GS;
+      // maximum over each node's planes; rows 4*grp+jj of this lane belong to node (4*grp+jj)/R
+      if (R >= 4) {
+        float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+        if (R >= 8) mx = fmaxf(mx, __shfl_xor(mx, 16));
+        if (R >= 16) mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool writer = (R == 4) || (R == 8 && (grp & 1) == 0) || (R == 16 && grp == 0);
+        const int pos = UNI ? wposk[n] : tbk + (4 * grp) / R;
+        const bool wr = UNI ? memk[n] : (ok[n] && pos < end);
+        if (writer && wr) {
+          sc[(int64_t)pos * GS + jc[n]] = mx;
+          lse_push(runM[n], runS[n], mx);
+        }
+      } else if (R == 2) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const float mx = fmaxf(v[2 * h2], v[2 * h2 + 1]);
+          const int pos = tbk + 2 * grp + h2;
+          if (ok[n] && pos < end) {
+            sc[(int64_t)pos * GS + jc[n]] = mx;
+            lse_push(runM[n], runS[n], mx);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int pos = tbk + 4 * grp + jj;
+          if (ok[n] && pos < end) {
+            sc[(int64_t)pos * GS + jc[n]] = v[jj];
+            lse_push(runM[n], runS[n], v[jj]);
+          }
         }
       }
     }
   };
 
-  auto compute = [&](const Frag (&af)[UN][NK], const float (&bv)[UN][4], int base, const bool (&mem)[UN],
-                     const int (&wpos)[UN]) {
+  auto compute = [&](const Frag (&af)[UN][NK], const float (&bv)[UN][4], int base, const bool (&mem)[UN][NT],
+                     const int (&wpos)[UN][NT]) {
 #pragma unroll
     for (int k = 0; k < UN; ++k) score_tile(k, af[k], bv[k], bv[k], base, mem[k], wpos[k]);
   };
@@ -421,7 +439,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
   // F8: decode the codes (lane k-slots s*8 .. s*8+7 of its d/4 codes per matrix step),
   // then score as the bf16 path does with the row scale in the multiplier.
   auto compute8 = [&](const uint4 (&rw)[UN][NR], const float (&bv)[UN][4], const float (&sv)[UN][4], int base,
-                      const bool (&mem)[UN], const int (&wpos)[UN]) {
+                      const bool (&mem)[UN][NT], const int (&wpos)[UN][NT]) {
     if constexpr (F8) {
 #pragma unroll
       for (int k = 0; k < UN; ++k) {
@@ -440,9 +458,9 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
   // the next and the parent entries of the one after are in flight.  The two register
   // buffers alternate by unrolling the loop twice.
   int ppA[UN], ppB[UN];
-  u64 rkA[UN], rkB[UN];
-  bool mA[UN], mB[UN];
-  int wA[UN], wB[UN];
+  u64 rkA[UN][NT], rkB[UN][NT];
+  bool mA[UN][NT], mB[UN][NT];
+  int wA[UN][NT], wB[UN][NT];
   uint32_t acA[UN], acB[UN];
   float bvA[UN][4], bvB[UN][4];
   fetch_par(start, ppA, rkA);
@@ -483,21 +501,23 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
     }
   }
   // per-column (max, sum exp) of this workgroup: lanes of one column, then the 4 waves
-  {
-    float M2 = __shfl_xor(runM, 16), S2 = __shfl_xor(runS, 16);
-    lse_merge(runM, runS, M2, S2);
-    M2 = __shfl_xor(runM, 32);
-    S2 = __shfl_xor(runS, 32);
-    lse_merge(runM, runS, M2, S2);
+  __shared__ float sM[4][16 * NT], sS[4][16 * NT];
+  __shared__ int sU[16 * NT], sJ[16 * NT];
+  __shared__ bool sOk[16 * NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    float rM = runM[n], rS = runS[n];
+    float M2 = __shfl_xor(rM, 16), S2 = __shfl_xor(rS, 16);
+    lse_merge(rM, rS, M2, S2);
+    M2 = __shfl_xor(rM, 32);
+    S2 = __shfl_xor(rS, 32);
+    lse_merge(rM, rS, M2, S2);
+    if (grp == 0) { sM[wave][16 * n + row] = rM; sS[wave][16 * n + row] = rS; }
+    if (wave == 0 && grp == 0) { sU[16 * n + row] = u[n]; sJ[16 * n + row] = jc[n]; sOk[16 * n + row] = ok[n]; }
   }
-  __shared__ float sM[4][16], sS[4][16];
-  __shared__ int sU[16], sJ[16];
-  __shared__ bool sOk[16];
-  if (grp == 0) { sM[wave][row] = runM; sS[wave][row] = runS; }
-  if (wave == 0 && grp == 0) { sU[row] = u; sJ[row] = jcol; sOk[row] = colok; }
   __syncthreads();
   const int c = threadIdx.x;
-  if (c < 16 && sOk[c]) {
+  if (c < 16 * NT && sOk[c]) {
     float Mx = sM[0][c], Sx = sS[0][c];
     for (int w = 1; w < 4; ++w) lse_merge(Mx, Sx, sM[w][c], sS[w][c]);
     float* pp = a.part + (((int64_t)sU[c] * a.W + blockIdx.x) * G + sJ[c]) * 2;
@@ -1638,20 +1658,29 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
 
 // Two tiles per wave per pipeline stage (for fp8 codes too: four would not fit in the
 // registers of four workgroups per compute unit, and fewer workgroups measured slower).
-template <typename T, int R, int D, bool F8, bool UNI>
+template <typename T, int R, int D, bool F8, bool UNI, int NT = 1>
 hipError_t launch_score(const ScoreArgs& a, int W, int rows, hipStream_t s) {
-  hipLaunchKernelGGL((zha_score_kernel<T, R, D, 2, F8, UNI>), dim3(W, rows), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((zha_score_kernel<T, R, D, 2, F8, UNI, NT>), dim3(W, rows), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-// rows: routing units, or groups of them (uni; R >= 4 there)
+template <typename T, int R, int D, bool F8>
+hipError_t launch_score_uni(const ScoreArgs& a, int W, int rows, int NT, hipStream_t s) {
+  switch (NT) {
+    case 1: return launch_score<T, R, D, F8, true, 1>(a, W, rows, s);
+    case 2: return launch_score<T, R, D, F8, true, 2>(a, W, rows, s);
+    default: return launch_score<T, R, D, F8, true, 4>(a, W, rows, s);
+  }
+}
+
+// rows: routing units, or groups of them (uni; R >= 4 there, NT column tiles of 16)
 template <typename T, int D, bool F8 = false>
-hipError_t launch_score_r(const ScoreArgs& a, int R, int W, int rows, bool uni, hipStream_t s) {
+hipError_t launch_score_r(const ScoreArgs& a, int R, int W, int rows, bool uni, int NT, hipStream_t s) {
   if (uni) {
     switch (R) {
-      case 4: return launch_score<T, 4, D, F8, true>(a, W, rows, s);
-      case 8: return launch_score<T, 8, D, F8, true>(a, W, rows, s);
-      default: return launch_score<T, 16, D, F8, true>(a, W, rows, s);
+      case 4: return launch_score_uni<T, 4, D, F8>(a, W, rows, NT, s);
+      case 8: return launch_score_uni<T, 8, D, F8>(a, W, rows, NT, s);
+      default: return launch_score_uni<T, 16, D, F8>(a, W, rows, NT, s);
     }
   }
   switch (R) {
@@ -1688,19 +1717,21 @@ int zha_score_wgs(const zha_tree* t, int level) {
   return (int)w;
 }
 
-// Union scoring groups the routing units that share one (sequence, KV head): the hr units of
-// each of TS consecutive queries, TS * Gq <= 16 columns of the matrix tile.  (Wider groups
-// in several column tiles, one per wave, measured no faster: every wave still loads each
-// tile, and a window shared by four waves leaves a quarter of the loads in flight.)  Only
-// worth it (and only built) when a group holds several units and a tile row holds one
-// node's planes for one lane group (R >= 4).
-int zha_union_queries(int R, int Gq, int Tq, int hr) {
+// Union groups hold the routing units that share one (sequence, KV head): the hr units of
+// each of TS consecutive queries.  Attention (and the kept-chunk flags the selections write
+// for it) groups TS * Gq <= 16 query heads: one column tile, four windows in flight per
+// workgroup.  Scoring groups up to 64 (four column tiles in every wave, one plane load for
+// all of them).  Only worth it (and only built) when a group holds several units and a tile
+// row holds one node's planes for one lane group (R >= 4).
+static int union_queries(int R, int Gq, int Tq, int hr, int cols) {
   if (R < 4 || Gq < 1 || Gq > 16) return 0;
-  int ts = 16 / Gq;
+  int ts = cols / Gq;
   if (ts > Tq) ts = Tq;
   if (ts < 1) ts = 1;
   return ts * hr > 1 ? ts : 0;
 }
+int zha_union_queries(int R, int Gq, int Tq, int hr) { return union_queries(R, Gq, Tq, hr, 16); }
+int zha_union_score_queries(int R, int Gq, int Tq, int hr) { return union_queries(R, Gq, Tq, hr, 64); }
 
 int zha_compact_chunks(int64_t nodes) { return (int)((nodes + CH - 1) / CH); }
 int zha_hist_bins() { return NB; }
@@ -1716,14 +1747,20 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
   int32_t* cntK = t->counts + (int64_t)(L + 2) * U;  // [L+2][U]
   const bool keep_all = p >= 1.0f;
   // union scoring: groups of the units sharing one (sequence, KV head), TS queries each
-  const int TS = zha_union_queries(t->R, t->G, t->Tq, t->hr);
-  // Union kernels pay a walk over each level's node ids and a list per group; they win when
-  // the units' kept sets overlap much (high p) or a group holds many units, and lose for
-  // pairs of units with sparse sets (measured: two queries of a block at p = 0.7, batch 8).
-  const bool uni = TS > 0 && t->krank[1] != nullptr && (TS * t->hr >= 4 || p >= 0.8f);
+  // Union kernels pay a walk over each level's node ids (scoring) or a list per group
+  // (attention); they win when the units' kept sets overlap much (high p) or a group holds
+  // many units, and lose for pairs of units with sparse sets (measured: two queries of a
+  // block at p = 0.7, batch 8).
+  const int TS = zha_union_queries(t->R, t->G, t->Tq, t->hr);         // attention groups
+  const int TSs = zha_union_score_queries(t->R, t->G, t->Tq, t->hr);  // scoring groups
+  const bool can = t->krank[1] != nullptr;
+  const bool uni = can && TS > 0 && (TS * t->hr >= 4 || p >= 0.8f);
+  const bool uni_s = can && TSs > 0 && (TSs * t->hr >= 4 || p >= 0.8f);
   t->uni_route = uni;
   const int NTC = uni ? (t->Tq + TS - 1) / TS : 1;
-  const int rows = uni ? t->U * NTC : U;  // rows of the scoring grid
+  const int NTCs = uni_s ? (t->Tq + TSs - 1) / TSs : 1;
+  const int NT = uni_s ? (TSs * t->G + 15) / 16 : 1;  // column tiles of a scoring group
+  const int rows = uni_s ? t->U * NTCs : U;             // rows of the scoring grid
   hipError_t e;
   for (int l = L; l >= 1; --l) {
     Level v;
@@ -1747,17 +1784,17 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     sa.scores = t->scores;
     sa.cap1 = t->cap[1];
     sa.part = t->spart;
-    if (uni) {
+    if (uni_s) {
       int64_t w = (t->cap[l] + 7) / 8;
       const int wr = zha_score_wgs_units(rows);
       sa.W = (int)(w < 1 ? 1 : (w > wr ? wr : w));
     } else {
       sa.W = zha_score_wgs(t, l);
     }
-    sa.krank = uni && l < L ? t->krank[l + 1] : nullptr;
-    sa.route_ctr = uni ? t->route_ctr : nullptr;
-    sa.TS = TS;
-    sa.NTC = NTC;
+    sa.krank = uni_s && l < L ? t->krank[l + 1] : nullptr;
+    sa.route_ctr = (uni || uni_s) ? t->route_ctr : nullptr;
+    sa.TS = TSs;
+    sa.NTC = NTCs;
     sa.G = Gr;
     sa.hr = t->hr;
     sa.Hkv = t->desc.n_kv_heads;
@@ -1765,14 +1802,14 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     sa.scale = scale;
     zha_time_begin(t, s, ZHA_K_SCORE, l);
     if (t->f8)
-      e = t->d == 64 ? launch_score_r<__bf16, 64, true>(sa, t->R, sa.W, rows, uni, s)
-                     : launch_score_r<__bf16, 128, true>(sa, t->R, sa.W, rows, uni, s);
+      e = t->d == 64 ? launch_score_r<__bf16, 64, true>(sa, t->R, sa.W, rows, uni_s, NT, s)
+                     : launch_score_r<__bf16, 128, true>(sa, t->R, sa.W, rows, uni_s, NT, s);
     else if (t->desc.dtype == ZHA_BF16)
-      e = t->d == 64 ? launch_score_r<__bf16, 64>(sa, t->R, sa.W, rows, uni, s)
-                     : launch_score_r<__bf16, 128>(sa, t->R, sa.W, rows, uni, s);
+      e = t->d == 64 ? launch_score_r<__bf16, 64>(sa, t->R, sa.W, rows, uni_s, NT, s)
+                     : launch_score_r<__bf16, 128>(sa, t->R, sa.W, rows, uni_s, NT, s);
     else
-      e = t->d == 64 ? launch_score_r<float, 64>(sa, t->R, sa.W, rows, uni, s)
-                     : launch_score_r<float, 128>(sa, t->R, sa.W, rows, uni, s);
+      e = t->d == 64 ? launch_score_r<float, 64>(sa, t->R, sa.W, rows, uni_s, NT, s)
+                     : launch_score_r<float, 128>(sa, t->R, sa.W, rows, uni_s, NT, s);
     if (e != hipSuccess) return e;
     zha_time_end(t, s, ZHA_K_SCORE, l);
 
@@ -1792,7 +1829,7 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
       sm.G = Gr;
       sm.p = p;
       sm.keep_all = keep_all ? 1 : 0;
-      sm.krank = uni ? t->krank[l] : nullptr;
+      sm.krank = (uni_s && l > 1) || (uni && l == 1) ? t->krank[l] : nullptr;
       sm.route_ctr = t->route_ctr;
       sm.uflag = uni && l == 1 ? t->uflag : nullptr;
       sm.ufstride = t->kstride;
@@ -1863,7 +1900,7 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     ca.kept_count = cntK + (int64_t)l * U;
     ca.next_nF = next_nF;
     ca.lb_error = t->lb_error;
-    ca.krank = uni ? t->krank[l] : nullptr;
+    ca.krank = (uni_s && l > 1) || (uni && l == 1) ? t->krank[l] : nullptr;
     ca.route_ctr = t->route_ctr;
     ca.uflag = uni && l == 1 ? t->uflag : nullptr;
     ca.hr = t->hr;
