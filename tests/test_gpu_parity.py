@@ -239,6 +239,8 @@ MULTI_VARIANTS = [
                                                             chunk=4, levels=2, n_refs=16), [65539], 3, "group", 3),
     ("block bf16 d128 C4 L3 R4 G4 B3 T4 short sequences", dict(batch=3, n_tokens=600, n_q_heads=16, chunk=4,
                                                                  levels=3, n_refs=4), [3, 1, 517], 4, "group", 4),
+    ("block bf16 d64 C4 L3 R4 G1 T16", dict(batch=2, n_tokens=3000, head_dim=64, n_q_heads=2, n_kv_heads=2, chunk=4,
+                                             levels=3, n_refs=4), [2950, 1234], 16, "group", 16),
 ]
 
 
@@ -306,6 +308,23 @@ def test_large_level_cut_paths():
     for p in (1e-6, 0.3, 0.9, 0.999999):
         r, a = full_check(case, tree, int(p < 0.5), p)
         say(f" p={p}", r, a)
+
+
+def test_maximum_shapes():
+    """The largest batch (64 sequences of ragged lengths), 16 query heads per KV head, 16
+    references, and 12 levels of chunk 2."""
+    cfg = small(batch=64, n_tokens=3000, n_q_heads=16, n_kv_heads=1, head_dim=64, chunk=2, levels=12, n_refs=16,
+                n_queries=2, needles_per_unit=2)
+    rng = np.random.default_rng(5)
+    lens = [int(x) for x in rng.integers(1, 3001, 64)]
+    lens[0], lens[1] = 1, 3000
+    say(f"case maximum shapes: B=64 lens {min(lens)}..{max(lens)}, G=16, C=2 L=12 R=16 d=64")
+    case = Case(cfg, lens=lens, n_queries=2)
+    tree = case.tree()
+    torch.cuda.synchronize()
+    say(" build", check_build(case, tree, sample=64))
+    r, a = full_check(case, tree, 0, 0.9)
+    say(" p=0.9", r, a)
 
 
 def test_large_level_with_short_sequence():
