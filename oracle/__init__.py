@@ -69,6 +69,12 @@ def _bind(path: str):
     L.zo_e4m3_row_exp.argtypes = [ctypes.c_double]
     L.zo_fp8_rows.restype = None
     L.zo_fp8_rows.argtypes = [_f64p, _i64, _int, _f64p, _f64p]
+    L.zo_e2m1_round.restype = ctypes.c_double
+    L.zo_e2m1_round.argtypes = [ctypes.c_double]
+    L.zo_e2m1_block_exp.restype = _int
+    L.zo_e2m1_block_exp.argtypes = [ctypes.c_double]
+    L.zo_fp4_rows.restype = None
+    L.zo_fp4_rows.argtypes = [_f64p, _i64, _int, _f64p, _f64p]
     L.zo_num_threads.restype = _int
     L.zo_num_threads.argtypes = []
     L.zo_set_num_threads.restype = None
@@ -157,6 +163,35 @@ def fp8_rows(m):
 def fp8_planes(m, lse, refs):
     """Planes with fp8-stored means: (m~ [n][R][d], b~ = LSE - r.m~ [n][R], scale [n][R])."""
     mq, sc = fp8_rows(m)
+    b = _f64(lse) - np.einsum("nrd,rd->nr", mq, _f64(refs))
+    return mq, b, sc
+
+
+def e2m1_round(x: float) -> float:
+    """Nearest OCP fp4 e2m1 value to x (|x| <= 6), ties to even mantissa."""
+    return lib().zo_e2m1_round(float(x))
+
+
+def e2m1_block_exp(amax: float) -> int:
+    """Smallest s with amax * 2^-s <= 6 (0 for amax = 0)."""
+    return lib().zo_e2m1_block_exp(float(amax))
+
+
+def fp4_rows(m):
+    """fp4 summary storage of rows m [..., d] (d a multiple of 32): (m~ = grid value * 2^s per
+    block of 32 values, scales 2^s [..., d / 32])."""
+    m = _f64(m)
+    shp = m.shape
+    d = shp[-1]
+    flat = m.reshape(-1, d)
+    out = np.empty_like(flat); sc = np.empty((flat.shape[0], d // 32))
+    lib().zo_fp4_rows(_p(flat, _f64p), flat.shape[0], d, _p(out, _f64p), _p(sc, _f64p))
+    return out.reshape(shp), sc.reshape(shp[:-1] + (d // 32,))
+
+
+def fp4_planes(m, lse, refs):
+    """Planes with fp4-stored means: (m~ [n][R][d], b~ = LSE - r.m~ [n][R], scales [n][R][d/32])."""
+    mq, sc = fp4_rows(m)
     b = _f64(lse) - np.einsum("nrd,rd->nr", mq, _f64(refs))
     return mq, b, sc
 

@@ -273,6 +273,58 @@ ZO_EXPORT void zo_fp8_rows(const double* m, int64_t n, int d, double* out, doubl
     }
 }
 
+/* ------------------------------------------------------- fp4 router summaries
+ *
+ * The 4-bit reading of the same passage ([wqu] opening bullets).  The grid is
+ * OCP fp4 e2m1: sign, 2 exponent bits with bias 1, 1 mantissa bit; magnitudes
+ * 0 and 0.5 (subnormal), 1, 1.5, 2, 3, 4, 6.  Four bits cannot hold a whole row
+ * under one scale, so a row of m is cut into blocks of 32 consecutive values,
+ * each stored as grid values times a power of two 2^s, s the smallest integer
+ * with max|m_block| 2^-s <= 6; each value rounded to the nearest grid value,
+ * ties to the value whose mantissa bit is 0.  b = LSE - r.m~ from the stored m~.
+ */
+
+/* Nearest e2m1 grid value to x (|x| <= 6), ties to even mantissa. */
+ZO_EXPORT double zo_e2m1_round(double x)
+{
+    const double a = fabs(x);
+    const double step = a < 2.0 ? 0.5 : (a < 4.0 ? 1.0 : 2.0);   /* spacing of the binade */
+    const double n = a / step;
+    double r = floor(n);
+    const double frac = n - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    const double v = r * step;
+    return x < 0 ? -v : v;
+}
+
+/* Scale exponent s of a block with largest magnitude amax: the smallest integer
+ * with amax 2^-s <= 6 (0 for an all-zero block). */
+ZO_EXPORT int zo_e2m1_block_exp(double amax)
+{
+    if (!(amax > 0.0)) return 0;
+    int e;
+    frexp(amax, &e);
+    int s = e - 4;                             /* amax 2^-s >= 2^3 > 6 */
+    while (ldexp(amax, -s) > 6.0) ++s;
+    return s;
+}
+
+/* Stores n rows of d values (d a multiple of 32) as fp4 summaries: out = grid
+ * value * 2^s per block of 32, scale[i][k / 32] = 2^s. */
+ZO_EXPORT void zo_fp4_rows(const double* m, int64_t n, int d, double* out, double* scale)
+{
+    const int nb = d / 32;
+    for (int64_t i = 0; i < n; ++i)
+        for (int blk = 0; blk < nb; ++blk) {
+            const double* mb = m + i * d + blk * 32;
+            double amax = 0.0;
+            for (int k = 0; k < 32; ++k) amax = fmax(amax, fabs(mb[k]));
+            const int sx = zo_e2m1_block_exp(amax);
+            for (int k = 0; k < 32; ++k) out[i * d + blk * 32 + k] = ldexp(zo_e2m1_round(ldexp(mb[k], -sx)), sx);
+            scale[i * nb + blk] = ldexp(1.0, sx);
+        }
+}
+
 /* Node score for head h: the maximum over the R tangent planes (query pre-scaled). */
 static double zo_score(const double* m_node, const double* b_node, int R, int d, const double* qh)
 {

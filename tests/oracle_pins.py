@@ -490,10 +490,81 @@ def pin_fp8_rows():
         _close(at_r, t.lse[l], 1e-12, f"fp8 plane at q = r, level {l}")
 
 
+def _e2m1_grid():
+    """Every OCP e2m1 value by its code (sign, 2-bit exponent with bias 1, 1 mantissa bit;
+    exponent field 0 is subnormal)."""
+    vals = {}
+    for c in range(16):
+        sgn, e, f = c >> 3, (c >> 1) & 3, c & 1
+        v = f * 0.5 if e == 0 else (1 + f / 2) * 2.0 ** (e - 1)
+        vals[c] = -v if sgn else v
+    return vals
+
+
+def pin_fp4_quantizer():
+    """The oracle's e2m1 rounding equals enumeration of the format's 16 codes (nearest, ties
+    to the even mantissa) on grid points, midpoints, just off midpoints and random values;
+    the grid is 0, 0.5, 1, 1.5, 2, 3, 4, 6."""
+    grid = _e2m1_grid()
+    pos = sorted(set(v for v in grid.values() if v >= 0))
+    assert pos == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    xs = []
+    for a, b in zip(pos, pos[1:]):
+        mid = 0.5 * (a + b)
+        xs += [a, mid, mid * (1 + 1e-9), mid * (1 - 1e-9), b]
+    rng = np.random.default_rng(8)
+    xs += list(rng.uniform(-6, 6, 3000))
+    for x in xs + [-v for v in xs]:
+        best = None
+        for c, v in grid.items():
+            d = abs(v - x)
+            if best is None or d < best[0] or (d == best[0] and (c & 1) == 0 and (best[1] & 1) == 1):
+                best = (d, c, v)
+        got = oracle.e2m1_round(x)
+        assert abs(got) == abs(best[2]), (x, got, best)
+
+
+def pin_fp4_blocks():
+    """Block storage: each block of 32 values has the smallest power-of-two scale bringing its
+    largest magnitude within 6 (checked against the neighbouring exponent), every stored
+    value is a grid value times its block's scale with error within half a grid step, and
+    blocks do not share scales; fp4 planes stay exact at q = r."""
+    grid = set(abs(v) for v in _e2m1_grid().values())
+    rng = np.random.default_rng(9)
+    m = rng.standard_normal((24, 128)) * 10.0 ** rng.uniform(-4, 3, (24, 1))
+    m[2] = 0.0
+    m[4, :32] = 6.0 * 2.0 ** -5            # an exact power-of-two boundary in one block
+    m[6, 32:64] *= 1e3                     # one loud block beside quiet ones
+    mq, sc = oracle.fp4_rows(m)
+    assert sc.shape == (24, 4)
+    for i in range(m.shape[0]):
+        for blk in range(4):
+            xb, qb, s = m[i, 32 * blk:32 * blk + 32], mq[i, 32 * blk:32 * blk + 32], sc[i, blk]
+            amax = np.max(np.abs(xb))
+            assert math.log2(s) == int(math.log2(s)), "scale is a power of two"
+            if amax == 0:
+                assert np.all(qb == 0) and s == 1.0
+                continue
+            assert amax / s <= 6.0 and amax / (s / 2) > 6.0, f"row {i} block {blk}: scale not minimal"
+            for v, x in zip(qb, xb):
+                assert abs(v) / s in grid, f"row {i} block {blk}: {v} is not a grid value times the scale"
+                a = abs(x) / s
+                half = 0.25 if a < 2.0 else (0.5 if a < 4.0 else 1.0)
+                assert abs(v - x) / s <= half * (1 + 1e-12), f"row {i} block {blk}: error beyond half a step"
+    assert sc[6, 1] > 100 * sc[6, 0], "each block has its own scale"
+    K, _, refs, _ = _rand(10, 40, 64, 4, 1)
+    t = oracle.tree_definition(K, refs, 4, 2)
+    for l in (1, 2):
+        mq, b, _ = oracle.fp4_planes(t.m[l], t.lse[l], refs)
+        at_r = b + np.einsum("nrd,rd->nr", mq, refs)
+        _close(at_r, t.lse[l], 1e-12, f"fp4 plane at q = r, level {l}")
+
+
 ALL_PINS = [
     pin_geometry, pin_tangent_planes, pin_merge_equals_definition, pin_top_p_minimal,
     pin_bruteforce_tiny, pin_nucleus_single_tokens, pin_exact_reference, pin_translation_permutation,
     pin_value_closed_forms, pin_equal_masses, pin_single_level_nesting, pin_growth,
     pin_dense_two_ways, pin_p_one_is_dense, pin_attend_set, pin_fp8_quantizer, pin_fp8_rows,
     pin_block_attend_set, pin_block_p_one_is_causal, pin_block_first_query_is_decode,
+    pin_fp4_quantizer, pin_fp4_blocks,
 ]

@@ -57,6 +57,12 @@ MUTANTS = [
      "for (int64_t x = N; x < E; ++x) in[x] = 1;"),
     ("block_tail_to_block_end", "int64_t E = N + t + 1;          /* positions 0 .. N+t may be read */",
      "int64_t E = N + t + 2;          /* positions 0 .. N+t may be read */"),
+    ("e2m1_ties_away", "    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;\n    const double v = r * step;\n    return x < 0 ? -v : v;\n}\n\n/* Scale exponent s of a block",
+     "    if (frac >= 0.5) r += 1.0;\n    const double v = r * step;\n    return x < 0 ? -v : v;\n}\n\n/* Scale exponent s of a block"),
+    ("e2m1_uniform_step", "const double step = a < 2.0 ? 0.5 : (a < 4.0 ? 1.0 : 2.0);", "const double step = 0.5;"),
+    ("fp4_scale_not_minimal", "while (ldexp(amax, -s) > 6.0) ++s;", "while (ldexp(amax, -s) > 3.0) ++s;"),
+    ("fp4_one_scale_per_row", "for (int k = 0; k < 32; ++k) amax = fmax(amax, fabs(mb[k]));",
+     "for (int k = 0; k < d; ++k) amax = fmax(amax, fabs(m[i * d + k]));"),
     ("attention_one_head", "const double* qh = q + (int64_t)h * d;\n        double mx = -INFINITY;\n        for (int64_t i = 0; i < nS; ++i) {",
      "const double* qh = q;\n        double mx = -INFINITY;\n        for (int64_t i = 0; i < nS; ++i) {"),
 ]
