@@ -41,10 +41,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-queries", type=int, default=12)
-    ap.add_argument("--summary", choices=["native", "fp8"], default="native",
+    ap.add_argument("--summary", choices=["native", "fp8", "fp4"], default="native",
                     help="storage of the planes' m for the headline measurement")
     ap.add_argument("--no-fp8", action="store_true",
-                    help="skip the extra pass with fp8 summaries (reported beside the headline)")
+                    help="skip the extra passes with fp8 and fp4 summaries (reported beside the headline)")
     ap.add_argument("--block", type=int, default=8,
                     help="also route and attend blocks of this many queries per sequence (0: skip)")
     ap.add_argument("--no-per-head", action="store_true",
@@ -379,7 +379,7 @@ def main():
         dom_live_us = 1e3 * sum(live) / len(live)
 
         # algorithmic bytes of each step (routes are deterministic: replay each query once, untimed)
-        S_node = R * (d + 8) if summary == "fp8" else R * (d * es + 4)
+        S_node = {"fp8": R * (d + 8), "fp4": R * (d // 2 + d // 32 + 4)}.get(summary, R * (d * es + 4))
         RU = U * (G if mode == "per_head" else 1)  # routing units
         Gr = G if mode == "group" else 1           # query heads per routing unit
         fr_tot = {l: 0 for l in range(1, L + 1)}
@@ -448,17 +448,19 @@ def main():
     ms_step, step_bytes, kappa, kernels = res["ms_step"], res["step_bytes"], res["kappa"], res["kernels"]
     roofline, seg_us, fr_tot, build_ms = res["roofline"], res["seg_us"], res["fr_tot"], res["build_ms"]
     layer_lens, dense_bytes, nsteps = res["layer_lens"], res["dense_bytes"], res["nsteps"]
-    fp8 = None
+    low = {}  # the same workload with low-precision summaries
     if not args.no_fp8 and args.summary == "native" and cfg.dtype == "bf16":
-        log("-- the same workload with fp8 summaries")
-        r8 = measure("fp8")
-        fp8 = dict(us_per_step=round(r8["ms_step"] * 1e3, 2), step_bytes=round(r8["step_bytes"]),
-                   step_gbs=round(r8["step_bytes"] / (r8["ms_step"] * 1e-3) / 1e9, 1), kappa=round(r8["kappa"], 4),
-                   roofline=r8["roofline"], build_us=round(1e3 * float(np.median(r8["build_ms"])), 1),
-                   tree_bytes=r8["tree_bytes"],
-                   kernels={k: round(v["avg_us"], 2) for k, v in r8["kernels"].items()})
-        if growing:
-            fp8["p_sweep"] = {str(x): round(r8["seg_us"].get("append", 0.0) + r8["seg_us"][x], 2) for x in p_sweep}
+        for sm in ("fp8", "fp4"):
+            log(f"-- the same workload with {sm} summaries")
+            r8 = measure(sm)
+            low[sm] = dict(us_per_step=round(r8["ms_step"] * 1e3, 2), step_bytes=round(r8["step_bytes"]),
+                           step_gbs=round(r8["step_bytes"] / (r8["ms_step"] * 1e-3) / 1e9, 1),
+                           kappa=round(r8["kappa"], 4), roofline=r8["roofline"],
+                           build_us=round(1e3 * float(np.median(r8["build_ms"])), 1), tree_bytes=r8["tree_bytes"],
+                           kernels={k: round(v["avg_us"], 2) for k, v in r8["kernels"].items()})
+            if growing:
+                low[sm]["p_sweep"] = {str(x): round(r8["seg_us"].get("append", 0.0) + r8["seg_us"][x], 2)
+                                      for x in p_sweep}
     sweep = None
     if args.sweep and not growing:
         sweep = geometry_sweep(measure, cfg, zi, torch, np, dev, N, B, Hkv, d, es, log)
@@ -547,8 +549,8 @@ def main():
         "kernels": {k: dict(launches=v["launches"], avg_us=round(v["avg_us"], 2)) for k, v in kernels.items()},
     }
     result["config"]["summary"] = args.summary
-    if fp8 is not None:
-        result["fp8_summaries"] = fp8
+    for sm, v in low.items():
+        result[f"{sm}_summaries"] = v
     if per_head is not None:
         result["per_head_routes"] = per_head
     if sweep is not None:

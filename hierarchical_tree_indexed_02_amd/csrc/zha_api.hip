@@ -48,8 +48,9 @@ zha_status check_desc(const zha_tree_desc* d) {
       d->max_tokens < 1 || d->head_dim < 1)
     return ZHA_ERR_INVALID;
   if (d->dtype != ZHA_F32 && d->dtype != ZHA_BF16) return ZHA_ERR_INVALID;
-  if (d->summary != ZHA_SUMMARY_NATIVE && d->summary != ZHA_SUMMARY_FP8) return ZHA_ERR_INVALID;
-  if (d->summary == ZHA_SUMMARY_FP8 && d->dtype != ZHA_BF16) return ZHA_ERR_UNSUPPORTED;
+  if (d->summary != ZHA_SUMMARY_NATIVE && d->summary != ZHA_SUMMARY_FP8 && d->summary != ZHA_SUMMARY_FP4)
+    return ZHA_ERR_INVALID;
+  if (d->summary != ZHA_SUMMARY_NATIVE && d->dtype != ZHA_BF16) return ZHA_ERR_UNSUPPORTED;
   if (d->n_q_heads % d->n_kv_heads != 0) return ZHA_ERR_INVALID;
   if (d->max_queries < 0) return ZHA_ERR_INVALID;
   {  // routing units of the largest route index the second grid dimension
@@ -167,6 +168,7 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   t->T = desc->max_tokens;
   t->esize = desc->dtype == ZHA_BF16 ? 2 : 4;
   t->f8 = desc->summary == ZHA_SUMMARY_FP8;
+  t->f4 = desc->summary == ZHA_SUMMARY_FP4;
   const int64_t Nc = (t->T / t->C) * t->C;
   int64_t span = 1;
   for (int l = 1; l <= t->L; ++l) {
@@ -228,9 +230,11 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   t->UGmax = ugmax;
   bool ok = true;
   for (int l = 1; l <= L && ok; ++l) {
-    ok = ok && dalloc(t, &t->m[l], (size_t)U * t->cap[l] * R * d * (t->f8 ? 1 : t->esize));
+    const size_t mrow = t->f4 ? (size_t)d / 2 : (size_t)d * (t->f8 ? 1 : t->esize);  // bytes per m row
+    ok = ok && dalloc(t, &t->m[l], (size_t)U * t->cap[l] * R * mrow);
     ok = ok && dalloc(t, &t->b[l], (size_t)U * t->cap[l] * R * sizeof(float));
     if (t->f8) ok = ok && dalloc(t, &t->ms[l], (size_t)U * t->cap[l] * R * sizeof(float));
+    if (t->f4) ok = ok && dalloc(t, &t->ms[l], (size_t)U * t->cap[l] * R * (d / 32));
     ok = ok && dalloc(t, &t->kept[l], (size_t)RUmax * t->cap[l] * sizeof(int32_t));
     if (uni) ok = ok && dalloc(t, &t->krank[l], (size_t)RUmax * t->cap[l] * sizeof(unsigned long long));
   }
@@ -443,6 +447,10 @@ zha_status zha_tree_copy_level(zha_tree_t t, int32_t level, void* m_out, float* 
     const hipError_t e = zha_launch_decode_fp8((const uint8_t*)t->m[level], t->ms[level], (int64_t)nm, t->d,
                                                (__bf16*)m_out, s);
     if (e != hipSuccess) return hip_fail("zha_tree_copy_level", e);
+  } else if (t->f4) {
+    const hipError_t e = zha_launch_decode_fp4((const uint8_t*)t->m[level], (const uint8_t*)t->ms[level], (int64_t)nm,
+                                               t->d, (__bf16*)m_out, nullptr, s);
+    if (e != hipSuccess) return hip_fail("zha_tree_copy_level", e);
   } else if (hipMemcpyAsync(m_out, t->m[level], nm * t->d * t->esize, hipMemcpyDeviceToDevice, s) != hipSuccess) {
     return ZHA_ERR_HIP;
   }
@@ -452,8 +460,13 @@ zha_status zha_tree_copy_level(zha_tree_t t, int32_t level, void* m_out, float* 
 }
 
 zha_status zha_tree_copy_scales(zha_tree_t t, int32_t level, float* scale_out, hipStream_t s) {
-  if (!t || !scale_out || level < 1 || level > t->L || !t->f8) return ZHA_ERR_INVALID;
+  if (!t || !scale_out || level < 1 || level > t->L || !(t->f8 || t->f4)) return ZHA_ERR_INVALID;
   const size_t nm = (size_t)t->U * t->cap[level] * t->R;
+  if (t->f4) {
+    const hipError_t e = zha_launch_decode_fp4((const uint8_t*)t->m[level], (const uint8_t*)t->ms[level], (int64_t)nm,
+                                               t->d, nullptr, scale_out, s);
+    return e == hipSuccess ? ZHA_OK : hip_fail("zha_tree_copy_scales", e);
+  }
   if (hipMemcpyAsync(scale_out, t->ms[level], nm * sizeof(float), hipMemcpyDeviceToDevice, s) != hipSuccess)
     return ZHA_ERR_HIP;
   return ZHA_OK;

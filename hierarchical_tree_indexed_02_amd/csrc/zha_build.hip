@@ -33,7 +33,9 @@ struct BuildArgs {
   const float* refs;        // [Hkv][R][d]
   void* m[ZHA_MAX_LEVELS + 2];
   float* b[ZHA_MAX_LEVELS + 2];
-  float* ms[ZHA_MAX_LEVELS + 2];    // fp8 summaries: row scales (m holds e4m3 codes); null entries otherwise
+  float* ms[ZHA_MAX_LEVELS + 2];    // fp8 summaries: row scales (m holds e4m3 codes); fp4: scale bytes per
+                                    // block of 32 (m holds e2m1 codes); null entries otherwise
+  int f4;                           // the low-precision summaries are fp4
   int64_t cap[ZHA_MAX_LEVELS + 2];
   int64_t lpn[ZHA_MAX_LEVELS + 2];  // leaves per node at level l: C^(l-1)
   float* spine;             // [U][L+1][E+2][NT]
@@ -159,14 +161,54 @@ __device__ __forceinline__ void leaf_planes(const T* Kb, int64_t c, int C, int l
   acc_finish(acc, lse, m);
 }
 
+// fp4 codes of one lane's E values (scaled by 2^-ex, |value| <= 6 after scaling), element 2i
+// in the low nibble of byte i, and the decoded values m~ = code * 2^ex.
+template <int E>
+__device__ __forceinline__ uint32_t fp4_encode(const float (&m)[E], int ex, float (&mt)[E]) {
+  static_assert(E == 4 || E == 8, "two or four code bytes per lane");
+  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = __builtin_ldexpf(m[e], -ex);
+  const float sc = __builtin_ldexpf(1.0f, ex);
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[0], x[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], 1.0f, 1);
+  auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0);
+  auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1);
+  mt[0] = v0[0]; mt[1] = v0[1]; mt[2] = v1[0]; mt[3] = v1[1];
+  if constexpr (E == 8) {
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4], x[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[6], x[7], 1.0f, 3);
+    auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2);
+    auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3);
+    mt[4] = v2[0]; mt[5] = v2[1]; mt[6] = v3[0]; mt[7] = v3[1];
+  }
+  return w;
+}
+
 // Store node j of level l: m~ = m rounded to the storage type, b = LSE - r.m~.  With fp8
-// summaries the row (16 lanes) shares one power-of-two scale from its largest magnitude.
+// summaries the row (16 lanes) shares one power-of-two scale from its largest magnitude;
+// with fp4, each block of 32 values (32/E lanes) has its own.
 template <typename T, int E, int D>
 __device__ __forceinline__ void emit(const BuildArgs& a, int u, int l, int64_t j, int r, int ln, const float (&rv)[E],
                                      float lse, const float (&m)[E]) {
   const int64_t row = ((int64_t)u * a.cap[l] + j) * a.R + r;
   float mt[E];
-  if (a.ms[l]) {
+  if (a.ms[l] && a.f4) {
+    constexpr int LB = 32 / E;  // lanes per block: a quad (d = 128) or a half row (d = 64)
+    static_assert(LB == 4 || LB == 8, "blocks of 32 values");
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(m[e]));
+    amax = fmaxf(amax, dpp_mov<0xB1>(amax));   // quad_perm [1,0,3,2]
+    amax = fmaxf(amax, dpp_mov<0x4E>(amax));   // quad_perm [2,3,0,1]: the quad's maximum
+    if (LB == 8) amax = fmaxf(amax, dpp_mov<0x141>(amax));  // row_half_mirror: the half row's
+    const int ex = fp4_block_exp(amax);
+    const uint32_t w = fp4_encode<E>(m, ex, mt);
+    uint8_t* cp = (uint8_t*)a.m[l] + row * (D / 2) + ln * (E / 2);
+    if constexpr (E == 8) *(uint32_t*)cp = w;
+    else *(uint16_t*)cp = (uint16_t)w;
+    if (ln % LB == 0) ((uint8_t*)a.ms[l])[row * (D / 32) + ln / LB] = (uint8_t)(ex + 127);
+  } else if (a.ms[l]) {
     float amax = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(m[e]));
@@ -463,6 +505,7 @@ BuildArgs make_args(const zha_tree* t, const void* K) {
     a.m[l] = t->m[l];
     a.b[l] = t->b[l];
     a.ms[l] = t->ms[l];
+    a.f4 = t->f4 ? 1 : 0;
     a.cap[l] = t->cap[l];
     a.lpn[l] = l >= 1 ? t->span[l] / t->C : 1;
   }
@@ -572,6 +615,33 @@ hipError_t zha_launch_append(zha_tree* t, const void* K, hipStream_t s) {
   if (e != hipSuccess) return e;
   zha_time_end(t, s, ZHA_K_APPEND, 0);
   return hipSuccess;
+}
+
+// Decoded fp4 summaries: out[row][k] = value(code) * 2^e of k's block, exact in bf16, and the
+// block scales as floats into scale_out [rows][d/32] (either output may be null).
+__global__ __launch_bounds__(256) void zha_decode_fp4_kernel(const uint8_t* codes, const uint8_t* scale, int64_t rows,
+                                                              int d, __bf16* out, float* scale_out) {
+  const int64_t n = rows * d / 2;  // code bytes
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t k = (2 * i) % d, rw = (2 * i) / d;
+    const float sc = fp4_scale(scale[rw * (d / 32) + k / 32]);
+    if (out) {
+      const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((uint32_t)codes[i], sc, 0);
+      out[2 * i] = Mf<__bf16>::from_f32(v[0]);
+      out[2 * i + 1] = Mf<__bf16>::from_f32(v[1]);
+    }
+    if (scale_out && k % 32 == 0) scale_out[rw * (d / 32) + k / 32] = sc;
+  }
+}
+
+hipError_t zha_launch_decode_fp4(const uint8_t* codes, const uint8_t* scale, int64_t rows, int d, __bf16* out,
+                                 float* scale_out, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  int64_t blocks = (rows * d / 2 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zha_decode_fp4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes, scale, rows, d, out,
+                     scale_out);
+  return hipGetLastError();
 }
 
 hipError_t zha_launch_decode_fp8(const uint8_t* codes, const float* scale, int64_t rows, int d, __bf16* out,

@@ -85,6 +85,25 @@ __device__ __forceinline__ int fp8_row_exp(float amax) {
   return ea - 8 + (mant > 0x600000u ? 1 : 0);
 }
 
+// fp4 (OCP e2m1) summaries: a row of m is cut into blocks of 32 values, each stored as e2m1
+// codes (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte with element 2i in the low
+// nibble of byte i, times a power-of-two scale 2^e, e the smallest integer with
+// max|m_block| * 2^-e <= 6, kept as the byte e + 127.  The hardware conversion rounds to the
+// nearest e2m1 value, ties to even mantissa (checked against enumeration of the format on
+// grid points, midpoints and near-midpoints; a negative value that rounds to zero keeps its
+// sign, which decodes to the same zero); decoding with the scale folded in is exact.
+
+// Scale exponent of a block whose largest magnitude is amax (0 for an all-zero block).
+__device__ __forceinline__ int fp4_block_exp(float amax) {
+  if (!(amax >= 1e-30f)) return 0;
+  const uint32_t u = __float_as_uint(amax);
+  const int ea = (int)((u >> 23) & 0xFF) - 127;   // amax = M * 2^ea, M in [1, 2)
+  const uint32_t mant = u & 0x7FFFFFu;            // M > 1.5 <=> mantissa field > 0.5 * 2^23
+  return ea - 2 + (mant > 0x400000u ? 1 : 0);
+}
+// Scale 2^e of a stored scale byte e + 127.
+__device__ __forceinline__ float fp4_scale(uint32_t byte) { return __uint_as_float(byte << 23); }
+
 // Value of e4m3 code c (normal or subnormal; codes here never hold NaN).
 __device__ __forceinline__ float fp8_value(uint32_t c) {
   const uint32_t e = (c >> 3) & 15u, m = c & 7u;
@@ -199,8 +218,10 @@ struct zha_tree {
   int64_t span[ZHA_MAX_LEVELS + 2]; // tokens covered by one node at each level: C^l
   void* m[ZHA_MAX_LEVELS + 2];      // level planes m [U][cap][R][d] (tree dtype, or fp8 e4m3 codes)
   float* b[ZHA_MAX_LEVELS + 2];     // level planes b [U][cap][R]
-  float* ms[ZHA_MAX_LEVELS + 2];    // fp8 summaries: power-of-two scale of each m row [U][cap][R] (else null)
+  float* ms[ZHA_MAX_LEVELS + 2];    // fp8 summaries: power-of-two scale of each m row [U][cap][R];
+                                    // fp4: scale bytes [U][cap][R][d/32] (else null)
   bool f8;                          // m stored as fp8 e4m3 codes
+  bool f4;                          // m stored as fp4 e2m1 codes; ms holds a scale byte per block of 32
   int32_t* kept[ZHA_MAX_LEVELS + 2];// per-level kept ids [U][cap]
   unsigned long long* krank[ZHA_MAX_LEVELS + 2];  // union routes: per-level (stamp << 32) | rank in the
                                     // unit's kept list, by node id [RUmax][cap] (null: no union routes)
@@ -268,6 +289,8 @@ hipError_t zha_launch_dense(const void* q, const void* K, const void* V, const Z
 hipError_t zha_launch_copy16(void* dst, const void* src, int64_t n16, hipStream_t s);
 hipError_t zha_launch_decode_fp8(const uint8_t* codes, const float* scale, int64_t rows, int d, __bf16* out,
                                  hipStream_t s);
+hipError_t zha_launch_decode_fp4(const uint8_t* codes, const uint8_t* scale, int64_t rows, int d, __bf16* out,
+                                 float* scale_out, hipStream_t s);
 int zha_sparse_wgs(int U);
 int zha_score_wgs_units(int RU);  // score workgroups per routing unit (before the level's own cap)
 // Union scoring of a route with Tq queries per sequence and hr units per (query, KV head):

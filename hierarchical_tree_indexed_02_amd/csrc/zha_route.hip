@@ -171,26 +171,43 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
+// Eight fp4 e2m1 codes (one dword, element 2i in the low nibble of byte i) as eight bf16
+// values times the block scale sc (exact: two significant bits and a power of two).
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t w, float sc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+  bf16x8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
 // Scores one level's frontier.  Rows of an MFMA tile are (node, reference query)
 // pairs: 16/R nodes per tile; columns are the KV head's query heads (G <= 16).
 // Lane i loads its row's plane slice (k-slot group i/16) straight from HBM; the
 // query fragments stay in registers for the whole workgroup.  F8: the planes are fp8
 // codes; lane (row, group) loads its row's d/4 contiguous codes, decodes them to bf16 in
 // registers, and the query fragments take the same k order (the dot product does not
-// depend on it); the row's scale multiplies the product.
+// depend on it); the row's scale multiplies the product.  F4 (SM = 2): the lane's d/4 values
+// are one block-of-32's share (d = 128: the whole block), decoded with the block scale.
 // UNI (R >= 4): the workgroup row scores the union of the frontiers of a group of routing
 // units in node-id order, in NT column tiles of 16 (column c = 16 * tile + lane row is head
 // jcol of unit cu(c)): every loaded plane tile feeds NT matrix products.  A node is loaded
 // when some column's unit has its parent kept (a stamped rank entry), and each column keeps
 // the scores of its unit's member nodes at the unit's frontier positions.
-template <typename T, int R, int D, int UN, bool F8, bool UNI, int NT>
+template <typename T, int R, int D, int UN, int SM, bool UNI, int NT>
 __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a) {
   typedef Mf<T> M;
+  constexpr bool F8 = SM == 1, F4 = SM == 2, LP = SM != 0;  // summary storage: native, fp8, fp4
   constexpr int NK = D / M::KPER;
-  constexpr int NR = F8 ? D / 64 : 1;   // 16-byte code loads per lane per tile (F8)
+  constexpr int NR = F8 ? D / 64 : 1;   // 16-byte code loads per lane per tile (F8; F4 uses one)
   constexpr int NPT = 16 / R;
   constexpr int SUPER = 4 * UN * NPT;
-  static_assert(!F8 || M::EPL == 8, "fp8 planes feed the bf16 matrix instruction");
+  static_assert(!LP || M::EPL == 8, "fp8 and fp4 planes feed the bf16 matrix instruction");
+  static_assert(!F4 || D % 64 == 0, "fp4 lanes hold whole code words");
   static_assert(!UNI || R >= 4, "union scoring keeps one node per lane group");
   static_assert(UNI || NT == 1, "one column tile unless scoring unions");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -238,15 +255,16 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
     const T* qp = (const T*)a.q + ((int64_t)u[n] * G + jc[n]) * D;
 #pragma unroll
     for (int s = 0; s < NK; ++s) {
-      const int k0 = F8 ? grp * (D / 4) + s * 8 : s * M::KPER + grp * M::EPL;
+      const int k0 = LP ? grp * (D / 4) + s * 8 : s * M::KPER + grp * M::EPL;
       qf[n][s] = ok[n] ? M::load(qp + k0) : M::zero();
     }
   }
   const int32_t* par = (!UNI && a.v.parent) ? a.v.parent + (int64_t)u[0] * a.v.cap_parent : nullptr;
   const T* mb = (const T*)a.m + (int64_t)up * a.capl * R * D;
-  const uint8_t* m8 = (const uint8_t*)a.m + (int64_t)up * a.capl * R * D;
+  const uint8_t* m8 = (const uint8_t*)a.m + (int64_t)up * a.capl * R * (F4 ? D / 2 : D);
   const float* bb = a.b + (int64_t)up * a.capl * R;
   const float* sb = F8 ? a.ms + (int64_t)up * a.capl * R : nullptr;
+  const uint8_t* sb4 = F4 ? (const uint8_t*)a.ms + (int64_t)up * a.capl * R * (D / 32) : nullptr;
   const int GS = score_stride(G);
   float runM[NT], runS[NT];
 #pragma unroll
@@ -412,17 +430,32 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
       if (!UNI && par) id = a.v.Cshift >= 0 ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
                                            : pp[k] * a.v.C + pos % a.v.C;
       id = v ? id : 0;
-      const uint8_t* cp = m8 + ((int64_t)id * R + (row % R)) * D + grp * (D / 4);
+      if constexpr (F4) {
+        // the lane's d/4 codes (d/8 bytes) and the scale of the block they lie in
+        const int64_t rw4 = (int64_t)id * R + (row % R);
+        const uint8_t* cp = m8 + rw4 * (D / 2) + grp * (D / 8);
+        if constexpr (D == 128) {
+          rw[k][0] = v ? *(const uint4*)cp : make_uint4(0u, 0u, 0u, 0u);
+        } else {
+          const uint2 q2 = v ? *(const uint2*)cp : make_uint2(0u, 0u);
+          rw[k][0] = make_uint4(q2.x, q2.y, 0u, 0u);
+        }
+        sv[k][0] = v ? fp4_scale(sb4[rw4 * (D / 32) + (grp * (D / 4)) / 32]) : 0.0f;
+      } else {
+        const uint8_t* cp = m8 + ((int64_t)id * R + (row % R)) * D + grp * (D / 4);
 #pragma unroll
-      for (int i = 0; i < NR; ++i) rw[k][i] = v ? *(const uint4*)(cp + 16 * i) : make_uint4(0u, 0u, 0u, 0u);
+        for (int i = 0; i < NR; ++i) rw[k][i] = v ? *(const uint4*)(cp + 16 * i) : make_uint4(0u, 0u, 0u, 0u);
+      }
       if constexpr (R >= 4) {
         const int id2 = __shfl(id, 4 * grp);
         const bool v2 = UNI ? ((act[k] >> ((4 * grp) / R)) & 1u) != 0 : tbk + (4 * grp) / R < end;
         const int64_t o = (int64_t)id2 * R + (4 * grp) % R;
         const float4 b4 = v2 ? *(const float4*)(bb + o) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        const float4 s4 = v2 ? *(const float4*)(sb + o) : make_float4(0.f, 0.f, 0.f, 0.f);
         bv[k][0] = b4.x; bv[k][1] = b4.y; bv[k][2] = b4.z; bv[k][3] = b4.w;
-        sv[k][0] = s4.x; sv[k][1] = s4.y; sv[k][2] = s4.z; sv[k][3] = s4.w;
+        if constexpr (F8) {
+          const float4 s4 = v2 ? *(const float4*)(sb + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+          sv[k][0] = s4.x; sv[k][1] = s4.y; sv[k][2] = s4.z; sv[k][3] = s4.w;
+        }
       } else {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -431,23 +464,30 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
           const bool v2 = tbk + r2 / R < end;
           const int64_t o = (int64_t)id2 * R + (r2 % R);
           bv[k][jj] = v2 ? bb[o] : -INFINITY;
-          sv[k][jj] = v2 ? sb[o] : 0.0f;
+          if constexpr (F8) sv[k][jj] = v2 ? sb[o] : 0.0f;
         }
       }
     }
   };
   // F8: decode the codes (lane k-slots s*8 .. s*8+7 of its d/4 codes per matrix step),
-  // then score as the bf16 path does with the row scale in the multiplier.
+  // then score as the bf16 path does with the row scale in the multiplier.  F4: decode with
+  // the block scale folded in (the multiplier is the logit scale alone).
   auto compute8 = [&](const uint4 (&rw)[UN][NR], const float (&bv)[UN][4], const float (&sv)[UN][4], int base,
                       const bool (&mem)[UN][NT], const int (&wpos)[UN][NT]) {
-    if constexpr (F8) {
+    if constexpr (LP) {
 #pragma unroll
       for (int k = 0; k < UN; ++k) {
         Frag afk[NK];
 #pragma unroll
         for (int s = 0; s < NK; ++s) {
-          const uint4 q4 = rw[k][s / 2];
-          afk[s] = (s & 1) ? fp8x8_to_bf16(q4.z, q4.w) : fp8x8_to_bf16(q4.x, q4.y);
+          if constexpr (F4) {
+            const uint4 q4 = rw[k][0];
+            const uint32_t wd = s == 0 ? q4.x : (s == 1 ? q4.y : (s == 2 ? q4.z : q4.w));
+            afk[s] = fp4x8_to_bf16(wd, sv[k][0]);
+          } else {
+            const uint4 q4 = rw[k][s / 2];
+            afk[s] = (s & 1) ? fp8x8_to_bf16(q4.z, q4.w) : fp8x8_to_bf16(q4.x, q4.y);
+          }
         }
         score_tile(k, afk, bv[k], sv[k], base, mem[k], wpos[k]);
       }
@@ -466,7 +506,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
   fetch_par(start, ppA, rkA);
   fetch_par(start + step, ppB, rkB);
   if constexpr (UNI) members(start, rkA, mA, wA, acA);
-  if constexpr (F8) {
+  if constexpr (LP) {
     uint4 rwA[UN][NR], rwB[UN][NR];
     float svA[UN][4], svB[UN][4];
     if (start < end) load_stage8(start, ppA, acA, rwA, bvA, svA);
@@ -1658,37 +1698,38 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
 
 // Two tiles per wave per pipeline stage (for fp8 codes too: four would not fit in the
 // registers of four workgroups per compute unit, and fewer workgroups measured slower).
-template <typename T, int R, int D, bool F8, bool UNI, int NT = 1>
+// SM: summary storage (0 native, 1 fp8, 2 fp4)
+template <typename T, int R, int D, int SM, bool UNI, int NT = 1>
 hipError_t launch_score(const ScoreArgs& a, int W, int rows, hipStream_t s) {
-  hipLaunchKernelGGL((zha_score_kernel<T, R, D, 2, F8, UNI, NT>), dim3(W, rows), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((zha_score_kernel<T, R, D, 2, SM, UNI, NT>), dim3(W, rows), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename T, int R, int D, bool F8>
+template <typename T, int R, int D, int SM>
 hipError_t launch_score_uni(const ScoreArgs& a, int W, int rows, int NT, hipStream_t s) {
   switch (NT) {
-    case 1: return launch_score<T, R, D, F8, true, 1>(a, W, rows, s);
-    case 2: return launch_score<T, R, D, F8, true, 2>(a, W, rows, s);
-    default: return launch_score<T, R, D, F8, true, 4>(a, W, rows, s);
+    case 1: return launch_score<T, R, D, SM, true, 1>(a, W, rows, s);
+    case 2: return launch_score<T, R, D, SM, true, 2>(a, W, rows, s);
+    default: return launch_score<T, R, D, SM, true, 4>(a, W, rows, s);
   }
 }
 
 // rows: routing units, or groups of them (uni; R >= 4 there, NT column tiles of 16)
-template <typename T, int D, bool F8 = false>
+template <typename T, int D, int SM = 0>
 hipError_t launch_score_r(const ScoreArgs& a, int R, int W, int rows, bool uni, int NT, hipStream_t s) {
   if (uni) {
     switch (R) {
-      case 4: return launch_score_uni<T, 4, D, F8>(a, W, rows, NT, s);
-      case 8: return launch_score_uni<T, 8, D, F8>(a, W, rows, NT, s);
-      default: return launch_score_uni<T, 16, D, F8>(a, W, rows, NT, s);
+      case 4: return launch_score_uni<T, 4, D, SM>(a, W, rows, NT, s);
+      case 8: return launch_score_uni<T, 8, D, SM>(a, W, rows, NT, s);
+      default: return launch_score_uni<T, 16, D, SM>(a, W, rows, NT, s);
     }
   }
   switch (R) {
-    case 1: return launch_score<T, 1, D, F8, false>(a, W, rows, s);
-    case 2: return launch_score<T, 2, D, F8, false>(a, W, rows, s);
-    case 4: return launch_score<T, 4, D, F8, false>(a, W, rows, s);
-    case 8: return launch_score<T, 8, D, F8, false>(a, W, rows, s);
-    default: return launch_score<T, 16, D, F8, false>(a, W, rows, s);
+    case 1: return launch_score<T, 1, D, SM, false>(a, W, rows, s);
+    case 2: return launch_score<T, 2, D, SM, false>(a, W, rows, s);
+    case 4: return launch_score<T, 4, D, SM, false>(a, W, rows, s);
+    case 8: return launch_score<T, 8, D, SM, false>(a, W, rows, s);
+    default: return launch_score<T, 16, D, SM, false>(a, W, rows, s);
   }
 }
 
@@ -1802,8 +1843,11 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     sa.scale = scale;
     zha_time_begin(t, s, ZHA_K_SCORE, l);
     if (t->f8)
-      e = t->d == 64 ? launch_score_r<__bf16, 64, true>(sa, t->R, sa.W, rows, uni_s, NT, s)
-                     : launch_score_r<__bf16, 128, true>(sa, t->R, sa.W, rows, uni_s, NT, s);
+      e = t->d == 64 ? launch_score_r<__bf16, 64, 1>(sa, t->R, sa.W, rows, uni_s, NT, s)
+                     : launch_score_r<__bf16, 128, 1>(sa, t->R, sa.W, rows, uni_s, NT, s);
+    else if (t->f4)
+      e = t->d == 64 ? launch_score_r<__bf16, 64, 2>(sa, t->R, sa.W, rows, uni_s, NT, s)
+                     : launch_score_r<__bf16, 128, 2>(sa, t->R, sa.W, rows, uni_s, NT, s);
     else if (t->desc.dtype == ZHA_BF16)
       e = t->d == 64 ? launch_score_r<__bf16, 64>(sa, t->R, sa.W, rows, uni_s, NT, s)
                      : launch_score_r<__bf16, 128>(sa, t->R, sa.W, rows, uni_s, NT, s);

@@ -21,15 +21,17 @@ class Tree:
 
     def __init__(self, batch, n_kv_heads, n_q_heads, head_dim, chunk, levels, n_refs, max_tokens,
                  dtype=torch.bfloat16, summary="native", per_head_routes=False, max_queries=1):
-        """summary: "native" (m stored in dtype) or "fp8" (e4m3 codes with a power-of-two
-        scale per node and reference; dtype bf16 only).  per_head_routes: the tree also serves
+        """summary: "native" (m stored in dtype), "fp8" (e4m3 codes with a power-of-two
+        scale per node and reference) or "fp4" (e2m1 codes with a power-of-two scale per block
+        of 32 values); fp8 and fp4 need dtype bf16.  per_head_routes: the tree also serves
         routes that give every query head its own kept set (route(..., mode="per_head")).
         max_queries: queries per sequence one route_multi may carry."""
-        if summary not in ("native", "fp8"):
+        codes = {"native": zha.ZHA_SUMMARY_NATIVE, "fp8": zha.ZHA_SUMMARY_FP8, "fp4": zha.ZHA_SUMMARY_FP4}
+        if summary not in codes:
             raise ValueError(f"unsupported summary storage {summary!r}")
         self.desc = zha.zha_tree_desc(batch, n_kv_heads, n_q_heads, head_dim, chunk, levels, n_refs, max_tokens,
                                       zdtype(dtype),
-                                      zha.ZHA_SUMMARY_FP8 if summary == "fp8" else zha.ZHA_SUMMARY_NATIVE,
+                                      codes[summary],
                                       1 if per_head_routes else 0, max_queries)
         self.RU = batch * n_kv_heads  # routing units of the last route
         self.dtype = dtype
@@ -121,8 +123,10 @@ class Tree:
         return m, b
 
     def scales(self, level: int, device="cuda"):
-        """Row scales [U][cap][R] fp32 of one level of a tree with fp8 summaries."""
-        sc = torch.empty((self.U, self.capacity(level), self.R), dtype=torch.float32, device=device)
+        """Scales of one level of a tree with low-precision summaries: fp8 [U][cap][R] (one
+        per row), fp4 [U][cap][R][d/32] (one per block of 32 values), fp32."""
+        shape = (self.U, self.capacity(level), self.R) + ((self.d // 32,) if self.summary == "fp4" else ())
+        sc = torch.empty(shape, dtype=torch.float32, device=device)
         zha.zha_tree_copy_scales(self.h, level, sc)
         return sc
 

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libzha.so")
 
 ZHA_OK, ZHA_ERR_INVALID, ZHA_ERR_CAPACITY, ZHA_ERR_NOMEM, ZHA_ERR_UNSUPPORTED, ZHA_ERR_HIP = range(6)
 ZHA_F32, ZHA_BF16 = 0, 1
-ZHA_SUMMARY_NATIVE, ZHA_SUMMARY_FP8 = 0, 1
+ZHA_SUMMARY_NATIVE, ZHA_SUMMARY_FP8, ZHA_SUMMARY_FP4 = 0, 1, 2
 ZHA_ROUTE_GROUP, ZHA_ROUTE_PER_HEAD = 0, 1
 ZHA_K_BUILD, ZHA_K_APPEND, ZHA_K_SCORE, ZHA_K_SELECT, ZHA_K_ATTEND, ZHA_K_MERGE, ZHA_K_MASS, ZHA_K_COMPACT = range(1, 9)
 KERNEL_NAMES = {1: "build", 2: "append", 3: "score", 4: "select", 5: "attend", 6: "merge", 7: "mass", 8: "compact"}

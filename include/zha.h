@@ -75,8 +75,15 @@ typedef enum { ZHA_F32 = 0, ZHA_BF16 = 1 } zha_dtype;
  * rounded to the nearest e4m3 value (ties to even mantissa, subnormals kept).
  * b = LSE - r.m~ is formed from the decoded m~ = code * 2^e, as for native
  * storage, so every plane stays exact at q = r.  A level-1 node then takes
- * R * (d + 8) bytes instead of R * (2d + 4). */
-typedef enum { ZHA_SUMMARY_NATIVE = 0, ZHA_SUMMARY_FP8 = 1 } zha_summary;
+ * R * (d + 8) bytes instead of R * (2d + 4).
+ * ZHA_SUMMARY_FP4 (tree dtype bf16 only): the 4-bit reading.  Each row is cut
+ * into blocks of 32 consecutive values, each stored as OCP fp4 e2m1 codes
+ * (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; two per byte, element 2i in the low
+ * nibble of byte i) times its own power-of-two scale 2^e, e the smallest
+ * integer with max|m_block| * 2^-e <= 6 (kept as the byte e + 127); values
+ * rounded to the nearest e2m1 value, ties to even mantissa.  b is formed from
+ * the decoded m~ as above.  A level-1 node takes R * (d/2 + d/32 + 4) bytes. */
+typedef enum { ZHA_SUMMARY_NATIVE = 0, ZHA_SUMMARY_FP8 = 1, ZHA_SUMMARY_FP4 = 2 } zha_summary;
 
 /* Shape of one layer's tree.  Supported: head_dim in {64, 128};
  * n_refs in {1, 2, 4, 8, 16}; group = n_q_heads / n_kv_heads in [1, 16];
@@ -243,13 +250,15 @@ ZHA_API zha_status zha_tree_level_capacity(zha_tree_t tree, int32_t level, int64
 
 /* Copies level `level` (1..L) of the tree: m_out [B*Hkv][cap][R][d] in the
  * tree dtype and b_out [B*Hkv][cap][R] float32 (cap from
- * zha_tree_level_capacity).  With fp8 summaries m_out receives the decoded
- * m~ = code * 2^e, exact in bf16.  Device buffers owned by the caller. */
+ * zha_tree_level_capacity).  With fp8 or fp4 summaries m_out receives the
+ * decoded m~ = code * 2^e, exact in bf16.  Device buffers owned by the caller. */
 ZHA_API zha_status zha_tree_copy_level(zha_tree_t tree, int32_t level, void* m_out, float* b_out,
                                hipStream_t stream);
 
-/* Copies the row scales 2^e of level `level` of a tree with fp8 summaries:
- * scale_out [B*Hkv][cap][R] float32, a device buffer owned by the caller.
+/* Copies the scales 2^e of level `level` of a tree with low-precision
+ * summaries: fp8, one per row, scale_out [B*Hkv][cap][R] float32; fp4, one per
+ * block of 32 values, scale_out [B*Hkv][cap][R][d/32] float32.  A device
+ * buffer owned by the caller.
  * Errors: ZHA_ERR_INVALID (null pointer, level out of range, native tree). */
 ZHA_API zha_status zha_tree_copy_scales(zha_tree_t tree, int32_t level, float* scale_out, hipStream_t stream);
 

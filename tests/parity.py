@@ -119,16 +119,38 @@ def _check_fp8_rows(mg, sg, m_o, where):
     assert err.max() <= 0, f"{where}: m excess {err.max():.3e}"
 
 
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def _check_fp4_rows(mg, sg, m_o, where):
+    """fp4 storage of one node's rows: grid membership per block of 32, minimal block scale,
+    error within half a grid step of the oracle's mean (plus the fp32 floor of the mean)."""
+    R, d = mg.shape
+    se = np.repeat(sg, 32, axis=1)                          # each value's block scale
+    codes = np.abs(mg) / se
+    assert np.isin(codes, E2M1).all(), f"{where}: stored m / scale is not an e2m1 value"
+    bmax = codes.reshape(R, d // 32, 32).max(axis=2)
+    omax = (np.abs(m_o) / se).reshape(R, d // 32, 32).max(axis=2)
+    nz = bmax > 0
+    assert np.all((bmax[nz] >= 3.0) & (bmax[nz] <= 6.0)), f"{where}: block scale not minimal"
+    assert np.all((omax[nz] <= 6.0 * (1 + 1e-5)) & (omax[nz] > 3.0 * (1 - 1e-5))), f"{where}: block scale not minimal"
+    a = np.abs(m_o) / se
+    half = np.where(a < 2.0, 0.25, np.where(a < 4.0, 0.5, 1.0))
+    err = np.abs(mg - m_o) - (half * se * (1 + 1e-5) + 1e-5 * np.abs(m_o) + 2e-5)
+    assert err.max() <= 0, f"{where}: m excess {err.max():.3e}"
+
+
 def check_build(case: Case, tree: Tree, sample=None, seed=0):
     """Checks stored planes against the oracle.  sample: nodes per (unit, level) or None for all."""
     cfg = case.cfg
     rel, floor = m_tol(cfg.dtype)
     fp8 = getattr(tree, "summary", "native") == "fp8"
+    fp4 = getattr(tree, "summary", "native") == "fp4"
     rng = np.random.default_rng(seed)
     worst_m, worst_b, n_checked = 0.0, 0.0, 0
     for l in range(1, tree.L + 1):
         m_d, b_d = tree.level(l)
-        s_d = tree.scales(l) if fp8 else None
+        s_d = tree.scales(l) if (fp8 or fp4) else None
         for b in range(case.B):
             N = case.lens[b]
             n_l = oracle.level_nodes(N, tree.C, l)
@@ -143,7 +165,7 @@ def check_build(case: Case, tree: Tree, sample=None, seed=0):
                 mg = m_d[u, torch.from_numpy(nodes).to(m_d.device)].float().cpu().numpy().astype(np.float64)
                 bg = b_d[u, torch.from_numpy(nodes).to(b_d.device)].cpu().numpy().astype(np.float64)
                 sg = (s_d[u, torch.from_numpy(nodes).to(s_d.device)].cpu().numpy().astype(np.float64)
-                      if fp8 else None)
+                      if (fp8 or fp4) else None)
                 refs = case.refs[g].astype(np.float64)
                 for i, j in enumerate(nodes):
                     t0 = j * tree.C ** l
@@ -151,6 +173,8 @@ def check_build(case: Case, tree: Tree, sample=None, seed=0):
                     m_o, _, lse_o = oracle.node_planes(Ku[t0:t1], 0, t1 - t0, refs)
                     if fp8:
                         _check_fp8_rows(mg[i], sg[i], m_o, f"fp8 level {l} unit {u} node {j}")
+                    elif fp4:
+                        _check_fp4_rows(mg[i], sg[i], m_o, f"fp4 level {l} unit {u} node {j}")
                     else:
                         err_m = np.abs(mg[i] - m_o) - (rel * np.abs(m_o) + floor)
                         assert err_m.max() <= 0, f"m level {l} unit {u} node {j}: excess {err_m.max():.3e}"

@@ -156,6 +156,66 @@ def test_fp8_rounding_exact():
     say(f" {got_m.size} stored values equal the oracle's rounding; scales {sorted(set(got_s.ravel().tolist()))}")
 
 
+@pytest.mark.parametrize("label,kw,lens", FP8_VARIANTS, ids=[v[0] for v in FP8_VARIANTS])
+def test_fp4_summaries(label, kw, lens):
+    """Planes stored as e2m1 codes with a power-of-two scale per block of 32 values: storage
+    checked against the oracle's means, routing teacher-forced on the decoded planes,
+    attention on the kept set."""
+    cfg = small(**kw, n_queries=4, needles_per_unit=4)
+    say(f"case fp4 summaries {label}: lens={lens}")
+    case = Case(cfg, lens=lens, n_queries=2)
+    tree = case.tree(summary="fp4")
+    torch.cuda.synchronize()
+    say(" build", check_build(case, tree, sample=None if sum(lens) < 20000 else 256))
+    for t in range(2):
+        for p in (0.5, 0.95):
+            r, a = full_check(case, tree, t, p)
+            say(f" t={t} p={p}", r, a)
+
+
+def test_fp4_rounding_exact():
+    """Leaves whose C keys are equal have m = that key exactly, so the stored codes can be
+    compared with the oracle's rounding bit for bit: every midpoint between neighbouring e2m1
+    values (ties go to the even mantissa) and its bf16 neighbours, in blocks whose largest
+    value sits on either side of a scale boundary."""
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    vals = []
+    for a_, b_ in zip(grid, grid[1:]):
+        m = 0.5 * (a_ + b_)
+        up = float(torch.nextafter(torch.tensor(m, dtype=torch.bfloat16), torch.tensor(1e9, dtype=torch.bfloat16)))
+        dn = float(torch.nextafter(torch.tensor(m, dtype=torch.bfloat16), torch.tensor(-1e9, dtype=torch.bfloat16)))
+        vals += [m, -m, up, -dn, dn, a_, -b_]
+    vals = (vals * 2)[:31]
+    d, C = 128, 4
+    blocks = [[6.0] + vals,                                   # largest exactly 6: scale 2^0
+              [12.0] + [2 * v for v in vals],                 # scale 2^1
+              [6.0 * 2.0 ** -4] + [v / 16 for v in vals],     # largest 0.375 = 6 * 2^-4
+              [-6.03125] + [v / 2 for v in vals]]             # just above 6: scale 2^1
+    rows = [sum(blocks[k:] + blocks[:k], []) for k in range(4)]
+    keys = np.array(rows, dtype=np.float32)
+    assert keys.shape == (4, d)
+    n_leaf = len(rows)
+    N = n_leaf * C
+    cfg = small(batch=1, n_tokens=N, n_q_heads=1, n_kv_heads=1, head_dim=d, chunk=C, levels=1, n_refs=4,
+                n_queries=2, needles_per_unit=1)
+    say(f"case fp4 rounding of exact midpoints: {n_leaf} leaves of {C} equal keys, d={d}")
+    case = Case(cfg, lens=[N], n_queries=2)
+    Kfull = np.repeat(keys, C, axis=0)
+    case.Kd[0, 0, :N] = torch.from_numpy(Kfull).to(case.Kd.device, torch.bfloat16)
+    assert torch.equal(case.Kd[0, 0, :N].float().cpu(), torch.from_numpy(Kfull)), "keys are bf16 values"
+    tree = case.tree(summary="fp4")
+    m_d, _ = tree.level(1)
+    s_d = tree.scales(1)
+    got_m = m_d[0, :n_leaf].double().cpu().numpy()            # [n_leaf][R][d]
+    got_s = s_d[0, :n_leaf].double().cpu().numpy()            # [n_leaf][R][d/32]
+    want_m, want_s = oracle.fp4_rows(np.repeat(keys[:, None, :].astype(np.float64), cfg.n_refs, axis=1))
+    bad = np.argwhere(got_m != want_m)
+    assert bad.size == 0, f"{len(bad)} stored values differ from the oracle's rounding, e.g. leaf/ref/k {bad[0].tolist()}: " \
+                          f"gpu {got_m[tuple(bad[0])]!r} oracle {want_m[tuple(bad[0])]!r}"
+    assert np.array_equal(got_s, want_s), "block scales differ"
+    say(f" {got_m.size} stored values equal the oracle's rounding; scales {sorted(set(got_s.ravel().tolist()))}")
+
+
 # --------------------------------------------------------------------------- per-query-head routing
 
 PER_HEAD_VARIANTS = [
@@ -432,7 +492,7 @@ def test_determinism():
 # --------------------------------------------------------------------------- growth
 
 def _valid_equal(case, t_inc, t_full):
-    fp8 = t_inc.summary == "fp8"
+    fp8 = t_inc.summary != "native"  # low-precision storage: scales too
     for l in range(1, t_inc.L + 1):
         m1, b1 = t_inc.level(l)
         m2, b2 = t_full.level(l)
@@ -450,7 +510,7 @@ def _valid_equal(case, t_inc, t_full):
                     assert torch.equal(s1[u, :n_l], s2[u, :n_l]), f"scale level {l} unit {u}"
 
 
-@pytest.mark.parametrize("dtype,summary", [("bf16", "native"), ("f32", "native"), ("bf16", "fp8")])
+@pytest.mark.parametrize("dtype,summary", [("bf16", "native"), ("f32", "native"), ("bf16", "fp8"), ("bf16", "fp4")])
 def test_append_equals_rebuild(dtype, summary):
     cfg = small(batch=2, n_tokens=1200, chunk=4, levels=4, n_refs=8, n_q_heads=8, n_kv_heads=2, n_queries=2,
                 needles_per_unit=4, append_steps=400, dtype=dtype)
@@ -529,6 +589,19 @@ def test_deep_256k_fp8_full():
     say("case deep_256k full, fp8 summaries: N=262144, 32q/4kv, d=128, C=4 L=6 R=16 p=0.95")
     case = Case(cfg, n_queries=2)
     tree = case.tree(summary="fp8")
+    torch.cuda.synchronize()
+    say(" build", check_build(case, tree, sample=24))
+    for t in range(2):
+        r, a = full_check(case, tree, t, 0.95)
+        say(f" t={t}", r, a)
+
+
+@pytest.mark.slow
+def test_deep_256k_fp4_full():
+    cfg = zi.get_config("deep_256k")
+    say("case deep_256k full, fp4 summaries: N=262144, 32q/4kv, d=128, C=4 L=6 R=16 p=0.95")
+    case = Case(cfg, n_queries=2)
+    tree = case.tree(summary="fp4")
     torch.cuda.synchronize()
     say(" build", check_build(case, tree, sample=24))
     for t in range(2):
