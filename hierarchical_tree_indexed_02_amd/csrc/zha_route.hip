@@ -1697,7 +1697,8 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
 }
 
 // Two tiles per wave per pipeline stage (for fp8 codes too: four would not fit in the
-// registers of four workgroups per compute unit, and fewer workgroups measured slower).
+// registers of four workgroups per compute unit, and fewer workgroups measured slower; for
+// fp4 codes four or eight tiles measured slower too).
 // SM: summary storage (0 native, 1 fp8, 2 fp4)
 template <typename T, int R, int D, int SM, bool UNI, int NT = 1>
 hipError_t launch_score(const ScoreArgs& a, int W, int rows, hipStream_t s) {
