@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--p", type=float, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--cpu-queries", type=int, default=12)
+    ap.add_argument("--cpu-queries", type=int, default=64)
     ap.add_argument("--summary", choices=["native", "fp8", "fp4"], default="native",
                     help="storage of the planes' m for the headline measurement")
     ap.add_argument("--no-fp8", action="store_true",
@@ -498,26 +498,30 @@ def main():
         dense_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
         log(f"dense {dense_us:.1f} us/step ({dense_bytes / (dense_us * 1e-6) / 1e9:.0f} GB/s)")
 
-    # the oracle on the host cores, on a bounded sample: one (sequence, KV head) unit
+    # the oracle on the host cores, on a bounded sample: the decode queries of two (sequence,
+    # KV head) units (about 10-20 s of host work), scaled to a whole step
     cpu = None
     if not args.no_cpu:
         import oracle
-        Ku, Vu = zi.unit_kv(cfg, 0, 0, q_all)
-        tree_o = oracle.tree_merge(Ku, zi.refs(cfg)[0], C, L)
         ncpu = min(args.cpu_queries, cfg.n_queries)
         qc = zi.queries(cfg, n=ncpu)
-        tc0 = time.time()
-        for t in range(ncpu):
-            qu = qc[t, 0, 0:G].astype(np.float64)
-            _, kept = oracle.route(tree_o, N, C, L, qu, p)
-            S = oracle.attend_set(N, C, kept[1])
-            oracle.attend(qu, Ku, Vu, S)
-        sec = time.time() - tc0
-        per_unit_step = sec / ncpu
+        units = [(0, g) for g in range(min(2, Hkv))]
+        sec = 0.0
+        for (b0, g0) in units:
+            Ku, Vu = zi.unit_kv(cfg, b0, g0, q_all)
+            tree_o = oracle.tree_merge(Ku, zi.refs(cfg)[g0], C, L)  # untimed
+            tc0 = time.time()
+            for t in range(ncpu):
+                qu = qc[t, b0, g0 * G:(g0 + 1) * G].astype(np.float64)
+                _, kept = oracle.route(tree_o, N, C, L, qu, p)
+                S = oracle.attend_set(N, C, kept[1])
+                oracle.attend(qu, Ku, Vu, S)
+            sec += time.time() - tc0
+        per_unit_step = sec / (ncpu * len(units))
         cpu = dict(value=round(per_unit_step * U * 1e6, 1), unit="us/step/layer", cores=oracle.num_threads(),
                    kind="oracle",
-                   sample=f"route+attend of unit (b=0, kv head 0) for {ncpu} queries ({sec:.1f} s), "
-                          f"scaled by {U} units to one full step; oracle tree built untimed")
+                   sample=f"route+attend of {len(units)} (sequence, KV head) units for {ncpu} decode queries each "
+                          f"({sec:.1f} s), scaled by {U} units to one full step; oracle trees built untimed")
         log(f"cpu oracle {cpu['value']:.0f} us/step on {cpu['cores']} threads")
 
     result = {
