@@ -16,6 +16,11 @@
 // their loads carry the nontemporal hint so they do not displace reused data in the caches.  P is split into two bf16
 // halves (hi + lo) so the softmax weights keep ~16 significant bits.  Partial
 // (max, sum, o) per workgroup are merged by zha_merge_kernel in fixed order.
+//
+// Union attention (UNI): the routing units of a group share one KV head (the heads of a
+// per-head route, or the queries of a block); the group walks the union of their kept
+// chunks once, one matrix column per unit head, and each column's softmax takes only the
+// tokens of its own unit's set.
 #include "zha_internal.h"
 
 namespace {

@@ -98,7 +98,7 @@ typedef struct {
     int32_t n_refs;       /* R: reference queries per KV head */
     int64_t max_tokens;   /* capacity per sequence (the K/V token stride) */
     zha_dtype dtype;      /* storage dtype of q, K and V, and of the planes' m when native */
-    zha_summary summary;  /* storage of the planes' m (ZHA_SUMMARY_FP8 needs dtype bf16) */
+    zha_summary summary;  /* storage of the planes' m (fp8 and fp4 need dtype bf16) */
     int32_t per_head_routes; /* nonzero: the tree also serves ZHA_ROUTE_PER_HEAD routes (its
                                 routing workspace is sized for B*Hq routing units) */
     int32_t max_queries;  /* queries per sequence one zha_route_multi may carry (0 is taken
@@ -114,12 +114,17 @@ typedef struct {
  * kept set per (sequence, query head), and attention of each head over its own
  * set.  A "routing unit" is a (sequence, KV head) in group mode and a
  * (sequence, query head) in per-head mode, numbered (b, KV head, head in group)
- * with the head fastest. */
+ * with the head fastest (zha_route_multi adds the query of the block, see
+ * there).  Routing units that share one KV head's planes may be scored
+ * together (one load of each plane for all of them) and attended together
+ * (one load of each K/V row); every unit's kept set and output are those it
+ * would get alone. */
 typedef enum { ZHA_ROUTE_GROUP = 0, ZHA_ROUTE_PER_HEAD = 1 } zha_route_mode;
 
-/* Kept leaf chunks of the last zha_route on a tree: a view into the tree's
- * workspace, valid until the next zha_route on the same tree.
- * counts: device [B*Hkv]; ids: device [B*Hkv][cap], each unit's ids ascending. */
+/* Kept leaf chunks of the last route on a tree: a view into the tree's
+ * workspace, valid until the next route on the same tree.
+ * counts: device [routing units]; ids: device [routing units][cap], each
+ * unit's ids ascending ([B*Hkv] for zha_route). */
 typedef struct {
     const int32_t* counts;
     const int32_t* ids;
