@@ -204,7 +204,8 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
       score_n = std::max(score_n, (size_t)ru * ((Gr + 3) & ~3));
       cand_n = std::max(cand_n, zha_sel_cand_entries(ru));
       ctr_n = std::max(ctr_n, zha_sel_ctr_words(ru));
-      const int ts = zha_union_queries(R, G, tq, hr), tss = zha_union_score_queries(R, G, tq, hr);
+      const int ts = zha_union_queries(R, G, tq, hr, desc->dtype == ZHA_BF16);
+      const int tss = zha_union_score_queries(R, G, tq, hr);
       if (tss > 0) {  // union scoring: partials of every unit for each workgroup of its group
         const int ng = U * ((tq + tss - 1) / tss);
         spart_n = std::max(spart_n, (size_t)ru * zha_score_wgs_units(ng) * Gr * 2);
@@ -220,7 +221,7 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   int ugmax = 0;  // union groups of the largest union route
   for (int i = 0; i < (desc->per_head_routes ? 2 : 1); ++i)
     for (int tq = 1; tq <= maxq; ++tq) {
-      const int ts = zha_union_queries(R, G, tq, hrs[i]);
+      const int ts = zha_union_queries(R, G, tq, hrs[i], desc->dtype == ZHA_BF16);
       if (ts > 0) {
         uni = true;
         ugmax = std::max(ugmax, U * ((tq + ts - 1) / ts));

@@ -23,6 +23,8 @@
 // tokens of its own unit's set.
 #include "zha_internal.h"
 
+#include <type_traits>
+
 namespace {
 
 struct AttArgs {
@@ -480,6 +482,259 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
   }
 }
 
+// Token of position p of a position list (sink and tail first, then the listed chunks).
+__device__ __forceinline__ int position_token(const Positions& P, int p, int C, int Cshift) {
+  if (p < P.nx) return (P.sink && p == 0) ? 0 : P.Nc + p - P.sink;
+  const int q = p - P.nx;
+  const int k = Cshift >= 0 ? (q >> Cshift) : q / C;
+  const int id = P.kp[k];
+  return Cshift >= 0 ? (id << Cshift) + (q & ((1 << Cshift) - 1)) : id * C + (q - k * C);
+}
+
+// Union attention over 16 * CT query heads of one group (bf16): every stage of 128 / CT
+// positions is loaded once by the whole workgroup into LDS (two buffers; the next two
+// stages' loads in flight in registers while one is computed), and wave w multiplies its
+// window (slot w / CT) with its 16 columns (tile w % CT), each column's softmax masked to
+// its own unit's set as in zha_attend_kernel<..., UNI>.
+template <int D, int CT>
+__global__ __launch_bounds__(256, 2) void zha_attend_union_lds_kernel(AttArgs a) {
+  typedef Mf<__bf16> M;
+  typedef PV<__bf16, D> PVT;
+  constexpr int NK = D / M::KPER, ND = D / 16;
+  constexpr int NWS = 4 / CT;                 // windows of ATT_STEP positions per stage
+  constexpr int TOK = ATT_STEP * NWS;         // positions per stage
+  constexpr int KST = PVT::LDS_STRIDE;        // LDS row stride (elements), K and V alike
+  constexpr int CPR = D / 8;                  // 16-byte pieces per row
+  constexpr int NLD = TOK * CPR / 256;        // pieces per thread per matrix and stage
+  constexpr int BUF = TOK * KST;              // elements of one matrix in one buffer
+  constexpr int COMB = 4 * 16 * D * 4 + 2 * 4 * 16 * 4;
+  constexpr int SMEM = 4 * BUF * 2 > COMB ? 4 * BUF * 2 : COMB;
+  static_assert(NLD * 256 == TOK * CPR, "whole pieces per thread");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  __bf16* skv = (__bf16*)smem;                // buffer b: K at 2b * BUF, V at (2b + 1) * BUF
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row = lane & 15, grp = lane >> 4;
+  const int ct = wave % CT, ws = wave / CT;
+  const int G = a.G;
+  const int col = 16 * ct + row;
+  // the lane's column: head jcol of routing unit u (query tq of the block)
+  const int up = blockIdx.y / a.NTC;
+  const int tc = blockIdx.y - up * a.NTC, g = up % a.Hkv, bi = up / a.Hkv;
+  const int per_t = a.hr * G;
+  const int tt = col / per_t, h = (col / G) % a.hr, tq = tc * a.TS + tt;
+  const bool colok = tt < a.TS && tq < a.Tq;
+  const int u = ((bi * a.Tq + min(tq, a.Tq - 1)) * a.Hkv + g) * a.hr + h;
+  const int jcol = col % G;
+  const int N = a.lens[bi];
+  const int Nc = (N / a.C) * a.C;
+  const int Ne = a.qtail ? N + min(tq, a.Tq - 1) + 1 : N;
+  const int tlast = min(tc * a.TS + a.TS, a.Tq) - 1;
+  const int Nend = a.qtail ? N + tlast + 1 : N;
+  Positions P;
+  P.nK = a.ucount[blockIdx.y];
+  P.kp = a.ulist + (int64_t)blockIdx.y * a.cap1;
+  P.sink = (Nc > 0 && (P.nK == 0 || P.kp[0] != 0)) ? 1 : 0;
+  P.nx = P.sink + (Nend - Nc);
+  P.P = P.nx + P.nK * a.C;
+  P.Nc = Nc;
+  const int end = P.P;
+  const bool chunk0 = Nc > 0 && !P.sink;  // token 0 is the list's first chunk token
+  const u64* kr1 = a.krank + (int64_t)u * a.cap1;
+  const uint32_t stamp = a.route_ctr[0];
+  const int64_t kvoff = (int64_t)up * a.T * D;
+  const __bf16* Kb = (const __bf16*)a.K + kvoff;
+  const __bf16* Vb = (const __bf16*)a.V + kvoff;
+
+  typename M::frag qf[NK];
+  {
+    const __bf16* qp = (const __bf16*)a.q + ((int64_t)u * G + jcol) * D + grp * M::EPL;
+#pragma unroll
+    for (int s = 0; s < NK; ++s) qf[s] = colok ? M::load(qp + s * M::KPER) : M::zero();
+  }
+  f32x4_t o[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt) o[dt] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f};
+  float mrun = -INFINITY, lrun = 0.0f;
+
+  const int start = blockIdx.x * TOK;
+  const int gstep = a.W * TOK;
+  // tokens of this thread's rows of the stage at ps (rows past the end read token 0)
+  auto tokens = [&](int ps, int (&tk)[NLD]) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int p = ps + (tid + 256 * i) / CPR;
+      tk[i] = p < end ? position_token(P, p, a.C, a.Cshift) : 0;
+    }
+  };
+  // loads of this thread's pieces of K and V of a stage whose tokens are known
+  auto issue = [&](const int (&tk)[NLD], bf16x8_t (&kr)[NLD], bf16x8_t (&vr)[NLD]) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int pc = (tid + 256 * i) % CPR;
+      kr[i] = M::load_stream(Kb + (int64_t)tk[i] * D + 8 * pc);
+      vr[i] = M::load_stream(Vb + (int64_t)tk[i] * D + 8 * pc);
+    }
+  };
+  auto store = [&](int b, const bf16x8_t (&kr)[NLD], const bf16x8_t (&vr)[NLD]) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int c = tid + 256 * i, r = c / CPR, pc = c % CPR;
+      *(bf16x8_t*)(skv + (2 * b) * BUF + r * KST + 8 * pc) = kr[i];
+      *(bf16x8_t*)(skv + (2 * b + 1) * BUF + r * KST + 8 * pc) = vr[i];
+    }
+  };
+  // stamps of the chunks of this lane's positions in its window of the stage at ps
+  auto fetch_rank = [&](int ps, uint32_t (&rk)[2][4]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int p = ps + ws * ATT_STEP + 16 * t + 4 * grp + jj;
+        const bool need = colok && p < end && p >= P.nx;
+        int k = 0;
+        if (need) {
+          const int tok = position_token(P, p, a.C, a.Cshift);
+          k = a.Cshift >= 0 ? (tok >> a.Cshift) : tok / a.C;
+        }
+        rk[t][jj] = need ? ((const uint32_t*)(kr1 + k))[1] : 0u;
+      }
+  };
+  auto member_bits = [&](int ps, const uint32_t (&rk)[2][4]) {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int p = ps + ws * ATT_STEP + 16 * t + 4 * grp + jj;
+        bool in;
+        if (p < P.nx) {
+          const int tok = (P.sink && p == 0) ? 0 : P.Nc + p - P.sink;
+          in = tok == 0 || tok < Ne;
+        } else {
+          in = p < end && (rk[t][jj] == stamp || (p == P.nx && chunk0));
+        }
+        bits |= (colok && in) ? (1u << (4 * t + jj)) : 0u;
+      }
+    return bits;
+  };
+  // online-softmax update of this wave's columns with its window of buffer b
+  auto compute = [&](int b, uint32_t bits) {
+    const __bf16* sk = skv + (2 * b) * BUF + ws * ATT_STEP * KST;
+    const __bf16* sv = skv + (2 * b + 1) * BUF + ws * ATT_STEP * KST;
+    float z[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int s = 0; s < NK; ++s)
+        acc = M::mma(*(const bf16x8_t*)(sk + (16 * t + row) * KST + s * M::KPER + grp * M::EPL), qf[s], acc);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        z[t][jj] = ((bits >> (4 * t + jj)) & 1u) ? acc[jj] * a.scale_log2 : -INFINITY;
+    }
+    float mloc = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
+                       fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float mnew = fmaxf(mrun, mloc);
+    float pr[2][4];
+    float alpha = 1.0f, psum = 0.0f;
+    if (mnew == -INFINITY) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) pr[t][jj] = 0.0f;
+    } else {
+      alpha = zexp2(mrun - mnew);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          pr[t][jj] = zexp2(z[t][jj] - mnew);
+          psum += pr[t][jj];
+        }
+    }
+    lrun = lrun * alpha + psum;
+    mrun = mnew;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) o[dt] *= alpha;
+    PVT::mma(o, sv, pr, lane);
+  };
+
+  // pipeline: while the stage at ps (in LDS buffer b) is computed, the next three stages'
+  // K/V are loading into registers (stored to LDS one stage ahead of use) and the tokens of
+  // the stage after those are being looked up, so no load waits on a lookup.  Register sets
+  // rotate with the stage index mod 3.
+  bf16x8_t kk[3][NLD], vv[3][NLD];
+  int tk[3][NLD];
+  uint32_t rk[3][2][4];
+  int ps = start, b = 0;
+  tokens(ps, tk[0]);
+  tokens(ps + gstep, tk[1]);
+  tokens(ps + 2 * gstep, tk[2]);
+  issue(tk[0], kk[0], vv[0]);
+  issue(tk[1], kk[1], vv[1]);
+  issue(tk[2], kk[2], vv[2]);
+  tokens(ps + 3 * gstep, tk[0]);
+  fetch_rank(ps, rk[0]);
+  store(0, kk[0], vv[0]);
+  __syncthreads();
+  auto iter = [&](auto J) {
+    constexpr int j = decltype(J)::value, j1 = (j + 1) % 3;  // set of stage ps, of ps + gstep
+    issue(tk[j], kk[j], vv[j]);        // stage ps + 3 gstep
+    tokens(ps + 4 * gstep, tk[j1]);
+    fetch_rank(ps + gstep, rk[j1]);
+    compute(b, member_bits(ps, rk[j]));
+    store(b ^ 1, kk[j1], vv[j1]);      // stage ps + gstep
+    __syncthreads();
+    b ^= 1;
+    ps += gstep;
+  };
+  while (ps < end) {
+    iter(std::integral_constant<int, 0>{});
+    if (ps >= end) break;
+    iter(std::integral_constant<int, 1>{});
+    if (ps >= end) break;
+    iter(std::integral_constant<int, 2>{});
+  }
+  // per-column partials: lane groups, then the waves of the column's tile
+  lrun += __shfl_xor(lrun, 16);
+  lrun += __shfl_xor(lrun, 32);
+  float* so = (float*)smem;                    // [4][16][D]
+  float* sm = so + 4 * 16 * D;                 // [4][16]
+  float* sl = sm + 4 * 16;                     // [4][16]
+  __shared__ int s_rec[16 * CT];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) so[(wave * 16 + row) * D + dt * 16 + 4 * grp + jj] = o[dt][jj];
+  if (grp == 0) { sm[wave * 16 + row] = mrun; sl[wave * 16 + row] = lrun; }
+  if (ws == 0 && grp == 0) s_rec[col] = colok ? (u * a.W + (int)blockIdx.x) * G + jcol : -1;
+  __syncthreads();
+  float* pml0 = a.part + (int64_t)a.U * a.W * G * D;
+  for (int i = tid; i < 16 * CT * D; i += 256) {
+    const int c = i / D, dd = i % D, c0 = c >> 4, hh = c & 15;
+    const int rec = s_rec[c];
+    if (rec < 0) continue;
+    float Mx = -INFINITY;
+    for (int w = c0; w < 4; w += CT) Mx = fmaxf(Mx, sm[w * 16 + hh]);
+    float acc = 0.0f, l = 0.0f;
+    if (Mx != -INFINITY) {
+      for (int w = c0; w < 4; w += CT) {
+        const float f = zexp2(sm[w * 16 + hh] - Mx);
+        acc += f * so[(w * 16 + hh) * D + dd];
+        l += f * sl[w * 16 + hh];
+      }
+    }
+    a.part[(int64_t)rec * D + dd] = acc;
+    if (dd == 0) {
+      pml0[(int64_t)rec * 2] = Mx;
+      pml0[(int64_t)rec * 2 + 1] = l;
+    }
+  }
+}
+
 // Merges the W partials of each (unit, head): the maximum first, then the scaled sums,
 // each thread summing a fixed subset of workgroups and the subsets combined in order.
 constexpr int MERGE_THREADS = 1024;
@@ -613,8 +868,9 @@ hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const vo
   a.scale_log2 = scale * ZHA_LOG2E;
   a.lens = t->geo;
   // union attention: the groups of the route's union scoring, when it had one
-  const int TS = zha_union_queries(t->R, t->G, t->Tq, t->hr);
+  const int TS = zha_union_queries(t->R, t->G, t->Tq, t->hr, t->desc.dtype == ZHA_BF16);
   const bool uni = t->uni_route;
+  const int CT = (TS * t->G + 15) / 16;  // column tiles of a union group
   a.krank = uni ? t->krank[1] : nullptr;
   a.route_ctr = t->route_ctr;
   a.ulist = t->ulist;
@@ -624,8 +880,19 @@ hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const vo
   const int rows = uni ? t->U * a.NTC : t->RU;
   if (uni) a.W = zha_sparse_wgs(rows);
   zha_time_begin(t, s, ZHA_K_ATTEND, 0);
-  hipError_t e = uni ? launch_att_dt<false, true>(a, LensArg<false>{}, t->desc.dtype, t->d, rows, s)
-                     : launch_att_dt<false>(a, LensArg<false>{}, t->desc.dtype, t->d, rows, s);
+  hipError_t e;
+  if (uni && CT > 1) {  // bf16 (wider groups are formed for bf16 only): windows staged in LDS
+    if (CT == 2)
+      hipLaunchKernelGGL((t->d == 64 ? zha_attend_union_lds_kernel<64, 2> : zha_attend_union_lds_kernel<128, 2>),
+                         dim3(a.W, rows), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((t->d == 64 ? zha_attend_union_lds_kernel<64, 4> : zha_attend_union_lds_kernel<128, 4>),
+                         dim3(a.W, rows), dim3(256), 0, s, a);
+    e = hipGetLastError();
+  } else {
+    e = uni ? launch_att_dt<false, true>(a, LensArg<false>{}, t->desc.dtype, t->d, rows, s)
+            : launch_att_dt<false>(a, LensArg<false>{}, t->desc.dtype, t->d, rows, s);
+  }
   if (e != hipSuccess) return e;
   zha_time_end(t, s, ZHA_K_ATTEND, 0);
   zha_time_begin(t, s, ZHA_K_MERGE, 0);

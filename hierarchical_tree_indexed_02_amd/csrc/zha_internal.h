@@ -295,6 +295,7 @@ int zha_sparse_wgs(int U);
 int zha_score_wgs_units(int RU);  // score workgroups per routing unit (before the level's own cap)
 // Union scoring of a route with Tq queries per sequence and hr units per (query, KV head):
 // queries per group (0: no union scoring) and groups per (sequence, KV head).
-int zha_union_queries(int R, int Gq, int Tq, int hr);        // attention groups (16 query heads)
+int zha_union_queries(int R, int Gq, int Tq, int hr, bool wide);  // attention groups (64 query heads when
+                                                                   // wide, i.e. bf16 K/V, else 16)
 int zha_union_score_queries(int R, int Gq, int Tq, int hr);  // scoring groups (64 query heads)
 int zha_dense_wgs(int U);

@@ -1760,11 +1760,12 @@ int zha_score_wgs(const zha_tree* t, int level) {
 }
 
 // Union groups hold the routing units that share one (sequence, KV head): the hr units of
-// each of TS consecutive queries.  Attention (and the kept-chunk flags the selections write
-// for it) groups TS * Gq <= 16 query heads: one column tile, four windows in flight per
-// workgroup.  Scoring groups up to 64 (four column tiles in every wave, one plane load for
-// all of them).  Only worth it (and only built) when a group holds several units and a tile
-// row holds one node's planes for one lane group (R >= 4).
+// each of TS consecutive queries.  Scoring groups up to 64 query heads (four column tiles in
+// every wave, one plane load for all of them).  Attention (and the kept-chunk flags the
+// selections write for it) groups up to 64 with bf16 K/V (windows staged once in LDS for
+// the workgroup's waves, one column tile per wave) and up to 16 otherwise (one column
+// tile).  Only worth it (and only built) when a group holds several units and a tile row
+// holds one node's planes for one lane group (R >= 4).
 static int union_queries(int R, int Gq, int Tq, int hr, int cols) {
   if (R < 4 || Gq < 1 || Gq > 16) return 0;
   int ts = cols / Gq;
@@ -1772,7 +1773,7 @@ static int union_queries(int R, int Gq, int Tq, int hr, int cols) {
   if (ts < 1) ts = 1;
   return ts * hr > 1 ? ts : 0;
 }
-int zha_union_queries(int R, int Gq, int Tq, int hr) { return union_queries(R, Gq, Tq, hr, 16); }
+int zha_union_queries(int R, int Gq, int Tq, int hr, bool wide) { return union_queries(R, Gq, Tq, hr, wide ? 64 : 16); }
 int zha_union_score_queries(int R, int Gq, int Tq, int hr) { return union_queries(R, Gq, Tq, hr, 64); }
 
 int zha_compact_chunks(int64_t nodes) { return (int)((nodes + CH - 1) / CH); }
@@ -1789,14 +1790,15 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
   int32_t* cntK = t->counts + (int64_t)(L + 2) * U;  // [L+2][U]
   const bool keep_all = p >= 1.0f;
   // union scoring: groups of the units sharing one (sequence, KV head), TS queries each
-  // Union kernels pay a walk over each level's node ids (scoring) or a list per group
-  // (attention); they win when the units' kept sets overlap much (high p) or a group holds
-  // many units, and lose for pairs of units with sparse sets (measured: two queries of a
-  // block at p = 0.7, batch 8).
-  const int TS = zha_union_queries(t->R, t->G, t->Tq, t->hr);         // attention groups
+  // Union kernels pay a walk over each level's node ids (scoring), or a list per group and
+  // every listed token computed for every column (attention).  Scoring wins when the units'
+  // kept sets overlap much (high p) or a group holds many units; attention only when they
+  // overlap much: high p, or the heads of one query (measured: a block of 8 queries at
+  // p = 0.7, batch 8, attends 2.7x slower over the union than per unit).
+  const int TS = zha_union_queries(t->R, t->G, t->Tq, t->hr, t->desc.dtype == ZHA_BF16);  // attention groups
   const int TSs = zha_union_score_queries(t->R, t->G, t->Tq, t->hr);  // scoring groups
   const bool can = t->krank[1] != nullptr;
-  const bool uni = can && TS > 0 && (TS * t->hr >= 4 || p >= 0.8f);
+  const bool uni = can && TS > 0 && (p >= 0.8f || (t->hr >= 4 && t->Tq == 1));
   const bool uni_s = can && TSs > 0 && (TSs * t->hr >= 4 || p >= 0.8f);
   t->uni_route = uni;
   const int NTC = uni ? (t->Tq + TS - 1) / TS : 1;
