@@ -136,6 +136,43 @@ def geometry_sweep(measure, cfg, zi, torch, np, dev, N, B, Hkv, d, es, log):
     return dict(fit=fit, rows=rows)
 
 
+
+def union_counts(tree, L, C, hr, Tq, Hkv, lens, qtail):
+    """Distinct work of the last route when all routing units of one (sequence, KV head)
+    are served together, as the union kernels serve them (its query heads after a per-head
+    route, its queries after a block route): per level, the distinct frontier nodes (every
+    top-level node; below, the existing children of the union of the units' kept nodes one
+    level up), and the distinct attended tokens (the union of kept chunks, the sink when no
+    unit keeps chunk 0, and the longest tail).  Returns (frontier per level, tokens, frontier
+    per level summed over units, kept per level summed over units)."""
+    import numpy as np
+    kept, fr_unit, kept_unit = {}, {}, {}
+    for l in range(1, L + 1):
+        nf, nk, ids = tree.route_level(l)
+        nk, ids = nk.cpu().numpy(), ids.cpu().numpy()
+        fr_unit[l], kept_unit[l] = int(nf.sum()), int(nk.sum())
+        per = {}
+        for u in range(len(nk)):
+            per.setdefault((u // (Tq * Hkv * hr), (u // hr) % Hkv), []).append(ids[u, :nk[u]])
+        kept[l] = {k: np.unique(np.concatenate(v)) for k, v in per.items()}
+    fr = {}
+    for l in range(1, L + 1):
+        tot = 0
+        for (b, g) in kept[l]:
+            n_l = -(-((lens[b] // C) * C) // C ** l)
+            if l == L:
+                tot += n_l
+            else:
+                j = kept[l + 1][(b, g)].astype(np.int64)
+                tot += int(np.clip(n_l - j * C, 0, C).sum())
+        fr[l] = tot
+    tok = 0
+    for (b, g), k1 in kept[1].items():
+        Nc = (lens[b] // C) * C
+        sink = 1 if (Nc > 0 and (len(k1) == 0 or k1[0] != 0)) else 0
+        tok += sink + (lens[b] + (Tq if qtail else 0) - Nc) + len(k1) * C
+    return fr, tok, fr_unit, kept_unit
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -234,37 +271,26 @@ def main():
         ev1.record()
         torch.cuda.synchronize()
         us = 1e3 * ev0.elapsed_time(ev1) / args.steps
-        # algorithmic bytes: replay the block's route once
+        # algorithmic bytes: replay the block's route once; a KV head's queries and query heads
+        # are served as one union, so each distinct node and token is counted once per KV head
         hr = G if mode == "per_head" else 1
-        RU = U * Tq * hr
         trees[0].route_multi(qb, p, 1.0, mode=mode)
         torch.cuda.synchronize()
         S_node = R * (d * es + 4)
-        route_bytes = 0
-        for l in range(1, L + 1):
-            nf, _, _ = trees[0].route_level(l)
-            route_bytes += int(nf.sum()) * S_node
-        _, nk, ids = trees[0].route_level(1)
-        nk1 = nk.cpu().numpy()
-        first = ids[:, 0].cpu().numpy()
-        Nc = (Nb // C) * C
-        tok = 0
-        for u in range(RU):
-            tq = (u // hr // Hkv) % Tq
-            sink = 1 if (Nc > 0 and (nk1[u] == 0 or first[u] != 0)) else 0
-            tok += sink + (Nb + tq + 1 - Nc) + int(nk1[u]) * C
+        ufr, tok, _, _ = union_counts(trees[0], L, C, hr, Tq, Hkv, [Nb] * B, True)
+        route_bytes = sum(ufr.values()) * S_node
         attend_bytes = tok * 2 * d * es
         nbytes = route_bytes + attend_bytes
         for tr in trees:
             tr.close()
         torch.cuda.empty_cache()
         log(f"block of {Tq} ({mode}): {us:.1f} us ({us / Tq:.1f} us per query), {nbytes / 1e6:.1f} MB "
-            f"({nbytes / (us * 1e-6) / 1e9:.0f} GB/s), kappa {tok / (RU * Nb):.3f}")
+            f"({nbytes / (us * 1e-6) / 1e9:.0f} GB/s), kappa {tok / (U * (Nb + Tq)):.3f}")
         for k, v in kernels.items():
             log(f"  {k:12s} {v['launches']:4d} launches  avg {v['avg_us']:8.2f} us")
         return dict(queries=Tq, cached_tokens=Nb, mode=mode, us_per_block=round(us, 2),
                     us_per_query=round(us / Tq, 2), block_bytes=round(nbytes),
-                    block_gbs=round(nbytes / (us * 1e-6) / 1e9, 1), kappa=round(tok / (RU * Nb), 4),
+                    block_gbs=round(nbytes / (us * 1e-6) / 1e9, 1), kappa=round(tok / (U * (Nb + Tq)), 4),
                     kernels={k: round(v["avg_us"], 2) for k, v in kernels.items()})
 
     def measure(summary, mode="group", C=C, L=L, R=R, refs=refs, p=p):
@@ -380,9 +406,10 @@ def main():
 
         # algorithmic bytes of each step (routes are deterministic: replay each query once, untimed)
         S_node = {"fp8": R * (d + 8), "fp4": R * (d // 2 + d // 32 + 4)}.get(summary, R * (d * es + 4))
-        RU = U * (G if mode == "per_head" else 1)  # routing units
+        hr = G if mode == "per_head" else 1        # routing units per (sequence, KV head)
         Gr = G if mode == "group" else 1           # query heads per routing unit
-        fr_tot = {l: 0 for l in range(1, L + 1)}
+        fr_tot = {l: 0 for l in range(1, L + 1)}   # distinct frontier nodes per (sequence, KV head)
+        fr_unit = {l: 0 for l in range(1, L + 1)}  # frontier nodes summed over routing units
         kept_tot = {l: 0 for l in range(1, L + 1)}
         attend_tok = 0
         steps_q = [i % nq for i in range(args.steps)]
@@ -390,32 +417,29 @@ def main():
             w = steps_q.count(t)
             trees[0].route(qd[t], p, 1.0, mode=mode)
             torch.cuda.synchronize()
+            ufr, utok, frs, kps = union_counts(trees[0], L, C, hr, 1, Hkv, layer_lens[0], False)
+            if hr == 1 and ufr != frs:
+                raise RuntimeError(f"frontier recount {ufr} disagrees with the route's counts {frs}")
             for l in range(1, L + 1):
-                nf, nk, ids = trees[0].route_level(l)
-                fr_tot[l] += w * int(nf.sum())
-                kept_tot[l] += w * int(nk.sum())
-                if l == 1:
-                    nk1 = nk.cpu().numpy()
-                    first = ids[:, 0].cpu().numpy()
-                    for u in range(RU):
-                        Nu = layer_lens[0][u // (RU // B)]
-                        Nc = (Nu // C) * C
-                        sink = 1 if (Nc > 0 and (nk1[u] == 0 or first[u] != 0)) else 0
-                        attend_tok += w * (sink + (Nu - Nc) + int(nk1[u]) * C)
+                fr_tot[l] += w * ufr[l]
+                fr_unit[l] += w * frs[l]
+                kept_tot[l] += w * kps[l]
+            attend_tok += w * utok
         nsteps = args.steps
         route_bytes = sum(fr_tot[l] for l in fr_tot) * S_node / nsteps
         attend_bytes = attend_tok * 2 * d * es / nsteps
         io_bytes = B * Hq * d * es + B * Hq * (d + 1) * 4 + 8 * sum(kept_tot.values()) / nsteps
         step_bytes = route_bytes + attend_bytes + io_bytes
         Ncur = layer_lens[0][0]
-        kappa = attend_tok / nsteps / (RU * Ncur)
+        kappa = attend_tok / nsteps / (U * Ncur)
         dense_bytes = U * Ncur * 2 * d * es
 
         # the dominant kernel: largest share of the step's time
         if dom_name.startswith("score_l"):
             l = dom["level"]
-            dom_bytes = fr_tot[l] / nsteps * (S_node + Gr * 4) + B * Hq * d * es + (fr_tot[l] / nsteps / C * 4 if l < L else 0)
-            traffic = committed_traffic(args.config) if l == 1 and summary == "native" else None
+            dom_bytes = (fr_tot[l] * S_node + fr_unit[l] * Gr * 4 + (fr_unit[l] / C * 4 if l < L else 0)) / nsteps \
+                + B * Hq * d * es
+            traffic = committed_traffic(args.config) if l == 1 and summary == "native" and mode == "group" else None
         elif dom_name == "attend":
             dom_bytes = attend_bytes + B * Hq * d * es
             traffic = None
