@@ -56,8 +56,9 @@ VARIANTS = [
     ("bf16 d128 wide C256 L1 R16", dict(batch=1, n_tokens=16484, chunk=256, levels=1, n_refs=16), [16484]),
     ("f32 d64 C4 L4 R16 G1", dict(batch=1, n_tokens=3000, head_dim=64, n_q_heads=1, n_kv_heads=1, chunk=4, levels=4,
                                   n_refs=16, dtype="f32", head_scale=False), [3000]),
-    # levels of up to 8192 nodes are selected by one workgroup (two load batches here);
-    # larger levels take the multi-workgroup masses, the histogram cut and the look-back compaction
+    # levels of up to 8192 nodes are selected by one workgroup (two load batches in "mid flat");
+    # larger levels take the multi-workgroup masses, the histogram cut and the look-back
+    # compaction ("large frontier", "large flat")
     ("bf16 d64 C16 L1 R4 G4 mid flat", dict(batch=2, n_tokens=100000, head_dim=64, n_q_heads=8, n_kv_heads=2,
                                             chunk=16, levels=1, n_refs=4), [100000, 75001]),
     ("bf16 d128 C4 L2 R16 G8 large frontier", dict(batch=1, n_tokens=65539, n_q_heads=16, n_kv_heads=2, chunk=4,
@@ -79,6 +80,8 @@ def test_variants(label, kw, lens):
         for p in (0.5, 0.9):
             r, a = full_check(case, tree, t, p)
             say(f" t={t} p={p}", r, a)
+    if "flat" in label or "frontier" in label:  # level 1 of 6250 nodes: one workgroup; 16384, 25000: many
+        assert selection_levels(tree, lambda: tree.route(case.qd[0], 0.9, 1.0)) == ([] if "mid" in label else [1])
     say(" dense", check_dense(case, 0))
 
 
@@ -354,6 +357,16 @@ def test_block_capacity_and_order():
     assert ei.value.status == zha.ZHA_ERR_CAPACITY
 
 
+def selection_levels(tree, route):
+    """Levels whose selection ran the multi-workgroup path (a mass kernel) in `route()`."""
+    tree.timing(True)
+    route()
+    torch.cuda.synchronize()
+    recs = tree.timing_read()
+    tree.timing(False)
+    return sorted({l for k, l, _ in recs if k == zha.ZHA_K_MASS})
+
+
 # --------------------------------------------------------------------------- large-level selection paths
 
 def test_large_level_cut_paths():
@@ -368,6 +381,7 @@ def test_large_level_cut_paths():
     for p in (1e-6, 0.3, 0.9, 0.999999):
         r, a = full_check(case, tree, int(p < 0.5), p)
         say(f" p={p}", r, a)
+    assert selection_levels(tree, lambda: tree.route(case.qd[0], 0.9, 1.0)) == [1]
 
 
 def test_maximum_shapes():
@@ -403,13 +417,15 @@ def test_large_level_with_short_sequence():
         say(f" p={p}", r, a)
 
 
-def test_equal_masses_large_level():
-    """All keys zero: every node of a 10000-node level carries the same mass, so the crossing
-    slice is one value held by every node (more than the candidate buffer) and the cut is
-    split by position: exactly the first ceil(p n) ids are kept."""
-    cfg = small(batch=1, n_tokens=40000, n_q_heads=8, n_kv_heads=2, chunk=4, levels=1, n_refs=4, head_dim=64,
+@pytest.mark.parametrize("N", [20000, 40000])
+def test_equal_masses_large_level(N):
+    """All keys zero: every node of a 5000-node level (one-workgroup selection) or a
+    10000-node level (multi-workgroup selection) carries the same mass, so the crossing slice is
+    one value held by every node (more than the candidate buffer) and the cut is split by
+    position: exactly the first ceil(p n) ids are kept."""
+    cfg = small(batch=1, n_tokens=N, n_q_heads=8, n_kv_heads=2, chunk=4, levels=1, n_refs=4, head_dim=64,
                 n_queries=2, needles_per_unit=2)
-    say("case equal masses: N=40000 C=4 L=1 R=4, K = 0, p=0.33333")
+    say(f"case equal masses: N={N} C=4 L=1 R=4, K = 0, p=0.33333")
     case = Case(cfg, n_queries=2)
     case.Kd.zero_()
     for key in case.K:
@@ -418,7 +434,8 @@ def test_equal_masses_large_level():
     p = 0.33333
     r, a = full_check(case, tree, 0, p)
     nf, nk, ids = tree.route_level(1)
-    n = 10000
+    n = N // 4
+    assert selection_levels(tree, lambda: tree.route(case.qd[0], p, 1.0)) == ([1] if n > 8192 else [])
     k = int(np.ceil(p * n))
     assert nf.cpu().tolist() == [n] * case.Hkv
     assert nk.cpu().tolist() == [k] * case.Hkv, nk.cpu().tolist()
