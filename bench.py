@@ -176,8 +176,8 @@ def union_counts(tree, L, C, hr, Tq, Hkv, lens, qtail):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the path would shard by (sequence, KV head) with no exchange, see DESIGN.md", flush=True)
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path would shard by (sequence, KV head), with no exchange between GPUs", flush=True)
         sys.exit(2)
     import numpy as np
     import torch

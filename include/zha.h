@@ -60,7 +60,7 @@ typedef enum {
     ZHA_ERR_INVALID = 1,      /* an argument is out of range or null */
     ZHA_ERR_CAPACITY = 2,     /* a length exceeds the tree's max_tokens */
     ZHA_ERR_NOMEM = 3,        /* device or host allocation failed */
-    ZHA_ERR_UNSUPPORTED = 4,  /* a shape this build does not implement */
+    ZHA_ERR_UNSUPPORTED = 4,  /* a shape the library does not implement */
     ZHA_ERR_HIP = 5           /* a HIP runtime call failed */
 } zha_status;
 
@@ -69,7 +69,7 @@ typedef enum { ZHA_F32 = 0, ZHA_BF16 = 1 } zha_dtype;
 /* Storage of the planes' m.  ZHA_SUMMARY_NATIVE: m in the tree dtype.
  * ZHA_SUMMARY_FP8 (tree dtype bf16 only): a low-precision router summary
  * ([wqu] opening bullets: a router variant in a 4-bit format was also tested;
- * the pages give no format, this build offers 8 bits).  Each (node, reference)
+ * the pages give no format; the library offers 8 bits here and 4 bits below).  Each (node, reference)
  * row of d values is stored as OCP fp8 e4m3 codes times a power-of-two scale
  * 2^e, e the smallest integer with max|m| * 2^-e <= 448; each value m * 2^-e is
  * rounded to the nearest e4m3 value (ties to even mantissa, subnormals kept).
