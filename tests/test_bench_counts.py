@@ -52,3 +52,15 @@ def test_union_counts_match_oracle_routes(N, hr, Tq):
     assert ufr == {l: len(want_fr.get(l, ())) for l in range(1, L + 1)}
     assert tok == sum(len(v) for v in want_tok.values())
     assert fr_unit == {l: sum(len(f[l]) for f in fr) for l in range(1, L + 1)}
+
+
+def test_bench_refuses_several_gpus():
+    """The benchmark runs on one GPU: asked for more it exits with status 2 and says so."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stdout + r.stderr
