@@ -491,6 +491,7 @@ __device__ __forceinline__ int position_token(const Positions& P, int p, int C, 
   return Cshift >= 0 ? (id << Cshift) + (q & ((1 << Cshift) - 1)) : id * C + (q - k * C);
 }
 
+
 // Union attention over 16 * CT query heads of one group (bf16): every stage of 128 / CT
 // positions is loaded once by the whole workgroup into LDS (two buffers; the next two
 // stages' loads in flight in registers while one is computed), and wave w multiplies its
@@ -559,15 +560,31 @@ __global__ __launch_bounds__(256, 2) void zha_attend_union_lds_kernel(AttArgs a)
 
   const int start = blockIdx.x * TOK;
   const int gstep = a.W * TOK;
-  // tokens of this thread's rows of the stage at ps (rows past the end read token 0)
-  auto tokens = [&](int ps, int (&tk)[NLD]) {
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int p = ps + (tid + 256 * i) / CPR;
-      tk[i] = p < end ? position_token(P, p, a.C, a.Cshift) : 0;
-    }
+  // Chunk ids of the stage at ps: lane j holds the j-th kept chunk its positions touch, read
+  // from a clamped (always readable) index, so the stage's tokens cost one load that no
+  // branch guards (a guarded load makes the compiler wait for every load in flight).
+  static_assert(TOK / 2 + 2 <= 64, "a stage touches at most 64 chunks (C >= 2)");
+  const int nidx = max(P.nK - 1, 0);
+  auto first_chunk = [&](int ps) {
+    const int q = ps - P.nx;
+    return q <= 0 ? 0 : (a.Cshift >= 0 ? (q >> a.Cshift) : q / a.C);
   };
-  // loads of this thread's pieces of K and V of a stage whose tokens are known
+  auto stage_ids = [&](int ps) -> int { return P.kp[min(first_chunk(ps) + lane, nidx)]; };
+  // token of position p of the stage at ps (positions at or past the end: token 0); every
+  // lane calls this together (it shuffles)
+  auto stage_token = [&](int ids, int ps, int p) -> int {
+    const int q = p - P.nx;
+    const int k = q > 0 ? (a.Cshift >= 0 ? (q >> a.Cshift) : q / a.C) : 0;
+    const int id = __shfl(ids, min(max(k - first_chunk(ps), 0), 63));
+    const int ct = a.Cshift >= 0 ? (id << a.Cshift) + (q & ((1 << a.Cshift) - 1)) : id * a.C + (q - k * a.C);
+    const int pre = (P.sink && p == 0) ? 0 : P.Nc + p - P.sink;
+    return p >= end ? 0 : (q < 0 ? pre : ct);
+  };
+  // tokens of this thread's rows of the stage at ps
+  auto tokens = [&](int ps, int ids, int (&tk)[NLD]) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) tk[i] = stage_token(ids, ps, ps + (tid + 256 * i) / CPR);
+  };
   auto issue = [&](const int (&tk)[NLD], bf16x8_t (&kr)[NLD], bf16x8_t (&vr)[NLD]) {
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
@@ -584,20 +601,19 @@ __global__ __launch_bounds__(256, 2) void zha_attend_union_lds_kernel(AttArgs a)
       *(bf16x8_t*)(skv + (2 * b + 1) * BUF + r * KST + 8 * pc) = vr[i];
     }
   };
-  // stamps of the chunks of this lane's positions in its window of the stage at ps
-  auto fetch_rank = [&](int ps, uint32_t (&rk)[2][4]) {
+  // stamps of the chunks of this lane's positions in its window of the stage at ps, for the
+  // lane's column unit (0 outside the chunk part; the rank load is unconditional)
+  auto fetch_rank = [&](int ps, int ids, uint32_t (&rk)[2][4]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int p = ps + ws * ATT_STEP + 16 * t + 4 * grp + jj;
+        const int tok = stage_token(ids, ps, p);
         const bool need = colok && p < end && p >= P.nx;
-        int k = 0;
-        if (need) {
-          const int tok = position_token(P, p, a.C, a.Cshift);
-          k = a.Cshift >= 0 ? (tok >> a.Cshift) : tok / a.C;
-        }
-        rk[t][jj] = need ? ((const uint32_t*)(kr1 + k))[1] : 0u;
+        const int k = need ? (a.Cshift >= 0 ? (tok >> a.Cshift) : tok / a.C) : 0;
+        const uint32_t st = ((const uint32_t*)(kr1 + k))[1];
+        rk[t][jj] = need ? st : 0u;
       }
   };
   auto member_bits = [&](int ps, const uint32_t (&rk)[2][4]) {
@@ -662,29 +678,38 @@ __global__ __launch_bounds__(256, 2) void zha_attend_union_lds_kernel(AttArgs a)
     PVT::mma(o, sv, pr, lane);
   };
 
-  // pipeline: while the stage at ps (in LDS buffer b) is computed, the next three stages'
-  // K/V are loading into registers (stored to LDS one stage ahead of use) and the tokens of
-  // the stage after those are being looked up, so no load waits on a lookup.  Register sets
-  // rotate with the stage index mod 3.
+  // pipeline over the stages ps, ps + gstep, ...: while the stage at ps (in LDS buffer b) is
+  // computed, the K/V of the next two stages are loading into registers (stored to LDS one
+  // stage ahead of use), the column stamps of the next stage and the chunk ids of the stage
+  // after those are in flight.  Every lookup is issued before the K/V loads of its iteration
+  // and consumed in a later one, so waiting for a lookup never drains the K/V loads.
+  // Register sets rotate with the stage index mod 3.
   bf16x8_t kk[3][NLD], vv[3][NLD];
-  int tk[3][NLD];
+  int ids[3];
   uint32_t rk[3][2][4];
   int ps = start, b = 0;
-  tokens(ps, tk[0]);
-  tokens(ps + gstep, tk[1]);
-  tokens(ps + 2 * gstep, tk[2]);
-  issue(tk[0], kk[0], vv[0]);
-  issue(tk[1], kk[1], vv[1]);
-  issue(tk[2], kk[2], vv[2]);
-  tokens(ps + 3 * gstep, tk[0]);
-  fetch_rank(ps, rk[0]);
+  ids[0] = stage_ids(ps);
+  ids[1] = stage_ids(ps + gstep);
+  ids[2] = stage_ids(ps + 2 * gstep);
+  {
+    int tk[NLD];
+    tokens(ps, ids[0], tk);
+    issue(tk, kk[0], vv[0]);
+    tokens(ps + gstep, ids[1], tk);
+    issue(tk, kk[1], vv[1]);
+  }
+  fetch_rank(ps, ids[0], rk[0]);
   store(0, kk[0], vv[0]);
   __syncthreads();
   auto iter = [&](auto J) {
-    constexpr int j = decltype(J)::value, j1 = (j + 1) % 3;  // set of stage ps, of ps + gstep
-    issue(tk[j], kk[j], vv[j]);        // stage ps + 3 gstep
-    tokens(ps + 4 * gstep, tk[j1]);
-    fetch_rank(ps + gstep, rk[j1]);
+    constexpr int j = decltype(J)::value, j1 = (j + 1) % 3, j2 = (j + 2) % 3;  // stages ps, +1, +2
+    ids[j] = stage_ids(ps + 3 * gstep);
+    fetch_rank(ps + gstep, ids[j1], rk[j1]);
+    {
+      int tk[NLD];
+      tokens(ps + 2 * gstep, ids[j2], tk);
+      issue(tk, kk[j2], vv[j2]);
+    }
     compute(b, member_bits(ps, rk[j]));
     store(b ^ 1, kk[j1], vv[j1]);      // stage ps + gstep
     __syncthreads();
