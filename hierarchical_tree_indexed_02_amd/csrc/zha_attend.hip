@@ -482,16 +482,6 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
   }
 }
 
-// Token of position p of a position list (sink and tail first, then the listed chunks).
-__device__ __forceinline__ int position_token(const Positions& P, int p, int C, int Cshift) {
-  if (p < P.nx) return (P.sink && p == 0) ? 0 : P.Nc + p - P.sink;
-  const int q = p - P.nx;
-  const int k = Cshift >= 0 ? (q >> Cshift) : q / C;
-  const int id = P.kp[k];
-  return Cshift >= 0 ? (id << Cshift) + (q & ((1 << Cshift) - 1)) : id * C + (q - k * C);
-}
-
-
 // Union attention over 16 * CT query heads of one group (bf16): every stage of 128 / CT
 // positions is loaded once by the whole workgroup into LDS (two buffers; the next two
 // stages' loads in flight in registers while one is computed), and wave w multiplies its
