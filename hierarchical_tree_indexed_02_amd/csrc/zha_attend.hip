@@ -592,19 +592,33 @@ __global__ __launch_bounds__(256, 2) void zha_attend_union_lds_kernel(AttArgs a)
     }
   };
   // stamps of the chunks of this lane's positions in its window of the stage at ps, for the
-  // lane's column unit (0 outside the chunk part; the rank load is unconditional)
+  // lane's column unit (0 outside the chunk part).  A lane's four consecutive positions lie in
+  // at most three consecutive kept chunks (two when C >= 3), so three stamps are loaded per
+  // group of four, straight from the chunk ids (a stamp needs no token); the loads are
+  // unconditional (clamped list entries are kept chunks, so always readable).
   auto fetch_rank = [&](int ps, int ids, uint32_t (&rk)[2][4]) {
+    const int cb = first_chunk(ps);
+    auto lidx = [&](int q) { return q > 0 ? (a.Cshift >= 0 ? (q >> a.Cshift) : q / a.C) : 0; };
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      const int p0 = ps + ws * ATT_STEP + 16 * t + 4 * grp;
+      const int k0 = lidx(p0 - P.nx), k3 = lidx(p0 + 3 - P.nx), k1 = min(k0 + 1, k3);
+      uint32_t st[3];
+      const int kc[3] = {k0, k1, k3};
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int id = __shfl(ids, min(max(kc[i] - cb, 0), 63));
+        st[i] = ((const uint32_t*)(kr1 + id))[1];
+      }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int p = ps + ws * ATT_STEP + 16 * t + 4 * grp + jj;
-        const int tok = stage_token(ids, ps, p);
+        const int p = p0 + jj;
         const bool need = colok && p < end && p >= P.nx;
-        const int k = need ? (a.Cshift >= 0 ? (tok >> a.Cshift) : tok / a.C) : 0;
-        const uint32_t st = ((const uint32_t*)(kr1 + k))[1];
-        rk[t][jj] = need ? st : 0u;
+        const int kj = lidx(p - P.nx);
+        const uint32_t sj = kj == k0 ? st[0] : (kj == k1 ? st[1] : st[2]);
+        rk[t][jj] = need ? sj : 0u;
       }
+    }
   };
   auto member_bits = [&](int ps, const uint32_t (&rk)[2][4]) {
     uint32_t bits = 0;
