@@ -314,17 +314,32 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
   // UNI: stamps (the high words of the kept-rank entries) of the chunks of this lane's
   // positions p0 + 16t + 4grp + jj for the lane's column unit (0 outside the chunk part).
   // Every lane calls this together (the token lookup shuffles).
+  // A lane's four consecutive positions lie in at most three consecutive kept chunks (two when
+  // C >= 3): three stamps per group of four, from the window's chunk ids (a stamp needs no
+  // token), loaded unconditionally (ids outside the list are 0, a readable entry).
   auto fetch_rank = [&](const Window<TD>& win, int p0, uint32_t (&rk)[2][4]) {
+    const int cb = Window<TD>::first_chunk(P, p0, a.C, a.Cshift);
+    auto lidx = [&](int q) { return q > 0 ? (a.Cshift >= 0 ? (q >> a.Cshift) : q / a.C) : 0; };
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      const int pg = p0 + 16 * t + 4 * grp;
+      const int k0 = lidx(pg - P.nx), k3 = lidx(pg + 3 - P.nx), k1 = min(k0 + 1, k3);
+      uint32_t st[3];
+      const int kc[3] = {k0, k1, k3};
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int id = __shfl(win.ids, min(max(kc[i] - cb, 0), 63));
+        st[i] = ((const uint32_t*)(kr1 + id))[1];
+      }
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int p = p0 + 16 * t + 4 * grp + jj;
-        const int tok = win.token(P, p0, p, end, a.C, a.Cshift);
+        const int p = pg + jj;
         const bool need = colok && p < end && p >= P.nx;
-        const int k = a.Cshift >= 0 ? (tok >> a.Cshift) : tok / a.C;
-        rk[t][jj] = need ? ((const uint32_t*)(kr1 + k))[1] : 0u;
+        const int kj = lidx(p - P.nx);
+        const uint32_t sj = kj == k0 ? st[0] : (kj == k1 ? st[1] : st[2]);
+        rk[t][jj] = need ? sj : 0u;
       }
+    }
   };
   // UNI: bit 4t + jj: position p0 + 16t + 4grp + jj is in the column's set: token 0 always,
   // the tail up to the column's own end, a chunk token when the column's unit kept it
