@@ -637,6 +637,15 @@ __global__ __launch_bounds__(256, 2) void zha_attend_union_lds_kernel(AttArgs a)
   };
   auto member_bits = [&](int ps, const uint32_t (&rk)[2][4]) {
     uint32_t bits = 0;
+    const int w0 = ps + ws * ATT_STEP;
+    if (w0 > P.nx && w0 + ATT_STEP <= end) {
+      // the whole window lies in the chunk part, past its first position: the stamp decides
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) bits |= (colok && rk[t][jj] == stamp) ? (1u << (4 * t + jj)) : 0u;
+      return bits;
+    }
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
