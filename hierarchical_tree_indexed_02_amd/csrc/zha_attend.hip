@@ -383,23 +383,19 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
     const float mnew = fmaxf(mrun, mloc);
+    // branch-free: a column with nothing in its set so far (mnew = -inf) takes 0 as its
+    // maximum, so alpha and every p are exp2(-inf) = 0 (its o and l are still 0)
+    const float msafe = mnew == -INFINITY ? 0.0f : mnew;
+    const float alpha = zexp2(mrun - msafe);
     float pr[2][4];
-    float alpha = 1.0f, psum = 0.0f;
-    if (mnew == -INFINITY) {
+    float psum = 0.0f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) pr[t][jj] = 0.0f;
-    } else {
-      alpha = zexp2(mrun - mnew);
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          pr[t][jj] = zexp2(z[t][jj] - mnew);
-          psum += pr[t][jj];
-        }
-    }
+      for (int jj = 0; jj < 4; ++jj) {
+        pr[t][jj] = zexp2(z[t][jj] - msafe);
+        psum += pr[t][jj];
+      }
     lrun = lrun * alpha + psum;
     mrun = mnew;
 #pragma unroll
@@ -682,23 +678,19 @@ __global__ __launch_bounds__(256, 2) void zha_attend_union_lds_kernel(AttArgs a)
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
     const float mnew = fmaxf(mrun, mloc);
+    // branch-free: a column with nothing in its set so far (mnew = -inf) takes 0 as its
+    // maximum, so alpha and every p are exp2(-inf) = 0 (its o and l are still 0)
+    const float msafe = mnew == -INFINITY ? 0.0f : mnew;
+    const float alpha = zexp2(mrun - msafe);
     float pr[2][4];
-    float alpha = 1.0f, psum = 0.0f;
-    if (mnew == -INFINITY) {
+    float psum = 0.0f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) pr[t][jj] = 0.0f;
-    } else {
-      alpha = zexp2(mrun - mnew);
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          pr[t][jj] = zexp2(z[t][jj] - mnew);
-          psum += pr[t][jj];
-        }
-    }
+      for (int jj = 0; jj < 4; ++jj) {
+        pr[t][jj] = zexp2(z[t][jj] - msafe);
+        psum += pr[t][jj];
+      }
     lrun = lrun * alpha + psum;
     mrun = mnew;
 #pragma unroll
