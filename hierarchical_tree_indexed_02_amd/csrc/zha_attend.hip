@@ -165,13 +165,19 @@ template <int D> struct PV<__bf16, D> {
   // o[dt] += V^T(d-tile dt) * P^T, k-slot e of lane group grp <-> token e<4 ? 4grp+e : 16+4grp+e-4
   __device__ static __forceinline__ void mma(f32x4_t (&o)[ND], const __bf16* lds, const float (&p)[2][4], int lane) {
     const int row = lane & 15, grp = lane >> 4;
+    // P = hi + lo, each half rounded to nearest even by the packed hardware conversion
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     bf16x8_t ph, pl;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = p[e >> 2][e & 3];
-      const __bf16 hi = Mf<__bf16>::from_f32(x);
-      ph[e] = hi;
-      pl[e] = Mf<__bf16>::from_f32(x - (float)hi);
+    for (int e = 0; e < 8; e += 2) {
+      const f32x2_t x = {p[e >> 2][e & 3], p[(e + 1) >> 2][(e + 1) & 3]};
+      const bf16x2_t h = __builtin_convertvector(x, bf16x2_t);
+      const bf16x2_t l = __builtin_convertvector(x - __builtin_convertvector(h, f32x2_t), bf16x2_t);
+      ph[e] = h[0];
+      ph[e + 1] = h[1];
+      pl[e] = l[0];
+      pl[e + 1] = l[1];
     }
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) {
