@@ -304,6 +304,11 @@ MULTI_VARIANTS = [
                                                                  levels=3, n_refs=4), [3, 1, 517], 4, "group", 4),
     ("block bf16 d64 C4 L3 R4 G1 T16", dict(batch=2, n_tokens=3000, head_dim=64, n_q_heads=2, n_kv_heads=2, chunk=4,
                                              levels=3, n_refs=4), [2950, 1234], 16, "group", 16),
+    # d = 64 union attention staged in LDS: 40 columns (four tiles per group) and 24 (two)
+    ("block bf16 d64 C4 L3 R8 G8 B2 T5", dict(batch=2, n_tokens=3000, head_dim=64, n_q_heads=16, n_kv_heads=2,
+                                               chunk=4, levels=3, n_refs=8), [2990, 1500], 5, "group", 5),
+    ("block bf16 d64 C4 L3 R8 G8 T3", dict(batch=1, n_tokens=2000, head_dim=64, n_q_heads=16, n_kv_heads=2, chunk=4,
+                                            levels=3, n_refs=8), [1990], 3, "group", 3),
 ]
 
 
