@@ -107,6 +107,20 @@ def test_fp8_summaries(label, kw, lens):
             say(f" t={t} p={p}", r, a)
 
 
+@pytest.mark.parametrize("summary", ["fp8", "fp4"])
+def test_low_precision_per_head_routing(summary):
+    """Per-head routes (union scoring of the eight heads of a KV head, union attention) over
+    fp8 and fp4 planes, teacher-forced on the decoded planes like the group routes."""
+    cfg = small(batch=2, n_tokens=5000, chunk=4, levels=3, n_refs=16, n_queries=4, needles_per_unit=4)
+    lens = [5000, 3333]
+    say(f"case per-head routes over {summary} planes: lens={lens} C=4 L=3 R=16 G=8")
+    case = Case(cfg, lens=lens, n_queries=2)
+    tree = case.tree(summary=summary, per_head_routes=True)
+    for t, p in ((0, 0.5), (1, 0.95)):
+        r, a = full_check(case, tree, t, p, mode="per_head")
+        say(f" t={t} p={p}", r, a)
+
+
 def _e4m3_nonnegative():
     """Every non-negative finite e4m3 value: zero, the subnormals f 2^-9 and the normals up to 448."""
     v = [f * 2.0 ** -9 for f in range(0, 8)] + [(1 + f / 8) * 2.0 ** (e - 7) for e in range(1, 16) for f in range(8)]
