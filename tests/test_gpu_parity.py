@@ -323,6 +323,9 @@ MULTI_VARIANTS = [
                                                chunk=4, levels=3, n_refs=8), [2990, 1500], 5, "group", 5),
     ("block bf16 d64 C4 L3 R8 G8 T3", dict(batch=1, n_tokens=2000, head_dim=64, n_q_heads=16, n_kv_heads=2, chunk=4,
                                             levels=3, n_refs=8), [1990], 3, "group", 3),
+    # f32 union scoring with four column tiles (40 columns); f32 attention groups of 16 columns
+    ("block f32 d128 C4 L3 R16 G8 T5", dict(batch=1, n_tokens=2000, n_q_heads=16, n_kv_heads=2, chunk=4, levels=3,
+                                            n_refs=16, dtype="f32"), [1990], 5, "group", 5),
 ]
 
 
