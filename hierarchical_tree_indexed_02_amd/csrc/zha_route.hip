@@ -260,6 +260,10 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
     }
   }
   const int32_t* par = (!UNI && a.v.parent) ? a.v.parent + (int64_t)u[0] * a.v.cap_parent : nullptr;
+  // always-readable bases for the unconditional parent-id and kept-rank loads (entry 0 is read
+  // when the real array is absent or the entry is not needed)
+  const int32_t* pload = par ? par : a.v.nodes;
+  const u64* kload = a.krank ? a.krank : (const u64*)a.scores;
   const T* mb = (const T*)a.m + (int64_t)up * a.capl * R * D;
   const uint8_t* m8 = (const uint8_t*)a.m + (int64_t)up * a.capl * R * (F4 ? D / 2 : D);
   const float* bb = a.b + (int64_t)up * a.capl * R;
@@ -281,12 +285,17 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
         const int id = base + (k * 4 + wave) * NPT + (4 * grp) / R;
         const int P = a.v.Cshift >= 0 ? (id >> a.v.Cshift) : id / a.v.C;
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
-          rk[k][n] = (a.krank && ok[n] && id < end) ? a.krank[(int64_t)u[n] * a.v.cap_parent + P] : 0;
+        for (int n = 0; n < NT; ++n) {
+          const bool need = a.krank && ok[n] && id < end;
+          const u64 x = kload[need ? (int64_t)u[n] * a.v.cap_parent + P : 0];  // unconditional load
+          rk[k][n] = need ? x : 0;
+        }
         pp[k] = 0;
       } else {
         const int pos = base + (k * 4 + wave) * NPT + row / R;
-        pp[k] = (par && pos < end) ? par[a.v.Cshift >= 0 ? (pos >> a.v.Cshift) : pos / a.v.C] : 0;
+        const bool need = par && pos < end;
+        const int32_t x = pload[need ? (a.v.Cshift >= 0 ? (pos >> a.v.Cshift) : pos / a.v.C) : 0];
+        pp[k] = need ? x : 0;
         rk[k][0] = 0;
       }
     }
@@ -338,23 +347,28 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
       if (!UNI && par) id = a.v.Cshift >= 0 ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
                                            : pp[k] * a.v.C + pos % a.v.C;
       id = v ? id : 0;
+      // loads are unconditional (inactive rows read node 0, whose results are never written),
+      // so no load sits under a branch that would make the compiler drain the loads in flight
       const T* mp = mb + ((int64_t)id * R + (row % R)) * D + grp * M::EPL;
 #pragma unroll
-      for (int s = 0; s < NK; ++s) af[k][s] = v ? M::load(mp + s * M::KPER) : M::zero();
+      for (int s = 0; s < NK; ++s) af[k][s] = M::load(mp + s * M::KPER);
       if constexpr (R >= 4) {
         // rows 4grp..4grp+3 of this lane belong to one node: its four offsets in one load
         const int id2 = __shfl(id, 4 * grp);
         const bool v2 = UNI ? ((act[k] >> ((4 * grp) / R)) & 1u) != 0 : tbk + (4 * grp) / R < end;
-        const float4 b4 = v2 ? *(const float4*)(bb + (int64_t)id2 * R + (4 * grp) % R)
-                             : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        bv[k][0] = b4.x; bv[k][1] = b4.y; bv[k][2] = b4.z; bv[k][3] = b4.w;
+        const float4 x = *(const float4*)(bb + (int64_t)id2 * R + (4 * grp) % R);
+        bv[k][0] = v2 ? x.x : -INFINITY;
+        bv[k][1] = v2 ? x.y : -INFINITY;
+        bv[k][2] = v2 ? x.z : -INFINITY;
+        bv[k][3] = v2 ? x.w : -INFINITY;
       } else {
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const int r2 = 4 * grp + jj;
           const int id2 = __shfl(id, r2);
           const bool v2 = tbk + r2 / R < end;
-          bv[k][jj] = v2 ? bb[(int64_t)id2 * R + (r2 % R)] : -INFINITY;
+          const float x = bb[(int64_t)id2 * R + (r2 % R)];
+          bv[k][jj] = v2 ? x : -INFINITY;
         }
       }
     }
@@ -435,25 +449,28 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
         const int64_t rw4 = (int64_t)id * R + (row % R);
         const uint8_t* cp = m8 + rw4 * (D / 2) + grp * (D / 8);
         if constexpr (D == 128) {
-          rw[k][0] = v ? *(const uint4*)cp : make_uint4(0u, 0u, 0u, 0u);
+          rw[k][0] = *(const uint4*)cp;
         } else {
-          const uint2 q2 = v ? *(const uint2*)cp : make_uint2(0u, 0u);
+          const uint2 q2 = *(const uint2*)cp;
           rw[k][0] = make_uint4(q2.x, q2.y, 0u, 0u);
         }
-        sv[k][0] = v ? fp4_scale(sb4[rw4 * (D / 32) + (grp * (D / 4)) / 32]) : 0.0f;
+        sv[k][0] = fp4_scale(sb4[rw4 * (D / 32) + (grp * (D / 4)) / 32]);
       } else {
         const uint8_t* cp = m8 + ((int64_t)id * R + (row % R)) * D + grp * (D / 4);
 #pragma unroll
-        for (int i = 0; i < NR; ++i) rw[k][i] = v ? *(const uint4*)(cp + 16 * i) : make_uint4(0u, 0u, 0u, 0u);
+        for (int i = 0; i < NR; ++i) rw[k][i] = *(const uint4*)(cp + 16 * i);
       }
       if constexpr (R >= 4) {
         const int id2 = __shfl(id, 4 * grp);
         const bool v2 = UNI ? ((act[k] >> ((4 * grp) / R)) & 1u) != 0 : tbk + (4 * grp) / R < end;
         const int64_t o = (int64_t)id2 * R + (4 * grp) % R;
-        const float4 b4 = v2 ? *(const float4*)(bb + o) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        bv[k][0] = b4.x; bv[k][1] = b4.y; bv[k][2] = b4.z; bv[k][3] = b4.w;
+        const float4 b4 = *(const float4*)(bb + o);
+        bv[k][0] = v2 ? b4.x : -INFINITY;
+        bv[k][1] = v2 ? b4.y : -INFINITY;
+        bv[k][2] = v2 ? b4.z : -INFINITY;
+        bv[k][3] = v2 ? b4.w : -INFINITY;
         if constexpr (F8) {
-          const float4 s4 = v2 ? *(const float4*)(sb + o) : make_float4(0.f, 0.f, 0.f, 0.f);
+          const float4 s4 = *(const float4*)(sb + o);
           sv[k][0] = s4.x; sv[k][1] = s4.y; sv[k][2] = s4.z; sv[k][3] = s4.w;
         }
       } else {
@@ -463,8 +480,9 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
           const int id2 = __shfl(id, r2);
           const bool v2 = tbk + r2 / R < end;
           const int64_t o = (int64_t)id2 * R + (r2 % R);
-          bv[k][jj] = v2 ? bb[o] : -INFINITY;
-          if constexpr (F8) sv[k][jj] = v2 ? sb[o] : 0.0f;
+          const float x = bb[o];
+          bv[k][jj] = v2 ? x : -INFINITY;
+          if constexpr (F8) sv[k][jj] = sb[o];
         }
       }
     }
