@@ -202,6 +202,12 @@ template <typename T, int R, int D, int UN, int SM, bool UNI, int NT>
 __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a) {
   typedef Mf<T> M;
   constexpr bool F8 = SM == 1, F4 = SM == 2, LP = SM != 0;  // summary storage: native, fp8, fp4
+  // FLAT: loads are issued unconditionally (inactive rows read a clamped, readable address and
+  // their results are discarded), so no load sits under a branch, after whose join the compiler
+  // waits for every load in flight.  Taken where it measured faster (union scoring, fp4 planes);
+  // the bandwidth-bound native and fp8 per-unit kernels keep guarded loads, which spare the
+  // small levels the reads of rows past the frontier.
+  constexpr bool FLAT = UNI || F4;
   constexpr int NK = D / M::KPER;
   constexpr int NR = F8 ? D / 64 : 1;   // 16-byte code loads per lane per tile (F8; F4 uses one)
   constexpr int NPT = 16 / R;
@@ -287,14 +293,14 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           const bool need = a.krank && ok[n] && id < end;
-          const u64 x = kload[need ? (int64_t)u[n] * a.v.cap_parent + P : 0];  // unconditional load
+          const u64 x = kload[need ? (int64_t)u[n] * a.v.cap_parent + P : 0];
           rk[k][n] = need ? x : 0;
         }
         pp[k] = 0;
       } else {
         const int pos = base + (k * 4 + wave) * NPT + row / R;
         const bool need = par && pos < end;
-        const int32_t x = pload[need ? (a.v.Cshift >= 0 ? (pos >> a.v.Cshift) : pos / a.v.C) : 0];
+        const int32_t x = (FLAT || need) ? pload[need ? (a.v.Cshift >= 0 ? (pos >> a.v.Cshift) : pos / a.v.C) : 0] : 0;
         pp[k] = need ? x : 0;
         rk[k][0] = 0;
       }
@@ -347,16 +353,16 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
       if (!UNI && par) id = a.v.Cshift >= 0 ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
                                            : pp[k] * a.v.C + pos % a.v.C;
       id = v ? id : 0;
-      // loads are unconditional (inactive rows read node 0, whose results are never written),
-      // so no load sits under a branch that would make the compiler drain the loads in flight
+      // inactive rows read node 0 (FLAT) or nothing; their results are never written
       const T* mp = mb + ((int64_t)id * R + (row % R)) * D + grp * M::EPL;
 #pragma unroll
-      for (int s = 0; s < NK; ++s) af[k][s] = M::load(mp + s * M::KPER);
+      for (int s = 0; s < NK; ++s) af[k][s] = (FLAT || v) ? M::load(mp + s * M::KPER) : M::zero();
       if constexpr (R >= 4) {
         // rows 4grp..4grp+3 of this lane belong to one node: its four offsets in one load
         const int id2 = __shfl(id, 4 * grp);
         const bool v2 = UNI ? ((act[k] >> ((4 * grp) / R)) & 1u) != 0 : tbk + (4 * grp) / R < end;
-        const float4 x = *(const float4*)(bb + (int64_t)id2 * R + (4 * grp) % R);
+        const float4 x = (FLAT || v2) ? *(const float4*)(bb + (int64_t)id2 * R + (4 * grp) % R)
+                                      : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         bv[k][0] = v2 ? x.x : -INFINITY;
         bv[k][1] = v2 ? x.y : -INFINITY;
         bv[k][2] = v2 ? x.z : -INFINITY;
@@ -367,7 +373,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
           const int r2 = 4 * grp + jj;
           const int id2 = __shfl(id, r2);
           const bool v2 = tbk + r2 / R < end;
-          const float x = bb[(int64_t)id2 * R + (r2 % R)];
+          const float x = (FLAT || v2) ? bb[(int64_t)id2 * R + (r2 % R)] : -INFINITY;
           bv[k][jj] = v2 ? x : -INFINITY;
         }
       }
@@ -458,19 +464,20 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
       } else {
         const uint8_t* cp = m8 + ((int64_t)id * R + (row % R)) * D + grp * (D / 4);
 #pragma unroll
-        for (int i = 0; i < NR; ++i) rw[k][i] = *(const uint4*)(cp + 16 * i);
+        for (int i = 0; i < NR; ++i) rw[k][i] = (FLAT || v) ? *(const uint4*)(cp + 16 * i) : make_uint4(0u, 0u, 0u, 0u);
       }
       if constexpr (R >= 4) {
         const int id2 = __shfl(id, 4 * grp);
         const bool v2 = UNI ? ((act[k] >> ((4 * grp) / R)) & 1u) != 0 : tbk + (4 * grp) / R < end;
         const int64_t o = (int64_t)id2 * R + (4 * grp) % R;
-        const float4 b4 = *(const float4*)(bb + o);
+        const float4 b4 = (FLAT || v2) ? *(const float4*)(bb + o)
+                                       : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         bv[k][0] = v2 ? b4.x : -INFINITY;
         bv[k][1] = v2 ? b4.y : -INFINITY;
         bv[k][2] = v2 ? b4.z : -INFINITY;
         bv[k][3] = v2 ? b4.w : -INFINITY;
         if constexpr (F8) {
-          const float4 s4 = *(const float4*)(sb + o);
+          const float4 s4 = (FLAT || v2) ? *(const float4*)(sb + o) : make_float4(0.f, 0.f, 0.f, 0.f);
           sv[k][0] = s4.x; sv[k][1] = s4.y; sv[k][2] = s4.z; sv[k][3] = s4.w;
         }
       } else {
@@ -480,9 +487,9 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
           const int id2 = __shfl(id, r2);
           const bool v2 = tbk + r2 / R < end;
           const int64_t o = (int64_t)id2 * R + (r2 % R);
-          const float x = bb[o];
+          const float x = (FLAT || v2) ? bb[o] : -INFINITY;
           bv[k][jj] = v2 ? x : -INFINITY;
-          if constexpr (F8) sv[k][jj] = sb[o];
+          if constexpr (F8) sv[k][jj] = (FLAT || v2) ? sb[o] : 0.0f;
         }
       }
     }
