@@ -4,13 +4,20 @@ One step = one decode step of one attention layer: route the B x Hq queries
 through that layer's tree (every level) and attend over the kept chunks plus
 sink and tail.  For a workload with decode-time growth (batch8_append_512k) a
 step first appends one K/V row per sequence (zha_append), then routes and
-attends once for each p of the workload's sweep; `value` is append + route +
-attend at the first p (or --p), and `p_sweep` gives every p.  Inputs are
+attends once for each p of the workload's sweep; its step time is append +
+route + attend at the first p, and `p_sweep` gives every p.  Inputs are
 resident in HBM before timing; steps cycle through `--layers` replicas of
 (K, V, tree) so every step reads its layer cold, and through `--queries`
-different decode queries.  Prints one JSON line.
+different decode queries.
 
-  python bench.py [--gpus 1] [--steps 40] [--warmup 5] [--config deep_256k]
+The headline workload (--config, default deep_256k) is measured with every
+extra leg (fp8 and fp4 summaries, per-head routes, a block of queries, dense
+decode on the same inputs, the CPU oracle); the other workloads of the metric
+(wide_256k, deep_1m, batch8_append_512k) follow as sub-records under
+`workloads`, each with its own step time, dense time and roofline.  Prints one
+JSON line.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config deep_256k]
 """
 from __future__ import annotations
 
@@ -18,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import re
 import sys
 import time
@@ -27,12 +35,16 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "ZHA decode µs/step/layer at 256K & 1M ctx; achieved HBM GB/s vs peak"
+SUB_WORKLOADS = ("wide_256k", "deep_1m", "batch8_append_512k")
+# layer replicas per workload: enough that a step never finds its layer in the 256 MB
+# last-level cache (one layer of the 1M and batched workloads is several GB)
+SUB_LAYERS = {"wide_256k": 4, "deep_1m": 2, "batch8_append_512k": 2}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="deep_256k")
     ap.add_argument("--layers", type=int, default=4)
@@ -49,6 +61,8 @@ def parse():
                     help="also route and attend blocks of this many queries per sequence (0: skip)")
     ap.add_argument("--no-per-head", action="store_true",
                     help="skip the extra pass that routes every query head alone (reported beside the headline)")
+    ap.add_argument("--workloads", default=",".join(SUB_WORKLOADS),
+                    help="comma-separated workloads measured after the headline as sub-records ('' for none)")
     ap.add_argument("--sweep", action="store_true",
                     help="also time the workload's inputs under other tree geometries (C, L, R) and p, and fit a "
                          "step-time model (bytes at the measured bandwidths + a fixed cost per routing level)")
@@ -86,6 +100,23 @@ def committed_traffic(workload: str):
     if not m_sha or not m_tr or m_sha.group(1) != score_kernel_sha():
         return None
     return float(m_tr.group(1))
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu's "Model name" line, read from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def pct(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q)) if len(xs) else None
 
 
 # Tree geometries (chunk C, levels L, references R) over the same 256K-token inputs: C^L = 4096
@@ -136,7 +167,6 @@ def geometry_sweep(measure, cfg, zi, torch, np, dev, N, B, Hkv, d, es, log):
     return dict(fit=fit, rows=rows)
 
 
-
 def union_counts(tree, L, C, hr, Tq, Hkv, lens, qtail):
     """Distinct work of the last route when all routing units of one (sequence, KV head)
     are served together, as the union kernels serve them (its query heads after a per-head
@@ -173,24 +203,49 @@ def union_counts(tree, L, C, hr, Tq, Hkv, lens, qtail):
         tok += sink + (lens[b] + (Tq if qtail else 0) - Nc) + len(k1) * C
     return fr, tok, fr_unit, kept_unit
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the path would shard by (sequence, KV head), with no exchange between GPUs", flush=True)
-        sys.exit(2)
-    import numpy as np
-    import torch
 
-    import zha_inputs as zi
-    from hierarchical_tree_indexed_02_amd import zha
-    from hierarchical_tree_indexed_02_amd.runtime import Tree, dense_decode
+def input_key(cfg):
+    """Fields that decide a workload's generated inputs (deep_256k and wide_256k share theirs)."""
+    return (cfg.seed, cfg.batch, cfg.n_tokens, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_queries,
+            cfg.needles_per_unit, cfg.needles_per_query, cfg.dtype, cfg.head_scale, cfg.append_steps)
 
-    cfg = zi.get_config(args.config)
-    p = args.p if args.p is not None else cfg.p[0]
+
+def load_inputs(cfg, zi, torch, dev, nq, workers=16):
+    """K, V [B][Hkv][max_tokens][d] on the device (the rows appended during decode included),
+    the first nq decode queries [nq][B][Hq][d] and the references, each unit generated from its
+    own stream in a parallel thread."""
+    from concurrent.futures import ThreadPoolExecutor
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    B, Hkv, d, N, T = cfg.batch, cfg.n_kv_heads, cfg.head_dim, cfg.n_tokens, cfg.max_tokens
+    q_all = zi.queries(cfg)
+    K0 = torch.empty((B, Hkv, T, d), dtype=dt, device=dev)
+    V0 = torch.empty((B, Hkv, T, d), dtype=dt, device=dev)
+
+    def gen(bg):
+        b, g = bg
+        Ku, Vu = zi.unit_kv(cfg, b, g, q_all)
+        app = zi.append_rows(cfg, b, g) if cfg.append_steps else None
+        return bg, Ku, Vu, app
+
+    pairs = [(b, g) for b in range(B) for g in range(Hkv)]
+    with ThreadPoolExecutor(max(1, min(workers, len(pairs)))) as ex:
+        for (b, g), Ku, Vu, app in ex.map(gen, pairs):
+            K0[b, g, :N] = torch.from_numpy(Ku).to(dev, dt)
+            V0[b, g, :N] = torch.from_numpy(Vu).to(dev, dt)
+            if app is not None:  # the rows each decode step appends (written before zha_append)
+                K0[b, g, N:] = torch.from_numpy(app[0]).to(dev, dt)
+                V0[b, g, N:] = torch.from_numpy(app[1]).to(dev, dt)
+    qd = torch.from_numpy(q_all[:nq]).to(dev, dt)
+    return K0, V0, qd, q_all
+
+
+def run_workload(cfg, args, env, headline, layers):
+    """Measures one workload; returns its record.  env: modules, device and the input cache."""
+    np, torch, zi, zha, Tree, dense_decode, dev = (env[k] for k in ("np", "torch", "zi", "zha", "Tree", "dense",
+                                                                   "dev"))
+    p = args.p if (args.p is not None and headline) else cfg.p[0]
     growing = cfg.append_steps > 0
     p_sweep = [p] + [x for x in cfg.p if x != p] if growing else [p]
-    dev = torch.device("cuda:0")
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     es = 2 if cfg.dtype == "bf16" else 4
     B, Hkv, Hq, d, N = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim, cfg.n_tokens
@@ -199,30 +254,25 @@ def main():
     nq = min(args.queries, cfg.n_queries)
 
     t0 = time.time()
-    q_all = zi.queries(cfg)
-    q_host = q_all[:nq]
-    K0 = torch.empty((B, Hkv, T, d), dtype=dt, device=dev)
-    V0 = torch.empty((B, Hkv, T, d), dtype=dt, device=dev)
-    for b in range(B):
-        for g in range(Hkv):
-            Ku, Vu = zi.unit_kv(cfg, b, g, q_all)
-            K0[b, g, :N] = torch.from_numpy(Ku).to(dev, dt)
-            V0[b, g, :N] = torch.from_numpy(Vu).to(dev, dt)
-            if growing:  # the rows each decode step appends (written by the caller before zha_append)
-                Ka, Va = zi.append_rows(cfg, b, g)
-                K0[b, g, N:] = torch.from_numpy(Ka).to(dev, dt)
-                V0[b, g, N:] = torch.from_numpy(Va).to(dev, dt)
-    qd = torch.from_numpy(q_host).to(dev, dt)
+    key = input_key(cfg)
+    if env["inputs"].get("key") != key:
+        env["inputs"].clear()
+        torch.cuda.empty_cache()
+        K0, V0, qd, q_all = load_inputs(cfg, zi, torch, dev, max(nq, args.block if headline else 0))
+        env["inputs"].update(key=key, K0=K0, V0=V0, qd=qd, q_all=q_all)
+        log(f"[{cfg.name}] inputs ready in {time.time() - t0:.1f}s")
+    else:
+        log(f"[{cfg.name}] inputs shared with the previous workload")
+    K0, V0, qd, q_all = (env["inputs"][k] for k in ("K0", "V0", "qd", "q_all"))
     refs = torch.from_numpy(zi.refs(cfg)).to(dev)
-    log(f"inputs ready in {time.time() - t0:.1f}s")
 
     Ks, Vs = [K0], [V0]
-    for _ in range(1, args.layers):
+    for _ in range(1, layers):
         Ks.append(K0.clone())
         Vs.append(V0.clone())
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(args.layers)]
-    lses = [torch.empty((B, Hq), dtype=torch.float32, device=dev) for _ in range(args.layers)]
+    outs = [torch.empty((B, Hq, d), dtype=torch.float32, device=dev) for _ in range(layers)]
+    lses = [torch.empty((B, Hq), dtype=torch.float32, device=dev) for _ in range(layers)]
 
     def kernel_table(recs):
         per = {}
@@ -238,16 +288,16 @@ def main():
         cached tokens, N_b = N - Tq when the block's rows would not fit after N."""
         Nb = N if N + Tq <= T else N - Tq
         trees = []
-        for li in range(args.layers):
+        for li in range(layers):
             tr = Tree(B, Hkv, Hq, d, C, L, R, T, dt, per_head_routes=mode == "per_head", max_queries=Tq)
             tr.build(Ks[li], refs, [Nb] * B)
             trees.append(tr)
         qb = torch.from_numpy(np.ascontiguousarray(q_all[:Tq].transpose(1, 0, 2, 3))).to(dev, dt)
-        ob = [torch.empty((B, Tq, Hq, d), dtype=torch.float32, device=dev) for _ in range(args.layers)]
-        lb = [torch.empty((B, Tq, Hq), dtype=torch.float32, device=dev) for _ in range(args.layers)]
+        ob = [torch.empty((B, Tq, Hq, d), dtype=torch.float32, device=dev) for _ in range(layers)]
+        lb = [torch.empty((B, Tq, Hq), dtype=torch.float32, device=dev) for _ in range(layers)]
 
         def step(i):
-            li = i % args.layers
+            li = i % layers
             trees[li].route_multi(qb, p, 1.0, mode=mode)
             trees[li].attend_multi(qb, Ks[li], Vs[li], 1.0, out=ob[li], lse=lb[li])
 
@@ -271,6 +321,8 @@ def main():
         ev1.record()
         torch.cuda.synchronize()
         us = 1e3 * ev0.elapsed_time(ev1) / args.steps
+        for tr in trees:
+            tr.check()
         # algorithmic bytes: replay the block's route once; a KV head's queries and query heads
         # are served as one union, so each distinct node and token is counted once per KV head
         hr = G if mode == "per_head" else 1
@@ -293,15 +345,15 @@ def main():
                     block_gbs=round(nbytes / (us * 1e-6) / 1e9, 1), kappa=round(tok / (U * (Nb + Tq)), 4),
                     kernels={k: round(v["avg_us"], 2) for k, v in kernels.items()})
 
-    def measure(summary, mode="group", C=C, L=L, R=R, refs=refs, p=p):
+    def measure(summary, mode="group", C=C, L=L, R=R, refs=refs, p=p, warm=False):
         """Builds one tree per layer replica with the given m storage (and geometry C, L, R),
         times the stage breakdown and the K-step region, and replays the routes for the
-        byte counts."""
+        byte counts.  warm: every step reads layer 0 with query 0 (its data partly cached)."""
         lens = [N] * B
-        layer_lens = [[N] * B for _ in range(args.layers)]
+        layer_lens = [[N] * B for _ in range(layers)]
         trees = []
         build_ms = []
-        for li in range(args.layers):
+        for li in range(layers):
             tr = Tree(B, Hkv, Hq, d, C, L, R, T, dt, summary=summary, per_head_routes=mode == "per_head")
             torch.cuda.synchronize()
             ev0.record()
@@ -311,9 +363,9 @@ def main():
             build_ms.append(ev0.elapsed_time(ev1))
             trees.append(tr)
         tree_bytes = trees[0].bytes()
-        log(f"trees built: {build_ms} ms; tree+workspace {tree_bytes / 1e9:.2f} GB per layer")
+        log(f"trees built: {[round(x, 3) for x in build_ms]} ms; tree+workspace {tree_bytes / 1e9:.2f} GB per layer")
 
-        if summary == args.summary:
+        if headline and summary == args.summary and mode == "group" and not warm:
             # a copy kernel of known size, for calibrating hardware byte counters in profiles
             cal_n16 = (256 << 20) // 16
             cal_src = torch.empty(cal_n16 * 16, dtype=torch.uint8, device=dev)
@@ -322,7 +374,7 @@ def main():
             torch.cuda.synchronize()
             del cal_src, cal_dst
 
-        segs = []  # growing workloads: per-step event pairs of append and of each p's route + attend
+        segs = []  # per-step event pairs: the step (fixed-size workloads) or append and each p's route + attend
 
         def seg(name, fn, record):
             if record:
@@ -337,11 +389,11 @@ def main():
         tmask = {}  # growing workloads: kernel timing mask, applied to the headline p's launches only
 
         def step(i, record=False):
-            li, t = i % args.layers, i % nq
+            li, t = (0, 0) if warm else (i % layers, i % nq)
             tr = trees[li]
+            if record:
+                segs.append({})
             if growing:
-                if record:
-                    segs.append({})
                 if layer_lens[li][0] < T:
                     layer_lens[li] = [n + 1 for n in layer_lens[li]]
                     if tmask:  # the append is timed in the breakdown pass only
@@ -355,8 +407,8 @@ def main():
                 if tmask:
                     tr.timing(False)
                 return
-            tr.route(qd[t], p, 1.0, mode=mode)
-            tr.attend(qd[t], Ks[li], Vs[li], 1.0, out=outs[li], lse=lses[li])
+            seg("step", lambda: (tr.route(qd[t], p, 1.0, mode=mode),
+                                 tr.attend(qd[t], Ks[li], Vs[li], 1.0, out=outs[li], lse=lses[li])), record)
 
         for i in range(args.warmup):
             step(i)
@@ -378,7 +430,8 @@ def main():
         kernels = kernel_table(recs)
         dom_name, dom = max(kernels.items(), key=lambda kv: kv[1]["total_ms"])
 
-        # timed region: K steps, with an event pair around the dominant kernel only
+        # timed region: K steps, with an event pair around the dominant kernel only, and one
+        # around each step (for the median and 90th percentile)
         for tr in trees:
             tr.timing(True, kernels=[dom["code"]], levels=[dom["level"]])
         if growing:
@@ -386,22 +439,27 @@ def main():
         torch.cuda.synchronize()
         ev0.record()
         for i in range(args.steps):
-            step(i, record=growing)
+            step(i, record=True)
         ev1.record()
         torch.cuda.synchronize()
         ms_total = ev0.elapsed_time(ev1)
         ms_step = ms_total / args.steps
         seg_us = {}
-        if growing:
-            for sg in segs:
-                for k, (a, b) in sg.items():
-                    seg_us.setdefault(k, []).append(1e3 * a.elapsed_time(b))
-            seg_us = {k: sum(v) / len(v) for k, v in seg_us.items()}
-            ms_step = (seg_us.get("append", 0.0) + seg_us[p]) * 1e-3  # append + route + attend at p
+        for sg in segs:
+            for k, (a, b) in sg.items():
+                seg_us.setdefault(k, []).append(1e3 * a.elapsed_time(b))
+        if growing:  # a step: its append (if the layer had room) + route + attend at p
+            per_step = [1e3 * sum(sg[k][0].elapsed_time(sg[k][1]) for k in ("append", p) if k in sg) for sg in segs]
+            seg_mean = {k: sum(v) / len(v) for k, v in seg_us.items()}
+            ms_step = (seg_mean.get("append", 0.0) + seg_mean[p]) * 1e-3  # append + route + attend at p
+        else:
+            per_step = seg_us["step"]
+            seg_mean = {}
         live = []
         for tr in trees:
             live += [ms for _, _, ms in tr.timing_read()]
             tr.timing(False)
+            tr.check()  # no device-side wait of a route gave up
         dom_live_us = 1e3 * sum(live) / len(live)
 
         # algorithmic bytes of each step (routes are deterministic: replay each query once, untimed)
@@ -412,7 +470,7 @@ def main():
         fr_unit = {l: 0 for l in range(1, L + 1)}  # frontier nodes summed over routing units
         kept_tot = {l: 0 for l in range(1, L + 1)}
         attend_tok = 0
-        steps_q = [i % nq for i in range(args.steps)]
+        steps_q = [0 if warm else i % nq for i in range(args.steps)]
         for t in sorted(set(steps_q)):
             w = steps_q.count(t)
             trees[0].route(qd[t], p, 1.0, mode=mode)
@@ -439,7 +497,7 @@ def main():
             l = dom["level"]
             dom_bytes = (fr_tot[l] * S_node + fr_unit[l] * Gr * 4 + (fr_unit[l] / C * 4 if l < L else 0)) / nsteps \
                 + B * Hq * d * es
-            traffic = committed_traffic(args.config) if l == 1 and summary == "native" and mode == "group" else None
+            traffic = committed_traffic(cfg.name) if l == 1 and summary == "native" and mode == "group" else None
         elif dom_name == "attend":
             dom_bytes = attend_bytes + B * Hq * d * es
             traffic = None
@@ -454,10 +512,10 @@ def main():
                         frac=round(achieved / PEAK_HBM_GBS, 4) if achieved else None,
                         traffic=traffic, bytes_per_launch=round(dom_bytes) if dom_bytes else None,
                         avg_launch_us=round(dom_live_us, 2))
-        log(f"step {ms_step * 1e3:.1f} us, {step_bytes / 1e6:.1f} MB/step ({step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s), "
-            f"kappa {kappa:.3f}")
+        log(f"step {ms_step * 1e3:.1f} us (median {pct(per_step, 50):.1f}, p90 {pct(per_step, 90):.1f}), "
+            f"{step_bytes / 1e6:.1f} MB/step ({step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s), kappa {kappa:.3f}")
         if growing:
-            log("  segments (us): " + ", ".join(f"{k}: {v:.1f}" for k, v in seg_us.items()))
+            log("  segments (us): " + ", ".join(f"{k}: {v:.1f}" for k, v in seg_mean.items()))
         for k, v in kernels.items():
             log(f"  {k:12s} {v['launches']:4d} launches  avg {v['avg_us']:8.2f} us")
 
@@ -465,92 +523,183 @@ def main():
             tr.close()
         torch.cuda.empty_cache()
         return dict(ms_step=ms_step, step_bytes=step_bytes, kappa=kappa, kernels=kernels, roofline=roofline,
-                    seg_us=seg_us, fr_tot=fr_tot, build_ms=build_ms, tree_bytes=tree_bytes, layer_lens=layer_lens,
-                    dense_bytes=dense_bytes, nsteps=nsteps)
+                    seg_us=seg_mean, fr_tot=fr_tot, build_ms=build_ms, tree_bytes=tree_bytes, layer_lens=layer_lens,
+                    dense_bytes=dense_bytes, nsteps=nsteps, median_us=pct(per_step, 50), p90_us=pct(per_step, 90))
 
-    res = measure(args.summary)
+    summary = args.summary if headline else "native"
+    log(f"== {cfg.name}: B={B} N={N} {Hq}q/{Hkv}kv d={d} C={C} L={L} R={R} p={p_sweep} ({layers} layer replicas)")
+    res = measure(summary)
     ms_step, step_bytes, kappa, kernels = res["ms_step"], res["step_bytes"], res["kappa"], res["kernels"]
-    roofline, seg_us, fr_tot, build_ms = res["roofline"], res["seg_us"], res["fr_tot"], res["build_ms"]
     layer_lens, dense_bytes, nsteps = res["layer_lens"], res["dense_bytes"], res["nsteps"]
-    low = {}  # the same workload with low-precision summaries
-    if not args.no_fp8 and args.summary == "native" and cfg.dtype == "bf16":
-        for sm in ("fp8", "fp4"):
-            log(f"-- the same workload with {sm} summaries")
-            r8 = measure(sm)
-            low[sm] = dict(us_per_step=round(r8["ms_step"] * 1e3, 2), step_bytes=round(r8["step_bytes"]),
-                           step_gbs=round(r8["step_bytes"] / (r8["ms_step"] * 1e-3) / 1e9, 1),
-                           kappa=round(r8["kappa"], 4), roofline=r8["roofline"],
-                           build_us=round(1e3 * float(np.median(r8["build_ms"])), 1), tree_bytes=r8["tree_bytes"],
-                           kernels={k: round(v["avg_us"], 2) for k, v in r8["kernels"].items()})
-            if growing:
-                low[sm]["p_sweep"] = {str(x): round(r8["seg_us"].get("append", 0.0) + r8["seg_us"][x], 2)
-                                      for x in p_sweep}
-    sweep = None
-    if args.sweep and not growing:
-        sweep = geometry_sweep(measure, cfg, zi, torch, np, dev, N, B, Hkv, d, es, log)
-    per_head = None
-    if not args.no_per_head and args.summary == "native":
-        log("-- the same workload, every query head routed alone")
-        rh = measure("native", mode="per_head")
-        per_head = dict(us_per_step=round(rh["ms_step"] * 1e3, 2), step_bytes=round(rh["step_bytes"]),
-                        step_gbs=round(rh["step_bytes"] / (rh["ms_step"] * 1e-3) / 1e9, 1),
-                        kappa=round(rh["kappa"], 4), roofline=rh["roofline"],
-                        kernels={k: round(v["avg_us"], 2) for k, v in rh["kernels"].items()})
-        if growing:
-            per_head["p_sweep"] = {str(x): round(rh["seg_us"].get("append", 0.0) + rh["seg_us"][x], 2) for x in p_sweep}
+    rec = {
+        "us_per_step": round(ms_step * 1e3, 2),
+        "median_us": round(res["median_us"], 2),
+        "p90_us": round(res["p90_us"], 2),
+        "roofline": res["roofline"],
+        "step_bytes": round(step_bytes),
+        "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "step_frac_of_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "dense_bytes": dense_bytes,
+        "kappa": round(kappa, 4),
+        "frontier_per_unit": {l: round(res["fr_tot"][l] / nsteps / U, 1) for l in range(L, 0, -1)},
+        "build_us": round(1e3 * float(np.median(res["build_ms"])), 1),
+        "tree_bytes": res["tree_bytes"],
+        "kernels": {k: dict(launches=v["launches"], avg_us=round(v["avg_us"], 2)) for k, v in kernels.items()},
+        "config": {"workload": cfg.name, "batch": B, "context": N, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "chunk": C, "levels": L, "refs": R, "p": p, "layers_cycled": layers, "summary": summary},
+    }
+    if growing:
+        rec["append_us"] = round(res["seg_us"].get("append", 0.0), 2)
+        rec["p_sweep"] = {str(x): round(res["seg_us"].get("append", 0.0) + res["seg_us"][x], 2) for x in p_sweep}
+        rec["config"]["appended_per_step"] = 1
 
-    block = None
-    if args.block > 0 and args.summary == "native":
-        log(f"-- blocks of {args.block} queries per sequence, each routed alone")
-        block = measure_block(args.block)
+    if headline:
+        log("-- warm: every step on the same layer and query")
+        rw = measure(summary, warm=True)
+        rec["warm_us_per_step"] = round(rw["ms_step"] * 1e3, 2)
+        low = {}  # the same workload with low-precision summaries
+        if not args.no_fp8 and args.summary == "native" and cfg.dtype == "bf16":
+            for sm in ("fp8", "fp4"):
+                log(f"-- the same workload with {sm} summaries")
+                r8 = measure(sm)
+                low[sm] = dict(us_per_step=round(r8["ms_step"] * 1e3, 2), median_us=round(r8["median_us"], 2),
+                               step_bytes=round(r8["step_bytes"]),
+                               step_gbs=round(r8["step_bytes"] / (r8["ms_step"] * 1e-3) / 1e9, 1),
+                               kappa=round(r8["kappa"], 4), roofline=r8["roofline"],
+                               build_us=round(1e3 * float(np.median(r8["build_ms"])), 1), tree_bytes=r8["tree_bytes"],
+                               kernels={k: round(v["avg_us"], 2) for k, v in r8["kernels"].items()})
+                if growing:
+                    low[sm]["p_sweep"] = {str(x): round(r8["seg_us"].get("append", 0.0) + r8["seg_us"][x], 2)
+                                          for x in p_sweep}
+        for sm, v in low.items():
+            rec[f"{sm}_summaries"] = v
+        if args.sweep and not growing:
+            rec["geometry_sweep"] = geometry_sweep(measure, cfg, zi, torch, np, dev, N, B, Hkv, d, es, log)
+        if not args.no_per_head and args.summary == "native":
+            log("-- the same workload, every query head routed alone")
+            rh = measure("native", mode="per_head")
+            rec["per_head_routes"] = dict(us_per_step=round(rh["ms_step"] * 1e3, 2), step_bytes=round(rh["step_bytes"]),
+                                          step_gbs=round(rh["step_bytes"] / (rh["ms_step"] * 1e-3) / 1e9, 1),
+                                          kappa=round(rh["kappa"], 4), roofline=rh["roofline"],
+                                          kernels={k: round(v["avg_us"], 2) for k, v in rh["kernels"].items()})
+            if growing:
+                rec["per_head_routes"]["p_sweep"] = {str(x): round(rh["seg_us"].get("append", 0.0) + rh["seg_us"][x], 2)
+                                                     for x in p_sweep}
+        if args.block > 0 and args.summary == "native":
+            log(f"-- blocks of {args.block} queries per sequence, each routed alone")
+            rec["query_block"] = measure_block(args.block)
 
     # dense decode on the same GPU and inputs, same protocol
-    dense_us = None
     if not args.no_dense:
         nb = zha.zha_dense_workspace_bytes(B, Hq, Hkv, d, T)
         ws = torch.empty(nb, dtype=torch.uint8, device=dev)
         for i in range(args.warmup):
-            li = i % args.layers
+            li = i % layers
             dense_decode(qd[i % nq], Ks[li], Vs[li], layer_lens[li], Hkv, 1.0, ws, outs[li], lses[li])
         torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
         ev0.record()
         for i in range(args.steps):
-            li = i % args.layers
+            li = i % layers
+            evs[i][0].record()
             dense_decode(qd[i % nq], Ks[li], Vs[li], layer_lens[li], Hkv, 1.0, ws, outs[li], lses[li])
+            evs[i][1].record()
         ev1.record()
         torch.cuda.synchronize()
         dense_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
-        log(f"dense {dense_us:.1f} us/step ({dense_bytes / (dense_us * 1e-6) / 1e9:.0f} GB/s)")
+        dense_med = pct([1e3 * a.elapsed_time(b) for a, b in evs], 50)
+        log(f"dense {dense_us:.1f} us/step (median {dense_med:.1f}; {dense_bytes / (dense_us * 1e-6) / 1e9:.0f} GB/s)")
+        rec["dense_us_per_step"] = round(dense_us, 2)
+        rec["dense_median_us"] = round(dense_med, 2)
+        rec["speedup_vs_dense"] = round(dense_us / (ms_step * 1e3), 3)
+    del Ks, Vs, outs, lses
+    torch.cuda.empty_cache()
+    return rec
 
-    # the oracle on the host cores, on a bounded sample: the decode queries of two (sequence,
-    # KV head) units (about 10-20 s of host work), scaled to a whole step
-    cpu = None
-    if not args.no_cpu:
-        import oracle
-        ncpu = min(args.cpu_queries, cfg.n_queries)
-        qc = zi.queries(cfg, n=ncpu)
-        units = [(0, g) for g in range(min(2, Hkv))]
-        sec = 0.0
-        for (b0, g0) in units:
-            Ku, Vu = zi.unit_kv(cfg, b0, g0, q_all)
-            tree_o = oracle.tree_merge(Ku, zi.refs(cfg)[g0], C, L)  # untimed
-            tc0 = time.time()
-            for t in range(ncpu):
+
+def cpu_baseline(cfg, args, env):
+    """The oracle on the host cores, on a bounded sample: the decode queries of two (sequence,
+    KV head) units (about 10-20 s of host work), scaled to a whole step; then the same on one
+    thread for a few queries of one unit."""
+    np, zi = env["np"], env["zi"]
+    import oracle
+    p = args.p if args.p is not None else cfg.p[0]
+    B, Hkv, N, C, L, G = cfg.batch, cfg.n_kv_heads, cfg.n_tokens, cfg.chunk, cfg.levels, cfg.group
+    U = B * Hkv
+    ncpu = min(args.cpu_queries, cfg.n_queries)
+    qc = zi.queries(cfg, n=ncpu)
+    q_all = env["inputs"].get("q_all") if env["inputs"].get("key") == input_key(cfg) else None
+    units = [(0, g) for g in range(min(2, Hkv))]
+    trees, kv = {}, {}
+    for (b0, g0) in units:
+        Ku, Vu = zi.unit_kv(cfg, b0, g0, q_all)
+        kv[(b0, g0)] = (Ku.astype(np.float64), Vu.astype(np.float64))
+        trees[(b0, g0)] = oracle.tree_merge(Ku, zi.refs(cfg)[g0], C, L)  # untimed
+
+    def run(pairs, nqq):
+        t0 = time.time()
+        for (b0, g0) in pairs:
+            Ku, Vu = kv[(b0, g0)]
+            for t in range(nqq):
                 qu = qc[t, b0, g0 * G:(g0 + 1) * G].astype(np.float64)
-                _, kept = oracle.route(tree_o, N, C, L, qu, p)
+                _, kept = oracle.route(trees[(b0, g0)], N, C, L, qu, p)
                 S = oracle.attend_set(N, C, kept[1])
                 oracle.attend(qu, Ku, Vu, S)
-            sec += time.time() - tc0
-        per_unit_step = sec / (ncpu * len(units))
-        cpu = dict(value=round(per_unit_step * U * 1e6, 1), unit="us/step/layer", cores=oracle.num_threads(),
-                   kind="oracle",
-                   sample=f"route+attend of {len(units)} (sequence, KV head) units for {ncpu} decode queries each "
-                          f"({sec:.1f} s), scaled by {U} units to one full step; oracle trees built untimed")
-        log(f"cpu oracle {cpu['value']:.0f} us/step on {cpu['cores']} threads")
+        return time.time() - t0
 
+    threads = oracle.num_threads()
+    sec = run(units, ncpu)
+    per_unit_step = sec / (ncpu * len(units))
+    n1 = min(4, ncpu)
+    oracle.set_num_threads(1)
+    try:
+        sec1 = run(units[:1], n1)
+    finally:
+        oracle.set_num_threads(threads)
+    one = dict(value=round(sec1 / n1 * U * 1e6, 1), unit="us/step/layer", cores=1,
+               sample=f"route+attend of 1 unit for {n1} decode queries ({sec1:.1f} s), scaled by {U} units")
+    cpu = dict(value=round(per_unit_step * U * 1e6, 1), unit="us/step/layer", cores=threads, kind="oracle",
+               cpu_model=cpu_model(),
+               sample=f"route+attend of {len(units)} (sequence, KV head) units for {ncpu} decode queries each "
+                      f"({sec:.1f} s), scaled by {U} units to one full step; oracle trees built untimed",
+               single_thread=one)
+    log(f"cpu oracle {cpu['value']:.0f} us/step on {threads} threads, {one['value']:.0f} us/step on 1 thread "
+        f"({cpu['cpu_model']})")
+    return cpu
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: the library runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path would shard by (sequence, KV head), with no exchange between GPUs", flush=True)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import zha_inputs as zi
+    from hierarchical_tree_indexed_02_amd import zha
+    from hierarchical_tree_indexed_02_amd.runtime import Tree, dense_decode
+
+    env = dict(np=np, torch=torch, zi=zi, zha=zha, Tree=Tree, dense=dense_decode, dev=torch.device("cuda:0"),
+               inputs={})
+    t_start = time.time()
+    cfg = zi.get_config(args.config)
+    head = run_workload(cfg, args, env, headline=True, layers=args.layers)
+    subs = {}
+    for name in [w for w in args.workloads.split(",") if w and w != cfg.name]:
+        subs[name] = run_workload(zi.get_config(name), args, env, headline=False,
+                                  layers=SUB_LAYERS.get(name, args.layers))
+        log(f"[{name}] {subs[name]['us_per_step']} us/step (dense {subs[name].get('dense_us_per_step')}); "
+            f"{time.time() - t_start:.0f} s so far")
+    env["inputs"].clear()
+    torch.cuda.empty_cache()
+    cpu = None if args.no_cpu else cpu_baseline(cfg, args, env)
+
+    ms_step = head["us_per_step"] * 1e-3
     result = {
         "metric": METRIC,
-        "value": round(ms_step * 1e3, 2),
+        "value": head["us_per_step"],
         "unit": "us/step/layer",
         "n_gpus": 1,
         "steps": args.steps,
@@ -561,34 +710,15 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded planted-needle keys/values, random reference queries)",
-        "config": {"workload": cfg.name, "batch": B, "context": N, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
-                   "chunk": C, "levels": L, "refs": R, "p": p, "layers_cycled": args.layers},
-        "roofline": roofline,
+        "config": head.pop("config"),
+        "roofline": head.pop("roofline"),
         "cpu_baseline": cpu,
-        "dense_us_per_step": round(dense_us, 2) if dense_us else None,
-        "speedup_vs_dense": round(dense_us / (ms_step * 1e3), 3) if dense_us else None,
-        "step_bytes": round(step_bytes),
-        "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
-        "step_frac_of_peak": round(step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "dense_bytes": dense_bytes,
-        "kappa": round(kappa, 4),
-        "frontier_per_unit": {l: round(fr_tot[l] / nsteps / U, 1) for l in range(L, 0, -1)},
-        "build_us": round(1e3 * float(np.median(build_ms)), 1),
-        "kernels": {k: dict(launches=v["launches"], avg_us=round(v["avg_us"], 2)) for k, v in kernels.items()},
     }
-    result["config"]["summary"] = args.summary
-    for sm, v in low.items():
-        result[f"{sm}_summaries"] = v
-    if per_head is not None:
-        result["per_head_routes"] = per_head
-    if sweep is not None:
-        result["geometry_sweep"] = sweep
-    if block is not None:
-        result["query_block"] = block
-    if growing:
-        result["append_us"] = round(seg_us.get("append", 0.0), 2)
-        result["p_sweep"] = {str(x): round(seg_us.get("append", 0.0) + seg_us[x], 2) for x in p_sweep}
-        result["config"]["appended_per_step"] = 1
+    head.pop("us_per_step")
+    result.update(head)
+    if subs:
+        result["workloads"] = subs
+    result["bench_wall_s"] = round(time.time() - t_start, 1)
     print(json.dumps(result), flush=True)
 
 

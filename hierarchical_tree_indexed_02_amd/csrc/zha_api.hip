@@ -144,6 +144,7 @@ const char* zha_status_str(zha_status s) {
     case ZHA_ERR_NOMEM: return "out of memory";
     case ZHA_ERR_UNSUPPORTED: return "unsupported shape";
     case ZHA_ERR_HIP: return "HIP runtime error";
+    case ZHA_ERR_DEVICE: return "a device-side wait gave up; the routes since the last check are not valid";
   }
   return "unknown status";
 }
@@ -283,6 +284,8 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
       ok = hipMemset(t->krank[l], 0, (size_t)RUmax * t->cap[l] * sizeof(unsigned long long)) == hipSuccess;
     if (uni) ok = ok && hipMemset(t->route_ctr, 0, sizeof(uint32_t)) == hipSuccess;
     if (uni) ok = ok && hipMemset(t->uflag, 0, (size_t)ugmax * t->kstride * sizeof(uint32_t)) == hipSuccess;
+    // union lists start as chunk 0 everywhere, so no entry is ever read before it is written
+    if (uni) ok = ok && hipMemset(t->ulist, 0, (size_t)ugmax * t->cap[1] * sizeof(int32_t)) == hipSuccess;
     // every unit's epoch starts at 1: status words of epoch 0 (all-zero memory) never match
     std::vector<uint32_t> ep((size_t)RUmax * 2, 0u);
     for (int u = 0; u < RUmax; ++u) ep[(size_t)u * 2] = 1u;
@@ -317,6 +320,7 @@ zha_status zha_build(zha_tree_t t, const void* K, const float* refs, const int32
   e = zha_launch_build(t, K, s);
   if (e != hipSuccess) return hip_fail("zha_build launch", e);
   t->built = true;
+  ++t->gen;
   return ZHA_OK;
 }
 
@@ -329,6 +333,7 @@ zha_status zha_append(zha_tree_t t, const void* K, const int32_t* new_seq_lens, 
     if (new_seq_lens[b] < t->len.n[b]) return ZHA_ERR_INVALID;
   t->len_prev = t->len;
   for (int b = 0; b < t->desc.batch; ++b) t->len.n[b] = new_seq_lens[b];
+  ++t->gen;  // the lengths changed: the last route's kept lists are stale from here on
   hipError_t e = zha_launch_append(t, K, s);
   if (e != hipSuccess) return hip_fail("zha_append launch", e);
   return ZHA_OK;
@@ -351,6 +356,7 @@ static zha_status route_queries(zha_tree* t, const void* q, int Tq, bool multi, 
   t->RU = t->U * Tq * t->hr;
   t->WS = zha_score_wgs_units(t->RU);
   t->WA = zha_sparse_wgs(t->RU);
+  t->route_gen = t->gen;
   hipError_t e = zha_launch_route(t, q, p, scale, s);
   if (e != hipSuccess) return hip_fail("zha_route launch", e);
   kept->counts = t->counts + (int64_t)(t->L + 2) * t->RU + t->RU;
@@ -378,6 +384,7 @@ zha_status zha_attend(zha_tree_t t, const void* q, const void* K, const void* V,
   if (!t || !q || !K || !V || !kept || !out || !lse) return ZHA_ERR_INVALID;
   if (!t->built) return ZHA_ERR_INVALID;
   if (kept->ids != t->kept[1]) return ZHA_ERR_INVALID;  // a view of this tree's last route
+  if (t->route_gen != t->gen) return ZHA_ERR_INVALID;   // built or appended to since that route
   if (t->multi) return ZHA_ERR_INVALID;                 // a block of queries: zha_attend_multi
   if (!isfinite(scale)) return ZHA_ERR_INVALID;
   hipError_t e = zha_launch_attend(t, q, K, V, scale, out, lse, s);
@@ -390,6 +397,7 @@ zha_status zha_attend_multi(zha_tree_t t, const void* q, int32_t n_queries, cons
   if (!t || !q || !K || !V || !kept || !out || !lse) return ZHA_ERR_INVALID;
   if (!t->built) return ZHA_ERR_INVALID;
   if (kept->ids != t->kept[1]) return ZHA_ERR_INVALID;
+  if (t->route_gen != t->gen) return ZHA_ERR_INVALID;           // built or appended to since that route
   if (!t->multi || n_queries != t->Tq) return ZHA_ERR_INVALID;  // the last route carried this block
   if (!isfinite(scale)) return ZHA_ERR_INVALID;
   for (int b = 0; b < t->desc.batch; ++b)  // the block's rows N .. N + Tq - 1 lie inside K and V
@@ -397,6 +405,21 @@ zha_status zha_attend_multi(zha_tree_t t, const void* q, int32_t n_queries, cons
   hipError_t e = zha_launch_attend(t, q, K, V, scale, out, lse, s);
   if (e != hipSuccess) return hip_fail("zha_attend_multi launch", e);
   return ZHA_OK;
+}
+
+zha_status zha_tree_check(zha_tree_t t, hipStream_t s) {
+  if (!t) return ZHA_ERR_INVALID;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail("zha_tree_check synchronize", e);
+  int32_t flag = 0;
+  e = hipMemcpy(&flag, t->lb_error, sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail("zha_tree_check read", e);
+  if (flag == 0) return ZHA_OK;
+  e = hipMemset(t->lb_error, 0, sizeof(int32_t));
+  if (e != hipSuccess) return hip_fail("zha_tree_check clear", e);
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail("zha_tree_check clear", e);
+  return ZHA_ERR_DEVICE;
 }
 
 size_t zha_dense_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,

@@ -568,15 +568,21 @@ __global__ __launch_bounds__(256, 2) void zha_attend_union_lds_kernel(AttArgs a)
   const int start = blockIdx.x * TOK;
   const int gstep = a.W * TOK;
   // Chunk ids of the stage at ps: lane j holds the j-th kept chunk its positions touch, read
-  // from a clamped (always readable) index, so the stage's tokens cost one load that no
-  // branch guards (a guarded load makes the compiler wait for every load in flight).
+  // from a clamped index, so the stage's tokens cost one load that no branch guards (a
+  // guarded load makes the compiler wait for every load in flight).  The clamped entry lies
+  // inside the group's list row whatever the count; a group with an empty list (a sequence
+  // without a complete chunk) has no written entry there, so its ids are taken as chunk 0,
+  // whose rank entry is always readable (only positions of the chunk part use them).
   static_assert(TOK / 2 + 2 <= 64, "a stage touches at most 64 chunks (C >= 2)");
   const int nidx = max(P.nK - 1, 0);
   auto first_chunk = [&](int ps) {
     const int q = ps - P.nx;
     return q <= 0 ? 0 : (a.Cshift >= 0 ? (q >> a.Cshift) : q / a.C);
   };
-  auto stage_ids = [&](int ps) -> int { return P.kp[min(first_chunk(ps) + lane, nidx)]; };
+  auto stage_ids = [&](int ps) -> int {
+    const int x = P.kp[min(first_chunk(ps) + lane, nidx)];
+    return P.nK > 0 ? x : 0;
+  };
   // token of position p of the stage at ps (positions at or past the end: token 0); every
   // lane calls this together (it shuffles)
   auto stage_token = [&](int ids, int ps, int p) -> int {
@@ -612,7 +618,7 @@ __global__ __launch_bounds__(256, 2) void zha_attend_union_lds_kernel(AttArgs a)
   // lane's column unit (0 outside the chunk part).  A lane's four consecutive positions lie in
   // at most three consecutive kept chunks (two when C >= 3), so three stamps are loaded per
   // group of four, straight from the chunk ids (a stamp needs no token); the loads are
-  // unconditional (clamped list entries are kept chunks, so always readable).
+  // unconditional (every id is a listed chunk, or chunk 0 for an empty list: readable).
   auto fetch_rank = [&](int ps, int ids, uint32_t (&rk)[2][4]) {
     const int cb = first_chunk(ps);
     auto lidx = [&](int q) { return q > 0 ? (a.Cshift >= 0 ? (q >> a.Cshift) : q / a.C) : 0; };

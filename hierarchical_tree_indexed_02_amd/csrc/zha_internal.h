@@ -203,8 +203,9 @@ __device__ __forceinline__ int union_group(int u, int hr, int Hkv, int Tq, int T
 #define ZHA_MAX_TIMING 256
 #define ZHA_MAX_BATCH 64
 
-// Sequence lengths travel by value in every kernel's arguments (no device copy,
-// so a sequence of calls can be captured into a graph).
+// Sequence lengths by value: the build, append and dense-decode launches take them in
+// their arguments; routing and sparse attention read them from the tree's device geometry
+// table instead (written by the build and append kernels), which keeps their arguments small.
 struct ZLens {
   int32_t n[ZHA_MAX_BATCH];
 };
@@ -263,6 +264,8 @@ struct zha_tree {
   ZLens len;                        // current lengths
   ZLens len_prev;                   // lengths before the last zha_append
   bool built;
+  uint64_t gen;                     // advanced by every zha_build and zha_append
+  uint64_t route_gen;               // gen when the last route ran (attention needs it current)
   int64_t bytes;
   // timing
   int32_t timing_kernels;           // bit k: time launches of kernel code k (0: timing off)

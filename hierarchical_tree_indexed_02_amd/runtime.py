@@ -58,6 +58,10 @@ class Tree:
     def bytes(self) -> int:
         return zha.zha_tree_bytes(self.h)
 
+    def check(self, stream=None):
+        """Synchronises and raises if a device-side bounded wait of a route gave up."""
+        zha.zha_tree_check(self.h, stream)
+
     def build(self, K, refs, seq_lens, stream=None):
         zha.zha_build(self.h, K, refs, seq_lens, stream)
 

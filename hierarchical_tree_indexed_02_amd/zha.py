@@ -15,7 +15,7 @@ from ctypes import POINTER, Structure, c_char_p, c_float, c_int, c_int32, c_int6
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libzha.so")
 
-ZHA_OK, ZHA_ERR_INVALID, ZHA_ERR_CAPACITY, ZHA_ERR_NOMEM, ZHA_ERR_UNSUPPORTED, ZHA_ERR_HIP = range(6)
+ZHA_OK, ZHA_ERR_INVALID, ZHA_ERR_CAPACITY, ZHA_ERR_NOMEM, ZHA_ERR_UNSUPPORTED, ZHA_ERR_HIP, ZHA_ERR_DEVICE = range(7)
 ZHA_F32, ZHA_BF16 = 0, 1
 ZHA_SUMMARY_NATIVE, ZHA_SUMMARY_FP8, ZHA_SUMMARY_FP4 = 0, 1, 2
 ZHA_ROUTE_GROUP, ZHA_ROUTE_PER_HEAD = 0, 1
@@ -65,6 +65,7 @@ def load():
             "zha_tree_create": (st, [POINTER(zha_tree_desc), POINTER(c_void_p)]),
             "zha_tree_destroy": (None, [vp]),
             "zha_tree_bytes": (st, [vp, POINTER(c_int64)]),
+            "zha_tree_check": (st, [vp, vp]),
             "zha_build": (st, [vp, vp, vp, _i32p, vp]),
             "zha_append": (st, [vp, vp, _i32p, vp]),
             "zha_route": (st, [vp, vp, c_float, c_float, POINTER(zha_kept), vp]),
@@ -140,6 +141,12 @@ def zha_tree_bytes(tree: int) -> int:
     v = c_int64()
     _check(load().zha_tree_bytes(tree, ctypes.byref(v)), "zha_tree_bytes")
     return v.value
+
+
+def zha_tree_check(tree: int, stream=None) -> None:
+    """Synchronises the stream and raises ZhaError(ZHA_ERR_DEVICE) if a device-side bounded
+    wait of the tree's routes gave up since the last check (the mark is cleared)."""
+    _check(load().zha_tree_check(tree, _stream(stream)), "zha_tree_check")
 
 
 def zha_build(tree: int, K, refs, seq_lens, stream=None) -> None:

@@ -61,7 +61,8 @@ typedef enum {
     ZHA_ERR_CAPACITY = 2,     /* a length exceeds the tree's max_tokens */
     ZHA_ERR_NOMEM = 3,        /* device or host allocation failed */
     ZHA_ERR_UNSUPPORTED = 4,  /* a shape the library does not implement */
-    ZHA_ERR_HIP = 5           /* a HIP runtime call failed */
+    ZHA_ERR_HIP = 5,          /* a HIP runtime call failed */
+    ZHA_ERR_DEVICE = 6        /* a device-side bounded wait gave up (see zha_tree_check) */
 } zha_status;
 
 typedef enum { ZHA_F32 = 0, ZHA_BF16 = 1 } zha_dtype;
@@ -209,6 +210,16 @@ ZHA_API zha_status zha_route_ex(zha_tree_t tree, const void* q, float p, float s
 ZHA_API zha_status zha_route_multi(zha_tree_t tree, const void* q, int32_t n_queries, float p, float scale,
                            zha_route_mode mode, zha_kept* kept, hipStream_t stream);
 
+/* Device-side health of a tree.  The ordered compaction of a large level chains
+ * its workgroups' kept counts with a decoupled look-back whose waits are bounded;
+ * a wait that gives up (never expected: every workgroup it waits on has been
+ * dispatched before it) marks the tree, and the kept lists of that route are then
+ * not valid.  zha_tree_check synchronises the stream (unlike every other entry
+ * point), reads the mark and clears it: ZHA_OK when no wait has given up since
+ * the tree was created or last checked, ZHA_ERR_DEVICE otherwise.
+ * Errors: ZHA_ERR_INVALID (null tree), ZHA_ERR_HIP. */
+ZHA_API zha_status zha_tree_check(zha_tree_t tree, hipStream_t stream);
+
 /* Exact attention of each query head over S = {token 0} U (tokens of the
  * kept chunks) U [Nc, N), S a set ([wqu] "How does top-p routing pick
  * tokens?": the first token is always kept; the trailing partial chunk is not
@@ -216,7 +227,8 @@ ZHA_API zha_status zha_route_multi(zha_tree_t tree, const void* q, int32_t n_que
  * q_h.k_t) v_t and lse_h = log sum_{t in S} exp(scale * q_h.k_t), computed
  * in float32 from the stored K and V.  kept: the view returned by zha_route
  * on this tree.  Errors: ZHA_ERR_INVALID (also when the last route was a
- * zha_route_multi), ZHA_ERR_HIP. */
+ * zha_route_multi, or when zha_build or zha_append changed the tree after the
+ * last route: the kept list no longer describes the cache), ZHA_ERR_HIP. */
 ZHA_API zha_status zha_attend(zha_tree_t tree, const void* q, const void* K, const void* V,
                       const zha_kept* kept, float scale, float* out, float* lse,
                       hipStream_t stream);
@@ -228,8 +240,9 @@ ZHA_API zha_status zha_attend(zha_tree_t tree, const void* q, const void* K, con
  * block's keys and values (written there by the caller; zha_append adds them
  * to the tree afterwards).  q: [B][Tq][Hq][d]; out: [B][Tq][Hq][d] float32;
  * lse: [B][Tq][Hq] float32; same formulas as zha_attend.
- * Errors: ZHA_ERR_INVALID (kept is not the view of this tree's last route, or
- * that route was not a zha_route_multi of n_queries queries), ZHA_ERR_CAPACITY
+ * Errors: ZHA_ERR_INVALID (kept is not the view of this tree's last route, that
+ * route was not a zha_route_multi of n_queries queries, or the tree was built or
+ * appended to after it), ZHA_ERR_CAPACITY
  * (N_b + n_queries > max_tokens for some b), ZHA_ERR_HIP. */
 ZHA_API zha_status zha_attend_multi(zha_tree_t tree, const void* q, int32_t n_queries, const void* K,
                             const void* V, const zha_kept* kept, float scale, float* out, float* lse,

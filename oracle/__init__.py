@@ -75,6 +75,9 @@ def _bind(path: str):
     L.zo_e2m1_block_exp.argtypes = [ctypes.c_double]
     L.zo_fp4_rows.restype = None
     L.zo_fp4_rows.argtypes = [_f64p, _i64, _int, _f64p, _f64p]
+    for fn in (L.zo_fp8_planes, L.zo_fp4_planes):
+        fn.restype = None
+        fn.argtypes = [_f64p, _f64p, _f64p, _i64, _int, _int, _f64p, _f64p, _f64p]
     L.zo_num_threads.restype = _int
     L.zo_num_threads.argtypes = []
     L.zo_set_num_threads.restype = None
@@ -160,11 +163,19 @@ def fp8_rows(m):
     return out.reshape(shp), sc.reshape(shp[:-1])
 
 
-def fp8_planes(m, lse, refs):
-    """Planes with fp8-stored means: (m~ [n][R][d], b~ = LSE - r.m~ [n][R], scale [n][R])."""
-    mq, sc = fp8_rows(m)
-    b = _f64(lse) - np.einsum("nrd,rd->nr", mq, _f64(refs))
+def _lowp_planes(fn, m, lse, refs, scale_shape):
+    m, lse, refs = _f64(m), _f64(lse), _f64(refs)
+    n, R, d = m.shape
+    mq = np.empty_like(m); b = np.empty((n, R)); sc = np.empty(scale_shape)
+    fn(_p(m, _f64p), _p(lse, _f64p), _p(refs, _f64p), n, R, d, _p(mq, _f64p), _p(b, _f64p), _p(sc, _f64p))
     return mq, b, sc
+
+
+def fp8_planes(m, lse, refs):
+    """Planes with fp8-stored means (zo_fp8_planes): (m~ [n][R][d], b~ = LSE - r.m~ [n][R],
+    scale [n][R])."""
+    m = _f64(m)
+    return _lowp_planes(lib().zo_fp8_planes, m, lse, refs, m.shape[:2])
 
 
 def e2m1_round(x: float) -> float:
@@ -190,10 +201,10 @@ def fp4_rows(m):
 
 
 def fp4_planes(m, lse, refs):
-    """Planes with fp4-stored means: (m~ [n][R][d], b~ = LSE - r.m~ [n][R], scales [n][R][d/32])."""
-    mq, sc = fp4_rows(m)
-    b = _f64(lse) - np.einsum("nrd,rd->nr", mq, _f64(refs))
-    return mq, b, sc
+    """Planes with fp4-stored means (zo_fp4_planes): (m~ [n][R][d], b~ = LSE - r.m~ [n][R],
+    scales [n][R][d/32])."""
+    m = _f64(m)
+    return _lowp_planes(lib().zo_fp4_planes, m, lse, refs, m.shape[:2] + (m.shape[2] // 32,))
 
 
 class Tree:

@@ -273,6 +273,19 @@ ZO_EXPORT void zo_fp8_rows(const double* m, int64_t n, int d, double* out, doubl
     }
 }
 
+/* Planes of n nodes with fp8-stored means.  m [n][R][d] and lse [n][R] are a
+ * node's exact means and log-sum-exps; mq receives the stored means (one scale
+ * per (node, reference) row, scale [n][R]) and b = LSE - r.m~ is formed from the
+ * stored mq, so every plane still equals LSE exactly at q = r. */
+ZO_EXPORT void zo_fp8_planes(const double* m, const double* lse, const double* refs, int64_t n, int R, int d,
+                             double* mq, double* b, double* scale)
+{
+    zo_fp8_rows(m, n * R, d, mq, scale);
+    for (int64_t i = 0; i < n; ++i)
+        for (int r = 0; r < R; ++r)
+            b[i * R + r] = lse[i * R + r] - zo_dot(refs + (int64_t)r * d, mq + (i * R + r) * d, d);
+}
+
 /* ------------------------------------------------------- fp4 router summaries
  *
  * The 4-bit reading of the same passage ([wqu] opening bullets).  The grid is
@@ -322,6 +335,19 @@ ZO_EXPORT void zo_fp4_rows(const double* m, int64_t n, int d, double* out, doubl
             const int sx = zo_e2m1_block_exp(amax);
             for (int k = 0; k < 32; ++k) out[i * d + blk * 32 + k] = ldexp(zo_e2m1_round(ldexp(mb[k], -sx)), sx);
             scale[i * nb + blk] = ldexp(1.0, sx);
+        }
+}
+
+/* Planes of n nodes with fp4-stored means (scale [n][R][d/32], one per block of
+ * 32 values); b = LSE - r.m~ from the stored means, as for fp8. */
+ZO_EXPORT void zo_fp4_planes(const double* m, const double* lse, const double* refs, int64_t n, int R, int d,
+                             double* mq, double* b, double* scale)
+{
+    zo_fp4_rows(m, n * R, d, mq, scale);
+    for (int64_t i = 0; i < n; ++i)
+        for (int r = 0; r < R; ++r) {
+            const double* stored = mq + (i * R + r) * d;
+            b[i * R + r] = lse[i * R + r] - zo_dot(refs + (int64_t)r * d, stored, d);
         }
 }
 

@@ -40,7 +40,14 @@ def m_tol(dtype):
 class Case:
     """Inputs of a workload on the host (fp32 arrays holding stored-dtype values) and on the GPU."""
 
-    def __init__(self, cfg: zi.Config, lens=None, n_queries=2, max_tokens=None, device="cuda"):
+    def __init__(self, cfg: zi.Config, lens=None, n_queries=2, max_tokens=None, device="cuda", host_units=None,
+                 host_f64=False, with_appended=False, workers=16):
+        """host_units: the (sequence, KV head) pairs whose keys and values stay on the host for
+        the oracle (None: every pair); host_f64: keep them as fp64 (the oracle's input type, so
+        no conversion per call); with_appended: also write the rows the workload appends
+        during decode (zi.append_rows) after the first n_tokens rows, on the GPU and the host.
+        Units are generated in parallel threads (each from its own stream)."""
+        from concurrent.futures import ThreadPoolExecutor
         self.cfg = cfg
         B, Hkv, d = cfg.batch, cfg.n_kv_heads, cfg.head_dim
         self.B, self.Hkv, self.Hq, self.d = B, Hkv, cfg.n_q_heads, d
@@ -53,12 +60,24 @@ class Case:
         self.Kd = torch.zeros((B, Hkv, self.T, d), dtype=dt, device=device)
         self.Vd = torch.zeros((B, Hkv, self.T, d), dtype=dt, device=device)
         self.K, self.V = {}, {}
-        for b in range(B):
-            for g in range(Hkv):
-                Ku, Vu = zi.unit_kv(cfg, b, g)
-                self.K[(b, g)], self.V[(b, g)] = Ku, Vu
-                self.Kd[b, g, :cfg.n_tokens] = torch.from_numpy(Ku).to(device=device, dtype=dt)
-                self.Vd[b, g, :cfg.n_tokens] = torch.from_numpy(Vu).to(device=device, dtype=dt)
+        keep = None if host_units is None else set(host_units)
+        hdt = np.float64 if host_f64 else np.float32
+
+        def gen(bg):
+            Ku, Vu = zi.unit_kv(cfg, *bg)
+            if with_appended and cfg.append_steps:
+                Ka, Va = zi.append_rows(cfg, *bg)
+                Ku, Vu = np.concatenate([Ku, Ka]), np.concatenate([Vu, Va])
+            return bg, Ku, Vu
+
+        pairs = [(b, g) for b in range(B) for g in range(Hkv)]
+        with ThreadPoolExecutor(max(1, min(workers, len(pairs)))) as ex:
+            for (b, g), Ku, Vu in ex.map(gen, pairs):
+                n = len(Ku)
+                self.Kd[b, g, :n] = torch.from_numpy(Ku).to(device=device, dtype=dt)
+                self.Vd[b, g, :n] = torch.from_numpy(Vu).to(device=device, dtype=dt)
+                if keep is None or (b, g) in keep:
+                    self.K[(b, g)], self.V[(b, g)] = Ku.astype(hdt, copy=False), Vu.astype(hdt, copy=False)
         self.refs_d = torch.from_numpy(self.refs).to(device)
         self.qd = torch.from_numpy(self.q).to(device=device, dtype=dt)
 
@@ -67,9 +86,11 @@ class Case:
         dt = TORCH_DT[self.cfg.dtype]
         n = len(Krows)
         for src, host in ((Krows, self.K), (Vrows, self.V)):
+            if (b, g) not in host:  # a unit without host copies
+                continue
             cur = host[(b, g)]
             if cur.shape[0] < start + n:
-                grown = np.zeros((start + n, self.d), np.float32)
+                grown = np.zeros((start + n, self.d), cur.dtype)
                 grown[:cur.shape[0]] = cur
                 host[(b, g)] = grown
             host[(b, g)][start:start + n] = src
@@ -140,8 +161,9 @@ def _check_fp4_rows(mg, sg, m_o, where):
     assert err.max() <= 0, f"{where}: m excess {err.max():.3e}"
 
 
-def check_build(case: Case, tree: Tree, sample=None, seed=0):
-    """Checks stored planes against the oracle.  sample: nodes per (unit, level) or None for all."""
+def check_build(case: Case, tree: Tree, sample=None, seed=0, units=None):
+    """Checks stored planes against the oracle.  sample: nodes per (unit, level) or None for all;
+    units: the (sequence, KV head) unit numbers b * Hkv + g to check (None: all)."""
     cfg = case.cfg
     rel, floor = m_tol(cfg.dtype)
     fp8 = getattr(tree, "summary", "native") == "fp8"
@@ -161,6 +183,8 @@ def check_build(case: Case, tree: Tree, sample=None, seed=0):
                 nodes = np.unique(np.concatenate([[0, n_l - 1], rng.choice(n_l, sample - 2, replace=False)]))
             for g in range(case.Hkv):
                 u = b * case.Hkv + g
+                if units is not None and u not in units:
+                    continue
                 Ku = np.ascontiguousarray(case.unit_kv(b, g)[0], dtype=np.float64)  # widened once per unit
                 mg = m_d[u, torch.from_numpy(nodes).to(m_d.device)].float().cpu().numpy().astype(np.float64)
                 bg = b_d[u, torch.from_numpy(nodes).to(b_d.device)].cpu().numpy().astype(np.float64)
@@ -324,6 +348,7 @@ def check_block(case: Case, tree: Tree, qb, p: float, out, lse, scale=1.0, mode=
     every routing unit, and the oracle's attention of query t over token 0, its GPU kept
     chunks, the partial chunk and the block's rows N .. N + t.  qb: host [B][Tq][Hq][d]."""
     Tq = qb.shape[1]
+    tree.check()  # no device-side wait of the route gave up
     sel = [x for x in block_units(case, Tq, mode) if units is None or x[0] in units]
     items = [(v, b, g, qb[b, t, g * case.G + h * nh:g * case.G + (h + 1) * nh].astype(np.float64) * scale)
              for v, b, t, g, h, nh in sel]
@@ -375,6 +400,7 @@ def route_attend(case: Case, tree: Tree, t: int, p: float, scale=1.0, mode="grou
 
 def full_check(case: Case, tree: Tree, t: int, p: float, scale=1.0, units=None, mode="group"):
     out, lse = route_attend(case, tree, t, p, scale, mode)
+    tree.check()  # no device-side wait of the route gave up
     r = check_route(case, tree, t, p, scale, units, mode)
     a = check_attend(case, tree, out, lse, t, scale, units, mode)
     return r, a

@@ -34,6 +34,7 @@ def test_binding_covers_every_symbol():
 def test_status_strings():
     assert zha.zha_status_str(zha.ZHA_OK) == "ok"
     assert "capacity" in zha.zha_status_str(zha.ZHA_ERR_CAPACITY)
+    assert "gave up" in zha.zha_status_str(zha.ZHA_ERR_DEVICE)
     assert zha.zha_status_str(99) == "unknown status"
 
 
@@ -84,6 +85,7 @@ def test_null_arguments_rejected():
     assert lib.zha_attend_multi(None, None, 2, None, None, None, ctypes.c_float(1.0), None, None,
                                 None) == zha.ZHA_ERR_INVALID
     assert lib.zha_tree_bytes(None, None) == zha.ZHA_ERR_INVALID
+    assert lib.zha_tree_check(None, None) == zha.ZHA_ERR_INVALID
     assert lib.zha_timing_enable(None, 1, -1) == zha.ZHA_ERR_INVALID
     n = ctypes.c_int32()
     assert lib.zha_timing_read(None, None, None, None, 0, ctypes.byref(n)) == zha.ZHA_ERR_INVALID

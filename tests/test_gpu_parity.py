@@ -323,6 +323,10 @@ MULTI_VARIANTS = [
                                                chunk=4, levels=3, n_refs=8), [2990, 1500], 5, "group", 5),
     ("block bf16 d64 C4 L3 R8 G8 T3", dict(batch=1, n_tokens=2000, head_dim=64, n_q_heads=16, n_kv_heads=2, chunk=4,
                                             levels=3, n_refs=8), [1990], 3, "group", 3),
+    # a sequence without a complete chunk beside a longer one, in union attention groups of 40
+    # columns (three tiles): the short sequence's groups have empty kept-chunk lists
+    ("block bf16 d128 C4 L3 R16 G8 B2 T5 empty list", dict(batch=2, n_tokens=3000, chunk=4, levels=3, n_refs=16),
+     [3, 2990], 5, "group", 5),
     # f32 union scoring with four column tiles (40 columns); f32 attention groups of 16 columns
     ("block f32 d128 C4 L3 R16 G8 T5", dict(batch=1, n_tokens=2000, n_q_heads=16, n_kv_heads=2, chunk=4, levels=3,
                                             n_refs=16, dtype="f32"), [1990], 5, "group", 5),
@@ -377,6 +381,35 @@ def test_block_capacity_and_order():
     with pytest.raises(zha.ZhaError) as ei:
         tree.attend_multi(qbd4, case.Kd, case.Vd)
     assert ei.value.status == zha.ZHA_ERR_CAPACITY
+
+
+def test_attend_needs_a_current_route():
+    """A route's kept lists describe the cache it was taken on: after an append (or a
+    rebuild) attention refuses them until the tree is routed again."""
+    cfg = small(batch=1, n_tokens=1100, n_q_heads=8, n_kv_heads=2, chunk=4, levels=2, n_refs=4, n_queries=4,
+                needles_per_unit=2, append_steps=8)
+    say("case stale route: N=1090 of max 1108, append then attend")
+    case = Case(cfg, lens=[1090], n_queries=4, max_tokens=1108)
+    tree = case.tree(max_queries=2)
+    route_attend(case, tree, 0, 0.9)
+    tree.append(case.Kd, [1094])  # completes a chunk: the kept list no longer covers the cache
+    with pytest.raises(zha.ZhaError) as ei:
+        tree.attend(case.qd[0], case.Kd, case.Vd)
+    assert ei.value.status == zha.ZHA_ERR_INVALID
+    case.lens = [1094]
+    r, a = full_check(case, tree, 1, 0.9)
+    say(" routed again after the append:", r, a)
+    qb, qbd = block_of(case, 2)
+    tree.route_multi(qbd, 0.9)
+    tree.build(case.Kd, case.refs_d, [1094])
+    with pytest.raises(zha.ZhaError) as ei:
+        tree.attend_multi(qbd, case.Kd, case.Vd)
+    assert ei.value.status == zha.ZHA_ERR_INVALID
+    tree.route_multi(qbd, 0.9)
+    out, lse = tree.attend_multi(qbd, case.Kd, case.Vd)
+    torch.cuda.synchronize()
+    say(" block routed again after the rebuild:", *check_block(case, tree, qb, 0.9, out, lse))
+    tree.check()
 
 
 def selection_levels(tree, route):
@@ -691,14 +724,3 @@ def test_wide_256k_full():
         r, a = full_check(case, tree, t, 0.95)
         say(f" t={t}", r, a)
 
-
-@pytest.mark.slow
-def test_deep_1m_full():
-    cfg = zi.get_config("deep_1m")
-    say("case deep_1m full: N=1048576, 32q/4kv, d=128, C=4 L=7 R=16 p=0.95")
-    case = Case(cfg, n_queries=1)
-    tree = case.tree()
-    torch.cuda.synchronize()
-    say(" build", check_build(case, tree, sample=12))
-    r, a = full_check(case, tree, 0, 0.95, units={0, 3})
-    say(" t=0", r, a)

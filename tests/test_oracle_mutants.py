@@ -63,6 +63,11 @@ MUTANTS = [
     ("fp4_scale_not_minimal", "while (ldexp(amax, -s) > 6.0) ++s;", "while (ldexp(amax, -s) > 3.0) ++s;"),
     ("fp4_one_scale_per_row", "for (int k = 0; k < 32; ++k) amax = fmax(amax, fabs(mb[k]));",
      "for (int k = 0; k < d; ++k) amax = fmax(amax, fabs(m[i * d + k]));"),
+    ("fp8_plane_offset_from_exact_mean",
+     "b[i * R + r] = lse[i * R + r] - zo_dot(refs + (int64_t)r * d, mq + (i * R + r) * d, d);",
+     "b[i * R + r] = lse[i * R + r] - zo_dot(refs + (int64_t)r * d, m + (i * R + r) * d, d);"),
+    ("fp4_plane_offset_sign", "b[i * R + r] = lse[i * R + r] - zo_dot(refs + (int64_t)r * d, stored, d);",
+     "b[i * R + r] = lse[i * R + r] + zo_dot(refs + (int64_t)r * d, stored, d);"),
     ("attention_one_head", "const double* qh = q + (int64_t)h * d;\n        double mx = -INFINITY;\n        for (int64_t i = 0; i < nS; ++i) {",
      "const double* qh = q;\n        double mx = -INFINITY;\n        for (int64_t i = 0; i < nS; ++i) {"),
 ]
