@@ -375,10 +375,17 @@ def run_workload(cfg, args, env, headline, layers):
             del cal_src, cal_dst
 
         segs = []  # per-step event pairs: the step (fixed-size workloads) or append and each p's route + attend
+        # every event of the timed region is created before it (creating one is a host-side
+        # allocation that can leave the GPU idle between steps)
+        nseg = 1 + len(p_sweep) if growing else 1
+        pool = [torch.cuda.Event(enable_timing=True) for _ in range(2 * nseg * args.steps)]
+        for e in pool:  # torch creates the device event at its first record
+            e.record()
+        torch.cuda.synchronize()
 
         def seg(name, fn, record):
             if record:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a, b = pool.pop(), pool.pop()
                 a.record()
                 fn()
                 b.record()
@@ -598,6 +605,10 @@ def run_workload(cfg, args, env, headline, layers):
             dense_decode(qd[i % nq], Ks[li], Vs[li], layer_lens[li], Hkv, 1.0, ws, outs[li], lses[li])
         torch.cuda.synchronize()
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in evs:  # the events exist on the device before the timed region
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
         ev0.record()
         for i in range(args.steps):
             li = i % layers

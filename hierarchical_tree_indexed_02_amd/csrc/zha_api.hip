@@ -13,6 +13,7 @@
 
 int zha_score_wgs(const zha_tree* t, int level);
 int zha_compact_chunks(int64_t nodes);
+int zha_small_score_rows();
 int zha_hist_bins();
 int64_t zha_sel_cand_entries(int U);
 int zha_sel_ctr_words(int U);
@@ -82,7 +83,8 @@ void free_tree(zha_tree* t) {
     if (t->kept[l]) (void)hipFree(t->kept[l]);
     if (t->krank[l]) (void)hipFree(t->krank[l]);
   }
-  void* ps[] = {t->refs,   t->spine,  t->sub_lse, t->sub_m,  t->counts,    t->geo,      t->scores,   t->spart,    t->keys,     t->apart,
+  void* ps[] = {t->refs,   t->spine,  t->sub_lse, t->sub_m,  t->counts,    t->geo,      t->scores,   t->spart[0], t->spart[1],
+                t->sscore[0], t->sscore[1], t->keys,     t->apart,
                 t->fh_cnt, t->fh_mass,  t->fh_edge,  t->cut,      t->sel_cand, t->sel_ctr, t->lb_status,
                 t->lb_epoch, t->lb_error, t->route_ctr, t->uflag, t->ulist, t->ucount};
   for (void* p : ps)
@@ -251,7 +253,10 @@ zha_status zha_tree_create(const zha_tree_desc* desc, zha_tree_t* out) {
   ok = ok && dalloc(t, &t->counts, (size_t)2 * (L + 2) * RUmax * sizeof(int32_t));
   ok = ok && dalloc(t, &t->geo, (size_t)(L + 2) * desc->batch * sizeof(int32_t));
   ok = ok && dalloc(t, &t->scores, (size_t)t->cap[1] * score_n * sizeof(float));
-  ok = ok && dalloc(t, &t->spart, spart_n * sizeof(float));
+  for (int i = 0; i < 2; ++i) {
+    ok = ok && dalloc(t, &t->sscore[i], (size_t)zha_small_score_rows() * score_n * sizeof(float));
+    ok = ok && dalloc(t, &t->spart[i], spart_n * sizeof(float));
+  }
   t->kstride = (t->cap[1] + 3) / 4 * 4;
   ok = ok && dalloc(t, &t->keys, (size_t)RUmax * t->kstride * sizeof(uint32_t));
   if (uni) {

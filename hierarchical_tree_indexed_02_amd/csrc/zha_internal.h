@@ -137,6 +137,61 @@ __device__ __forceinline__ float max16(float x) {
   return x;
 }
 
+// Wave-wide reductions on gfx950 with every lane ending with the same bits: the row of 16
+// lanes by DPP (as above), then the row pairs by v_permlane16_swap and the halves by
+// v_permlane32_swap (each lane adds the same two values in the same order).
+__device__ __forceinline__ float wave_sum(float x) {
+  x = sum16(x);
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = max16(x);
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, dpp_u32<0xB1>(x));
+  x = min(x, dpp_u32<0x4E>(x));
+  x = min(x, dpp_u32<0x141>(x));
+  x = min(x, dpp_u32<0x140>(x));
+  auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = min(a[0], a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return min(b[0], b[1]);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u32<0xB1>(x));
+  x = max(x, dpp_u32<0x4E>(x));
+  x = max(x, dpp_u32<0x141>(x));
+  x = max(x, dpp_u32<0x140>(x));
+  auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max(a[0], a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max(b[0], b[1]);
+}
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long x) {
+  auto step = [](unsigned long long v, uint32_t lo, uint32_t hi) { return v + (((unsigned long long)hi << 32) | lo); };
+  x = step(x, dpp_u32<0xB1>((uint32_t)x), dpp_u32<0xB1>((uint32_t)(x >> 32)));
+  x = step(x, dpp_u32<0x4E>((uint32_t)x), dpp_u32<0x4E>((uint32_t)(x >> 32)));
+  x = step(x, dpp_u32<0x141>((uint32_t)x), dpp_u32<0x141>((uint32_t)(x >> 32)));
+  x = step(x, dpp_u32<0x140>((uint32_t)x), dpp_u32<0x140>((uint32_t)(x >> 32)));
+  auto al = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  auto ah = __builtin_amdgcn_permlane16_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+  x = ((((unsigned long long)ah[0]) << 32) | al[0]) + ((((unsigned long long)ah[1]) << 32) | al[1]);
+  auto bl = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  auto bh = __builtin_amdgcn_permlane32_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+  return ((((unsigned long long)bh[0]) << 32) | bl[0]) + ((((unsigned long long)bh[1]) << 32) | bl[1]);
+}
+
 // fp32 accumulator of one (node, reference query) while its children are folded in:
 // running maximum M, S = sum exp(x - M), V = sum exp(x - M) * m (this lane's slice).
 // Folding child (x, m) and finishing give LSE = M + log S, mean = V / S, the exact
@@ -239,8 +294,9 @@ struct zha_tree {
   float* sub_lse;                   // [U][cap_S][R] fp32 LSE of finished level-S nodes (S < L only)
   float* sub_m;                     // [U][cap_S][R][d] fp32 means of finished level-S nodes
   int32_t* counts;                  // [2][L+2][U]: frontier counts, kept counts per level
-  float* scores;                    // [U][cap1][G rounded up to 4]
-  float* spart;                     // [U][WS][G][2] score-kernel partial log-sum-exp
+  float* scores;                    // [U][cap1][G rounded up to 4] scores of a level of more than 1024 nodes
+  float* sscore[2];                 // [U][1024][G rounded up to 4] scores of smaller levels, by level parity
+  float* spart[2];                  // [U][WS][G][2] score-kernel partial log-sum-exp, by level parity
   uint32_t* keys;                   // [U][kstride] node-mass keys of the level being selected
   int64_t kstride;                  // cap1 rounded up to a multiple of 4
   uint32_t* fh_cnt;                 // [U][1024] fine mass histogram (zero between levels)

@@ -25,6 +25,8 @@
 // prefix whose mass reaches p times the frontier's total.  Masses are compared as
 // fp32 bit patterns ("keys") and summed as 40-bit fixed-point integers, so every
 // sum is exact and independent of order: results are bit-identical run to run.
+#include <algorithm>
+
 #include "zha_internal.h"
 
 namespace {
@@ -152,7 +154,34 @@ struct ScoreArgs {
                           // the unit's kept list; null at the top level (every node is a member)
   uint32_t* route_ctr;    // route stamp; the top level's first workgroup advances it
   int TS, NTC;            // queries per group; groups per (sequence, KV head)
+  // PSEL (one routing unit per grid row): the parent level l+1 has at most WN frontier nodes
+  // and was scored but not selected; every workgroup selects it itself (one wave, from the
+  // parent level's scores and partials) and scores the children of its kept nodes.
+  // Workgroup 0 of each unit publishes the parent level's selection.
+  Level pv;               // the parent level (its frontier: pv.parent, pv.parent_nF, pv.nodes)
+  const float* pscores;   // the parent level's scores [U][pstride][score row]
+  int64_t pstride;
+  int32_t* pkept;         // kept ids of the parent level [U][pcapl] (written by workgroup 0)
+  int64_t pcapl;
+  int32_t* pnF_out;       // the parent level's frontier counts [U]
+  int32_t* pkept_count;   // the parent level's kept counts [U]
+  int32_t* nF_out;        // this level's frontier counts [U]
+  float p;
+  int keep_all;
 };
+
+// Selection of a level of at most WN frontier nodes by one wave (see wave_select).
+constexpr int WN = 1024;
+struct WaveSh {
+  uint32_t keys[WN];      // mass keys by frontier position
+  int32_t fid[WN];        // node ids by frontier position
+  int32_t kept[WN];       // kept node ids, ascending
+  uint32_t hcnt[1024];    // histogram of the key range
+  u64 hmass[1024];
+  uint32_t ckey[64], cpos[64];
+};
+__device__ void wave_select(const Level& v, int u, int capF, const float* scores, int64_t sstride, int G, float p,
+                            int keep_all, WaveSh& sh, int& nF_out, int& nk_out, int& nx_out);
 
 // Eight fp8 e4m3 codes (two dwords) as eight bf16 values (exact), by the hardware
 // conversion; element e is byte e.
@@ -198,9 +227,10 @@ __device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t w, float sc) {
 // jcol of unit cu(c)): every loaded plane tile feeds NT matrix products.  A node is loaded
 // when some column's unit has its parent kept (a stamped rank entry), and each column keeps
 // the scores of its unit's member nodes at the unit's frontier positions.
-template <typename T, int R, int D, int UN, int SM, bool UNI, int NT>
-__global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a) {
+template <typename T, int R, int D, int UN, int SM, bool UNI, int NT, bool PSEL>
+__global__ __launch_bounds__(256, UNI ? 2 : (PSEL ? 3 : 4)) void zha_score_kernel(ScoreArgs a) {
   typedef Mf<T> M;
+  static_assert(!PSEL || !UNI, "in-kernel parent selection serves one routing unit per grid row");
   constexpr bool F8 = SM == 1, F4 = SM == 2, LP = SM != 0;  // summary storage: native, fp8, fp4
   // FLAT: loads are issued unconditionally (inactive rows read a clamped, readable address and
   // their results are discarded), so no load sits under a branch, after whose join the compiler
@@ -247,7 +277,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
     up = plane_unit(u[0], a.hr, a.Hkv, a.Tq);
     ok[0] = row < G;
     jc[0] = row;
-    end = frontier_size(a.v, u[0]);
+    end = PSEL ? 0 : frontier_size(a.v, u[0]);
   }
   const uint32_t stamp = (UNI && a.krank) ? a.route_ctr[0] : 0u;
   // Super-tiles are dealt to the workgroups in turn: at any moment the unit's workgroups
@@ -255,6 +285,24 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
   const int start = blockIdx.x * SUPER;
   const int step = a.W * SUPER;
 
+  // PSEL: the workgroup selects the parent level first (its query loads then go out with
+  // the first plane loads); the kept parents are read from LDS
+  __shared__ WaveSh wsh_[1];  // referenced by the PSEL instantiations only
+  if constexpr (PSEL) {
+    WaveSh& wsh = wsh_[0];
+    int nFp, nk, nx;
+    wave_select(a.pv, u[0], (int)a.pcapl, a.pscores, a.pstride, G, a.p, a.keep_all, wsh, nFp, nk, nx);
+    end = nx;
+    if (blockIdx.x == 0) {  // publish the parent level's selection (one workgroup per unit)
+      if (threadIdx.x == 0) {
+        a.pnF_out[u[0]] = nFp;
+        a.pkept_count[u[0]] = nk;
+        a.nF_out[u[0]] = nx;
+      }
+      int32_t* kp = a.pkept + (int64_t)u[0] * a.pcapl;
+      for (int i = threadIdx.x; i < nk; i += blockDim.x) kp[i] = wsh.kept[i];
+    }
+  }
   typename M::frag qf[NT][NK];
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
@@ -265,7 +313,8 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
       qf[n][s] = ok[n] ? M::load(qp + k0) : M::zero();
     }
   }
-  const int32_t* par = (!UNI && a.v.parent) ? a.v.parent + (int64_t)u[0] * a.v.cap_parent : nullptr;
+  const int32_t* par = (!UNI && !PSEL && a.v.parent) ? a.v.parent + (int64_t)u[0] * a.v.cap_parent : nullptr;
+  const bool has_par = PSEL || par != nullptr;
   // always-readable bases for the unconditional parent-id and kept-rank loads (entry 0 is read
   // when the real array is absent or the entry is not needed)
   const int32_t* pload = par ? par : a.v.nodes;
@@ -299,8 +348,11 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
         pp[k] = 0;
       } else {
         const int pos = base + (k * 4 + wave) * NPT + row / R;
-        const bool need = par && pos < end;
-        const int32_t x = (FLAT || need) ? pload[need ? (a.v.Cshift >= 0 ? (pos >> a.v.Cshift) : pos / a.v.C) : 0] : 0;
+        const bool need = has_par && pos < end;
+        const int pidx = need ? (a.v.Cshift >= 0 ? (pos >> a.v.Cshift) : pos / a.v.C) : 0;
+        int32_t x;
+        if constexpr (PSEL) x = wsh_[0].kept[pidx];
+        else x = (FLAT || need) ? pload[pidx] : 0;
         pp[k] = need ? x : 0;
         rk[k][0] = 0;
       }
@@ -350,7 +402,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
       const int pos = tbk + row / R;
       const bool v = UNI ? ((act[k] >> (row / R)) & 1u) != 0 : pos < end;
       int id = pos;
-      if (!UNI && par) id = a.v.Cshift >= 0 ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
+      if (!UNI && has_par) id = a.v.Cshift >= 0 ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
                                            : pp[k] * a.v.C + pos % a.v.C;
       id = v ? id : 0;
       // inactive rows read node 0 (FLAT) or nothing; their results are never written
@@ -447,7 +499,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : 4) void zha_score_kernel(ScoreArgs a
       const int pos = tbk + row / R;
       const bool v = UNI ? ((act[k] >> (row / R)) & 1u) != 0 : pos < end;
       int id = pos;
-      if (!UNI && par) id = a.v.Cshift >= 0 ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
+      if (!UNI && has_par) id = a.v.Cshift >= 0 ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
                                            : pp[k] * a.v.C + pos % a.v.C;
       id = v ? id : 0;
       if constexpr (F4) {
@@ -706,6 +758,339 @@ __device__ __forceinline__ uint4 load4c(const uint32_t* k, int pos, int ncap) {
   return *(const uint4*)(k + min(pos, ncap - 4));
 }
 
+
+// ------------------------------------------------------------ small-frontier selection
+//
+// A frontier of at most WN nodes is selected by a workgroup of SSEL = 256 threads, thread
+// t holding positions t, t + 256, t + 512, t + 768.  Every load of a thread is issued at once
+// (parent ids and score rows at positions clamped to the level's capacity, so none waits
+// for the frontier size).  The per-head log-sum-exp over the frontier is a maximum then a
+// sum, each over the thread's positions, the wave (DPP and lane swaps: every lane gets the
+// same bits) and the four waves in order; then the mass keys and their fixed-point total.
+// The cut: a histogram of NB slices of the key range (LDS atomics), a scan over the threads
+// from the heaviest slice down for the crossing slice, and its keys ranked by one wave (at
+// most 64, one per lane); more than 64 keys in the slice narrow the range to it and the
+// histogram is repeated.  The kept nodes are written in position order: each wave counts
+// its 256 positions (ballots), then writes them after the earlier waves' counts.  The rule
+// is that of the multi-wave selections: keep keys above the cut key tau, and keys equal to
+// tau up to the position tie_last.
+
+constexpr int SSEL = 256;            // threads of the small selection
+constexpr int SSPT = WN / SSEL;      // frontier positions per thread
+static_assert(SSPT == 4 && NB == 4 * SSEL, "four positions and four histogram slices per thread");
+
+__device__ void wave_select(const Level& v, int u, int capF, const float* scores, int64_t sstride, int G, float p,
+                            int keep_all, WaveSh& sh, int& nF_out, int& nk_out, int& nx_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const u64 lt = (1ull << lane) - 1ull;  // lanes below this one
+  __shared__ float s_red[SSEL / 64][16];
+  __shared__ uint32_t s_min[SSEL / 64], s_max[SSEL / 64];
+  __shared__ u64 s_tot[SSEL / 64], s_scan[SSEL / 64];
+  __shared__ uint32_t s_bin, s_nc, s_tau;
+  __shared__ int s_tie;
+  __shared__ u64 s_above;
+  __shared__ int s_cnt[SSEL / 64], s_last;
+  // every load at once: the frontier size, parent ids and score rows (clamped positions)
+  const int nF = frontier_size(v, u);
+  const int nchild = child_nodes(v, u);
+  const int32_t* par = v.parent ? v.parent + (int64_t)u * v.cap_parent : nullptr;
+  const int GS = score_stride(G);
+  const float* sc = scores + (int64_t)u * sstride * GS;
+  const int cmax = max(capF, 1) - 1;
+  int pid[SSPT];
+  float4 sv[SSPT][4];
+#pragma unroll
+  for (int k = 0; k < SSPT; ++k) {
+    const int pc = min(tid + SSEL * k, cmax);
+    pid[k] = par ? par[v.Cshift >= 0 ? pc >> v.Cshift : pc / v.C] : 0;
+    load_scores(sc + (int64_t)pc * GS, G, sv[k]);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    sh.hcnt[tid + SSEL * e] = 0;
+    sh.hmass[tid + SSEL * e] = 0;
+  }
+  if (tid == 0) s_nc = 0;
+  bool val[SSPT];
+#pragma unroll
+  for (int k = 0; k < SSPT; ++k) val[k] = tid + SSEL * k < nF;
+  // per-head maximum, then sum of exp(s - max), over the frontier
+  float lse[16];
+#pragma unroll
+  for (int h4 = 0; h4 < 4; ++h4) {
+    if (4 * h4 < G) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < SSPT; ++k) {
+          const float x = j == 0 ? sv[k][h4].x : (j == 1 ? sv[k][h4].y : (j == 2 ? sv[k][h4].z : sv[k][h4].w));
+          m = val[k] ? fmaxf(m, x) : m;
+        }
+        m = wave_max(m);
+        if (lane == 0) s_red[wave][4 * h4 + j] = m;
+      }
+    }
+  }
+  __syncthreads();
+  float hmax[16];
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < SSEL / 64; ++w) m = fmaxf(m, h < G ? s_red[w][h] : -INFINITY);
+    hmax[h] = m;
+  }
+  __syncthreads();  // s_red is reused for the sums
+#pragma unroll
+  for (int h4 = 0; h4 < 4; ++h4) {
+    if (4 * h4 < G) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float M = hmax[4 * h4 + j];
+        float e = 0.0f;
+#pragma unroll
+        for (int k = 0; k < SSPT; ++k) {
+          const float x = j == 0 ? sv[k][h4].x : (j == 1 ? sv[k][h4].y : (j == 2 ? sv[k][h4].z : sv[k][h4].w));
+          e += (val[k] && x != -INFINITY) ? zexp(x - M) : 0.0f;
+        }
+        e = wave_sum(e);
+        if (lane == 0) s_red[wave][4 * h4 + j] = e;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    float S = 0.0f;
+#pragma unroll
+    for (int w = 0; w < SSEL / 64; ++w) S += h < G ? s_red[w][h] : 0.0f;
+    lse[h] = (h < G && hmax[h] != -INFINITY) ? hmax[h] + zlog(S) : 0.0f;
+  }
+  // node ids and mass keys by position; their range and fixed-point total
+  const float invG = 1.0f / (float)G;
+  uint32_t key[SSPT];
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  u64 tot = 0;
+#pragma unroll
+  for (int k = 0; k < SSPT; ++k) {
+    const int pos = tid + SSEL * k;
+    key[k] = mass_key(sv[k], lse, G, invG);
+    if (val[k]) {
+      sh.fid[pos] = par ? (v.Cshift >= 0 ? (pid[k] << v.Cshift) + (pos & ((1 << v.Cshift) - 1))
+                                         : pid[k] * v.C + pos % v.C)
+                        : pos;
+      sh.keys[pos] = key[k];
+      kmin = min(kmin, key[k]);
+      kmax = max(kmax, key[k]);
+      tot += fx_mass(key[k]);
+    }
+  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  tot = wave_sum_u64(tot);
+  if (lane == 0) { s_min[wave] = kmin; s_max[wave] = kmax; s_tot[wave] = tot; }
+  __syncthreads();
+  kmin = s_min[0]; kmax = s_max[0]; tot = s_tot[0];
+#pragma unroll
+  for (int w = 1; w < SSEL / 64; ++w) { kmin = min(kmin, s_min[w]); kmax = max(kmax, s_max[w]); tot += s_tot[w]; }
+  const bool all = keep_all || nF == 0 || tot == 0;  // tot 0: every mass rounds to zero
+  uint32_t tau = 0;
+  int tie_last = 0x7FFFFFFF;
+  if (!all) {
+    const u64 T = target_of(p, tot);
+    uint32_t lo = kmin, hi = kmax;
+    u64 above = 0;
+    for (int round = 0;; ++round) {
+      const int shift = range_shift(lo, hi);
+      if (round > 0) {  // a narrowed range: a fresh histogram
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sh.hcnt[tid + SSEL * e] = 0;
+          sh.hmass[tid + SSEL * e] = 0;
+        }
+        if (tid == 0) s_nc = 0;
+        __syncthreads();
+      }
+#pragma unroll
+      for (int k = 0; k < SSPT; ++k) {
+        if (val[k] && key[k] >= lo && key[k] <= hi) {
+          const uint32_t bn = range_bin(key[k], lo, shift);
+          atomicAdd(&sh.hcnt[bn], 1u);
+          atomicAdd(&sh.hmass[bn], fx_mass(key[k]));
+        }
+      }
+      __syncthreads();
+      // thread t owns slices NB-1-4t .. NB-4-4t (heaviest first); the mass above them is a
+      // prefix over the threads
+      u64 m4[4], msum = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        m4[e] = sh.hmass[NB - 1 - 4 * tid - e];
+        msum += m4[e];
+      }
+      u64 inc = msum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const u64 y = __shfl_up(inc, o);
+        inc += lane >= o ? y : 0;
+      }
+      if (lane == 63) s_scan[wave] = inc;
+      __syncthreads();
+      u64 before = above + inc - msum;
+#pragma unroll
+      for (int w = 0; w < SSEL / 64; ++w) before += w < wave ? s_scan[w] : 0;
+      if (before < T && before + msum >= T) {  // exactly one thread
+        u64 run = before;
+        int f = 3;
+        for (int e = 0; e < 4; ++e) {
+          if (run + m4[e] >= T) { f = e; break; }
+          run += m4[e];
+        }
+        s_bin = (uint32_t)(NB - 1 - 4 * tid - f);
+        s_above = run;
+      }
+      __syncthreads();
+      const uint32_t bin = s_bin;
+      above = s_above;
+      const uint32_t cnt = sh.hcnt[bin];
+      uint32_t nlo, nhi;
+      slice_range(lo, hi, bin, &nlo, &nhi);
+      if (cnt <= 64u) {
+        // the slice's keys, by all threads, in any order
+#pragma unroll
+        for (int k = 0; k < SSPT; ++k) {
+          if (val[k] && key[k] >= nlo && key[k] <= nhi) {
+            const uint32_t slot = atomicAdd(&s_nc, 1u);
+            sh.ckey[slot] = key[k];
+            sh.cpos[slot] = (uint32_t)(tid + SSEL * k);
+          }
+        }
+        __syncthreads();
+        if (wave == 0) {
+          const bool mine = lane < (int)cnt;
+          const uint32_t mk = sh.ckey[mine ? lane : 0], mp = sh.cpos[mine ? lane : 0];
+          const u64 mm = fx_mass(mk);
+          u64 bf = above;
+          for (int j = 0; j < (int)cnt; ++j) {  // (readlane returns int: every word widened unsigned)
+            const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mk, j);
+            const uint32_t qj = (uint32_t)__builtin_amdgcn_readlane((int)mp, j);
+            const u64 mj = ((u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mm >> 32), j) << 32) |
+                           (u64)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mm, j);
+            bf += (kj > mk || (kj == mk && qj < mp)) ? mj : 0;
+          }
+          const u64 c = __ballot(mine && bf < T && bf + mm >= T);
+          const int cl = c ? __ffsll((unsigned long long)c) - 1 : 0;
+          if (lane == 0) {
+            s_tau = (uint32_t)__builtin_amdgcn_readlane((int)mk, cl);
+            s_tie = __builtin_amdgcn_readlane((int)mp, cl);
+          }
+        }
+        __syncthreads();
+        tau = s_tau;
+        tie_last = s_tie;
+        break;
+      }
+      if (nhi <= nlo) {
+        // more than 64 keys of one value: the first n_take of them in position order
+        const uint32_t n_take = ties_to_take(nlo, T, above);
+        tau = nlo;
+        if (n_take < cnt) {
+          if (wave == 0) {
+            uint32_t seen = 0;
+            int tl = 0;
+            for (int r0 = 0; r0 < nF; r0 += 64) {
+              const int pos = r0 + lane;
+              const bool eq = pos < nF && sh.keys[min(pos, nF - 1)] == tau;
+              const u64 b = __ballot(eq);
+              const uint32_t pc = (uint32_t)__popcll(b);
+              if (seen + pc >= n_take) {  // the n_take-th equal key lies in this row
+                const uint32_t rank = seen + (uint32_t)__popcll(b & lt);
+                const u64 w = __ballot(eq && rank == n_take - 1);
+                tl = r0 + (__ffsll((unsigned long long)w) - 1);
+                break;
+              }
+              seen += pc;
+            }
+            if (lane == 0) s_tie = tl;
+          }
+          __syncthreads();
+          tie_last = s_tie;
+        }
+        break;
+      }
+      lo = nlo;
+      hi = nhi;
+    }
+  }
+  // the kept nodes in position order: wave w writes positions [256 w, 256 w + 256) after the
+  // kept counts of the waves before it
+  bool kp[SSPT];
+  int cnt_w = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int pos = SSEL * wave + 64 * r + lane;
+    const uint32_t k = sh.keys[min(pos, max(nF, 1) - 1)];
+    kp[r] = pos < nF && (all || k > tau || (k == tau && pos <= tie_last));
+    cnt_w += __popcll(__ballot(kp[r]));
+  }
+  if (lane == 0) s_cnt[wave] = cnt_w;
+  if (tid == 0) s_last = -1;
+  __syncthreads();
+  int base = 0, nk = 0;
+#pragma unroll
+  for (int w = 0; w < SSEL / 64; ++w) {
+    base += w < wave ? s_cnt[w] : 0;
+    nk += s_cnt[w];
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int pos = SSEL * wave + 64 * r + lane;
+    const u64 b = __ballot(kp[r]);
+    if (kp[r]) {
+      const int id = sh.fid[pos];
+      sh.kept[base + __popcll(b & lt)] = id;
+      if (pos == nF - 1) s_last = id;
+    }
+    base += __popcll(b);
+  }
+  __syncthreads();
+  const int last_id = s_last;
+  nF_out = nF;
+  nk_out = nk;
+  nx_out = last_id >= 0 ? next_frontier(nk, last_id, v.C, nchild) : v.C * nk;
+}
+
+struct WaveArgs {
+  Level v;
+  const float* scores;    // [U][sstride][score row]
+  int64_t sstride;
+  int G;
+  float p;
+  int keep_all;
+  int32_t* kept;          // [U][capl]
+  int64_t capl;
+  int32_t* nF_out;        // [U]
+  int32_t* kept_count;    // [U]
+  int32_t* next_nF;       // [U]; null at level 1
+};
+
+// A level of at most WN nodes whose selection is not run by the next level's scoring
+// launch (level 1, or routes of grouped units): one workgroup of SSEL threads per unit.
+__global__ __launch_bounds__(SSEL) void zha_select_wave_kernel(WaveArgs a) {
+  __shared__ WaveSh sh;
+  const int u = blockIdx.x;
+  int nF, nk, nx;
+  wave_select(a.v, u, (int)a.capl, a.scores, a.sstride, a.G, a.p, a.keep_all, sh, nF, nk, nx);
+  int32_t* kp = a.kept + (int64_t)u * a.capl;
+  for (int i = threadIdx.x; i < nk; i += SSEL) kp[i] = sh.kept[i];
+  if (threadIdx.x == 0) {
+    a.nF_out[u] = nF;
+    a.kept_count[u] = nk;
+    if (a.next_nF) a.next_nF[u] = nx;
+  }
+}
 
 // Selection state of one workgroup (LDS).  ST = 512 threads: two waves per SIMD keep the
 // throughput phases at full issue rate while a serial step waits only on its own
@@ -1725,9 +2110,9 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
 // registers of four workgroups per compute unit, and fewer workgroups measured slower; for
 // fp4 codes four or eight tiles measured slower too).
 // SM: summary storage (0 native, 1 fp8, 2 fp4)
-template <typename T, int R, int D, int SM, bool UNI, int NT = 1>
+template <typename T, int R, int D, int SM, bool UNI, int NT = 1, bool PSEL = false>
 hipError_t launch_score(const ScoreArgs& a, int W, int rows, hipStream_t s) {
-  hipLaunchKernelGGL((zha_score_kernel<T, R, D, 2, SM, UNI, NT>), dim3(W, rows), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((zha_score_kernel<T, R, D, 2, SM, UNI, NT, PSEL>), dim3(W, rows), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1740,9 +2125,19 @@ hipError_t launch_score_uni(const ScoreArgs& a, int W, int rows, int NT, hipStre
   }
 }
 
-// rows: routing units, or groups of them (uni; R >= 4 there, NT column tiles of 16)
+// rows: routing units, or groups of them (uni; R >= 4 there, NT column tiles of 16); psel:
+// the parent level's selection runs in every workgroup (one routing unit per row)
 template <typename T, int D, int SM = 0>
-hipError_t launch_score_r(const ScoreArgs& a, int R, int W, int rows, bool uni, int NT, hipStream_t s) {
+hipError_t launch_score_r(const ScoreArgs& a, int R, int W, int rows, bool uni, int NT, bool psel, hipStream_t s) {
+  if (psel) {
+    switch (R) {
+      case 1: return launch_score<T, 1, D, SM, false, 1, true>(a, W, rows, s);
+      case 2: return launch_score<T, 2, D, SM, false, 1, true>(a, W, rows, s);
+      case 4: return launch_score<T, 4, D, SM, false, 1, true>(a, W, rows, s);
+      case 8: return launch_score<T, 8, D, SM, false, 1, true>(a, W, rows, s);
+      default: return launch_score<T, 16, D, SM, false, 1, true>(a, W, rows, s);
+    }
+  }
   if (uni) {
     switch (R) {
       case 4: return launch_score_uni<T, 4, D, SM>(a, W, rows, NT, s);
@@ -1802,6 +2197,7 @@ int zha_union_queries(int R, int Gq, int Tq, int hr, bool wide) { return union_q
 int zha_union_score_queries(int R, int Gq, int Tq, int hr) { return union_queries(R, Gq, Tq, hr, 64); }
 
 int zha_compact_chunks(int64_t nodes) { return (int)((nodes + CH - 1) / CH); }
+int zha_small_score_rows() { return WN; }  // rows per routing unit of the small score buffers
 int zha_hist_bins() { return NB; }
 int64_t zha_sel_cand_entries(int U) { return (int64_t)U * sel_regions(U) * LCAND; }
 int zha_sel_ctr_words(int U) { return U * (1 + KSMAX); }
@@ -1831,6 +2227,17 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
   const int NT = uni_s ? (TSs * t->G + 15) / 16 : 1;  // column tiles of a scoring group
   const int rows = uni_s ? t->U * NTCs : U;             // rows of the scoring grid
   hipError_t e;
+  // Scores and scoring partials of consecutive levels live in different buffers, so a launch
+  // can read one level's while writing the next's: a level of at most WN nodes writes the
+  // small score buffer of its parity, a larger one the full buffer; partials alternate by
+  // parity.
+  auto sbuf = [&](int l) { return t->cap[l] <= WN ? t->sscore[l & 1] : t->scores; };
+  auto sstride = [&](int l) { return t->cap[l] <= WN ? (int64_t)WN : t->cap[1]; };
+  auto pbuf = [&](int l) { return t->spart[l & 1]; };
+  // Levels of at most WN nodes in routes of one-unit rows are selected by the next level's
+  // scoring launch (every workgroup selects them itself, from their scores and partials).
+  auto deferred = [&](int l) { return !uni_s && l > 1 && t->cap[l] <= WN; };
+  Level pvl;  // the previous (parent) level, for the next launch's selection of it
   for (int l = L; l >= 1; --l) {
     Level v;
     v.parent = l < L ? t->kept[l + 1] : nullptr;
@@ -1850,15 +2257,31 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     sa.ms = t->ms[l];
     sa.q = q;
     sa.capl = t->cap[l];
-    sa.scores = t->scores;
-    sa.cap1 = t->cap[1];
-    sa.part = t->spart;
+    sa.scores = sbuf(l);
+    sa.cap1 = sstride(l);
+    sa.part = pbuf(l);
+    const bool psel = l < L && deferred(l + 1);
+    if (psel) {
+      sa.pv = pvl;
+      sa.pscores = sbuf(l + 1);
+      sa.pstride = sstride(l + 1);
+      sa.pkept = t->kept[l + 1];
+      sa.pcapl = t->cap[l + 1];
+      sa.pnF_out = cntF + (int64_t)(l + 1) * U;
+      sa.pkept_count = cntK + (int64_t)(l + 1) * U;
+      sa.nF_out = cntF + (int64_t)l * U;
+    }
+    sa.p = p;
+    sa.keep_all = keep_all ? 1 : 0;
     if (uni_s) {
       int64_t w = (t->cap[l] + 7) / 8;
       const int wr = zha_score_wgs_units(rows);
       sa.W = (int)(w < 1 ? 1 : (w > wr ? wr : w));
     } else {
       sa.W = zha_score_wgs(t, l);
+      // every workgroup of a launch that selects the parent level pays for that selection:
+      // one round of resident workgroups (three per compute unit) pays it once
+      if (psel) sa.W = std::max(1, std::min(sa.W, 768 / U));
     }
     sa.krank = uni_s && l < L ? t->krank[l + 1] : nullptr;
     sa.route_ctr = (uni || uni_s) ? t->route_ctr : nullptr;
@@ -1871,26 +2294,48 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     sa.scale = scale;
     zha_time_begin(t, s, ZHA_K_SCORE, l);
     if (t->f8)
-      e = t->d == 64 ? launch_score_r<__bf16, 64, 1>(sa, t->R, sa.W, rows, uni_s, NT, s)
-                     : launch_score_r<__bf16, 128, 1>(sa, t->R, sa.W, rows, uni_s, NT, s);
+      e = t->d == 64 ? launch_score_r<__bf16, 64, 1>(sa, t->R, sa.W, rows, uni_s, NT, psel, s)
+                     : launch_score_r<__bf16, 128, 1>(sa, t->R, sa.W, rows, uni_s, NT, psel, s);
     else if (t->f4)
-      e = t->d == 64 ? launch_score_r<__bf16, 64, 2>(sa, t->R, sa.W, rows, uni_s, NT, s)
-                     : launch_score_r<__bf16, 128, 2>(sa, t->R, sa.W, rows, uni_s, NT, s);
+      e = t->d == 64 ? launch_score_r<__bf16, 64, 2>(sa, t->R, sa.W, rows, uni_s, NT, psel, s)
+                     : launch_score_r<__bf16, 128, 2>(sa, t->R, sa.W, rows, uni_s, NT, psel, s);
     else if (t->desc.dtype == ZHA_BF16)
-      e = t->d == 64 ? launch_score_r<__bf16, 64>(sa, t->R, sa.W, rows, uni_s, NT, s)
-                     : launch_score_r<__bf16, 128>(sa, t->R, sa.W, rows, uni_s, NT, s);
+      e = t->d == 64 ? launch_score_r<__bf16, 64>(sa, t->R, sa.W, rows, uni_s, NT, psel, s)
+                     : launch_score_r<__bf16, 128>(sa, t->R, sa.W, rows, uni_s, NT, psel, s);
     else
-      e = t->d == 64 ? launch_score_r<float, 64>(sa, t->R, sa.W, rows, uni_s, NT, s)
-                     : launch_score_r<float, 128>(sa, t->R, sa.W, rows, uni_s, NT, s);
+      e = t->d == 64 ? launch_score_r<float, 64>(sa, t->R, sa.W, rows, uni_s, NT, psel, s)
+                     : launch_score_r<float, 128>(sa, t->R, sa.W, rows, uni_s, NT, psel, s);
     if (e != hipSuccess) return e;
     zha_time_end(t, s, ZHA_K_SCORE, l);
+    pvl = v;
+    if (deferred(l)) continue;  // selected by the next level's scoring launch
 
+    if (!uni_s && t->cap[l] <= WN) {
+      WaveArgs wa;
+      wa.v = v;
+      wa.scores = sbuf(l);
+      wa.sstride = sstride(l);
+      wa.G = Gr;
+      wa.p = p;
+      wa.keep_all = keep_all ? 1 : 0;
+      wa.kept = t->kept[l];
+      wa.capl = t->cap[l];
+      wa.nF_out = cntF + (int64_t)l * U;
+      wa.kept_count = cntK + (int64_t)l * U;
+      wa.next_nF = next_nF;
+      zha_time_begin(t, s, ZHA_K_SELECT, l);
+      hipLaunchKernelGGL(zha_select_wave_kernel, dim3(U), dim3(SSEL), 0, s, wa);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      zha_time_end(t, s, ZHA_K_SELECT, l);
+      continue;
+    }
     if (t->cap[l] <= SMALL_NODES) {
       SmallArgs sm;
       sm.v = v;
-      sm.scores = t->scores;
-      sm.cap1 = t->cap[1];
-      sm.part = t->spart;
+      sm.scores = sbuf(l);
+      sm.cap1 = sstride(l);
+      sm.part = pbuf(l);
       sm.W = sa.W;
       sm.kept = t->kept[l];
       sm.capl = t->cap[l];
@@ -1920,9 +2365,9 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
     if (!keep_all) {
       MassArgs ma;
       ma.v = v;
-      ma.scores = t->scores;
-      ma.cap1 = t->cap[1];
-      ma.part = t->spart;
+      ma.scores = sbuf(l);
+      ma.cap1 = sstride(l);
+      ma.part = pbuf(l);
       ma.W = sa.W;
       ma.keys = t->keys;
       ma.kstride = t->kstride;

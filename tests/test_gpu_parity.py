@@ -472,6 +472,21 @@ def test_large_level_with_short_sequence():
         say(f" p={p}", r, a)
 
 
+def test_small_level_p_sweep():
+    """Every level of at most 1024 nodes (level 1 by its own selection launch, levels 2 and 3
+    by the next level's scoring launch) across many p: the crossing slice lands on heavier and
+    lighter candidates of every mass magnitude."""
+    cfg = small(batch=2, n_tokens=4096, chunk=4, levels=3, n_refs=16, n_queries=4, needles_per_unit=4)
+    say("case small-level p sweep: B=2 N=4096,3001 C=4 L=3 R=16 G=8, 40 values of p")
+    case = Case(cfg, lens=[4096, 3001], n_queries=4)
+    tree = case.tree()
+    amb = 0
+    for i, p in enumerate(np.linspace(0.02, 0.998, 40)):
+        r, a = full_check(case, tree, i % 4, float(p))
+        amb += r["ambiguous"]
+    say(f" 40 routes, {amb} ambiguous nodes in all")
+
+
 @pytest.mark.parametrize("N", [20000, 40000])
 def test_equal_masses_large_level(N):
     """All keys zero: every node of a 5000-node level (one-workgroup selection) or a
