@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include <algorithm>
@@ -435,11 +436,43 @@ size_t zha_dense_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_
   return (size_t)U * zha_dense_wgs(U) * (n_q_heads / n_kv_heads) * (head_dim + 2) * sizeof(float);
 }
 
-zha_status zha_dense_decode(const void* q, const void* K, const void* V, const int32_t* seq_lens, int32_t batch,
-                            int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int64_t max_tokens,
-                            zha_dtype dtype, float scale, float* out, float* lse, void* workspace,
-                            size_t workspace_bytes, hipStream_t s) {
-  if (!q || !K || !V || !seq_lens || !out || !lse || !workspace) return ZHA_ERR_INVALID;
+}  // extern "C"
+
+// Split-K partials of zha_dense_decode_noalloc: one array per GPU, held until the process
+// ends.  Host code never passes `scratch` itself to a kernel (on the host it names a
+// stand-in, not device memory): the device address is taken once per device with
+// hipGetSymbolAddress, with that device current, and kept in g_scratch.
+static __device__ __align__(256) float scratch[ZHA_DENSE_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+constexpr int ZHA_MAX_DEVICES = 256;
+std::mutex g_scratch_mu;
+void* g_scratch[ZHA_MAX_DEVICES];
+
+// The current device's address of `scratch` (taken on the first call on that device).
+zha_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail("zha_dense_decode_noalloc hipGetDevice", e);
+  if (dev < 0 || dev >= ZHA_MAX_DEVICES) return ZHA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail("zha_dense_decode_noalloc hipGetSymbolAddress", e);
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return ZHA_OK;
+}
+
+// Validation and launch of dense decode; workspace null: the partials go to the device's
+// scratch array (checked to fit before anything touches the device).
+zha_status dense_decode_impl(const void* q, const void* K, const void* V, const int32_t* seq_lens, int32_t batch,
+                             int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int64_t max_tokens,
+                             zha_dtype dtype, float scale, float* out, float* lse, void* workspace,
+                             size_t workspace_bytes, bool noalloc, hipStream_t s) {
+  if (!q || !K || !V || !seq_lens || !out || !lse || (!noalloc && !workspace)) return ZHA_ERR_INVALID;
   if (batch < 1 || n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads != 0 || max_tokens < 1)
     return ZHA_ERR_INVALID;
   if (dtype != ZHA_F32 && dtype != ZHA_BF16) return ZHA_ERR_INVALID;
@@ -447,8 +480,9 @@ zha_status zha_dense_decode(const void* q, const void* K, const void* V, const i
   if (batch > ZHA_MAX_BATCH || (head_dim != 64 && head_dim != 128) || n_q_heads / n_kv_heads > 16 ||
       max_tokens >= ((int64_t)1 << 31))
     return ZHA_ERR_UNSUPPORTED;
-  if (workspace_bytes < zha_dense_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, max_tokens))
-    return ZHA_ERR_INVALID;
+  const size_t need = zha_dense_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, max_tokens);
+  if (noalloc && need > ZHA_DENSE_SCRATCH_BYTES) return ZHA_ERR_CAPACITY;
+  if (!noalloc && workspace_bytes < need) return ZHA_ERR_INVALID;
   ZLens len;
   memset(&len, 0, sizeof(len));
   for (int b = 0; b < batch; ++b) {
@@ -456,11 +490,34 @@ zha_status zha_dense_decode(const void* q, const void* K, const void* V, const i
     if ((int64_t)seq_lens[b] > max_tokens) return ZHA_ERR_CAPACITY;
     len.n[b] = seq_lens[b];
   }
+  if (noalloc) {
+    const zha_status st = scratch_address(&workspace);
+    if (st != ZHA_OK) return st;
+  }
   const int U = batch * n_kv_heads;
   hipError_t e = zha_launch_dense(q, K, V, len, batch, n_q_heads, n_kv_heads, head_dim, max_tokens, dtype, scale,
                                   out, lse, (float*)workspace, zha_dense_wgs(U), s);
-  if (e != hipSuccess) return hip_fail("zha_dense_decode launch", e);
+  if (e != hipSuccess) return hip_fail(noalloc ? "zha_dense_decode_noalloc launch" : "zha_dense_decode launch", e);
   return ZHA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+zha_status zha_dense_decode(const void* q, const void* K, const void* V, const int32_t* seq_lens, int32_t batch,
+                            int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim, int64_t max_tokens,
+                            zha_dtype dtype, float scale, float* out, float* lse, void* workspace,
+                            size_t workspace_bytes, hipStream_t s) {
+  return dense_decode_impl(q, K, V, seq_lens, batch, n_q_heads, n_kv_heads, head_dim, max_tokens, dtype, scale, out,
+                           lse, workspace, workspace_bytes, false, s);
+}
+
+zha_status zha_dense_decode_noalloc(const void* q, const void* K, const void* V, const int32_t* seq_lens,
+                                    int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                    int64_t max_tokens, zha_dtype dtype, float scale, float* out, float* lse,
+                                    hipStream_t s) {
+  return dense_decode_impl(q, K, V, seq_lens, batch, n_q_heads, n_kv_heads, head_dim, max_tokens, dtype, scale, out,
+                           lse, nullptr, 0, true, s);
 }
 
 zha_status zha_tree_level_capacity(zha_tree_t t, int32_t level, int64_t* nodes) {

@@ -76,6 +76,8 @@ def load():
             "zha_dense_decode": (st, [vp, vp, vp, _i32p, c_int32, c_int32, c_int32, c_int32, c_int64, c_int,
                                       c_float, vp, vp, vp, c_size_t, vp]),
             "zha_dense_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32, c_int32, c_int64]),
+            "zha_dense_decode_noalloc": (st, [vp, vp, vp, _i32p, c_int32, c_int32, c_int32, c_int32, c_int64, c_int,
+                                              c_float, vp, vp, vp]),
             "zha_tree_level_capacity": (st, [vp, c_int32, POINTER(c_int64)]),
             "zha_tree_copy_level": (st, [vp, c_int32, vp, vp, vp]),
             "zha_tree_copy_scales": (st, [vp, c_int32, vp, vp]),
@@ -197,6 +199,16 @@ def zha_dense_decode(q, K, V, seq_lens, batch, n_q_heads, n_kv_heads, head_dim, 
     _check(load().zha_dense_decode(_ptr(q), _ptr(K), _ptr(V), _lens(seq_lens), batch, n_q_heads, n_kv_heads,
                                    head_dim, max_tokens, dtype, float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
                                    int(workspace_bytes), _stream(stream)), "zha_dense_decode")
+
+
+ZHA_DENSE_SCRATCH_BYTES = 8 << 20
+
+
+def zha_dense_decode_noalloc(q, K, V, seq_lens, batch, n_q_heads, n_kv_heads, head_dim, max_tokens, dtype, scale, out,
+                             lse, stream=None) -> None:
+    _check(load().zha_dense_decode_noalloc(_ptr(q), _ptr(K), _ptr(V), _lens(seq_lens), batch, n_q_heads, n_kv_heads,
+                                           head_dim, max_tokens, dtype, float(scale), _ptr(out), _ptr(lse),
+                                           _stream(stream)), "zha_dense_decode_noalloc")
 
 
 def zha_tree_level_capacity(tree: int, level: int) -> int:

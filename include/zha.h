@@ -261,6 +261,24 @@ ZHA_API zha_status zha_dense_decode(const void* q, const void* K, const void* V,
 ZHA_API size_t zha_dense_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                  int32_t head_dim, int64_t max_tokens);
 
+/* zha_dense_decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels and
+ * results, with the split-K partials in a fixed array of ZHA_DENSE_SCRATCH_BYTES bytes that
+ * the library holds on each GPU it runs on until the process ends (its device address is
+ * taken on the first call on that GPU).  No device memory is allocated or freed by any
+ * call.  Shapes whose partials need more than the array
+ * (zha_dense_workspace_bytes(...) > ZHA_DENSE_SCRATCH_BYTES) are rejected before anything
+ * is enqueued.  Every call on one GPU uses the same array: calls that overlap on a GPU
+ * (other streams, other host threads) race and must be serialised by the caller.
+ * Errors: as zha_dense_decode; ZHA_ERR_CAPACITY also for shapes beyond the array;
+ * ZHA_ERR_HIP when the array's address cannot be obtained. */
+#define ZHA_DENSE_SCRATCH_BYTES ((size_t)8 << 20)
+ZHA_API zha_status zha_dense_decode_noalloc(const void* q, const void* K, const void* V,
+                                    const int32_t* seq_lens /* host [B] */,
+                                    int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int32_t head_dim, int64_t max_tokens, zha_dtype dtype,
+                                    float scale, float* out, float* lse, hipStream_t stream);
+
 /* ---- inspection (tests and benchmarks) -------------------------------- */
 
 /* Node capacity of a level (per unit): ceil(C*floor(max_tokens/C) / C^level). */

@@ -93,6 +93,23 @@ def test_null_arguments_rejected():
     assert lib.zha_calibration_copy(16, 24, 1, None) == zha.ZHA_ERR_INVALID  # misaligned
 
 
+def test_dense_noalloc_rejects_oversized_shapes_on_host():
+    """Shapes whose partials exceed the library's fixed array are refused before the device
+    is touched (this runs without a GPU)."""
+    fake = 1 << 40  # never dereferenced
+    # 64 sequences x 64 KV heads x 16 query heads each: far beyond ZHA_DENSE_SCRATCH_BYTES
+    need = zha.zha_dense_workspace_bytes(64, 1024, 64, 128, 1000)
+    assert need > zha.ZHA_DENSE_SCRATCH_BYTES
+    with pytest.raises(zha.ZhaError) as ei:
+        zha.zha_dense_decode_noalloc(fake, fake, fake, [100] * 64, 64, 1024, 64, 128, 1000, zha.ZHA_BF16, 1.0, fake,
+                                     fake, stream=0)
+    assert ei.value.status == zha.ZHA_ERR_CAPACITY
+    with pytest.raises(zha.ZhaError) as ei:  # ordinary validation first, as for zha_dense_decode
+        zha.zha_dense_decode_noalloc(0, fake, fake, [100], 1, 32, 4, 128, 1000, zha.ZHA_BF16, 1.0, fake, fake,
+                                     stream=0)
+    assert ei.value.status == zha.ZHA_ERR_INVALID
+
+
 def test_dense_validation_on_host():
     lens = [100]
     ws = zha.zha_dense_workspace_bytes(1, 32, 4, 128, 1000)
