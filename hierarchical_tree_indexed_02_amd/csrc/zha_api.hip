@@ -19,7 +19,7 @@ int zha_hist_bins();
 int64_t zha_sel_cand_entries(int U);
 int zha_sel_ctr_words(int U);
 size_t zha_spine_bytes(int L, int d, int R);
-size_t zha_build_lds_bytes(int S, int L, int d, int R, int esize);
+size_t zha_build_lds_bytes(int C, int S, int L, int d, int R, int esize);
 
 namespace {
 
@@ -70,7 +70,8 @@ zha_status check_desc(const zha_tree_desc* d) {
   double span = pow((double)d->chunk, (double)d->levels);
   if (span > (double)(1 << 30)) return ZHA_ERR_UNSUPPORTED;
   const int esize = d->dtype == ZHA_BF16 ? 2 : 4;
-  if (zha_build_lds_bytes(subtree_level(d->chunk, d->levels), d->levels, d->head_dim, d->n_refs, esize) > 160 * 1024)
+  if (zha_build_lds_bytes(d->chunk, subtree_level(d->chunk, d->levels), d->levels, d->head_dim, d->n_refs, esize) >
+      160 * 1024)
     return ZHA_ERR_UNSUPPORTED;
   return ZHA_OK;
 }

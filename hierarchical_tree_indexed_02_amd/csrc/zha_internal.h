@@ -111,15 +111,17 @@ __device__ __forceinline__ float fp8_value(uint32_t c) {
   return (c & 0x80u) ? -v : v;
 }
 
-// Sum over the 16 lanes of a DPP row (xor butterfly: every lane ends with the same bits).
 // Sum over each row of 16 lanes, the total left in every lane of the row, with four
 // DPP adds (data-parallel-primitive lane moves within a row, no LDS round trip): swap
 // neighbours, swap pairs (each lane then holds its quad's sum), add the half-row mirror
 // (lanes i and 7-i: each lane holds its 8-lane half's sum), add the row mirror (lanes i
-// and 15-i).  Fixed order: every caller gets the same bits for the same inputs.
+// and 15-i).  Fixed order: every caller gets the same bits for the same inputs.  Every
+// source lane of these four patterns lies in the row, so bound_ctrl (zero for a lane with
+// no source) never applies; it lets the compiler fold each move into the add or max that
+// uses it (v_add_f32_dpp).
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 __device__ __forceinline__ float sum16(float x) {
   x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
@@ -156,7 +158,7 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, true);
 }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
   x = min(x, dpp_u32<0xB1>(x));
@@ -289,7 +291,7 @@ struct zha_tree {
   int UGmax;                        // union groups the workspace is sized for
   bool uni_route;                   // the last route ran the union kernels
   float* refs;                      // [Hkv][R][d]
-  float* spine;                     // [U][L+1][R*16][E+2] open-node accumulators
+  float* spine;                     // [U][L+1] open-node accumulators (layout of the build path)
   int S;                            // subtree level of the build (highest level of <= 256 tokens)
   float* sub_lse;                   // [U][cap_S][R] fp32 LSE of finished level-S nodes (S < L only)
   float* sub_m;                     // [U][cap_S][R][d] fp32 means of finished level-S nodes
