@@ -63,9 +63,9 @@ def parse():
                     help="skip the extra pass that routes every query head alone (reported beside the headline)")
     ap.add_argument("--workloads", default=",".join(SUB_WORKLOADS),
                     help="comma-separated workloads measured after the headline as sub-records ('' for none)")
-    ap.add_argument("--sweep", action="store_true",
-                    help="also time the workload's inputs under other tree geometries (C, L, R) and p, and fit a "
-                         "step-time model (bytes at the measured bandwidths + a fixed cost per routing level)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip timing the headline inputs under other tree geometries (C, L, R) and p against the "
+                         "step model")
     return ap.parse_args()
 
 
@@ -119,18 +119,91 @@ def pct(xs, q):
     return float(np.percentile(np.asarray(xs, dtype=np.float64), q)) if len(xs) else None
 
 
-# Tree geometries (chunk C, levels L, references R) over the same 256K-token inputs: C^L = 4096
-# tokens per top node except where noted, and the flat C = 256 tree.
-SWEEP = [(4, 6, 16, 0.95), (4, 6, 4, 0.95), (4, 6, 1, 0.95), (4, 6, 16, 0.7), (8, 4, 16, 0.95), (8, 4, 4, 0.95),
-         (16, 3, 16, 0.95), (16, 3, 4, 0.95), (64, 2, 16, 0.95), (4, 5, 16, 0.95), (256, 1, 16, 0.95),
-         (256, 1, 4, 0.95), (256, 1, 16, 0.7)]
+# Tree geometries (chunk C, levels L, references R, p) over the same 256K-token inputs: every R
+# and p of the pages' sweep on the deep C = 4, L = 6 tree, and trees of other C and L (C^L =
+# 4096 tokens per top node, 1024 for C = 4, L = 5, the flat C = 256 tree) at R = 16, p = 0.95.
+SWEEP = [(4, 6, R, p) for R in (16, 4, 2, 1) for p in (0.95, 0.7, 0.9, 0.99)] + \
+    [(8, 4, 16, 0.95), (16, 3, 16, 0.95), (64, 2, 16, 0.95), (4, 5, 16, 0.95), (256, 1, 16, 0.95)]
+
+
+def level_caps(N, C, L):
+    """Nodes per unit at each level 1..L of a tree over N tokens."""
+    Nc = (N // C) * C
+    return [-(-Nc // C ** l) for l in range(1, L + 1)]
+
+
+def level_kind(l, cap):
+    """How the route selects a level: inside the next level's scoring launch (fused), in a
+    one-workgroup launch (wave: level 1 of <= 1024 nodes; small: <= 8192), or with the
+    many-workgroup mass and compaction launches (large)."""
+    if cap > 8192:
+        return "large"
+    if cap <= 1024:
+        return "fused" if l > 1 else "wave"
+    return "small"
+
+
+def launches(caps):
+    """Launches of one group route + attend: a scoring launch per level, the selection launches
+    of each level by kind, attention and merge."""
+    n = len(caps) + 2
+    for l in range(1, len(caps) + 1):
+        n += {"fused": 0, "wave": 1, "small": 1, "large": 3}[level_kind(l, caps[l - 1])]
+    return n
+
+
+def model_constants(res, caps, bw):
+    """Constants of the step model, measured at one geometry (res: its measure() record with
+    the per-launch times of the stage-breakdown pass; bw: bytes per microsecond of dense
+    decode on the same GPU and inputs) -- not fitted:
+      delta     how much an event-timed launch overstates its share of the step: (sum of the
+                launch times - the step time) / launches;
+      t_wave    one worker wave of a scoring launch: the top level's launch, whose few nodes
+                leave every workgroup one super-tile (a launch takes at least this long);
+      c_fused   selection of a small level inside the next level's scoring launch: the time
+                those launches take beyond their own scoring;
+      c_small   the one-workgroup selection launch; c_large: selection, mass and compaction of a
+                large level;
+      c_attend  attention and merge beyond streaming the attended bytes."""
+    k = {n: v["avg_us"] for n, v in res["kernels"].items()}
+    L = len(caps)
+    Bl = res["route_bytes_l"]
+    delta = (sum(k.values()) - res["ms_step"] * 1e3) / launches(caps)
+    t_wave = k[f"score_l{L}"] - delta
+    fused = [l for l in range(1, L) if level_kind(l + 1, caps[l]) == "fused"]
+    c_fused = (sum(k[f"score_l{l}"] - delta - max(t_wave, Bl[l] / bw) for l in fused) / len(fused)) if fused else 0.0
+    small = [l for l in range(1, L + 1) if level_kind(l, caps[l - 1]) == "small"]
+    large = [l for l in range(1, L + 1) if level_kind(l, caps[l - 1]) == "large"]
+    c_small = sum(k.get(f"select_l{l}", 0.0) - delta for l in small) / len(small) if small else 0.0
+    c_large = (sum(k.get(f"mass_l{l}", 0.0) + k.get(f"select_l{l}", 0.0) + k.get(f"compact_l{l}", 0.0) - 3 * delta
+                   for l in large) / len(large)) if large else 0.0
+    c_attend = k.get("attend", 0.0) + k.get("merge", 0.0) - 2 * delta - res["attend_bytes"] / bw
+    return dict(bw_gbs=round(bw * 1e-3, 1), delta_us=round(delta, 2), t_wave_us=round(t_wave, 2),
+                c_fused_us=round(c_fused, 2), c_small_us=round(c_small, 2), c_large_us=round(c_large, 2),
+                c_attend_us=round(c_attend, 2))
+
+
+def model_step(row, m):
+    """Step time of one geometry from the four segments of the pages' model: build (none in a
+    decode step without growth), per-level routing (each level's scoring launch streams its
+    plane bytes at the dense bandwidth but takes at least one worker wave), node scan (each
+    level's selection, by kind) and attention (the attended K/V bytes at the dense bandwidth
+    plus its fixed time).  Returns the total and the segments in microseconds."""
+    bw = m["bw_gbs"] * 1e3  # bytes per microsecond
+    caps = row["caps"]
+    route = sum(max(m["t_wave_us"], b / bw) for b in row["route_bytes_l"].values())
+    scan = 0.0
+    for l in range(1, len(caps) + 1):
+        kind = level_kind(l, caps[l - 1])
+        scan += {"fused": m["c_fused_us"], "wave": m["t_wave_us"] + m["c_fused_us"], "small": m["c_small_us"],
+                 "large": m["c_large_us"]}[kind]
+    attend = row["attend_bytes"] / bw + m["c_attend_us"]
+    return route + scan + attend, dict(route=round(route, 1), scan=round(scan, 1), attend=round(attend, 1))
 
 
 def geometry_sweep(measure, cfg, zi, torch, np, dev, N, B, Hkv, d, es, log):
-    """Times route + attend under each geometry of SWEEP and fits
-        t_step = route_bytes / BW_route + attend_bytes / BW_attend + n_small * c_small + n_large * c_large + c0
-    by least squares (n_small / n_large: routing levels of at most / more than 8192 nodes
-    per unit); returns one record per geometry with the fitted prediction."""
+    """Times route + attend under each geometry of SWEEP on the workload's inputs; returns one
+    record per geometry (the step model's prediction is added once dense decode is timed)."""
     rows = []
     for C, L, R, p in SWEEP:
         if C ** L > N:
@@ -139,32 +212,83 @@ def geometry_sweep(measure, cfg, zi, torch, np, dev, N, B, Hkv, d, es, log):
         refs = torch.from_numpy(zi.refs(g)).to(dev)
         log(f"-- geometry C={C} L={L} R={R} p={p}")
         r = measure("native", "group", C=C, L=L, R=R, refs=refs, p=p)
-        caps = [-(-((N // C) * C) // C ** l) for l in range(1, L + 1)]
-        n_small = sum(1 for c in caps if c <= 8192)
-        kern = r["kernels"]
-        route_us = sum(v["avg_us"] for k, v in kern.items() if k.split("_l")[0] in ("score", "select", "mass", "compact"))
-        att_us = kern.get("attend", {}).get("avg_us", 0.0)
-        S_node = R * (d * es + 4)
-        route_bytes = sum(r["fr_tot"].values()) * S_node / r["nsteps"]
+        caps = level_caps(N, C, L)
         rows.append(dict(C=C, L=L, R=R, p=p, us_per_step=round(r["ms_step"] * 1e3, 2),
-                         step_bytes=round(r["step_bytes"]), route_bytes=round(route_bytes),
-                         attend_bytes=round(r["step_bytes"] - route_bytes), kappa=round(r["kappa"], 4),
-                         route_us=round(route_us, 1), attend_us=round(att_us, 1), small_levels=n_small,
-                         large_levels=L - n_small, tree_bytes=r["tree_bytes"]))
-    X = np.array([[x["route_bytes"] / 1e9, x["attend_bytes"] / 1e9, x["small_levels"], x["large_levels"], 1.0]
-                  for x in rows])
-    y = np.array([x["us_per_step"] for x in rows])
-    coef, *_ = np.linalg.lstsq(X, y, rcond=None)
-    for x, pred in zip(rows, X @ coef):
-        x["model_us"] = round(float(pred), 1)
-    fit = dict(us_per_GB_route=round(float(coef[0]), 2), us_per_GB_attend=round(float(coef[1]), 2),
-               us_per_small_level=round(float(coef[2]), 2), us_per_large_level=round(float(coef[3]), 2),
-               us_fixed=round(float(coef[4]), 2))
-    log("geometry sweep fit: " + ", ".join(f"{k} {v}" for k, v in fit.items()))
+                         median_us=round(r["median_us"], 2), step_bytes=round(r["step_bytes"]),
+                         route_bytes_l={str(l): round(v) for l, v in r["route_bytes_l"].items()},
+                         attend_bytes=round(r["attend_bytes"]), kappa=round(r["kappa"], 4), caps=caps,
+                         levels_by_kind={kd: sum(1 for l in range(1, L + 1) if level_kind(l, caps[l - 1]) == kd)
+                                         for kd in ("fused", "wave", "small", "large")},
+                         kernels={k: round(v["avg_us"], 2) for k, v in r["kernels"].items()},
+                         tree_bytes=r["tree_bytes"]))
+    return rows
+
+
+def sweep_model(rows, consts, log):
+    """Adds the step model's prediction to every geometry; returns the summary record."""
+    worst = 0.0
     for x in rows:
-        log(f"  C={x['C']:3d} L={x['L']} R={x['R']:2d} p={x['p']}: {x['us_per_step']:8.1f} us (model {x['model_us']:8.1f}), "
-            f"kappa {x['kappa']:.3f}, route {x['route_bytes'] / 1e6:7.1f} MB, attend {x['attend_bytes'] / 1e6:6.1f} MB")
-    return dict(fit=fit, rows=rows)
+        pred, segs = model_step(x, consts)
+        x["model_us"] = round(pred, 1)
+        x["model_segments_us"] = segs
+        x["model_err"] = round(pred / x["us_per_step"] - 1.0, 4)
+        worst = max(worst, abs(x["model_err"]))
+        log(f"  C={x['C']:3d} L={x['L']} R={x['R']:2d} p={x['p']}: {x['us_per_step']:8.1f} us, model {pred:8.1f} "
+            f"({100 * x['model_err']:+.1f}%), kappa {x['kappa']:.3f}")
+    log(f"step model: {consts}; worst error {100 * worst:.1f}%")
+    return dict(constants=consts, worst_abs_err=round(worst, 4), rows=rows)
+
+
+NEAR = 1e-4  # a node is near the cut when its log mass, or the cumulative mass at the cut, is this close
+
+
+def near_cut_counts(tree, torch, q, p, scale, C, L, lens, Hkv, G):
+    """Nodes near each level's cut in the last group route of q [B][Hq][d]: from the tree's
+    stored planes, each frontier node's mass (its per-head softmax over the frontier of the
+    scores max_r (b_r + q.m~_r), averaged over the group's heads) in fp64, ordered by mass
+    against the route's own kept count k; counted are the nodes whose log mass lies within
+    NEAR of the k-th or (k+1)-th node's, and those two when the cumulative mass there lies
+    within NEAR of p.  These are the decisions that fp32 arithmetic (the kernels) and fp64
+    (the oracle) may take differently.  Returns ({level: count}, frontier nodes)."""
+    counts, nodes = {}, 0
+    qf = q.double() * scale
+    kept_prev = None
+    for l in range(L, 0, -1):
+        nf, nk, ids = tree.route_level(l)
+        m_all, b_all = tree.level(l)
+        c_l = 0
+        kept_now = []
+        for b, N in enumerate(lens):
+            Nc = (N // C) * C
+            n_l = -(-Nc // C ** l)
+            for g in range(Hkv):
+                u = b * Hkv + g
+                if l == L:
+                    F = torch.arange(n_l, device=ids.device)
+                else:
+                    par = kept_prev[u]
+                    F = (par[:, None] * C + torch.arange(C, device=ids.device)[None, :]).reshape(-1)
+                    F = F[F < n_l]
+                k = int(nk[u])
+                kept_now.append(ids[u, :k].long())
+                nodes += len(F)
+                if len(F) == 0 or k <= 0 or k >= len(F) or p >= 1.0:
+                    continue
+                mF = m_all[u, F].double()                      # [F][R][d]
+                bF = b_all[u, F].double()                      # [F][R]
+                qh = qf[b, g * G:(g + 1) * G]                  # [G][d]
+                s_ = (torch.einsum("frd,hd->hfr", mF, qh) + bF[None]).amax(dim=2)  # [G][F]
+                w = torch.exp(s_ - torch.logsumexp(s_, dim=1, keepdim=True)).mean(dim=0)
+                order = torch.argsort(w, descending=True)
+                lw = torch.log(w)
+                near = (torch.abs(lw - lw[order[k - 1]]) < NEAR) | (torch.abs(lw - lw[order[k]]) < NEAR)
+                cs = torch.cumsum(w[order], 0) / w.sum()
+                c_prev = float(cs[k - 2]) if k >= 2 else -1.0
+                extra = 2 if min(abs(c_prev - p), abs(float(cs[k - 1]) - p)) < NEAR else 0
+                c_l += int(near.sum()) + extra
+        counts[l] = c_l
+        kept_prev = kept_now
+    return counts, nodes
 
 
 def union_counts(tree, L, C, hr, Tq, Hkv, lens, qtail):
@@ -345,7 +469,7 @@ def run_workload(cfg, args, env, headline, layers):
                     block_gbs=round(nbytes / (us * 1e-6) / 1e9, 1), kappa=round(tok / (U * (Nb + Tq)), 4),
                     kernels={k: round(v["avg_us"], 2) for k, v in kernels.items()})
 
-    def measure(summary, mode="group", C=C, L=L, R=R, refs=refs, p=p, warm=False):
+    def measure(summary, mode="group", C=C, L=L, R=R, refs=refs, p=p, warm=False, near_cut=False):
         """Builds one tree per layer replica with the given m storage (and geometry C, L, R),
         times the stage breakdown and the K-step region, and replays the routes for the
         byte counts.  warm: every step reads layer 0 with query 0 (its data partly cached)."""
@@ -478,10 +602,15 @@ def run_workload(cfg, args, env, headline, layers):
         kept_tot = {l: 0 for l in range(1, L + 1)}
         attend_tok = 0
         steps_q = [0 if warm else i % nq for i in range(args.steps)]
+        near = [] if near_cut and mode == "group" else None
         for t in sorted(set(steps_q)):
             w = steps_q.count(t)
             trees[0].route(qd[t], p, 1.0, mode=mode)
             torch.cuda.synchronize()
+            if near is not None and len(near) < 4:  # the first four distinct queries
+                cnt, nod = near_cut_counts(trees[0], torch, qd[t], p, 1.0, C, L, layer_lens[0], Hkv, G)
+                near.append(dict(query=t, near_cut=sum(cnt.values()), by_level={str(k): v for k, v in cnt.items()},
+                                 frontier_nodes=nod))
             ufr, utok, frs, kps = union_counts(trees[0], L, C, hr, 1, Hkv, layer_lens[0], False)
             if hr == 1 and ufr != frs:
                 raise RuntimeError(f"frontier recount {ufr} disagrees with the route's counts {frs}")
@@ -531,11 +660,14 @@ def run_workload(cfg, args, env, headline, layers):
         torch.cuda.empty_cache()
         return dict(ms_step=ms_step, step_bytes=step_bytes, kappa=kappa, kernels=kernels, roofline=roofline,
                     seg_us=seg_mean, fr_tot=fr_tot, build_ms=build_ms, tree_bytes=tree_bytes, layer_lens=layer_lens,
-                    dense_bytes=dense_bytes, nsteps=nsteps, median_us=pct(per_step, 50), p90_us=pct(per_step, 90))
+                    dense_bytes=dense_bytes, nsteps=nsteps, median_us=pct(per_step, 50), p90_us=pct(per_step, 90),
+                    route_bytes_l={l: fr_tot[l] * S_node / nsteps for l in fr_tot}, attend_bytes=attend_bytes,
+                    near_cut=near)
 
+    sweep_rows = None
     summary = args.summary if headline else "native"
     log(f"== {cfg.name}: B={B} N={N} {Hq}q/{Hkv}kv d={d} C={C} L={L} R={R} p={p_sweep} ({layers} layer replicas)")
-    res = measure(summary)
+    res = measure(summary, near_cut=True)
     ms_step, step_bytes, kappa, kernels = res["ms_step"], res["step_bytes"], res["kappa"], res["kernels"]
     layer_lens, dense_bytes, nsteps = res["layer_lens"], res["dense_bytes"], res["nsteps"]
     rec = {
@@ -550,6 +682,7 @@ def run_workload(cfg, args, env, headline, layers):
         "kappa": round(kappa, 4),
         "frontier_per_unit": {l: round(res["fr_tot"][l] / nsteps / U, 1) for l in range(L, 0, -1)},
         "build_us": round(1e3 * float(np.median(res["build_ms"])), 1),
+        "near_cut_per_step": res["near_cut"],
         "tree_bytes": res["tree_bytes"],
         "kernels": {k: dict(launches=v["launches"], avg_us=round(v["avg_us"], 2)) for k, v in kernels.items()},
         "config": {"workload": cfg.name, "batch": B, "context": N, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
@@ -580,8 +713,8 @@ def run_workload(cfg, args, env, headline, layers):
                                           for x in p_sweep}
         for sm, v in low.items():
             rec[f"{sm}_summaries"] = v
-        if args.sweep and not growing:
-            rec["geometry_sweep"] = geometry_sweep(measure, cfg, zi, torch, np, dev, N, B, Hkv, d, es, log)
+        if not args.no_sweep and not growing:
+            sweep_rows = geometry_sweep(measure, cfg, zi, torch, np, dev, N, B, Hkv, d, es, log)
         if not args.no_per_head and args.summary == "native":
             log("-- the same workload, every query head routed alone")
             rh = measure("native", mode="per_head")
@@ -623,6 +756,11 @@ def run_workload(cfg, args, env, headline, layers):
         rec["dense_us_per_step"] = round(dense_us, 2)
         rec["dense_median_us"] = round(dense_med, 2)
         rec["speedup_vs_dense"] = round(dense_us / (ms_step * 1e3), 3)
+        if sweep_rows:
+            log("-- geometry sweep against the step model (bandwidth of dense decode; constants measured here)")
+            bw = dense_bytes / dense_us  # bytes per microsecond
+            consts = model_constants(res, level_caps(N, C, L), bw)
+            rec["geometry_sweep"] = sweep_model(sweep_rows, consts, log)
     del Ks, Vs, outs, lses
     torch.cuda.empty_cache()
     return rec

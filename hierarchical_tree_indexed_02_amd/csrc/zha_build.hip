@@ -730,9 +730,13 @@ template <int E> __device__ __forceinline__ void round_bf16(const float (&m)[E],
     mt[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
   }
 }
+// Streaming (nontemporal) stores: a tree is written once and read by later routes, so its
+// lines need not stay in the caches on the way out.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 template <int E> __device__ __forceinline__ void store_words(__bf16* p, const uint32_t (&w)[E / 2]) {
-  if constexpr (E == 8) *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
-  else *(uint2*)p = make_uint2(w[0], w[1]);
+  if constexpr (E == 8) __builtin_nontemporal_store(u32x4_t{w[0], w[1], w[2], w[3]}, (u32x4_t*)p);
+  else __builtin_nontemporal_store(u32x2_t{w[0], w[1]}, (u32x2_t*)p);
 }
 // This lane's part of r.m~ (the row's 16 lanes are summed by sum16).
 template <int E> __device__ __forceinline__ float dot_part(const float (&rv)[E], const float (&mt)[E]) {
@@ -764,7 +768,7 @@ __device__ __forceinline__ void emit_row(const BuildArgs& a, int u, int l, int64
   round_bf16<E>(m, w, mt);
   store_words<E>((__bf16*)a.m[l] + row * D + E * c, w);
   const float s = sum16(dot_part<E>(rv, mt));
-  if (c == 0) a.b[l][row] = lse - s;
+  if (c == 0) __builtin_nontemporal_store(lse - s, a.b[l] + row);
 }
 
 // This lane's reference slices R[4 g + v][E c .. E c + E] in registers.
@@ -799,7 +803,7 @@ __device__ __forceinline__ void emit4(const BuildArgs& a, int u, int l, int64_t 
   for (int v = 0; v < 4; ++v) dot[v] = sum16(dot[v]);
   if (c < 4 && 4 * g + c < a.R) {
     const float bv = c == 0 ? lse[0] - dot[0] : c == 1 ? lse[1] - dot[1] : c == 2 ? lse[2] - dot[2] : lse[3] - dot[3];
-    a.b[l][row0 + c] = bv;
+    __builtin_nontemporal_store(bv, a.b[l] + row0 + c);
   }
 }
 
