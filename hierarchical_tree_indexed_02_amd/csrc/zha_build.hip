@@ -7,7 +7,10 @@
 // so the plane b_r + q.m~_r is exact at q = r for the stored values.  Leaves
 // cover C raw tokens; a parent is the exact log-sum-exp combination of its C
 // children's fp32 (LSE, mean) ([aitop] abstract: recursively compressed key
-// summaries).  The build runs in two kernels.  zha_build_subtree_kernel: one
+// summaries).  Trees of bf16 keys with C = 4 are built by the matrix-core kernels of
+// the section below (zha_build_c4_kernel and its upper-level and append kernels); every
+// other tree by the per-thread kernels described here, in two kernels.
+// zha_build_subtree_kernel: one
 // workgroup per node of the subtree level S (the highest level covering at most
 // 256 tokens) streams that node's tokens in order, four tokens ahead of use:
 // tokens fold into the leaf accumulator (registers), each finished leaf folds

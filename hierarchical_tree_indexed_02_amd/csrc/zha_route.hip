@@ -13,6 +13,12 @@
 //                       HBM once and score them on the matrix cores (G query heads x
 //                       R planes per node is a small dense product), and write the
 //                       per-workgroup (max, sum exp) partials of each head's scores.
+//   levels of <= 1024 nodes: selected by the next level's scoring launch, every one of
+//                       whose workgroups first repeats the selection (a 256-thread block:
+//                       LSE per head, keys, a histogram, the crossing bin ranked by one
+//                       wave, ordered compaction) from the scores, then scores its share of
+//                       the frontier that selection defines; level 1 of that size takes
+//                       zha_select_wave_kernel, the same selection in its own launch.
 //   levels of <= 8192 nodes: zha_select_small_kernel, one workgroup per unit,
 //                       forms the node masses, finds the exact cut and compacts, in LDS.
 //   large frontiers:    zha_mass_kernel (many workgroups) forms the masses and an exact
@@ -30,8 +36,6 @@
 #include "zha_internal.h"
 
 namespace {
-
-
 
 constexpr int NB = 1024;                 // histogram slices
 constexpr int SMALL_NODES = 8192;        // frontiers up to this size are selected in one workgroup
