@@ -626,6 +626,53 @@ def test_append_equals_rebuild(dtype, summary):
     say(" ", r, a)
 
 
+# Shapes of the matrix-core build (bf16 keys, C = 4): references that fill only part of a
+# lane group (R = 1, 2), both head dimensions, trees of one level and of five to seven (the
+# upper-level kernel), fp8 and fp4 summaries, and lengths whose last 64-leaf workgroup is
+# partial, exactly full, or the only one; appends cross leaf, level-2, level-3 and level-4
+# boundaries.
+C4_SHAPES = [
+    ("d128 R1 L6", dict(n_refs=1, levels=6), [4100, 3072, 257], "native"),
+    ("d64 R2 L5", dict(n_refs=2, levels=5, head_dim=64), [6001, 4160, 63], "native"),
+    ("d128 R8 L1", dict(n_refs=8, levels=1), [1001, 6], "native"),
+    ("d64 R16 L6 fp8", dict(n_refs=16, levels=6, head_dim=64), [5000], "fp8"),
+    ("d128 R4 L7 fp4", dict(n_refs=4, levels=7), [20000, 16387], "fp4"),
+]
+
+
+@pytest.mark.parametrize("label,kw,lens,summary", C4_SHAPES, ids=[v[0] for v in C4_SHAPES])
+def test_c4_build_shapes(label, kw, lens, summary):
+    B = len(lens)
+    cfg = small(batch=B, n_tokens=max(lens), chunk=4, n_q_heads=8, n_kv_heads=2, n_queries=2, needles_per_unit=4,
+                append_steps=300, **kw)
+    say(f"case C=4 build {label} ({summary} summaries): lens={lens}")
+    case = Case(cfg, lens=lens, max_tokens=max(lens) + 300)
+    tree = case.tree(summary=summary)
+    torch.cuda.synchronize()
+    say(" build", check_build(case, tree, sample=None if sum(lens) < 12000 else 128))
+    rows = {(b, g): zi.append_rows(cfg, b, g) for b in range(B) for g in range(cfg.n_kv_heads)}
+    cur = list(case.lens)
+    done = 0
+    for k in (1, 3, 4, 60, 1, 200, 31):
+        for b in range(B):
+            for g in range(cfg.n_kv_heads):
+                Kr, Vr = rows[(b, g)]
+                case.add_rows(b, g, cur[b], Kr[done:done + k], Vr[done:done + k])
+        cur = [n + k for n in cur]
+        tree.append(case.Kd, cur)
+        done += k
+    case.lens = cur
+    full = case.tree(summary=summary)
+    torch.cuda.synchronize()
+    _valid_equal(case, tree, full)
+    say(" appended tree bitwise equal to a rebuild; lens", cur)
+    say(" build after appends", check_build(case, tree, sample=64))
+    r, a = full_check(case, tree, 0, 0.9)
+    say(" ", r, a)
+    full.close()
+    tree.close()
+
+
 def test_batched_append_p_sweep():
     """Batched decode with growth, routing at several p per step (reduced sizes)."""
     cfg = small("batch8_append_512k", n_tokens=8192, append_steps=64, n_queries=64)
