@@ -99,13 +99,16 @@ constexpr int ATT_STEP = 32;  // positions per wave step
 // Token lookup for one wave's window of ATT_STEP positions starting at p0.  The chunk
 // ids the window touches (at most ATT_STEP / C + 2) are fetched with one load, lane j
 // holding the j-th, and handed to the lanes that need them with a shuffle, so a window's
-// K/V addresses cost one dependent load that can be issued windows ahead.
-template <bool DENSE>
+// K/V addresses cost one dependent load that can be issued windows ahead.  PO2: the chunk
+// is a power of two (Cshift >= 0) and every lookup is shifts and selects, with no branch
+// between the K/V loads of a window (the generic form divides by C and returns early).
+template <bool DENSE, bool PO2 = false>
 struct Window {
   int ids;  // this lane's chunk id (lane j: chunk cb + j of the window)
 
   __device__ static __forceinline__ int first_chunk(const Positions& P, int p0, int C, int Cshift) {
     const int q = p0 - P.nx;
+    if constexpr (PO2) return max(q, 0) >> Cshift;
     if (q <= 0) return 0;
     return Cshift >= 0 ? (q >> Cshift) : q / C;
   }
@@ -120,6 +123,16 @@ struct Window {
   // Every lane of the wave must call this together (it shuffles).
   __device__ __forceinline__ int token(const Positions& P, int p0, int p, int end, int C, int Cshift) const {
     if (DENSE) return p < end ? p : 0;
+    if constexpr (PO2) {
+      const int q = p - P.nx;
+      const int qc = max(q, 0);
+      const int src = min(max((qc >> Cshift) - first_chunk(P, p0, C, Cshift), 0), 63);
+      const int id = __shfl(ids, src);
+      const int ctok = (id << Cshift) + (qc & ((1 << Cshift) - 1));
+      const int xtok = (P.sink && p == 0) ? 0 : P.Nc + p - P.sink;  // sink, then the tail
+      const int tok = q < 0 ? xtok : ctok;
+      return p < end ? tok : 0;
+    }
     const int q = p - P.nx;
     int k = 0;
     if (q > 0) k = Cshift >= 0 ? (q >> Cshift) : q / C;
@@ -145,8 +158,8 @@ template <int D> struct PV<__bf16, D> {
   static constexpr int RPI = 64 / CPR;                        // rows per load instruction
   static constexpr int NLD = ATT_STEP / RPI;
 
-  template <bool DENSE>
-  __device__ static __forceinline__ void load(vfrag& vf, const __bf16* Vb, const Positions& P, const Window<DENSE>& win,
+  template <class WIN>
+  __device__ static __forceinline__ void load(vfrag& vf, const __bf16* Vb, const Positions& P, const WIN& win,
                                               int p0, int end, int C, int Cshift, int lane) {
 #pragma unroll
     for (int k = 0; k < NLD; ++k) {
@@ -199,8 +212,8 @@ template <int D> struct PV<float, D> {
   static constexpr int LDS_ELEMS = 0;
   static constexpr int ND = D / 16;
   typedef float vfrag[2][4][ND];
-  template <bool DENSE>
-  __device__ static __forceinline__ void load(vfrag& vf, const float* Vb, const Positions& P, const Window<DENSE>& win,
+  template <class WIN>
+  __device__ static __forceinline__ void load(vfrag& vf, const float* Vb, const Positions& P, const WIN& win,
                                               int p0, int end, int C, int Cshift, int lane) {
     const int row = lane & 15, grp = lane >> 4;
 #pragma unroll
@@ -224,11 +237,14 @@ template <int D> struct PV<float, D> {
   }
 };
 
-template <typename T, int D, bool DENSE, bool UNI>
-__global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_attend_kernel(AttArgs a, LensArg<DENSE> la) {
+// Two waves per SIMD for bf16 K/V (at most 256 registers per lane; a second workgroup per
+// compute unit keeps twice the K/V loads in flight).
+template <typename T, int D, bool DENSE, bool UNI, bool PO2 = false>
+__global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void zha_attend_kernel(AttArgs a, LensArg<DENSE> la) {
   typedef Mf<T> M;
   typedef PV<T, D> PVT;
   constexpr bool TD = DENSE;  // positions are tokens
+  typedef Window<TD, PO2 && !DENSE> Win;
   constexpr int NK = D / M::KPER;
   constexpr int ND = D / 16;
   constexpr int LDS_WAVE = PVT::LDS_ELEMS > 0 ? PVT::LDS_ELEMS : 1;
@@ -307,7 +323,7 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
 
   // One window: K rows of the two 16-token tiles (lane row r -> position p0 + 16t + r) and
   // the V tile, loaded into registers.
-  auto load_kv = [&](typename M::frag (&kf)[2][NK], typename PVT::vfrag& vf, const Window<TD>& win, int p0) {
+  auto load_kv = [&](typename M::frag (&kf)[2][NK], typename PVT::vfrag& vf, const Win& win, int p0) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int tok = win.token(P, p0, p0 + 16 * t + row, end, a.C, a.Cshift);
@@ -315,7 +331,7 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
 #pragma unroll
       for (int s = 0; s < NK; ++s) kf[t][s] = M::load_stream(kr + s * M::KPER);
     }
-    PVT::template load<TD>(vf, Vb, P, win, p0, end, a.C, a.Cshift, lane);
+    PVT::load(vf, Vb, P, win, p0, end, a.C, a.Cshift, lane);
   };
   // UNI: stamps (the high words of the kept-rank entries) of the chunks of this lane's
   // positions p0 + 16t + 4grp + jj for the lane's column unit (0 outside the chunk part).
@@ -323,8 +339,8 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
   // A lane's four consecutive positions lie in at most three consecutive kept chunks (two when
   // C >= 3): three stamps per group of four, from the window's chunk ids (a stamp needs no
   // token), loaded unconditionally (ids outside the list are 0, a readable entry).
-  auto fetch_rank = [&](const Window<TD>& win, int p0, uint32_t (&rk)[2][4]) {
-    const int cb = Window<TD>::first_chunk(P, p0, a.C, a.Cshift);
+  auto fetch_rank = [&](const Win& win, int p0, uint32_t (&rk)[2][4]) {
+    const int cb = Win::first_chunk(P, p0, a.C, a.Cshift);
     auto lidx = [&](int q) { return q > 0 ? (a.Cshift >= 0 ? (q >> a.Cshift) : q / a.C) : 0; };
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -418,7 +434,7 @@ __global__ __launch_bounds__(256, (UNI && sizeof(T) == 2) ? 2 : 1) void zha_atte
   // computed, the K/V loads of window i+1 and the chunk ids of window i+2 are in flight.
   // The two register buffers alternate by unrolling the loop twice.
   int p0 = start + wave * ATT_STEP;
-  Window<TD> w0, w1;
+  Win w0, w1;
   typename M::frag kA[2][NK], kB[2][NK];
   typename PVT::vfrag vA, vB;
   if constexpr (UNI) {
@@ -862,6 +878,12 @@ __global__ __launch_bounds__(MERGE_THREADS) void zha_merge_kernel(const float* p
 // rows: routing units, or groups of them (UNI)
 template <typename T, int D, bool DENSE, bool UNI = false>
 hipError_t launch_att(const AttArgs& a, const LensArg<DENSE>& la, int rows, hipStream_t s) {
+  if constexpr (!DENSE && !UNI) {
+    if (a.Cshift >= 0) {
+      hipLaunchKernelGGL((zha_attend_kernel<T, D, false, false, true>), dim3(a.W, rows), dim3(256), 0, s, a, la);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((zha_attend_kernel<T, D, DENSE, UNI>), dim3(a.W, rows), dim3(256), 0, s, a, la);
   return hipGetLastError();
 }
