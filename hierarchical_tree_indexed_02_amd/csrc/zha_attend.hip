@@ -825,6 +825,21 @@ __global__ __launch_bounds__(MERGE_THREADS) void zha_merge_kernel(const float* p
   __shared__ float s_red[MERGE_THREADS / 64];
   __shared__ float4 s_o[NGRP][TPR];
   __shared__ float s_l[NGRP];
+  const int j = tid / TPR, c = tid % TPR;
+  // thread (j, c) takes records j, j + NGRP, ... in batches; the first batch is in flight
+  // while the maximum is formed
+  float2 ml[MERGE_BATCH];
+  float4 v[MERGE_BATCH];
+  auto load_batch = [&](int w0) {
+#pragma unroll
+    for (int k = 0; k < MERGE_BATCH; ++k) {  // unconditional loads from clamped records (W >= 1)
+      const int w = w0 + k * NGRP, wc = min(w, W - 1);
+      const float2 x = *(const float2*)(pml + (int64_t)wc * G * 2);
+      v[k] = *(const float4*)(po + (int64_t)wc * G * D + 4 * c);
+      ml[k] = w < W ? x : make_float2(0.0f, 0.0f);  // y = 0: the record is skipped
+    }
+  };
+  load_batch(j);
   float mx = -INFINITY;
   for (int w = tid; w < W; w += MERGE_THREADS) {
     const float2 r = *(const float2*)(pml + (int64_t)w * G * 2);
@@ -836,18 +851,10 @@ __global__ __launch_bounds__(MERGE_THREADS) void zha_merge_kernel(const float* p
   __syncthreads();
   float M = s_red[0];
   for (int k = 1; k < MERGE_THREADS / 64; ++k) M = fmaxf(M, s_red[k]);
-  const int j = tid / TPR, c = tid % TPR;
   float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   float lsum = 0.0f;
   for (int w0 = j; w0 < W; w0 += NGRP * MERGE_BATCH) {
-    float2 ml[MERGE_BATCH];
-    float4 v[MERGE_BATCH];
-#pragma unroll
-    for (int k = 0; k < MERGE_BATCH; ++k) {
-      const int w = w0 + k * NGRP;
-      ml[k] = w < W ? *(const float2*)(pml + (int64_t)w * G * 2) : make_float2(0.0f, 0.0f);
-      v[k] = w < W ? *(const float4*)(po + (int64_t)w * G * D + 4 * c) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    }
+    if (w0 > j) load_batch(w0);
 #pragma unroll
     for (int k = 0; k < MERGE_BATCH; ++k) {
       if (ml[k].y > 0.0f) {
