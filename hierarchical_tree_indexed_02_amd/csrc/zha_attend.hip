@@ -885,9 +885,9 @@ __global__ __launch_bounds__(MERGE_THREADS) void zha_merge_kernel(const float* p
 // rows: routing units, or groups of them (UNI)
 template <typename T, int D, bool DENSE, bool UNI = false>
 hipError_t launch_att(const AttArgs& a, const LensArg<DENSE>& la, int rows, hipStream_t s) {
-  if constexpr (!DENSE && !UNI) {
+  if constexpr (!DENSE) {
     if (a.Cshift >= 0) {
-      hipLaunchKernelGGL((zha_attend_kernel<T, D, false, false, true>), dim3(a.W, rows), dim3(256), 0, s, a, la);
+      hipLaunchKernelGGL((zha_attend_kernel<T, D, false, UNI, true>), dim3(a.W, rows), dim3(256), 0, s, a, la);
       return hipGetLastError();
     }
   }
