@@ -520,7 +520,7 @@ __global__ __launch_bounds__(256, sizeof(T) == 2 ? 2 : 1) void zha_attend_kernel
 // stages' loads in flight in registers while one is computed), and wave w multiplies its
 // window (slot w / CT) with its 16 columns (tile w % CT), each column's softmax masked to
 // its own unit's set as in zha_attend_kernel<..., UNI>.
-template <int D, int CT>
+template <int D, int CT, bool PO2 = false>
 __global__ __launch_bounds__(256, 2) void zha_attend_union_lds_kernel(AttArgs a) {
   typedef Mf<__bf16> M;
   typedef PV<__bf16, D> PVT;
@@ -591,9 +591,10 @@ __global__ __launch_bounds__(256, 2) void zha_attend_union_lds_kernel(AttArgs a)
   // whose rank entry is always readable (only positions of the chunk part use them).
   static_assert(TOK / 2 + 2 <= 64, "a stage touches at most 64 chunks (C >= 2)");
   const int nidx = max(P.nK - 1, 0);
+  const bool csh = PO2 || a.Cshift >= 0;  // PO2: the chunk is a power of two (no division)
   auto first_chunk = [&](int ps) {
     const int q = ps - P.nx;
-    return q <= 0 ? 0 : (a.Cshift >= 0 ? (q >> a.Cshift) : q / a.C);
+    return q <= 0 ? 0 : (csh ? (q >> a.Cshift) : q / a.C);
   };
   auto stage_ids = [&](int ps) -> int {
     const int x = P.kp[min(first_chunk(ps) + lane, nidx)];
@@ -603,9 +604,9 @@ __global__ __launch_bounds__(256, 2) void zha_attend_union_lds_kernel(AttArgs a)
   // lane calls this together (it shuffles)
   auto stage_token = [&](int ids, int ps, int p) -> int {
     const int q = p - P.nx;
-    const int k = q > 0 ? (a.Cshift >= 0 ? (q >> a.Cshift) : q / a.C) : 0;
+    const int k = q > 0 ? (csh ? (q >> a.Cshift) : q / a.C) : 0;
     const int id = __shfl(ids, min(max(k - first_chunk(ps), 0), 63));
-    const int ct = a.Cshift >= 0 ? (id << a.Cshift) + (q & ((1 << a.Cshift) - 1)) : id * a.C + (q - k * a.C);
+    const int ct = csh ? (id << a.Cshift) + (q & ((1 << a.Cshift) - 1)) : id * a.C + (q - k * a.C);
     const int pre = (P.sink && p == 0) ? 0 : P.Nc + p - P.sink;
     return p >= end ? 0 : (q < 0 ? pre : ct);
   };
@@ -637,7 +638,7 @@ __global__ __launch_bounds__(256, 2) void zha_attend_union_lds_kernel(AttArgs a)
   // unconditional (every id is a listed chunk, or chunk 0 for an empty list: readable).
   auto fetch_rank = [&](int ps, int ids, uint32_t (&rk)[2][4]) {
     const int cb = first_chunk(ps);
-    auto lidx = [&](int q) { return q > 0 ? (a.Cshift >= 0 ? (q >> a.Cshift) : q / a.C) : 0; };
+    auto lidx = [&](int q) { return q > 0 ? (csh ? (q >> a.Cshift) : q / a.C) : 0; };
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int p0 = ps + ws * ATT_STEP + 16 * t + 4 * grp;
@@ -968,11 +969,14 @@ hipError_t zha_launch_attend(zha_tree* t, const void* q, const void* K, const vo
   zha_time_begin(t, s, ZHA_K_ATTEND, 0);
   hipError_t e;
   if (uni && CT > 1) {  // bf16 (wider groups are formed for bf16 only): windows staged in LDS
+    const bool p2 = a.Cshift >= 0;
     if (CT == 2)
-      hipLaunchKernelGGL((t->d == 64 ? zha_attend_union_lds_kernel<64, 2> : zha_attend_union_lds_kernel<128, 2>),
+      hipLaunchKernelGGL((t->d == 64 ? (p2 ? zha_attend_union_lds_kernel<64, 2, true> : zha_attend_union_lds_kernel<64, 2>)
+                                     : (p2 ? zha_attend_union_lds_kernel<128, 2, true> : zha_attend_union_lds_kernel<128, 2>)),
                          dim3(a.W, rows), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((t->d == 64 ? zha_attend_union_lds_kernel<64, 4> : zha_attend_union_lds_kernel<128, 4>),
+      hipLaunchKernelGGL((t->d == 64 ? (p2 ? zha_attend_union_lds_kernel<64, 4, true> : zha_attend_union_lds_kernel<64, 4>)
+                                     : (p2 ? zha_attend_union_lds_kernel<128, 4, true> : zha_attend_union_lds_kernel<128, 4>)),
                          dim3(a.W, rows), dim3(256), 0, s, a);
     e = hipGetLastError();
   } else {
