@@ -231,7 +231,9 @@ __device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t w, float sc) {
 // jcol of unit cu(c)): every loaded plane tile feeds NT matrix products.  A node is loaded
 // when some column's unit has its parent kept (a stamped rank entry), and each column keeps
 // the scores of its unit's member nodes at the unit's frontier positions.
-template <typename T, int R, int D, int UN, int SM, bool UNI, int NT, bool PSEL>
+// PO2: the chunk is a power of two, so node and parent ids are shifts (the generic form divides
+// by C under a branch on every id).
+template <typename T, int R, int D, int UN, int SM, bool UNI, int NT, bool PSEL, bool PO2 = false>
 __global__ __launch_bounds__(256, UNI ? 2 : (PSEL ? 3 : 4)) void zha_score_kernel(ScoreArgs a) {
   typedef Mf<T> M;
   static_assert(!PSEL || !UNI, "in-kernel parent selection serves one routing unit per grid row");
@@ -251,6 +253,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : (PSEL ? 3 : 4)) void zha_score_kerne
   static_assert(!UNI || R >= 4, "union scoring keeps one node per lane group");
   static_assert(UNI || NT == 1, "one column tile unless scoring unions");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool csh = PO2 || a.v.Cshift >= 0;
   const int row = lane & 15, grp = lane >> 4;
   const int G = a.G;
   // per column tile n: u[n] the routing unit (frontier, scores, partials) of this lane's
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : (PSEL ? 3 : 4)) void zha_score_kerne
     for (int k = 0; k < UN; ++k) {
       if constexpr (UNI) {
         const int id = base + (k * 4 + wave) * NPT + (4 * grp) / R;
-        const int P = a.v.Cshift >= 0 ? (id >> a.v.Cshift) : id / a.v.C;
+        const int P = csh ? (id >> a.v.Cshift) : id / a.v.C;
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           const bool need = a.krank && ok[n] && id < end;
@@ -353,7 +356,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : (PSEL ? 3 : 4)) void zha_score_kerne
       } else {
         const int pos = base + (k * 4 + wave) * NPT + row / R;
         const bool need = has_par && pos < end;
-        const int pidx = need ? (a.v.Cshift >= 0 ? (pos >> a.v.Cshift) : pos / a.v.C) : 0;
+        const int pidx = need ? (csh ? (pos >> a.v.Cshift) : pos / a.v.C) : 0;
         int32_t x;
         if constexpr (PSEL) x = wsh_[0].kept[pidx];
         else x = (FLAT || need) ? pload[pidx] : 0;
@@ -377,7 +380,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : (PSEL ? 3 : 4)) void zha_score_kerne
         if (a.krank) {
           m = ok[n] && id < end && (uint32_t)(rk[k][n] >> 32) == stamp;
           const int rank = (int)(uint32_t)rk[k][n];
-          pos = a.v.Cshift >= 0 ? (rank << a.v.Cshift) + (id & ((1 << a.v.Cshift) - 1)) : rank * a.v.C + id % a.v.C;
+          pos = csh ? (rank << a.v.Cshift) + (id & ((1 << a.v.Cshift) - 1)) : rank * a.v.C + id % a.v.C;
         } else {
           m = ok[n] && id < end;
           pos = id;
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : (PSEL ? 3 : 4)) void zha_score_kerne
       const int pos = tbk + row / R;
       const bool v = UNI ? ((act[k] >> (row / R)) & 1u) != 0 : pos < end;
       int id = pos;
-      if (!UNI && has_par) id = a.v.Cshift >= 0 ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
+      if (!UNI && has_par) id = csh ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
                                            : pp[k] * a.v.C + pos % a.v.C;
       id = v ? id : 0;
       // inactive rows read node 0 (FLAT) or nothing; their results are never written
@@ -503,7 +506,7 @@ __global__ __launch_bounds__(256, UNI ? 2 : (PSEL ? 3 : 4)) void zha_score_kerne
       const int pos = tbk + row / R;
       const bool v = UNI ? ((act[k] >> (row / R)) & 1u) != 0 : pos < end;
       int id = pos;
-      if (!UNI && has_par) id = a.v.Cshift >= 0 ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
+      if (!UNI && has_par) id = csh ? (pp[k] << a.v.Cshift) + (pos & ((1 << a.v.Cshift) - 1))
                                            : pp[k] * a.v.C + pos % a.v.C;
       id = v ? id : 0;
       if constexpr (F4) {
@@ -2116,6 +2119,12 @@ __global__ __launch_bounds__(CPT) void zha_compact_kernel(CompactArgs a) {
 // SM: summary storage (0 native, 1 fp8, 2 fp4)
 template <typename T, int R, int D, int SM, bool UNI, int NT = 1, bool PSEL = false>
 hipError_t launch_score(const ScoreArgs& a, int W, int rows, hipStream_t s) {
+  if constexpr (!UNI && !PSEL) {  // the streaming levels of one-unit rows: shifts for power-of-two chunks
+    if (a.v.Cshift >= 0) {
+      hipLaunchKernelGGL((zha_score_kernel<T, R, D, 2, SM, false, 1, false, true>), dim3(W, rows), dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((zha_score_kernel<T, R, D, 2, SM, UNI, NT, PSEL>), dim3(W, rows), dim3(256), 0, s, a);
   return hipGetLastError();
 }
