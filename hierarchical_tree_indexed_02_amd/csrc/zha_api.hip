@@ -576,8 +576,10 @@ zha_status zha_route_copy_level(zha_tree_t t, int32_t level, int32_t* frontier_c
 zha_status zha_timing_enable(zha_tree_t t, int32_t kernel_mask, int32_t level_mask) {
   if (!t) return ZHA_ERR_INVALID;
   if (kernel_mask && !t->ev[0]) {
+    // timing-only events: no system-scope fence when recorded (the writeback and invalidation
+    // of the caches that fence costs would sit between the timed launch and its neighbours)
     for (int i = 0; i < 2 * ZHA_MAX_TIMING; ++i)
-      if (hipEventCreate(&t->ev[i]) != hipSuccess) return ZHA_ERR_HIP;
+      if (hipEventCreateWithFlags(&t->ev[i], hipEventDisableSystemFence) != hipSuccess) return ZHA_ERR_HIP;
   }
   t->timing_kernels = kernel_mask;
   t->timing_levels = level_mask;

@@ -314,7 +314,8 @@ ZHA_API zha_status zha_route_copy_level(zha_tree_t tree, int32_t level, int32_t*
  * the caller has synchronised the stream, zha_timing_read returns for each
  * recorded launch its kernel code, its level and its duration in ms, and
  * clears the record.  At most 256 launches are kept between reads; later ones
- * are not recorded.  Not for use under stream capture. */
+ * are not recorded.  The events only measure time (they are recorded without a
+ * system-scope fence).  Not for use under stream capture. */
 enum { ZHA_K_BUILD = 1, ZHA_K_APPEND = 2, ZHA_K_SCORE = 3, ZHA_K_SELECT = 4,
        ZHA_K_ATTEND = 5, ZHA_K_MERGE = 6, ZHA_K_MASS = 7, ZHA_K_COMPACT = 8 };
 #define ZHA_TIMING_ALL (-1)
