@@ -158,8 +158,8 @@ def model_constants(res, caps, bw):
     decode on the same GPU and inputs) -- not fitted:
       delta     how much an event-timed launch overstates its share of the step: (sum of the
                 launch times - the step time) / launches;
-      t_wave    one worker wave of a scoring launch: the top level's launch, whose few nodes
-                leave every workgroup one super-tile (a launch takes at least this long);
+      t_wave    the worker-wave cost of a scoring launch, paid on top of streaming its bytes:
+                the top level's launch (every workgroup one super-tile) less its bytes' time;
       c_fused   selection of a small level inside the next level's scoring launch: the time
                 those launches take beyond their own scoring;
       c_small   the one-workgroup selection launch; c_large: selection, mass and compaction of a
@@ -169,9 +169,9 @@ def model_constants(res, caps, bw):
     L = len(caps)
     Bl = res["route_bytes_l"]
     delta = (sum(k.values()) - res["ms_step"] * 1e3) / launches(caps)
-    t_wave = k[f"score_l{L}"] - delta
+    t_wave = k[f"score_l{L}"] - delta - Bl[L] / bw
     fused = [l for l in range(1, L) if level_kind(l + 1, caps[l]) == "fused"]
-    c_fused = (sum(k[f"score_l{l}"] - delta - max(t_wave, Bl[l] / bw) for l in fused) / len(fused)) if fused else 0.0
+    c_fused = (sum(k[f"score_l{l}"] - delta - (t_wave + Bl[l] / bw) for l in fused) / len(fused)) if fused else 0.0
     small = [l for l in range(1, L + 1) if level_kind(l, caps[l - 1]) == "small"]
     large = [l for l in range(1, L + 1) if level_kind(l, caps[l - 1]) == "large"]
     c_small = sum(k.get(f"select_l{l}", 0.0) - delta for l in small) / len(small) if small else 0.0
@@ -186,12 +186,12 @@ def model_constants(res, caps, bw):
 def model_step(row, m):
     """Step time of one geometry from the four segments of the pages' model: build (none in a
     decode step without growth), per-level routing (each level's scoring launch streams its
-    plane bytes at the dense bandwidth but takes at least one worker wave), node scan (each
+    plane bytes at the dense bandwidth and pays one worker wave on top), node scan (each
     level's selection, by kind) and attention (the attended K/V bytes at the dense bandwidth
     plus its fixed time).  Returns the total and the segments in microseconds."""
     bw = m["bw_gbs"] * 1e3  # bytes per microsecond
     caps = row["caps"]
-    route = sum(max(m["t_wave_us"], b / bw) for b in row["route_bytes_l"].values())
+    route = sum(m["t_wave_us"] + b / bw for b in row["route_bytes_l"].values())
     scan = 0.0
     for l in range(1, len(caps) + 1):
         kind = level_kind(l, caps[l - 1])
