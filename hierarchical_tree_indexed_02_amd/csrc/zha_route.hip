@@ -2388,7 +2388,11 @@ hipError_t zha_launch_route(zha_tree* t, const void* q, float p, float scale, hi
       ma.fh_mass = (u64*)t->fh_mass;
       ma.fh_edge = (u64*)t->fh_edge;
       ma.G = Gr;
+      // 1024 positions per workgroup, at most 512 workgroups in all: every workgroup adds its
+      // histogram to the unit's with global atomics, and with many routing units (per-head
+      // routes, batches) more workgroups only contend on those addresses
       int64_t wm = (t->cap[l] + 1023) / 1024;
+      wm = std::min<int64_t>(wm, std::max(1, 512 / U));
       ma.WM = (int)(wm > 256 ? 256 : (wm < 1 ? 1 : wm));
       zha_time_begin(t, s, ZHA_K_MASS, l);
       hipLaunchKernelGGL(zha_mass_kernel, dim3(ma.WM, U), dim3(256), 0, s, ma);
