@@ -472,6 +472,68 @@ def test_large_level_with_short_sequence():
         say(f" p={p}", r, a)
 
 
+GRAPH_CASES = [
+    ("bf16 d128 C4 L3 R16 G8 B2", dict(batch=2, n_tokens=5000, chunk=4, levels=3, n_refs=16)),
+    ("bf16 d128 C4 L2 R16 G8 large level", dict(batch=1, n_tokens=65539, n_q_heads=16, n_kv_heads=2, chunk=4, levels=2,
+                                                  n_refs=16)),
+]
+
+
+@pytest.mark.parametrize("label,kw", GRAPH_CASES, ids=[c[0] for c in GRAPH_CASES])
+def test_route_attend_graph_replays(label, kw):
+    """Route + attend captured in a HIP graph (they allocate nothing, enqueue no memset and do
+    not wait on the host): every replay, with another query's eager route and attention and a
+    synchronisation before it, equals the eager result bit for bit -- small levels selected
+    inside the next level's launch, and a 16384-node level with the mass, cut and look-back
+    compaction (whose epochs advance on the device)."""
+    cfg = small(**kw, n_queries=2, needles_per_unit=4)
+    say(f"case graph replays, {label}")
+    case = Case(cfg, n_queries=2)
+    tree = case.tree()
+    q0, q1 = case.qd[0], case.qd[1]
+
+    def kept_lists():
+        _, nk, ids = tree.route_level(1)
+        nk = nk.cpu().tolist()
+        ids = ids.cpu()
+        return nk, [ids[u, :n].clone() for u, n in enumerate(nk)]
+
+    tree.route(q0, 0.9, 1.0)
+    o_ref, l_ref = tree.attend(q0, case.Kd, case.Vd, 1.0)
+    torch.cuda.synchronize()
+    o_ref, l_ref = o_ref.clone(), l_ref.clone()
+    nk_ref, ids_ref = kept_lists()
+    qs = q0.clone()
+    out = torch.empty_like(o_ref)
+    lse = torch.empty_like(l_ref)
+    side = torch.cuda.Stream()  # warm-up on a side stream before capture
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        tree.route(qs, 0.9, 1.0)
+        tree.attend(qs, case.Kd, case.Vd, 1.0, out=out, lse=lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tree.route(qs, 0.9, 1.0)
+        tree.attend(qs, case.Kd, case.Vd, 1.0, out=out, lse=lse)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        tree.route(q1, 0.5, 1.0)  # eager work of another query between replays
+        tree.attend(q1, case.Kd, case.Vd, 1.0)
+        torch.cuda.synchronize()
+        out.zero_()
+        lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        nk, ids = kept_lists()
+        assert nk == nk_ref, f"replay {rep}: kept counts {nk} != {nk_ref}"
+        assert all(torch.equal(a, b) for a, b in zip(ids, ids_ref)), f"replay {rep}: kept ids differ"
+        assert torch.equal(out, o_ref) and torch.equal(lse, l_ref), f"replay {rep}: attention differs"
+    tree.check()
+    say(f" 4 replays bit-identical to the eager route and attention (kept {sum(nk_ref)} chunks)")
+
+
 def test_small_level_p_sweep():
     """Every level of at most 1024 nodes (level 1 by its own selection launch, levels 2 and 3
     by the next level's scoring launch) across many p: the crossing slice lands on heavier and
